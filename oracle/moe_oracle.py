@@ -1,0 +1,368 @@
+"""fp64 CPU oracle of the sparse MoE feed-forward layer (forward pass).
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the package's smoke check and the
+benchmark's CPU-baseline leg may import or run this module.  The GPU library
+never calls it and shares no code with it; the two meet only in the seeded
+input generator (``synth``), which holds none of the layer's arithmetic.
+
+What it computes.  The layer is exact (not an approximation), so the oracle
+is the plain definition written out step by step in fp64, reading the exact
+stored input values (bf16 expanded by placing its 16 bits on top of an fp32
+pattern, fp32 promoted).  Sources, all on the page "MoE: how sparse
+activation saves compute" unless another page is named:
+
+  * SwiGLU expert F(u) = W_down (SiLU(W_gate u) * W_up u)        -- §3.1, eq. F(u)
+  * router scores z = W_route u and softmax p                     -- §3.2, eqs. z, p
+  * top-k set S_t, renormalised weights a = p / sum_{S_t} p,
+    combine y_t = sum_{i in S_t} a_{t,i} F_i(u_t)                 -- §3.2, eqs. a, y
+  * top-1 (Switch) keeps the selected probability as the weight  -- §3.2, last paragraph
+  * capacity C = ceil(c T / N), overflow tokens skip the layer    -- §3.5, eq. C
+  * for k > 1 capacity counts dispatches (k T)                   -- §3.5, second paragraph
+  * shapes [T,d] -> [T,N] -> [T,k] -> per expert [L_i,d]         -- §3.6
+  * f_i, P_i and L_aux = alpha N sum f_i P_i                      -- §3.4, eqs. f, P, L_aux
+  * overflow and empty-slot ledgers                               -- §3.8
+  * parameter ledger P_all = N 3dh, P_active = k 3dh              -- §3.3
+  * dense all-experts reference (every expert evaluated, weight 0
+    where unselected)                                             -- appendix, moe_lab.py main()
+  * LatentMoE: d->l projection, routed experts at width l, RMSNorm
+    after aggregation and before the l->d projection, shared
+    experts at width d, SiTU-GLU soft caps on both GLU factors    -- page "Stable LatentMoE
+                                                                     interactive demo", the
+                                                                     width-separation, RMSNorm
+                                                                     and SiTU-GLU passages
+
+Readings where the pages are silent (listed again in the design doc):
+  * ties in top-k go to the lower expert index; slots are ordered by
+    descending p;
+  * capacity ranks are in token order (the first C tokens that reach an
+    expert are kept), the order in which the appendix code's
+    ``torch.where(top_idx == e)`` lists them;
+  * a dropped slot contributes 0 and the remaining weights are not
+    renormalised;
+  * f_i is the argmax indicator of §3.4's formula, taken before capacity;
+  * SiTU-GLU(g, v) = SiLU(beta_g tanh(g / beta_g)) * beta_u tanh(v / beta_u);
+  * RMSNorm(r) = r / sqrt(mean(r^2) + eps), no learned gain;
+  * LatentMoE routes on the full-width u, adds shared experts with weight 1.
+
+Pins (tests/test_oracle_pins.py): the capacity example [10,3,2,1] -> drops
+6/4/0; the balanced/collapsed aux example (1.0000 / 2.8449); the parameter
+ledger; the seed-7 routing loads [8,7,8,9]; sparse == dense brute force;
+N=1 reduces to a torch.nn.functional SwiGLU; softmax/top-k against torch;
+dispatch order against torch.where; RMSNorm against torch's rms_norm;
+latent limits (beta -> inf gives SwiGLU; identity projections give
+RMSNorm(plain); scale invariance); the 12.4% latent parameter saving.
+Parity unpinned: the exact SiTU-GLU form and the LatentMoE wiring are
+readings, pinned only through the limits and invariants above.
+"""
+from __future__ import annotations
+
+import math
+from typing import Callable, Dict, Optional, Sequence
+
+import numpy as np
+
+# ---------------------------------------------------------------------------
+# Stored values -> fp64 (exact)
+# ---------------------------------------------------------------------------
+
+
+def expand(stored: np.ndarray) -> np.ndarray:
+    """Exact fp64 value of stored bf16 bit patterns (uint16) or fp32 values."""
+    a = np.asarray(stored)
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    if a.dtype in (np.float32, np.float64):
+        return a.astype(np.float64)
+    raise TypeError(f"unsupported stored dtype {a.dtype}")
+
+
+# ---------------------------------------------------------------------------
+# Router: scores, softmax, top-k, gate weights  (§3.2)
+# ---------------------------------------------------------------------------
+
+
+def router_logits(u: np.ndarray, w_route: np.ndarray) -> np.ndarray:
+    """z[t, i] = (W_route u_t)_i; u [T, d], W_route [N, d]."""
+    return u @ w_route.T
+
+
+def softmax(z: np.ndarray) -> np.ndarray:
+    """Row-wise softmax; the row max is subtracted before exponentiating."""
+    m = z.max(axis=1, keepdims=True)
+    e = np.exp(z - m)
+    return e / e.sum(axis=1, keepdims=True)
+
+
+def select_topk(p: np.ndarray, k: int) -> np.ndarray:
+    """S_t: the k experts of largest p, by descending p, ties to the lower index."""
+    order = np.argsort(-p, axis=1, kind="stable")
+    return order[:, :k].astype(np.int64)
+
+
+def topk_margin(z: np.ndarray, k: int) -> np.ndarray:
+    """z_(k) - z_(k+1) per token (descending order statistics); +inf when k = N."""
+    N = z.shape[1]
+    if k >= N:
+        return np.full(z.shape[0], np.inf)
+    zs = -np.sort(-z, axis=1)
+    return zs[:, k - 1] - zs[:, k]
+
+
+def gate_weights(p: np.ndarray, idx: np.ndarray, gate: str) -> np.ndarray:
+    """Combine weights of the selected experts.
+
+    renorm: a = p / sum_{j in S_t} p_j (Mixtral-style, §3.2 eq. a);
+    prob:   a = p (Switch top-1 keeps the selected probability, §3.2).
+    """
+    psel = np.take_along_axis(p, idx, axis=1)
+    if gate == "renorm":
+        return psel / psel.sum(axis=1, keepdims=True)
+    if gate == "prob":
+        return psel
+    raise ValueError(gate)
+
+
+def route(u: np.ndarray, w_route: np.ndarray, k: int, gate: str) -> Dict[str, np.ndarray]:
+    z = router_logits(u, w_route)
+    p = softmax(z)
+    idx = select_topk(p, k)
+    return {"z": z, "p": p, "idx": idx, "a": gate_weights(p, idx, gate),
+            "margin": topk_margin(z, k)}
+
+
+# ---------------------------------------------------------------------------
+# Capacity and dispatch  (§3.5, §3.6, §3.8)
+# ---------------------------------------------------------------------------
+
+
+def capacity_from_factor(T: int, N: int, k: int, c: float) -> int:
+    """Per-expert slots C = ceil(c * k * T / N) (k dispatches per token)."""
+    return int(math.ceil((c * k * T) / N))
+
+
+def dispatch(idx: np.ndarray, N: int, capacity: Optional[int]) -> Dict[str, np.ndarray]:
+    """Group the (token, slot) dispatches by expert, in token order.
+
+    rank(t, s) counts the earlier tokens that chose the same expert; a dispatch
+    is kept iff rank < C.  perm lists entries t*k+s sorted by (expert, token);
+    row_of gives each kept entry its row in the expert-sorted kept rows.
+    """
+    T, k = idx.shape
+    C = None if capacity is None or capacity < 0 else int(capacity)
+    counts = np.zeros(N, dtype=np.int64)
+    rank = np.zeros((T, k), dtype=np.int64)
+    for t in range(T):
+        for s in range(k):
+            e = int(idx[t, s])
+            rank[t, s] = counts[e]
+            counts[e] += 1
+    kept_counts = counts if C is None else np.minimum(counts, C)
+    offsets = np.concatenate([[0], np.cumsum(counts)])
+    kept_offsets = np.concatenate([[0], np.cumsum(kept_counts)])
+    kept = np.ones((T, k), dtype=bool) if C is None else rank < C
+    perm = np.empty(T * k, dtype=np.int64)
+    row_of = np.full(T * k, -1, dtype=np.int64)
+    for t in range(T):
+        for s in range(k):
+            e = int(idx[t, s])
+            perm[offsets[e] + rank[t, s]] = t * k + s
+            if kept[t, s]:
+                row_of[t * k + s] = kept_offsets[e] + rank[t, s]
+    out = {"counts": counts, "offsets": offsets, "kept_counts": kept_counts,
+           "kept_offsets": kept_offsets, "rank": rank.reshape(-1), "perm": perm,
+           "row_of": row_of, "drop": (~kept).reshape(-1).astype(np.uint8)}
+    if C is not None:
+        out["overflow"] = int(np.maximum(counts - C, 0).sum())
+        out["empty_slots"] = int(np.maximum(C - counts, 0).sum())
+        out["static_slots"] = N * C
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Experts  (§3.1; LatentMoE page for SiTU-GLU)
+# ---------------------------------------------------------------------------
+
+
+def silu(x: np.ndarray) -> np.ndarray:
+    with np.errstate(over="ignore"):
+        return x / (1.0 + np.exp(-x))
+
+
+def swiglu(g: np.ndarray, v: np.ndarray) -> np.ndarray:
+    return silu(g) * v
+
+
+def situ_glu(g: np.ndarray, v: np.ndarray, beta_g: float, beta_u: float) -> np.ndarray:
+    """Soft-capped GLU: both factors pass through beta * tanh(x / beta) first."""
+    return silu(beta_g * np.tanh(g / beta_g)) * (beta_u * np.tanh(v / beta_u))
+
+
+def make_act(act: str, beta_g: float = 4.0, beta_u: float = 25.0) -> Callable:
+    if act == "swiglu":
+        return swiglu
+    if act == "situ":
+        return lambda g, v: situ_glu(g, v, beta_g, beta_u)
+    raise ValueError(act)
+
+
+def expert_forward(x: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray,
+                   w_down: np.ndarray, act: Callable) -> np.ndarray:
+    """F(x) for rows x [M, w]: W_down act(W_gate x, W_up x); gate/up [h, w], down [w, h]."""
+    g = x @ w_gate.T
+    v = x @ w_up.T
+    return act(g, v) @ w_down.T
+
+
+def rmsnorm(r: np.ndarray, eps: float) -> np.ndarray:
+    """r / sqrt(mean(r^2) + eps), per row, no gain."""
+    return r / np.sqrt(np.mean(r * r, axis=-1, keepdims=True) + eps)
+
+
+# ---------------------------------------------------------------------------
+# Statistics  (§3.4, §3.3)
+# ---------------------------------------------------------------------------
+
+
+def balance_stats(p: np.ndarray, alpha: float) -> Dict[str, np.ndarray]:
+    """f_i = share of tokens whose argmax is i; P_i = mean p; N sum f P; alpha N sum f P."""
+    T, N = p.shape
+    f = np.bincount(np.argmax(p, axis=1), minlength=N) / T
+    P = p.mean(axis=0)
+    s = N * float(np.sum(f * P))
+    return {"f": f, "P": P, "n_sum_fP": s, "aux": alpha * s}
+
+
+def param_ledger(N: int, k: int, d: int, h: int) -> Dict[str, int]:
+    """Expert parameters: one SwiGLU expert 3dh, all N 3dh, active per token k 3dh."""
+    one = d * h + d * h + h * d
+    return {"one": one, "all": N * one, "active": k * one}
+
+
+def latent_param_saving(d: int, l: int, H: int, E: int) -> float:
+    """Share of routed-expert-side parameters saved by running experts at width l
+    instead of d, counting the added d->l and l->d projections."""
+    full = E * 3 * H * d
+    latent = E * 3 * H * l + 2 * d * l
+    return 1.0 - latent / full
+
+
+# ---------------------------------------------------------------------------
+# Forward passes
+# ---------------------------------------------------------------------------
+
+ExpertFn = Callable[[int], Sequence[np.ndarray]]
+
+
+def _expert64(experts: ExpertFn, e: int):
+    return tuple(expand(w) for w in experts(e))
+
+
+def combine_routed(x: np.ndarray, r: Dict[str, np.ndarray], disp: Dict[str, np.ndarray],
+                   experts: ExpertFn, act: Callable, k: int, out_width: int,
+                   tokens: Optional[np.ndarray] = None) -> np.ndarray:
+    """y_t = sum over kept slots of a_{t,s} F_{idx[t,s]}(x_t), for the given tokens.
+
+    Only selected (and kept) experts run; each expert is evaluated on the rows
+    routed to it.  Rows of tokens outside ``tokens`` are skipped.
+    """
+    want = None if tokens is None else {int(t): i for i, t in enumerate(tokens)}
+    n_out = x.shape[0] if tokens is None else len(tokens)
+    y = np.zeros((n_out, out_width))
+    N = len(disp["counts"])
+    for e in range(N):
+        lo = int(disp["offsets"][e])
+        kept = int(disp["kept_counts"][e])
+        ent = disp["perm"][lo:lo + kept]
+        toks = ent // k
+        slots = ent % k
+        if want is not None:
+            sel = np.array([int(t) in want for t in toks], dtype=bool)
+            toks, slots = toks[sel], slots[sel]
+        if toks.size == 0:
+            continue
+        wg, wu, wd = _expert64(experts, e)
+        xe = x[toks] if want is None else x[[want[int(t)] for t in toks]]
+        fe = expert_forward(xe, wg, wu, wd, act)
+        a = r["a"][toks, slots]
+        dst = toks if want is None else np.array([want[int(t)] for t in toks])
+        for j in range(toks.size):   # one dispatch per (token, slot): no collisions
+            y[dst[j]] += a[j] * fe[j]
+    return y
+
+
+def forward(u_st: np.ndarray, w_route_st: np.ndarray, experts: ExpertFn, *, k: int,
+            gate: str = "renorm", act: str = "swiglu", capacity: Optional[int] = None,
+            beta_g: float = 4.0, beta_u: float = 25.0, alpha: float = 0.01,
+            tokens: Optional[np.ndarray] = None,
+            u_rows_st: Optional[np.ndarray] = None) -> Dict[str, object]:
+    """Plain MoE layer.  Routing and dispatch over all T tokens (capacity depends
+    on every token); outputs y for ``tokens`` (all when None).
+
+    u_st [T, d], w_route_st [N, d] stored; experts(e) -> stored (gate [h,d],
+    up [h,d], down [d,h]).  ``u_rows_st`` may hold the rows of ``tokens`` when
+    u_st is only needed for routing (it is the same data)."""
+    u = expand(u_st)
+    N = w_route_st.shape[0]
+    r = route(u, expand(w_route_st), k, gate)
+    disp = dispatch(r["idx"], N, capacity)
+    x = u if tokens is None else (expand(u_rows_st) if u_rows_st is not None else u[tokens])
+    y = combine_routed(x, r, disp, experts, make_act(act, beta_g, beta_u), k, u.shape[1],
+                       tokens)
+    return {**r, "disp": disp, "y": y, "stats": balance_stats(r["p"], alpha)}
+
+
+def forward_dense(u_st: np.ndarray, w_route_st: np.ndarray, experts: ExpertFn, *, k: int,
+                  gate: str = "renorm", act: str = "swiglu", capacity: Optional[int] = None,
+                  beta_g: float = 4.0, beta_u: float = 25.0) -> np.ndarray:
+    """Brute force: evaluate every expert on every token and weight it by the
+    token's (kept) combine weight, 0 where unselected."""
+    u = expand(u_st)
+    T = u.shape[0]
+    N = w_route_st.shape[0]
+    r = route(u, expand(w_route_st), k, gate)
+    disp = dispatch(r["idx"], N, capacity)
+    kept = (1 - disp["drop"].reshape(T, k)).astype(np.float64)
+    fn = make_act(act, beta_g, beta_u)
+    y = np.zeros_like(u)
+    for e in range(N):
+        wg, wu, wd = _expert64(experts, e)
+        w = np.zeros(T)
+        for s in range(k):
+            w += (r["idx"][:, s] == e) * r["a"][:, s] * kept[:, s]
+        y += w[:, None] * expert_forward(u, wg, wu, wd, fn)
+    return y
+
+
+def latent_forward(u_st: np.ndarray, w_route_st: np.ndarray, experts: ExpertFn,
+                   w_ldown_st: np.ndarray, w_lup_st: np.ndarray, shared: ExpertFn,
+                   n_shared: int, *, k: int, gate: str = "renorm", act: str = "situ",
+                   capacity: Optional[int] = None, beta_g: float = 4.0,
+                   beta_u: float = 25.0, rms_eps: float = 1e-6, alpha: float = 0.01,
+                   tokens: Optional[np.ndarray] = None,
+                   u_rows_st: Optional[np.ndarray] = None) -> Dict[str, object]:
+    """LatentMoE layer: x_l = W_ldown u; route on u; r = sum a E_i(x_l) at width l;
+    y = W_lup RMSNorm(r) + sum_j SwiGLU_j(u) over the shared experts."""
+    u = expand(u_st)
+    N = w_route_st.shape[0]
+    rt = route(u, expand(w_route_st), k, gate)
+    disp = dispatch(rt["idx"], N, capacity)
+    ux = u if tokens is None else (expand(u_rows_st) if u_rows_st is not None else u[tokens])
+    w_ldown = expand(w_ldown_st)
+    w_lup = expand(w_lup_st)
+    xl = ux @ w_ldown.T
+    rsum = combine_routed(xl, rt, disp, experts, make_act(act, beta_g, beta_u), k,
+                          w_ldown.shape[0], tokens)
+    rn = rmsnorm(rsum, rms_eps)
+    y = rn @ w_lup.T
+    for j in range(n_shared):
+        sg, su, sd = (expand(w) for w in shared(j))
+        y = y + expert_forward(ux, sg, su, sd, swiglu)
+    return {**rt, "disp": disp, "x_l": xl, "r": rsum, "r_norm": rn, "y": y,
+            "stats": balance_stats(rt["p"], alpha)}
+
+
+def relative_error(y: np.ndarray, y_ref: np.ndarray) -> float:
+    """max|y - y_ref| / max|y_ref| over every compared element."""
+    den = float(np.max(np.abs(y_ref)))
+    num = float(np.max(np.abs(np.asarray(y, dtype=np.float64) - y_ref)))
+    return num / den if den > 0 else num

@@ -1,0 +1,466 @@
+"""Pins of the fp64 oracle against facts fixed outside the oracle itself:
+values the pages print for worked examples, closed forms, library routines
+for special cases, invariants, and brute force on tiny inputs.
+
+Each test names the passage it follows.  Page 3 is "MoE: how sparse
+activation saves compute"; page 5 is "Stable LatentMoE interactive demo".
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle as O
+import synth
+from synth import configs as C
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+def tiny_experts(cfg):
+    return lambda e: cfg.expert(e)
+
+
+# ---------------------------------------------------------------------------
+# Capacity and drops (page 3, §01, §3.5 eq. C, §3.8, §09 ex. 2-3, appendix)
+# ---------------------------------------------------------------------------
+
+
+def test_capacity_example_uneven_and_even():
+    g = gold("capacity_example.json")
+    T, N = g["T"], g["N"]
+    uneven = np.array(g["uneven_assignment"])[:, None]
+    even = (np.arange(T) % N)[:, None]
+    for i, c in enumerate(g["factors"]):
+        cap = O.capacity_from_factor(T, N, 1, c)
+        assert cap == g["capacity"][i]
+        d = O.dispatch(uneven, N, cap)
+        assert d["counts"].tolist() == g["uneven_loads"]
+        assert d["overflow"] == g["uneven_dropped"][i]
+        assert int(d["drop"].sum()) == g["uneven_dropped"][i]
+        assert d["empty_slots"] == g["uneven_empty_slots"][i]
+        assert d["static_slots"] == g["static_slots"][i]
+        de = O.dispatch(even, N, cap)
+        assert de["overflow"] == g["even_dropped"][i] == int(de["drop"].sum())
+
+
+def test_capacity_counts_dispatches_for_topk():
+    # §3.5 second paragraph: with k slots per token, capacity is sized on k*T.
+    assert O.capacity_from_factor(16, 4, 2, 1.0) == 8
+    assert O.capacity_from_factor(16384, 8, 1, 1.25) == 2560
+
+
+def test_token_order_drops_first_c_kept():
+    # Reading: the first C tokens reaching an expert are kept.
+    idx = np.array(C.PLANTED_ASSIGNMENT)[:, None]
+    d = O.dispatch(idx, 4, 4)
+    dropped_tokens = np.nonzero(d["drop"])[0].tolist()
+    assert dropped_tokens == [4, 5, 6, 7, 8, 9]
+    d6 = O.dispatch(idx, 4, 6)
+    assert np.nonzero(d6["drop"])[0].tolist() == [6, 7, 8, 9]
+
+
+# ---------------------------------------------------------------------------
+# Balance statistics (page 3, §3.4 eqs. f, P, L_aux; §04 printed values)
+# ---------------------------------------------------------------------------
+
+
+def test_aux_balanced_and_collapsed():
+    g = gold("aux_example.json")
+    T, N, v = g["T"], g["N"], g["logit_value"]
+    bal = np.zeros((T, N))
+    bal[np.arange(T), np.arange(T) % N] = v
+    col = np.zeros((T, N))
+    col[:, 0] = v
+    sb = O.balance_stats(O.softmax(bal), alpha=0.01)
+    assert np.allclose(sb["f"], g["balanced"]["f"], atol=0)
+    assert np.allclose(sb["P"], g["balanced"]["P"], atol=1e-15)
+    assert round(sb["n_sum_fP"], 4) == g["balanced"]["n_sum_fP"]
+    sc = O.balance_stats(O.softmax(col), alpha=0.01)
+    assert sc["f"].tolist() == g["collapsed"]["f"]
+    assert [round(x, 4) for x in sc["P"]] == g["collapsed"]["P_4dp"]
+    assert round(sc["n_sum_fP"], 4) == g["collapsed"]["n_sum_fP_4dp"]
+    # Closed forms: P_0 = e^2/(e^2+3), the others 1/(e^2+3); N sum f P = 4 P_0.
+    e2 = math.exp(2.0)
+    assert abs(sc["P"][0] - e2 / (e2 + 3)) < 1e-15
+    assert abs(sc["P"][1] - 1 / (e2 + 3)) < 1e-15
+    assert abs(sc["n_sum_fP"] - 4 * e2 / (e2 + 3)) < 1e-14
+    assert abs(sc["aux"] - 0.01 * sc["n_sum_fP"]) < 1e-16
+
+
+def test_f_is_argmax_before_capacity():
+    # f counts argmax choices, independent of how many were dropped.
+    idx = np.array(C.PLANTED_ASSIGNMENT)
+    p = np.full((16, 4), 0.1)
+    p[np.arange(16), idx] = 0.7
+    s = O.balance_stats(p, 0.01)
+    assert (s["f"] * 16).tolist() == [10, 3, 2, 1]
+
+
+# ---------------------------------------------------------------------------
+# Parameter ledger (page 3, §01 and §3.3)
+# ---------------------------------------------------------------------------
+
+
+def test_param_ledger_matches_page():
+    g = gold("ledger_example.json")
+    L = O.param_ledger(g["N"], g["k"], g["d"], g["h"])
+    assert L["one"] == g["one"] and L["all"] == g["all"] and L["active"] == g["active"]
+    assert L["all"] / L["active"] == g["ratio"] == g["N"] / g["k"]
+    assert round(L["all"] * 2 / 2**30, 3) == g["bf16_gib_3dp"]
+
+
+def test_forward_touches_only_k_experts_per_token():
+    # The forward evaluates exactly the k selected experts of a token, i.e.
+    # k*3dh expert parameters out of N*3dh (active/total = k/N).
+    cfg = C.TINY
+    seen = []
+
+    def experts(e):
+        seen.append(e)
+        return cfg.expert(e)
+
+    u = cfg.u()[:1]
+    out = O.forward(u, cfg.w_route(), experts, k=cfg.k)
+    assert sorted(seen) == sorted(out["idx"][0].tolist())
+    L = O.param_ledger(cfg.N, cfg.k, cfg.d, cfg.h)
+    touched = sum(sum(w.size for w in cfg.expert(e)) for e in seen)
+    assert touched == L["active"] and L["all"] // L["active"] == cfg.N // cfg.k
+
+
+# ---------------------------------------------------------------------------
+# Routing worked example (page 3, §3.6 and §04: seed 7 -> loads [8,7,8,9])
+# ---------------------------------------------------------------------------
+
+
+def test_seed7_routing_loads():
+    g = gold("routing_seed7.json")
+    torch.manual_seed(g["seed"])
+    x = torch.randn(g["T"], g["d"])
+    gate = torch.nn.Linear(g["d"], g["N"], bias=False)
+    r = O.route(x.double().numpy(), gate.weight.detach().double().numpy(), g["k"], "renorm")
+    assert list(r["idx"].shape) == g["idx_shape"]
+    loads = np.bincount(r["idx"].reshape(-1), minlength=g["N"]).tolist()
+    assert loads == g["loads"] and sum(loads) == g["T"] * g["k"]
+    # The fp32 selection of the page's code agrees (margins are large).
+    probs = F.softmax(gate(x).float(), dim=-1)
+    _, ti = probs.topk(g["k"], dim=-1)
+    assert np.array_equal(ti.numpy(), r["idx"])
+
+
+# ---------------------------------------------------------------------------
+# Softmax, top-k and gate weights against torch (page 3, §3.2)
+# ---------------------------------------------------------------------------
+
+
+def test_softmax_topk_against_torch():
+    rng = np.random.default_rng(0)
+    z = rng.normal(size=(200, 8)) * 3
+    p = O.softmax(z)
+    assert np.allclose(p, torch.softmax(torch.from_numpy(z), dim=1).numpy(), atol=1e-15, rtol=0)
+    for k in (1, 2, 3, 8):
+        idx = O.select_topk(p, k)
+        tv, ti = torch.topk(torch.from_numpy(p), k, dim=1)
+        assert np.array_equal(idx, ti.numpy())
+        a = O.gate_weights(p, idx, "renorm")
+        assert np.allclose(a.sum(1), 1.0, atol=1e-15)
+        assert np.allclose(a, (tv / tv.sum(1, keepdim=True)).numpy(), atol=1e-15)
+        assert np.allclose(O.gate_weights(p, idx, "prob"), tv.numpy(), atol=0)
+    # k = 1 renormalised weight is exactly 1; the Switch weight is max p.
+    idx1 = O.select_topk(p, 1)
+    assert np.all(O.gate_weights(p, idx1, "renorm") == 1.0)
+    assert np.allclose(O.gate_weights(p, idx1, "prob")[:, 0], p.max(1), atol=0)
+
+
+def test_topk_ties_go_to_lower_index_and_margin():
+    z = np.array([[1.0, 2.0, 2.0, 0.5], [3.0, 3.0, 3.0, 3.0]])
+    p = O.softmax(z)
+    assert O.select_topk(p, 2).tolist() == [[1, 2], [0, 1]]
+    m = O.topk_margin(z, 2)
+    assert m[0] == 1.0 and m[1] == 0.0
+    assert np.isinf(O.topk_margin(z, 4)).all()
+
+
+def test_router_logits_orientation():
+    # z = W_route u with W_route [N, d]: the same as torch's F.linear.
+    rng = np.random.default_rng(1)
+    u = rng.normal(size=(5, 7))
+    w = rng.normal(size=(3, 7))
+    ref = F.linear(torch.from_numpy(u), torch.from_numpy(w)).numpy()
+    assert np.allclose(O.router_logits(u, w), ref, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# Dispatch (page 3, §3.6 and the appendix's torch.where grouping)
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("T,N,k,cap", [(64, 4, 2, None), (300, 8, 2, 40), (100, 16, 4, 20),
+                                       (50, 8, 1, 3)])
+def test_dispatch_matches_torch_where_order(T, N, k, cap):
+    rng = np.random.default_rng(T + N)
+    idx = np.stack([rng.permutation(N)[:k] for _ in range(T)])
+    d = O.dispatch(idx, N, cap)
+    assert int(d["counts"].sum()) == k * T            # sum_i L_i = kT (§3.6)
+    ti = torch.from_numpy(idx)
+    for e in range(N):
+        tok, slot = torch.where(ti == e)
+        seg = d["perm"][d["offsets"][e]:d["offsets"][e + 1]]
+        assert np.array_equal(seg // k, tok.numpy())
+        assert np.array_equal(seg % k, slot.numpy())
+        kept = min(len(seg), cap) if cap is not None else len(seg)
+        assert np.array_equal(d["row_of"][seg[:kept]],
+                              d["kept_offsets"][e] + np.arange(kept))
+        assert np.all(d["row_of"][seg[kept:]] == -1)
+        assert np.all(d["drop"][seg[kept:]] == 1) and np.all(d["drop"][seg[:kept]] == 0)
+    if cap is not None:
+        assert d["overflow"] == int(np.maximum(d["counts"] - cap, 0).sum()) == int(d["drop"].sum())
+
+
+# ---------------------------------------------------------------------------
+# Expert and full layer (page 3, §3.1, §3.2; appendix dense reference)
+# ---------------------------------------------------------------------------
+
+
+def test_single_expert_is_torch_swiglu():
+    # N = 1, k = 1, renorm: the layer is one SwiGLU FFN.  Non-square shapes so
+    # a transposed operand cannot pass.
+    rng = np.random.default_rng(2)
+    T, d, h = 9, 12, 20
+    u = rng.normal(size=(T, d))
+    wg, wu = rng.normal(size=(h, d)) / 3, rng.normal(size=(h, d)) / 3
+    wd = rng.normal(size=(d, h)) / 4
+    out = O.forward(u, np.ones((1, d)), lambda e: (wg, wu, wd), k=1)
+    tu = torch.from_numpy(u)
+    ref = F.linear(F.silu(F.linear(tu, torch.from_numpy(wg))) * F.linear(tu, torch.from_numpy(wu)),
+                   torch.from_numpy(wd)).numpy()
+    assert np.allclose(out["y"], ref, atol=1e-13, rtol=0)
+    assert out["y"].shape == (T, d)                   # output width d (§3.6)
+
+
+def test_silu_against_torch():
+    x = np.linspace(-50, 50, 1001)
+    assert np.allclose(O.silu(x), F.silu(torch.from_numpy(x)).numpy(), atol=1e-15, rtol=1e-15)
+
+
+@pytest.mark.parametrize("cfg", [C.TINY, C.TINY.with_(k=1, gate="prob"),
+                                 C.TINY.with_(capacity_factor=0.6),
+                                 C.TINY_PLANTED, C.TINY_PLANTED.with_(capacity_factor=1.5)])
+def test_sparse_equals_dense_brute_force(cfg):
+    cap = (None if cfg.capacity_factor is None
+           else O.capacity_from_factor(cfg.T, cfg.N, cfg.k, cfg.capacity_factor))
+    u, wr = cfg.u(), cfg.w_route()
+    sp = O.forward(u, wr, tiny_experts(cfg), k=cfg.k, gate=cfg.gate, capacity=cap)
+    de = O.forward_dense(u, wr, tiny_experts(cfg), k=cfg.k, gate=cfg.gate, capacity=cap)
+    assert O.relative_error(sp["y"], de) <= 1e-13
+
+
+def test_k_equals_n_is_probability_weighted_dense_sum():
+    cfg = C.TINY.with_(k=4)
+    u, wr = cfg.u(), cfg.w_route()
+    out = O.forward(u, wr, tiny_experts(cfg), k=4)
+    p = O.softmax(O.expand(u) @ O.expand(wr).T)
+    ref = sum(p[:, [e]] * O.expert_forward(O.expand(u), *(O.expand(w) for w in cfg.expert(e)),
+                                           O.swiglu) for e in range(4))
+    assert O.relative_error(out["y"], ref) < 1e-13
+
+
+def test_planted_variant_end_to_end():
+    cfg = C.TINY_PLANTED
+    u, wr = cfg.u(), cfg.w_route()
+    for c, drops in ((1.0, 6), (1.5, 4), (2.5, 0)):
+        cap = O.capacity_from_factor(cfg.T, cfg.N, 1, c)
+        out = O.forward(u, wr, tiny_experts(cfg), k=1, gate="prob", capacity=cap)
+        assert out["idx"][:, 0].tolist() == C.PLANTED_ASSIGNMENT
+        assert out["disp"]["counts"].tolist() == [10, 3, 2, 1]
+        assert int(out["disp"]["drop"].sum()) == drops
+        dropped = np.nonzero(out["disp"]["drop"])[0]
+        assert np.all(out["y"][dropped] == 0.0)          # overflow skips the layer
+        assert out["margin"].min() > 7.0
+
+
+def test_unselected_expert_perturbation_leaves_y_identical():
+    cfg = C.TINY
+    u, wr = cfg.u(), cfg.w_route()
+    base = O.forward(u, wr, tiny_experts(cfg), k=2)
+    used = set(base["idx"].reshape(-1).tolist())
+    unused = [e for e in range(cfg.N) if e not in used]
+    # Route a single token so that some expert is certainly unselected.
+    u1 = u[:1]
+    b1 = O.forward(u1, wr, tiny_experts(cfg), k=2)
+    off = [e for e in range(cfg.N) if e not in b1["idx"][0]]
+    assert off
+
+    def big(e):
+        g, up, dn = cfg.expert(e)
+        if e in off:
+            return g * 1e3, up * 1e3, dn * 1e3
+        return g, up, dn
+
+    p1 = O.forward(u1, wr, big, k=2)
+    assert np.array_equal(p1["y"], b1["y"])
+    del unused
+
+
+# ---------------------------------------------------------------------------
+# LatentMoE pieces (page 5: width separation, RMSNorm, SiTU-GLU)
+# ---------------------------------------------------------------------------
+
+
+def test_rmsnorm_against_torch():
+    rng = np.random.default_rng(3)
+    r = rng.normal(size=(6, 33)) * 5
+    ref = F.rms_norm(torch.from_numpy(r), (33,), eps=1e-6).numpy()
+    assert np.allclose(O.rmsnorm(r, 1e-6), ref, atol=1e-14, rtol=0)
+
+
+def test_situ_glu_limits_and_bound():
+    rng = np.random.default_rng(4)
+    g, v = rng.normal(size=1000) * 3, rng.normal(size=1000) * 3
+    assert np.allclose(O.situ_glu(g, v, 1e9, 1e9), O.swiglu(g, v), rtol=1e-12, atol=1e-15)
+    big = np.concatenate([np.linspace(-1e6, 1e6, 2001), [np.inf, -np.inf]])
+    G, V = np.meshgrid(big, big)
+    a = O.situ_glu(G, V, 4.0, 25.0)
+    assert np.all(np.abs(a) <= 100.0)                 # beta_g * beta_u bound
+    assert np.abs(a).max() <= O.silu(np.array(4.0)) * 25.0 + 1e-12
+    # Small arguments: the caps are near-identity (tanh(x/b)*b ~ x).
+    s = np.array([1e-3, -2e-3])
+    assert np.allclose(O.situ_glu(s, s, 4.0, 25.0), O.swiglu(s, s), rtol=1e-6)
+
+
+SMALL_LATENT = C.LATENT.with_(name="latent_small", T=40, d=32, l=16, h=24, N=8, k=2,
+                              n_shared=2, h_shared=24, w_dtype="f32", act_dtype="f32",
+                              router_dtype="f32")
+
+
+def _latent(cfg, **kw):
+    return O.latent_forward(cfg.u(), cfg.w_route(), lambda e: cfg.expert(e), cfg.w_ldown(),
+                            cfg.w_lup(), lambda j: cfg.shared(j), cfg.n_shared, k=cfg.k,
+                            act=cfg.act, rms_eps=cfg.rms_eps, **kw)
+
+
+def test_latent_identity_projections_reduce_to_rmsnorm_of_plain():
+    cfg = C.TINY.with_(act="swiglu")
+    u, wr = cfg.u(), cfg.w_route()
+    plain = O.forward(u, wr, tiny_experts(cfg), k=cfg.k)["y"]
+    eye = np.eye(cfg.d)
+    lat = O.latent_forward(u, wr, tiny_experts(cfg), eye, eye, None, 0, k=cfg.k,
+                           act="swiglu", rms_eps=1e-6)["y"]
+    ref = F.rms_norm(torch.from_numpy(plain), (cfg.d,), eps=1e-6).numpy()
+    assert np.allclose(lat, ref, atol=1e-13)
+
+
+def test_latent_sparse_equals_dense_and_scale_invariance():
+    cfg = SMALL_LATENT
+    out = _latent(cfg)
+    # Dense brute force of the routed branch at width l.
+    u = O.expand(cfg.u())
+    xl = u @ O.expand(cfg.w_ldown()).T
+    r = out
+    rsum = np.zeros((cfg.T, cfg.l))
+    act = O.make_act("situ")
+    for e in range(cfg.N):
+        w = np.zeros(cfg.T)
+        for s in range(cfg.k):
+            w += (r["idx"][:, s] == e) * r["a"][:, s]
+        rsum += w[:, None] * O.expert_forward(xl, *(O.expand(x) for x in cfg.expert(e)), act)
+    assert O.relative_error(out["r"], rsum) < 1e-13
+    # Scaling every routed expert's down matrix leaves y unchanged (RMSNorm);
+    # the scale is taken in fp64 after expansion so the stored values stay exact.
+    def scaled_expert(e):
+        g, up, dn = cfg.expert(e)
+        return g, up, O.expand(dn) * 7.0
+
+    kw = dict(k=cfg.k, act="situ", rms_eps=0.0)
+    scaled = O.latent_forward(cfg.u(), cfg.w_route(), scaled_expert, cfg.w_ldown(), cfg.w_lup(),
+                              lambda j: cfg.shared(j), cfg.n_shared, **kw)
+    base0 = O.latent_forward(cfg.u(), cfg.w_route(), lambda e: cfg.expert(e), cfg.w_ldown(),
+                             cfg.w_lup(), lambda j: cfg.shared(j), cfg.n_shared, **kw)
+    assert O.relative_error(scaled["y"], base0["y"]) < 1e-13
+
+
+def test_latent_shared_experts_are_torch_swiglu():
+    # Zero routed down matrices: the routed branch is RMSNorm(0) = 0 and y is
+    # the sum of the shared SwiGLU experts.
+    cfg = SMALL_LATENT
+    out = O.latent_forward(cfg.u(), cfg.w_route(),
+                           lambda e: (cfg.expert(e)[0], cfg.expert(e)[1], 0 * cfg.expert(e)[2]),
+                           cfg.w_ldown(), cfg.w_lup(), lambda j: cfg.shared(j), cfg.n_shared,
+                           k=cfg.k, act="situ", rms_eps=1e-6)
+    tu = torch.from_numpy(O.expand(cfg.u()))
+    ref = 0
+    for j in range(cfg.n_shared):
+        g, up, dn = (torch.from_numpy(O.expand(w)) for w in cfg.shared(j))
+        ref = ref + F.linear(F.silu(F.linear(tu, g)) * F.linear(tu, up), dn)
+    assert np.allclose(out["y"], ref.numpy(), atol=1e-13)
+
+
+def test_latent_parameter_saving_closed_form():
+    g = gold("latent_saving.json")
+    s = O.latent_param_saving(g["d"], g["l"], g["H"], g["E"])
+    assert abs(s - g["saving_approx"]) < g["tolerance"]
+
+
+# ---------------------------------------------------------------------------
+# Stored-value expansion and bf16 rounding (page 2, §六: the fp16 subnormal
+# lesson -- every hand-written conversion is tested on its special cases)
+# ---------------------------------------------------------------------------
+
+
+def test_expand_bf16_matches_torch():
+    bits = np.arange(0, 1 << 16, dtype=np.uint32).astype(np.uint16)
+    ours = O.expand(bits)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).double().numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], ref[~nan])
+
+
+def _bf16_value(b):
+    return float(O.expand(np.array([b], dtype=np.uint16))[0])
+
+
+def test_bf16_rounding_brute_force():
+    rng = np.random.default_rng(5)
+    xs = np.concatenate([rng.normal(size=3000) * 10.0 ** rng.integers(-45, 39, 3000),
+                         [0.0, -0.0, 1e-45, 9.2e-41, 1.1754942e-38, 1.1754944e-38,
+                          3.3895e38, 3.3896e38, 3.4e38, 1e300, -1e-300]])
+    grid = O.expand(np.arange(0, 0x7F81, dtype=np.uint32).astype(np.uint16))  # +0 .. +Inf
+    grid[0x7F80] = 2.0 ** 128   # IEEE: overflow is decided as if the exponent were unbounded
+    for x in xs:
+        b = synth.f64_to_bf16_bits(x)
+        ax = abs(x)
+        j = np.searchsorted(grid, ax)
+        cands = [c for c in (j - 1, j) if 0 <= c < grid.size]
+        best = min(cands, key=lambda c: (abs(grid[c] - ax), c & 1))
+        expect = best | (0x8000 if math.copysign(1.0, x) < 0 else 0)
+        assert b == expect, (x, hex(b), hex(expect))
+    assert synth.f64_to_bf16_bits(float("inf")) == 0x7F80
+    assert synth.f64_to_bf16_bits(float("-inf")) == 0xFF80
+    assert math.isnan(_bf16_value(synth.f64_to_bf16_bits(float("nan"))))
+    # Exact ties: 1 + 2^-8 lies between 1 and 1 + 2^-7, goes to even (1.0).
+    assert synth.f64_to_bf16_bits(1.0 + 2 ** -8) == 0x3F80
+    assert synth.f64_to_bf16_bits(1.0 + 3 * 2 ** -8) == 0x3F82
+    # Smallest subnormal and its half (tie to even -> 0).
+    assert synth.f64_to_bf16_bits(2.0 ** -133) == 0x0001
+    assert synth.f64_to_bf16_bits(2.0 ** -134) == 0x0000
+    assert synth.f64_to_bf16_bits(3 * 2.0 ** -134) == 0x0002
+
+
+def test_round_matches_torch_on_fp32_exact_values():
+    # For values that are exact fp32 numbers torch's fp32->bf16 conversion is a
+    # single rounding, so it must agree with the direct rounding.
+    rng = np.random.default_rng(6)
+    x = rng.normal(size=100000).astype(np.float32).astype(np.float64)
+    ours = synth.round_to(x, "bf16")
+    ref = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy()
+    assert np.array_equal(ours.view(np.int16), ref)
