@@ -1,0 +1,184 @@
+"""MoE-layer forward benchmark on one MI355X.
+
+Default workload: the Mixtral-shape layer (d=4096, h=14336, N=8 experts,
+top-2 renormalised, bf16, T=16384 tokens).  Inputs and weights are seeded
+synthetic data already resident in HBM when the timed region starts.  One
+step is one whole moe_forward (route, dispatch, expert gate/up, expert down,
+combine).  Prints one JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/sec at 1 GPU; % bf16 MFMA peak (prefill), % HBM BW (decode)"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="mixtral_prefill_t16384")
+    p.add_argument("--decode-workload", default="mixtral_decode_t32",
+                   help="second workload reported beside the main one ('' to skip)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-tokens", type=int, default=384)
+    return p.parse_args()
+
+
+def algorithmic(cfg, counts_kept):
+    """Algorithmic work of one forward: expert FLOPs on kept rows, and the
+    bytes of the selected experts' weights (each touched expert read once)."""
+    R = int(sum(counts_kept))
+    xw = cfg.x_width
+    wb = 2 if cfg.w_dtype == "bf16" else 4
+    gu_flops = 2.0 * R * xw * 2 * cfg.h
+    down_flops = 2.0 * R * cfg.h * xw
+    touched = sum(1 for c in counts_kept if c > 0)
+    gu_bytes = touched * 2 * cfg.h * xw * wb
+    down_bytes = touched * cfg.h * xw * wb
+    return {"rows": R, "gu_flops": gu_flops, "down_flops": down_flops, "gu_bytes": gu_bytes,
+            "down_bytes": down_bytes, "touched": touched}
+
+
+def run_workload(cfg, steps, warmup):
+    import numpy as np
+    import torch
+
+    import sparse_mixture_experts_11_amd as moe
+    from tests import harness as H
+
+    desc = H.desc_for(cfg)
+    w = H.upload_layer(cfg)
+    u = H.to_device(cfg.u())
+    y = H.y_buffer(cfg)
+    out = H.out_buffers(cfg)
+    ws = moe.workspace(desc)
+    stages = moe.moe_stage_names(desc)
+    stream = torch.cuda.current_stream()
+
+    def mk():
+        return [torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+
+    for _ in range(warmup):
+        moe.moe_forward(desc, w, u, y, out, ws)
+    torch.cuda.synchronize()
+    ev = [mk() for _ in range(steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(steps):
+        moe.moe_forward_traced(desc, w, u, y, out, ws, ev[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    per_stage = {s: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(steps)]))
+                 for j, s in enumerate(stages)}
+    kept = np.diff(H.to_host(out["kept_offsets"]))
+    return {"ms_per_step": total_ms / steps, "stages_ms": per_stage,
+            "alg": algorithmic(cfg, kept), "desc": desc}
+
+
+def cpu_baseline(cfg, n_tokens):
+    """The fp64 oracle, as it stands, on the first n tokens of the workload."""
+    import numpy as np  # noqa: F401
+    from threadpoolctl import threadpool_info
+
+    import oracle as O
+
+    sub = cfg.with_(T=n_tokens)
+    cap = None if cfg.capacity_factor is None else O.capacity_from_factor(
+        sub.T, sub.N, sub.k, sub.capacity_factor)
+    u = sub.u()
+    wr = sub.w_route()
+    t0 = time.perf_counter()
+    O.forward(u, wr, lambda e: sub.expert(e), k=sub.k, gate=sub.gate, act=sub.act,
+              capacity=cap, beta_g=sub.beta_g, beta_u=sub.beta_u, alpha=sub.aux_alpha)
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"fp64 oracle forward of the first {n_tokens} of {cfg.T} tokens "
+                      f"(same weights; includes expanding the stored bf16 weights), {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py measures one GPU only (asked for {args.gpus}); this layer has no "
+              "multi-GPU path here", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from synth import configs as C
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    cfg = C.ALL[args.workload]
+    print(f"[bench] {cfg.name}: uploading weights", file=sys.stderr, flush=True)
+    r = run_workload(cfg, args.steps, args.warmup)
+    tok_s = cfg.T / (r["ms_per_step"] / 1e3)
+    alg = r["alg"]
+    total_flops = alg["gu_flops"] + alg["down_flops"]
+    decode_like = cfg.T <= 64
+    if decode_like:
+        t = r["stages_ms"]["expert_gate_up"] / 1e3
+        achieved = alg["gu_bytes"] / t / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS, "traffic": None,
+                "kernel": "decode_kernel<true> (expert gate/up)"}
+    else:
+        t = r["stages_ms"]["expert_gate_up"] / 1e3
+        achieved = alg["gu_flops"] / t / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                "kernel": "grouped_gemm_kernel<EP_GLU> (expert gate/up)"}
+    line = {
+        "metric": METRIC, "value": tok_s, "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": r["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if cfg.act_dtype == "bf16" else "f32", "data": "synthetic",
+        "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "h": cfg.h, "N": cfg.N,
+                   "k": cfg.k, "parallelism": "single GPU"},
+        "tflops": total_flops / (r["ms_per_step"] / 1e3) / 1e12,
+        "expert_gemm_frac_bf16_peak": total_flops / (
+            (r["stages_ms"]["expert_gate_up"] + r["stages_ms"]["expert_down"]) / 1e3) / 1e12
+            / PEAK_BF16_TFLOPS,
+        "stages_ms": r["stages_ms"],
+        "roofline": roof,
+    }
+    if args.decode_workload:
+        dc = C.ALL[args.decode_workload]
+        print(f"[bench] {dc.name}", file=sys.stderr, flush=True)
+        rd = run_workload(dc, args.steps, args.warmup)
+        a = rd["alg"]
+        wbytes = a["gu_bytes"] + a["down_bytes"]
+        line["decode"] = {
+            "workload": dc.name, "tokens_per_s": dc.T / (rd["ms_per_step"] / 1e3),
+            "ms_per_step": rd["ms_per_step"], "stages_ms": rd["stages_ms"],
+            "selected_expert_weight_bytes": wbytes,
+            "hbm_frac_whole_forward": wbytes / (rd["ms_per_step"] / 1e3) / 1e9 / PEAK_HBM_GBS,
+            "hbm_frac_expert_kernels": wbytes / ((rd["stages_ms"]["expert_gate_up"] +
+                                                  rd["stages_ms"]["expert_down"]) / 1e3)
+            / 1e9 / PEAK_HBM_GBS,
+        }
+        del rd
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(cfg, min(args.cpu_sample_tokens, cfg.T))
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

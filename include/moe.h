@@ -1,0 +1,205 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) sparse mixture-of-experts
+ * feed-forward layer, forward pass.
+ *
+ * The layer (page "MoE: how sparse activation saves compute", sections 3.1,
+ * 3.2, 3.5, 3.6):
+ *   z_t   = W_route u_t                      router scores, [T, N]
+ *   p_t   = softmax(z_t)                     fp32
+ *   S_t   = the k experts of largest p       descending p, ties -> lower index
+ *   a_t,i = p_t,i / sum_{j in S_t} p_t,j     (MOE_GATE_RENORM)
+ *         = p_t,i                            (MOE_GATE_PROB, Switch top-1 style)
+ *   dispatch: (token, slot) pairs grouped by expert in token order; with a
+ *   capacity C only the first C tokens reaching an expert are kept, the
+ *   others contribute 0 (their token skips the layer through the residual)
+ *   F_i(x) = W_down,i act(W_gate,i x, W_up,i x)
+ *   y_t   = sum over kept slots of a_t,i F_i(u_t)
+ * with act = SwiGLU, SiLU(g) * v, or SiTU-GLU, SiLU(bg tanh(g/bg)) * bu tanh(v/bu)
+ * (page "Stable LatentMoE interactive demo", SiTU-GLU passage).
+ *
+ * Latent variant (same page, width-separation and RMSNorm passages):
+ *   x_l = W_ldown u (d -> l); routing still reads u; experts map l -> h -> l;
+ *   r   = sum a E_i(x_l);  y = W_lup (r / sqrt(mean(r^2) + eps))
+ *         + sum_j SwiGLU_j(u) over n_shared shared experts of hidden h_shared.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *     never frees or keeps them.  Layouts are row-major and densely packed.
+ *   - bf16 tensors hold raw bfloat16 bit patterns (uint16).
+ *   - Calls are asynchronous on the given HIP stream (0 = the null stream),
+ *     allocate nothing and never synchronise the host with the device.
+ *   - Arguments are validated synchronously before any launch.  On error no
+ *     kernel is launched and a status other than MOE_OK is returned:
+ *       MOE_ERR_ARG          a null required pointer, an unset or out-of-range
+ *                            descriptor field (see moe_desc_init)
+ *       MOE_ERR_UNSUPPORTED  a valid layer these kernels do not implement
+ *                            (there is no fallback path)
+ *       MOE_ERR_WORKSPACE    ws is null or smaller than moe_workspace_bytes()
+ *       MOE_ERR_HIP          a launch failed (hipGetLastError after launch)
+ *   - No exceptions cross the ABI; the library holds no mutable global state,
+ *     so calls on different streams with different workspaces may overlap.
+ *     Results are bitwise deterministic (no floating-point atomics).
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t *moe_stream_t; /* a hipStream_t */
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_ARG = 1,
+  MOE_ERR_UNSUPPORTED = 2,
+  MOE_ERR_WORKSPACE = 3,
+  MOE_ERR_HIP = 4
+} moe_status_t;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
+
+/* Combine weight of a selected expert (page "MoE: how sparse activation
+   saves compute", section 3.2: Mixtral renormalises over S_t; Switch top-1
+   keeps the selected probability). */
+typedef enum { MOE_GATE_RENORM = 0, MOE_GATE_PROB = 1 } moe_gate_t;
+
+typedef enum { MOE_ACT_SWIGLU = 0, MOE_ACT_SITU_GLU = 1 } moe_act_t;
+
+/* Layer descriptor.  Every field must be set explicitly: moe_desc_init()
+   fills all of them with an "unset" sentinel and validation rejects any
+   field still holding it (a silently inherited default is a bug source). */
+typedef struct moe_desc {
+  int64_t T;          /* tokens, >= 1 */
+  int32_t d;          /* model width */
+  int32_t h;          /* routed-expert hidden width (H of the latent layer) */
+  int32_t N;          /* routed experts, 1..1024 */
+  int32_t k;          /* experts per token, 1..min(N, 32) */
+  int32_t capacity;   /* slots per expert C >= 0, or -1 for unlimited */
+  int32_t act_dtype;  /* moe_dtype_t of u, y and intermediate activations */
+  int32_t w_dtype;    /* moe_dtype_t of expert and projection weights */
+  int32_t router_dtype; /* moe_dtype_t of W_route */
+  int32_t gate;       /* moe_gate_t */
+  int32_t act;        /* moe_act_t of the routed experts */
+  float beta_g;       /* SiTU-GLU caps (> 0, finite); ignored by SwiGLU */
+  float beta_u;
+  int32_t l;          /* 0: plain layer; > 0: latent width */
+  int32_t n_shared;   /* latent: shared SwiGLU experts (>= 0); plain: 0 */
+  int32_t h_shared;   /* latent: shared-expert hidden width; plain: 0 */
+  float rms_eps;      /* latent: RMSNorm epsilon (>= 0); plain: any finite */
+  float aux_alpha;    /* alpha of the auxiliary balance term (finite) */
+} moe_desc_t;
+
+/* Device pointers of the layer's weights.
+   Plain layer: W_route [N, d]; W_gate, W_up [N, h, d]; W_down [N, d, h].
+   Latent layer: W_route [N, d]; W_gate, W_up [N, h, l]; W_down [N, l, h];
+   W_ldown [l, d]; W_lup [d, l]; Ws_gate, Ws_up [n_shared, h_shared, d];
+   Ws_down [n_shared, d, h_shared].  Unused pointers may be null.
+   Each expert's matrices are contiguous and experts follow one another, so
+   only the selected experts' bytes are ever read. */
+typedef struct moe_weights {
+  const void *W_route, *W_gate, *W_up, *W_down;
+  const void *W_ldown, *W_lup, *Ws_gate, *Ws_up, *Ws_down;
+} moe_weights_t;
+
+/* Optional outputs of moe_forward (device pointers; each may be null, the
+   workspace then holds the value).  Shapes as in moe_route/moe_dispatch. */
+typedef struct moe_outputs {
+  int32_t *topk_idx;
+  float *topk_w;
+  float *stats;
+  int32_t *counts, *offsets, *kept_offsets, *perm, *row_of;
+  uint8_t *drop;
+} moe_outputs_t;
+
+/* Sets every field of *desc to the "unset" sentinel. */
+void moe_desc_init(moe_desc_t *desc);
+
+const char *moe_status_string(moe_status_t s);
+
+/* Bytes of workspace any entry point below needs for this layer (the same
+   figure serves all of them).  *bytes receives 0 on error. */
+moe_status_t moe_workspace_bytes(const moe_desc_t *desc, size_t *bytes);
+
+/* Capacity C = ceil(c * k * T / N): with k slots per token capacity counts
+   k*T dispatches (section 3.5; at k = 1 this is ceil(c T / N)).
+   Returns -1 if T < 1, N < 1, k < 1 or c is not finite and positive. */
+int32_t moe_capacity_from_factor(int64_t T, int32_t N, int32_t k, double c);
+
+/* Router: scores, fp32 softmax, top-k and gate weights (section 3.2), plus
+   balance statistics (section 3.4).
+     u        [T, d] act_dtype (plain and latent layers both route on u)
+     W_route  [N, d] router_dtype
+     topk_idx [T, k] int32 out: experts of each token, by descending p
+     topk_w   [T, k] fp32 out: combine weights a
+     stats    [2N + 2] fp32 out, nullable: f_0..f_{N-1} (share of tokens whose
+              argmax is i, before capacity), P_0..P_{N-1} (mean p),
+              N sum f P, aux_alpha N sum f P. */
+moe_status_t moe_route(const moe_desc_t *desc, const void *u, const void *W_route,
+                       int32_t *topk_idx, float *topk_w, float *stats, void *ws,
+                       size_t ws_bytes, moe_stream_t stream);
+
+/* Dispatch: group the T*k (token, slot) entries e = t*k + s by expert in
+   token order (sections 3.5, 3.6, 3.8).
+     topk_idx     [T, k] int32 in (values in [0, N); a token names an expert once)
+     counts       [N]   int32 out: L_i, entries routed to expert i (before capacity)
+     offsets      [N+1] int32 out: exclusive prefix sum of L
+     kept_offsets [N+1] int32 out: exclusive prefix sum of min(L_i, C)
+     perm         [T*k] int32 out: entries sorted by (expert, token); the kept
+                  entries of expert i are perm[offsets[i] .. offsets[i] + min(L_i, C))
+     row_of       [T*k] int32 out, by entry: row kept_offsets[i] + rank of a kept
+                  entry, -1 for a dropped one
+     drop         [T*k] uint8 out, by entry: 1 if rank >= C */
+moe_status_t moe_dispatch(const moe_desc_t *desc, const int32_t *topk_idx, int32_t *counts,
+                          int32_t *offsets, int32_t *kept_offsets, int32_t *perm,
+                          int32_t *row_of, uint8_t *drop, void *ws, size_t ws_bytes,
+                          moe_stream_t stream);
+
+/* Routed experts (section 3.1): for every expert i and each of its kept
+   entries j (in perm order), y_perm[kept_offsets[i] + j] = F_i(x[token]).
+     x        [T, w] act_dtype, w = d (plain) or l (latent: x = W_ldown u)
+     W_gate, W_up [N, h, w]; W_down [N, w, h]  w_dtype
+     y_perm   [sum_i min(L_i, C), w] fp32 out (rows beyond the kept total untouched)
+   Only experts with at least one kept entry read their weights. */
+moe_status_t moe_expert_ffn(const moe_desc_t *desc, const void *x, const int32_t *perm,
+                            const int32_t *offsets, const int32_t *kept_offsets,
+                            const void *W_gate, const void *W_up, const void *W_down,
+                            float *y_perm, void *ws, size_t ws_bytes, moe_stream_t stream);
+
+/* Combine (section 3.2 eq. for y): y_t = sum_s [row_of[t*k+s] >= 0]
+   topk_w[t,s] * y_perm[row_of[t*k+s]] in fp32, rounded once to act_dtype.
+   Dropped slots add 0 and the other weights are not renormalised; a token
+   with every slot dropped gets y_t = 0.
+   Plain layer: y [T, d].  Latent layer: y [T, l] receives RMSNorm(r) (the
+   input of W_lup), r the weighted sum above. */
+moe_status_t moe_combine(const moe_desc_t *desc, const float *y_perm, const int32_t *row_of,
+                         const float *topk_w, void *y, moe_stream_t stream);
+
+/* Whole layer: route -> dispatch -> experts -> combine (and, for the latent
+   layer, the d->l projection, shared experts, RMSNorm and l->d projection).
+     u [T, d] act_dtype in; y [T, d] act_dtype out; out nullable. */
+moe_status_t moe_forward(const moe_desc_t *desc, const moe_weights_t *w, const void *u,
+                         void *y, const moe_outputs_t *out, void *ws, size_t ws_bytes,
+                         moe_stream_t stream);
+
+/* moe_forward that also records events[0..n_events) on the stream: events[0]
+   before the first kernel and events[i] after stage i, with the stages in
+   the order moe_stage_name(i) lists them (i = 1..).  Extra events are
+   recorded at the end; n_events may be smaller than the stage count.  The
+   events are hipEvent_t handles created by the caller. */
+moe_status_t moe_forward_traced(const moe_desc_t *desc, const moe_weights_t *w, const void *u,
+                                void *y, const moe_outputs_t *out, void *ws, size_t ws_bytes,
+                                moe_stream_t stream, void *const *events, int32_t n_events);
+
+/* Name of stage i (1-based) of moe_forward for this layer, or null past the
+   last stage; *n_stages (nullable) receives the stage count. */
+const char *moe_stage_name(const moe_desc_t *desc, int32_t i, int32_t *n_stages);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

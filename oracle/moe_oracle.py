@@ -290,6 +290,42 @@ def combine_routed(x: np.ndarray, r: Dict[str, np.ndarray], disp: Dict[str, np.n
     return y
 
 
+def combine_rows(y_rows: np.ndarray, row_of: np.ndarray, a: np.ndarray,
+                 rms_eps: Optional[float] = None) -> np.ndarray:
+    """The combine step on its own: y_t = sum over kept slots s of
+    a[t, s] * y_rows[row_of[t*k + s]] (rows of dropped slots are -1 and add
+    nothing).  With rms_eps, the latent layer's RMSNorm follows."""
+    T, k = a.shape
+    y = np.zeros((T, y_rows.shape[1]))
+    for t in range(T):
+        for s in range(k):
+            r = int(row_of[t * k + s])
+            if r >= 0:
+                y[t] += a[t, s] * y_rows[r]
+    return y if rms_eps is None else rmsnorm(y, rms_eps)
+
+
+def expert_rows(x: np.ndarray, disp: Dict[str, np.ndarray], experts: ExpertFn, act: Callable,
+                k: int, rows: Optional[np.ndarray] = None) -> Dict[int, np.ndarray]:
+    """F_e(x_t) for kept rows of the expert-sorted layout: row kept_offsets[e] + j
+    holds the output of the j-th kept entry of expert e.  Returns {row: vector}
+    for the requested rows (all kept rows when None)."""
+    N = len(disp["counts"])
+    want = None if rows is None else set(int(r) for r in rows)
+    out = {}
+    for e in range(N):
+        lo, kept = int(disp["kept_offsets"][e]), int(disp["kept_counts"][e])
+        js = [j for j in range(kept) if want is None or lo + j in want]
+        if not js:
+            continue
+        ent = disp["perm"][int(disp["offsets"][e]) + np.array(js)]
+        wg, wu, wd = _expert64(experts, e)
+        fe = expert_forward(x[ent // k], wg, wu, wd, act)
+        for i, j in enumerate(js):
+            out[lo + j] = fe[i]
+    return out
+
+
 def forward(u_st: np.ndarray, w_route_st: np.ndarray, experts: ExpertFn, *, k: int,
             gate: str = "renorm", act: str = "swiglu", capacity: Optional[int] = None,
             beta_g: float = 4.0, beta_u: float = 25.0, alpha: float = 0.01,

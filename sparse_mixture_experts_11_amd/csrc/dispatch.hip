@@ -1,0 +1,146 @@
+// Dispatch: group the T*k (token, slot) entries by expert in token order,
+// with per-expert capacity (page "MoE: how sparse activation saves compute",
+// sections 3.5, 3.6 and 3.8).
+//
+// Three launches, no host synchronisation, integer-only and deterministic:
+//   1. count: each block histograms one chunk of entries in LDS;
+//   2. scan:  one block turns the per-chunk histograms into per-chunk
+//             exclusive bases (chunk order = token order), L_i, offsets and
+//             kept offsets;
+//   3. rank:  one wave per chunk walks its entries 64 at a time; lanes that
+//             name the same expert find each other with ballots over the
+//             expert id bits, so each entry's rank is
+//             base[chunk][e] + (earlier lanes with e) -- a stable,
+//             token-order rank without atomics deciding any order.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+namespace {
+
+constexpr int kChunk = 1024;  // entries per chunk
+constexpr int kMaxN = 1024;
+
+__global__ __launch_bounds__(256) void dispatch_count_kernel(const int32_t *__restrict__ idx,
+                                                             int64_t E, int N,
+                                                             int32_t *__restrict__ blk_counts) {
+  __shared__ int32_t hist[kMaxN];
+  for (int n = threadIdx.x; n < N; n += blockDim.x) hist[n] = 0;
+  __syncthreads();
+  const int64_t lo = (int64_t)blockIdx.x * kChunk;
+  const int64_t hi = lo + kChunk < E ? lo + kChunk : E;
+  for (int64_t j = lo + threadIdx.x; j < hi; j += blockDim.x) {
+    const int e = idx[j];
+    if (e >= 0 && e < N) atomicAdd(&hist[e], 1);  // integer: order-free
+  }
+  __syncthreads();
+  for (int n = threadIdx.x; n < N; n += blockDim.x)
+    blk_counts[(int64_t)blockIdx.x * N + n] = hist[n];
+}
+
+// Inclusive block scan of one value per thread (blockDim.x == 1024).
+__device__ int block_incl_scan(int v, int *tmp) {
+  tmp[threadIdx.x] = v;
+  __syncthreads();
+  for (int o = 1; o < (int)blockDim.x; o <<= 1) {
+    const int add = (int)threadIdx.x >= o ? tmp[threadIdx.x - o] : 0;
+    __syncthreads();
+    tmp[threadIdx.x] += add;
+    __syncthreads();
+  }
+  const int r = tmp[threadIdx.x];
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(1024) void dispatch_scan_kernel(
+    int32_t *__restrict__ blk_counts, int nblk, int N, int capacity, int32_t *__restrict__ counts,
+    int32_t *__restrict__ offsets, int32_t *__restrict__ kept_offsets) {
+  __shared__ int tmp[1024];
+  const int n = threadIdx.x;  // N <= 1024: one expert per thread
+  int total = 0;
+  if (n < N) {
+    for (int b = 0; b < nblk; ++b) {
+      const int c = blk_counts[(int64_t)b * N + n];
+      blk_counts[(int64_t)b * N + n] = total;  // becomes the chunk's base
+      total += c;
+    }
+    counts[n] = total;
+  }
+  const int kept = (n < N) ? ((capacity >= 0 && total > capacity) ? capacity : total) : 0;
+  const int inc_all = block_incl_scan(n < N ? total : 0, tmp);
+  const int inc_kept = block_incl_scan(kept, tmp);
+  if (n < N) {
+    offsets[n + 1] = inc_all;
+    kept_offsets[n + 1] = inc_kept;
+  }
+  if (n == 0) {
+    offsets[0] = 0;
+    kept_offsets[0] = 0;
+  }
+}
+
+__global__ __launch_bounds__(64) void dispatch_rank_kernel(
+    const int32_t *__restrict__ idx, int64_t E, int N, int nbits, int capacity,
+    const int32_t *__restrict__ blk_counts, const int32_t *__restrict__ offsets,
+    const int32_t *__restrict__ kept_offsets, int32_t *__restrict__ perm,
+    int32_t *__restrict__ row_of, uint8_t *__restrict__ drop) {
+  __shared__ int32_t base[kMaxN];
+  const int lane = threadIdx.x;
+  for (int n = lane; n < N; n += 64) base[n] = blk_counts[(int64_t)blockIdx.x * N + n];
+  __syncthreads();
+  const int64_t lo = (int64_t)blockIdx.x * kChunk;
+  const int64_t hi = lo + kChunk < E ? lo + kChunk : E;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int64_t j0 = lo; j0 < hi; j0 += 64) {
+    const int64_t j = j0 + lane;
+    int e = (j < hi) ? idx[j] : -1;
+    const bool ok = e >= 0 && e < N;
+    if (!ok) e = -1;
+    uint64_t same = __ballot(ok);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = ok && ((e >> b) & 1);
+      const uint64_t ones = __ballot(bit);
+      same &= bit ? ones : ~ones;
+    }
+    int r = 0;
+    if (ok) r = base[e] + __popcll(same & below);
+    __syncthreads();  // every lane has read base[] before it moves on
+    if (ok && (63 - __clzll(same)) == lane) base[e] += __popcll(same);
+    __syncthreads();
+    if (j < hi) {
+      if (ok) {
+        perm[offsets[e] + r] = (int32_t)j;
+        const bool kept = capacity < 0 || r < capacity;
+        row_of[j] = kept ? kept_offsets[e] + r : -1;
+        drop[j] = kept ? 0 : 1;
+      } else {
+        row_of[j] = -1;
+        drop[j] = 1;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+int dispatch_blocks(int64_t entries) { return (int)((entries + kChunk - 1) / kChunk); }
+
+hipError_t launch_dispatch(const int32_t *idx, int64_t T, int k, int N, int capacity,
+                           int32_t *counts, int32_t *offsets, int32_t *kept_offsets,
+                           int32_t *perm, int32_t *row_of, uint8_t *drop,
+                           int32_t *blk_counts, hipStream_t st) {
+  const int64_t E = T * k;
+  const int nblk = dispatch_blocks(E);
+  int nbits = 0;
+  while ((1 << nbits) < N) ++nbits;
+  hipLaunchKernelGGL(dispatch_count_kernel, dim3(nblk), dim3(256), 0, st, idx, E, N, blk_counts);
+  hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(1024), 0, st, blk_counts, nblk, N,
+                     capacity, counts, offsets, kept_offsets);
+  hipLaunchKernelGGL(dispatch_rank_kernel, dim3(nblk), dim3(64), 0, st, idx, E, N, nbits,
+                     capacity, blk_counts, offsets, kept_offsets, perm, row_of, drop);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,302 @@
+// Grouped GEMM on bf16 MFMA for the expert projections (page "MoE: how
+// sparse activation saves compute", section 3.1: F(u) = W_down act(W_gate u,
+// W_up u); section 3.6: expert i works on its own [L_i, d] block of rows).
+//
+//   C_g[r, n] = sum_k A[arow(g, r), k] * B_g[n, k]      (both operands K-contiguous)
+//
+// One 256x256 output tile per 256-thread workgroup (4 waves of 128x128 on
+// v_mfma_f32_32x32x16_bf16), K in steps of 64 staged through a double-buffered,
+// XOR-swizzled LDS tile (2 x 64 KiB).  A rows are gathered through the
+// dispatch permutation inside the loader, so the expert-sorted copy of the
+// activations is never written.  Tiles are found on the device from the
+// per-group m-tile prefix; surplus workgroups exit, so no host sync is needed.
+//
+// Epilogues: EP_GLU pairs 128 gate columns with the matching 128 up columns in
+// one tile and writes act(gate, up) as bf16 (the hidden of a SwiGLU or
+// SiTU-GLU expert); EP_F32 / EP_BF16 store the product; EP_ADD_BF16 adds two
+// fp32 matrices before rounding (the latent layer's shared-expert outputs).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+namespace {
+
+constexpr int BM = 256;
+constexpr int BN = 256;
+constexpr int BK = 64;
+constexpr int kThreads = 256;
+constexpr int kStageBytes = (BM + BN) * BK * 2;  // 64 KiB
+constexpr int kMSuper = 8;                       // m-tiles per scheduling group
+
+// Byte offset of 16-byte chunk c of row r inside one [256][64] bf16 tile.
+__device__ __forceinline__ uint32_t swz(int r, int c) {
+  return (uint32_t)(r * 128 + ((c ^ (r & 7)) << 4));
+}
+
+__device__ __forceinline__ bf16x8 lds_frag(const char *tile, int r, int c) {
+  return *reinterpret_cast<const bf16x8 *>(tile + swz(r, c));
+}
+
+template <int EPI>
+__global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[2 * kStageBytes];
+
+  // ---- which tile: XCD-aware remap (block i runs on XCD i % 8), then
+  // (group, m-super, n, m) order so concurrent tiles on one XCD share rows.
+  const int64_t nb = gridDim.x;
+  const int64_t bid = blockIdx.x;
+  const int64_t L = (bid & 7) * (nb >> 3) + (bid >> 3);
+  const int glu = (EPI == EP_GLU);
+  const int64_t NT = glu ? (a.ncols + 127) / 128 : (a.ncols + BN - 1) / BN;
+
+  int g;
+  int64_t local, MTg, Mg;
+  if (a.mode == GM_DENSE) {
+    const int64_t MT = (a.M_dense + BM - 1) / BM;
+    g = (int)(L / (MT * NT));
+    if (g >= a.G) return;
+    local = L - (int64_t)g * MT * NT;
+    MTg = MT;
+    Mg = a.M_dense;
+  } else {
+    const int64_t total = (int64_t)a.tile_start[a.G] * NT;
+    if (L >= total) return;
+    int lo = 0, hi = a.G;  // largest g with tile_start[g] * NT <= L
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if ((int64_t)a.tile_start[mid] * NT <= L) lo = mid; else hi = mid;
+    }
+    g = lo;
+    local = L - (int64_t)a.tile_start[g] * NT;
+    MTg = a.tile_start[g + 1] - a.tile_start[g];
+    Mg = a.kept_offsets[g + 1] - a.kept_offsets[g];
+  }
+  const int64_t ms = local / (kMSuper * NT);
+  const int64_t rem = local - ms * kMSuper * NT;
+  const int64_t msz = (MTg - ms * kMSuper) < kMSuper ? (MTg - ms * kMSuper) : kMSuper;
+  const int64_t n_tile = rem / msz;
+  const int64_t m_tile = ms * kMSuper + (rem - n_tile * msz);
+  const int64_t m0 = m_tile * BM;
+  const int mrows = (int)((Mg - m0) < BM ? (Mg - m0) : BM);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lc = tid & 7;    // loader chunk
+  const int lr = tid >> 3;   // loader base row (0..31)
+
+  // ---- loader offsets (bytes), fixed over the K loop.
+  const int64_t seg0 = (a.mode == GM_DENSE) ? 0 : a.kept_offsets[g];
+  uint32_t aoff[8], boff[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = lr + 32 * i;
+    const int64_t rr = m0 + (r < mrows ? r : mrows - 1);
+    int64_t arow;
+    if (a.mode == GM_GATHER) arow = a.perm[a.offsets[g] + rr] / a.kslots;
+    else if (a.mode == GM_SEGMENT) arow = seg0 + rr;
+    else arow = (int64_t)g * a.a_group_rows + rr;
+    aoff[i] = (uint32_t)(arow * a.lda * 2) + (uint32_t)(lc << 4);
+    int64_t brow;
+    if (glu) {
+      const int64_t n = n_tile * 128 + (r & 127);
+      brow = n < a.ncols ? n : a.ncols - 1;
+    } else {
+      const int64_t n = n_tile * BN + r;
+      brow = n < a.ncols ? n : a.ncols - 1;
+    }
+    boff[i] = (uint32_t)(brow * a.K * 2) + (uint32_t)(lc << 4);
+  }
+  const uint16_t *Bg = a.B + (int64_t)g * a.strideB;
+  const uint16_t *Ug = glu ? a.B2 + (int64_t)g * a.strideB : Bg;
+  const uint32_t bbytes = (uint32_t)((int64_t)a.ncols * a.K * 2);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.A, 0xFFFFFFFFu);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bg, bbytes);
+  const __amdgpu_buffer_rsrc_t ru = make_rsrc(Ug, bbytes);
+
+  u32x4 ga[8], gb[8];
+  auto gload = [&](int k0) {
+    const uint32_t so = (uint32_t)k0 * 2;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ga[i] = buf_load16(ra, aoff[i], so);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) gb[i] = buf_load16((glu && i >= 4) ? ru : rb, boff[i], so);
+  };
+  auto lstore = [&](int stage) {
+    char *ta = smem + stage * kStageBytes;
+    char *tb = ta + BM * BK * 2;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4 *>(ta + swz(lr + 32 * i, lc)) = ga[i];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4 *>(tb + swz(lr + 32 * i, lc)) = gb[i];
+  };
+
+  // Per-wave fragment rows.
+  int arow_l[4], brow_l[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    arow_l[i] = wm * 128 + i * 32 + (lane & 31);
+    brow_l[i] = glu ? (wn * 64 + (i & 1) * 32 + (i >> 1) * 128 + (lane & 31))
+                    : (wn * 128 + i * 32 + (lane & 31));
+  }
+  const int khalf = lane >> 5;
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int KT = a.K / BK;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < KT; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < KT) gload((kt + 1) * BK);
+    const char *ta = smem + cur * kStageBytes;
+    const char *tb = ta + BM * BK * 2;
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      const int c = ks * 2 + khalf;
+      bf16x8 fa[4], fb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) fa[i] = lds_frag(ta, arow_l[i], c);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) fb[j] = lds_frag(tb, brow_l[j], c);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < KT) lstore(cur ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue.  Lane holds, for A block i and B block j, output row
+  // wm*128 + i*32 + lane%32 and columns 8q + 4*(lane/32) + {0..3}, q = 0..3.
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = wm * 128 + i * 32 + (lane & 31);
+    if (r >= mrows) continue;
+    const int64_t orow = (a.mode == GM_DENSE) ? (int64_t)g * a.out_group_stride + m0 + r
+                                              : seg0 + m0 + r;
+    if constexpr (EPI == EP_GLU) {
+#pragma unroll
+      for (int jp = 0; jp < 2; ++jp) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t col = n_tile * 128 + wn * 64 + jp * 32 + 8 * q + 4 * khalf;
+          if (col >= a.ncols) continue;
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            v[e] = glu_act(acc[i][jp][4 * q + e], acc[i][jp + 2][4 * q + e], a.act, a.beta_g,
+                           a.beta_u);
+          uint2 pk;
+          pk.x = pack_bf16x2(v[0], v[1]);
+          pk.y = pack_bf16x2(v[2], v[3]);
+          *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(a.out) + orow * a.ldo + col) = pk;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t col = n_tile * BN + wn * 128 + j * 32 + 8 * q + 4 * khalf;
+          if (col >= a.ncols) continue;
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e];
+          if constexpr (EPI == EP_F32) {
+            *reinterpret_cast<float4 *>(reinterpret_cast<float *>(a.out) + orow * a.ldo + col) =
+                make_float4(v[0], v[1], v[2], v[3]);
+          } else {
+            if constexpr (EPI == EP_ADD_BF16) {
+              const float4 p0 = *reinterpret_cast<const float4 *>(a.add0 + orow * a.ldo + col);
+              v[0] += p0.x; v[1] += p0.y; v[2] += p0.z; v[3] += p0.w;
+              if (a.add1 != nullptr) {
+                const float4 p1 = *reinterpret_cast<const float4 *>(a.add1 + orow * a.ldo + col);
+                v[0] += p1.x; v[1] += p1.y; v[2] += p1.z; v[3] += p1.w;
+              }
+            }
+            uint2 pk;
+            pk.x = pack_bf16x2(v[0], v[1]);
+            pk.y = pack_bf16x2(v[2], v[3]);
+            *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(a.out) + orow * a.ldo + col) =
+                pk;
+          }
+        }
+      }
+    }
+  }
+}
+
+// tile_start[g] = sum_{g' < g} ceil(M_g' / BM), M_g = kept rows of group g.
+__global__ __launch_bounds__(1024) void tile_prefix_kernel(const int32_t *__restrict__ kept_offsets,
+                                                           int G, int32_t *__restrict__ tile_start) {
+  __shared__ int tmp[1024];
+  int run = 0;  // carried across rounds of 1024 groups
+  for (int base = 0; base < G; base += 1024) {
+    const int g = base + threadIdx.x;
+    const int m = (g < G) ? kept_offsets[g + 1] - kept_offsets[g] : 0;
+    tmp[threadIdx.x] = (m + BM - 1) / BM;
+    __syncthreads();
+    for (int o = 1; o < 1024; o <<= 1) {
+      const int add = (int)threadIdx.x >= o ? tmp[threadIdx.x - o] : 0;
+      __syncthreads();
+      tmp[threadIdx.x] += add;
+      __syncthreads();
+    }
+    if (g < G) tile_start[g + 1] = run + tmp[threadIdx.x];
+    run += tmp[1023];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) tile_start[0] = 0;
+}
+
+}  // namespace
+
+int gemm_bm() { return BM; }
+
+int64_t gemm_mtile_bound(int64_t rows_total, int groups) {
+  return (rows_total + BM - 1) / BM + groups;
+}
+
+hipError_t launch_tile_prefix(const int32_t *kept_offsets, int G, int32_t *tile_start,
+                              hipStream_t st) {
+  hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, st, kept_offsets, G, tile_start);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm(const GemmArgs &a, int epi, int64_t mtiles_bound, hipStream_t st) {
+  const int64_t NT = (epi == EP_GLU) ? (a.ncols + 127) / 128 : (a.ncols + BN - 1) / BN;
+  int64_t tiles;
+  if (a.mode == GM_DENSE) tiles = (int64_t)a.G * ((a.M_dense + BM - 1) / BM) * NT;
+  else tiles = mtiles_bound * NT;
+  const int64_t grid = (tiles + 7) / 8 * 8;
+  if (grid == 0) return hipSuccess;
+  switch (epi) {
+    case EP_GLU:
+      hipLaunchKernelGGL(grouped_gemm_kernel<EP_GLU>, dim3(grid), dim3(kThreads), 0, st, a);
+      break;
+    case EP_F32:
+      hipLaunchKernelGGL(grouped_gemm_kernel<EP_F32>, dim3(grid), dim3(kThreads), 0, st, a);
+      break;
+    case EP_BF16:
+      hipLaunchKernelGGL(grouped_gemm_kernel<EP_BF16>, dim3(grid), dim3(kThreads), 0, st, a);
+      break;
+    default:
+      hipLaunchKernelGGL(grouped_gemm_kernel<EP_ADD_BF16>, dim3(grid), dim3(kThreads), 0, st, a);
+      break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,92 @@
+// Internal launch interface between the C ABI (moe_api.hip) and the kernels.
+// Every launcher enqueues on `st` and returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---- router (route.hip) ----------------------------------------------------
+// Waves the router kernels launch for T tokens (sizes the stats partials).
+int route_waves(int64_t T, int N);
+// Wave-per-token-group router for N <= 64: scores, softmax, top-k, weights.
+hipError_t launch_route_wave(const void *u, bool u_bf16, const void *W, bool w_bf16, int64_t T,
+                             int d, int N, int k, int gate, int32_t *idx, float *w,
+                             float *part_p, int32_t *part_cnt, hipStream_t st);
+// Softmax + top-k from materialised fp32 logits [T, N] (N <= 1024).
+hipError_t launch_topk_logits(const float *logits, int64_t T, int N, int k, int gate,
+                              int32_t *idx, float *w, float *part_p, int32_t *part_cnt,
+                              hipStream_t st);
+// f, P, N sum fP, alpha N sum fP from the per-wave partials.
+hipError_t launch_stats_finalize(const float *part_p, const int32_t *part_cnt, int waves,
+                                 int64_t T, int N, float alpha, float *stats, hipStream_t st);
+
+// ---- dispatch (dispatch.hip) ----------------------------------------------
+int dispatch_blocks(int64_t entries);
+hipError_t launch_dispatch(const int32_t *idx, int64_t T, int k, int N, int capacity,
+                           int32_t *counts, int32_t *offsets, int32_t *kept_offsets,
+                           int32_t *perm, int32_t *row_of, uint8_t *drop,
+                           int32_t *blk_counts, hipStream_t st);
+
+// ---- grouped GEMM on bf16 MFMA (gemm.hip) -----------------------------------
+enum GemmMode { GM_GATHER = 0, GM_SEGMENT = 1, GM_DENSE = 2 };
+enum GemmEpi { EP_GLU = 0, EP_F32 = 1, EP_BF16 = 2, EP_ADD_BF16 = 3 };
+
+struct GemmArgs {
+  // A: rows of K bf16 values, row stride lda (elements).
+  const uint16_t *A;
+  int64_t lda;
+  // B: per group, rows of K values (K-contiguous); B2 holds the "up" rows
+  // of a GLU pair (same layout as B).  Group g starts at g * strideB.
+  const uint16_t *B;
+  const uint16_t *B2;
+  int64_t strideB;
+  int K;
+  int ncols;        // output columns per group (h for GLU)
+  int mode;         // GemmMode
+  int G;            // groups
+  int64_t M_dense;  // rows per group in GM_DENSE
+  int64_t a_group_rows;  // GM_DENSE: A row offset between groups (0: shared A)
+  int kslots;       // k, to turn perm entries into token rows (GM_GATHER)
+  const int32_t *perm, *offsets, *kept_offsets;
+  const int32_t *tile_start;  // [G+1] m-tile prefix (GM_GATHER / GM_SEGMENT)
+  void *out;
+  int64_t ldo;
+  int64_t out_group_stride;   // GM_DENSE: rows of output per group
+  const float *add0, *add1;   // EP_ADD_BF16: out = acc + add0 + add1 (fp32, ldo)
+  int act;                    // 0 SwiGLU, 1 SiTU-GLU
+  float beta_g, beta_u;
+};
+// Upper bound of m-tiles (host side, no device sync).
+int64_t gemm_mtile_bound(int64_t rows_total, int groups);
+int gemm_bm();
+hipError_t launch_tile_prefix(const int32_t *kept_offsets, int G, int32_t *tile_start,
+                              hipStream_t st);
+hipError_t launch_gemm(const GemmArgs &a, int epi, int64_t mtiles_bound, hipStream_t st);
+
+// ---- decode-sized experts (decode.hip) -------------------------------------
+// Max rows per expert the decode kernels take.
+constexpr int kDecodeMaxRows = 64;
+hipError_t launch_decode_gu(const uint16_t *x, int64_t T, int w, const int32_t *perm,
+                            const int32_t *offsets, const int32_t *kept_offsets, int kslots,
+                            const uint16_t *Wg, const uint16_t *Wu, int h, int N, int act,
+                            float bg, float bu, uint16_t *hid, hipStream_t st);
+hipError_t launch_decode_down(const uint16_t *hid, int64_t T, const int32_t *kept_offsets,
+                              const uint16_t *Wd, int h, int w, int N, float *y_perm,
+                              hipStream_t st);
+
+// ---- fp32 SIMT experts (simt.hip) ------------------------------------------
+hipError_t launch_simt_gu(const float *x, const int32_t *perm, const int32_t *offsets,
+                          const int32_t *kept_offsets, int kslots, const float *Wg,
+                          const float *Wu, int w, int h, int N, int act, float bg, float bu,
+                          float *hid, hipStream_t st);
+hipError_t launch_simt_down(const float *hid, const int32_t *kept_offsets, const float *Wd,
+                            int h, int w, int N, float *y_perm, hipStream_t st);
+
+// ---- combine (combine.hip) ---------------------------------------------------
+hipError_t launch_combine(const float *y_perm, const int32_t *row_of, const float *topk_w,
+                          int64_t T, int k, int width, bool out_bf16, bool rmsnorm,
+                          float eps, void *y, hipStream_t st);
+
+}  // namespace moe

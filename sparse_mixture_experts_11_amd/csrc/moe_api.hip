@@ -1,0 +1,530 @@
+// C ABI of the MoE layer: descriptor validation, workspace layout and the
+// stage sequence.  Every call validates first (no launch on error), then
+// enqueues kernels on the caller's stream and returns without synchronising.
+#include <math.h>
+#include <string.h>
+
+#include "../../include/moe.h"
+#include "kernels.hpp"
+
+using namespace moe;
+
+namespace {
+
+constexpr int32_t kUnsetI32 = INT32_MIN;
+constexpr int64_t kUnsetI64 = INT64_MIN;
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxK = 32;
+constexpr int kRouteWaveMaxN = 64;
+constexpr uint64_t k4G = 1ull << 32;
+
+bool unset_f(float x) { return isnan(x); }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Byte regions of the workspace.  Offsets are relative to ws; a size of 0
+// means the region is not used by this layer.
+struct Layout {
+  size_t idx, w, stats, part_p, part_cnt, logits;
+  size_t counts, offsets, kept_offsets, perm, row_of, drop, blk_counts, tile_start;
+  size_t x_l, hid, y_perm, rn, hs, ys;
+  size_t total;
+};
+
+int64_t kept_rows_bound(const moe_desc_t &d) {
+  const int64_t E = d.T * d.k;
+  if (d.capacity >= 0) {
+    const int64_t cap = (int64_t)d.capacity * d.N;
+    return cap < E ? cap : E;
+  }
+  return E;
+}
+
+bool is_latent(const moe_desc_t &d) { return d.l > 0; }
+int xwidth(const moe_desc_t &d) { return is_latent(d) ? d.l : d.d; }
+bool bf16_path(const moe_desc_t &d) { return d.act_dtype == MOE_BF16; }
+bool decode_path(const moe_desc_t &d) { return bf16_path(d) && d.T <= kDecodeMaxRows; }
+bool router_gemm(const moe_desc_t &d) { return d.N > kRouteWaveMaxN; }
+
+Layout layout(const moe_desc_t &d) {
+  Layout L;
+  memset(&L, 0, sizeof(L));
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align256(bytes);
+    return o;
+  };
+  const int64_t E = d.T * d.k;
+  const int64_t R = kept_rows_bound(d);
+  const size_t act = bf16_path(d) ? 2 : 4;
+  const int waves = route_waves(d.T, d.N);
+  L.idx = take(E * 4);
+  L.w = take(E * 4);
+  L.stats = take((2 * (size_t)d.N + 2) * 4);
+  L.part_p = take((size_t)waves * d.N * 4);
+  L.part_cnt = take((size_t)waves * d.N * 4);
+  L.logits = router_gemm(d) ? take((size_t)d.T * d.N * 4) : 0;
+  L.counts = take((size_t)d.N * 4);
+  L.offsets = take(((size_t)d.N + 1) * 4);
+  L.kept_offsets = take(((size_t)d.N + 1) * 4);
+  L.perm = take(E * 4);
+  L.row_of = take(E * 4);
+  L.drop = take(E);
+  L.blk_counts = take((size_t)dispatch_blocks(E) * d.N * 4);
+  L.tile_start = take(((size_t)d.N + 1) * 4);
+  if (is_latent(d)) L.x_l = take((size_t)d.T * d.l * 2);
+  L.hid = take((size_t)R * d.h * act);
+  L.y_perm = take((size_t)R * xwidth(d) * 4);
+  if (is_latent(d)) {
+    L.rn = take((size_t)d.T * d.l * 2);
+    if (d.n_shared > 0) {
+      L.hs = take((size_t)d.n_shared * d.T * d.h_shared * 2);
+      L.ys = take((size_t)d.n_shared * d.T * d.d * 4);
+    }
+  }
+  L.total = off;
+  return L;
+}
+
+moe_status_t validate(const moe_desc_t *dp) {
+  if (dp == nullptr) return MOE_ERR_ARG;
+  const moe_desc_t &d = *dp;
+  // Every field must have been set.
+  if (d.T == kUnsetI64 || d.d == kUnsetI32 || d.h == kUnsetI32 || d.N == kUnsetI32 ||
+      d.k == kUnsetI32 || d.capacity == kUnsetI32 || d.act_dtype == kUnsetI32 ||
+      d.w_dtype == kUnsetI32 || d.router_dtype == kUnsetI32 || d.gate == kUnsetI32 ||
+      d.act == kUnsetI32 || unset_f(d.beta_g) || unset_f(d.beta_u) || d.l == kUnsetI32 ||
+      d.n_shared == kUnsetI32 || d.h_shared == kUnsetI32 || unset_f(d.rms_eps) ||
+      unset_f(d.aux_alpha))
+    return MOE_ERR_ARG;
+  // Ranges.
+  if (d.T < 1 || d.d < 1 || d.h < 1 || d.N < 1 || d.N > kMaxExperts || d.k < 1 || d.k > d.N ||
+      d.k > kMaxK || d.capacity < -1)
+    return MOE_ERR_ARG;
+  if ((d.act_dtype != MOE_F32 && d.act_dtype != MOE_BF16) ||
+      (d.w_dtype != MOE_F32 && d.w_dtype != MOE_BF16) ||
+      (d.router_dtype != MOE_F32 && d.router_dtype != MOE_BF16))
+    return MOE_ERR_ARG;
+  if ((d.gate != MOE_GATE_RENORM && d.gate != MOE_GATE_PROB) ||
+      (d.act != MOE_ACT_SWIGLU && d.act != MOE_ACT_SITU_GLU))
+    return MOE_ERR_ARG;
+  if (!isfinite(d.beta_g) || !isfinite(d.beta_u) || !isfinite(d.rms_eps) ||
+      !isfinite(d.aux_alpha) || d.rms_eps < 0.f)
+    return MOE_ERR_ARG;
+  if (d.act == MOE_ACT_SITU_GLU && (d.beta_g <= 0.f || d.beta_u <= 0.f)) return MOE_ERR_ARG;
+  if (d.l < 0 || d.n_shared < 0 || d.h_shared < 0) return MOE_ERR_ARG;
+  if (d.l == 0 && (d.n_shared != 0 || d.h_shared != 0)) return MOE_ERR_ARG;
+  if (d.n_shared > 0 && d.h_shared < 1) return MOE_ERR_ARG;
+  if (d.T * (int64_t)d.k > (int64_t)INT32_MAX) return MOE_ERR_UNSUPPORTED;
+
+  // What the kernels implement (no fallback path).
+  if (d.act_dtype != d.w_dtype) return MOE_ERR_UNSUPPORTED;
+  if (d.d % 8 != 0) return MOE_ERR_UNSUPPORTED;
+  if (d.act_dtype == MOE_F32) {
+    if (d.router_dtype != MOE_F32 || d.l != 0 || router_gemm(d)) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+  }
+  if (router_gemm(d) && (d.router_dtype != MOE_BF16 || d.d % 64 != 0)) return MOE_ERR_UNSUPPORTED;
+  if (d.d % 128 != 0 || d.h % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  const int64_t R = kept_rows_bound(d);
+  if (is_latent(d)) {
+    if (d.l % 128 != 0 || d.l > 4096 || d.n_shared > 2) return MOE_ERR_UNSUPPORTED;
+    if (d.n_shared > 0 && d.h_shared % 128 != 0) return MOE_ERR_UNSUPPORTED;
+    if ((uint64_t)d.T * d.l * 2 >= k4G) return MOE_ERR_UNSUPPORTED;
+    if ((uint64_t)d.n_shared * d.T * d.h_shared * 2 >= k4G) return MOE_ERR_UNSUPPORTED;
+  }
+  if (d.d > 16384) return MOE_ERR_UNSUPPORTED;
+  // 32-bit buffer addressing of gathered / streamed operands.
+  if ((uint64_t)d.T * d.d * 2 >= k4G || (uint64_t)R * d.h * 2 >= k4G ||
+      (uint64_t)d.h * xwidth(d) * 2 >= k4G || (uint64_t)d.N * d.d * 2 >= k4G)
+    return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+template <typename T>
+T *region(void *ws, size_t off) {
+  return reinterpret_cast<T *>(reinterpret_cast<char *>(ws) + off);
+}
+
+moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+#define MOE_TRY(expr)                          \
+  do {                                         \
+    const hipError_t e_ = (expr);              \
+    if (e_ != hipSuccess) return MOE_ERR_HIP;  \
+  } while (0)
+
+// ---- stages (no validation; callers validated) ------------------------------
+
+hipError_t do_route(const moe_desc_t &d, const Layout &L, const void *u, const void *W_route,
+                    int32_t *idx, float *w, float *stats, void *ws, hipStream_t st) {
+  float *pp = region<float>(ws, L.part_p);
+  int32_t *pc = region<int32_t>(ws, L.part_cnt);
+  hipError_t e;
+  if (router_gemm(d)) {
+    GemmArgs a;
+    memset(&a, 0, sizeof(a));
+    a.A = static_cast<const uint16_t *>(u);
+    a.lda = d.d;
+    a.B = static_cast<const uint16_t *>(W_route);
+    a.K = d.d;
+    a.ncols = d.N;
+    a.mode = GM_DENSE;
+    a.G = 1;
+    a.M_dense = d.T;
+    a.out = region<float>(ws, L.logits);
+    a.ldo = d.N;
+    e = launch_gemm(a, EP_F32, 0, st);
+    if (e != hipSuccess) return e;
+    e = launch_topk_logits(region<float>(ws, L.logits), d.T, d.N, d.k, d.gate, idx, w, pp, pc, st);
+  } else {
+    e = launch_route_wave(u, d.act_dtype == MOE_BF16, W_route, d.router_dtype == MOE_BF16, d.T,
+                          d.d, d.N, d.k, d.gate, idx, w, pp, pc, st);
+  }
+  if (e != hipSuccess || stats == nullptr) return e;
+  return launch_stats_finalize(pp, pc, route_waves(d.T, d.N), d.T, d.N, d.aux_alpha, stats, st);
+}
+
+hipError_t do_dispatch(const moe_desc_t &d, const Layout &L, const int32_t *idx, int32_t *counts,
+                       int32_t *offsets, int32_t *kept_offsets, int32_t *perm, int32_t *row_of,
+                       uint8_t *drop, void *ws, hipStream_t st) {
+  return launch_dispatch(idx, d.T, d.k, d.N, d.capacity, counts, offsets, kept_offsets, perm,
+                         row_of, drop, region<int32_t>(ws, L.blk_counts), st);
+}
+
+// Grouped-GEMM prefill path needs the m-tile prefix of the kept counts.
+bool ffn_uses_gemm(const moe_desc_t &d) { return bf16_path(d) && !decode_path(d); }
+
+hipError_t do_tile_prefix(const moe_desc_t &d, const Layout &L, const int32_t *kept_offsets,
+                          void *ws, hipStream_t st) {
+  if (!ffn_uses_gemm(d)) return hipSuccess;
+  return launch_tile_prefix(kept_offsets, d.N, region<int32_t>(ws, L.tile_start), st);
+}
+
+hipError_t do_ffn_gate_up(const moe_desc_t &d, const Layout &L, const void *x, const int32_t *perm,
+                          const int32_t *offsets, const int32_t *kept_offsets, const void *Wg,
+                          const void *Wu, void *ws, hipStream_t st) {
+  const int w = xwidth(d);
+  if (!bf16_path(d))
+    return launch_simt_gu(static_cast<const float *>(x), perm, offsets, kept_offsets, d.k,
+                          static_cast<const float *>(Wg), static_cast<const float *>(Wu), w, d.h,
+                          d.N, d.act, d.beta_g, d.beta_u, region<float>(ws, L.hid), st);
+  if (decode_path(d))
+    return launch_decode_gu(static_cast<const uint16_t *>(x), d.T, w, perm, offsets, kept_offsets,
+                            d.k, static_cast<const uint16_t *>(Wg),
+                            static_cast<const uint16_t *>(Wu), d.h, d.N, d.act, d.beta_g, d.beta_u,
+                            region<uint16_t>(ws, L.hid), st);
+  GemmArgs a;
+  memset(&a, 0, sizeof(a));
+  a.A = static_cast<const uint16_t *>(x);
+  a.lda = w;
+  a.B = static_cast<const uint16_t *>(Wg);
+  a.B2 = static_cast<const uint16_t *>(Wu);
+  a.strideB = (int64_t)d.h * w;
+  a.K = w;
+  a.ncols = d.h;
+  a.mode = GM_GATHER;
+  a.G = d.N;
+  a.kslots = d.k;
+  a.perm = perm;
+  a.offsets = offsets;
+  a.kept_offsets = kept_offsets;
+  a.tile_start = region<int32_t>(ws, L.tile_start);
+  a.out = region<uint16_t>(ws, L.hid);
+  a.ldo = d.h;
+  a.act = d.act;
+  a.beta_g = d.beta_g;
+  a.beta_u = d.beta_u;
+  return launch_gemm(a, EP_GLU, gemm_mtile_bound(kept_rows_bound(d), d.N), st);
+}
+
+hipError_t do_ffn_down(const moe_desc_t &d, const Layout &L, const int32_t *kept_offsets,
+                       const void *Wd, float *y_perm, void *ws, hipStream_t st) {
+  const int w = xwidth(d);
+  if (!bf16_path(d))
+    return launch_simt_down(region<float>(ws, L.hid), kept_offsets,
+                            static_cast<const float *>(Wd), d.h, w, d.N, y_perm, st);
+  if (decode_path(d))
+    return launch_decode_down(region<uint16_t>(ws, L.hid), d.T, kept_offsets,
+                              static_cast<const uint16_t *>(Wd), d.h, w, d.N, y_perm, st);
+  GemmArgs a;
+  memset(&a, 0, sizeof(a));
+  a.A = region<uint16_t>(ws, L.hid);
+  a.lda = d.h;
+  a.B = static_cast<const uint16_t *>(Wd);
+  a.strideB = (int64_t)w * d.h;
+  a.K = d.h;
+  a.ncols = w;
+  a.mode = GM_SEGMENT;
+  a.G = d.N;
+  a.kept_offsets = kept_offsets;
+  a.tile_start = region<int32_t>(ws, L.tile_start);
+  a.out = y_perm;
+  a.ldo = w;
+  return launch_gemm(a, EP_F32, gemm_mtile_bound(kept_rows_bound(d), d.N), st);
+}
+
+// Dense (one or few groups) projection: out[g*T + r] = A[g*a_rows + r] . B_g
+hipError_t dense_gemm(const uint16_t *A, int64_t lda, int64_t a_group_rows, const uint16_t *B,
+                      const uint16_t *B2, int64_t strideB, int K, int ncols, int G, int64_t M,
+                      void *out, int64_t ldo, int epi, const float *add0, const float *add1,
+                      int act, hipStream_t st) {
+  GemmArgs a;
+  memset(&a, 0, sizeof(a));
+  a.A = A;
+  a.lda = lda;
+  a.a_group_rows = a_group_rows;
+  a.B = B;
+  a.B2 = B2;
+  a.strideB = strideB;
+  a.K = K;
+  a.ncols = ncols;
+  a.mode = GM_DENSE;
+  a.G = G;
+  a.M_dense = M;
+  a.out = out;
+  a.ldo = ldo;
+  a.out_group_stride = M;
+  a.add0 = add0;
+  a.add1 = add1;
+  a.act = act;
+  a.beta_g = 1.f;
+  a.beta_u = 1.f;
+  return launch_gemm(a, epi, 0, st);
+}
+
+struct Tracer {
+  void *const *ev;
+  int n;
+  int next;
+  hipStream_t st;
+  hipError_t mark() {
+    if (next < n) {
+      const hipError_t e = hipEventRecord(static_cast<hipEvent_t>(ev[next]), st);
+      ++next;
+      return e;
+    }
+    return hipSuccess;
+  }
+};
+
+const char *const kPlainStages[] = {"route", "dispatch", "expert_gate_up", "expert_down",
+                                    "combine"};
+const char *const kLatentStages[] = {"route",         "dispatch",        "latent_down_proj",
+                                     "expert_gate_up", "expert_down",     "combine_rmsnorm",
+                                     "shared_gate_up", "shared_down",     "latent_up_proj"};
+
+moe_status_t forward_impl(const moe_desc_t *desc, const moe_weights_t *wts, const void *u, void *y,
+                          const moe_outputs_t *out, void *ws, size_t ws_bytes, hipStream_t st,
+                          void *const *events, int n_events) {
+  const moe_status_t v = validate(desc);
+  if (v != MOE_OK) return v;
+  const moe_desc_t &d = *desc;
+  if (wts == nullptr || u == nullptr || y == nullptr || wts->W_route == nullptr ||
+      wts->W_gate == nullptr || wts->W_up == nullptr || wts->W_down == nullptr)
+    return MOE_ERR_ARG;
+  if (is_latent(d) && (wts->W_ldown == nullptr || wts->W_lup == nullptr)) return MOE_ERR_ARG;
+  if (is_latent(d) && d.n_shared > 0 &&
+      (wts->Ws_gate == nullptr || wts->Ws_up == nullptr || wts->Ws_down == nullptr))
+    return MOE_ERR_ARG;
+  const Layout L = layout(d);
+  if (ws == nullptr || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (n_events > 0 && events == nullptr) return MOE_ERR_ARG;
+
+  moe_outputs_t o;
+  memset(&o, 0, sizeof(o));
+  if (out != nullptr) o = *out;
+  int32_t *idx = o.topk_idx ? o.topk_idx : region<int32_t>(ws, L.idx);
+  float *tw = o.topk_w ? o.topk_w : region<float>(ws, L.w);
+  float *stats = o.stats ? o.stats : region<float>(ws, L.stats);
+  int32_t *counts = o.counts ? o.counts : region<int32_t>(ws, L.counts);
+  int32_t *offsets = o.offsets ? o.offsets : region<int32_t>(ws, L.offsets);
+  int32_t *kept_offsets = o.kept_offsets ? o.kept_offsets : region<int32_t>(ws, L.kept_offsets);
+  int32_t *perm = o.perm ? o.perm : region<int32_t>(ws, L.perm);
+  int32_t *row_of = o.row_of ? o.row_of : region<int32_t>(ws, L.row_of);
+  uint8_t *drop = o.drop ? o.drop : region<uint8_t>(ws, L.drop);
+  float *y_perm = region<float>(ws, L.y_perm);
+
+  Tracer tr{events, n_events, 0, st};
+  MOE_TRY(tr.mark());
+  MOE_TRY(do_route(d, L, u, wts->W_route, idx, tw, stats, ws, st));
+  MOE_TRY(tr.mark());
+  MOE_TRY(do_dispatch(d, L, idx, counts, offsets, kept_offsets, perm, row_of, drop, ws, st));
+  MOE_TRY(do_tile_prefix(d, L, kept_offsets, ws, st));
+  MOE_TRY(tr.mark());
+  const void *x = u;
+  if (is_latent(d)) {
+    uint16_t *xl = region<uint16_t>(ws, L.x_l);
+    MOE_TRY(dense_gemm(static_cast<const uint16_t *>(u), d.d, 0,
+                       static_cast<const uint16_t *>(wts->W_ldown), nullptr, 0, d.d, d.l, 1, d.T,
+                       xl, d.l, EP_BF16, nullptr, nullptr, 0, st));
+    MOE_TRY(tr.mark());
+    x = xl;
+  }
+  MOE_TRY(do_ffn_gate_up(d, L, x, perm, offsets, kept_offsets, wts->W_gate, wts->W_up, ws, st));
+  MOE_TRY(tr.mark());
+  MOE_TRY(do_ffn_down(d, L, kept_offsets, wts->W_down, y_perm, ws, st));
+  MOE_TRY(tr.mark());
+  if (!is_latent(d)) {
+    MOE_TRY(launch_combine(y_perm, row_of, tw, d.T, d.k, d.d, bf16_path(d), false, 0.f, y, st));
+    MOE_TRY(tr.mark());
+  } else {
+    uint16_t *rn = region<uint16_t>(ws, L.rn);
+    MOE_TRY(launch_combine(y_perm, row_of, tw, d.T, d.k, d.l, true, true, d.rms_eps, rn, st));
+    MOE_TRY(tr.mark());
+    const float *add0 = nullptr, *add1 = nullptr;
+    if (d.n_shared > 0) {
+      uint16_t *hs = region<uint16_t>(ws, L.hs);
+      float *ys = region<float>(ws, L.ys);
+      MOE_TRY(dense_gemm(static_cast<const uint16_t *>(u), d.d, 0,
+                         static_cast<const uint16_t *>(wts->Ws_gate),
+                         static_cast<const uint16_t *>(wts->Ws_up), (int64_t)d.h_shared * d.d, d.d,
+                         d.h_shared, d.n_shared, d.T, hs, d.h_shared, EP_GLU, nullptr, nullptr,
+                         MOE_ACT_SWIGLU, st));
+      MOE_TRY(tr.mark());
+      MOE_TRY(dense_gemm(hs, d.h_shared, d.T, static_cast<const uint16_t *>(wts->Ws_down), nullptr,
+                         (int64_t)d.d * d.h_shared, d.h_shared, d.d, d.n_shared, d.T, ys, d.d,
+                         EP_F32, nullptr, nullptr, 0, st));
+      MOE_TRY(tr.mark());
+      add0 = ys;
+      add1 = d.n_shared > 1 ? ys + (int64_t)d.T * d.d : nullptr;
+    } else {
+      MOE_TRY(tr.mark());
+      MOE_TRY(tr.mark());
+    }
+    MOE_TRY(dense_gemm(rn, d.l, 0, static_cast<const uint16_t *>(wts->W_lup), nullptr, 0, d.l, d.d,
+                       1, d.T, y, d.d, add0 ? EP_ADD_BF16 : EP_BF16, add0, add1, 0, st));
+    MOE_TRY(tr.mark());
+  }
+  while (tr.next < tr.n) MOE_TRY(tr.mark());
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+void moe_desc_init(moe_desc_t *d) {
+  if (d == nullptr) return;
+  d->T = kUnsetI64;
+  d->d = d->h = d->N = d->k = d->capacity = kUnsetI32;
+  d->act_dtype = d->w_dtype = d->router_dtype = d->gate = d->act = kUnsetI32;
+  d->beta_g = d->beta_u = NAN;
+  d->l = d->n_shared = d->h_shared = kUnsetI32;
+  d->rms_eps = NAN;
+  d->aux_alpha = NAN;
+}
+
+const char *moe_status_string(moe_status_t s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "layer not supported by these kernels";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_HIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+moe_status_t moe_workspace_bytes(const moe_desc_t *desc, size_t *bytes) {
+  if (bytes == nullptr) return MOE_ERR_ARG;
+  *bytes = 0;
+  const moe_status_t v = validate(desc);
+  if (v != MOE_OK) return v;
+  *bytes = layout(*desc).total;
+  return MOE_OK;
+}
+
+int32_t moe_capacity_from_factor(int64_t T, int32_t N, int32_t k, double c) {
+  if (T < 1 || N < 1 || k < 1 || !isfinite(c) || c <= 0.0) return -1;
+  const double v = ceil((c * (double)k * (double)T) / (double)N);
+  if (v > (double)INT32_MAX) return -1;
+  return (int32_t)v;
+}
+
+moe_status_t moe_route(const moe_desc_t *desc, const void *u, const void *W_route,
+                       int32_t *topk_idx, float *topk_w, float *stats, void *ws, size_t ws_bytes,
+                       moe_stream_t stream) {
+  const moe_status_t v = validate(desc);
+  if (v != MOE_OK) return v;
+  if (u == nullptr || W_route == nullptr || topk_idx == nullptr || topk_w == nullptr)
+    return MOE_ERR_ARG;
+  const Layout L = layout(*desc);
+  if (ws == nullptr || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  return hip_status(do_route(*desc, L, u, W_route, topk_idx, topk_w, stats, ws,
+                             reinterpret_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_dispatch(const moe_desc_t *desc, const int32_t *topk_idx, int32_t *counts,
+                          int32_t *offsets, int32_t *kept_offsets, int32_t *perm, int32_t *row_of,
+                          uint8_t *drop, void *ws, size_t ws_bytes, moe_stream_t stream) {
+  const moe_status_t v = validate(desc);
+  if (v != MOE_OK) return v;
+  if (topk_idx == nullptr || counts == nullptr || offsets == nullptr || kept_offsets == nullptr ||
+      perm == nullptr || row_of == nullptr || drop == nullptr)
+    return MOE_ERR_ARG;
+  const Layout L = layout(*desc);
+  if (ws == nullptr || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  return hip_status(do_dispatch(*desc, L, topk_idx, counts, offsets, kept_offsets, perm, row_of,
+                                drop, ws, reinterpret_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_expert_ffn(const moe_desc_t *desc, const void *x, const int32_t *perm,
+                            const int32_t *offsets, const int32_t *kept_offsets,
+                            const void *W_gate, const void *W_up, const void *W_down,
+                            float *y_perm, void *ws, size_t ws_bytes, moe_stream_t stream) {
+  const moe_status_t v = validate(desc);
+  if (v != MOE_OK) return v;
+  if (x == nullptr || perm == nullptr || offsets == nullptr || kept_offsets == nullptr ||
+      W_gate == nullptr || W_up == nullptr || W_down == nullptr || y_perm == nullptr)
+    return MOE_ERR_ARG;
+  const Layout L = layout(*desc);
+  if (ws == nullptr || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  MOE_TRY(do_tile_prefix(*desc, L, kept_offsets, ws, st));
+  MOE_TRY(do_ffn_gate_up(*desc, L, x, perm, offsets, kept_offsets, W_gate, W_up, ws, st));
+  MOE_TRY(do_ffn_down(*desc, L, kept_offsets, W_down, y_perm, ws, st));
+  return MOE_OK;
+}
+
+moe_status_t moe_combine(const moe_desc_t *desc, const float *y_perm, const int32_t *row_of,
+                         const float *topk_w, void *y, moe_stream_t stream) {
+  const moe_status_t v = validate(desc);
+  if (v != MOE_OK) return v;
+  if (y_perm == nullptr || row_of == nullptr || topk_w == nullptr || y == nullptr)
+    return MOE_ERR_ARG;
+  const moe_desc_t &d = *desc;
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (is_latent(d))
+    return hip_status(
+        launch_combine(y_perm, row_of, topk_w, d.T, d.k, d.l, true, true, d.rms_eps, y, st));
+  return hip_status(
+      launch_combine(y_perm, row_of, topk_w, d.T, d.k, d.d, bf16_path(d), false, 0.f, y, st));
+}
+
+moe_status_t moe_forward(const moe_desc_t *desc, const moe_weights_t *w, const void *u, void *y,
+                         const moe_outputs_t *out, void *ws, size_t ws_bytes,
+                         moe_stream_t stream) {
+  return forward_impl(desc, w, u, y, out, ws, ws_bytes, reinterpret_cast<hipStream_t>(stream),
+                      nullptr, 0);
+}
+
+moe_status_t moe_forward_traced(const moe_desc_t *desc, const moe_weights_t *w, const void *u,
+                                void *y, const moe_outputs_t *out, void *ws, size_t ws_bytes,
+                                moe_stream_t stream, void *const *events, int32_t n_events) {
+  return forward_impl(desc, w, u, y, out, ws, ws_bytes, reinterpret_cast<hipStream_t>(stream),
+                      events, n_events < 0 ? 0 : n_events);
+}
+
+const char *moe_stage_name(const moe_desc_t *desc, int32_t i, int32_t *n_stages) {
+  if (n_stages) *n_stages = 0;
+  if (validate(desc) != MOE_OK) return nullptr;
+  const bool lat = is_latent(*desc);
+  const int n = lat ? 9 : 5;
+  if (n_stages) *n_stages = n;
+  if (i < 1 || i > n) return nullptr;
+  return lat ? kLatentStages[i - 1] : kPlainStages[i - 1];
+}
+
+}  // extern "C"

@@ -1,0 +1,352 @@
+"""GPU parity: the HIP library, called through its C ABI, against the fp64 oracle
+on the same seeded inputs.  Stage tests feed each entry point oracle-made
+inputs; end-to-end tests run moe_forward and compare every output."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import sparse_mixture_experts_11_amd as moe
+from synth import configs as C
+from tests import harness as H
+from tests import parity as PR
+import synth as S
+
+pytestmark = pytest.mark.gpu
+
+# Parity cases the oracle finishes in seconds: several tiles and ragged tails.
+MIX_S = C.MIXTRAL_PREFILL.with_(name="mixtral_small_t1000", T=1000, d=1024, h=2048)
+CASES = {
+    "tiny": C.TINY,
+    "tiny_k4": C.TINY.with_(name="tiny_k4", k=4),
+    "tiny_planted_c4": C.TINY_PLANTED,
+    "tiny_planted_c6": C.TINY_PLANTED.with_(capacity_factor=1.5),
+    "tiny_planted_c10": C.TINY_PLANTED.with_(capacity_factor=2.5),
+    "tiny_planted_empty_expert": C.TINY_PLANTED.with_(planted=tuple([0] * 10 + [1] * 5 + [3]),
+                                                      capacity_factor=1.5),
+    "mcu_t1": C.MCU_DECODE,
+    "mcu_t4096": C.MCU_BATCH,
+    "mixtral_small_t1000": MIX_S,
+    "mixtral_small_t37_decode": MIX_S.with_(T=37),
+    "mixtral_small_t64_decode": MIX_S.with_(T=64),
+    "mixtral_small_t65": MIX_S.with_(T=65),
+    "switch_small_t2000": C.SWITCH_SKEWED.with_(T=2000, d=1024, h=1024),
+    "switch_small_t48_decode": C.SWITCH_SKEWED.with_(T=48, d=1024, h=1024),
+    "latent_small_t700": C.LATENT.with_(T=700, d=512, l=384, h=256, N=96, k=6, h_shared=256),
+    "latent_small_wave_router": C.LATENT.with_(T=300, d=512, l=256, h=256, N=40, k=4,
+                                               h_shared=128, n_shared=1),
+    "latent_small_decode_t20": C.LATENT.with_(T=20, d=512, l=384, h=256, N=96, k=6, h_shared=256),
+}
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def oracle_capacity(cfg):
+    if cfg.capacity_factor is None:
+        return None
+    return O.capacity_from_factor(cfg.T, cfg.N, cfg.k, cfg.capacity_factor)
+
+
+def oracle_forward(cfg, tokens=None):
+    experts = lambda e: cfg.expert(e)  # noqa: E731
+    cap = oracle_capacity(cfg)
+    u = cfg.u()
+    if cfg.latent:
+        return O.latent_forward(u, cfg.w_route(), experts, cfg.w_ldown(), cfg.w_lup(),
+                                lambda j: cfg.shared(j), cfg.n_shared, k=cfg.k, gate=cfg.gate,
+                                act=cfg.act, capacity=cap, beta_g=cfg.beta_g, beta_u=cfg.beta_u,
+                                rms_eps=cfg.rms_eps, alpha=cfg.aux_alpha, tokens=tokens)
+    return O.forward(u, cfg.w_route(), experts, k=cfg.k, gate=cfg.gate, act=cfg.act,
+                     capacity=cap, beta_g=cfg.beta_g, beta_u=cfg.beta_u, alpha=cfg.aux_alpha,
+                     tokens=tokens)
+
+
+def run_forward(cfg, weights=None, u=None):
+    desc = H.desc_for(cfg)
+    w = weights if weights is not None else H.upload_layer(cfg)
+    u = u if u is not None else H.to_device(cfg.u())
+    y = H.y_buffer(cfg)
+    out = H.out_buffers(cfg)
+    ws = moe.workspace(desc)
+    moe.moe_forward(desc, w, u, y, out, ws)
+    torch.cuda.synchronize()
+    return y, out
+
+
+def check_forward(cfg, ref, y, out, tokens=None):
+    """Compare a moe_forward result against the oracle (all tokens or a sample)."""
+    T, k = cfg.T, cfg.k
+    gidx = H.to_host(out["topk_idx"])
+    routing = PR.compare_routing(cfg, gidx, ref)
+    ok = PR.usable_tokens(cfg, ref, routing)
+    # Combine weights.
+    gw = H.to_host(out["topk_w"]).reshape(T, k)
+    werr = np.abs(gw[routing["same"]] - ref["a"][routing["same"]]).max()
+    assert werr <= PR.W_TOL[cfg.act_dtype], werr
+    # Dispatch: bit-exact when no near tie flipped.
+    if routing["flipped"] == 0:
+        PR.compare_dispatch({key: H.to_host(out[key]) for key in
+                             ("counts", "offsets", "kept_offsets", "perm", "row_of", "drop")},
+                            ref["disp"])
+    # Balance statistics (argmax shares exact, means to fp32 accuracy).
+    st = H.to_host(out["stats"])
+    N = cfg.N
+    if routing["flipped"] == 0:
+        assert np.array_equal(np.rint(st[:N] * T).astype(np.int64),
+                              np.rint(ref["stats"]["f"] * T).astype(np.int64))
+    assert np.allclose(st[N:2 * N], ref["stats"]["P"], rtol=1e-4, atol=1e-6)
+    assert abs(st[2 * N] - ref["stats"]["n_sum_fP"]) <= 1e-4 * max(1.0, ref["stats"]["n_sum_fP"])
+    # Outputs.
+    yg = H.expand_device_output(y)
+    if tokens is not None:
+        yg = yg[tokens]
+        ok = ok[tokens]
+    err = PR.rel_err(yg[ok], ref["y"][ok])
+    log(f"  {cfg.name}: rel err {err:.3e}, near ties {routing['near']}, flipped "
+        f"{routing['flipped']}, compared {int(ok.sum())} tokens")
+    assert err <= PR.TOL[cfg.act_dtype], err
+    return routing
+
+
+# ---------------------------------------------------------------------------
+# End-to-end on parity-size cases
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_forward_parity(name):
+    cfg = CASES[name]
+    log(f"[forward] {name} T={cfg.T} d={cfg.d} h={cfg.h} N={cfg.N} k={cfg.k}")
+    ref = oracle_forward(cfg)
+    y, out = run_forward(cfg)
+    check_forward(cfg, ref, y, out)
+    if cfg.planted is not None:
+        # The worked example: loads [10,3,2,1]; C = 4/6/10 drop 6/4/0.
+        drops = int(H.to_host(out["drop"]).sum())
+        assert drops == int(ref["disp"]["drop"].sum())
+
+
+def test_planted_drops_match_page_example():
+    for c, drops in ((1.0, 6), (1.5, 4), (2.5, 0)):
+        cfg = C.TINY_PLANTED.with_(capacity_factor=c)
+        log(f"[planted] capacity factor {c}")
+        y, out = run_forward(cfg)
+        assert H.to_host(out["counts"]).tolist() == [10, 3, 2, 1]
+        dr = H.to_host(out["drop"])
+        assert int(dr.sum()) == drops
+        yd = H.expand_device_output(y)[dr.astype(bool)]
+        assert np.all(yd == 0.0)
+
+
+def test_zero_capacity_gives_zero_output():
+    cfg = MIX_S.with_(T=300)
+    log("[capacity 0]")
+    desc = H.desc_for(cfg, capacity=0)
+    w = H.upload_layer(cfg)
+    u = H.to_device(cfg.u())
+    y = H.y_buffer(cfg)
+    y.fill_(1.0)
+    out = H.out_buffers(cfg)
+    moe.moe_forward(desc, w, u, y, out, moe.workspace(desc))
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(y).item() == 0
+    assert int(H.to_host(out["drop"]).sum()) == cfg.T * cfg.k
+
+
+def test_deterministic_bitwise():
+    for cfg in (MIX_S, CASES["latent_small_t700"], C.MCU_DECODE):
+        log(f"[determinism] {cfg.name}")
+        w = H.upload_layer(cfg)
+        u = H.to_device(cfg.u())
+        y1, o1 = run_forward(cfg, w, u)
+        y2, o2 = run_forward(cfg, w, u)
+        assert torch.equal(y1.view(torch.int16) if y1.dtype == torch.bfloat16 else y1,
+                           y2.view(torch.int16) if y2.dtype == torch.bfloat16 else y2)
+        for key in o1:
+            assert torch.equal(o1[key], o2[key]), key
+
+
+@pytest.mark.parametrize("name", ["mcu_t1", "mixtral_small_t37_decode", "tiny"])
+def test_unselected_expert_perturbation(name):
+    cfg = CASES[name]
+    log(f"[perturb] {name}")
+    ref_idx = O.route(O.expand(cfg.u()), O.expand(cfg.w_route()), cfg.k, cfg.gate)["idx"]
+    unused = sorted(set(range(cfg.N)) - set(ref_idx.reshape(-1).tolist()))
+    if not unused:
+        pytest.skip("every expert is selected by some token")
+    w = H.upload_layer(cfg)
+    u = H.to_device(cfg.u())
+    y0, _ = run_forward(cfg, w, u)
+    for e in unused:
+        for key in ("W_gate", "W_up", "W_down"):
+            w[key][e] *= 1000.0
+    y1, _ = run_forward(cfg, w, u)
+    a = y0.view(torch.int16) if y0.dtype == torch.bfloat16 else y0
+    b = y1.view(torch.int16) if y1.dtype == torch.bfloat16 else y1
+    assert torch.equal(a, b)
+
+
+# ---------------------------------------------------------------------------
+# Stage tests: each entry point fed oracle-made inputs
+# ---------------------------------------------------------------------------
+
+STAGE_CASES = ["tiny", "tiny_planted_c4", "mcu_t4096", "mixtral_small_t1000",
+               "mixtral_small_t37_decode", "switch_small_t2000", "latent_small_t700"]
+
+
+@pytest.mark.parametrize("name", STAGE_CASES)
+def test_stage_route(name):
+    cfg = CASES[name]
+    log(f"[route] {name}")
+    desc = H.desc_for(cfg)
+    ref = O.route(O.expand(cfg.u()), O.expand(cfg.w_route()), cfg.k, cfg.gate)
+    E = cfg.T * cfg.k
+    idx = torch.empty(E, dtype=torch.int32, device="cuda")
+    w = torch.empty(E, dtype=torch.float32, device="cuda")
+    st = torch.empty(2 * cfg.N + 2, dtype=torch.float32, device="cuda")
+    moe.moe_route(desc, H.to_device(cfg.u()), H.to_device(cfg.w_route()), idx, w, st,
+                  moe.workspace(desc))
+    torch.cuda.synchronize()
+    routing = PR.compare_routing(cfg, H.to_host(idx), ref)
+    same = routing["same"]
+    gw = H.to_host(w).reshape(cfg.T, cfg.k)
+    assert np.abs(gw[same] - ref["a"][same]).max() <= PR.W_TOL[cfg.act_dtype]
+    stats = O.balance_stats(ref["p"], cfg.aux_alpha)
+    s = H.to_host(st)
+    assert np.allclose(s[cfg.N:2 * cfg.N], stats["P"], rtol=1e-4, atol=1e-6)
+    assert abs(s[2 * cfg.N + 1] - stats["aux"]) <= 1e-4 * max(stats["aux"], 1e-3)
+
+
+@pytest.mark.parametrize("name", STAGE_CASES + ["switch_small_t48_decode"])
+def test_stage_dispatch(name):
+    cfg = CASES[name]
+    log(f"[dispatch] {name}")
+    desc = H.desc_for(cfg)
+    ref = O.route(O.expand(cfg.u()), O.expand(cfg.w_route()), cfg.k, cfg.gate)
+    rd = O.dispatch(ref["idx"], cfg.N, oracle_capacity(cfg))
+    out = H.out_buffers(cfg)
+    moe.moe_dispatch(desc, H.to_device(ref["idx"].reshape(-1)), out["counts"], out["offsets"],
+                     out["kept_offsets"], out["perm"], out["row_of"], out["drop"],
+                     moe.workspace(desc))
+    torch.cuda.synchronize()
+    PR.compare_dispatch({k: H.to_host(out[k]) for k in
+                         ("counts", "offsets", "kept_offsets", "perm", "row_of", "drop")}, rd)
+
+
+def test_stage_dispatch_random_assignments():
+    # Many experts, many chunks, capacity: random distinct top-k rows.
+    rng = np.random.default_rng(0)
+    for T, N, k, cap in ((5000, 896, 16, 70), (3000, 8, 2, 700), (100, 1024, 32, 2),
+                         (2049, 64, 3, -1)):
+        log(f"[dispatch random] T={T} N={N} k={k} cap={cap}")
+        cfg = C.LATENT.with_(T=T, N=N, k=k)
+        idx = np.stack([rng.permutation(N)[:k] for _ in range(T)]).astype(np.int32)
+        desc = H.desc_for(cfg, capacity=cap)
+        out = H.out_buffers(cfg)
+        moe.moe_dispatch(desc, H.to_device(idx.reshape(-1)), out["counts"], out["offsets"],
+                         out["kept_offsets"], out["perm"], out["row_of"], out["drop"],
+                         moe.workspace(desc))
+        torch.cuda.synchronize()
+        rd = O.dispatch(idx, N, None if cap < 0 else cap)
+        PR.compare_dispatch({key: H.to_host(out[key]) for key in
+                             ("counts", "offsets", "kept_offsets", "perm", "row_of", "drop")}, rd)
+
+
+@pytest.mark.parametrize("name", STAGE_CASES + ["mcu_t1", "latent_small_decode_t20"])
+def test_stage_expert_ffn(name):
+    cfg = CASES[name]
+    log(f"[expert_ffn] {name}")
+    desc = H.desc_for(cfg)
+    u64 = O.expand(cfg.u())
+    ref = O.route(u64, O.expand(cfg.w_route()), cfg.k, cfg.gate)
+    rd = O.dispatch(ref["idx"], cfg.N, oracle_capacity(cfg))
+    # Expert input: u, or for the latent layer a seeded stand-in for x_l.
+    if cfg.latent:
+        x_st = S.normal_stored(cfg.seed + 100, 99, cfg.T * cfg.l, 1.0, cfg.act_dtype).reshape(
+            cfg.T, cfg.l)
+    else:
+        x_st = cfg.u()
+    act = O.make_act(cfg.act, cfg.beta_g, cfg.beta_u)
+    rows = O.expert_rows(O.expand(x_st), rd, lambda e: cfg.expert(e), act, cfg.k)
+    R = int(rd["kept_offsets"][-1])
+    w = H.upload_layer(cfg)
+    y_perm = torch.full((max(R, 1), cfg.x_width), float("nan"), device="cuda")
+    moe.moe_expert_ffn(desc, H.to_device(x_st), H.to_device(rd["perm"]),
+                       H.to_device(rd["offsets"]), H.to_device(rd["kept_offsets"]), w["W_gate"],
+                       w["W_up"], w["W_down"], y_perm, moe.workspace(desc))
+    torch.cuda.synchronize()
+    if R == 0:
+        return
+    yr = np.stack([rows[r] for r in range(R)])
+    err = PR.rel_err(H.to_host(y_perm)[:R].astype(np.float64), yr)
+    log(f"  rel err {err:.3e}")
+    assert err <= PR.TOL[cfg.act_dtype]
+
+
+@pytest.mark.parametrize("name", STAGE_CASES)
+def test_stage_combine(name):
+    cfg = CASES[name]
+    log(f"[combine] {name}")
+    desc = H.desc_for(cfg)
+    ref = O.route(O.expand(cfg.u()), O.expand(cfg.w_route()), cfg.k, cfg.gate)
+    rd = O.dispatch(ref["idx"], cfg.N, oracle_capacity(cfg))
+    R = max(int(rd["kept_offsets"][-1]), 1)
+    width = cfg.x_width
+    y_rows = S.normal_stored(cfg.seed + 7, 98, R * width, 1.0, "f32").reshape(R, width)
+    a32 = S.round_to(ref["a"], "f32")
+    want = O.combine_rows(O.expand(y_rows), rd["row_of"], O.expand(a32),
+                          rms_eps=cfg.rms_eps if cfg.latent else None)
+    out_dtype = torch.bfloat16 if (cfg.latent or cfg.act_dtype == "bf16") else torch.float32
+    y = torch.empty((cfg.T, width), dtype=out_dtype, device="cuda")
+    moe.moe_combine(desc, H.to_device(y_rows), H.to_device(rd["row_of"]),
+                    H.to_device(a32.reshape(-1)), y)
+    torch.cuda.synchronize()
+    err = PR.rel_err(H.expand_device_output(y), want)
+    # fp32 sums then one rounding to the output dtype.
+    tol = 2 ** -8 if out_dtype == torch.bfloat16 else 1e-6
+    assert err <= tol, err
+
+
+# ---------------------------------------------------------------------------
+# Full-size workloads: every routing/dispatch output, sampled y rows
+# ---------------------------------------------------------------------------
+
+
+def sample_tokens(T, n, seed):
+    rng = np.random.default_rng(seed)
+    s = set(rng.choice(T, size=min(n, T), replace=False).tolist()) | {0, T - 1}
+    return np.array(sorted(s))
+
+
+@pytest.mark.parametrize("cfg", [C.MIXTRAL_PREFILL, C.MIXTRAL_DECODE, C.SWITCH_SKEWED,
+                                 C.MCU_BATCH, C.MCU_DECODE, C.TINY],
+                         ids=lambda c: c.name)
+@pytest.mark.timeout(600)
+def test_full_size_forward(cfg):
+    log(f"[full] {cfg.name}")
+    tokens = None if cfg.T <= 64 else sample_tokens(cfg.T, 24, cfg.seed)
+    ref = oracle_forward(cfg, tokens=tokens)
+    y, out = run_forward(cfg)
+    routing = check_forward(cfg, ref, y, out, tokens=tokens)
+    if cfg is C.SWITCH_SKEWED:
+        counts = H.to_host(out["counts"])
+        log(f"  loads {counts.tolist()} capacity {H.capacity_of(cfg)} "
+            f"dropped {int(H.to_host(out['drop']).sum())}")
+    assert routing["near"] <= cfg.T // 100
+
+
+@pytest.mark.timeout(1200)
+def test_full_size_latent():
+    cfg = C.LATENT
+    log(f"[full] {cfg.name}: uploading {cfg.N} experts")
+    tokens = sample_tokens(cfg.T, 6, cfg.seed)
+    ref = oracle_forward(cfg, tokens=tokens)
+    y, out = run_forward(cfg)
+    check_forward(cfg, ref, y, out, tokens=tokens)

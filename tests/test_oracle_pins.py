@@ -464,3 +464,20 @@ def test_round_matches_torch_on_fp32_exact_values():
     ours = synth.round_to(x, "bf16")
     ref = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy()
     assert np.array_equal(ours.view(np.int16), ref)
+
+
+def test_combine_rows_and_expert_rows_rebuild_forward():
+    # The staged oracle (expert rows, then combine) equals the one-pass forward,
+    # with and without capacity.
+    for cfg in (C.TINY, C.TINY_PLANTED):
+        cap = (None if cfg.capacity_factor is None
+               else O.capacity_from_factor(cfg.T, cfg.N, cfg.k, cfg.capacity_factor))
+        u, wr = cfg.u(), cfg.w_route()
+        out = O.forward(u, wr, tiny_experts(cfg), k=cfg.k, gate=cfg.gate, capacity=cap)
+        d = out["disp"]
+        rows = O.expert_rows(O.expand(u), d, tiny_experts(cfg), O.swiglu, cfg.k)
+        R = int(d["kept_offsets"][-1])
+        assert sorted(rows) == list(range(R))
+        y_rows = np.stack([rows[r] for r in range(R)])
+        y = O.combine_rows(y_rows, d["row_of"], out["a"])
+        assert O.relative_error(y, out["y"]) < 1e-14
