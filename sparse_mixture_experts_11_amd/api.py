@@ -143,6 +143,9 @@ def moe_forward(desc, weights: Mapping[str, torch.Tensor], u, y, out=None, ws=No
 def moe_forward_traced(desc, weights, u, y, out, ws, events, stream=None) -> None:
     """events: list of torch.cuda.Event(enable_timing=True); recorded between stages."""
     w = _weights(weights)
+    for e in events:
+        if not e.cuda_event:   # torch creates its event handle on first record
+            e.record()
     handles = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
     _check(L.load().moe_forward_traced(ctypes.byref(desc), ctypes.byref(w), _ptr(u), _ptr(y),
                                        _outputs(out), _ptr(ws), ws.numel(), _stream(stream),

@@ -54,6 +54,15 @@ __device__ __forceinline__ T wave_max(T v) {
   return v;
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 values -> packed bf16 pair (hardware round to nearest even).
+__device__ __forceinline__ uint32_t pack_bf16x2_hw(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+
+// ---- precise activations (fp32 path) -------------------------------------
 __device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
 
 // act(g, v): SwiGLU (situ == 0) or SiTU-GLU with caps beta_g, beta_u.
@@ -63,6 +72,42 @@ __device__ __forceinline__ float glu_act(float g, float v, int situ, float bg, f
     v = bu * tanhf(v / bu);
   }
   return silu(g) * v;
+}
+
+// ---- fast activations (bf16 epilogues) ------------------------------------
+// exp(x) = 2^(x log2 e) on the hardware exp2 (about 1 ulp); SiLU(x) =
+// x / (1 + e^-x) with the hardware reciprocal.  tanh(y) for |y| >= 1/16 is
+// (1 - t) / (1 + t), t = e^(-2|y|) <= 0.89, so the subtraction amplifies the
+// error of t by at most 8x (a few 1e-7 relative); below 1/16 the odd Taylor
+// series y - y^3/3 + 2y^5/15 (truncation < 2e-10 relative).  The bf16
+// outputs these feed are rounded to 2^-9 relative, far above these errors.
+__device__ __forceinline__ float fast_exp(float x) {
+  return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
+}
+
+__device__ __forceinline__ float fast_silu(float x) {
+  return x * __builtin_amdgcn_rcpf(1.0f + fast_exp(-x));
+}
+
+__device__ __forceinline__ float fast_tanh(float y) {
+  const float ay = fabsf(y);
+  float r;
+  if (ay < 0.0625f) {
+    const float y2 = y * y;
+    r = ay * (1.0f + y2 * (-0.3333333333f + y2 * 0.1333333333f));
+  } else {
+    const float t = fast_exp(-2.0f * ay);
+    r = (1.0f - t) * __builtin_amdgcn_rcpf(1.0f + t);
+  }
+  return copysignf(r, y);
+}
+
+__device__ __forceinline__ float glu_act_fast(float g, float v, int situ, float bg, float bu) {
+  if (situ) {
+    g = bg * fast_tanh(g * __builtin_amdgcn_rcpf(bg));
+    v = bu * fast_tanh(v * __builtin_amdgcn_rcpf(bu));
+  }
+  return fast_silu(g) * v;
 }
 
 }  // namespace moe

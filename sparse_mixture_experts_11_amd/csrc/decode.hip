@@ -128,10 +128,10 @@ __global__ __launch_bounds__(256) void decode_kernel(
     if constexpr (GLU) {
       float v[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] = glu_act(acc1[tg][r], acc2[tg][r], act, bg, bu);
+      for (int r = 0; r < 4; ++r) v[r] = glu_act_fast(acc1[tg][r], acc2[tg][r], act, bg, bu);
       uint2 pk;
-      pk.x = pack_bf16x2(v[0], v[1]);
-      pk.y = pack_bf16x2(v[2], v[3]);
+      pk.x = pack_bf16x2_hw(v[0], v[1]);
+      pk.y = pack_bf16x2_hw(v[2], v[3]);
       *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(out) + orow * ldo + r4) = pk;
     } else {
       *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(out) + orow * ldo + r4) = acc1[tg];

@@ -4,12 +4,18 @@
 //
 //   C_g[r, n] = sum_k A[arow(g, r), k] * B_g[n, k]      (both operands K-contiguous)
 //
-// One 256x256 output tile per 256-thread workgroup (4 waves of 128x128 on
-// v_mfma_f32_32x32x16_bf16), K in steps of 64 staged through a double-buffered,
-// XOR-swizzled LDS tile (2 x 64 KiB).  A rows are gathered through the
-// dispatch permutation inside the loader, so the expert-sorted copy of the
-// activations is never written.  Tiles are found on the device from the
-// per-group m-tile prefix; surplus workgroups exit, so no host sync is needed.
+// One 256x256 output tile per 256-thread workgroup: 4 waves, each 128x128 on
+// v_mfma_f32_32x32x16_bf16 (16 accumulator blocks in AGPRs).  K advances 64
+// at a time through two 64 KiB LDS stages filled by direct global->LDS
+// buffer loads (no VGPR staging); A rows are gathered through the dispatch
+// permutation by those loads, so the expert-sorted copy of the activations
+// is never written.  Per k-step: three MFMA sub-steps each overlapping the
+// next sub-step's fragment reads, one barrier, and a fourth sub-step that
+// overlaps the next stage's first reads and issues the loads of the stage
+// after it -- a whole k-step of latency cover for every load.
+// Tiles are found on the device from the per-group m-tile prefix and spread
+// over the XCDs in contiguous ranges; surplus workgroups exit, so the host
+// never waits for the routing result.
 //
 // Epilogues: EP_GLU pairs 128 gate columns with the matching 128 up columns in
 // one tile and writes act(gate, up) as bf16 (the hidden of a SwiGLU or
@@ -29,7 +35,8 @@ constexpr int kThreads = 256;
 constexpr int kStageBytes = (BM + BN) * BK * 2;  // 64 KiB
 constexpr int kMSuper = 8;                       // m-tiles per scheduling group
 
-// Byte offset of 16-byte chunk c of row r inside one [256][64] bf16 tile.
+// Byte offset of 16-byte chunk c of row r inside one [256][64] bf16 tile
+// (chunk XOR-swizzled with the row's low three bits).
 __device__ __forceinline__ uint32_t swz(int r, int c) {
   return (uint32_t)(r * 128 + ((c ^ (r & 7)) << 4));
 }
@@ -42,26 +49,27 @@ template <int EPI>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[2 * kStageBytes];
 
-  // ---- which tile: XCD-aware remap (block i runs on XCD i % 8), then
-  // (group, m-super, n, m) order so concurrent tiles on one XCD share rows.
-  const int64_t nb = gridDim.x;
-  const int64_t bid = blockIdx.x;
-  const int64_t L = (bid & 7) * (nb >> 3) + (bid >> 3);
+  // ---- which tile: XCD-aware remap (block i runs on XCD i % 8: each XCD
+  // takes one contiguous eighth of the real tiles), then (group, m-super, n,
+  // m) order so the tiles running together on one XCD share A and B rows.
   const int glu = (EPI == EP_GLU);
   const int64_t NT = glu ? (a.ncols + 127) / 128 : (a.ncols + BN - 1) / BN;
+  const int64_t real_tiles = (a.mode == GM_DENSE)
+                                 ? (int64_t)a.G * ((a.M_dense + BM - 1) / BM) * NT
+                                 : (int64_t)a.tile_start[a.G] * NT;
+  const int64_t bid = blockIdx.x;
+  const int64_t L = (bid & 7) * ((real_tiles + 7) >> 3) + (bid >> 3);
+  if (L >= real_tiles) return;
 
   int g;
   int64_t local, MTg, Mg;
   if (a.mode == GM_DENSE) {
     const int64_t MT = (a.M_dense + BM - 1) / BM;
     g = (int)(L / (MT * NT));
-    if (g >= a.G) return;
     local = L - (int64_t)g * MT * NT;
     MTg = MT;
     Mg = a.M_dense;
   } else {
-    const int64_t total = (int64_t)a.tile_start[a.G] * NT;
-    if (L >= total) return;
     int lo = 0, hi = a.G;  // largest g with tile_start[g] * NT <= L
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
@@ -98,7 +106,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
     if (a.mode == GM_GATHER) arow = a.perm[a.offsets[g] + rr] / a.kslots;
     else if (a.mode == GM_SEGMENT) arow = seg0 + rr;
     else arow = (int64_t)g * a.a_group_rows + rr;
-    aoff[i] = (uint32_t)(arow * a.lda * 2) + (uint32_t)(lc << 4);
+    const int pc = lc ^ (r & 7);  // the chunk this lane's LDS slot holds
+    aoff[i] = (uint32_t)(arow * a.lda * 2) + (uint32_t)(pc << 4);
     int64_t brow;
     if (glu) {
       const int64_t n = n_tile * 128 + (r & 127);
@@ -107,7 +116,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
       const int64_t n = n_tile * BN + r;
       brow = n < a.ncols ? n : a.ncols - 1;
     }
-    boff[i] = (uint32_t)(brow * a.K * 2) + (uint32_t)(lc << 4);
+    boff[i] = (uint32_t)(brow * a.K * 2) + (uint32_t)(pc << 4);
   }
   const uint16_t *Bg = a.B + (int64_t)g * a.strideB;
   const uint16_t *Ug = glu ? a.B2 + (int64_t)g * a.strideB : Bg;
@@ -116,21 +125,22 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bg, bbytes);
   const __amdgpu_buffer_rsrc_t ru = make_rsrc(Ug, bbytes);
 
-  u32x4 ga[8], gb[8];
-  auto gload = [&](int k0) {
+  // Direct global -> LDS loads: instruction i of wave w fills the 1 KiB of
+  // rows 32i + 8w .. +7 and lane l lands at byte 16 l of it.
+  typedef __attribute__((address_space(3))) void *lds_ptr_t;
+  auto gload = [&](int k0, int stage) {
     const uint32_t so = (uint32_t)k0 * 2;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) ga[i] = buf_load16(ra, aoff[i], so);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) gb[i] = buf_load16((glu && i >= 4) ? ru : rb, boff[i], so);
-  };
-  auto lstore = [&](int stage) {
     char *ta = smem + stage * kStageBytes;
     char *tb = ta + BM * BK * 2;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4 *>(ta + swz(lr + 32 * i, lc)) = ga[i];
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(ta + (32 * i + 8 * wave) * 128), 16,
+                                               aoff[i], so, 0, 0);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4 *>(tb + swz(lr + 32 * i, lc)) = gb[i];
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds((glu && i >= 4) ? ru : rb,
+                                               (lds_ptr_t)(tb + (32 * i + 8 * wave) * 128), 16,
+                                               boff[i], so, 0, 0);
   };
 
   // Per-wave fragment rows.
@@ -151,32 +161,90 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int KT = a.K / BK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < KT) gload((kt + 1) * BK);
-    const char *ta = smem + cur * kStageBytes;
-    const char *tb = ta + BM * BK * 2;
+  bf16x8 fa[4], fb[4], na[4], nb[4];
+  auto read_frags = [&](const char *stage_base, int ks, bf16x8 (&xa)[4], bf16x8 (&xb)[4]) {
+    const char *ta = stage_base;
+    const char *tb = stage_base + BM * BK * 2;
+    const int c = ks * 2 + khalf;
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      const int c = ks * 2 + khalf;
-      bf16x8 fa[4], fb[4];
+    for (int i = 0; i < 4; ++i) xa[i] = lds_frag(ta, arow_l[i], c);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) fa[i] = lds_frag(ta, arow_l[i], c);
+    for (int j = 0; j < 4; ++j) xb[j] = lds_frag(tb, brow_l[j], c);
+  };
+  auto mfma16 = [&](const bf16x8 (&xa)[4], const bf16x8 (&xb)[4]) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) fb[j] = lds_frag(tb, brow_l[j], c);
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xb[j], xa[i], acc[i][j], 0, 0, 0);
+  };
+  auto copy_frags = [&]() {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+    for (int i = 0; i < 4; ++i) {
+      fa[i] = na[i];
+      fb[i] = nb[i];
     }
-    if (kt + 1 < KT) lstore(cur ^ 1);
-    __syncthreads();
+  };
+
+  // A sub-step is one fenced scheduling region: the fragment reads for the
+  // next sub-step (and any loads) interleaved with this sub-step's 16 MFMAs.
+#define MOE_SUBSTEP(READ_STMT, EXTRA_STMT, EXTRA_MASK, EXTRA_N)          \
+  do {                                                                  \
+    READ_STMT;                                                          \
+    EXTRA_STMT;                                                         \
+    mfma16(fa, fb);                                                     \
+    _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_) {                  \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                \
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                \
+      __builtin_amdgcn_sched_group_barrier(EXTRA_MASK, EXTRA_N, 0);     \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                \
+    }                                                                   \
+    __builtin_amdgcn_sched_barrier(0);                                  \
+    copy_frags();                                                       \
+  } while (0)
+#define MOE_WAIT_LOADS() asm volatile("s_waitcnt vmcnt(0)" ::: "memory")
+
+  // K >= 128, so KT >= 2.  Stage s lives in LDS buffer s & 1.
+  const int KT = a.K / BK;
+  gload(0, 0);
+  gload(BK, 1);
+  asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  __syncthreads();
+  read_frags(smem, 0, fa, fb);
+  for (int kt = 0; kt + 2 < KT; ++kt) {
+    const char *sc = smem + (kt & 1) * kStageBytes;
+    const char *sn = smem + ((kt + 1) & 1) * kStageBytes;
+    __builtin_amdgcn_sched_barrier(0);
+    MOE_SUBSTEP(read_frags(sc, 1, na, nb), (void)0, 0x000, 0);
+    MOE_SUBSTEP(read_frags(sc, 2, na, nb), (void)0, 0x000, 0);
+    MOE_SUBSTEP(read_frags(sc, 3, na, nb), (void)0, 0x000, 0);
+    MOE_WAIT_LOADS();   // stage kt+1 has landed (this wave's part)
+    __syncthreads();    // ... everyone's part; buffer kt & 1 is free
+    __builtin_amdgcn_sched_barrier(0);
+    MOE_SUBSTEP(read_frags(sn, 0, na, nb), gload((kt + 2) * BK, kt & 1), 0x020, 2);
   }
+  {
+    // k-step KT-2: no stage left to load.
+    const int kt = KT - 2;
+    const char *sc = smem + (kt & 1) * kStageBytes;
+    const char *sn = smem + ((kt + 1) & 1) * kStageBytes;
+    __builtin_amdgcn_sched_barrier(0);
+    MOE_SUBSTEP(read_frags(sc, 1, na, nb), (void)0, 0x000, 0);
+    MOE_SUBSTEP(read_frags(sc, 2, na, nb), (void)0, 0x000, 0);
+    MOE_SUBSTEP(read_frags(sc, 3, na, nb), (void)0, 0x000, 0);
+    MOE_WAIT_LOADS();
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    MOE_SUBSTEP(read_frags(sn, 0, na, nb), (void)0, 0x000, 0);
+    // k-step KT-1.
+    __builtin_amdgcn_sched_barrier(0);
+    MOE_SUBSTEP(read_frags(sn, 1, na, nb), (void)0, 0x000, 0);
+    MOE_SUBSTEP(read_frags(sn, 2, na, nb), (void)0, 0x000, 0);
+    MOE_SUBSTEP(read_frags(sn, 3, na, nb), (void)0, 0x000, 0);
+    mfma16(fa, fb);
+  }
+#undef MOE_WAIT_LOADS
+#undef MOE_SUBSTEP
 
   // ---- epilogue.  Lane holds, for A block i and B block j, output row
   // wm*128 + i*32 + lane%32 and columns 8q + 4*(lane/32) + {0..3}, q = 0..3.
@@ -196,11 +264,11 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
           float v[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            v[e] = glu_act(acc[i][jp][4 * q + e], acc[i][jp + 2][4 * q + e], a.act, a.beta_g,
-                           a.beta_u);
+            v[e] = glu_act_fast(acc[i][jp][4 * q + e], acc[i][jp + 2][4 * q + e], a.act,
+                                a.beta_g, a.beta_u);
           uint2 pk;
-          pk.x = pack_bf16x2(v[0], v[1]);
-          pk.y = pack_bf16x2(v[2], v[3]);
+          pk.x = pack_bf16x2_hw(v[0], v[1]);
+          pk.y = pack_bf16x2_hw(v[2], v[3]);
           *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(a.out) + orow * a.ldo + col) = pk;
         }
       }
@@ -227,8 +295,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
               }
             }
             uint2 pk;
-            pk.x = pack_bf16x2(v[0], v[1]);
-            pk.y = pack_bf16x2(v[2], v[3]);
+            pk.x = pack_bf16x2_hw(v[0], v[1]);
+            pk.y = pack_bf16x2_hw(v[2], v[3]);
             *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(a.out) + orow * a.ldo + col) =
                 pk;
           }

@@ -10,7 +10,8 @@ namespace moe {
 namespace {
 
 constexpr int kRouteBlock = 256;       // 4 waves
-constexpr int kRouteMaxWaves = 1024;   // per launch (sizes the stats partials)
+constexpr int kRouteMaxWaves = 8192;   // wave router, per launch (sizes the stats partials)
+constexpr int kLogitsMaxWaves = 1024;  // top-k over materialised logits (N up to 1024)
 
 template <bool BF16>
 __device__ __forceinline__ void load8(const void *base, int64_t off, float (&x)[8]) {
@@ -233,29 +234,46 @@ __global__ __launch_bounds__(kRouteBlock) void topk_logits_kernel(
   }
 }
 
-// stats = [f(N), P(N), N sum f P, alpha N sum f P]; one block, fixed order.
-__global__ __launch_bounds__(1024) void stats_finalize_kernel(const float *__restrict__ part_p,
-                                                              const int32_t *__restrict__ part_cnt,
-                                                              int waves, int64_t T, int N,
-                                                              float alpha, float *__restrict__ stats) {
+// stats = [f(N), P(N), N sum f P, alpha N sum f P], in two fixed-order passes:
+// one block per expert reduces its per-wave partials, then one block sums
+// f_i P_i over the experts.
+__global__ __launch_bounds__(256) void stats_expert_kernel(const float *__restrict__ part_p,
+                                                           const int32_t *__restrict__ part_cnt,
+                                                           int waves, int64_t T, int N,
+                                                           float *__restrict__ stats) {
+  __shared__ float sp[256];
+  __shared__ int64_t sc[256];
+  const int n = blockIdx.x;
+  float p = 0.f;
+  int64_t c = 0;
+  for (int wv = threadIdx.x; wv < waves; wv += 256) {
+    p += part_p[(int64_t)wv * N + n];
+    c += part_cnt[(int64_t)wv * N + n];
+  }
+  sp[threadIdx.x] = p;
+  sc[threadIdx.x] = c;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if ((int)threadIdx.x < s) {
+      sp[threadIdx.x] += sp[threadIdx.x + s];
+      sc[threadIdx.x] += sc[threadIdx.x + s];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    stats[n] = (float)((double)sc[0] / (double)T);
+    stats[N + n] = sp[0] / (float)T;
+  }
+}
+
+__global__ __launch_bounds__(1024) void stats_total_kernel(int N, float alpha,
+                                                           float *__restrict__ stats) {
   __shared__ float red[1024];
   float local = 0.f;
-  for (int n = threadIdx.x; n < N; n += blockDim.x) {
-    float sp = 0.f;
-    int64_t sc = 0;
-    for (int wv = 0; wv < waves; ++wv) {
-      sp += part_p[(int64_t)wv * N + n];
-      sc += part_cnt[(int64_t)wv * N + n];
-    }
-    const float f = (float)((double)sc / (double)T);
-    const float P = sp / (float)T;
-    stats[n] = f;
-    stats[N + n] = P;
-    local += f * P;
-  }
+  for (int n = threadIdx.x; n < N; n += 1024) local += stats[n] * stats[N + n];
   red[threadIdx.x] = local;
   __syncthreads();
-  for (int s = blockDim.x / 2; s > 0; s >>= 1) {
+  for (int s = 512; s > 0; s >>= 1) {
     if ((int)threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
     __syncthreads();
   }
@@ -289,8 +307,12 @@ hipError_t launch_rw_n(const void *u, const void *W, int64_t T, int d, int N, in
 int route_waves(int64_t T, int N) {
   const int tpw = N <= 8 ? 4 : (N <= 16 ? 2 : 1);
   int64_t groups = (T + tpw - 1) / tpw;
-  if (N > 64) groups = T;
-  int64_t waves = groups < kRouteMaxWaves ? groups : kRouteMaxWaves;
+  int64_t cap = kRouteMaxWaves;
+  if (N > 64) {
+    groups = T;
+    cap = kLogitsMaxWaves;
+  }
+  int64_t waves = groups < cap ? groups : cap;
   waves = (waves + 3) / 4 * 4;  // whole blocks of 4 waves
   return (int)waves;
 }
@@ -323,8 +345,9 @@ hipError_t launch_topk_logits(const float *logits, int64_t T, int N, int k, int 
 
 hipError_t launch_stats_finalize(const float *part_p, const int32_t *part_cnt, int waves,
                                  int64_t T, int N, float alpha, float *stats, hipStream_t st) {
-  hipLaunchKernelGGL(stats_finalize_kernel, dim3(1), dim3(1024), 0, st, part_p, part_cnt, waves,
-                     T, N, alpha, stats);
+  hipLaunchKernelGGL(stats_expert_kernel, dim3(N), dim3(256), 0, st, part_p, part_cnt, waves, T,
+                     N, stats);
+  hipLaunchKernelGGL(stats_total_kernel, dim3(1), dim3(1024), 0, st, N, alpha, stats);
   return hipGetLastError();
 }
 
