@@ -40,6 +40,14 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t v
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
 }
 
+// Workgroup barrier that leaves vector-memory loads in flight: LDS traffic
+// is drained (lgkmcnt 0) but, unlike __syncthreads(), no vmcnt(0) is forced,
+// so callers wait for exactly the loads they need with s_waitcnt vmcnt(N).
+// The memory clobber keeps the compiler from moving memory accesses across.
+__device__ __forceinline__ void barrier_keep_loads() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 template <typename T>
 __device__ __forceinline__ T wave_sum(T v) {
 #pragma unroll

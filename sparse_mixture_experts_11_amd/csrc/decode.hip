@@ -19,7 +19,10 @@ namespace {
 
 constexpr int RB = 16;      // weight rows per workgroup
 constexpr int kWaves = 4;   // split-K ways
-constexpr int U = 4;        // k-steps of 32 per unrolled iteration
+// k-steps of 32 per unrolled iteration: gate/up streams two matrices, so 4
+// steps already keep 8 KiB per wave in flight; down streams one, so 8.
+template <bool GLU>
+constexpr int unroll_of() { return GLU ? 4 : 8; }
 
 template <bool GLU, int TG>
 __global__ __launch_bounds__(256) void decode_kernel(
@@ -61,6 +64,7 @@ __global__ __launch_bounds__(256) void decode_kernel(
     acc2[tg] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   const bf16x8 zero = {};
+  constexpr int U = unroll_of<GLU>();
   int k = 0;
   for (; k + 32 * U <= Kw; k += 32 * U) {
     bf16x8 a1[U], a2[U], b[TG][U];

@@ -6,13 +6,16 @@
 //
 // One 256x256 output tile per 256-thread workgroup: 4 waves, each 128x128 on
 // v_mfma_f32_32x32x16_bf16 (16 accumulator blocks in AGPRs).  K advances 64
-// at a time through two 64 KiB LDS stages filled by direct global->LDS
-// buffer loads (no VGPR staging); A rows are gathered through the dispatch
-// permutation by those loads, so the expert-sorted copy of the activations
-// is never written.  Per k-step: three MFMA sub-steps each overlapping the
-// next sub-step's fragment reads, one barrier, and a fourth sub-step that
-// overlaps the next stage's first reads and issues the loads of the stage
-// after it -- a whole k-step of latency cover for every load.
+// at a time.  A (the activations, mostly L2 hits) is double-buffered and B
+// (the weights, streamed) sits in a ring of three 32 KiB LDS stages -- 160 KiB
+// in all -- filled by direct global->LDS buffer loads (no VGPR staging); A
+// rows are gathered through the dispatch permutation by those loads, so the
+// expert-sorted copy of the activations is never written.  Per k-step: three
+// MFMA sub-steps, each overlapping the next sub-step's fragment reads, one
+// barrier, and a fourth sub-step that overlaps the next stage's first reads.
+// The loads are spread over the k-step (B two stages ahead in sub-steps 0-1,
+// A one stage ahead in sub-step 3) so the address unit works alongside the
+// MFMAs instead of in one burst after the barrier.
 // Tiles are found on the device from the per-group m-tile prefix and spread
 // over the XCDs in contiguous ranges; surplus workgroups exit, so the host
 // never waits for the routing result.
@@ -32,7 +35,8 @@ constexpr int BM = 256;
 constexpr int BN = 256;
 constexpr int BK = 64;
 constexpr int kThreads = 256;
-constexpr int kStageBytes = (BM + BN) * BK * 2;  // 64 KiB
+constexpr int kABytes = BM * BK * 2;   // 32 KiB per A stage
+constexpr int kBBytes = BN * BK * 2;   // 32 KiB per B stage
 constexpr int kMSuper = 8;                       // m-tiles per scheduling group
 
 // Byte offset of 16-byte chunk c of row r inside one [256][64] bf16 tile
@@ -47,7 +51,9 @@ __device__ __forceinline__ bf16x8 lds_frag(const char *tile, int r, int c) {
 
 template <int EPI>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * kStageBytes];
+  // A (activations, L2-resident) double-buffered; B (weights, streamed) in a
+  // ring of three so its loads get two k-steps of cover: 160 KiB in all.
+  __shared__ __attribute__((aligned(16))) char smem[2 * kABytes + 3 * kBBytes];
 
   // ---- which tile: XCD-aware remap (block i runs on XCD i % 8: each XCD
   // takes one contiguous eighth of the real tiles), then (group, m-super, n,
@@ -128,19 +134,24 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
   // Direct global -> LDS loads: instruction i of wave w fills the 1 KiB of
   // rows 32i + 8w .. +7 and lane l lands at byte 16 l of it.
   typedef __attribute__((address_space(3))) void *lds_ptr_t;
-  auto gload = [&](int k0, int stage) {
+  auto aload = [&](int k0, int buf) {
     const uint32_t so = (uint32_t)k0 * 2;
-    char *ta = smem + stage * kStageBytes;
-    char *tb = ta + BM * BK * 2;
+    char *ta = smem + buf * kABytes;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(ta + (32 * i + 8 * wave) * 128), 16,
                                                aoff[i], so, 0, 0);
+  };
+  auto bload = [&](int k0, int buf, int half) {
+    const uint32_t so = (uint32_t)k0 * 2;
+    char *tb = smem + 2 * kABytes + buf * kBBytes;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int j = 0; j < 4; ++j) {
+      const int i = 4 * half + j;
       __builtin_amdgcn_raw_ptr_buffer_load_lds((glu && i >= 4) ? ru : rb,
                                                (lds_ptr_t)(tb + (32 * i + 8 * wave) * 128), 16,
                                                boff[i], so, 0, 0);
+    }
   };
 
   // Per-wave fragment rows.
@@ -162,9 +173,9 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   bf16x8 fa[4], fb[4], na[4], nb[4];
-  auto read_frags = [&](const char *stage_base, int ks, bf16x8 (&xa)[4], bf16x8 (&xb)[4]) {
-    const char *ta = stage_base;
-    const char *tb = stage_base + BM * BK * 2;
+  auto read_frags = [&](int kt, int ks, bf16x8 (&xa)[4], bf16x8 (&xb)[4]) {
+    const char *ta = smem + (kt & 1) * kABytes;
+    const char *tb = smem + 2 * kABytes + (kt % 3) * kBBytes;
     const int c = ks * 2 + khalf;
 #pragma unroll
     for (int i = 0; i < 4; ++i) xa[i] = lds_frag(ta, arow_l[i], c);
@@ -204,43 +215,45 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
   } while (0)
 #define MOE_WAIT_LOADS() asm volatile("s_waitcnt vmcnt(0)" ::: "memory")
 
-  // K >= 128, so KT >= 2.  Stage s lives in LDS buffer s & 1.
+  // K >= 128, so KT >= 2.  Stage s: A in buffer s & 1, B in buffer s % 3.
+  // Loads are spread over the k-step so the address unit works alongside the
+  // MFMAs: B(kt+2) during sub-steps 0-1 of step kt (buffer (kt+2) % 3 was
+  // released by the barrier ending step kt-1), A(kt+2) during sub-step 3
+  // after step kt's barrier.  Before a barrier only B(kt+2) may still fly.
   const int KT = a.K / BK;
-  gload(0, 0);
-  gload(BK, 1);
-  asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-  __syncthreads();
-  read_frags(smem, 0, fa, fb);
+  aload(0, 0);
+  bload(0, 0, 0);
+  bload(0, 0, 1);
+  aload(BK, 1);
+  bload(BK, 1, 0);
+  bload(BK, 1, 1);
+  asm volatile("s_waitcnt vmcnt(16)" ::: "memory");  // stage 0 landed
+  barrier_keep_loads();
+  read_frags(0, 0, fa, fb);
   for (int kt = 0; kt + 2 < KT; ++kt) {
-    const char *sc = smem + (kt & 1) * kStageBytes;
-    const char *sn = smem + ((kt + 1) & 1) * kStageBytes;
     __builtin_amdgcn_sched_barrier(0);
-    MOE_SUBSTEP(read_frags(sc, 1, na, nb), (void)0, 0x000, 0);
-    MOE_SUBSTEP(read_frags(sc, 2, na, nb), (void)0, 0x000, 0);
-    MOE_SUBSTEP(read_frags(sc, 3, na, nb), (void)0, 0x000, 0);
-    MOE_WAIT_LOADS();   // stage kt+1 has landed (this wave's part)
-    __syncthreads();    // ... everyone's part; buffer kt & 1 is free
+    MOE_SUBSTEP(read_frags(kt, 1, na, nb), bload((kt + 2) * BK, (kt + 2) % 3, 0), 0x020, 1);
+    MOE_SUBSTEP(read_frags(kt, 2, na, nb), bload((kt + 2) * BK, (kt + 2) % 3, 1), 0x020, 1);
+    MOE_SUBSTEP(read_frags(kt, 3, na, nb), (void)0, 0x000, 0);
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");  // stage kt+1 landed
+    barrier_keep_loads();
     __builtin_amdgcn_sched_barrier(0);
-    MOE_SUBSTEP(read_frags(sn, 0, na, nb), gload((kt + 2) * BK, kt & 1), 0x020, 2);
+    MOE_SUBSTEP(read_frags(kt + 1, 0, na, nb), aload((kt + 2) * BK, kt & 1), 0x020, 1);
   }
   {
-    // k-step KT-2: no stage left to load.
     const int kt = KT - 2;
-    const char *sc = smem + (kt & 1) * kStageBytes;
-    const char *sn = smem + ((kt + 1) & 1) * kStageBytes;
     __builtin_amdgcn_sched_barrier(0);
-    MOE_SUBSTEP(read_frags(sc, 1, na, nb), (void)0, 0x000, 0);
-    MOE_SUBSTEP(read_frags(sc, 2, na, nb), (void)0, 0x000, 0);
-    MOE_SUBSTEP(read_frags(sc, 3, na, nb), (void)0, 0x000, 0);
+    MOE_SUBSTEP(read_frags(kt, 1, na, nb), (void)0, 0x000, 0);
+    MOE_SUBSTEP(read_frags(kt, 2, na, nb), (void)0, 0x000, 0);
+    MOE_SUBSTEP(read_frags(kt, 3, na, nb), (void)0, 0x000, 0);
     MOE_WAIT_LOADS();
-    __syncthreads();
+    barrier_keep_loads();
     __builtin_amdgcn_sched_barrier(0);
-    MOE_SUBSTEP(read_frags(sn, 0, na, nb), (void)0, 0x000, 0);
-    // k-step KT-1.
+    MOE_SUBSTEP(read_frags(kt + 1, 0, na, nb), (void)0, 0x000, 0);
     __builtin_amdgcn_sched_barrier(0);
-    MOE_SUBSTEP(read_frags(sn, 1, na, nb), (void)0, 0x000, 0);
-    MOE_SUBSTEP(read_frags(sn, 2, na, nb), (void)0, 0x000, 0);
-    MOE_SUBSTEP(read_frags(sn, 3, na, nb), (void)0, 0x000, 0);
+    MOE_SUBSTEP(read_frags(kt + 1, 1, na, nb), (void)0, 0x000, 0);
+    MOE_SUBSTEP(read_frags(kt + 1, 2, na, nb), (void)0, 0x000, 0);
+    MOE_SUBSTEP(read_frags(kt + 1, 3, na, nb), (void)0, 0x000, 0);
     mfma16(fa, fb);
   }
 #undef MOE_WAIT_LOADS

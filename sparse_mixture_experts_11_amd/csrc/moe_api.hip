@@ -193,12 +193,21 @@ hipError_t do_dispatch(const moe_desc_t &d, const Layout &L, const int32_t *idx,
                          row_of, drop, region<int32_t>(ws, L.blk_counts), st);
 }
 
-// Grouped-GEMM prefill path needs the m-tile prefix of the kept counts.
-bool ffn_uses_gemm(const moe_desc_t &d) { return bf16_path(d) && !decode_path(d); }
+// Expert-projection kernel family for a layer: fp32 on the vector ALUs,
+// decode-sized T streams the selected experts' weights, otherwise the tiled
+// grouped GEMM.
+enum FfnPath { FFN_SIMT, FFN_DECODE, FFN_TILED };
 
+FfnPath ffn_path(const moe_desc_t &d) {
+  if (!bf16_path(d)) return FFN_SIMT;
+  if (decode_path(d)) return FFN_DECODE;
+  return FFN_TILED;
+}
+
+// The tiled path finds its work from a per-expert prefix of m-tiles.
 hipError_t do_tile_prefix(const moe_desc_t &d, const Layout &L, const int32_t *kept_offsets,
                           void *ws, hipStream_t st) {
-  if (!ffn_uses_gemm(d)) return hipSuccess;
+  if (ffn_path(d) != FFN_TILED) return hipSuccess;
   return launch_tile_prefix(kept_offsets, d.N, region<int32_t>(ws, L.tile_start), st);
 }
 

@@ -12,6 +12,7 @@ namespace {
 constexpr int kRouteBlock = 256;       // 4 waves
 constexpr int kRouteMaxWaves = 8192;   // wave router, per launch (sizes the stats partials)
 constexpr int kLogitsMaxWaves = 1024;  // top-k over materialised logits (N up to 1024)
+constexpr int kRouteSmallT = 256;      // at or below: one block per token (N <= 64)
 
 template <bool BF16>
 __device__ __forceinline__ void load8(const void *base, int64_t off, float (&x)[8]) {
@@ -137,6 +138,54 @@ __global__ __launch_bounds__(kRouteBlock) void route_wave_kernel(
   if (part_p != nullptr && lane < N) {
     part_p[(int64_t)wave * N + lane] = acc_p;
     part_cnt[(int64_t)wave * N + lane] = acc_cnt;
+  }
+}
+
+// Small T: one 4-wave block per token.  Each thread accumulates its share of
+// the d-loop for every expert; the 4 wave partials meet in LDS and wave 0
+// adds them in a fixed order, then selects.  Stats partials are per token.
+template <bool UB, bool WB, int NMAX>
+__global__ __launch_bounds__(kRouteBlock) void route_small_kernel(
+    const void *__restrict__ u, const void *__restrict__ W, int64_t T, int d, int N, int k,
+    int gate, int32_t *__restrict__ idx, float *__restrict__ w, float *__restrict__ part_p,
+    int32_t *__restrict__ part_cnt) {
+  __shared__ float red[kRouteBlock / 64][NMAX];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t t = blockIdx.x;
+  float acc[NMAX];
+#pragma unroll
+  for (int n = 0; n < NMAX; ++n) acc[n] = 0.f;
+  for (int base = threadIdx.x * 8; base < d; base += kRouteBlock * 8) {
+    float x[8];
+    load8<UB>(u, t * d + base, x);
+#pragma unroll
+    for (int n = 0; n < NMAX; ++n) {
+      if (n < N) {
+        float wv[8];
+        load8<WB>(W, (int64_t)n * d + base, wv);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[n] = fmaf(x[j], wv[j], acc[n]);
+      }
+    }
+  }
+#pragma unroll
+  for (int n = 0; n < NMAX; ++n) {
+    const float v = (n < N) ? wave_sum(acc[n]) : 0.f;
+    if (lane == 0) red[wave][n] = v;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  float z[NMAX];
+#pragma unroll
+  for (int n = 0; n < NMAX; ++n)
+    z[n] = ((red[0][n] + red[1][n]) + red[2][n]) + red[3][n];
+  float acc_p = 0.f;
+  int acc_cnt = 0;
+  select_and_write<NMAX>(z, N, k, gate, t, lane, idx, w, acc_p, acc_cnt);
+  if (part_p != nullptr && lane < N) {
+    part_p[t * N + lane] = acc_p;
+    part_cnt[t * N + lane] = acc_cnt;
   }
 }
 
@@ -293,9 +342,23 @@ hipError_t launch_rw(const void *u, const void *W, int64_t T, int d, int N, int 
   return hipGetLastError();
 }
 
+template <bool UB, bool WB, int NMAX>
+hipError_t launch_rs(const void *u, const void *W, int64_t T, int d, int N, int k, int gate,
+                     int32_t *idx, float *w, float *pp, int32_t *pc, hipStream_t st) {
+  hipLaunchKernelGGL((route_small_kernel<UB, WB, NMAX>), dim3((unsigned)T), dim3(kRouteBlock), 0,
+                     st, u, W, T, d, N, k, gate, idx, w, pp, pc);
+  return hipGetLastError();
+}
+
 template <bool UB, bool WB>
 hipError_t launch_rw_n(const void *u, const void *W, int64_t T, int d, int N, int k, int gate,
                        int32_t *idx, float *w, float *pp, int32_t *pc, hipStream_t st) {
+  if (T <= kRouteSmallT) {
+    if (N <= 8) return launch_rs<UB, WB, 8>(u, W, T, d, N, k, gate, idx, w, pp, pc, st);
+    if (N <= 16) return launch_rs<UB, WB, 16>(u, W, T, d, N, k, gate, idx, w, pp, pc, st);
+    if (N <= 32) return launch_rs<UB, WB, 32>(u, W, T, d, N, k, gate, idx, w, pp, pc, st);
+    return launch_rs<UB, WB, 64>(u, W, T, d, N, k, gate, idx, w, pp, pc, st);
+  }
   if (N <= 8) return launch_rw<UB, WB, 8, 4>(u, W, T, d, N, k, gate, idx, w, pp, pc, st);
   if (N <= 16) return launch_rw<UB, WB, 16, 2>(u, W, T, d, N, k, gate, idx, w, pp, pc, st);
   if (N <= 32) return launch_rw<UB, WB, 32, 1>(u, W, T, d, N, k, gate, idx, w, pp, pc, st);
@@ -305,6 +368,7 @@ hipError_t launch_rw_n(const void *u, const void *W, int64_t T, int d, int N, in
 }  // namespace
 
 int route_waves(int64_t T, int N) {
+  if (N <= 64 && T <= kRouteSmallT) return (int)T;  // one partial row per token
   const int tpw = N <= 8 ? 4 : (N <= 16 ? 2 : 1);
   int64_t groups = (T + tpw - 1) / tpw;
   int64_t cap = kRouteMaxWaves;

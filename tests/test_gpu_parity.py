@@ -34,9 +34,13 @@ CASES = {
     "mixtral_small_t37_decode": MIX_S.with_(T=37),
     "mixtral_small_t64_decode": MIX_S.with_(T=64),
     "mixtral_small_t65": MIX_S.with_(T=65),
+    "mixtral_small_t3000_tiled": MIX_S.with_(T=3000),
     "switch_small_t2000": C.SWITCH_SKEWED.with_(T=2000, d=1024, h=1024),
     "switch_small_t48_decode": C.SWITCH_SKEWED.with_(T=48, d=1024, h=1024),
+    "switch_small_t6000_tiled": C.SWITCH_SKEWED.with_(T=6000, d=1024, h=1024),
     "latent_small_t700": C.LATENT.with_(T=700, d=512, l=384, h=256, N=96, k=6, h_shared=256),
+    "latent_small_stream_t900": C.LATENT.with_(T=900, d=512, l=512, h=256, N=96, k=6,
+                                               h_shared=256),
     "latent_small_wave_router": C.LATENT.with_(T=300, d=512, l=256, h=256, N=40, k=4,
                                                h_shared=128, n_shared=1),
     "latent_small_decode_t20": C.LATENT.with_(T=20, d=512, l=384, h=256, N=96, k=6, h_shared=256),
@@ -197,8 +201,11 @@ def test_unselected_expert_perturbation(name):
 # Stage tests: each entry point fed oracle-made inputs
 # ---------------------------------------------------------------------------
 
+# Expert-kernel families: SIMT (fp32), decode (T <= 64), tiled grouped GEMM
+# (otherwise; one and several m-tiles per expert).
 STAGE_CASES = ["tiny", "tiny_planted_c4", "mcu_t4096", "mixtral_small_t1000",
-               "mixtral_small_t37_decode", "switch_small_t2000", "latent_small_t700"]
+               "mixtral_small_t3000_tiled", "mixtral_small_t37_decode", "switch_small_t2000",
+               "switch_small_t6000_tiled", "latent_small_t700", "latent_small_stream_t900"]
 
 
 @pytest.mark.parametrize("name", STAGE_CASES)
