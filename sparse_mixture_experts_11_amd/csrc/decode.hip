@@ -3,10 +3,11 @@
 // the MoE deployment gap", section 二: experts are stored grouped and looked
 // up by index, and only the selected experts' weights are read).
 //
-// Each workgroup owns 16 weight rows of one expert and all K; its 4 waves
+// Each workgroup owns 32 weight rows of one expert and all K; its 4 waves
 // split K, stream the rows straight from HBM into MFMA operands
-// (v_mfma_f32_16x16x32_bf16: 16 weight rows x up to 16 tokens per group),
-// and reduce their partial sums through LDS in a fixed order.  Experts with
+// (v_mfma_f32_16x16x32_bf16: 16 weight rows x up to 16 tokens per group; each
+// token fragment feeds both 16-row blocks of the wave), and reduce their
+// partial sums through LDS in a fixed order.  Experts with
 // no kept token exit before touching their weights.
 //   GLU = true : hid[row] = act(W_gate x, W_up x), x rows gathered via perm
 //   GLU = false: y_perm[row] = W_down hid[row], fp32
@@ -17,10 +18,11 @@ namespace moe {
 
 namespace {
 
-constexpr int RB = 16;      // weight rows per workgroup
-constexpr int kWaves = 4;   // split-K ways
-// k-steps of 32 per unrolled iteration: gate/up streams two matrices, so 4
-// steps already keep 8 KiB per wave in flight; down streams one, so 8.
+constexpr int NRB = 2;          // 16-row weight blocks per wave (token fragments reused NRB x)
+constexpr int RB = 16 * NRB;    // weight rows per workgroup
+constexpr int kWaves = 4;       // split-K ways
+// k-steps of 32 per unrolled iteration (weight bytes in flight per wave:
+// 2 KiB x NRB x matrices x U).
 template <bool GLU>
 constexpr int unroll_of() { return GLU ? 4 : 8; }
 
@@ -30,7 +32,8 @@ __global__ __launch_bounds__(256) void decode_kernel(
     const int32_t *__restrict__ offsets, const int32_t *__restrict__ kept_offsets, int kslots,
     const uint16_t *__restrict__ W1, const uint16_t *__restrict__ W2, int64_t wrows, int K,
     int act, float bg, float bu, void *__restrict__ out, int64_t ldo) {
-  __shared__ f32x4 red[kWaves - 1][GLU ? 2 : 1][TG][64];
+  constexpr int NM = GLU ? 2 : 1;
+  __shared__ f32x4 red[kWaves - 1][NM][NRB][TG][64];
   const int e = blockIdx.y;
   const int M = kept_offsets[e + 1] - kept_offsets[e];
   if (M == 0) return;
@@ -44,6 +47,7 @@ __global__ __launch_bounds__(256) void decode_kernel(
 
   const uint16_t *w1 = W1 + ((int64_t)e * wrows + row0 + li) * K + kb + kq;
   const uint16_t *w2 = GLU ? W2 + ((int64_t)e * wrows + row0 + li) * K + kb + kq : nullptr;
+  const int64_t rbs = (int64_t)16 * K;  // next 16-row block
   const uint16_t *xr[TG];
   bool xv[TG];
 #pragma unroll
@@ -57,22 +61,25 @@ __global__ __launch_bounds__(256) void decode_kernel(
   }
   const int ngroups = (M + 15) / 16;
 
-  f32x4 acc1[TG], acc2[TG];
+  f32x4 acc[NM][NRB][TG];
 #pragma unroll
-  for (int tg = 0; tg < TG; ++tg) {
-    acc1[tg] = f32x4{0.f, 0.f, 0.f, 0.f};
-    acc2[tg] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int m = 0; m < NM; ++m)
+#pragma unroll
+    for (int r = 0; r < NRB; ++r)
+#pragma unroll
+      for (int tg = 0; tg < TG; ++tg) acc[m][r][tg] = f32x4{0.f, 0.f, 0.f, 0.f};
   const bf16x8 zero = {};
   constexpr int U = unroll_of<GLU>();
   int k = 0;
   for (; k + 32 * U <= Kw; k += 32 * U) {
-    bf16x8 a1[U], a2[U], b[TG][U];
+    bf16x8 a[NM][NRB][U], b[TG][U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      a1[u] = *reinterpret_cast<const bf16x8 *>(w1 + k + 32 * u);
-      if (GLU) a2[u] = *reinterpret_cast<const bf16x8 *>(w2 + k + 32 * u);
-    }
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int r = 0; r < NRB; ++r) {
+        a[0][r][u] = *reinterpret_cast<const bf16x8 *>(w1 + r * rbs + k + 32 * u);
+        if (GLU) a[NM - 1][r][u] = *reinterpret_cast<const bf16x8 *>(w2 + r * rbs + k + 32 * u);
+      }
 #pragma unroll
     for (int tg = 0; tg < TG; ++tg)
 #pragma unroll
@@ -83,24 +90,33 @@ __global__ __launch_bounds__(256) void decode_kernel(
     for (int tg = 0; tg < TG; ++tg) {
       if (tg < ngroups) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          acc1[tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[u], b[tg][u], acc1[tg], 0, 0, 0);
-          if (GLU)
-            acc2[tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2[u], b[tg][u], acc2[tg], 0, 0, 0);
-        }
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int m = 0; m < NM; ++m)
+#pragma unroll
+            for (int r = 0; r < NRB; ++r)
+              acc[m][r][tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[m][r][u], b[tg][u],
+                                                                     acc[m][r][tg], 0, 0, 0);
       }
     }
   }
   for (; k < Kw; k += 32) {
-    const bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(w1 + k);
-    bf16x8 a2 = zero;
-    if (GLU) a2 = *reinterpret_cast<const bf16x8 *>(w2 + k);
+    bf16x8 a[NM][NRB];
+#pragma unroll
+    for (int r = 0; r < NRB; ++r) {
+      a[0][r] = *reinterpret_cast<const bf16x8 *>(w1 + r * rbs + k);
+      if (GLU) a[NM - 1][r] = *reinterpret_cast<const bf16x8 *>(w2 + r * rbs + k);
+    }
 #pragma unroll
     for (int tg = 0; tg < TG; ++tg) {
       if (tg < ngroups) {
         const bf16x8 b = xv[tg] ? *reinterpret_cast<const bf16x8 *>(xr[tg] + k) : zero;
-        acc1[tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b, acc1[tg], 0, 0, 0);
-        if (GLU) acc2[tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2, b, acc2[tg], 0, 0, 0);
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+          for (int r = 0; r < NRB; ++r)
+            acc[m][r][tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[m][r], b, acc[m][r][tg], 0,
+                                                                   0, 0);
       }
     }
   }
@@ -108,37 +124,43 @@ __global__ __launch_bounds__(256) void decode_kernel(
   // Fixed-order split-K reduction: wave 0 adds waves 1, 2, 3 in turn.
   if (wave > 0) {
 #pragma unroll
-    for (int tg = 0; tg < TG; ++tg) {
-      red[wave - 1][0][tg][lane] = acc1[tg];
-      if (GLU) red[wave - 1][GLU ? 1 : 0][tg][lane] = acc2[tg];
-    }
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int r = 0; r < NRB; ++r)
+#pragma unroll
+        for (int tg = 0; tg < TG; ++tg) red[wave - 1][m][r][tg][lane] = acc[m][r][tg];
   }
   __syncthreads();
   if (wave != 0) return;
 #pragma unroll
   for (int w = 0; w < kWaves - 1; ++w)
 #pragma unroll
-    for (int tg = 0; tg < TG; ++tg) {
-      acc1[tg] += red[w][0][tg][lane];
-      if (GLU) acc2[tg] += red[w][GLU ? 1 : 0][tg][lane];
-    }
-  // Lane holds rows row0 + 4*(lane/16) + {0..3} of token tg*16 + lane%16.
-  const int r4 = row0 + 4 * (lane >> 4);
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int r = 0; r < NRB; ++r)
+#pragma unroll
+        for (int tg = 0; tg < TG; ++tg) acc[m][r][tg] += red[w][m][r][tg][lane];
+  // Lane holds rows row0 + 16r + 4*(lane/16) + {0..3} of token tg*16 + lane%16.
 #pragma unroll
   for (int tg = 0; tg < TG; ++tg) {
     const int j = tg * 16 + li;
     if (tg >= ngroups || j >= M) continue;
     const int64_t orow = kept_offsets[e] + j;
-    if constexpr (GLU) {
-      float v[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] = glu_act_fast(acc1[tg][r], acc2[tg][r], act, bg, bu);
-      uint2 pk;
-      pk.x = pack_bf16x2_hw(v[0], v[1]);
-      pk.y = pack_bf16x2_hw(v[2], v[3]);
-      *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(out) + orow * ldo + r4) = pk;
-    } else {
-      *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(out) + orow * ldo + r4) = acc1[tg];
+    for (int r = 0; r < NRB; ++r) {
+      const int col = row0 + 16 * r + 4 * (lane >> 4);
+      if constexpr (GLU) {
+        float v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = glu_act_fast(acc[0][r][tg][q], acc[1][r][tg][q], act, bg, bu);
+        uint2 pk;
+        pk.x = pack_bf16x2_hw(v[0], v[1]);
+        pk.y = pack_bf16x2_hw(v[2], v[3]);
+        *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(out) + orow * ldo + col) = pk;
+      } else {
+        *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(out) + orow * ldo + col) =
+            acc[0][r][tg];
+      }
     }
   }
 }
