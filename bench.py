@@ -35,6 +35,9 @@ def parse():
                    help="second workload reported beside the main one ('' to skip)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-tokens", type=int, default=384)
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run a plain 1 GiB device-to-device copy (3 times) so that "
+                        "hardware byte counters can be scaled against a known size")
     return p.parse_args()
 
 
@@ -51,6 +54,24 @@ def algorithmic(cfg, counts_kept):
     down_bytes = touched * cfg.h * xw * wb
     return {"rows": R, "gu_flops": gu_flops, "down_flops": down_flops, "gu_bytes": gu_bytes,
             "down_bytes": down_bytes, "touched": touched}
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the workload's dominant kernel, from the
+    rocprofv3 counter runs recorded in profiles/hbm_traffic.json, or None when
+    there is no record or the kernel source changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)["workloads"].get(workload)
+    if rec is None:
+        return None
+    with open(os.path.join(ROOT, rec["source"]), "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != rec["source_sha256"]:
+            return None
+    return rec["bytes"]
 
 
 def run_workload(cfg, steps, warmup):
@@ -141,12 +162,13 @@ def main():
     if intensity < ridge:
         achieved = alg["gu_bytes"] / t / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": achieved / PEAK_HBM_GBS, "traffic": None, "kernel": kernel}
+                "frac": achieved / PEAK_HBM_GBS, "traffic": measured_traffic(cfg.name),
+                "kernel": kernel}
     else:
         achieved = alg["gu_flops"] / t / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
-                "kernel": kernel}
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                "traffic": measured_traffic(cfg.name), "kernel": kernel}
     roof["algorithmic_per_launch"] = {"flops": alg["gu_flops"], "bytes": alg["gu_bytes"],
                                       "rows": alg["rows"], "experts_touched": alg["touched"]}
     line = {
@@ -178,6 +200,13 @@ def main():
             / 1e9 / PEAK_HBM_GBS,
         }
         del rd
+    if args.copy_calibration:
+        src = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda")   # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(cfg, min(args.cpu_sample_tokens, cfg.T))
