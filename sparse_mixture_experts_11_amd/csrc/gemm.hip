@@ -4,14 +4,16 @@
 //
 //   C_g[r, n] = sum_k A[arow(g, r), k] * B_g[n, k]      (both operands K-contiguous)
 //
-// One 256x256 output tile per 256-thread workgroup: 4 waves, each 128x128 on
-// v_mfma_f32_32x32x16_bf16 (16 accumulator blocks in AGPRs).  K advances 64
-// at a time.  A (the activations, mostly L2 hits) is double-buffered and B
-// (the weights, streamed) sits in a ring of three 32 KiB LDS stages -- 160 KiB
-// in all -- filled by direct global->LDS buffer loads (no VGPR staging); A
+// One 256x256 output tile per 512-thread workgroup: 8 waves, two per SIMD,
+// each 128x64 on v_mfma_f32_32x32x16_bf16 (8 accumulator blocks, 223 VGPRs
+// so two waves fit a SIMD).  The second wave on a SIMD issues MFMAs while its
+// sibling waits on a load issue or the barrier.  K advances 64 at a time.
+// A (the activations, mostly L2 hits) is double-buffered and B (the weights,
+// streamed) sits in a ring of three 32 KiB LDS stages -- 160 KiB in all --
+// filled by direct global->LDS buffer loads (no VGPR staging); A
 // rows are gathered through the dispatch permutation by those loads, so the
 // expert-sorted copy of the activations is never written.  Per k-step: three
-// MFMA sub-steps, each overlapping the next sub-step's fragment reads, one
+// 8-MFMA sub-steps, each overlapping the next sub-step's fragment reads, one
 // barrier, and a fourth sub-step that overlaps the next stage's first reads.
 // The loads are spread over the k-step (B two stages ahead in sub-steps 0-1,
 // A one stage ahead in sub-step 3) so the address unit works alongside the
@@ -34,7 +36,7 @@ namespace {
 constexpr int BM = 256;
 constexpr int BN = 256;
 constexpr int BK = 64;
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;  // 8 waves: two per SIMD
 constexpr int kABytes = BM * BK * 2;   // 32 KiB per A stage
 constexpr int kBBytes = BN * BK * 2;   // 32 KiB per B stage
 constexpr int kMSuper = 8;                       // m-tiles per scheduling group
@@ -63,8 +65,13 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
   const int64_t real_tiles = (a.mode == GM_DENSE)
                                  ? (int64_t)a.G * ((a.M_dense + BM - 1) / BM) * NT
                                  : (int64_t)a.tile_start[a.G] * NT;
+  // The grid is an upper bound on the tile count, so it can exceed 8 x per;
+  // the remap is one-to-one only on blocks 0 .. 8 x per - 1, and any block
+  // past that would land on a tile of the next XCD's range a second time.
   const int64_t bid = blockIdx.x;
-  const int64_t L = (bid & 7) * ((real_tiles + 7) >> 3) + (bid >> 3);
+  const int64_t per = (real_tiles + 7) >> 3;
+  if ((bid >> 3) >= per) return;
+  const int64_t L = (bid & 7) * per + (bid >> 3);
   if (L >= real_tiles) return;
 
   int g;
@@ -97,16 +104,16 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
   const int lc = tid & 7;    // loader chunk
-  const int lr = tid >> 3;   // loader base row (0..31)
+  const int lr = tid >> 3;   // loader base row (0..63)
 
   // ---- loader offsets (bytes), fixed over the K loop.
   const int64_t seg0 = (a.mode == GM_DENSE) ? 0 : a.kept_offsets[g];
-  uint32_t aoff[8], boff[8];
+  uint32_t aoff[4], boff[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = lr + 32 * i;
+  for (int i = 0; i < 4; ++i) {
+    const int r = lr + 64 * i;
     const int64_t rr = m0 + (r < mrows ? r : mrows - 1);
     int64_t arow;
     if (a.mode == GM_GATHER) arow = a.perm[a.offsets[g] + rr] / a.kslots;
@@ -132,81 +139,79 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
   const __amdgpu_buffer_rsrc_t ru = make_rsrc(Ug, bbytes);
 
   // Direct global -> LDS loads: instruction i of wave w fills the 1 KiB of
-  // rows 32i + 8w .. +7 and lane l lands at byte 16 l of it.
+  // rows 64i + 8w .. +7 and lane l lands at byte 16 l of it.
   typedef __attribute__((address_space(3))) void *lds_ptr_t;
   auto aload = [&](int k0, int buf) {
     const uint32_t so = (uint32_t)k0 * 2;
     char *ta = smem + buf * kABytes;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(ta + (32 * i + 8 * wave) * 128), 16,
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(ta + (64 * i + 8 * wave) * 128), 16,
                                                aoff[i], so, 0, 0);
   };
   auto bload = [&](int k0, int buf, int half) {
     const uint32_t so = (uint32_t)k0 * 2;
     char *tb = smem + 2 * kABytes + buf * kBBytes;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int i = 4 * half + j;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds((glu && i >= 4) ? ru : rb,
-                                               (lds_ptr_t)(tb + (32 * i + 8 * wave) * 128), 16,
+    for (int j = 0; j < 2; ++j) {
+      const int i = 2 * half + j;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds((glu && i >= 2) ? ru : rb,
+                                               (lds_ptr_t)(tb + (64 * i + 8 * wave) * 128), 16,
                                                boff[i], so, 0, 0);
     }
   };
 
   // Per-wave fragment rows.
-  int arow_l[4], brow_l[4];
+  int arow_l[4], brow_l[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    arow_l[i] = wm * 128 + i * 32 + (lane & 31);
-    brow_l[i] = glu ? (wn * 64 + (i & 1) * 32 + (i >> 1) * 128 + (lane & 31))
-                    : (wn * 128 + i * 32 + (lane & 31));
-  }
+  for (int i = 0; i < 4; ++i) arow_l[i] = wm * 128 + i * 32 + (lane & 31);
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    brow_l[j] = glu ? (wn * 32 + j * 128 + (lane & 31)) : (wn * 64 + j * 32 + (lane & 31));
   const int khalf = lane >> 5;
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  bf16x8 fa[4], fb[4], na[4], nb[4];
-  auto read_frags = [&](int kt, int ks, bf16x8 (&xa)[4], bf16x8 (&xb)[4]) {
+  bf16x8 fa[4], fb[2], na[4], nb[2];
+  auto read_frags = [&](int kt, int ks, bf16x8 (&xa)[4], bf16x8 (&xb)[2]) {
     const char *ta = smem + (kt & 1) * kABytes;
     const char *tb = smem + 2 * kABytes + (kt % 3) * kBBytes;
     const int c = ks * 2 + khalf;
 #pragma unroll
     for (int i = 0; i < 4; ++i) xa[i] = lds_frag(ta, arow_l[i], c);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) xb[j] = lds_frag(tb, brow_l[j], c);
+    for (int j = 0; j < 2; ++j) xb[j] = lds_frag(tb, brow_l[j], c);
   };
-  auto mfma16 = [&](const bf16x8 (&xa)[4], const bf16x8 (&xb)[4]) {
+  auto mfma16 = [&](const bf16x8 (&xa)[4], const bf16x8 (&xb)[2]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 2; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xb[j], xa[i], acc[i][j], 0, 0, 0);
   };
   auto copy_frags = [&]() {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      fa[i] = na[i];
-      fb[i] = nb[i];
-    }
+    for (int i = 0; i < 4; ++i) fa[i] = na[i];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) fb[j] = nb[j];
   };
 
   // A sub-step is one fenced scheduling region: the fragment reads for the
-  // next sub-step (and any loads) interleaved with this sub-step's 16 MFMAs.
+  // next sub-step (and any loads) interleaved with this sub-step's 8 MFMAs.
 #define MOE_SUBSTEP(READ_STMT, EXTRA_STMT, EXTRA_MASK, EXTRA_N)          \
   do {                                                                  \
     READ_STMT;                                                          \
     EXTRA_STMT;                                                         \
     mfma16(fa, fb);                                                     \
-    _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_) {                  \
+    _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) {                  \
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                \
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                \
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                \
       __builtin_amdgcn_sched_group_barrier(EXTRA_MASK, EXTRA_N, 0);     \
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                \
     }                                                                   \
@@ -227,7 +232,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
   aload(BK, 1);
   bload(BK, 1, 0);
   bload(BK, 1, 1);
-  asm volatile("s_waitcnt vmcnt(16)" ::: "memory");  // stage 0 landed
+  asm volatile("s_waitcnt vmcnt(8)" ::: "memory");   // stage 0 landed
   barrier_keep_loads();
   read_frags(0, 0, fa, fb);
   for (int kt = 0; kt + 2 < KT; ++kt) {
@@ -235,7 +240,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
     MOE_SUBSTEP(read_frags(kt, 1, na, nb), bload((kt + 2) * BK, (kt + 2) % 3, 0), 0x020, 1);
     MOE_SUBSTEP(read_frags(kt, 2, na, nb), bload((kt + 2) * BK, (kt + 2) % 3, 1), 0x020, 1);
     MOE_SUBSTEP(read_frags(kt, 3, na, nb), (void)0, 0x000, 0);
-    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");  // stage kt+1 landed
+    asm volatile("s_waitcnt vmcnt(4)" ::: "memory");  // stage kt+1 landed
     barrier_keep_loads();
     __builtin_amdgcn_sched_barrier(0);
     MOE_SUBSTEP(read_frags(kt + 1, 0, na, nb), aload((kt + 2) * BK, kt & 1), 0x020, 1);
@@ -260,7 +265,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
 #undef MOE_SUBSTEP
 
   // ---- epilogue.  Lane holds, for A block i and B block j, output row
-  // wm*128 + i*32 + lane%32 and columns 8q + 4*(lane/32) + {0..3}, q = 0..3.
+  // wm*128 + i*32 + lane%32 and columns 8q + 4*(lane/32) + {0..3}, q = 0..3,
+  // of the wave's 32-column block j (GLU: j = 0 gate, j = 1 up).
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = wm * 128 + i * 32 + (lane & 31);
@@ -269,28 +275,25 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
                                               : seg0 + m0 + r;
     if constexpr (EPI == EP_GLU) {
 #pragma unroll
-      for (int jp = 0; jp < 2; ++jp) {
+      for (int q = 0; q < 4; ++q) {
+        const int64_t col = n_tile * 128 + wn * 32 + 8 * q + 4 * khalf;
+        if (col >= a.ncols) continue;
+        float v[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int64_t col = n_tile * 128 + wn * 64 + jp * 32 + 8 * q + 4 * khalf;
-          if (col >= a.ncols) continue;
-          float v[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            v[e] = glu_act_fast(acc[i][jp][4 * q + e], acc[i][jp + 2][4 * q + e], a.act,
-                                a.beta_g, a.beta_u);
-          uint2 pk;
-          pk.x = pack_bf16x2_hw(v[0], v[1]);
-          pk.y = pack_bf16x2_hw(v[2], v[3]);
-          *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(a.out) + orow * a.ldo + col) = pk;
-        }
+        for (int e = 0; e < 4; ++e)
+          v[e] = glu_act_fast(acc[i][0][4 * q + e], acc[i][1][4 * q + e], a.act, a.beta_g,
+                              a.beta_u);
+        uint2 pk;
+        pk.x = pack_bf16x2_hw(v[0], v[1]);
+        pk.y = pack_bf16x2_hw(v[2], v[3]);
+        *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(a.out) + orow * a.ldo + col) = pk;
       }
     } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < 2; ++j) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int64_t col = n_tile * BN + wn * 128 + j * 32 + 8 * q + 4 * khalf;
+          const int64_t col = n_tile * BN + wn * 64 + j * 32 + 8 * q + 4 * khalf;
           if (col >= a.ncols) continue;
           float v[4];
 #pragma unroll
