@@ -26,6 +26,8 @@
 // one tile and writes act(gate, up) as bf16 (the hidden of a SwiGLU or
 // SiTU-GLU expert); EP_F32 / EP_BF16 store the product; EP_ADD_BF16 adds two
 // fp32 matrices before rounding (the latent layer's shared-expert outputs).
+#include <cmath>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -33,11 +35,9 @@ namespace moe {
 
 namespace {
 
-constexpr int BM = 256;
 constexpr int BN = 256;
 constexpr int BK = 64;
 constexpr int kThreads = 512;  // 8 waves: two per SIMD
-constexpr int kABytes = BM * BK * 2;   // 32 KiB per A stage
 constexpr int kBBytes = BN * BK * 2;   // 32 KiB per B stage
 constexpr int kMSuper = 8;                       // m-tiles per scheduling group
 
@@ -51,10 +51,13 @@ __device__ __forceinline__ bf16x8 lds_frag(const char *tile, int r, int c) {
   return *reinterpret_cast<const bf16x8 *>(tile + swz(r, c));
 }
 
-template <int EPI>
+// BM = 256 (waves 128x64) or 192 (waves 96x64, for experts with few rows).
+template <int EPI, int BM>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
+  constexpr int MI = BM / 64;              // 32-row A blocks per wave
+  constexpr int kABytes = BM * BK * 2;     // 32 or 24 KiB per A stage
   // A (activations, L2-resident) double-buffered; B (weights, streamed) in a
-  // ring of three so its loads get two k-steps of cover: 160 KiB in all.
+  // ring of three so its loads get two k-steps of cover: 160 / 144 KiB.
   __shared__ __attribute__((aligned(16))) char smem[2 * kABytes + 3 * kBBytes];
 
   // ---- which tile: XCD-aware remap (block i runs on XCD i % 8: each XCD
@@ -110,9 +113,12 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
 
   // ---- loader offsets (bytes), fixed over the K loop.
   const int64_t seg0 = (a.mode == GM_DENSE) ? 0 : a.kept_offsets[g];
+  // Per-wave arrays are sized for the largest MI (4) and used up to MI: host
+  // compilation drops the launch stub of a kernel template whose local arrays
+  // have a template-dependent size.
   uint32_t aoff[4], boff[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < MI; ++i) {
     const int r = lr + 64 * i;
     const int64_t rr = m0 + (r < mrows ? r : mrows - 1);
     int64_t arow;
@@ -121,6 +127,11 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
     else arow = (int64_t)g * a.a_group_rows + rr;
     const int pc = lc ^ (r & 7);  // the chunk this lane's LDS slot holds
     aoff[i] = (uint32_t)(arow * a.lda * 2) + (uint32_t)(pc << 4);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = lr + 64 * i;
+    const int pc = lc ^ (r & 7);
     int64_t brow;
     if (glu) {
       const int64_t n = n_tile * 128 + (r & 127);
@@ -145,7 +156,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
     const uint32_t so = (uint32_t)k0 * 2;
     char *ta = smem + buf * kABytes;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(ta + (64 * i + 8 * wave) * 128), 16,
                                                aoff[i], so, 0, 0);
   };
@@ -164,7 +175,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
   // Per-wave fragment rows.
   int arow_l[4], brow_l[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) arow_l[i] = wm * 128 + i * 32 + (lane & 31);
+  for (int i = 0; i < MI; ++i) arow_l[i] = wm * (BM / 2) + i * 32 + (lane & 31);
 #pragma unroll
   for (int j = 0; j < 2; ++j)
     brow_l[j] = glu ? (wn * 32 + j * 128 + (lane & 31)) : (wn * 64 + j * 32 + (lane & 31));
@@ -172,7 +183,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
 
   f32x16 acc[4][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -184,20 +195,20 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
     const char *tb = smem + 2 * kABytes + (kt % 3) * kBBytes;
     const int c = ks * 2 + khalf;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) xa[i] = lds_frag(ta, arow_l[i], c);
+    for (int i = 0; i < MI; ++i) xa[i] = lds_frag(ta, arow_l[i], c);
 #pragma unroll
     for (int j = 0; j < 2; ++j) xb[j] = lds_frag(tb, brow_l[j], c);
   };
   auto mfma16 = [&](const bf16x8 (&xa)[4], const bf16x8 (&xb)[2]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xb[j], xa[i], acc[i][j], 0, 0, 0);
   };
   auto copy_frags = [&]() {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fa[i] = na[i];
+    for (int i = 0; i < MI; ++i) fa[i] = na[i];
 #pragma unroll
     for (int j = 0; j < 2; ++j) fb[j] = nb[j];
   };
@@ -209,7 +220,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
     READ_STMT;                                                          \
     EXTRA_STMT;                                                         \
     mfma16(fa, fb);                                                     \
-    _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) {                  \
+    _Pragma("unroll") for (int i_ = 0; i_ < MI; ++i_) {                 \
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                \
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                \
       __builtin_amdgcn_sched_group_barrier(EXTRA_MASK, EXTRA_N, 0);     \
@@ -232,7 +243,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
   aload(BK, 1);
   bload(BK, 1, 0);
   bload(BK, 1, 1);
-  asm volatile("s_waitcnt vmcnt(8)" ::: "memory");   // stage 0 landed
+  if constexpr (MI == 4) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");  // stage 0 landed
+  else asm volatile("s_waitcnt vmcnt(7)" ::: "memory");
   barrier_keep_loads();
   read_frags(0, 0, fa, fb);
   for (int kt = 0; kt + 2 < KT; ++kt) {
@@ -268,8 +280,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
   // wm*128 + i*32 + lane%32 and columns 8q + 4*(lane/32) + {0..3}, q = 0..3,
   // of the wave's 32-column block j (GLU: j = 0 gate, j = 1 up).
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = wm * 128 + i * 32 + (lane & 31);
+  for (int i = 0; i < MI; ++i) {
+    const int r = wm * (BM / 2) + i * 32 + (lane & 31);
     if (r >= mrows) continue;
     const int64_t orow = (a.mode == GM_DENSE) ? (int64_t)g * a.out_group_stride + m0 + r
                                               : seg0 + m0 + r;
@@ -322,15 +334,16 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
   }
 }
 
-// tile_start[g] = sum_{g' < g} ceil(M_g' / BM), M_g = kept rows of group g.
+// tile_start[g] = sum_{g' < g} ceil(M_g' / bm), M_g = kept rows of group g.
 __global__ __launch_bounds__(1024) void tile_prefix_kernel(const int32_t *__restrict__ kept_offsets,
-                                                           int G, int32_t *__restrict__ tile_start) {
+                                                           int G, int bm,
+                                                           int32_t *__restrict__ tile_start) {
   __shared__ int tmp[1024];
   int run = 0;  // carried across rounds of 1024 groups
   for (int base = 0; base < G; base += 1024) {
     const int g = base + threadIdx.x;
     const int m = (g < G) ? kept_offsets[g + 1] - kept_offsets[g] : 0;
-    tmp[threadIdx.x] = (m + BM - 1) / BM;
+    tmp[threadIdx.x] = (m + bm - 1) / bm;
     __syncthreads();
     for (int o = 1; o < 1024; o <<= 1) {
       const int add = (int)threadIdx.x >= o ? tmp[threadIdx.x - o] : 0;
@@ -345,42 +358,58 @@ __global__ __launch_bounds__(1024) void tile_prefix_kernel(const int32_t *__rest
   if (threadIdx.x == 0) tile_start[0] = 0;
 }
 
-}  // namespace
-
-int gemm_bm() { return BM; }
-
-int64_t gemm_mtile_bound(int64_t rows_total, int groups) {
-  return (rows_total + BM - 1) / BM + groups;
+// One launch per (epilogue, tile height) pair, written out so that every
+// kernel instance is referenced from a non-template function.
+hipError_t launch_kernel(const GemmArgs &a, int epi, int bm, int64_t grid, hipStream_t st) {
+  const dim3 g(grid), b(kThreads);
+  if (bm == 192) {
+    switch (epi) {
+      case EP_GLU: grouped_gemm_kernel<EP_GLU, 192><<<g, b, 0, st>>>(a); break;
+      case EP_F32: grouped_gemm_kernel<EP_F32, 192><<<g, b, 0, st>>>(a); break;
+      case EP_BF16: grouped_gemm_kernel<EP_BF16, 192><<<g, b, 0, st>>>(a); break;
+      default: grouped_gemm_kernel<EP_ADD_BF16, 192><<<g, b, 0, st>>>(a); break;
+    }
+  } else {
+    switch (epi) {
+      case EP_GLU: grouped_gemm_kernel<EP_GLU, 256><<<g, b, 0, st>>>(a); break;
+      case EP_F32: grouped_gemm_kernel<EP_F32, 256><<<g, b, 0, st>>>(a); break;
+      case EP_BF16: grouped_gemm_kernel<EP_BF16, 256><<<g, b, 0, st>>>(a); break;
+      default: grouped_gemm_kernel<EP_ADD_BF16, 256><<<g, b, 0, st>>>(a); break;
+    }
+  }
+  return hipGetLastError();
 }
 
-hipError_t launch_tile_prefix(const int32_t *kept_offsets, int G, int32_t *tile_start,
+}  // namespace
+
+int gemm_pick_bm(double rows_per_group) {
+  // The m-tile height that pads an average group least (256 on ties).
+  if (rows_per_group <= 0) return 256;
+  const double w256 = std::ceil(rows_per_group / 256.0) * 256.0 - rows_per_group;
+  const double w192 = std::ceil(rows_per_group / 192.0) * 192.0 - rows_per_group;
+  return w192 < w256 ? 192 : 256;
+}
+
+int64_t gemm_mtile_bound(int64_t rows_total, int groups, int bm) {
+  return (rows_total + bm - 1) / bm + groups;
+}
+
+hipError_t launch_tile_prefix(const int32_t *kept_offsets, int G, int bm, int32_t *tile_start,
                               hipStream_t st) {
-  hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, st, kept_offsets, G, tile_start);
+  hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, st, kept_offsets, G, bm,
+                     tile_start);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm(const GemmArgs &a, int epi, int64_t mtiles_bound, hipStream_t st) {
+  const int bm = a.bm == 192 ? 192 : 256;
   const int64_t NT = (epi == EP_GLU) ? (a.ncols + 127) / 128 : (a.ncols + BN - 1) / BN;
   int64_t tiles;
-  if (a.mode == GM_DENSE) tiles = (int64_t)a.G * ((a.M_dense + BM - 1) / BM) * NT;
+  if (a.mode == GM_DENSE) tiles = (int64_t)a.G * ((a.M_dense + bm - 1) / bm) * NT;
   else tiles = mtiles_bound * NT;
   const int64_t grid = (tiles + 7) / 8 * 8;
   if (grid == 0) return hipSuccess;
-  switch (epi) {
-    case EP_GLU:
-      hipLaunchKernelGGL(grouped_gemm_kernel<EP_GLU>, dim3(grid), dim3(kThreads), 0, st, a);
-      break;
-    case EP_F32:
-      hipLaunchKernelGGL(grouped_gemm_kernel<EP_F32>, dim3(grid), dim3(kThreads), 0, st, a);
-      break;
-    case EP_BF16:
-      hipLaunchKernelGGL(grouped_gemm_kernel<EP_BF16>, dim3(grid), dim3(kThreads), 0, st, a);
-      break;
-    default:
-      hipLaunchKernelGGL(grouped_gemm_kernel<EP_ADD_BF16>, dim3(grid), dim3(kThreads), 0, st, a);
-      break;
-  }
-  return hipGetLastError();
+  return launch_kernel(a, epi, bm, grid, st);
 }
 
 }  // namespace moe

@@ -57,11 +57,13 @@ struct GemmArgs {
   const float *add0, *add1;   // EP_ADD_BF16: out = acc + add0 + add1 (fp32, ldo)
   int act;                    // 0 SwiGLU, 1 SiTU-GLU
   float beta_g, beta_u;
+  int bm;                     // m-tile height: 192, else 256
 };
+// m-tile height for groups of about rows_per_group rows (192 or 256).
+int gemm_pick_bm(double rows_per_group);
 // Upper bound of m-tiles (host side, no device sync).
-int64_t gemm_mtile_bound(int64_t rows_total, int groups);
-int gemm_bm();
-hipError_t launch_tile_prefix(const int32_t *kept_offsets, int G, int32_t *tile_start,
+int64_t gemm_mtile_bound(int64_t rows_total, int groups, int bm);
+hipError_t launch_tile_prefix(const int32_t *kept_offsets, int G, int bm, int32_t *tile_start,
                               hipStream_t st);
 hipError_t launch_gemm(const GemmArgs &a, int epi, int64_t mtiles_bound, hipStream_t st);
 

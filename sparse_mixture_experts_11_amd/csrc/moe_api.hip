@@ -204,11 +204,18 @@ FfnPath ffn_path(const moe_desc_t &d) {
   return FFN_TILED;
 }
 
+// m-tile height of the routed expert GEMMs, from the mean kept rows per
+// expert (known on the host without waiting for the routing).
+int routed_bm(const moe_desc_t &d) {
+  return gemm_pick_bm((double)kept_rows_bound(d) / (double)d.N);
+}
+
 // The tiled path finds its work from a per-expert prefix of m-tiles.
 hipError_t do_tile_prefix(const moe_desc_t &d, const Layout &L, const int32_t *kept_offsets,
                           void *ws, hipStream_t st) {
   if (ffn_path(d) != FFN_TILED) return hipSuccess;
-  return launch_tile_prefix(kept_offsets, d.N, region<int32_t>(ws, L.tile_start), st);
+  return launch_tile_prefix(kept_offsets, d.N, routed_bm(d), region<int32_t>(ws, L.tile_start),
+                            st);
 }
 
 hipError_t do_ffn_gate_up(const moe_desc_t &d, const Layout &L, const void *x, const int32_t *perm,
@@ -245,7 +252,8 @@ hipError_t do_ffn_gate_up(const moe_desc_t &d, const Layout &L, const void *x, c
   a.act = d.act;
   a.beta_g = d.beta_g;
   a.beta_u = d.beta_u;
-  return launch_gemm(a, EP_GLU, gemm_mtile_bound(kept_rows_bound(d), d.N), st);
+  a.bm = routed_bm(d);
+  return launch_gemm(a, EP_GLU, gemm_mtile_bound(kept_rows_bound(d), d.N, a.bm), st);
 }
 
 hipError_t do_ffn_down(const moe_desc_t &d, const Layout &L, const int32_t *kept_offsets,
@@ -271,7 +279,8 @@ hipError_t do_ffn_down(const moe_desc_t &d, const Layout &L, const int32_t *kept
   a.tile_start = region<int32_t>(ws, L.tile_start);
   a.out = y_perm;
   a.ldo = w;
-  return launch_gemm(a, EP_F32, gemm_mtile_bound(kept_rows_bound(d), d.N), st);
+  a.bm = routed_bm(d);
+  return launch_gemm(a, EP_F32, gemm_mtile_bound(kept_rows_bound(d), d.N, a.bm), st);
 }
 
 // Dense (one or few groups) projection: out[g*T + r] = A[g*a_rows + r] . B_g

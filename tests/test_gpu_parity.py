@@ -35,6 +35,8 @@ CASES = {
     "mixtral_small_t64_decode": MIX_S.with_(T=64),
     "mixtral_small_t65": MIX_S.with_(T=65),
     "mixtral_small_t3000_tiled": MIX_S.with_(T=3000),
+    # about 300 rows per expert: 192-row m-tiles, two or three per expert
+    "mixtral_small_t1200_bm192": MIX_S.with_(T=1200),
     "switch_small_t2000": C.SWITCH_SKEWED.with_(T=2000, d=1024, h=1024),
     "switch_small_t48_decode": C.SWITCH_SKEWED.with_(T=48, d=1024, h=1024),
     "switch_small_t6000_tiled": C.SWITCH_SKEWED.with_(T=6000, d=1024, h=1024),
@@ -202,9 +204,10 @@ def test_unselected_expert_perturbation(name):
 # ---------------------------------------------------------------------------
 
 # Expert-kernel families: SIMT (fp32), decode (T <= 64), tiled grouped GEMM
-# (otherwise; one and several m-tiles per expert).
+# (otherwise; one and several m-tiles per expert, 256- and 192-row tiles).
 STAGE_CASES = ["tiny", "tiny_planted_c4", "mcu_t4096", "mixtral_small_t1000",
-               "mixtral_small_t3000_tiled", "mixtral_small_t37_decode", "switch_small_t2000",
+               "mixtral_small_t3000_tiled", "mixtral_small_t1200_bm192",
+               "mixtral_small_t37_decode", "switch_small_t2000",
                "switch_small_t6000_tiled", "latent_small_t700", "latent_small_stream_t900"]
 
 
