@@ -56,6 +56,18 @@ def algorithmic(cfg, counts_kept):
             "down_bytes": down_bytes, "touched": touched}
 
 
+def tile_rows(cfg):
+    """m-tile height the library uses for the routed expert GEMMs (for the
+    kernel label only): whichever of 256 and 192 pads the mean kept rows per
+    expert least."""
+    import math
+    kept = cfg.T * cfg.k if cfg.capacity_factor is None else min(
+        cfg.T * cfg.k, cfg.N * math.ceil(cfg.capacity_factor * cfg.k * cfg.T / cfg.N))
+    e = kept / cfg.N
+    w = {bm: math.ceil(e / bm) * bm - e for bm in (256, 192)}
+    return 192 if w[192] < w[256] else 256
+
+
 def measured_traffic(workload):
     """HBM bytes per launch of the workload's dominant kernel, from the
     rocprofv3 counter runs recorded in profiles/hbm_traffic.json, or None when
@@ -108,8 +120,12 @@ def run_workload(cfg, steps, warmup):
     total_ms = t_start.elapsed_time(t_end)
     per_stage = {s: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(steps)]))
                  for j, s in enumerate(stages)}
+    # first stage start to last stage end of each step (excludes the gap
+    # between steps, which the whole-run figure includes)
+    per_step = [ev[i][0].elapsed_time(ev[i][-1]) for i in range(steps)]
     kept = np.diff(H.to_host(out["kept_offsets"]))
     return {"ms_per_step": total_ms / steps, "stages_ms": per_stage,
+            "step_ms_median": float(np.median(per_step)), "step_ms_min": float(np.min(per_step)),
             "alg": algorithmic(cfg, kept), "desc": desc}
 
 
@@ -130,7 +146,14 @@ def cpu_baseline(cfg, n_tokens):
               capacity=cap, beta_g=sub.beta_g, beta_u=sub.beta_u, alpha=sub.aux_alpha)
     dt = time.perf_counter() - t0
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": n_tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "cpu_model": model, "host_cpus": os.cpu_count(),
             "sample": f"fp64 oracle forward of the first {n_tokens} of {cfg.T} tokens "
                       f"(same weights; includes expanding the stored bf16 weights), {dt:.1f} s"}
 
@@ -157,8 +180,12 @@ def main():
     t = r["stages_ms"]["expert_gate_up"] / 1e3
     intensity = alg["gu_flops"] / alg["gu_bytes"]
     ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
-    kernel = ("decode_kernel<true> (expert gate/up)" if cfg.T <= 64
-              else "grouped_gemm_kernel<EP_GLU> (expert gate/up)")
+    if cfg.act_dtype != "bf16":
+        kernel = "simt_gu_kernel (fp32 expert gate/up)"
+    elif cfg.T <= 64:
+        kernel = "decode_kernel<true, 2> (expert gate/up)"
+    else:
+        kernel = f"grouped_gemm_kernel<EP_GLU, {tile_rows(cfg)}> (expert gate/up)"
     if intensity < ridge:
         achieved = alg["gu_bytes"] / t / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -174,6 +201,7 @@ def main():
     line = {
         "metric": METRIC, "value": tok_s, "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": r["ms_per_step"],
+        "step_ms_median": r["step_ms_median"], "step_ms_min": r["step_ms_min"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if cfg.act_dtype == "bf16" else "f32", "data": "synthetic",
         "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "h": cfg.h, "N": cfg.N,
