@@ -123,6 +123,112 @@ __global__ __launch_bounds__(64) void dispatch_rank_kernel(
   }
 }
 
+// Small inputs (at most 1024 entries): the balance statistics and the whole
+// dispatch in one 1024-thread block.  Wave w takes entries 64w .. 64w+63;
+// lanes naming the same expert find each other with ballots over the expert
+// id bits (rank within the wave), each group's highest lane records the
+// group size in hist[w][e], and an entry's rank is its rank within the wave
+// plus hist[w'][e] over the earlier waves w' -- the same stable token-order
+// rank as the chunked kernels, with no atomics deciding any order.
+constexpr int kTailWaves = 16;
+constexpr int kTailMaxN = 1024;
+
+__global__ __launch_bounds__(1024) void small_tail_kernel(
+    const float *__restrict__ part_p, const int32_t *__restrict__ part_cnt, int waves, int64_t T,
+    float alpha, float *__restrict__ stats, const int32_t *__restrict__ idx, int E, int N,
+    int nbits, int capacity, int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
+    int32_t *__restrict__ kept_offsets, int32_t *__restrict__ perm, int32_t *__restrict__ row_of,
+    uint8_t *__restrict__ drop) {
+  __shared__ int32_t hist[kTailWaves][kTailMaxN];
+  __shared__ int32_t base_all[kTailMaxN], base_kept[kTailMaxN];
+  __shared__ int tmp[1024];
+  __shared__ float red[1024];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+
+  if (stats != nullptr) {
+    // f_n = (argmax count) / T, P_n = (sum of p) / T, partial rows summed in
+    // row order; N * sum_n f_n P_n by a fixed tree.
+    float fp = 0.f;
+    if (tid < N) {
+      float p = 0.f;
+      int64_t c = 0;
+      for (int wv = 0; wv < waves; ++wv) {
+        p += part_p[(int64_t)wv * N + tid];
+        c += part_cnt[(int64_t)wv * N + tid];
+      }
+      const float f = (float)((double)c / (double)T);
+      const float P = p / (float)T;
+      stats[tid] = f;
+      stats[N + tid] = P;
+      fp = f * P;
+    }
+    red[tid] = fp;
+    __syncthreads();
+    for (int s = 512; s > 0; s >>= 1) {
+      if (tid < s) red[tid] += red[tid + s];
+      __syncthreads();
+    }
+    if (tid == 0) {
+      const float v = (float)N * red[0];
+      stats[2 * N] = v;
+      stats[2 * N + 1] = alpha * v;
+    }
+  }
+  if (perm == nullptr) return;
+
+  for (int i = tid; i < kTailWaves * N; i += 1024) hist[i / N][i % N] = 0;
+  __syncthreads();
+  int e = (tid < E) ? idx[tid] : -1;
+  const bool ok = e >= 0 && e < N;
+  if (!ok) e = -1;
+  uint64_t same = __ballot(ok);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = ok && ((e >> b) & 1);
+    const uint64_t ones = __ballot(bit);
+    same &= bit ? ones : ~ones;
+  }
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int r_wave = ok ? __popcll(same & below) : 0;
+  if (ok && (63 - __clzll(same)) == lane) hist[wave][e] = __popcll(same);
+  __syncthreads();
+
+  // Per-expert totals, offsets and kept offsets (thread n = expert n).
+  int total = 0;
+  if (tid < N)
+    for (int w = 0; w < kTailWaves; ++w) total += hist[w][tid];
+  const int kept = (tid < N) ? ((capacity >= 0 && total > capacity) ? capacity : total) : 0;
+  const int inc_all = block_incl_scan(tid < N ? total : 0, tmp);
+  const int inc_kept = block_incl_scan(kept, tmp);
+  if (tid < N) {
+    base_all[tid] = inc_all - total;
+    base_kept[tid] = inc_kept - kept;
+    counts[tid] = total;
+    offsets[tid + 1] = inc_all;
+    kept_offsets[tid + 1] = inc_kept;
+  }
+  if (tid == 0) {
+    offsets[0] = 0;
+    kept_offsets[0] = 0;
+  }
+  __syncthreads();
+
+  if (tid < E) {
+    if (ok) {
+      int r = r_wave;
+      for (int w = 0; w < wave; ++w) r += hist[w][e];
+      perm[base_all[e] + r] = tid;
+      const bool keep = capacity < 0 || r < capacity;
+      row_of[tid] = keep ? base_kept[e] + r : -1;
+      drop[tid] = keep ? 0 : 1;
+    } else {
+      row_of[tid] = -1;
+      drop[tid] = 1;
+    }
+  }
+}
+
 }  // namespace
 
 int dispatch_blocks(int64_t entries) { return (int)((entries + kChunk - 1) / kChunk); }
@@ -140,6 +246,23 @@ hipError_t launch_dispatch(const int32_t *idx, int64_t T, int k, int N, int capa
                      capacity, counts, offsets, kept_offsets);
   hipLaunchKernelGGL(dispatch_rank_kernel, dim3(nblk), dim3(64), 0, st, idx, E, N, nbits,
                      capacity, blk_counts, offsets, kept_offsets, perm, row_of, drop);
+  return hipGetLastError();
+}
+
+bool small_tail_fits(int64_t entries, int N) {
+  return entries <= kTailWaves * 64 && N <= kTailMaxN;
+}
+
+hipError_t launch_small_tail(const float *part_p, const int32_t *part_cnt, int waves, int64_t T,
+                             float alpha, float *stats, const int32_t *idx, int k, int N,
+                             int capacity, int32_t *counts, int32_t *offsets,
+                             int32_t *kept_offsets, int32_t *perm, int32_t *row_of,
+                             uint8_t *drop, hipStream_t st) {
+  int nbits = 0;
+  while ((1 << nbits) < N) ++nbits;
+  hipLaunchKernelGGL(small_tail_kernel, dim3(1), dim3(1024), 0, st, part_p, part_cnt, waves, T,
+                     alpha, stats, idx, (int)(T * k), N, nbits, capacity, counts, offsets,
+                     kept_offsets, perm, row_of, drop);
   return hipGetLastError();
 }
 

@@ -28,6 +28,15 @@ hipError_t launch_dispatch(const int32_t *idx, int64_t T, int k, int N, int capa
                            int32_t *counts, int32_t *offsets, int32_t *kept_offsets,
                            int32_t *perm, int32_t *row_of, uint8_t *drop,
                            int32_t *blk_counts, hipStream_t st);
+// At most 1024 entries and 1024 experts: one launch does the balance
+// statistics (when stats != nullptr, from the router's partial rows) and
+// the whole dispatch (when perm != nullptr).
+bool small_tail_fits(int64_t entries, int N);
+hipError_t launch_small_tail(const float *part_p, const int32_t *part_cnt, int waves, int64_t T,
+                             float alpha, float *stats, const int32_t *idx, int k, int N,
+                             int capacity, int32_t *counts, int32_t *offsets,
+                             int32_t *kept_offsets, int32_t *perm, int32_t *row_of,
+                             uint8_t *drop, hipStream_t st);
 
 // ---- grouped GEMM on bf16 MFMA (gemm.hip) -----------------------------------
 enum GemmMode { GM_GATHER = 0, GM_SEGMENT = 1, GM_DENSE = 2 };

@@ -186,9 +186,19 @@ hipError_t do_route(const moe_desc_t &d, const Layout &L, const void *u, const v
   return launch_stats_finalize(pp, pc, route_waves(d.T, d.N), d.T, d.N, d.aux_alpha, stats, st);
 }
 
+// At most 1024 (token, slot) entries: one single-block launch does the
+// dispatch, and inside a forward also the balance statistics the router
+// left as partial rows (the router then skips its own two-launch finish).
+bool small_tail(const moe_desc_t &d) { return small_tail_fits(d.T * d.k, d.N); }
+
+// stats != nullptr only when the router deferred its statistics to here.
 hipError_t do_dispatch(const moe_desc_t &d, const Layout &L, const int32_t *idx, int32_t *counts,
                        int32_t *offsets, int32_t *kept_offsets, int32_t *perm, int32_t *row_of,
-                       uint8_t *drop, void *ws, hipStream_t st) {
+                       uint8_t *drop, float *stats, void *ws, hipStream_t st) {
+  if (small_tail(d))
+    return launch_small_tail(region<float>(ws, L.part_p), region<int32_t>(ws, L.part_cnt),
+                             route_waves(d.T, d.N), d.T, d.aux_alpha, stats, idx, d.k, d.N,
+                             d.capacity, counts, offsets, kept_offsets, perm, row_of, drop, st);
   return launch_dispatch(idx, d.T, d.k, d.N, d.capacity, counts, offsets, kept_offsets, perm,
                          row_of, drop, region<int32_t>(ws, L.blk_counts), st);
 }
@@ -366,9 +376,12 @@ moe_status_t forward_impl(const moe_desc_t *desc, const moe_weights_t *wts, cons
 
   Tracer tr{events, n_events, 0, st};
   MOE_TRY(tr.mark());
-  MOE_TRY(do_route(d, L, u, wts->W_route, idx, tw, stats, ws, st));
+  // Small inputs finish the statistics inside the dispatch launch.
+  const bool fused_stats = small_tail(d);
+  MOE_TRY(do_route(d, L, u, wts->W_route, idx, tw, fused_stats ? nullptr : stats, ws, st));
   MOE_TRY(tr.mark());
-  MOE_TRY(do_dispatch(d, L, idx, counts, offsets, kept_offsets, perm, row_of, drop, ws, st));
+  MOE_TRY(do_dispatch(d, L, idx, counts, offsets, kept_offsets, perm, row_of, drop,
+                      fused_stats ? stats : nullptr, ws, st));
   MOE_TRY(do_tile_prefix(d, L, kept_offsets, ws, st));
   MOE_TRY(tr.mark());
   const void *x = u;
@@ -485,7 +498,7 @@ moe_status_t moe_dispatch(const moe_desc_t *desc, const int32_t *topk_idx, int32
   const Layout L = layout(*desc);
   if (ws == nullptr || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   return hip_status(do_dispatch(*desc, L, topk_idx, counts, offsets, kept_offsets, perm, row_of,
-                                drop, ws, reinterpret_cast<hipStream_t>(stream)));
+                                drop, nullptr, ws, reinterpret_cast<hipStream_t>(stream)));
 }
 
 moe_status_t moe_expert_ffn(const moe_desc_t *desc, const void *x, const int32_t *perm,

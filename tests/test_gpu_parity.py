@@ -251,10 +251,13 @@ def test_stage_dispatch(name):
 
 
 def test_stage_dispatch_random_assignments():
-    # Many experts, many chunks, capacity: random distinct top-k rows.
+    # Many experts, many chunks, capacity: random distinct top-k rows; the
+    # last five take the single-block path (at most 1024 entries), up to its
+    # limits of 1024 entries and 1024 experts.
     rng = np.random.default_rng(0)
     for T, N, k, cap in ((5000, 896, 16, 70), (3000, 8, 2, 700), (100, 1024, 32, 2),
-                         (2049, 64, 3, -1)):
+                         (2049, 64, 3, -1), (32, 1024, 32, 1), (512, 8, 2, 100), (1, 8, 2, -1),
+                         (33, 96, 6, 3), (200, 5, 5, 150)):
         log(f"[dispatch random] T={T} N={N} k={k} cap={cap}")
         cfg = C.LATENT.with_(T=T, N=N, k=k)
         idx = np.stack([rng.permutation(N)[:k] for _ in range(T)]).astype(np.int32)
