@@ -24,8 +24,12 @@
 //
 // Epilogues: EP_GLU pairs 128 gate columns with the matching 128 up columns in
 // one tile and writes act(gate, up) as bf16 (the hidden of a SwiGLU or
-// SiTU-GLU expert); EP_F32 / EP_BF16 store the product; EP_ADD_BF16 adds two
+// SiTU-GLU expert); EP_F32 stores the fp32 product through LDS so each store
+// writes a whole output row, and handles any column count (the router logits
+// have N columns); EP_BF16 stores the rounded product; EP_ADD_BF16 adds two
 // fp32 matrices before rounding (the latent layer's shared-expert outputs).
+// The bf16 epilogues store 4 columns at a time: their column counts (h, d, l)
+// are multiples of 128.
 #include <cmath>
 
 #include "common.hpp"
@@ -275,6 +279,50 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
   }
 #undef MOE_WAIT_LOADS
 #undef MOE_SUBSTEP
+
+  if constexpr (EPI == EP_F32) {
+    // fp32 tile through LDS, the rows of one wm at a time, so that each store
+    // instruction writes one whole 1 KiB output row (the register layout
+    // would write 32-byte pieces of 32 rows).  Row pitch padded by 16 bytes.
+    constexpr int kRows = BM / 2;
+    constexpr int kPitch = BN * 4 + 16;
+    static_assert(kRows * kPitch <= 2 * kABytes + 3 * kBBytes, "staging exceeds LDS");
+    __syncthreads();  // every wave has finished reading the operand stages
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      if (wm == half) {
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int rl = i * 32 + (lane & 31);
+              const int c = wn * 64 + j * 32 + 8 * q + 4 * khalf;
+              *reinterpret_cast<f32x4 *>(smem + rl * kPitch + c * 4) =
+                  f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                        acc[i][j][4 * q + 3]};
+            }
+      }
+      __syncthreads();
+      const int64_t col = n_tile * BN + 4 * lane;
+      for (int rl = wave; rl < kRows; rl += kThreads / 64) {
+        const int r = half * kRows + rl;
+        if (r >= mrows || col >= a.ncols) continue;
+        const int64_t orow = (a.mode == GM_DENSE) ? (int64_t)g * a.out_group_stride + m0 + r
+                                                  : seg0 + m0 + r;
+        const f32x4 v = *reinterpret_cast<const f32x4 *>(smem + rl * kPitch + 16 * lane);
+        float *dst = reinterpret_cast<float *>(a.out) + orow * a.ldo + col;
+        if (col + 4 <= a.ncols) {
+          *reinterpret_cast<f32x4 *>(dst) = v;
+        } else {
+          for (int e = 0; e < (int)(a.ncols - col); ++e) dst[e] = v[e];
+        }
+      }
+      __syncthreads();
+    }
+    return;
+  }
 
   // ---- epilogue.  Lane holds, for A block i and B block j, output row
   // wm*128 + i*32 + lane%32 and columns 8q + 4*(lane/32) + {0..3}, q = 0..3,

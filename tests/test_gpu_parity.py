@@ -46,6 +46,10 @@ CASES = {
     "latent_small_wave_router": C.LATENT.with_(T=300, d=512, l=256, h=256, N=40, k=4,
                                                h_shared=128, n_shared=1),
     "latent_small_decode_t20": C.LATENT.with_(T=20, d=512, l=384, h=256, N=96, k=6, h_shared=256),
+    # router logits through the GEMM with a column count that is not a
+    # multiple of 4
+    "latent_small_n97": C.LATENT.with_(T=300, d=512, l=256, h=256, N=97, k=5, h_shared=128,
+                                       n_shared=1),
 }
 
 
