@@ -11,7 +11,7 @@ namespace {
 
 constexpr int kRouteBlock = 256;       // 4 waves
 constexpr int kRouteMaxWaves = 8192;   // wave router, per launch (sizes the stats partials)
-constexpr int kLogitsMaxWaves = 1024;  // top-k over materialised logits (N up to 1024)
+constexpr int kLogitsMaxWaves = 8192;  // top-k over materialised logits (N up to 1024): a wave per token up to 8192 tokens
 constexpr int kRouteSmallT = 256;      // at or below: one block per token (N <= 64)
 
 template <bool BF16>
