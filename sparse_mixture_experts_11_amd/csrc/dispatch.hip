@@ -154,7 +154,8 @@ __global__ __launch_bounds__(1024) void small_tail_kernel(
     if (tid < N) {
       float p = 0.f;
       int64_t c = 0;
-      for (int wv = 0; wv < waves; ++wv) {
+#pragma unroll 8
+      for (int wv = 0; wv < waves; ++wv) {  // independent loads, issued in batches
         p += part_p[(int64_t)wv * N + tid];
         c += part_cnt[(int64_t)wv * N + tid];
       }

@@ -13,6 +13,7 @@ constexpr int kRouteBlock = 256;       // 4 waves
 constexpr int kRouteMaxWaves = 8192;   // wave router, per launch (sizes the stats partials)
 constexpr int kLogitsMaxWaves = 8192;  // top-k over materialised logits (N up to 1024): a wave per token up to 8192 tokens
 constexpr int kRouteSmallT = 256;      // at or below: one block per token (N <= 64)
+constexpr int kSmallBlock = 512;       // 8 waves: d = 4096 in one load round
 
 template <bool BF16>
 __device__ __forceinline__ void load8(const void *base, int64_t off, float (&x)[8]) {
@@ -141,22 +142,22 @@ __global__ __launch_bounds__(kRouteBlock) void route_wave_kernel(
   }
 }
 
-// Small T: one 4-wave block per token.  Each thread accumulates its share of
-// the d-loop for every expert; the 4 wave partials meet in LDS and wave 0
+// Small T: one 8-wave block per token.  Each thread accumulates its share of
+// the d-loop for every expert; the 8 wave partials meet in LDS and wave 0
 // adds them in a fixed order, then selects.  Stats partials are per token.
 template <bool UB, bool WB, int NMAX>
-__global__ __launch_bounds__(kRouteBlock) void route_small_kernel(
+__global__ __launch_bounds__(kSmallBlock) void route_small_kernel(
     const void *__restrict__ u, const void *__restrict__ W, int64_t T, int d, int N, int k,
     int gate, int32_t *__restrict__ idx, float *__restrict__ w, float *__restrict__ part_p,
     int32_t *__restrict__ part_cnt) {
-  __shared__ float red[kRouteBlock / 64][NMAX];
+  __shared__ float red[kSmallBlock / 64][NMAX];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int64_t t = blockIdx.x;
   float acc[NMAX];
 #pragma unroll
   for (int n = 0; n < NMAX; ++n) acc[n] = 0.f;
-  for (int base = threadIdx.x * 8; base < d; base += kRouteBlock * 8) {
+  for (int base = threadIdx.x * 8; base < d; base += kSmallBlock * 8) {
     float x[8];
     load8<UB>(u, t * d + base, x);
 #pragma unroll
@@ -179,7 +180,9 @@ __global__ __launch_bounds__(kRouteBlock) void route_small_kernel(
   float z[NMAX];
 #pragma unroll
   for (int n = 0; n < NMAX; ++n)
-    z[n] = ((red[0][n] + red[1][n]) + red[2][n]) + red[3][n];
+    z[n] = ((((((red[0][n] + red[1][n]) + red[2][n]) + red[3][n]) + red[4][n]) + red[5][n]) +
+            red[6][n]) +
+           red[7][n];
   float acc_p = 0.f;
   int acc_cnt = 0;
   select_and_write<NMAX>(z, N, k, gate, t, lane, idx, w, acc_p, acc_cnt);
@@ -345,7 +348,7 @@ hipError_t launch_rw(const void *u, const void *W, int64_t T, int d, int N, int 
 template <bool UB, bool WB, int NMAX>
 hipError_t launch_rs(const void *u, const void *W, int64_t T, int d, int N, int k, int gate,
                      int32_t *idx, float *w, float *pp, int32_t *pc, hipStream_t st) {
-  hipLaunchKernelGGL((route_small_kernel<UB, WB, NMAX>), dim3((unsigned)T), dim3(kRouteBlock), 0,
+  hipLaunchKernelGGL((route_small_kernel<UB, WB, NMAX>), dim3((unsigned)T), dim3(kSmallBlock), 0,
                      st, u, W, T, d, N, k, gate, idx, w, pp, pc);
   return hipGetLastError();
 }
