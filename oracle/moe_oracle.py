@@ -42,7 +42,10 @@ Readings where the pages are silent (listed again in the design doc):
   * f_i is the argmax indicator of §3.4's formula, taken before capacity;
   * SiTU-GLU(g, v) = SiLU(beta_g tanh(g / beta_g)) * beta_u tanh(v / beta_u);
   * RMSNorm(r) = r / sqrt(mean(r^2) + eps), no learned gain;
-  * LatentMoE routes on the full-width u, adds shared experts with weight 1.
+  * LatentMoE routes on the full-width u, adds shared experts with weight 1;
+  * Quantile Balancing: score = router logit z, selection on z + b with the
+    combine weights from the unbiased p, a_t = k-th largest z_t + b,
+    q = round(k T / N), histogram of 256 bins over [min, max] of required.
 
 Pins (tests/test_oracle_pins.py): the capacity example [10,3,2,1] -> drops
 6/4/0; the balanced/collapsed aux example (1.0000 / 2.8449); the parameter
@@ -51,8 +54,13 @@ N=1 reduces to a torch.nn.functional SwiGLU; softmax/top-k against torch;
 dispatch order against torch.where; RMSNorm against torch's rms_norm;
 latent limits (beta -> inf gives SwiGLU; identity projections give
 RMSNorm(plain); scale invariance); the 12.4% latent parameter saving.
-Parity unpinned: the exact SiTU-GLU form and the LatentMoE wiring are
-readings, pinned only through the limits and invariants above.
+Quantile Balancing pins: after the exact update every expert admits exactly
+q tokens under the fixed cutoffs; a constant shift of b shifts b' by the same
+constant; the histogram estimate lies within one bin of the exact value; a
+hand-worked 4-token example; b = 0 reproduces the unbiased routing.
+Parity unpinned: the exact SiTU-GLU form, the LatentMoE wiring and the
+Quantile Balancing readings (score, cutoff, q, bins) are readings, pinned
+only through the limits and invariants above.
 """
 from __future__ import annotations
 
@@ -122,12 +130,86 @@ def gate_weights(p: np.ndarray, idx: np.ndarray, gate: str) -> np.ndarray:
     raise ValueError(gate)
 
 
-def route(u: np.ndarray, w_route: np.ndarray, k: int, gate: str) -> Dict[str, np.ndarray]:
+def route(u: np.ndarray, w_route: np.ndarray, k: int, gate: str,
+          bias: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+    """Router.  With a selection bias b (Quantile Balancing, page "Stable
+    LatentMoE interactive demo", QB passage) the k experts are the largest
+    z_t + b, while the combine weights still come from the unbiased p."""
     z = router_logits(u, w_route)
     p = softmax(z)
-    idx = select_topk(p, k)
-    return {"z": z, "p": p, "idx": idx, "a": gate_weights(p, idx, gate),
-            "margin": topk_margin(z, k)}
+    if bias is None:
+        idx = select_topk(p, k)
+        margin = topk_margin(z, k)
+    else:
+        sb = z + np.asarray(bias, dtype=np.float64)[None, :]
+        idx = select_topk(sb, k)
+        margin = topk_margin(sb, k)
+    return {"z": z, "p": p, "idx": idx, "a": gate_weights(p, idx, gate), "margin": margin}
+
+
+# ---------------------------------------------------------------------------
+# Quantile Balancing  (page "Stable LatentMoE interactive demo", QB passage)
+# ---------------------------------------------------------------------------
+#
+# With token t's cutoff a_t held fixed, expert j takes token t exactly when
+# z_tj + b_j >= a_t, i.e. when b_j >= required_tj = a_t - z_tj.  A bias that
+# makes expert j take exactly q tokens is therefore the q-th smallest
+# required_tj over the tokens: one step, no learning rate.  Readings (the page
+# gives only this outline): the score is the router logit z; a_t is the k-th
+# largest z_t + b under the current bias; q = round(k T / N); the histogram
+# estimate uses 256 equal bins over each expert's [min, max] of required and
+# interpolates linearly inside the bin that holds the q-th value.
+
+
+def qb_target(T: int, N: int, k: int) -> int:
+    """Target tokens per expert, q = round(k T / N), at least 1, at most T."""
+    return int(min(T, max(1, int(math.floor(k * T / N + 0.5)))))
+
+
+def qb_cutoff(z: np.ndarray, bias: np.ndarray, k: int) -> np.ndarray:
+    """a_t = the k-th largest of z_t + b (descending order statistic)."""
+    sb = z + np.asarray(bias, dtype=np.float64)[None, :]
+    return -np.sort(-sb, axis=1)[:, k - 1]
+
+
+def qb_required(z: np.ndarray, bias: np.ndarray, k: int) -> np.ndarray:
+    """required[t, j] = a_t - z[t, j]: the smallest b_j that still admits t."""
+    return qb_cutoff(z, bias, k)[:, None] - z
+
+
+def qb_bias_exact(z: np.ndarray, bias: np.ndarray, k: int, q: int) -> np.ndarray:
+    """b'_j = the q-th smallest required[:, j] (1-based q)."""
+    req = qb_required(z, bias, k)
+    return np.sort(req, axis=0)[q - 1, :]
+
+
+def qb_bias_histogram(z: np.ndarray, bias: np.ndarray, k: int, q: int,
+                      bins: int = 256) -> np.ndarray:
+    """Histogram estimate of the q-th smallest required value per expert."""
+    req = qb_required(z, bias, k)
+    T, N = req.shape
+    out = np.empty(N)
+    for j in range(N):
+        col = req[:, j]
+        lo, hi = float(col.min()), float(col.max())
+        if hi <= lo:
+            out[j] = lo
+            continue
+        width = (hi - lo) / bins
+        b = np.minimum(np.floor((col - lo) / width).astype(np.int64), bins - 1)
+        counts = np.bincount(b, minlength=bins)
+        cum = np.cumsum(counts)
+        m = int(np.searchsorted(cum, q))          # first bin with cum >= q
+        before = int(cum[m - 1]) if m > 0 else 0
+        out[j] = lo + width * (m + (q - before) / counts[m])
+    return out
+
+
+def qb_loads(z: np.ndarray, bias: np.ndarray, k: int) -> np.ndarray:
+    """Tokens each expert receives when routing on z + b (no capacity)."""
+    sb = z + np.asarray(bias, dtype=np.float64)[None, :]
+    idx = select_topk(sb, k)
+    return np.bincount(idx.ravel(), minlength=z.shape[1])
 
 
 # ---------------------------------------------------------------------------
@@ -330,16 +412,18 @@ def forward(u_st: np.ndarray, w_route_st: np.ndarray, experts: ExpertFn, *, k: i
             gate: str = "renorm", act: str = "swiglu", capacity: Optional[int] = None,
             beta_g: float = 4.0, beta_u: float = 25.0, alpha: float = 0.01,
             tokens: Optional[np.ndarray] = None,
-            u_rows_st: Optional[np.ndarray] = None) -> Dict[str, object]:
+            u_rows_st: Optional[np.ndarray] = None,
+            bias: Optional[np.ndarray] = None) -> Dict[str, object]:
     """Plain MoE layer.  Routing and dispatch over all T tokens (capacity depends
-    on every token); outputs y for ``tokens`` (all when None).
+    on every token); outputs y for ``tokens`` (all when None); ``bias`` is an
+    optional selection bias (see ``route``).
 
     u_st [T, d], w_route_st [N, d] stored; experts(e) -> stored (gate [h,d],
     up [h,d], down [d,h]).  ``u_rows_st`` may hold the rows of ``tokens`` when
     u_st is only needed for routing (it is the same data)."""
     u = expand(u_st)
     N = w_route_st.shape[0]
-    r = route(u, expand(w_route_st), k, gate)
+    r = route(u, expand(w_route_st), k, gate, bias)
     disp = dispatch(r["idx"], N, capacity)
     x = u if tokens is None else (expand(u_rows_st) if u_rows_st is not None else u[tokens])
     y = combine_routed(x, r, disp, experts, make_act(act, beta_g, beta_u), k, u.shape[1],
@@ -349,13 +433,14 @@ def forward(u_st: np.ndarray, w_route_st: np.ndarray, experts: ExpertFn, *, k: i
 
 def forward_dense(u_st: np.ndarray, w_route_st: np.ndarray, experts: ExpertFn, *, k: int,
                   gate: str = "renorm", act: str = "swiglu", capacity: Optional[int] = None,
-                  beta_g: float = 4.0, beta_u: float = 25.0) -> np.ndarray:
+                  beta_g: float = 4.0, beta_u: float = 25.0,
+                  bias: Optional[np.ndarray] = None) -> np.ndarray:
     """Brute force: evaluate every expert on every token and weight it by the
     token's (kept) combine weight, 0 where unselected."""
     u = expand(u_st)
     T = u.shape[0]
     N = w_route_st.shape[0]
-    r = route(u, expand(w_route_st), k, gate)
+    r = route(u, expand(w_route_st), k, gate, bias)
     disp = dispatch(r["idx"], N, capacity)
     kept = (1 - disp["drop"].reshape(T, k)).astype(np.float64)
     fn = make_act(act, beta_g, beta_u)
@@ -375,12 +460,13 @@ def latent_forward(u_st: np.ndarray, w_route_st: np.ndarray, experts: ExpertFn,
                    capacity: Optional[int] = None, beta_g: float = 4.0,
                    beta_u: float = 25.0, rms_eps: float = 1e-6, alpha: float = 0.01,
                    tokens: Optional[np.ndarray] = None,
-                   u_rows_st: Optional[np.ndarray] = None) -> Dict[str, object]:
+                   u_rows_st: Optional[np.ndarray] = None,
+                   bias: Optional[np.ndarray] = None) -> Dict[str, object]:
     """LatentMoE layer: x_l = W_ldown u; route on u; r = sum a E_i(x_l) at width l;
     y = W_lup RMSNorm(r) + sum_j SwiGLU_j(u) over the shared experts."""
     u = expand(u_st)
     N = w_route_st.shape[0]
-    rt = route(u, expand(w_route_st), k, gate)
+    rt = route(u, expand(w_route_st), k, gate, bias)
     disp = dispatch(rt["idx"], N, capacity)
     ux = u if tokens is None else (expand(u_rows_st) if u_rows_st is not None else u[tokens])
     w_ldown = expand(w_ldown_st)

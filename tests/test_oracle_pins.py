@@ -481,3 +481,108 @@ def test_combine_rows_and_expert_rows_rebuild_forward():
         y_rows = np.stack([rows[r] for r in range(R)])
         y = O.combine_rows(y_rows, d["row_of"], out["a"])
         assert O.relative_error(y, out["y"]) < 1e-14
+
+
+# ---------------------------------------------------------------------------
+# Quantile Balancing (page "Stable LatentMoE interactive demo", QB passage):
+# with the cutoffs a_t fixed, b'_j is the q-th smallest required_tj.
+# ---------------------------------------------------------------------------
+
+
+def _qb_logits(seed, T, N, hot=()):
+    rng = np.random.default_rng(seed)
+    u = rng.normal(size=(T, 64))
+    w = rng.normal(size=(N, 64)) / 8.0
+    for j in hot:
+        w[j] *= 6.0
+    return u @ w.T
+
+
+def test_qb_hand_example():
+    # k = 1, T = 4, N = 2, b = 0: a_t = max_j z_tj = [2, 1, 1, 3];
+    # required columns: expert 0 [0, 0, 1, 0], expert 1 [2, 0.6, 0, 4];
+    # q = round(1 * 4 / 2) = 2, so b' = [0, 0.6] (second smallest of each).
+    z = np.array([[2.0, 0.0], [1.0, 0.4], [0.0, 1.0], [3.0, -1.0]])
+    b0 = np.zeros(2)
+    assert O.qb_target(4, 2, 1) == 2
+    assert np.allclose(O.qb_cutoff(z, b0, 1), [2.0, 1.0, 1.0, 3.0])
+    assert np.allclose(O.qb_required(z, b0, 1), [[0, 2], [0, 0.6], [1, 0], [0, 4]])
+    assert np.allclose(O.qb_bias_exact(z, b0, 1, 2), [0.0, 0.6])
+
+
+def test_qb_exact_is_the_q_th_order_statistic():
+    # Fewer than q tokens need strictly less bias than b'_j, at least q need at
+    # most b'_j: the defining property of the q-th smallest required value.
+    for seed, (T, N, k) in enumerate(((200, 8, 2), (333, 24, 3), (64, 5, 1))):
+        z = _qb_logits(seed, T, N)
+        b = np.random.default_rng(seed + 50).normal(size=N) * 0.3
+        q = O.qb_target(T, N, k)
+        bx = O.qb_bias_exact(z, b, k, q)
+        req = O.qb_required(z, b, k)
+        assert np.all((req < bx[None, :]).sum(axis=0) < q)
+        assert np.all((req <= bx[None, :]).sum(axis=0) >= q)
+
+
+def test_qb_shift_of_the_bias_shifts_the_update():
+    # Adding c to every b_j leaves the selection alone and raises every cutoff
+    # by c, so every required value and the update shift by c.
+    z = _qb_logits(3, 300, 12)
+    b = np.random.default_rng(4).normal(size=12) * 0.2
+    q = O.qb_target(300, 12, 2)
+    for c in (0.75, -3.0):
+        assert np.allclose(O.qb_bias_exact(z, b + c, 2, q), O.qb_bias_exact(z, b, 2, q) + c,
+                           atol=1e-12)
+        assert np.allclose(O.qb_bias_histogram(z, b + c, 2, q),
+                           O.qb_bias_histogram(z, b, 2, q) + c, atol=1e-9)
+
+
+def test_qb_histogram_within_one_bin_of_exact():
+    for seed, (T, N, k) in enumerate(((500, 16, 2), (2000, 8, 1), (100, 40, 4))):
+        z = _qb_logits(seed + 10, T, N)
+        b = np.zeros(N)
+        q = O.qb_target(T, N, k)
+        req = O.qb_required(z, b, k)
+        width = (req.max(axis=0) - req.min(axis=0)) / 256
+        err = np.abs(O.qb_bias_histogram(z, b, k, q) - O.qb_bias_exact(z, b, k, q))
+        assert np.all(err <= width * (1 + 1e-9))
+
+
+def test_qb_zero_bias_is_plain_routing():
+    rng = np.random.default_rng(8)
+    u = rng.normal(size=(50, 32))
+    w = rng.normal(size=(10, 32))
+    r0 = O.route(u, w, 3, "renorm")
+    rb = O.route(u, w, 3, "renorm", bias=np.zeros(10))
+    assert np.array_equal(r0["idx"], rb["idx"])
+    assert np.allclose(r0["a"], rb["a"], atol=0)
+
+
+def test_qb_bias_moves_selection_but_not_weights_source():
+    # A large bias on one expert makes every token select it, and its weight is
+    # still the renormalised unbiased probability.
+    rng = np.random.default_rng(9)
+    u = rng.normal(size=(30, 16))
+    w = rng.normal(size=(6, 16))
+    b = np.zeros(6)
+    b[4] = 1e3
+    r = O.route(u, w, 2, "renorm", bias=b)
+    assert np.all(r["idx"][:, 0] == 4)
+    p = O.softmax(O.router_logits(u, w))
+    ps = np.take_along_axis(p, r["idx"], axis=1)
+    assert np.allclose(r["a"], ps / ps.sum(axis=1, keepdims=True), rtol=1e-14)
+
+
+def test_qb_update_cools_hot_experts():
+    # Two experts with 6x router rows take far more than their share; a few
+    # Quantile Balancing steps (each recomputing the cutoffs) bring the
+    # busiest expert much closer to the target load.
+    T, N, k = 4000, 16, 2
+    z = _qb_logits(12, T, N, hot=(0, 1))
+    q = O.qb_target(T, N, k)
+    b = np.zeros(N)
+    before = O.qb_loads(z, b, k).max()
+    for _ in range(3):
+        b = O.qb_bias_exact(z, b, k, q)
+    after = O.qb_loads(z, b, k).max()
+    assert before > 3 * q
+    assert after < 1.5 * q
