@@ -129,10 +129,36 @@ def run_workload(cfg, steps, warmup):
                  for j, s in enumerate(stages)}
     per_step = [ev[i][0].elapsed_time(ev[i][-1]) for i in range(steps)]
     kept = np.diff(H.to_host(out["kept_offsets"]))
-    return {"ms_per_step": total_ms / steps, "stages_ms": per_stage,
-            "traced_step_ms": {"median": float(np.median(per_step)), "min": float(np.min(per_step)),
-                               "mean": float(np.mean(per_step))},
-            "alg": algorithmic(cfg, kept), "desc": desc}
+    r = {"ms_per_step": total_ms / steps, "stages_ms": per_stage,
+         "traced_step_ms": {"median": float(np.median(per_step)), "min": float(np.min(per_step)),
+                            "mean": float(np.mean(per_step))},
+         "alg": algorithmic(cfg, kept), "desc": desc}
+    if cfg.act_dtype == "bf16" and cfg.router_dtype == "bf16":
+        r["quantile_balancing"] = time_qb(moe, desc, u, w["W_route"], ws, cfg, steps)
+    return r
+
+
+def time_qb(moe, desc, u, w_route, ws, cfg, steps):
+    """One Quantile Balancing bias update (router logits, cutoffs, per-expert
+    quantile) from zero bias, exact and histogram, averaged over `steps`."""
+    import torch
+
+    nb = torch.empty(cfg.N, dtype=torch.float32, device="cuda")
+    res = {}
+    for name, method in (("exact_ms", moe.QB_EXACT), ("histogram_ms", moe.QB_HISTOGRAM)):
+        for _ in range(2):
+            moe.moe_qb_update(desc, u, w_route, None, nb, ws, method=method)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(steps):
+            moe.moe_qb_update(desc, u, w_route, None, nb, ws, method=method)
+        b.record()
+        torch.cuda.synchronize()
+        res[name] = a.elapsed_time(b) / steps
+    res["q"] = int((2 * cfg.k * cfg.T + cfg.N) // (2 * cfg.N))
+    return res
 
 
 def cpu_baseline(cfg, n_tokens):
@@ -218,6 +244,8 @@ def main():
         "stages_ms": r["stages_ms"],
         "roofline": roof,
     }
+    if "quantile_balancing" in r:
+        line["quantile_balancing"] = r["quantile_balancing"]
     if args.decode_workload:
         dc = C.ALL[args.decode_workload]
         print(f"[bench] {dc.name}", file=sys.stderr, flush=True)

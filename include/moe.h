@@ -99,10 +99,14 @@ typedef struct moe_desc {
    W_ldown [l, d]; W_lup [d, l]; Ws_gate, Ws_up [n_shared, h_shared, d];
    Ws_down [n_shared, d, h_shared].  Unused pointers may be null.
    Each expert's matrices are contiguous and experts follow one another, so
-   only the selected experts' bytes are ever read. */
+   only the selected experts' bytes are ever read.
+   selection_bias [N] fp32, nullable: the router picks the top-k of z + b
+   (Quantile Balancing bias, see moe_qb_update) while the combine weights
+   still come from the unbiased softmax; null = no bias. */
 typedef struct moe_weights {
   const void *W_route, *W_gate, *W_up, *W_down;
   const void *W_ldown, *W_lup, *Ws_gate, *Ws_up, *Ws_down;
+  const float *selection_bias;
 } moe_weights_t;
 
 /* Optional outputs of moe_forward (device pointers; each may be null, the
@@ -141,6 +145,36 @@ int32_t moe_capacity_from_factor(int64_t T, int32_t N, int32_t k, double c);
 moe_status_t moe_route(const moe_desc_t *desc, const void *u, const void *W_route,
                        int32_t *topk_idx, float *topk_w, float *stats, void *ws,
                        size_t ws_bytes, moe_stream_t stream);
+
+/* moe_route with a selection bias (page "Stable LatentMoE interactive demo",
+   Quantile Balancing passage): topk_idx holds the k largest z + bias (ties to
+   the lower index, by descending z + bias), topk_w the weights from the
+   unbiased p (renormalised over the selected set, or p itself for
+   MOE_GATE_PROB), and stats keep the unbiased arg-max for f.
+     bias [N] fp32 device pointer; null gives moe_route exactly. */
+moe_status_t moe_route_biased(const moe_desc_t *desc, const void *u, const void *W_route,
+                              const float *bias, int32_t *topk_idx, float *topk_w,
+                              float *stats, void *ws, size_t ws_bytes, moe_stream_t stream);
+
+/* One Quantile Balancing step (same passage): with each token's cutoff a_t,
+   the k-th largest z_t + bias, held fixed, expert j admits token t exactly
+   when bias_j >= a_t - z_tj, so the bias that admits q tokens is the q-th
+   smallest of required_tj = a_t - z_tj over the T tokens.
+     u        [T, d] bf16; W_route [N, d] bf16 (the router's logits z are
+              computed on the MFMA path: needs act and router dtype bf16)
+     bias     [N] fp32 in, nullable (null = zeros): the current bias
+     q        target tokens per expert, 1..T; q <= 0 selects round(k T / N)
+     method   0: exact q-th smallest (radix select);
+              1: estimate from a 256-bin histogram over each expert's
+                 [min, max] of required, linear inside the bin (within one bin
+                 width of the exact value)
+     new_bias [N] fp32 out (may equal bias only if the caller does not need
+              the old values; the update reads bias before writing new_bias)
+   MOE_ERR_ARG for q > T or an unknown method; MOE_ERR_UNSUPPORTED for fp32
+   activations or router weights. */
+moe_status_t moe_qb_update(const moe_desc_t *desc, const void *u, const void *W_route,
+                           const float *bias, int32_t q, int32_t method, float *new_bias,
+                           void *ws, size_t ws_bytes, moe_stream_t stream);
 
 /* Dispatch: group the T*k (token, slot) entries e = t*k + s by expert in
    token order (sections 3.5, 3.6, 3.8).

@@ -14,8 +14,9 @@ MOE_ACT_SWIGLU, MOE_ACT_SITU_GLU = 0, 1
 
 # Every symbol include/moe.h declares.
 EXPORTS = ("moe_desc_init", "moe_status_string", "moe_workspace_bytes",
-           "moe_capacity_from_factor", "moe_route", "moe_dispatch", "moe_expert_ffn",
-           "moe_combine", "moe_forward", "moe_forward_traced", "moe_stage_name")
+           "moe_capacity_from_factor", "moe_route", "moe_route_biased", "moe_qb_update",
+           "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward", "moe_forward_traced",
+           "moe_stage_name")
 
 
 class MoeDesc(ctypes.Structure):
@@ -30,7 +31,8 @@ class MoeDesc(ctypes.Structure):
 
 class MoeWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("W_route", "W_gate", "W_up", "W_down", "W_ldown",
-                                                "W_lup", "Ws_gate", "Ws_up", "Ws_down")]
+                                                "W_lup", "Ws_gate", "Ws_up", "Ws_down",
+                                                "selection_bias")]
 
 
 class MoeOutputs(ctypes.Structure):
@@ -67,6 +69,10 @@ def load() -> ctypes.CDLL:
     lib.moe_capacity_from_factor.restype = I32
     lib.moe_route.argtypes = [D, P, P, P, P, P, P, SZ, P]
     lib.moe_route.restype = I32
+    lib.moe_route_biased.argtypes = [D, P, P, P, P, P, P, P, SZ, P]
+    lib.moe_route_biased.restype = I32
+    lib.moe_qb_update.argtypes = [D, P, P, P, I32, I32, P, P, SZ, P]
+    lib.moe_qb_update.restype = I32
     lib.moe_dispatch.argtypes = [D, P, P, P, P, P, P, P, P, SZ, P]
     lib.moe_dispatch.restype = I32
     lib.moe_expert_ffn.argtypes = [D, P, P, P, P, P, P, P, P, P, SZ, P]

@@ -94,6 +94,25 @@ def moe_route(desc, u, W_route, topk_idx, topk_w, stats, ws, stream=None) -> Non
            "moe_route")
 
 
+def moe_route_biased(desc, u, W_route, bias, topk_idx, topk_w, stats, ws, stream=None) -> None:
+    """moe_route picking the top-k of z + bias (bias: [N] fp32 device tensor or None)."""
+    _check(L.load().moe_route_biased(ctypes.byref(desc), _ptr(u), _ptr(W_route), _ptr(bias),
+                                     _ptr(topk_idx), _ptr(topk_w), _ptr(stats), _ptr(ws),
+                                     ws.numel(), _stream(stream)), "moe_route_biased")
+
+
+QB_EXACT, QB_HISTOGRAM = 0, 1
+
+
+def moe_qb_update(desc, u, W_route, bias, new_bias, ws, q=0, method=QB_EXACT,
+                  stream=None) -> None:
+    """One Quantile Balancing step: new_bias[j] = q-th smallest (or its
+    histogram estimate) of cutoff_t - z_tj; q = 0 selects round(kT/N)."""
+    _check(L.load().moe_qb_update(ctypes.byref(desc), _ptr(u), _ptr(W_route), _ptr(bias),
+                                  int(q), int(method), _ptr(new_bias), _ptr(ws), ws.numel(),
+                                  _stream(stream)), "moe_qb_update")
+
+
 def moe_dispatch(desc, topk_idx, counts, offsets, kept_offsets, perm, row_of, drop, ws,
                  stream=None) -> None:
     _check(L.load().moe_dispatch(ctypes.byref(desc), _ptr(topk_idx), _ptr(counts), _ptr(offsets),

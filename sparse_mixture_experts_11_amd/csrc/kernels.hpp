@@ -11,13 +11,15 @@ namespace moe {
 // Waves the router kernels launch for T tokens (sizes the stats partials).
 int route_waves(int64_t T, int N);
 // Wave-per-token-group router for N <= 64: scores, softmax, top-k, weights.
+// bias: optional [N] selection bias (top-k of z + bias; weights from the
+// unbiased softmax).
 hipError_t launch_route_wave(const void *u, bool u_bf16, const void *W, bool w_bf16, int64_t T,
-                             int d, int N, int k, int gate, int32_t *idx, float *w,
-                             float *part_p, int32_t *part_cnt, hipStream_t st);
+                             int d, int N, int k, int gate, const float *bias, int32_t *idx,
+                             float *w, float *part_p, int32_t *part_cnt, hipStream_t st);
 // Softmax + top-k from materialised fp32 logits [T, N] (N <= 1024).
 hipError_t launch_topk_logits(const float *logits, int64_t T, int N, int k, int gate,
-                              int32_t *idx, float *w, float *part_p, int32_t *part_cnt,
-                              hipStream_t st);
+                              const float *bias, int32_t *idx, float *w, float *part_p,
+                              int32_t *part_cnt, hipStream_t st);
 // f, P, N sum fP, alpha N sum fP from the per-wave partials.
 hipError_t launch_stats_finalize(const float *part_p, const int32_t *part_cnt, int waves,
                                  int64_t T, int N, float alpha, float *stats, hipStream_t st);
@@ -75,6 +77,13 @@ int64_t gemm_mtile_bound(int64_t rows_total, int groups, int bm);
 hipError_t launch_tile_prefix(const int32_t *kept_offsets, int G, int bm, int32_t *tile_start,
                               hipStream_t st);
 hipError_t launch_gemm(const GemmArgs &a, int epi, int64_t mtiles_bound, hipStream_t st);
+
+// ---- Quantile Balancing (qb.hip) -------------------------------------------
+// One update from the fp32 logits [T, N]: req [N, T] scratch; new_bias [N]
+// gets the q-th smallest (method 0) or its histogram estimate (method 1) of
+// required = cutoff - z per expert.
+hipError_t launch_qb_update(const float *logits, int64_t T, int N, int k, const float *bias, int q,
+                            int method, float *req, float *new_bias, hipStream_t st);
 
 // ---- decode-sized experts (decode.hip) -------------------------------------
 // Max rows per expert the decode kernels take.

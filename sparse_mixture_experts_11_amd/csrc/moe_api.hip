@@ -28,6 +28,7 @@ struct Layout {
   size_t idx, w, stats, part_p, part_cnt, logits;
   size_t counts, offsets, kept_offsets, perm, row_of, drop, blk_counts, tile_start;
   size_t x_l, hid, y_perm, rn, hs, ys;
+  size_t qb_logits, qb_req;  // Quantile Balancing: logits [T, N], required [N, T]
   size_t total;
 };
 
@@ -83,6 +84,8 @@ Layout layout(const moe_desc_t &d) {
       L.ys = take((size_t)d.n_shared * d.T * d.d * 4);
     }
   }
+  L.qb_logits = take((size_t)d.T * d.N * 4);
+  L.qb_req = take((size_t)d.T * d.N * 4);
   L.total = off;
   return L;
 }
@@ -158,7 +161,8 @@ moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ER
 // ---- stages (no validation; callers validated) ------------------------------
 
 hipError_t do_route(const moe_desc_t &d, const Layout &L, const void *u, const void *W_route,
-                    int32_t *idx, float *w, float *stats, void *ws, hipStream_t st) {
+                    const float *bias, int32_t *idx, float *w, float *stats, void *ws,
+                    hipStream_t st) {
   float *pp = region<float>(ws, L.part_p);
   int32_t *pc = region<int32_t>(ws, L.part_cnt);
   hipError_t e;
@@ -177,10 +181,11 @@ hipError_t do_route(const moe_desc_t &d, const Layout &L, const void *u, const v
     a.ldo = d.N;
     e = launch_gemm(a, EP_F32, 0, st);
     if (e != hipSuccess) return e;
-    e = launch_topk_logits(region<float>(ws, L.logits), d.T, d.N, d.k, d.gate, idx, w, pp, pc, st);
+    e = launch_topk_logits(region<float>(ws, L.logits), d.T, d.N, d.k, d.gate, bias, idx, w, pp,
+                           pc, st);
   } else {
     e = launch_route_wave(u, d.act_dtype == MOE_BF16, W_route, d.router_dtype == MOE_BF16, d.T,
-                          d.d, d.N, d.k, d.gate, idx, w, pp, pc, st);
+                          d.d, d.N, d.k, d.gate, bias, idx, w, pp, pc, st);
   }
   if (e != hipSuccess || stats == nullptr) return e;
   return launch_stats_finalize(pp, pc, route_waves(d.T, d.N), d.T, d.N, d.aux_alpha, stats, st);
@@ -378,7 +383,8 @@ moe_status_t forward_impl(const moe_desc_t *desc, const moe_weights_t *wts, cons
   MOE_TRY(tr.mark());
   // Small inputs finish the statistics inside the dispatch launch.
   const bool fused_stats = small_tail(d);
-  MOE_TRY(do_route(d, L, u, wts->W_route, idx, tw, fused_stats ? nullptr : stats, ws, st));
+  MOE_TRY(do_route(d, L, u, wts->W_route, wts->selection_bias, idx, tw,
+                   fused_stats ? nullptr : stats, ws, st));
   MOE_TRY(tr.mark());
   MOE_TRY(do_dispatch(d, L, idx, counts, offsets, kept_offsets, perm, row_of, drop,
                       fused_stats ? stats : nullptr, ws, st));
@@ -474,17 +480,53 @@ int32_t moe_capacity_from_factor(int64_t T, int32_t N, int32_t k, double c) {
   return (int32_t)v;
 }
 
-moe_status_t moe_route(const moe_desc_t *desc, const void *u, const void *W_route,
-                       int32_t *topk_idx, float *topk_w, float *stats, void *ws, size_t ws_bytes,
-                       moe_stream_t stream) {
+moe_status_t moe_route_biased(const moe_desc_t *desc, const void *u, const void *W_route,
+                              const float *bias, int32_t *topk_idx, float *topk_w,
+                              float *stats, void *ws, size_t ws_bytes, moe_stream_t stream) {
   const moe_status_t v = validate(desc);
   if (v != MOE_OK) return v;
   if (u == nullptr || W_route == nullptr || topk_idx == nullptr || topk_w == nullptr)
     return MOE_ERR_ARG;
   const Layout L = layout(*desc);
   if (ws == nullptr || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
-  return hip_status(do_route(*desc, L, u, W_route, topk_idx, topk_w, stats, ws,
+  return hip_status(do_route(*desc, L, u, W_route, bias, topk_idx, topk_w, stats, ws,
                              reinterpret_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_route(const moe_desc_t *desc, const void *u, const void *W_route,
+                       int32_t *topk_idx, float *topk_w, float *stats, void *ws, size_t ws_bytes,
+                       moe_stream_t stream) {
+  return moe_route_biased(desc, u, W_route, nullptr, topk_idx, topk_w, stats, ws, ws_bytes,
+                          stream);
+}
+
+moe_status_t moe_qb_update(const moe_desc_t *desc, const void *u, const void *W_route,
+                           const float *bias, int32_t q, int32_t method, float *new_bias,
+                           void *ws, size_t ws_bytes, moe_stream_t stream) {
+  const moe_status_t v = validate(desc);
+  if (v != MOE_OK) return v;
+  const moe_desc_t &d = *desc;
+  if (u == nullptr || W_route == nullptr || new_bias == nullptr) return MOE_ERR_ARG;
+  if (method != 0 && method != 1) return MOE_ERR_ARG;
+  if (q > d.T) return MOE_ERR_ARG;
+  // The logits come from the bf16 MFMA GEMM (d is a multiple of 128 here).
+  if (d.act_dtype != MOE_BF16 || d.router_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  const Layout L = layout(d);
+  if (ws == nullptr || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  // q <= 0: round(k T / N) = floor((2 k T + N) / (2 N)), clamped to [1, T].
+  int64_t qq = q;
+  if (qq <= 0) {
+    qq = (2 * (int64_t)d.k * d.T + d.N) / (2 * (int64_t)d.N);
+    if (qq < 1) qq = 1;
+    if (qq > d.T) qq = d.T;
+  }
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  float *logits = region<float>(ws, L.qb_logits);
+  MOE_TRY(dense_gemm(static_cast<const uint16_t *>(u), d.d, 0,
+                     static_cast<const uint16_t *>(W_route), nullptr, 0, d.d, d.N, 1, d.T, logits,
+                     d.N, EP_F32, nullptr, nullptr, 0, st));
+  return hip_status(launch_qb_update(logits, d.T, d.N, d.k, bias, (int)qq, method,
+                                     region<float>(ws, L.qb_req), new_bias, st));
 }
 
 moe_status_t moe_dispatch(const moe_desc_t *desc, const int32_t *topk_idx, int32_t *counts,

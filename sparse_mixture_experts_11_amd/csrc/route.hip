@@ -34,13 +34,15 @@ __device__ __forceinline__ void load8(const void *base, int64_t off, float (&x)[
 }
 
 // Selection and weights for one token whose N scores z[] every lane holds.
-// Lane s < k ends with the s-th selected expert (descending z, ties to the
-// lower index) and writes it; lane n < N accumulates the statistics of
-// expert n.
+// Lane s < k ends with the s-th selected expert (descending z, or descending
+// z + bias with a selection bias; ties to the lower index) and writes it; the
+// weights come from the unbiased softmax.  Lane n < N accumulates the
+// statistics of expert n (f counts the unbiased arg-max).
 template <int NMAX>
 __device__ __forceinline__ void select_and_write(const float (&z)[NMAX], int N, int k, int gate,
-                                                 int64_t t, int lane, int32_t *idx, float *w,
-                                                 float &acc_p, int &acc_cnt) {
+                                                 const float *bias, int64_t t, int lane,
+                                                 int32_t *idx, float *w, float &acc_p,
+                                                 int &acc_cnt) {
   float m = -INFINITY;
 #pragma unroll
   for (int n = 0; n < NMAX; ++n)
@@ -57,18 +59,32 @@ __device__ __forceinline__ void select_and_write(const float (&z)[NMAX], int N, 
 #pragma unroll
   for (int n = 0; n < NMAX; ++n)
     if (n == lane) mine_p = e[n] * inv;
+  float zs[NMAX];  // selection scores
+#pragma unroll
+  for (int n = 0; n < NMAX; ++n) zs[n] = (bias != nullptr && n < N) ? z[n] + bias[n] : z[n];
+  int first = 0;  // unbiased arg-max (ties: lower index), for f
+  if (bias != nullptr) {
+    float bz = -INFINITY;
+    int best = -1;
+#pragma unroll
+    for (int n = 0; n < NMAX; ++n)
+      if (n < N && (best < 0 || z[n] > bz)) {
+        best = n;
+        bz = z[n];
+      }
+    first = best;
+  }
   uint64_t taken = 0;
   int my_idx = 0;
   float my_p = 0.f;
-  int first = 0;
   for (int sl = 0; sl < k; ++sl) {
     int best = -1;
     float bz = -INFINITY;
 #pragma unroll
     for (int n = 0; n < NMAX; ++n) {
-      if (n < N && !((taken >> n) & 1ull) && (best < 0 || z[n] > bz)) {
+      if (n < N && !((taken >> n) & 1ull) && (best < 0 || zs[n] > bz)) {
         best = n;
-        bz = z[n];
+        bz = zs[n];
       }
     }
     float bp = 0.f;
@@ -76,7 +92,7 @@ __device__ __forceinline__ void select_and_write(const float (&z)[NMAX], int N, 
     for (int n = 0; n < NMAX; ++n)
       if (n == best) bp = e[n] * inv;
     taken |= 1ull << best;
-    if (sl == 0) first = best;
+    if (sl == 0 && bias == nullptr) first = best;
     if (lane == sl) {
       my_idx = best;
       my_p = bp;
@@ -94,8 +110,8 @@ __device__ __forceinline__ void select_and_write(const float (&z)[NMAX], int N, 
 template <bool UB, bool WB, int NMAX, int TPW>
 __global__ __launch_bounds__(kRouteBlock) void route_wave_kernel(
     const void *__restrict__ u, const void *__restrict__ W, int64_t T, int d, int N, int k,
-    int gate, int32_t *__restrict__ idx, float *__restrict__ w, float *__restrict__ part_p,
-    int32_t *__restrict__ part_cnt) {
+    int gate, const float *__restrict__ bias, int32_t *__restrict__ idx, float *__restrict__ w,
+    float *__restrict__ part_p, int32_t *__restrict__ part_cnt) {
   const int lane = threadIdx.x & 63;
   const int wave = blockIdx.x * (kRouteBlock / 64) + (threadIdx.x >> 6);
   const int nwaves = gridDim.x * (kRouteBlock / 64);
@@ -133,7 +149,8 @@ __global__ __launch_bounds__(kRouteBlock) void route_wave_kernel(
       float z[NMAX];
 #pragma unroll
       for (int n = 0; n < NMAX; ++n) z[n] = (n < N) ? wave_sum(acc[i][n]) : 0.f;
-      if (t0 + i < T) select_and_write<NMAX>(z, N, k, gate, t0 + i, lane, idx, w, acc_p, acc_cnt);
+      if (t0 + i < T)
+        select_and_write<NMAX>(z, N, k, gate, bias, t0 + i, lane, idx, w, acc_p, acc_cnt);
     }
   }
   if (part_p != nullptr && lane < N) {
@@ -148,8 +165,8 @@ __global__ __launch_bounds__(kRouteBlock) void route_wave_kernel(
 template <bool UB, bool WB, int NMAX>
 __global__ __launch_bounds__(kSmallBlock) void route_small_kernel(
     const void *__restrict__ u, const void *__restrict__ W, int64_t T, int d, int N, int k,
-    int gate, int32_t *__restrict__ idx, float *__restrict__ w, float *__restrict__ part_p,
-    int32_t *__restrict__ part_cnt) {
+    int gate, const float *__restrict__ bias, int32_t *__restrict__ idx, float *__restrict__ w,
+    float *__restrict__ part_p, int32_t *__restrict__ part_cnt) {
   __shared__ float red[kSmallBlock / 64][NMAX];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -185,7 +202,7 @@ __global__ __launch_bounds__(kSmallBlock) void route_small_kernel(
            red[7][n];
   float acc_p = 0.f;
   int acc_cnt = 0;
-  select_and_write<NMAX>(z, N, k, gate, t, lane, idx, w, acc_p, acc_cnt);
+  select_and_write<NMAX>(z, N, k, gate, bias, t, lane, idx, w, acc_p, acc_cnt);
   if (part_p != nullptr && lane < N) {
     part_p[t * N + lane] = acc_p;
     part_cnt[t * N + lane] = acc_cnt;
@@ -195,8 +212,9 @@ __global__ __launch_bounds__(kSmallBlock) void route_small_kernel(
 // One wave per token over materialised logits, N <= 64 * NPL.
 template <int NPL>
 __global__ __launch_bounds__(kRouteBlock) void topk_logits_kernel(
-    const float *__restrict__ logits, int64_t T, int N, int k, int gate, int32_t *__restrict__ idx,
-    float *__restrict__ w, float *__restrict__ part_p, int32_t *__restrict__ part_cnt) {
+    const float *__restrict__ logits, int64_t T, int N, int k, int gate,
+    const float *__restrict__ bias, int32_t *__restrict__ idx, float *__restrict__ w,
+    float *__restrict__ part_p, int32_t *__restrict__ part_cnt) {
   const int lane = threadIdx.x & 63;
   const int wave = blockIdx.x * (kRouteBlock / 64) + (threadIdx.x >> 6);
   const int nwaves = gridDim.x * (kRouteBlock / 64);
@@ -227,8 +245,37 @@ __global__ __launch_bounds__(kRouteBlock) void topk_logits_kernel(
     }
     s = wave_sum(s);
     const float inv = 1.0f / s;
+    float zs[NPL];  // selection scores
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+      const int n = lane + 64 * j;
+      zs[j] = (bias != nullptr && n < N) ? z[j] + bias[n] : z[j];
+    }
+    int first = 0;  // unbiased arg-max (ties: lower index), for f
+    if (bias != nullptr) {
+      float bz = -INFINITY;
+      int bn = 0x7FFFFFFF;
+#pragma unroll
+      for (int j = 0; j < NPL; ++j) {
+        const int n = lane + 64 * j;
+        if (n < N && (bn == 0x7FFFFFFF || z[j] > bz)) {
+          bz = z[j];
+          bn = n;
+        }
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        const float oz = __shfl_xor(bz, o, 64);
+        const int on = __shfl_xor(bn, o, 64);
+        if (oz > bz || (oz == bz && on < bn)) {
+          bz = oz;
+          bn = on;
+        }
+      }
+      first = bn;
+    }
     uint32_t taken = 0;
-    int my_idx = 0, first = 0;
+    int my_idx = 0;
     float my_p = 0.f;
     for (int sl = 0; sl < k; ++sl) {
       // Local best among this lane's untaken experts (ties: lower index).
@@ -238,8 +285,8 @@ __global__ __launch_bounds__(kRouteBlock) void topk_logits_kernel(
 #pragma unroll
       for (int j = 0; j < NPL; ++j) {
         const int n = lane + 64 * j;
-        if (n < N && !((taken >> j) & 1u) && (bn == 0x7FFFFFFF || z[j] > bz)) {
-          bz = z[j];
+        if (n < N && !((taken >> j) & 1u) && (bn == 0x7FFFFFFF || zs[j] > bz)) {
+          bz = zs[j];
           bn = n;
           bp = e[j] * inv;
         }
@@ -257,7 +304,7 @@ __global__ __launch_bounds__(kRouteBlock) void topk_logits_kernel(
         }
       }
       if ((bn & 63) == lane) taken |= 1u << (bn >> 6);
-      if (sl == 0) first = bn;
+      if (sl == 0 && bias == nullptr) first = bn;
       if (lane == sl) {
         my_idx = bn;
         my_p = bp;
@@ -338,34 +385,34 @@ __global__ __launch_bounds__(1024) void stats_total_kernel(int N, float alpha,
 
 template <bool UB, bool WB, int NMAX, int TPW>
 hipError_t launch_rw(const void *u, const void *W, int64_t T, int d, int N, int k, int gate,
-                     int32_t *idx, float *w, float *pp, int32_t *pc, hipStream_t st) {
+                     const float *bias, int32_t *idx, float *w, float *pp, int32_t *pc, hipStream_t st) {
   const int waves = route_waves(T, N);
   hipLaunchKernelGGL((route_wave_kernel<UB, WB, NMAX, TPW>), dim3(waves / 4), dim3(kRouteBlock), 0,
-                     st, u, W, T, d, N, k, gate, idx, w, pp, pc);
+                     st, u, W, T, d, N, k, gate, bias, idx, w, pp, pc);
   return hipGetLastError();
 }
 
 template <bool UB, bool WB, int NMAX>
 hipError_t launch_rs(const void *u, const void *W, int64_t T, int d, int N, int k, int gate,
-                     int32_t *idx, float *w, float *pp, int32_t *pc, hipStream_t st) {
+                     const float *bias, int32_t *idx, float *w, float *pp, int32_t *pc, hipStream_t st) {
   hipLaunchKernelGGL((route_small_kernel<UB, WB, NMAX>), dim3((unsigned)T), dim3(kSmallBlock), 0,
-                     st, u, W, T, d, N, k, gate, idx, w, pp, pc);
+                     st, u, W, T, d, N, k, gate, bias, idx, w, pp, pc);
   return hipGetLastError();
 }
 
 template <bool UB, bool WB>
 hipError_t launch_rw_n(const void *u, const void *W, int64_t T, int d, int N, int k, int gate,
-                       int32_t *idx, float *w, float *pp, int32_t *pc, hipStream_t st) {
+                       const float *bias, int32_t *idx, float *w, float *pp, int32_t *pc, hipStream_t st) {
   if (T <= kRouteSmallT) {
-    if (N <= 8) return launch_rs<UB, WB, 8>(u, W, T, d, N, k, gate, idx, w, pp, pc, st);
-    if (N <= 16) return launch_rs<UB, WB, 16>(u, W, T, d, N, k, gate, idx, w, pp, pc, st);
-    if (N <= 32) return launch_rs<UB, WB, 32>(u, W, T, d, N, k, gate, idx, w, pp, pc, st);
-    return launch_rs<UB, WB, 64>(u, W, T, d, N, k, gate, idx, w, pp, pc, st);
+    if (N <= 8) return launch_rs<UB, WB, 8>(u, W, T, d, N, k, gate, bias, idx, w, pp, pc, st);
+    if (N <= 16) return launch_rs<UB, WB, 16>(u, W, T, d, N, k, gate, bias, idx, w, pp, pc, st);
+    if (N <= 32) return launch_rs<UB, WB, 32>(u, W, T, d, N, k, gate, bias, idx, w, pp, pc, st);
+    return launch_rs<UB, WB, 64>(u, W, T, d, N, k, gate, bias, idx, w, pp, pc, st);
   }
-  if (N <= 8) return launch_rw<UB, WB, 8, 4>(u, W, T, d, N, k, gate, idx, w, pp, pc, st);
-  if (N <= 16) return launch_rw<UB, WB, 16, 2>(u, W, T, d, N, k, gate, idx, w, pp, pc, st);
-  if (N <= 32) return launch_rw<UB, WB, 32, 1>(u, W, T, d, N, k, gate, idx, w, pp, pc, st);
-  return launch_rw<UB, WB, 64, 1>(u, W, T, d, N, k, gate, idx, w, pp, pc, st);
+  if (N <= 8) return launch_rw<UB, WB, 8, 4>(u, W, T, d, N, k, gate, bias, idx, w, pp, pc, st);
+  if (N <= 16) return launch_rw<UB, WB, 16, 2>(u, W, T, d, N, k, gate, bias, idx, w, pp, pc, st);
+  if (N <= 32) return launch_rw<UB, WB, 32, 1>(u, W, T, d, N, k, gate, bias, idx, w, pp, pc, st);
+  return launch_rw<UB, WB, 64, 1>(u, W, T, d, N, k, gate, bias, idx, w, pp, pc, st);
 }
 
 }  // namespace
@@ -385,27 +432,27 @@ int route_waves(int64_t T, int N) {
 }
 
 hipError_t launch_route_wave(const void *u, bool u_bf16, const void *W, bool w_bf16, int64_t T,
-                             int d, int N, int k, int gate, int32_t *idx, float *w,
-                             float *part_p, int32_t *part_cnt, hipStream_t st) {
-  if (u_bf16 && w_bf16) return launch_rw_n<true, true>(u, W, T, d, N, k, gate, idx, w, part_p, part_cnt, st);
-  if (u_bf16) return launch_rw_n<true, false>(u, W, T, d, N, k, gate, idx, w, part_p, part_cnt, st);
-  if (w_bf16) return launch_rw_n<false, true>(u, W, T, d, N, k, gate, idx, w, part_p, part_cnt, st);
-  return launch_rw_n<false, false>(u, W, T, d, N, k, gate, idx, w, part_p, part_cnt, st);
+                             int d, int N, int k, int gate, const float *bias, int32_t *idx,
+                             float *w, float *part_p, int32_t *part_cnt, hipStream_t st) {
+  if (u_bf16 && w_bf16) return launch_rw_n<true, true>(u, W, T, d, N, k, gate, bias, idx, w, part_p, part_cnt, st);
+  if (u_bf16) return launch_rw_n<true, false>(u, W, T, d, N, k, gate, bias, idx, w, part_p, part_cnt, st);
+  if (w_bf16) return launch_rw_n<false, true>(u, W, T, d, N, k, gate, bias, idx, w, part_p, part_cnt, st);
+  return launch_rw_n<false, false>(u, W, T, d, N, k, gate, bias, idx, w, part_p, part_cnt, st);
 }
 
 hipError_t launch_topk_logits(const float *logits, int64_t T, int N, int k, int gate,
-                              int32_t *idx, float *w, float *part_p, int32_t *part_cnt,
-                              hipStream_t st) {
+                              const float *bias, int32_t *idx, float *w, float *part_p,
+                              int32_t *part_cnt, hipStream_t st) {
   const int waves = route_waves(T, N);
   const dim3 grid(waves / 4), block(kRouteBlock);
   if (N <= 256)
-    hipLaunchKernelGGL(topk_logits_kernel<4>, grid, block, 0, st, logits, T, N, k, gate, idx, w,
+    hipLaunchKernelGGL(topk_logits_kernel<4>, grid, block, 0, st, logits, T, N, k, gate, bias, idx, w,
                        part_p, part_cnt);
   else if (N <= 512)
-    hipLaunchKernelGGL(topk_logits_kernel<8>, grid, block, 0, st, logits, T, N, k, gate, idx, w,
+    hipLaunchKernelGGL(topk_logits_kernel<8>, grid, block, 0, st, logits, T, N, k, gate, bias, idx, w,
                        part_p, part_cnt);
   else
-    hipLaunchKernelGGL(topk_logits_kernel<16>, grid, block, 0, st, logits, T, N, k, gate, idx, w,
+    hipLaunchKernelGGL(topk_logits_kernel<16>, grid, block, 0, st, logits, T, N, k, gate, bias, idx, w,
                        part_p, part_cnt);
   return hipGetLastError();
 }

@@ -108,6 +108,24 @@ def test_stage_entry_points_validate():
     assert lib.moe_combine(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, n) == L.MOE_ERR_ARG
 
 
+def test_qb_entry_points_validate():
+    lib = L.load()
+    d = good()
+    n = None
+    big = 1 << 40
+    qb = lib.moe_qb_update
+    assert qb(ctypes.byref(d), n, FAKE, n, 0, 0, FAKE, FAKE, big, n) == L.MOE_ERR_ARG
+    assert qb(ctypes.byref(d), FAKE, FAKE, n, 0, 0, n, FAKE, big, n) == L.MOE_ERR_ARG
+    assert qb(ctypes.byref(d), FAKE, FAKE, n, 0, 2, FAKE, FAKE, big, n) == L.MOE_ERR_ARG
+    assert qb(ctypes.byref(d), FAKE, FAKE, n, d.T + 1, 0, FAKE, FAKE, big, n) == L.MOE_ERR_ARG
+    assert qb(ctypes.byref(d), FAKE, FAKE, n, 0, 1, FAKE, FAKE, 10, n) == L.MOE_ERR_WORKSPACE
+    tiny = H.desc_for(C.TINY)  # fp32 activations: no MFMA logits path
+    assert qb(ctypes.byref(tiny), FAKE, FAKE, n, 0, 0, FAKE, FAKE, big, n) == \
+        L.MOE_ERR_UNSUPPORTED
+    assert lib.moe_route_biased(ctypes.byref(d), n, FAKE, FAKE, FAKE, FAKE, n, FAKE, big, n) == \
+        L.MOE_ERR_ARG
+
+
 def test_workspace_monotone_in_T_and_sized():
     prev = 0
     for T in (1, 2, 33, 64, 65, 1000, 16384):
