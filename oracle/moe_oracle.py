@@ -45,7 +45,10 @@ Readings where the pages are silent (listed again in the design doc):
   * LatentMoE routes on the full-width u, adds shared experts with weight 1;
   * Quantile Balancing: score = router logit z, selection on z + b with the
     combine weights from the unbiased p, a_t = k-th largest z_t + b,
-    q = round(k T / N), histogram of 256 bins over [min, max] of required.
+    q = round(k T / N), histogram of 256 bins over [min, max] of required;
+  * FP8 expert weights: OCP E4M3 codes (the format whose largest value, 448,
+    the SiTU-GLU passage quotes) with one fp32 scale per weight row; a
+    stored row is its scale times each code's exact value.
 
 Pins (tests/test_oracle_pins.py): the capacity example [10,3,2,1] -> drops
 6/4/0; the balanced/collapsed aux example (1.0000 / 2.8449); the parameter
@@ -58,6 +61,9 @@ Quantile Balancing pins: after the exact update every expert admits exactly
 q tokens under the fixed cutoffs; a constant shift of b shifts b' by the same
 constant; the histogram estimate lies within one bin of the exact value; a
 hand-worked 4-token example; b = 0 reproduces the unbiased routing.
+FP8 pins: all 256 E4M3 codes decode as torch.float8_e4m3fn does, with the
+format's landmarks (448, 2^-9, 2^-6, -0, NaN) and a hand-expanded scaled
+matrix.
 Parity unpinned: the exact SiTU-GLU form, the LatentMoE wiring and the
 Quantile Balancing readings (score, cutoff, q, bins) are readings, pinned
 only through the limits and invariants above.
@@ -74,8 +80,31 @@ import numpy as np
 # ---------------------------------------------------------------------------
 
 
-def expand(stored: np.ndarray) -> np.ndarray:
-    """Exact fp64 value of stored bf16 bit patterns (uint16) or fp32 values."""
+def e4m3_value(code: int) -> float:
+    """Exact value of one OCP FP8 E4M3 code: bit 7 sign, bits 6..3 the
+    exponent with bias 7, bits 2..0 the mantissa.  Exponent field 0 holds the
+    subnormals m * 2^-9; S.1111.111 is NaN; there are no infinities."""
+    sign = -1.0 if code & 0x80 else 1.0
+    e, m = (code >> 3) & 0xF, code & 0x7
+    if e == 0xF and m == 0x7:
+        return math.nan
+    if e == 0:
+        return sign * m * 2.0 ** -9
+    return sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+E4M3_TABLE = np.array([e4m3_value(c) for c in range(256)], dtype=np.float64)
+
+
+def expand(stored) -> np.ndarray:
+    """Exact fp64 value of stored bf16 bit patterns (uint16), fp32 values, or
+    an FP8 row-scaled matrix (an object with ``codes`` [..., rows, cols] uint8
+    and ``scale`` [..., rows] fp32): element (r, c) = scale[r] * E4M3(code)."""
+    if hasattr(stored, "codes") and hasattr(stored, "scale"):
+        codes = np.asarray(stored.codes)
+        scale = np.asarray(stored.scale, dtype=np.float32).astype(np.float64)
+        assert codes.dtype == np.uint8 and scale.shape == codes.shape[:-1]
+        return scale[..., None] * E4M3_TABLE[codes]
     a = np.asarray(stored)
     if a.dtype == np.uint16:
         return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)

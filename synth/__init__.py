@@ -6,11 +6,13 @@ none of the MoE layer's arithmetic. Every element is a pure function of
 ``synth.c``), so any slice of any tensor can be regenerated independently.
 
 Stored values are returned as numpy arrays of the storage type:
-``uint16`` bit patterns for bf16, ``float32`` for fp32.
+``uint16`` bit patterns for bf16, ``float32`` for fp32, and for fp8 weights an
+``Fp8Rows`` pair of ``uint8`` E4M3 codes with one ``float32`` scale per row.
 """
 from __future__ import annotations
 
 import ctypes
+import dataclasses
 import os
 import subprocess
 
@@ -62,6 +64,9 @@ def _load():
         lib.synth_stream_key.restype = u64
         lib.synth_splitmix64.argtypes = [u64, u64]
         lib.synth_splitmix64.restype = u64
+        lib.synth_f64_to_e4m3.argtypes = [dbl]
+        lib.synth_f64_to_e4m3.restype = ctypes.c_uint8
+        lib.synth_normal_e4m3_rows.argtypes = [u64, u64, u64, u64, u64, dbl, ptr, ptr]
         _lib = lib
     return _lib
 
@@ -120,3 +125,34 @@ def splitmix64(key: int, n: int) -> int:
 
 def stream_key(seed: int, tid: int) -> int:
     return int(_load().synth_stream_key(seed, tid))
+
+
+@dataclasses.dataclass(frozen=True)
+class Fp8Rows:
+    """A matrix stored as OCP FP8 E4M3 codes with one fp32 scale per row:
+    row r holds scale[r] times the E4M3 value of each code."""
+    codes: np.ndarray   # uint8 [..., rows, cols]
+    scale: np.ndarray   # float32 [..., rows]
+
+    @property
+    def shape(self):
+        return self.codes.shape
+
+
+def f64_to_e4m3(x: float) -> int:
+    return int(_load().synth_f64_to_e4m3(float(x)))
+
+
+def normal_fp8_rows(seed: int, tid: int, rows: int, cols: int, std: float,
+                    start: int = 0, codes: np.ndarray | None = None,
+                    scale: np.ndarray | None = None) -> Fp8Rows:
+    """``std * N(0,1)`` elements [start, start + rows*cols) as E4M3 rows: the
+    same draws as ``normal_stored`` with the same arguments, each row scaled by
+    max|row| / 448 (rounded to fp32) and rounded to E4M3, nearest-even."""
+    rows, cols = int(rows), int(cols)
+    if codes is None:
+        codes = np.empty(rows * cols, dtype=np.uint8)
+    if scale is None:
+        scale = np.empty(rows, dtype=np.float32)
+    _load().synth_normal_e4m3_rows(seed, tid, start, rows, cols, std, _ptr(codes), _ptr(scale))
+    return Fp8Rows(codes.reshape(rows, cols), scale.reshape(rows))

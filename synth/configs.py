@@ -28,7 +28,7 @@ class Layer:
     N: int                      # routed experts (E for the latent layer)
     k: int
     act_dtype: str = "bf16"     # "f32" | "bf16"
-    w_dtype: str = "bf16"
+    w_dtype: str = "bf16"      # routed experts: "f32" | "bf16" | "fp8" (E4M3 rows)
     router_dtype: str = "bf16"
     gate: str = "renorm"        # "renorm" (a = p / sum_S p) | "prob" (a = p)
     act: str = "swiglu"         # "swiglu" | "situ"
@@ -100,20 +100,25 @@ class Layer:
         u = S.round_to(u, self.act_dtype)
         return u if rows is None else u[np.asarray(rows)]
 
-    # Routed expert e: gate/up [h, x_width], down [x_width, h].
+    # Routed expert e: gate/up [h, x_width], down [x_width, h].  With
+    # w_dtype "fp8" each is an Fp8Rows drawn from the same values.
+    def _expert_matrix(self, tid, rows, cols, std, start):
+        if self.w_dtype == "fp8":
+            return S.normal_fp8_rows(self.seed, tid, rows, cols, std, start=start)
+        return S.normal_stored(self.seed, tid, rows * cols, std, self.w_dtype,
+                               start=start).reshape(rows, cols)
+
     def expert(self, e: int):
         xw, h = self.x_width, self.h
         n = h * xw
-        g = S.normal_stored(self.seed, S.TID_W_GATE, n, 1.0 / math.sqrt(xw), self.w_dtype,
-                            start=e * n).reshape(h, xw)
-        u = S.normal_stored(self.seed, S.TID_W_UP, n, 1.0 / math.sqrt(xw), self.w_dtype,
-                            start=e * n).reshape(h, xw)
-        dn = S.normal_stored(self.seed, S.TID_W_DOWN, n, 1.0 / math.sqrt(h), self.w_dtype,
-                             start=e * n).reshape(xw, h)
+        g = self._expert_matrix(S.TID_W_GATE, h, xw, 1.0 / math.sqrt(xw), e * n)
+        u = self._expert_matrix(S.TID_W_UP, h, xw, 1.0 / math.sqrt(xw), e * n)
+        dn = self._expert_matrix(S.TID_W_DOWN, xw, h, 1.0 / math.sqrt(h), e * n)
         return g, u, dn
 
-    def expert_tensor(self, which: str, out: Optional[np.ndarray] = None) -> np.ndarray:
-        """Whole stacked routed-expert tensor: gate/up [N,h,xw], down [N,xw,h]."""
+    def expert_tensor(self, which: str, out: Optional[np.ndarray] = None):
+        """Whole stacked routed-expert tensor: gate/up [N,h,xw], down [N,xw,h]
+        (fp8: an Fp8Rows of codes [N,rows,cols] and scales [N,rows])."""
         xw, h = self.x_width, self.h
         n = self.N * h * xw
         tid, std, shape = {
@@ -121,16 +126,26 @@ class Layer:
             "up": (S.TID_W_UP, 1.0 / math.sqrt(xw), (self.N, h, xw)),
             "down": (S.TID_W_DOWN, 1.0 / math.sqrt(h), (self.N, xw, h)),
         }[which]
+        if self.w_dtype == "fp8":
+            m = S.normal_fp8_rows(self.seed, tid, self.N * shape[1], shape[2], std,
+                                  codes=None if out is None else out.reshape(-1))
+            return S.Fp8Rows(m.codes.reshape(shape), m.scale.reshape(shape[:2]))
         flat = None if out is None else out.reshape(-1)
         return S.normal_stored(self.seed, tid, n, std, self.w_dtype, out=flat).reshape(shape)
 
+    # Latent projections and shared experts are stored in the activation
+    # dtype when the routed experts are fp8.
+    @property
+    def dense_w_dtype(self) -> str:
+        return self.act_dtype if self.w_dtype == "fp8" else self.w_dtype
+
     def w_ldown(self) -> np.ndarray:   # [l, d]
         return S.normal_stored(self.seed, S.TID_W_LDOWN, self.l * self.d,
-                               1.0 / math.sqrt(self.d), self.w_dtype).reshape(self.l, self.d)
+                               1.0 / math.sqrt(self.d), self.dense_w_dtype).reshape(self.l, self.d)
 
     def w_lup(self) -> np.ndarray:     # [d, l]
         return S.normal_stored(self.seed, S.TID_W_LUP, self.d * self.l,
-                               1.0 / math.sqrt(self.l), self.w_dtype).reshape(self.d, self.l)
+                               1.0 / math.sqrt(self.l), self.dense_w_dtype).reshape(self.d, self.l)
 
     def shared_tensor(self, which: str) -> np.ndarray:
         """Shared experts: gate/up [S,h_s,d], down [S,d,h_s]."""
@@ -138,21 +153,21 @@ class Layer:
         n = Sx * hs * d
         if which == "gate":
             return S.normal_stored(self.seed, S.TID_WS_GATE, n, 1.0 / math.sqrt(d),
-                                   self.w_dtype).reshape(Sx, hs, d)
+                                   self.dense_w_dtype).reshape(Sx, hs, d)
         if which == "up":
             return S.normal_stored(self.seed, S.TID_WS_UP, n, 1.0 / math.sqrt(d),
-                                   self.w_dtype).reshape(Sx, hs, d)
+                                   self.dense_w_dtype).reshape(Sx, hs, d)
         return S.normal_stored(self.seed, S.TID_WS_DOWN, n, 1.0 / math.sqrt(hs),
-                               self.w_dtype).reshape(Sx, d, hs)
+                               self.dense_w_dtype).reshape(Sx, d, hs)
 
     def shared(self, j: int):
         Sx, hs, d = self.n_shared, self.h_shared, self.d
         n = hs * d
-        g = S.normal_stored(self.seed, S.TID_WS_GATE, n, 1.0 / math.sqrt(d), self.w_dtype,
+        g = S.normal_stored(self.seed, S.TID_WS_GATE, n, 1.0 / math.sqrt(d), self.dense_w_dtype,
                             start=j * n).reshape(hs, d)
-        u = S.normal_stored(self.seed, S.TID_WS_UP, n, 1.0 / math.sqrt(d), self.w_dtype,
+        u = S.normal_stored(self.seed, S.TID_WS_UP, n, 1.0 / math.sqrt(d), self.dense_w_dtype,
                             start=j * n).reshape(hs, d)
-        dn = S.normal_stored(self.seed, S.TID_WS_DOWN, n, 1.0 / math.sqrt(hs), self.w_dtype,
+        dn = S.normal_stored(self.seed, S.TID_WS_DOWN, n, 1.0 / math.sqrt(hs), self.dense_w_dtype,
                              start=j * n).reshape(d, hs)
         return g, u, dn
 
@@ -179,5 +194,11 @@ SWITCH_SKEWED = Layer("switch_top1_skewed_t16384", T=16384, d=4096, h=14336, N=8
 LATENT = Layer("latent_t8192", T=8192, d=4096, h=3072, N=896, k=16, act="situ",
                l=3584, n_shared=2, h_shared=3072, seed=4)
 
+# FP8 E4M3 routed-expert weights (row-scaled), same draws as the bf16 layers.
+MIXTRAL_DECODE_FP8 = MIXTRAL_DECODE.with_(name="mixtral_decode_t32_fp8", w_dtype="fp8")
+MIXTRAL_PREFILL_FP8 = MIXTRAL_PREFILL.with_(name="mixtral_prefill_t16384_fp8", w_dtype="fp8")
+LATENT_FP8 = LATENT.with_(name="latent_t8192_fp8", w_dtype="fp8")
+
 ALL = {c.name: c for c in (TINY, TINY_PLANTED, MCU_BATCH, MCU_DECODE, MIXTRAL_PREFILL,
-                           MIXTRAL_DECODE, SWITCH_SKEWED, LATENT)}
+                           MIXTRAL_DECODE, SWITCH_SKEWED, LATENT, MIXTRAL_DECODE_FP8,
+                           MIXTRAL_PREFILL_FP8, LATENT_FP8)}

@@ -26,9 +26,12 @@
  *   - bf16: direct round-to-nearest-even from fp64 to the bf16 grid (1 sign,
  *     8 exponent, 7 mantissa bits), including subnormals, overflow to Inf and
  *     NaN propagation.  No intermediate fp32 rounding (no double rounding).
+ *   - fp8 E4M3 rows: per-row fp32 scale max|row| / 448, codes rounded
+ *     nearest-even from fp64 (synth_normal_e4m3_rows).
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #define SM_GAMMA 0x9E3779B97F4A7C15ULL
@@ -160,4 +163,62 @@ void synth_normal_f32(uint64_t seed, uint64_t tensor_id, uint64_t start,
 #define EMIT_F32(i, v) out[i] = (float)(std * (v))
   FOR_EACH_NORMAL(K, start, count, EMIT_F32);
 #undef EMIT_F32
+}
+
+/* Round one fp64 value to an OCP FP8 E4M3 code, nearest-even, directly.
+   E4M3: 1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits; exponent
+   field 0 holds the subnormals m * 2^-9; there are no infinities and
+   S.1111.111 is NaN, so the largest finite magnitude is 1.75 * 2^8 = 448
+   (code 0x7E).  Magnitudes at or above 448 saturate to it. */
+uint8_t synth_f64_to_e4m3(double x) {
+  const uint8_t sign = signbit(x) ? 0x80u : 0u;
+  if (isnan(x)) return (uint8_t)(sign | 0x7Fu);
+  const double a = fabs(x);
+  if (a >= 448.0) return (uint8_t)(sign | 0x7Eu);
+  /* Unbiased exponent of a (clamped at the smallest normal exponent -6);
+     the quantum of that binade is 2^(ue-3). */
+  int fe = 0;
+  if (a > 0.0) frexp(a, &fe); /* a = m 2^fe, m in [0.5, 1) */
+  int ue = a > 0.0 ? fe - 1 : -6;
+  if (ue < -6) ue = -6;
+  const double n = nearbyint(ldexp(a, 3 - ue)); /* exact scaling, ties to even */
+  const double r = ldexp(n, ue - 3);
+  if (r < 0x1.0p-6) return (uint8_t)(sign | (uint8_t)n); /* subnormal or zero */
+  int re = 0;
+  frexp(r, &re);
+  const int be = re - 1 + 7; /* 1..15 */
+  const int man = (int)ldexp(r, 3 - (re - 1)) - 8;
+  return (uint8_t)(sign | (uint8_t)(be << 3) | (uint8_t)man);
+}
+
+/* rows x cols values std * N(0,1)[start + r*cols + c], each row stored as
+   E4M3 codes with one fp32 scale: scale_r = (float)(max_c |v_rc| / 448)
+   (1 for an all-zero row), code_rc = E4M3(v_rc / scale_r). */
+void synth_normal_e4m3_rows(uint64_t seed, uint64_t tensor_id, uint64_t start, uint64_t rows,
+                            uint64_t cols, double std, uint8_t *codes, float *scale) {
+  const uint64_t K = synth_stream_key(seed, tensor_id);
+#pragma omp parallel
+  {
+    double *row = (double *)malloc(cols * sizeof(double));
+#pragma omp for schedule(static)
+    for (int64_t r = 0; r < (int64_t)rows; ++r) {
+      uint64_t cached = UINT64_MAX;
+      double c = 0.0, s = 0.0, amax = 0.0;
+      for (uint64_t i = 0; i < cols; ++i) {
+        const uint64_t e = start + (uint64_t)r * cols + i;
+        if ((e >> 1) != cached) {
+          cached = e >> 1;
+          normal_pair(K, cached, &c, &s);
+        }
+        const double v = std * ((e & 1) ? s : c);
+        row[i] = v;
+        if (fabs(v) > amax) amax = fabs(v);
+      }
+      const float sc = amax > 0.0 ? (float)(amax / 448.0) : 1.0f;
+      scale[r] = sc;
+      for (uint64_t i = 0; i < cols; ++i)
+        codes[(uint64_t)r * cols + i] = synth_f64_to_e4m3(row[i] / (double)sc);
+    }
+    free(row);
+  }
 }

@@ -586,3 +586,74 @@ def test_qb_update_cools_hot_experts():
     after = O.qb_loads(z, b, k).max()
     assert before > 3 * q
     assert after < 1.5 * q
+
+
+# ---------------------------------------------------------------------------
+# FP8 E4M3 expert weights (page 5, SiTU-GLU passage: E4M3's largest value is
+# 448).  The format itself is OCP FP8 E4M3.
+# ---------------------------------------------------------------------------
+
+
+def test_e4m3_decode_matches_torch():
+    # torch's float8_e4m3fn is an independent implementation of the format.
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64)
+    ref = ref.numpy()
+    mine = O.E4M3_TABLE
+    assert np.array_equal(np.isnan(mine), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(mine[ok], ref[ok])
+    assert np.array_equal(np.signbit(mine[ok]), np.signbit(ref[ok]))
+
+
+def test_e4m3_landmarks():
+    v = O.e4m3_value
+    assert v(0x7E) == 448.0 and v(0xFE) == -448.0       # largest finite (page 5)
+    assert v(0x38) == 1.0 and v(0xB8) == -1.0
+    assert v(0x01) == 2.0 ** -9                          # smallest subnormal
+    assert v(0x08) == 2.0 ** -6                          # smallest normal
+    assert v(0x07) == 7 * 2.0 ** -9                      # largest subnormal
+    assert v(0x00) == 0.0 and math.copysign(1.0, v(0x80)) == -1.0
+    assert math.isnan(v(0x7F)) and math.isnan(v(0xFF))
+    assert np.isfinite(O.E4M3_TABLE).sum() == 254
+    pos = O.E4M3_TABLE[:0x7F]
+    assert np.all(np.diff(pos) > 0)                      # codes 0..0x7E increase
+
+
+def test_fp8_rows_expand_by_hand():
+    m = synth.Fp8Rows(np.array([[0x38, 0x40, 0x3C], [0xB8, 0x00, 0x01]], dtype=np.uint8),
+                      np.array([2.0, 0.5], dtype=np.float32))
+    # 0x40 = 2^(8-7) = 2, 0x3C = 1.5, 0x01 = 2^-9; each row times its own scale
+    want = np.array([[2.0, 4.0, 3.0], [-0.5, 0.0, 2.0 ** -10]])
+    assert np.array_equal(O.expand(m), want)
+
+
+def test_synth_e4m3_encoder_matches_torch():
+    # The generator's nearest-even rounding against torch's cast, on values
+    # exact in fp32 (so torch's float -> fp8 path rounds them once): random
+    # magnitudes over the whole range, subnormals, exact ties and saturation.
+    rng = np.random.default_rng(5)
+    x = np.concatenate([
+        rng.standard_normal(4000) * 40.0,
+        rng.uniform(-2 ** -6, 2 ** -6, 1000),
+        (O.E4M3_TABLE[1:0x7E] + O.E4M3_TABLE[2:0x7F]) / 2,   # midpoints
+        -(O.E4M3_TABLE[1:0x7E] + O.E4M3_TABLE[2:0x7F]) / 2,
+        [0.0, -0.0, 448.0, -448.0, 2.0 ** -10, 3 * 2.0 ** -11],
+    ]).astype(np.float32).astype(np.float64)
+    mine = np.array([synth.f64_to_e4m3(v) for v in x], dtype=np.uint8)
+    ref = torch.from_numpy(x.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8)
+    assert np.array_equal(mine, ref.numpy())
+    assert synth.f64_to_e4m3(1000.0) == 0x7E and synth.f64_to_e4m3(-500.0) == 0xFE
+
+
+def test_synth_fp8_rows_follow_the_bf16_draws():
+    rows, cols, std = 6, 256, 0.05
+    q = synth.normal_fp8_rows(3, synth.TID_W_GATE, rows, cols, std, start=512)
+    v = synth.normal_f64(3, synth.TID_W_GATE, rows * cols, std, start=512).reshape(rows, cols)
+    assert np.allclose(q.scale, np.abs(v).max(axis=1) / 448.0, rtol=1e-7, atol=0)
+    w = O.expand(q)
+    # E4M3 keeps 3 mantissa bits: relative rounding error <= 2^-4 above the
+    # subnormal range, absolute <= 2^-10 * scale below it.
+    err = np.abs(w - v)
+    bound = np.maximum(np.abs(v) * 2.0 ** -4, q.scale[:, None] * 2.0 ** -10)
+    assert np.all(err <= bound * (1 + 1e-12))
+    assert np.array_equal(np.abs(w).max(axis=1), q.scale.astype(np.float64) * 448.0)
