@@ -60,7 +60,12 @@ typedef enum {
   MOE_ERR_HIP = 4
 } moe_status_t;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
+/* MOE_FP8_E4M3: OCP FP8 E4M3 codes (1 sign, 4 exponent bits with bias 7, 3
+   mantissa bits; no infinities, S.1111.111 is NaN; largest finite 448, the
+   bound page "Stable LatentMoE interactive demo" quotes in its SiTU-GLU
+   passage), with one fp32 scale per weight row.  Only for the routed
+   experts' weights (w_dtype) under bf16 activations. */
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype_t;
 
 /* Combine weight of a selected expert (page "MoE: how sparse activation
    saves compute", section 3.2: Mixtral renormalises over S_t; Switch top-1
@@ -80,7 +85,8 @@ typedef struct moe_desc {
   int32_t k;          /* experts per token, 1..min(N, 32) */
   int32_t capacity;   /* slots per expert C >= 0, or -1 for unlimited */
   int32_t act_dtype;  /* moe_dtype_t of u, y and intermediate activations */
-  int32_t w_dtype;    /* moe_dtype_t of expert and projection weights */
+  int32_t w_dtype;    /* moe_dtype_t of the routed experts' weights; the latent
+                         projections and shared experts use act_dtype */
   int32_t router_dtype; /* moe_dtype_t of W_route */
   int32_t gate;       /* moe_gate_t */
   int32_t act;        /* moe_act_t of the routed experts */
@@ -102,11 +108,17 @@ typedef struct moe_desc {
    only the selected experts' bytes are ever read.
    selection_bias [N] fp32, nullable: the router picks the top-k of z + b
    (Quantile Balancing bias, see moe_qb_update) while the combine weights
-   still come from the unbiased softmax; null = no bias. */
+   still come from the unbiased softmax; null = no bias.
+   gate_scale, up_scale [N, h] and down_scale [N, w] fp32 (w = d, or l for
+   the latent layer): with w_dtype MOE_FP8_E4M3 all three are required and
+   W_gate / W_up / W_down hold E4M3 codes (uint8, same shapes), weight row r
+   of expert i being scale[i, r] times its codes' values; with any other
+   w_dtype all three must be null. */
 typedef struct moe_weights {
   const void *W_route, *W_gate, *W_up, *W_down;
   const void *W_ldown, *W_lup, *Ws_gate, *Ws_up, *Ws_down;
   const float *selection_bias;
+  const float *gate_scale, *up_scale, *down_scale;
 } moe_weights_t;
 
 /* Optional outputs of moe_forward (device pointers; each may be null, the
@@ -202,6 +214,18 @@ moe_status_t moe_expert_ffn(const moe_desc_t *desc, const void *x, const int32_t
                             const int32_t *offsets, const int32_t *kept_offsets,
                             const void *W_gate, const void *W_up, const void *W_down,
                             float *y_perm, void *ws, size_t ws_bytes, moe_stream_t stream);
+
+/* moe_expert_ffn with per-row weight scales (the same computation, with
+   W_gate, W_up, W_down expanded as described at moe_weights_t):
+     gate_scale, up_scale [N, h]; down_scale [N, w]  fp32 device pointers,
+     all three required when w_dtype is MOE_FP8_E4M3, all three null
+     otherwise (MOE_ERR_ARG if not). */
+moe_status_t moe_expert_ffn_scaled(const moe_desc_t *desc, const void *x, const int32_t *perm,
+                                   const int32_t *offsets, const int32_t *kept_offsets,
+                                   const void *W_gate, const void *W_up, const void *W_down,
+                                   const float *gate_scale, const float *up_scale,
+                                   const float *down_scale, float *y_perm, void *ws,
+                                   size_t ws_bytes, moe_stream_t stream);
 
 /* Combine (section 3.2 eq. for y): y_t = sum_s [row_of[t*k+s] >= 0]
    topk_w[t,s] * y_perm[row_of[t*k+s]] in fp32, rounded once to act_dtype.

@@ -8,15 +8,15 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SO_PATH = os.path.join(HERE, "libmoe.so")
 
 MOE_OK, MOE_ERR_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
-MOE_F32, MOE_BF16 = 0, 1
+MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 MOE_GATE_RENORM, MOE_GATE_PROB = 0, 1
 MOE_ACT_SWIGLU, MOE_ACT_SITU_GLU = 0, 1
 
 # Every symbol include/moe.h declares.
 EXPORTS = ("moe_desc_init", "moe_status_string", "moe_workspace_bytes",
            "moe_capacity_from_factor", "moe_route", "moe_route_biased", "moe_qb_update",
-           "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward", "moe_forward_traced",
-           "moe_stage_name")
+           "moe_dispatch", "moe_expert_ffn", "moe_expert_ffn_scaled", "moe_combine",
+           "moe_forward", "moe_forward_traced", "moe_stage_name")
 
 
 class MoeDesc(ctypes.Structure):
@@ -32,7 +32,8 @@ class MoeDesc(ctypes.Structure):
 class MoeWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("W_route", "W_gate", "W_up", "W_down", "W_ldown",
                                                 "W_lup", "Ws_gate", "Ws_up", "Ws_down",
-                                                "selection_bias")]
+                                                "selection_bias", "gate_scale", "up_scale",
+                                                "down_scale")]
 
 
 class MoeOutputs(ctypes.Structure):
@@ -77,6 +78,8 @@ def load() -> ctypes.CDLL:
     lib.moe_dispatch.restype = I32
     lib.moe_expert_ffn.argtypes = [D, P, P, P, P, P, P, P, P, P, SZ, P]
     lib.moe_expert_ffn.restype = I32
+    lib.moe_expert_ffn_scaled.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
+    lib.moe_expert_ffn_scaled.restype = I32
     lib.moe_combine.argtypes = [D, P, P, P, P, P]
     lib.moe_combine.restype = I32
     lib.moe_forward.argtypes = [D, ctypes.POINTER(MoeWeights), P, P,

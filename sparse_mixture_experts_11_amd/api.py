@@ -15,7 +15,7 @@ import torch
 from . import _lib as L
 from ._lib import MoeDesc, MoeOutputs, MoeWeights  # noqa: F401
 
-_DT = {"f32": L.MOE_F32, "bf16": L.MOE_BF16}
+_DT = {"f32": L.MOE_F32, "bf16": L.MOE_BF16, "fp8": L.MOE_FP8_E4M3}
 _GATE = {"renorm": L.MOE_GATE_RENORM, "prob": L.MOE_GATE_PROB}
 _ACT = {"swiglu": L.MOE_ACT_SWIGLU, "situ": L.MOE_ACT_SITU_GLU}
 
@@ -126,6 +126,15 @@ def moe_expert_ffn(desc, x, perm, offsets, kept_offsets, W_gate, W_up, W_down, y
                                    _ptr(kept_offsets), _ptr(W_gate), _ptr(W_up), _ptr(W_down),
                                    _ptr(y_perm), _ptr(ws), ws.numel(), _stream(stream)),
            "moe_expert_ffn")
+
+
+def moe_expert_ffn_scaled(desc, x, perm, offsets, kept_offsets, W_gate, W_up, W_down,
+                          gate_scale, up_scale, down_scale, y_perm, ws, stream=None) -> None:
+    _check(L.load().moe_expert_ffn_scaled(ctypes.byref(desc), _ptr(x), _ptr(perm), _ptr(offsets),
+                                          _ptr(kept_offsets), _ptr(W_gate), _ptr(W_up),
+                                          _ptr(W_down), _ptr(gate_scale), _ptr(up_scale),
+                                          _ptr(down_scale), _ptr(y_perm), _ptr(ws), ws.numel(),
+                                          _stream(stream)), "moe_expert_ffn_scaled")
 
 
 def moe_combine(desc, y_perm, row_of, topk_w, y, stream=None) -> None:

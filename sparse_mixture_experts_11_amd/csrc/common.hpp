@@ -70,6 +70,17 @@ __device__ __forceinline__ uint32_t pack_bf16x2_hw(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
+// Eight OCP FP8 E4M3 codes (byte j = element j) -> the bf16x8 MFMA operand.
+// Every E4M3 value is exact in bf16 (3 mantissa bits, exponents -9..8), and
+// v_cvt_scalef32_pk_bf16_fp8 with scale 1 converts two codes exactly.
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+  const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+  const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+  const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+  const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+  return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
 // ---- precise activations (fp32 path) -------------------------------------
 __device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
 

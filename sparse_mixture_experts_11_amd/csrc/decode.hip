@@ -16,6 +16,10 @@
 // weights.
 //   GLU = true : hid[row] = act(W_gate x, W_up x), x rows gathered via perm
 //   GLU = false: y_perm[row] = W_down hid[row], fp32
+// FP8 weights (E4M3 codes, one fp32 scale per weight row) stream the same
+// bytes per window, so each window covers twice the k; the operands are
+// widened to bf16 exactly after the LDS read, and the row scales multiply
+// the fp32 sums after the split-K reduction.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -27,22 +31,25 @@ constexpr int NRB = 2;          // 16-row weight blocks per wave (token fragment
 constexpr int RB = 16 * NRB;    // weight rows per workgroup
 constexpr int kWaves = 4;       // split-K ways
 // k-steps of 32 per iteration: 16 KiB of weights per wave per iteration
-// (GLU: 2 matrices x 32 rows x 256 B; down: 32 rows x 512 B).
-template <bool GLU>
-constexpr int unroll_of() { return GLU ? 4 : 8; }
-// Per-wave LDS slice: one iteration's weights, row pitch U * 64 bytes.
+// (GLU: 2 matrices x 32 rows x 256 B; down: 32 rows x 512 B), so U = 4 / 8
+// for bf16 weights and 8 / 16 for fp8.
+template <bool GLU, bool FP8>
+constexpr int unroll_of() { return (GLU ? 4 : 8) * (FP8 ? 2 : 1); }
+// Per-wave LDS slice: one iteration's weights, row pitch U * 32 * ES bytes.
 constexpr int kSlice = 16384;
 
-template <bool GLU, int TG>
+template <bool GLU, int TG, bool FP8>
 __global__ __launch_bounds__(256) void decode_kernel(
     const uint16_t *__restrict__ x, int64_t ldx, const int32_t *__restrict__ perm,
     const int32_t *__restrict__ offsets, const int32_t *__restrict__ kept_offsets, int kslots,
-    const uint16_t *__restrict__ W1, const uint16_t *__restrict__ W2, int64_t wrows, int K,
-    int act, float bg, float bu, void *__restrict__ out, int64_t ldo) {
+    const void *__restrict__ W1, const void *__restrict__ W2, const float *__restrict__ S1,
+    const float *__restrict__ S2, int64_t wrows, int K, int act, float bg, float bu,
+    void *__restrict__ out, int64_t ldo) {
   constexpr int NM = GLU ? 2 : 1;
-  constexpr int U = unroll_of<GLU>();
-  constexpr int kPitch = U * 64;          // bytes of one row's window in a slice
-  constexpr int kLoads = 2 * U;           // 1 KiB load instructions per matrix
+  constexpr int ES = FP8 ? 1 : 2;         // bytes per weight
+  constexpr int U = unroll_of<GLU, FP8>();
+  constexpr int kPitch = U * 32 * ES;     // bytes of one row's window in a slice
+  constexpr int kLoads = kPitch / 32;     // 1 KiB load instructions per matrix
   static_assert(NM * RB * kPitch == kSlice, "slice holds one iteration");
   // After the loop the same LDS holds the partial sums of waves 1 .. 3.
   constexpr int kRedBytes = NM * NRB * TG * 64 * 16;
@@ -60,14 +67,21 @@ __global__ __launch_bounds__(256) void decode_kernel(
   const int Kw = K / kWaves;
   const int kb = wave * Kw;
 
-  const uint16_t *w1 = W1 + ((int64_t)e * wrows + row0 + li) * K + kb + kq;
-  const uint16_t *w2 = GLU ? W2 + ((int64_t)e * wrows + row0 + li) * K + kb + kq : nullptr;
-  const int64_t rbs = (int64_t)16 * K;  // next 16-row block
+  const int64_t rowK = (int64_t)K * ES;  // bytes of one weight row
+  const char *w1 = static_cast<const char *>(W1) + ((int64_t)e * wrows + row0 + li) * rowK +
+                   (int64_t)(kb + kq) * ES;
+  const char *w2 = GLU ? static_cast<const char *>(W2) + ((int64_t)e * wrows + row0 + li) * rowK +
+                             (int64_t)(kb + kq) * ES
+                       : nullptr;
+  const int64_t rbs = 16 * rowK;  // next 16-row block
   // Whole-line loads: instruction i takes rows 8*(i%4) + lane/8 and the
   // 128-byte piece i/4 of the iteration's window; lane%8 picks 16 bytes.
   const int lr = lane >> 3, lc = lane & 7;
-  const uint16_t *g1 = W1 + ((int64_t)e * wrows + row0 + lr) * K + kb + 8 * lc;
-  const uint16_t *g2 = GLU ? W2 + ((int64_t)e * wrows + row0 + lr) * K + kb + 8 * lc : nullptr;
+  const char *g1 = static_cast<const char *>(W1) + ((int64_t)e * wrows + row0 + lr) * rowK +
+                   (int64_t)kb * ES + 16 * lc;
+  const char *g2 = GLU ? static_cast<const char *>(W2) + ((int64_t)e * wrows + row0 + lr) * rowK +
+                             (int64_t)kb * ES + 16 * lc
+                       : nullptr;
   char *slice = smem + wave * kSlice;
   const uint16_t *xr[TG];
   bool xv[TG];
@@ -90,14 +104,37 @@ __global__ __launch_bounds__(256) void decode_kernel(
 #pragma unroll
       for (int tg = 0; tg < TG; ++tg) acc[m][r][tg] = f32x4{0.f, 0.f, 0.f, 0.f};
   const bf16x8 zero = {};
+  // One MFMA operand (8 weights of row r, k-step u, this lane's k quarter)
+  // from the slice: 16 bytes of bf16, or 8 bytes of fp8 widened to bf16.
+  auto slice_frag = [&](int m, int r, int u) -> bf16x8 {
+    const char *row = slice + m * RB * kPitch + r * kPitch;
+    if constexpr (FP8) {
+      const int q = lane >> 4;
+      const int c = 2 * u + (q >> 1);
+      const uint2 raw = *reinterpret_cast<const uint2 *>(row + ((c ^ li) << 4) + 8 * (q & 1));
+      return e4m3x8_to_bf16x8(raw.x, raw.y);
+    } else {
+      const int c = 4 * u + (lane >> 4);
+      return *reinterpret_cast<const bf16x8 *>(row + ((c ^ li) << 4));
+    }
+  };
+  auto global_frag = [&](const char *w, int64_t byte_off) -> bf16x8 {
+    if constexpr (FP8) {
+      const uint2 raw = *reinterpret_cast<const uint2 *>(w + byte_off);
+      return e4m3x8_to_bf16x8(raw.x, raw.y);
+    } else {
+      return *reinterpret_cast<const bf16x8 *>(w + byte_off);
+    }
+  };
   int k = 0;
   for (; k + 32 * U <= Kw; k += 32 * U) {
-    bf16x8 v[NM][kLoads], b[TG][U];
+    u32x4 v[NM][kLoads];
+    bf16x8 b[TG][U];
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
-      const int64_t off = (int64_t)(8 * (i % 4)) * K + 64 * (i / 4) + k;
-      v[0][i] = *reinterpret_cast<const bf16x8 *>(g1 + off);
-      if (GLU) v[NM - 1][i] = *reinterpret_cast<const bf16x8 *>(g2 + off);
+      const int64_t off = (int64_t)(8 * (i % 4)) * rowK + 128 * (i / 4) + (int64_t)k * ES;
+      v[0][i] = *reinterpret_cast<const u32x4 *>(g1 + off);
+      if (GLU) v[NM - 1][i] = *reinterpret_cast<const u32x4 *>(g2 + off);
     }
 #pragma unroll
     for (int tg = 0; tg < TG; ++tg)
@@ -112,33 +149,52 @@ __global__ __launch_bounds__(256) void decode_kernel(
       for (int i = 0; i < kLoads; ++i) {
         const int r = 8 * (i % 4) + lr;
         const int c = 8 * (i / 4) + lc;
-        *reinterpret_cast<bf16x8 *>(slice + m * RB * kPitch + r * kPitch + ((c ^ (r & 15)) << 4)) =
+        *reinterpret_cast<u32x4 *>(slice + m * RB * kPitch + r * kPitch + ((c ^ (r & 15)) << 4)) =
             v[m][i];
       }
-    // MFMA operands: lane l takes row 16 rb + l%16, chunk 4u + l/16.
-    bf16x8 a[NM][NRB][U];
+    // MFMA operands: lane l takes row 16 rb + l%16, k values 32u + 8(l/16) .. +7.
+    if constexpr (FP8) {
+      // Widened operands of one k-step at a time (all U would not fit
+      // beside the loads in flight).
 #pragma unroll
-    for (int m = 0; m < NM; ++m)
+      for (int u = 0; u < U; ++u) {
+        bf16x8 a[NM][NRB];
 #pragma unroll
-      for (int rb = 0; rb < NRB; ++rb)
+        for (int m = 0; m < NM; ++m)
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int r = 16 * rb + li;
-          const int c = 4 * u + (lane >> 4);
-          a[m][rb][u] = *reinterpret_cast<const bf16x8 *>(slice + m * RB * kPitch + r * kPitch +
-                                                          ((c ^ li) << 4));
+          for (int rb = 0; rb < NRB; ++rb) a[m][rb] = slice_frag(m, 16 * rb + li, u);
+#pragma unroll
+        for (int tg = 0; tg < TG; ++tg) {
+          if (tg < ngroups) {
+#pragma unroll
+            for (int m = 0; m < NM; ++m)
+#pragma unroll
+              for (int r = 0; r < NRB; ++r)
+                acc[m][r][tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[m][r], b[tg][u],
+                                                                       acc[m][r][tg], 0, 0, 0);
+          }
         }
+      }
+    } else {
+      bf16x8 a[NM][NRB][U];
 #pragma unroll
-    for (int tg = 0; tg < TG; ++tg) {
-      if (tg < ngroups) {
+      for (int m = 0; m < NM; ++m)
 #pragma unroll
-        for (int u = 0; u < U; ++u)
+        for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
-          for (int m = 0; m < NM; ++m)
+          for (int u = 0; u < U; ++u) a[m][rb][u] = slice_frag(m, 16 * rb + li, u);
 #pragma unroll
-            for (int r = 0; r < NRB; ++r)
-              acc[m][r][tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[m][r][u], b[tg][u],
-                                                                     acc[m][r][tg], 0, 0, 0);
+      for (int tg = 0; tg < TG; ++tg) {
+        if (tg < ngroups) {
+#pragma unroll
+          for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int m = 0; m < NM; ++m)
+#pragma unroll
+              for (int r = 0; r < NRB; ++r)
+                acc[m][r][tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[m][r][u], b[tg][u],
+                                                                       acc[m][r][tg], 0, 0, 0);
+        }
       }
     }
   }
@@ -146,8 +202,8 @@ __global__ __launch_bounds__(256) void decode_kernel(
     bf16x8 a[NM][NRB];
 #pragma unroll
     for (int r = 0; r < NRB; ++r) {
-      a[0][r] = *reinterpret_cast<const bf16x8 *>(w1 + r * rbs + k);
-      if (GLU) a[NM - 1][r] = *reinterpret_cast<const bf16x8 *>(w2 + r * rbs + k);
+      a[0][r] = global_frag(w1, r * rbs + (int64_t)k * ES);
+      if (GLU) a[NM - 1][r] = global_frag(w2, r * rbs + (int64_t)k * ES);
     }
 #pragma unroll
     for (int tg = 0; tg < TG; ++tg) {
@@ -190,6 +246,20 @@ __global__ __launch_bounds__(256) void decode_kernel(
         for (int tg = 0; tg < TG; ++tg) acc[m][r][tg] += theirs[m][r][tg][lane];
   }
   // Lane holds rows row0 + 16r + 4*(lane/16) + {0..3} of token tg*16 + lane%16.
+  // FP8: those rows' scales multiply the sums (fp32) before the epilogue.
+  f32x4 sc[NM][NRB];
+#pragma unroll
+  for (int m = 0; m < NM; ++m)
+#pragma unroll
+    for (int r = 0; r < NRB; ++r) {
+      if constexpr (FP8) {
+        const float *S = (m == 0) ? S1 : S2;
+        sc[m][r] = *reinterpret_cast<const f32x4 *>(S + (int64_t)e * wrows + row0 + 16 * r +
+                                                    4 * (lane >> 4));
+      } else {
+        sc[m][r] = f32x4{1.f, 1.f, 1.f, 1.f};
+      }
+    }
 #pragma unroll
   for (int tg = 0; tg < TG; ++tg) {
     const int j = tg * 16 + li;
@@ -201,28 +271,34 @@ __global__ __launch_bounds__(256) void decode_kernel(
       if constexpr (GLU) {
         float v[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) v[q] = glu_act_fast(acc[0][r][tg][q], acc[1][r][tg][q], act, bg, bu);
+        for (int q = 0; q < 4; ++q) {
+          const float g = FP8 ? acc[0][r][tg][q] * sc[0][r][q] : acc[0][r][tg][q];
+          const float u = FP8 ? acc[1][r][tg][q] * sc[1][r][q] : acc[1][r][tg][q];
+          v[q] = glu_act_fast(g, u, act, bg, bu);
+        }
         uint2 pk;
         pk.x = pack_bf16x2_hw(v[0], v[1]);
         pk.y = pack_bf16x2_hw(v[2], v[3]);
         *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(out) + orow * ldo + col) = pk;
       } else {
         *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(out) + orow * ldo + col) =
-            acc[0][r][tg];
+            FP8 ? acc[0][r][tg] * sc[0][r] : acc[0][r][tg];
       }
     }
   }
 }
 
-template <bool GLU>
+template <bool GLU, bool FP8>
 hipError_t launch_decode(int tg, dim3 grid, hipStream_t st, const uint16_t *x, int64_t ldx,
                          const int32_t *perm, const int32_t *offsets, const int32_t *kept_offsets,
-                         int kslots, const uint16_t *W1, const uint16_t *W2, int64_t wrows, int K,
-                         int act, float bg, float bu, void *out, int64_t ldo) {
-#define MOE_DECODE_CASE(TGV)                                                                     \
-  case TGV:                                                                                      \
-    hipLaunchKernelGGL((decode_kernel<GLU, TGV>), grid, dim3(256), 0, st, x, ldx, perm, offsets, \
-                       kept_offsets, kslots, W1, W2, wrows, K, act, bg, bu, out, ldo);           \
+                         int kslots, const void *W1, const void *W2, const float *S1,
+                         const float *S2, int64_t wrows, int K, int act, float bg, float bu,
+                         void *out, int64_t ldo) {
+#define MOE_DECODE_CASE(TGV)                                                                  \
+  case TGV:                                                                                   \
+    hipLaunchKernelGGL((decode_kernel<GLU, TGV, FP8>), grid, dim3(256), 0, st, x, ldx, perm,  \
+                       offsets, kept_offsets, kslots, W1, W2, S1, S2, wrows, K, act, bg, bu,  \
+                       out, ldo);                                                             \
     break;
   switch (tg) {
     MOE_DECODE_CASE(1)
@@ -239,21 +315,30 @@ hipError_t launch_decode(int tg, dim3 grid, hipStream_t st, const uint16_t *x, i
 
 hipError_t launch_decode_gu(const uint16_t *x, int64_t T, int w, const int32_t *perm,
                             const int32_t *offsets, const int32_t *kept_offsets, int kslots,
-                            const uint16_t *Wg, const uint16_t *Wu, int h, int N, int act,
-                            float bg, float bu, uint16_t *hid, hipStream_t st) {
+                            const void *Wg, const void *Wu, const float *sg, const float *su,
+                            int h, int N, int act, float bg, float bu, uint16_t *hid,
+                            hipStream_t st) {
   const int64_t maxrows = T < kDecodeMaxRows ? T : kDecodeMaxRows;
   const int tg = (int)((maxrows + 15) / 16);
-  return launch_decode<true>(tg, dim3(h / RB, N), st, x, w, perm, offsets, kept_offsets, kslots,
-                             Wg, Wu, h, w, act, bg, bu, hid, h);
+  const dim3 grid(h / RB, N);
+  if (sg != nullptr)
+    return launch_decode<true, true>(tg, grid, st, x, w, perm, offsets, kept_offsets, kslots, Wg,
+                                     Wu, sg, su, h, w, act, bg, bu, hid, h);
+  return launch_decode<true, false>(tg, grid, st, x, w, perm, offsets, kept_offsets, kslots, Wg,
+                                    Wu, nullptr, nullptr, h, w, act, bg, bu, hid, h);
 }
 
 hipError_t launch_decode_down(const uint16_t *hid, int64_t T, const int32_t *kept_offsets,
-                              const uint16_t *Wd, int h, int w, int N, float *y_perm,
-                              hipStream_t st) {
+                              const void *Wd, const float *sd, int h, int w, int N,
+                              float *y_perm, hipStream_t st) {
   const int64_t maxrows = T < kDecodeMaxRows ? T : kDecodeMaxRows;
   const int tg = (int)((maxrows + 15) / 16);
-  return launch_decode<false>(tg, dim3(w / RB, N), st, hid, h, nullptr, nullptr,
-                              kept_offsets, 1, Wd, nullptr, w, h, 0, 1.f, 1.f, y_perm, w);
+  const dim3 grid(w / RB, N);
+  if (sd != nullptr)
+    return launch_decode<false, true>(tg, grid, st, hid, h, nullptr, nullptr, kept_offsets, 1,
+                                      Wd, nullptr, sd, nullptr, w, h, 0, 1.f, 1.f, y_perm, w);
+  return launch_decode<false, false>(tg, grid, st, hid, h, nullptr, nullptr, kept_offsets, 1, Wd,
+                                     nullptr, nullptr, nullptr, w, h, 0, 1.f, 1.f, y_perm, w);
 }
 
 }  // namespace moe

@@ -30,6 +30,12 @@
 // fp32 matrices before rounding (the latent layer's shared-expert outputs).
 // The bf16 epilogues store 4 columns at a time: their column counts (h, d, l)
 // are multiples of 128.
+//
+// FP8 weights (routed experts, EP_GLU and EP_F32): B holds OCP E4M3 codes,
+// one 64-byte row per weight row and k-step in a 16 KiB stage, 16-byte
+// chunk c of row r at chunk c ^ ((r >> 2) & 3); each fragment read takes 8
+// codes and widens them exactly to bf16, and the per-row scales multiply the
+// fp32 sums in the epilogue.
 #include <cmath>
 
 #include "common.hpp"
@@ -55,9 +61,19 @@ __device__ __forceinline__ bf16x8 lds_frag(const char *tile, int r, int c) {
   return *reinterpret_cast<const bf16x8 *>(tile + swz(r, c));
 }
 
+// FP8 B stage: the 8 codes of k-step quarter kq (0..7) of row r, widened.
+__device__ __forceinline__ bf16x8 lds_frag8(const char *tile, int r, int kq) {
+  const int c = kq >> 1;
+  const uint2 raw = *reinterpret_cast<const uint2 *>(
+      tile + r * 64 + ((c ^ ((r >> 2) & 3)) << 4) + 8 * (kq & 1));
+  return e4m3x8_to_bf16x8(raw.x, raw.y);
+}
+
 // BM = 256 (waves 128x64) or 192 (waves 96x64, for experts with few rows).
-template <int EPI, int BM>
+template <int EPI, int BM, bool FP8 = false>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
+  static_assert(!FP8 || EPI == EP_GLU || EPI == EP_F32, "fp8 weights: routed experts only");
+  constexpr int ES = FP8 ? 1 : 2;          // bytes per B element
   constexpr int MI = BM / 64;              // 32-row A blocks per wave
   constexpr int kABytes = BM * BK * 2;     // 32 or 24 KiB per A stage
   // A (activations, L2-resident) double-buffered; B (weights, streamed) in a
@@ -132,10 +148,12 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
     const int pc = lc ^ (r & 7);  // the chunk this lane's LDS slot holds
     aoff[i] = (uint32_t)(arow * a.lda * 2) + (uint32_t)(pc << 4);
   }
+  // B rows: bf16, instruction i fills rows 64i + tid/8 (8 lanes a row);
+  // fp8, instruction i (0, 1) fills rows 128i + tid/4 (4 lanes a row).
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = lr + 64 * i;
-    const int pc = lc ^ (r & 7);
+  for (int i = 0; i < (FP8 ? 2 : 4); ++i) {
+    const int r = FP8 ? (tid >> 2) + 128 * i : lr + 64 * i;
+    const int pc = FP8 ? ((tid & 3) ^ ((r >> 2) & 3)) : (lc ^ (r & 7));
     int64_t brow;
     if (glu) {
       const int64_t n = n_tile * 128 + (r & 127);
@@ -144,11 +162,11 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
       const int64_t n = n_tile * BN + r;
       brow = n < a.ncols ? n : a.ncols - 1;
     }
-    boff[i] = (uint32_t)(brow * a.K * 2) + (uint32_t)(pc << 4);
+    boff[i] = (uint32_t)(brow * a.K * ES) + (uint32_t)(pc << 4);
   }
-  const uint16_t *Bg = a.B + (int64_t)g * a.strideB;
-  const uint16_t *Ug = glu ? a.B2 + (int64_t)g * a.strideB : Bg;
-  const uint32_t bbytes = (uint32_t)((int64_t)a.ncols * a.K * 2);
+  const char *Bg = static_cast<const char *>(a.B) + (int64_t)g * a.strideB * ES;
+  const char *Ug = glu ? static_cast<const char *>(a.B2) + (int64_t)g * a.strideB * ES : Bg;
+  const uint32_t bbytes = (uint32_t)((int64_t)a.ncols * a.K * ES);
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.A, 0xFFFFFFFFu);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bg, bbytes);
   const __amdgpu_buffer_rsrc_t ru = make_rsrc(Ug, bbytes);
@@ -165,14 +183,21 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
                                                aoff[i], so, 0, 0);
   };
   auto bload = [&](int k0, int buf, int half) {
-    const uint32_t so = (uint32_t)k0 * 2;
+    const uint32_t so = (uint32_t)k0 * ES;
     char *tb = smem + 2 * kABytes + buf * kBBytes;
+    if constexpr (FP8) {
+      // GLU: rows 0-127 gate, 128-255 up.
+      __builtin_amdgcn_raw_ptr_buffer_load_lds((glu && half) ? ru : rb,
+                                               (lds_ptr_t)(tb + (128 * half + 16 * wave) * 64),
+                                               16, boff[half], so, 0, 0);
+    } else {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int i = 2 * half + j;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds((glu && i >= 2) ? ru : rb,
-                                               (lds_ptr_t)(tb + (64 * i + 8 * wave) * 128), 16,
-                                               boff[i], so, 0, 0);
+      for (int j = 0; j < 2; ++j) {
+        const int i = 2 * half + j;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds((glu && i >= 2) ? ru : rb,
+                                                 (lds_ptr_t)(tb + (64 * i + 8 * wave) * 128), 16,
+                                                 boff[i], so, 0, 0);
+      }
     }
   };
 
@@ -201,7 +226,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < MI; ++i) xa[i] = lds_frag(ta, arow_l[i], c);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) xb[j] = lds_frag(tb, brow_l[j], c);
+    for (int j = 0; j < 2; ++j) xb[j] = FP8 ? lds_frag8(tb, brow_l[j], c) : lds_frag(tb, brow_l[j], c);
   };
   auto mfma16 = [&](const bf16x8 (&xa)[4], const bf16x8 (&xb)[2]) {
 #pragma unroll
@@ -247,8 +272,11 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
   aload(BK, 1);
   bload(BK, 1, 0);
   bload(BK, 1, 1);
-  if constexpr (MI == 4) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");  // stage 0 landed
-  else asm volatile("s_waitcnt vmcnt(7)" ::: "memory");
+  // stage 0 landed: stage 1's MI A loads and 4 (fp8: 2) B loads may fly
+  if constexpr (MI == 4 && !FP8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else if constexpr (MI == 3 && !FP8) asm volatile("s_waitcnt vmcnt(7)" ::: "memory");
+  else if constexpr (MI == 4) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
   barrier_keep_loads();
   read_frags(0, 0, fa, fb);
   for (int kt = 0; kt + 2 < KT; ++kt) {
@@ -256,7 +284,9 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
     MOE_SUBSTEP(read_frags(kt, 1, na, nb), bload((kt + 2) * BK, (kt + 2) % 3, 0), 0x020, 1);
     MOE_SUBSTEP(read_frags(kt, 2, na, nb), bload((kt + 2) * BK, (kt + 2) % 3, 1), 0x020, 1);
     MOE_SUBSTEP(read_frags(kt, 3, na, nb), (void)0, 0x000, 0);
-    asm volatile("s_waitcnt vmcnt(4)" ::: "memory");  // stage kt+1 landed
+    // stage kt+1 landed; only B(kt+2) may still fly
+    if constexpr (FP8) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
     barrier_keep_loads();
     __builtin_amdgcn_sched_barrier(0);
     MOE_SUBSTEP(read_frags(kt + 1, 0, na, nb), aload((kt + 2) * BK, kt & 1), 0x020, 1);
@@ -280,6 +310,28 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
 #undef MOE_WAIT_LOADS
 #undef MOE_SUBSTEP
 
+  // FP8: the scales of this lane's output columns (the weight rows), for
+  // block j and column group q: 4 columns from n_tile*BN + wn*64 + 32j + 8q
+  // + 4*khalf (GLU: j = 0 the gate rows, j = 1 the up rows of the columns
+  // n_tile*128 + wn*32 + 8q + 4*khalf).  Columns past the end read a valid
+  // row and are never stored.
+  f32x4 bsc[2][4];
+  if constexpr (FP8) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float *S = (glu && j) ? a.bscale2 : a.bscale;
+        const int64_t c0 = glu ? n_tile * 128 + wn * 32 + 8 * q + 4 * khalf
+                               : n_tile * BN + wn * 64 + j * 32 + 8 * q + 4 * khalf;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int64_t c = c0 + e < a.ncols ? c0 + e : a.ncols - 1;
+          bsc[j][q][e] = S[(int64_t)g * a.ncols + c];
+        }
+      }
+  }
+
   if constexpr (EPI == EP_F32) {
     // fp32 tile through LDS, the rows of one wm at a time, so that each store
     // instruction writes one whole 1 KiB output row (the register layout
@@ -299,9 +351,10 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
             for (int q = 0; q < 4; ++q) {
               const int rl = i * 32 + (lane & 31);
               const int c = wn * 64 + j * 32 + 8 * q + 4 * khalf;
-              *reinterpret_cast<f32x4 *>(smem + rl * kPitch + c * 4) =
-                  f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                        acc[i][j][4 * q + 3]};
+              f32x4 v = f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                              acc[i][j][4 * q + 3]};
+              if constexpr (FP8) v *= bsc[j][q];
+              *reinterpret_cast<f32x4 *>(smem + rl * kPitch + c * 4) = v;
             }
       }
       __syncthreads();
@@ -340,9 +393,14 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
         if (col >= a.ncols) continue;
         float v[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          v[e] = glu_act_fast(acc[i][0][4 * q + e], acc[i][1][4 * q + e], a.act, a.beta_g,
-                              a.beta_u);
+        for (int e = 0; e < 4; ++e) {
+          float gs = acc[i][0][4 * q + e], us = acc[i][1][4 * q + e];
+          if constexpr (FP8) {
+            gs *= bsc[0][q][e];
+            us *= bsc[1][q][e];
+          }
+          v[e] = glu_act_fast(gs, us, a.act, a.beta_g, a.beta_u);
+        }
         uint2 pk;
         pk.x = pack_bf16x2_hw(v[0], v[1]);
         pk.y = pack_bf16x2_hw(v[2], v[3]);
@@ -410,6 +468,17 @@ __global__ __launch_bounds__(1024) void tile_prefix_kernel(const int32_t *__rest
 // kernel instance is referenced from a non-template function.
 hipError_t launch_kernel(const GemmArgs &a, int epi, int bm, int64_t grid, hipStream_t st) {
   const dim3 g(grid), b(kThreads);
+  if (a.bscale != nullptr) {
+    if (epi != EP_GLU && epi != EP_F32) return hipErrorInvalidValue;
+    if (epi == EP_GLU) {
+      if (bm == 192) grouped_gemm_kernel<EP_GLU, 192, true><<<g, b, 0, st>>>(a);
+      else grouped_gemm_kernel<EP_GLU, 256, true><<<g, b, 0, st>>>(a);
+    } else {
+      if (bm == 192) grouped_gemm_kernel<EP_F32, 192, true><<<g, b, 0, st>>>(a);
+      else grouped_gemm_kernel<EP_F32, 256, true><<<g, b, 0, st>>>(a);
+    }
+    return hipGetLastError();
+  }
   if (bm == 192) {
     switch (epi) {
       case EP_GLU: grouped_gemm_kernel<EP_GLU, 192><<<g, b, 0, st>>>(a); break;

@@ -49,10 +49,13 @@ struct GemmArgs {
   const uint16_t *A;
   int64_t lda;
   // B: per group, rows of K values (K-contiguous); B2 holds the "up" rows
-  // of a GLU pair (same layout as B).  Group g starts at g * strideB.
-  const uint16_t *B;
-  const uint16_t *B2;
+  // of a GLU pair (same layout as B).  Group g starts at g * strideB
+  // (elements).  bf16 values, or E4M3 codes when bscale is set: then row n
+  // of group g is scaled by bscale[g * ncols + n] (bscale2 for B2).
+  const void *B;
+  const void *B2;
   int64_t strideB;
+  const float *bscale, *bscale2;
   int K;
   int ncols;        // output columns per group (h for GLU)
   int mode;         // GemmMode
@@ -88,13 +91,16 @@ hipError_t launch_qb_update(const float *logits, int64_t T, int N, int k, const 
 // ---- decode-sized experts (decode.hip) -------------------------------------
 // Max rows per expert the decode kernels take.
 constexpr int kDecodeMaxRows = 64;
+// W* are bf16, or E4M3 codes when the row scales s* are given (fp32, one
+// per weight row: [N, h] for gate/up, [N, w] for down).
 hipError_t launch_decode_gu(const uint16_t *x, int64_t T, int w, const int32_t *perm,
                             const int32_t *offsets, const int32_t *kept_offsets, int kslots,
-                            const uint16_t *Wg, const uint16_t *Wu, int h, int N, int act,
-                            float bg, float bu, uint16_t *hid, hipStream_t st);
+                            const void *Wg, const void *Wu, const float *sg, const float *su,
+                            int h, int N, int act, float bg, float bu, uint16_t *hid,
+                            hipStream_t st);
 hipError_t launch_decode_down(const uint16_t *hid, int64_t T, const int32_t *kept_offsets,
-                              const uint16_t *Wd, int h, int w, int N, float *y_perm,
-                              hipStream_t st);
+                              const void *Wd, const float *sd, int h, int w, int N,
+                              float *y_perm, hipStream_t st);
 
 // ---- fp32 SIMT experts (simt.hip) ------------------------------------------
 hipError_t launch_simt_gu(const float *x, const int32_t *perm, const int32_t *offsets,

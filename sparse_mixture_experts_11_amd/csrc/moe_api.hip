@@ -46,6 +46,7 @@ int xwidth(const moe_desc_t &d) { return is_latent(d) ? d.l : d.d; }
 bool bf16_path(const moe_desc_t &d) { return d.act_dtype == MOE_BF16; }
 bool decode_path(const moe_desc_t &d) { return bf16_path(d) && d.T <= kDecodeMaxRows; }
 bool router_gemm(const moe_desc_t &d) { return d.N > kRouteWaveMaxN; }
+bool fp8_experts(const moe_desc_t &d) { return d.w_dtype == MOE_FP8_E4M3; }
 
 Layout layout(const moe_desc_t &d) {
   Layout L;
@@ -106,7 +107,7 @@ moe_status_t validate(const moe_desc_t *dp) {
       d.k > kMaxK || d.capacity < -1)
     return MOE_ERR_ARG;
   if ((d.act_dtype != MOE_F32 && d.act_dtype != MOE_BF16) ||
-      (d.w_dtype != MOE_F32 && d.w_dtype != MOE_BF16) ||
+      (d.w_dtype != MOE_F32 && d.w_dtype != MOE_BF16 && d.w_dtype != MOE_FP8_E4M3) ||
       (d.router_dtype != MOE_F32 && d.router_dtype != MOE_BF16))
     return MOE_ERR_ARG;
   if ((d.gate != MOE_GATE_RENORM && d.gate != MOE_GATE_PROB) ||
@@ -122,7 +123,9 @@ moe_status_t validate(const moe_desc_t *dp) {
   if (d.T * (int64_t)d.k > (int64_t)INT32_MAX) return MOE_ERR_UNSUPPORTED;
 
   // What the kernels implement (no fallback path).
-  if (d.act_dtype != d.w_dtype) return MOE_ERR_UNSUPPORTED;
+  // Expert weights in the activation dtype, or fp8 E4M3 under bf16 activations.
+  if (d.act_dtype != d.w_dtype && !(fp8_experts(d) && d.act_dtype == MOE_BF16))
+    return MOE_ERR_UNSUPPORTED;
   if (d.d % 8 != 0) return MOE_ERR_UNSUPPORTED;
   if (d.act_dtype == MOE_F32) {
     if (d.router_dtype != MOE_F32 || d.l != 0 || router_gemm(d)) return MOE_ERR_UNSUPPORTED;
@@ -233,9 +236,11 @@ hipError_t do_tile_prefix(const moe_desc_t &d, const Layout &L, const int32_t *k
                             st);
 }
 
+// sg, su, sd: fp8 row scales (null for bf16 / fp32 weights).
 hipError_t do_ffn_gate_up(const moe_desc_t &d, const Layout &L, const void *x, const int32_t *perm,
                           const int32_t *offsets, const int32_t *kept_offsets, const void *Wg,
-                          const void *Wu, void *ws, hipStream_t st) {
+                          const void *Wu, const float *sg, const float *su, void *ws,
+                          hipStream_t st) {
   const int w = xwidth(d);
   if (!bf16_path(d))
     return launch_simt_gu(static_cast<const float *>(x), perm, offsets, kept_offsets, d.k,
@@ -243,15 +248,16 @@ hipError_t do_ffn_gate_up(const moe_desc_t &d, const Layout &L, const void *x, c
                           d.N, d.act, d.beta_g, d.beta_u, region<float>(ws, L.hid), st);
   if (decode_path(d))
     return launch_decode_gu(static_cast<const uint16_t *>(x), d.T, w, perm, offsets, kept_offsets,
-                            d.k, static_cast<const uint16_t *>(Wg),
-                            static_cast<const uint16_t *>(Wu), d.h, d.N, d.act, d.beta_g, d.beta_u,
+                            d.k, Wg, Wu, sg, su, d.h, d.N, d.act, d.beta_g, d.beta_u,
                             region<uint16_t>(ws, L.hid), st);
   GemmArgs a;
   memset(&a, 0, sizeof(a));
   a.A = static_cast<const uint16_t *>(x);
   a.lda = w;
-  a.B = static_cast<const uint16_t *>(Wg);
-  a.B2 = static_cast<const uint16_t *>(Wu);
+  a.B = Wg;
+  a.B2 = Wu;
+  a.bscale = sg;
+  a.bscale2 = su;
   a.strideB = (int64_t)d.h * w;
   a.K = w;
   a.ncols = d.h;
@@ -272,19 +278,20 @@ hipError_t do_ffn_gate_up(const moe_desc_t &d, const Layout &L, const void *x, c
 }
 
 hipError_t do_ffn_down(const moe_desc_t &d, const Layout &L, const int32_t *kept_offsets,
-                       const void *Wd, float *y_perm, void *ws, hipStream_t st) {
+                       const void *Wd, const float *sd, float *y_perm, void *ws, hipStream_t st) {
   const int w = xwidth(d);
   if (!bf16_path(d))
     return launch_simt_down(region<float>(ws, L.hid), kept_offsets,
                             static_cast<const float *>(Wd), d.h, w, d.N, y_perm, st);
   if (decode_path(d))
-    return launch_decode_down(region<uint16_t>(ws, L.hid), d.T, kept_offsets,
-                              static_cast<const uint16_t *>(Wd), d.h, w, d.N, y_perm, st);
+    return launch_decode_down(region<uint16_t>(ws, L.hid), d.T, kept_offsets, Wd, sd, d.h, w,
+                              d.N, y_perm, st);
   GemmArgs a;
   memset(&a, 0, sizeof(a));
   a.A = region<uint16_t>(ws, L.hid);
   a.lda = d.h;
-  a.B = static_cast<const uint16_t *>(Wd);
+  a.B = Wd;
+  a.bscale = sd;
   a.strideB = (int64_t)w * d.h;
   a.K = d.h;
   a.ncols = w;
@@ -358,6 +365,10 @@ moe_status_t forward_impl(const moe_desc_t *desc, const moe_weights_t *wts, cons
       wts->W_gate == nullptr || wts->W_up == nullptr || wts->W_down == nullptr)
     return MOE_ERR_ARG;
   if (is_latent(d) && (wts->W_ldown == nullptr || wts->W_lup == nullptr)) return MOE_ERR_ARG;
+  // Row scales: all three with fp8 expert weights, none otherwise.
+  const bool any_scale = wts->gate_scale || wts->up_scale || wts->down_scale;
+  const bool all_scales = wts->gate_scale && wts->up_scale && wts->down_scale;
+  if (fp8_experts(d) ? !all_scales : any_scale) return MOE_ERR_ARG;
   if (is_latent(d) && d.n_shared > 0 &&
       (wts->Ws_gate == nullptr || wts->Ws_up == nullptr || wts->Ws_down == nullptr))
     return MOE_ERR_ARG;
@@ -399,9 +410,10 @@ moe_status_t forward_impl(const moe_desc_t *desc, const moe_weights_t *wts, cons
     MOE_TRY(tr.mark());
     x = xl;
   }
-  MOE_TRY(do_ffn_gate_up(d, L, x, perm, offsets, kept_offsets, wts->W_gate, wts->W_up, ws, st));
+  MOE_TRY(do_ffn_gate_up(d, L, x, perm, offsets, kept_offsets, wts->W_gate, wts->W_up,
+                         wts->gate_scale, wts->up_scale, ws, st));
   MOE_TRY(tr.mark());
-  MOE_TRY(do_ffn_down(d, L, kept_offsets, wts->W_down, y_perm, ws, st));
+  MOE_TRY(do_ffn_down(d, L, kept_offsets, wts->W_down, wts->down_scale, y_perm, ws, st));
   MOE_TRY(tr.mark());
   if (!is_latent(d)) {
     MOE_TRY(launch_combine(y_perm, row_of, tw, d.T, d.k, d.d, bf16_path(d), false, 0.f, y, st));
@@ -543,22 +555,36 @@ moe_status_t moe_dispatch(const moe_desc_t *desc, const int32_t *topk_idx, int32
                                 drop, nullptr, ws, reinterpret_cast<hipStream_t>(stream)));
 }
 
-moe_status_t moe_expert_ffn(const moe_desc_t *desc, const void *x, const int32_t *perm,
-                            const int32_t *offsets, const int32_t *kept_offsets,
-                            const void *W_gate, const void *W_up, const void *W_down,
-                            float *y_perm, void *ws, size_t ws_bytes, moe_stream_t stream) {
+moe_status_t moe_expert_ffn_scaled(const moe_desc_t *desc, const void *x, const int32_t *perm,
+                                   const int32_t *offsets, const int32_t *kept_offsets,
+                                   const void *W_gate, const void *W_up, const void *W_down,
+                                   const float *gate_scale, const float *up_scale,
+                                   const float *down_scale, float *y_perm, void *ws,
+                                   size_t ws_bytes, moe_stream_t stream) {
   const moe_status_t v = validate(desc);
   if (v != MOE_OK) return v;
   if (x == nullptr || perm == nullptr || offsets == nullptr || kept_offsets == nullptr ||
       W_gate == nullptr || W_up == nullptr || W_down == nullptr || y_perm == nullptr)
     return MOE_ERR_ARG;
+  const bool any_scale = gate_scale || up_scale || down_scale;
+  const bool all_scales = gate_scale && up_scale && down_scale;
+  if (fp8_experts(*desc) ? !all_scales : any_scale) return MOE_ERR_ARG;
   const Layout L = layout(*desc);
   if (ws == nullptr || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   MOE_TRY(do_tile_prefix(*desc, L, kept_offsets, ws, st));
-  MOE_TRY(do_ffn_gate_up(*desc, L, x, perm, offsets, kept_offsets, W_gate, W_up, ws, st));
-  MOE_TRY(do_ffn_down(*desc, L, kept_offsets, W_down, y_perm, ws, st));
+  MOE_TRY(do_ffn_gate_up(*desc, L, x, perm, offsets, kept_offsets, W_gate, W_up, gate_scale,
+                         up_scale, ws, st));
+  MOE_TRY(do_ffn_down(*desc, L, kept_offsets, W_down, down_scale, y_perm, ws, st));
   return MOE_OK;
+}
+
+moe_status_t moe_expert_ffn(const moe_desc_t *desc, const void *x, const int32_t *perm,
+                            const int32_t *offsets, const int32_t *kept_offsets,
+                            const void *W_gate, const void *W_up, const void *W_down,
+                            float *y_perm, void *ws, size_t ws_bytes, moe_stream_t stream) {
+  return moe_expert_ffn_scaled(desc, x, perm, offsets, kept_offsets, W_gate, W_up, W_down,
+                               nullptr, nullptr, nullptr, y_perm, ws, ws_bytes, stream);
 }
 
 moe_status_t moe_combine(const moe_desc_t *desc, const float *y_perm, const int32_t *row_of,

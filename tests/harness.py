@@ -80,11 +80,36 @@ def upload_stacked(cfg: C.Layer, which: str, device="cuda", chunk_experts: int =
     return dev
 
 
+def upload_stacked_fp8(cfg: C.Layer, which: str, device="cuda"):
+    """FP8 routed-expert tensor on the device: (E4M3 codes uint8 [N, rows,
+    cols], fp32 row scales [N, rows]), generated a few experts at a time."""
+    xw, h, N = cfg.x_width, cfg.h, cfg.N
+    rows, cols = (h, xw) if which in ("gate", "up") else (xw, h)
+    per = rows * cols
+    import synth as S
+    tid, std = {"gate": (S.TID_W_GATE, 1 / math.sqrt(xw)), "up": (S.TID_W_UP, 1 / math.sqrt(xw)),
+                "down": (S.TID_W_DOWN, 1 / math.sqrt(h))}[which]
+    codes = torch.empty((N, rows, cols), dtype=torch.uint8, device=device)
+    scale = torch.empty((N, rows), dtype=torch.float32, device=device)
+    step = max(1, min(N, (256 << 20) // per))
+    stage = torch.empty(step * per, dtype=torch.uint8, pin_memory=True)
+    for e0 in range(0, N, step):
+        n = min(step, N - e0)
+        m = S.normal_fp8_rows(cfg.seed, tid, n * rows, cols, std, start=e0 * per,
+                              codes=stage.numpy()[:n * per])
+        codes.view(-1)[e0 * per:(e0 + n) * per].copy_(stage[:n * per], non_blocking=False)
+        scale[e0:e0 + n].copy_(torch.from_numpy(m.scale.reshape(n, rows)))
+    return codes, scale
+
+
 def upload_layer(cfg: C.Layer, device="cuda") -> Dict[str, torch.Tensor]:
-    w = {"W_route": to_device(cfg.w_route(), device),
-         "W_gate": upload_stacked(cfg, "gate", device),
-         "W_up": upload_stacked(cfg, "up", device),
-         "W_down": upload_stacked(cfg, "down", device)}
+    w = {"W_route": to_device(cfg.w_route(), device)}
+    if cfg.w_dtype == "fp8":
+        for name in ("gate", "up", "down"):
+            w["W_" + name], w[name + "_scale"] = upload_stacked_fp8(cfg, name, device)
+    else:
+        for name in ("gate", "up", "down"):
+            w["W_" + name] = upload_stacked(cfg, name, device)
     if cfg.latent:
         w["W_ldown"] = to_device(cfg.w_ldown(), device)
         w["W_lup"] = to_device(cfg.w_lup(), device)

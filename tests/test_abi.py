@@ -159,3 +159,40 @@ def test_stage_names():
 def test_status_strings():
     for s in range(5):
         assert moe.moe_status_string(s)
+
+
+def call_forward_fp8(desc, scales=(4096, 4096, 4096), ws_bytes=10):
+    w = L.MoeWeights(*([4096] * 4 + [None] * 6 + list(scales)))
+    return L.load().moe_forward(ctypes.byref(desc), ctypes.byref(w), FAKE, FAKE, None, FAKE,
+                                ws_bytes, None)
+
+
+def test_fp8_weights_validate():
+    lib = L.load()
+    n = None
+    d = H.desc_for(C.MIXTRAL_DECODE_FP8)
+    assert d.w_dtype == L.MOE_FP8_E4M3
+    # All three row scales, or none: a complete set gets as far as the workspace check.
+    assert call_forward_fp8(d) == L.MOE_ERR_WORKSPACE
+    assert call_forward_fp8(d, scales=(4096, None, 4096)) == L.MOE_ERR_ARG
+    assert call_forward_fp8(d, scales=(None, None, None)) == L.MOE_ERR_ARG
+    plain = H.desc_for(C.MIXTRAL_DECODE)
+    assert call_forward_fp8(plain, scales=(None, None, 4096)) == L.MOE_ERR_ARG
+    assert call_forward_fp8(plain, scales=(None, None, None)) == L.MOE_ERR_WORKSPACE
+    # fp8 experts need bf16 activations; no other dtype code is accepted.
+    f32 = H.desc_for(C.TINY.with_(w_dtype="fp8"))
+    assert call_forward_fp8(f32, ws_bytes=1 << 40) == L.MOE_ERR_UNSUPPORTED
+    d3 = H.desc_for(C.MIXTRAL_DECODE_FP8)
+    d3.w_dtype = 3
+    assert call_forward_fp8(d3) == L.MOE_ERR_ARG
+    # The expert stage: the unscaled entry point cannot take fp8 weights.
+    big = 1 << 40
+    assert lib.moe_expert_ffn(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                              FAKE, big, n) == L.MOE_ERR_ARG
+    ffn = lib.moe_expert_ffn_scaled
+    assert ffn(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+               FAKE, 10, n) == L.MOE_ERR_WORKSPACE
+    assert ffn(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, n, FAKE, FAKE,
+               FAKE, big, n) == L.MOE_ERR_ARG
+    assert ffn(ctypes.byref(plain), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, n, n, FAKE,
+               FAKE, big, n) == L.MOE_ERR_ARG
