@@ -33,6 +33,8 @@ def parse():
     p.add_argument("--workload", default="mixtral_prefill_t16384")
     p.add_argument("--decode-workload", default="mixtral_decode_t32",
                    help="second workload reported beside the main one ('' to skip)")
+    p.add_argument("--fp8-decode-workload", default="mixtral_decode_t32_fp8",
+                   help="the decode workload with FP8 E4M3 expert weights ('' to skip)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-tokens", type=int, default=384)
     p.add_argument("--copy-calibration", action="store_true",
@@ -46,12 +48,13 @@ def algorithmic(cfg, counts_kept):
     bytes of the selected experts' weights (each touched expert read once)."""
     R = int(sum(counts_kept))
     xw = cfg.x_width
-    wb = 2 if cfg.w_dtype == "bf16" else 4
+    wb = {"bf16": 2, "f32": 4, "fp8": 1}[cfg.w_dtype]
+    sb = 4 if cfg.w_dtype == "fp8" else 0      # fp32 scale per weight row
     gu_flops = 2.0 * R * xw * 2 * cfg.h
     down_flops = 2.0 * R * cfg.h * xw
     touched = sum(1 for c in counts_kept if c > 0)
-    gu_bytes = touched * 2 * cfg.h * xw * wb
-    down_bytes = touched * cfg.h * xw * wb
+    gu_bytes = touched * 2 * cfg.h * (xw * wb + sb)
+    down_bytes = touched * xw * (cfg.h * wb + sb)
     return {"rows": R, "gu_flops": gu_flops, "down_flops": down_flops, "gu_bytes": gu_bytes,
             "down_bytes": down_bytes, "touched": touched}
 
@@ -215,9 +218,10 @@ def main():
     if cfg.act_dtype != "bf16":
         kernel = "simt_gu_kernel (fp32 expert gate/up)"
     elif cfg.T <= 64:
-        kernel = "decode_kernel<true, 2> (expert gate/up)"
+        kernel = f"decode_kernel<true, 2, {str(cfg.w_dtype == 'fp8').lower()}> (expert gate/up)"
     else:
-        kernel = f"grouped_gemm_kernel<EP_GLU, {tile_rows(cfg)}> (expert gate/up)"
+        kernel = (f"grouped_gemm_kernel<EP_GLU, {tile_rows(cfg)}"
+                  f"{', true' if cfg.w_dtype == 'fp8' else ''}> (expert gate/up)")
     if intensity < ridge:
         achieved = alg["gu_bytes"] / t / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -237,7 +241,7 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if cfg.act_dtype == "bf16" else "f32", "data": "synthetic",
         "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "h": cfg.h, "N": cfg.N,
-                   "k": cfg.k, "parallelism": "single GPU"},
+                   "k": cfg.k, "expert_weights": cfg.w_dtype, "parallelism": "single GPU"},
         "tflops": total_flops / (r["ms_per_step"] / 1e3) / 1e12,
         "expert_stage_tflops": total_flops / (
             (r["stages_ms"]["expert_gate_up"] + r["stages_ms"]["expert_down"]) / 1e3) / 1e12,
@@ -246,14 +250,17 @@ def main():
     }
     if "quantile_balancing" in r:
         line["quantile_balancing"] = r["quantile_balancing"]
-    if args.decode_workload:
-        dc = C.ALL[args.decode_workload]
+    for key, name in (("decode", args.decode_workload), ("decode_fp8", args.fp8_decode_workload)):
+        if not name:
+            continue
+        dc = C.ALL[name]
         print(f"[bench] {dc.name}", file=sys.stderr, flush=True)
         rd = run_workload(dc, args.steps, args.warmup)
         a = rd["alg"]
         wbytes = a["gu_bytes"] + a["down_bytes"]
-        line["decode"] = {
-            "workload": dc.name, "tokens_per_s": dc.T / (rd["ms_per_step"] / 1e3),
+        line[key] = {
+            "workload": dc.name, "expert_weights": dc.w_dtype,
+            "tokens_per_s": dc.T / (rd["ms_per_step"] / 1e3),
             "ms_per_step": rd["ms_per_step"], "stages_ms": rd["stages_ms"],
             "selected_expert_weight_bytes": wbytes,
             "hbm_frac_whole_forward": wbytes / (rd["ms_per_step"] / 1e3) / 1e9 / PEAK_HBM_GBS,

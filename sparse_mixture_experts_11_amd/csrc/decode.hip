@@ -16,10 +16,10 @@
 // weights.
 //   GLU = true : hid[row] = act(W_gate x, W_up x), x rows gathered via perm
 //   GLU = false: y_perm[row] = W_down hid[row], fp32
-// FP8 weights (E4M3 codes, one fp32 scale per weight row) stream the same
-// bytes per window, so each window covers twice the k; the operands are
-// widened to bf16 exactly after the LDS read, and the row scales multiply
-// the fp32 sums after the split-K reduction.
+// FP8 weights (E4M3 codes, one fp32 scale per weight row) use 256-byte row
+// windows, 256 k; the operands are widened to bf16 exactly after the LDS
+// read, and the row scales multiply the fp32 sums after the split-K
+// reduction.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -30,13 +30,14 @@ namespace {
 constexpr int NRB = 2;          // 16-row weight blocks per wave (token fragments reused NRB x)
 constexpr int RB = 16 * NRB;    // weight rows per workgroup
 constexpr int kWaves = 4;       // split-K ways
-// k-steps of 32 per iteration: 16 KiB of weights per wave per iteration
-// (GLU: 2 matrices x 32 rows x 256 B; down: 32 rows x 512 B), so U = 4 / 8
-// for bf16 weights and 8 / 16 for fp8.
+// k-steps of 32 per iteration.  bf16: 16 KiB of weights per wave per
+// iteration (GLU: 2 matrices x 32 rows x 256 B, U = 4; down: 32 rows x
+// 512 B, U = 8).  fp8: 256-byte row windows for both (U = 8): GLU streams
+// 16 KiB, down 8 KiB, which keeps it at two workgroups per CU (a 512-byte
+// window's operand registers push it past 256 VGPRs; measured 0.13 vs
+// 0.10 ms at the Mixtral decode shape).
 template <bool GLU, bool FP8>
-constexpr int unroll_of() { return (GLU ? 4 : 8) * (FP8 ? 2 : 1); }
-// Per-wave LDS slice: one iteration's weights, row pitch U * 32 * ES bytes.
-constexpr int kSlice = 16384;
+constexpr int unroll_of() { return FP8 ? 8 : (GLU ? 4 : 8); }
 
 template <bool GLU, int TG, bool FP8>
 __global__ __launch_bounds__(256) void decode_kernel(
@@ -50,7 +51,8 @@ __global__ __launch_bounds__(256) void decode_kernel(
   constexpr int U = unroll_of<GLU, FP8>();
   constexpr int kPitch = U * 32 * ES;     // bytes of one row's window in a slice
   constexpr int kLoads = kPitch / 32;     // 1 KiB load instructions per matrix
-  static_assert(NM * RB * kPitch == kSlice, "slice holds one iteration");
+  constexpr int kSlice = NM * RB * kPitch;  // per-wave LDS slice: one iteration's weights
+  static_assert(kPitch >= 256, "the chunk swizzle XORs with 4 row bits: 16 chunks a row");
   // After the loop the same LDS holds the partial sums of waves 1 .. 3.
   constexpr int kRedBytes = NM * NRB * TG * 64 * 16;
   constexpr int kLds = kWaves * kSlice > (kWaves - 1) * kRedBytes ? kWaves * kSlice
