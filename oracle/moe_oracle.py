@@ -48,7 +48,10 @@ Readings where the pages are silent (listed again in the design doc):
     q = round(k T / N), histogram of 256 bins over [min, max] of required;
   * FP8 expert weights: OCP E4M3 codes (the format whose largest value, 448,
     the SiTU-GLU passage quotes) with one fp32 scale per weight row; a
-    stored row is its scale times each code's exact value.
+    stored row is its scale times each code's exact value;
+  * MXFP4 expert weights (the MCU page stores 4-bit experts): OCP MX FP4,
+    E2M1 elements in runs of 32 along a row sharing one E8M0 scale, two
+    elements a byte with the even element in the low nibble.
 
 Pins (tests/test_oracle_pins.py): the capacity example [10,3,2,1] -> drops
 6/4/0; the balanced/collapsed aux example (1.0000 / 2.8449); the parameter
@@ -63,7 +66,9 @@ constant; the histogram estimate lies within one bin of the exact value; a
 hand-worked 4-token example; b = 0 reproduces the unbiased routing.
 FP8 pins: all 256 E4M3 codes decode as torch.float8_e4m3fn does, with the
 format's landmarks (448, 2^-9, 2^-6, -0, NaN) and a hand-expanded scaled
-matrix.
+matrix.  MXFP4 pins: E8M0 against torch.float8_e8m0fnu; every E2M1 value
+against torch's decode of the E4M3 code with the same sign, exponent and
+mantissa (E2M1 is a subset of E4M3); a hand-expanded two-block matrix.
 Parity unpinned: the exact SiTU-GLU form, the LatentMoE wiring and the
 Quantile Balancing readings (score, cutoff, q, bins) are readings, pinned
 only through the limits and invariants above.
@@ -96,10 +101,41 @@ def e4m3_value(code: int) -> float:
 E4M3_TABLE = np.array([e4m3_value(c) for c in range(256)], dtype=np.float64)
 
 
+def e2m1_value(code: int) -> float:
+    """Exact value of one OCP FP4 E2M1 code (4 bits): bit 3 sign, bits 2..1
+    the exponent with bias 1, bit 0 the mantissa; exponent field 0 holds the
+    subnormal m * 0.5.  No infinities or NaN."""
+    sign = -1.0 if code & 0x8 else 1.0
+    e, m = (code >> 1) & 0x3, code & 0x1
+    if e == 0:
+        return sign * m * 0.5
+    return sign * (1.0 + m / 2.0) * 2.0 ** (e - 1)
+
+
+def e8m0_value(code: int) -> float:
+    """Exact value of one OCP E8M0 scale byte: 2^(code - 127); 0xFF is NaN."""
+    return math.nan if code == 0xFF else 2.0 ** (code - 127)
+
+
+E2M1_TABLE = np.array([e2m1_value(c) for c in range(16)], dtype=np.float64)
+E8M0_TABLE = np.array([e8m0_value(c) for c in range(256)], dtype=np.float64)
+
+
 def expand(stored) -> np.ndarray:
     """Exact fp64 value of stored bf16 bit patterns (uint16), fp32 values, or
     an FP8 row-scaled matrix (an object with ``codes`` [..., rows, cols] uint8
     and ``scale`` [..., rows] fp32): element (r, c) = scale[r] * E4M3(code)."""
+    if hasattr(stored, "packed") and hasattr(stored, "block_scale"):
+        # OCP MXFP4: element 2i of a row in the low nibble of byte i, each run
+        # of 32 elements times its E8M0 scale.
+        packed = np.asarray(stored.packed)
+        assert packed.dtype == np.uint8
+        codes = np.stack([packed & 0xF, packed >> 4], axis=-1).reshape(
+            packed.shape[:-1] + (packed.shape[-1] * 2,))
+        vals = E2M1_TABLE[codes]
+        sc = E8M0_TABLE[np.asarray(stored.block_scale)]
+        assert sc.shape[-1] * 32 == vals.shape[-1]
+        return (vals.reshape(vals.shape[:-1] + (-1, 32)) * sc[..., None]).reshape(vals.shape)
     if hasattr(stored, "codes") and hasattr(stored, "scale"):
         codes = np.asarray(stored.codes)
         scale = np.asarray(stored.scale, dtype=np.float32).astype(np.float64)

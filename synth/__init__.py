@@ -6,8 +6,10 @@ none of the MoE layer's arithmetic. Every element is a pure function of
 ``synth.c``), so any slice of any tensor can be regenerated independently.
 
 Stored values are returned as numpy arrays of the storage type:
-``uint16`` bit patterns for bf16, ``float32`` for fp32, and for fp8 weights an
-``Fp8Rows`` pair of ``uint8`` E4M3 codes with one ``float32`` scale per row.
+``uint16`` bit patterns for bf16, ``float32`` for fp32, for fp8 weights an
+``Fp8Rows`` pair of ``uint8`` E4M3 codes with one ``float32`` scale per row,
+and for MXFP4 weights an ``MxFp4Rows`` pair of packed E2M1 codes with one
+E8M0 scale byte per 32 values.
 """
 from __future__ import annotations
 
@@ -67,6 +69,9 @@ def _load():
         lib.synth_f64_to_e4m3.argtypes = [dbl]
         lib.synth_f64_to_e4m3.restype = ctypes.c_uint8
         lib.synth_normal_e4m3_rows.argtypes = [u64, u64, u64, u64, u64, dbl, ptr, ptr]
+        lib.synth_f64_to_e2m1.argtypes = [dbl]
+        lib.synth_f64_to_e2m1.restype = ctypes.c_uint8
+        lib.synth_normal_mxfp4_rows.argtypes = [u64, u64, u64, u64, u64, dbl, ptr, ptr]
         _lib = lib
     return _lib
 
@@ -156,3 +161,36 @@ def normal_fp8_rows(seed: int, tid: int, rows: int, cols: int, std: float,
         scale = np.empty(rows, dtype=np.float32)
     _load().synth_normal_e4m3_rows(seed, tid, start, rows, cols, std, _ptr(codes), _ptr(scale))
     return Fp8Rows(codes.reshape(rows, cols), scale.reshape(rows))
+
+
+@dataclasses.dataclass(frozen=True)
+class MxFp4Rows:
+    """A matrix stored as OCP MXFP4: E2M1 codes packed two per byte (element
+    2i in the low nibble of byte i of its row) and one E8M0 scale byte per
+    32 consecutive elements of a row (value 2^(s - 127))."""
+    packed: np.ndarray        # uint8 [..., rows, cols / 2]
+    block_scale: np.ndarray   # uint8 [..., rows, cols / 32]
+
+    @property
+    def shape(self):
+        return self.packed.shape[:-1] + (self.packed.shape[-1] * 2,)
+
+
+def f64_to_e2m1(x: float) -> int:
+    return int(_load().synth_f64_to_e2m1(float(x)))
+
+
+def normal_mxfp4_rows(seed: int, tid: int, rows: int, cols: int, std: float,
+                      start: int = 0, packed: np.ndarray | None = None,
+                      scale: np.ndarray | None = None) -> MxFp4Rows:
+    """``std * N(0,1)`` elements [start, start + rows*cols) as MXFP4 rows: the
+    same draws as ``normal_stored``, each run of 32 scaled by 2^e with
+    e = floor(log2 max|v|) - 2 and rounded to E2M1 nearest-even."""
+    rows, cols = int(rows), int(cols)
+    assert cols % 32 == 0
+    if packed is None:
+        packed = np.empty(rows * cols // 2, dtype=np.uint8)
+    if scale is None:
+        scale = np.empty(rows * cols // 32, dtype=np.uint8)
+    _load().synth_normal_mxfp4_rows(seed, tid, start, rows, cols, std, _ptr(packed), _ptr(scale))
+    return MxFp4Rows(packed.reshape(rows, cols // 2), scale.reshape(rows, cols // 32))

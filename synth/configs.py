@@ -28,7 +28,7 @@ class Layer:
     N: int                      # routed experts (E for the latent layer)
     k: int
     act_dtype: str = "bf16"     # "f32" | "bf16"
-    w_dtype: str = "bf16"      # routed experts: "f32" | "bf16" | "fp8" (E4M3 rows)
+    w_dtype: str = "bf16"      # routed experts: "f32" | "bf16" | "fp8" (E4M3 rows) | "mxfp4"
     router_dtype: str = "bf16"
     gate: str = "renorm"        # "renorm" (a = p / sum_S p) | "prob" (a = p)
     act: str = "swiglu"         # "swiglu" | "situ"
@@ -105,6 +105,8 @@ class Layer:
     def _expert_matrix(self, tid, rows, cols, std, start):
         if self.w_dtype == "fp8":
             return S.normal_fp8_rows(self.seed, tid, rows, cols, std, start=start)
+        if self.w_dtype == "mxfp4":
+            return S.normal_mxfp4_rows(self.seed, tid, rows, cols, std, start=start)
         return S.normal_stored(self.seed, tid, rows * cols, std, self.w_dtype,
                                start=start).reshape(rows, cols)
 
@@ -130,6 +132,10 @@ class Layer:
             m = S.normal_fp8_rows(self.seed, tid, self.N * shape[1], shape[2], std,
                                   codes=None if out is None else out.reshape(-1))
             return S.Fp8Rows(m.codes.reshape(shape), m.scale.reshape(shape[:2]))
+        if self.w_dtype == "mxfp4":
+            m = S.normal_mxfp4_rows(self.seed, tid, self.N * shape[1], shape[2], std)
+            return S.MxFp4Rows(m.packed.reshape(shape[:2] + (shape[2] // 2,)),
+                               m.block_scale.reshape(shape[:2] + (shape[2] // 32,)))
         flat = None if out is None else out.reshape(-1)
         return S.normal_stored(self.seed, tid, n, std, self.w_dtype, out=flat).reshape(shape)
 
@@ -137,7 +143,7 @@ class Layer:
     # dtype when the routed experts are fp8.
     @property
     def dense_w_dtype(self) -> str:
-        return self.act_dtype if self.w_dtype == "fp8" else self.w_dtype
+        return self.act_dtype if self.w_dtype in ("fp8", "mxfp4") else self.w_dtype
 
     def w_ldown(self) -> np.ndarray:   # [l, d]
         return S.normal_stored(self.seed, S.TID_W_LDOWN, self.l * self.d,
@@ -198,7 +204,10 @@ LATENT = Layer("latent_t8192", T=8192, d=4096, h=3072, N=896, k=16, act="situ",
 MIXTRAL_DECODE_FP8 = MIXTRAL_DECODE.with_(name="mixtral_decode_t32_fp8", w_dtype="fp8")
 MIXTRAL_PREFILL_FP8 = MIXTRAL_PREFILL.with_(name="mixtral_prefill_t16384_fp8", w_dtype="fp8")
 LATENT_FP8 = LATENT.with_(name="latent_t8192_fp8", w_dtype="fp8")
+# MXFP4 routed-expert weights (E2M1 in blocks of 32 with E8M0 scales): the
+# decode workload.
+MIXTRAL_DECODE_MXFP4 = MIXTRAL_DECODE.with_(name="mixtral_decode_t32_mxfp4", w_dtype="mxfp4")
 
 ALL = {c.name: c for c in (TINY, TINY_PLANTED, MCU_BATCH, MCU_DECODE, MIXTRAL_PREFILL,
                            MIXTRAL_DECODE, SWITCH_SKEWED, LATENT, MIXTRAL_DECODE_FP8,
-                           MIXTRAL_PREFILL_FP8, LATENT_FP8)}
+                           MIXTRAL_PREFILL_FP8, LATENT_FP8, MIXTRAL_DECODE_MXFP4)}

@@ -28,6 +28,8 @@
  *     NaN propagation.  No intermediate fp32 rounding (no double rounding).
  *   - fp8 E4M3 rows: per-row fp32 scale max|row| / 448, codes rounded
  *     nearest-even from fp64 (synth_normal_e4m3_rows).
+ *   - MXFP4 rows: E8M0 scale per 32 values, E2M1 elements rounded
+ *     nearest-even (synth_normal_mxfp4_rows).
  */
 #include <math.h>
 #include <stdint.h>
@@ -220,5 +222,64 @@ void synth_normal_e4m3_rows(uint64_t seed, uint64_t tensor_id, uint64_t start, u
         codes[(uint64_t)r * cols + i] = synth_f64_to_e4m3(row[i] / (double)sc);
     }
     free(row);
+  }
+}
+
+/* Round one fp64 value to an OCP E2M1 (FP4) code, nearest-even, saturating:
+   1 sign bit, 2 exponent bits with bias 1, 1 mantissa bit; magnitudes
+   0, 0.5, 1, 1.5, 2, 3, 4, 6 (codes 0..7), no infinities or NaN. */
+uint8_t synth_f64_to_e2m1(double x) {
+  static const double mag[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+  const uint8_t sign = signbit(x) ? 0x8u : 0u;
+  const double a = fabs(x);
+  if (isnan(x)) return sign; /* not produced by the generator */
+  if (a >= 6.0) return (uint8_t)(sign | 7u);
+  int best = 0;
+  for (int c = 1; c < 8; ++c) {
+    const double d = fabs(a - mag[c]), db = fabs(a - mag[best]);
+    /* ties go to the code with an even mantissa bit (the even code) */
+    if (d < db || (d == db && (c & 1) == 0)) best = c;
+  }
+  return (uint8_t)(sign | (uint8_t)best);
+}
+
+/* rows x cols values std * N(0,1)[start + r*cols + c] as OCP MXFP4: each run
+   of 32 along a row shares the E8M0 scale 2^e with e = floor(log2(max |v|))
+   - 2 (2 = the largest E2M1 exponent; e clamped to [-127, 127], 2^-127 for
+   an all-zero block), and each element is E2M1(v / 2^e).  Element c of a row
+   sits in byte c/2 of packed, the low nibble for even c.  cols % 32 == 0. */
+void synth_normal_mxfp4_rows(uint64_t seed, uint64_t tensor_id, uint64_t start, uint64_t rows,
+                             uint64_t cols, double std, uint8_t *packed, uint8_t *scale) {
+  const uint64_t K = synth_stream_key(seed, tensor_id);
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < (int64_t)rows; ++r) {
+    uint64_t cached = UINT64_MAX;
+    double c0 = 0.0, s0 = 0.0;
+    for (uint64_t b = 0; b < cols / 32; ++b) {
+      double v[32], amax = 0.0;
+      for (int i = 0; i < 32; ++i) {
+        const uint64_t e = start + (uint64_t)r * cols + b * 32 + (uint64_t)i;
+        if ((e >> 1) != cached) {
+          cached = e >> 1;
+          normal_pair(K, cached, &c0, &s0);
+        }
+        v[i] = std * ((e & 1) ? s0 : c0);
+        if (fabs(v[i]) > amax) amax = fabs(v[i]);
+      }
+      int ex = -127;
+      if (amax > 0.0) {
+        int fe = 0;
+        frexp(amax, &fe); /* amax = m 2^fe, m in [0.5, 1): floor(log2) = fe - 1 */
+        ex = fe - 1 - 2;
+        if (ex < -127) ex = -127;
+        if (ex > 127) ex = 127;
+      }
+      scale[(uint64_t)r * (cols / 32) + b] = (uint8_t)(ex + 127);
+      for (int i = 0; i < 32; i += 2) {
+        const uint8_t lo = synth_f64_to_e2m1(ldexp(v[i], -ex));
+        const uint8_t hi = synth_f64_to_e2m1(ldexp(v[i + 1], -ex));
+        packed[((uint64_t)r * cols + b * 32 + (uint64_t)i) / 2] = (uint8_t)(lo | (hi << 4));
+      }
+    }
   }
 }

@@ -657,3 +657,73 @@ def test_synth_fp8_rows_follow_the_bf16_draws():
     bound = np.maximum(np.abs(v) * 2.0 ** -4, q.scale[:, None] * 2.0 ** -10)
     assert np.all(err <= bound * (1 + 1e-12))
     assert np.array_equal(np.abs(w).max(axis=1), q.scale.astype(np.float64) * 448.0)
+
+
+# ---------------------------------------------------------------------------
+# MXFP4 expert weights (page "Kestrel-MCU notes #13", section 二: 4-bit
+# experts).  The format is OCP MX FP4: E2M1 elements, one E8M0 scale per 32.
+# ---------------------------------------------------------------------------
+
+
+def test_e8m0_decode_matches_torch():
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e8m0fnu).to(torch.float64)
+    ref = ref.numpy()
+    assert np.array_equal(np.isnan(O.E8M0_TABLE), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(O.E8M0_TABLE[ok], ref[ok])
+    assert O.e8m0_value(127) == 1.0 and O.e8m0_value(0) == 2.0 ** -127
+
+
+def test_e2m1_is_the_e4m3_subset():
+    # An E2M1 value with exponent field e > 0 and mantissa bit m is the E4M3
+    # value with exponent field e + 6 (bias 1 -> 7) and mantissa bits m << 2;
+    # the subnormal 0.5 is E4M3 0x30.  torch decodes the E4M3 side.
+    e4 = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    for c in range(16):
+        sign, e, m = (c >> 3) & 1, (c >> 1) & 3, c & 1
+        if e == 0:
+            code8 = (sign << 7) | (0x30 if m else 0x00)
+        else:
+            code8 = (sign << 7) | ((e + 6) << 3) | (m << 2)
+        assert O.e2m1_value(c) == e4[code8], c
+    assert sorted(set(abs(v) for v in O.E2M1_TABLE)) == [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def test_mxfp4_expand_by_hand():
+    # One row of 64: block 0 scale 2^0, block 1 scale 2^-3.  Byte 0 = 0x72:
+    # element 0 = code 2 (1.0), element 1 = code 7 (6.0).
+    packed = np.zeros((1, 32), dtype=np.uint8)
+    packed[0, 0] = 0x72
+    packed[0, 16] = 0x9B      # elements 32, 33: code 0xB (-1.5), code 0x9 (-0.5)
+    m = synth.MxFp4Rows(packed, np.array([[127, 124]], dtype=np.uint8))
+    w = O.expand(m)
+    want = np.zeros((1, 64))
+    want[0, 0], want[0, 1] = 1.0, 6.0
+    want[0, 32], want[0, 33] = -1.5 / 8, -0.5 / 8
+    assert np.array_equal(w, want)
+
+
+def test_synth_e2m1_encoder_brute_force():
+    # Nearest E2M1 value by exhaustive search, ties to the even code.
+    vals = [O.e2m1_value(c) for c in range(8)]
+    rng = np.random.default_rng(9)
+    xs = list(rng.uniform(-7, 7, 3000)) + [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -5.0, 6.0, 9.0]
+    for x in xs:
+        a = min(abs(x), 6.0)
+        best = min(range(8), key=lambda c: (abs(a - vals[c]), c & 1))
+        want = best | (8 if x < 0 else 0)
+        assert synth.f64_to_e2m1(x) == want, x
+
+
+def test_synth_mxfp4_rows_follow_the_bf16_draws():
+    rows, cols, std = 5, 128, 0.05
+    q = synth.normal_mxfp4_rows(3, synth.TID_W_UP, rows, cols, std, start=256)
+    v = synth.normal_f64(3, synth.TID_W_UP, rows * cols, std, start=256).reshape(rows, cols)
+    blk = v.reshape(rows, cols // 32, 32)
+    amax = np.abs(blk).max(axis=-1)
+    assert np.array_equal(q.block_scale.astype(int) - 127, np.floor(np.log2(amax)).astype(int) - 2)
+    w = O.expand(q).reshape(rows, cols // 32, 32)
+    # Elements of [0.5, 4) times the block scale keep 1 mantissa bit: error
+    # <= a quarter of the value's binade step; the top binade saturates at 6.
+    sc = 2.0 ** (q.block_scale.astype(int) - 127)
+    assert np.all(np.abs(w - blk) <= np.maximum(np.abs(blk) / 4, 0.25 * sc[..., None]) + 1e-15)
