@@ -35,6 +35,8 @@ def parse():
                    help="second workload reported beside the main one ('' to skip)")
     p.add_argument("--fp8-decode-workload", default="mixtral_decode_t32_fp8",
                    help="the decode workload with FP8 E4M3 expert weights ('' to skip)")
+    p.add_argument("--mxfp4-decode-workload", default="mixtral_decode_t32_mxfp4",
+                   help="the decode workload with MXFP4 expert weights ('' to skip)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-tokens", type=int, default=384)
     p.add_argument("--copy-calibration", action="store_true",
@@ -48,13 +50,15 @@ def algorithmic(cfg, counts_kept):
     bytes of the selected experts' weights (each touched expert read once)."""
     R = int(sum(counts_kept))
     xw = cfg.x_width
-    wb = {"bf16": 2, "f32": 4, "fp8": 1}[cfg.w_dtype]
-    sb = 4 if cfg.w_dtype == "fp8" else 0      # fp32 scale per weight row
+    # bytes per weight, and scale bytes per weight row of K elements
+    wb = {"bf16": 2, "f32": 4, "fp8": 1, "mxfp4": 0.5}[cfg.w_dtype]
+    def sb(K):
+        return {"fp8": 4, "mxfp4": K // 32}.get(cfg.w_dtype, 0)
     gu_flops = 2.0 * R * xw * 2 * cfg.h
     down_flops = 2.0 * R * cfg.h * xw
     touched = sum(1 for c in counts_kept if c > 0)
-    gu_bytes = touched * 2 * cfg.h * (xw * wb + sb)
-    down_bytes = touched * xw * (cfg.h * wb + sb)
+    gu_bytes = touched * 2 * cfg.h * (xw * wb + sb(xw))
+    down_bytes = touched * xw * (cfg.h * wb + sb(cfg.h))
     return {"rows": R, "gu_flops": gu_flops, "down_flops": down_flops, "gu_bytes": gu_bytes,
             "down_bytes": down_bytes, "touched": touched}
 
@@ -218,7 +222,8 @@ def main():
     if cfg.act_dtype != "bf16":
         kernel = "simt_gu_kernel (fp32 expert gate/up)"
     elif cfg.T <= 64:
-        kernel = f"decode_kernel<true, 2, {str(cfg.w_dtype == 'fp8').lower()}> (expert gate/up)"
+        wf = {"bf16": 0, "fp8": 1, "mxfp4": 2}[cfg.w_dtype]
+        kernel = f"decode_kernel<true, 2, {wf}> (expert gate/up)"
     else:
         kernel = (f"grouped_gemm_kernel<EP_GLU, {tile_rows(cfg)}"
                   f"{', true' if cfg.w_dtype == 'fp8' else ''}> (expert gate/up)")
@@ -250,7 +255,8 @@ def main():
     }
     if "quantile_balancing" in r:
         line["quantile_balancing"] = r["quantile_balancing"]
-    for key, name in (("decode", args.decode_workload), ("decode_fp8", args.fp8_decode_workload)):
+    for key, name in (("decode", args.decode_workload), ("decode_fp8", args.fp8_decode_workload),
+                      ("decode_mxfp4", args.mxfp4_decode_workload)):
         if not name:
             continue
         dc = C.ALL[name]

@@ -63,9 +63,17 @@ typedef enum {
 /* MOE_FP8_E4M3: OCP FP8 E4M3 codes (1 sign, 4 exponent bits with bias 7, 3
    mantissa bits; no infinities, S.1111.111 is NaN; largest finite 448, the
    bound page "Stable LatentMoE interactive demo" quotes in its SiTU-GLU
-   passage), with one fp32 scale per weight row.  Only for the routed
-   experts' weights (w_dtype) under bf16 activations. */
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype_t;
+   passage), with one fp32 scale per weight row.
+   MOE_MXFP4: OCP MX FP4 (the 4-bit experts of page "Kestrel-MCU notes #13",
+   section 二, in the OCP microscaling form): E2M1 codes (1 sign, 2 exponent
+   bits with bias 1, 1 mantissa bit: +-0, 0.5, 1, 1.5, 2, 3, 4, 6) packed two
+   per byte, element 2i of a row in the low nibble of byte i, and one E8M0
+   scale byte (2^(s - 127), 0xFF NaN) per 32 consecutive elements of a row.
+   Both only for the routed experts' weights (w_dtype) under bf16
+   activations; MXFP4 only on the decode path (T <= 64), with each
+   contraction width (the expert input width and h) below 2048 or a multiple
+   of 512 (MOE_ERR_UNSUPPORTED otherwise). */
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2, MOE_MXFP4 = 3 } moe_dtype_t;
 
 /* Combine weight of a selected expert (page "MoE: how sparse activation
    saves compute", section 3.2: Mixtral renormalises over S_t; Switch top-1
@@ -109,16 +117,20 @@ typedef struct moe_desc {
    selection_bias [N] fp32, nullable: the router picks the top-k of z + b
    (Quantile Balancing bias, see moe_qb_update) while the combine weights
    still come from the unbiased softmax; null = no bias.
-   gate_scale, up_scale [N, h] and down_scale [N, w] fp32 (w = d, or l for
-   the latent layer): with w_dtype MOE_FP8_E4M3 all three are required and
-   W_gate / W_up / W_down hold E4M3 codes (uint8, same shapes), weight row r
-   of expert i being scale[i, r] times its codes' values; with any other
-   w_dtype all three must be null. */
+   Scales (w = d, or l for the latent layer):
+   - w_dtype MOE_FP8_E4M3: W_gate / W_up / W_down hold E4M3 codes (uint8,
+     same shapes) and gate_scale, up_scale [N, h], down_scale [N, w] are fp32:
+     weight row r of expert i is scale[i, r] times its codes' values;
+   - w_dtype MOE_MXFP4: W_gate, W_up [N, h, w/2] and W_down [N, w, h/2] hold
+     packed E2M1 codes and gate_scale, up_scale [N, h, w/32], down_scale
+     [N, w, h/32] are E8M0 bytes (uint8), one per 32 elements of a row;
+   - any other w_dtype: all three must be null.
+   With fp8 or MXFP4 all three are required. */
 typedef struct moe_weights {
   const void *W_route, *W_gate, *W_up, *W_down;
   const void *W_ldown, *W_lup, *Ws_gate, *Ws_up, *Ws_down;
   const float *selection_bias;
-  const float *gate_scale, *up_scale, *down_scale;
+  const void *gate_scale, *up_scale, *down_scale;
 } moe_weights_t;
 
 /* Optional outputs of moe_forward (device pointers; each may be null, the
@@ -215,16 +227,16 @@ moe_status_t moe_expert_ffn(const moe_desc_t *desc, const void *x, const int32_t
                             const void *W_gate, const void *W_up, const void *W_down,
                             float *y_perm, void *ws, size_t ws_bytes, moe_stream_t stream);
 
-/* moe_expert_ffn with per-row weight scales (the same computation, with
-   W_gate, W_up, W_down expanded as described at moe_weights_t):
-     gate_scale, up_scale [N, h]; down_scale [N, w]  fp32 device pointers,
-     all three required when w_dtype is MOE_FP8_E4M3, all three null
-     otherwise (MOE_ERR_ARG if not). */
+/* moe_expert_ffn with weight scales (the same computation, with W_gate,
+   W_up, W_down expanded as described at moe_weights_t):
+     gate_scale, up_scale, down_scale  device pointers in the layout
+     moe_weights_t gives for w_dtype, all three required for MOE_FP8_E4M3
+     and MOE_MXFP4, all three null otherwise (MOE_ERR_ARG if not). */
 moe_status_t moe_expert_ffn_scaled(const moe_desc_t *desc, const void *x, const int32_t *perm,
                                    const int32_t *offsets, const int32_t *kept_offsets,
                                    const void *W_gate, const void *W_up, const void *W_down,
-                                   const float *gate_scale, const float *up_scale,
-                                   const float *down_scale, float *y_perm, void *ws,
+                                   const void *gate_scale, const void *up_scale,
+                                   const void *down_scale, float *y_perm, void *ws,
                                    size_t ws_bytes, moe_stream_t stream);
 
 /* Combine (section 3.2 eq. for y): y_t = sum_s [row_of[t*k+s] >= 0]

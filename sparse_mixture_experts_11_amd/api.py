@@ -15,7 +15,7 @@ import torch
 from . import _lib as L
 from ._lib import MoeDesc, MoeOutputs, MoeWeights  # noqa: F401
 
-_DT = {"f32": L.MOE_F32, "bf16": L.MOE_BF16, "fp8": L.MOE_FP8_E4M3}
+_DT = {"f32": L.MOE_F32, "bf16": L.MOE_BF16, "fp8": L.MOE_FP8_E4M3, "mxfp4": L.MOE_MXFP4}
 _GATE = {"renorm": L.MOE_GATE_RENORM, "prob": L.MOE_GATE_PROB}
 _ACT = {"swiglu": L.MOE_ACT_SWIGLU, "situ": L.MOE_ACT_SITU_GLU}
 

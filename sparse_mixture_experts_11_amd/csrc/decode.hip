@@ -19,7 +19,9 @@
 // FP8 weights (E4M3 codes, one fp32 scale per weight row) use 256-byte row
 // windows, 256 k; the operands are widened to bf16 exactly after the LDS
 // read, and the row scales multiply the fp32 sums after the split-K
-// reduction.
+// reduction.  MXFP4 weights (E2M1 codes two a byte, one E8M0 scale per 32 k)
+// use 256-byte windows of 512 k; each k-step's operand is 4 bytes, widened
+// with its block scale folded in (v_cvt_scalef32_pk_bf16_fp4, exact).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -30,26 +32,52 @@ namespace {
 constexpr int NRB = 2;          // 16-row weight blocks per wave (token fragments reused NRB x)
 constexpr int RB = 16 * NRB;    // weight rows per workgroup
 constexpr int kWaves = 4;       // split-K ways
+// Weight formats.
+constexpr int WF_BF16 = WFMT_BF16;   // bf16
+constexpr int WF_FP8 = WFMT_FP8;     // E4M3, fp32 scale per weight row
+constexpr int WF_MX4 = WFMT_MXFP4;   // MXFP4: E2M1 pairs, E8M0 scale per 32 k
+// Bytes of one weight row per 32-k step.
+template <int WF>
+constexpr int kstep_bytes() { return WF == WF_BF16 ? 64 : (WF == WF_FP8 ? 32 : 16); }
 // k-steps of 32 per iteration.  bf16: 16 KiB of weights per wave per
 // iteration (GLU: 2 matrices x 32 rows x 256 B, U = 4; down: 32 rows x
-// 512 B, U = 8).  fp8: 256-byte row windows for both (U = 8): GLU streams
-// 16 KiB, down 8 KiB, which keeps it at two workgroups per CU (a 512-byte
-// window's operand registers push it past 256 VGPRs; measured 0.13 vs
-// 0.10 ms at the Mixtral decode shape).
-template <bool GLU, bool FP8>
-constexpr int unroll_of() { return FP8 ? 8 : (GLU ? 4 : 8); }
+// 512 B, U = 8).  fp8 and MXFP4: 256-byte row windows for both (U = 8 and
+// 16): GLU streams 16 KiB, down 8 KiB, which keeps it at two workgroups per
+// CU (a 512-byte fp8 window's operand registers push it past 256 VGPRs;
+// measured 0.13 vs 0.10 ms at the Mixtral decode shape).
+template <bool GLU, int WF>
+constexpr int unroll_of() { return WF == WF_BF16 ? (GLU ? 4 : 8) : 256 / kstep_bytes<WF>(); }
 
-template <bool GLU, int TG, bool FP8>
+// An E8M0 scale byte as the f32 2^(s - 127) (0: 2^-127, 0xFF: NaN).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
+  return __uint_as_float(s == 0 ? 0x00400000u : (s == 0xFF ? 0x7FC00000u : s << 23));
+}
+
+// Eight E2M1 codes (4 bytes, element 2i in the low nibble of byte i) times
+// 2^(s - 127) -> the bf16x8 MFMA operand (exact while in the bf16 range).
+__device__ __forceinline__ bf16x8 e2m1x8_to_bf16x8(uint32_t raw, float scale) {
+  const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(raw, scale, 0);
+  const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(raw, scale, 1);
+  const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(raw, scale, 2);
+  const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(raw, scale, 3);
+  return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// S1, S2: fp32 row scales [N][wrows] (WF_FP8) or E8M0 block scales
+// [N][wrows][K/32] (WF_MX4).
+template <bool GLU, int TG, int WF>
 __global__ __launch_bounds__(256) void decode_kernel(
     const uint16_t *__restrict__ x, int64_t ldx, const int32_t *__restrict__ perm,
     const int32_t *__restrict__ offsets, const int32_t *__restrict__ kept_offsets, int kslots,
-    const void *__restrict__ W1, const void *__restrict__ W2, const float *__restrict__ S1,
-    const float *__restrict__ S2, int64_t wrows, int K, int act, float bg, float bu,
+    const void *__restrict__ W1, const void *__restrict__ W2, const void *__restrict__ S1,
+    const void *__restrict__ S2, int64_t wrows, int K, int act, float bg, float bu,
     void *__restrict__ out, int64_t ldo) {
+  constexpr bool FP8 = WF == WF_FP8;
+  constexpr bool MX4 = WF == WF_MX4;
   constexpr int NM = GLU ? 2 : 1;
-  constexpr int ES = FP8 ? 1 : 2;         // bytes per weight
-  constexpr int U = unroll_of<GLU, FP8>();
-  constexpr int kPitch = U * 32 * ES;     // bytes of one row's window in a slice
+  constexpr int KSB = kstep_bytes<WF>();  // bytes per row per 32-k step
+  constexpr int U = unroll_of<GLU, WF>();
+  constexpr int kPitch = U * KSB;         // bytes of one row's window in a slice
   constexpr int kLoads = kPitch / 32;     // 1 KiB load instructions per matrix
   constexpr int kSlice = NM * RB * kPitch;  // per-wave LDS slice: one iteration's weights
   static_assert(kPitch >= 256, "the chunk swizzle XORs with 4 row bits: 16 chunks a row");
@@ -69,20 +97,30 @@ __global__ __launch_bounds__(256) void decode_kernel(
   const int Kw = K / kWaves;
   const int kb = wave * Kw;
 
-  const int64_t rowK = (int64_t)K * ES;  // bytes of one weight row
+  // Byte offset of element k of a weight row (k a multiple of 8).
+  auto kbytes = [](int64_t k) -> int64_t { return k * KSB / 32; };
+  const int64_t rowK = kbytes(K);  // bytes of one weight row
   const char *w1 = static_cast<const char *>(W1) + ((int64_t)e * wrows + row0 + li) * rowK +
-                   (int64_t)(kb + kq) * ES;
+                   kbytes(kb + kq);
   const char *w2 = GLU ? static_cast<const char *>(W2) + ((int64_t)e * wrows + row0 + li) * rowK +
-                             (int64_t)(kb + kq) * ES
+                             kbytes(kb + kq)
                        : nullptr;
+  // MXFP4 block scales of this lane's row (row0 + li; + 16 for block 1).
+  const int KB = K / 32;
+  const uint8_t *sb1 = MX4 ? static_cast<const uint8_t *>(S1) +
+                                 ((int64_t)e * wrows + row0 + li) * KB + kb / 32
+                           : nullptr;
+  const uint8_t *sb2 = (MX4 && GLU) ? static_cast<const uint8_t *>(S2) +
+                                          ((int64_t)e * wrows + row0 + li) * KB + kb / 32
+                                    : nullptr;
   const int64_t rbs = 16 * rowK;  // next 16-row block
   // Whole-line loads: instruction i takes rows 8*(i%4) + lane/8 and the
   // 128-byte piece i/4 of the iteration's window; lane%8 picks 16 bytes.
   const int lr = lane >> 3, lc = lane & 7;
   const char *g1 = static_cast<const char *>(W1) + ((int64_t)e * wrows + row0 + lr) * rowK +
-                   (int64_t)kb * ES + 16 * lc;
+                   kbytes(kb) + 16 * lc;
   const char *g2 = GLU ? static_cast<const char *>(W2) + ((int64_t)e * wrows + row0 + lr) * rowK +
-                             (int64_t)kb * ES + 16 * lc
+                             kbytes(kb) + 16 * lc
                        : nullptr;
   char *slice = smem + wave * kSlice;
   const uint16_t *xr[TG];
@@ -107,10 +145,15 @@ __global__ __launch_bounds__(256) void decode_kernel(
       for (int tg = 0; tg < TG; ++tg) acc[m][r][tg] = f32x4{0.f, 0.f, 0.f, 0.f};
   const bf16x8 zero = {};
   // One MFMA operand (8 weights of row r, k-step u, this lane's k quarter)
-  // from the slice: 16 bytes of bf16, or 8 bytes of fp8 widened to bf16.
-  auto slice_frag = [&](int m, int r, int u) -> bf16x8 {
+  // from the slice: 16 bytes of bf16, 8 bytes of fp8 or 4 bytes of MXFP4
+  // (with its block scale sc) widened to bf16.
+  auto slice_frag = [&](int m, int r, int u, float sc) -> bf16x8 {
     const char *row = slice + m * RB * kPitch + r * kPitch;
-    if constexpr (FP8) {
+    if constexpr (MX4) {
+      const uint32_t raw =
+          *reinterpret_cast<const uint32_t *>(row + ((u ^ li) << 4) + 4 * (lane >> 4));
+      return e2m1x8_to_bf16x8(raw, sc);
+    } else if constexpr (FP8) {
       const int q = lane >> 4;
       const int c = 2 * u + (q >> 1);
       const uint2 raw = *reinterpret_cast<const uint2 *>(row + ((c ^ li) << 4) + 8 * (q & 1));
@@ -120,8 +163,10 @@ __global__ __launch_bounds__(256) void decode_kernel(
       return *reinterpret_cast<const bf16x8 *>(row + ((c ^ li) << 4));
     }
   };
-  auto global_frag = [&](const char *w, int64_t byte_off) -> bf16x8 {
-    if constexpr (FP8) {
+  auto global_frag = [&](const char *w, int64_t byte_off, float sc) -> bf16x8 {
+    if constexpr (MX4) {
+      return e2m1x8_to_bf16x8(*reinterpret_cast<const uint32_t *>(w + byte_off), sc);
+    } else if constexpr (FP8) {
       const uint2 raw = *reinterpret_cast<const uint2 *>(w + byte_off);
       return e4m3x8_to_bf16x8(raw.x, raw.y);
     } else {
@@ -131,19 +176,25 @@ __global__ __launch_bounds__(256) void decode_kernel(
   int k = 0;
   for (; k + 32 * U <= Kw; k += 32 * U) {
     u32x4 v[NM][kLoads];
-    bf16x8 b[TG][U];
+    // Token fragments of the whole window up front (MXFP4: per k-step in its
+    // loop below, 16 k-steps of them would not fit beside the loads).
+    constexpr int UB = MX4 ? 1 : U;
+    bf16x8 b[TG][UB];
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
-      const int64_t off = (int64_t)(8 * (i % 4)) * rowK + 128 * (i / 4) + (int64_t)k * ES;
+      const int64_t off = (int64_t)(8 * (i % 4)) * rowK + 128 * (i / 4) + kbytes(k);
       v[0][i] = *reinterpret_cast<const u32x4 *>(g1 + off);
       if (GLU) v[NM - 1][i] = *reinterpret_cast<const u32x4 *>(g2 + off);
     }
+    if constexpr (!MX4) {
 #pragma unroll
-    for (int tg = 0; tg < TG; ++tg)
+      for (int tg = 0; tg < TG; ++tg)
 #pragma unroll
-      for (int u = 0; u < U; ++u)
-        b[tg][u] = (tg < ngroups && xv[tg]) ? *reinterpret_cast<const bf16x8 *>(xr[tg] + k + 32 * u)
-                                           : zero;
+        for (int u = 0; u < U; ++u)
+          b[tg][u] = (tg < ngroups && xv[tg])
+                         ? *reinterpret_cast<const bf16x8 *>(xr[tg] + k + 32 * u)
+                         : zero;
+    }
     // Into the wave's own slice: row r's 16-byte chunk c sits at chunk c ^ (r & 15).
 #pragma unroll
     for (int m = 0; m < NM; ++m)
@@ -155,7 +206,45 @@ __global__ __launch_bounds__(256) void decode_kernel(
             v[m][i];
       }
     // MFMA operands: lane l takes row 16 rb + l%16, k values 32u + 8(l/16) .. +7.
-    if constexpr (FP8) {
+    if constexpr (MX4) {
+      // The window's 16 block scales of each of the lane's rows (4-byte
+      // aligned: K % 512 == 0 whenever this loop runs).
+      uint32_t sw[NM][NRB][4];
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            sw[m][rb][j] = *reinterpret_cast<const uint32_t *>(
+                (m == 0 ? sb1 : sb2) + (int64_t)rb * 16 * KB + k / 32 + 4 * j);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+#pragma unroll
+        for (int tg = 0; tg < TG; ++tg)
+          b[tg][0] = (tg < ngroups && xv[tg])
+                         ? *reinterpret_cast<const bf16x8 *>(xr[tg] + k + 32 * u)
+                         : zero;
+        bf16x8 a[NM][NRB];
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+          for (int rb = 0; rb < NRB; ++rb)
+            a[m][rb] = slice_frag(m, 16 * rb + li, u,
+                                  e8m0_to_f32((sw[m][rb][u >> 2] >> (8 * (u & 3))) & 0xFF));
+#pragma unroll
+        for (int tg = 0; tg < TG; ++tg) {
+          if (tg < ngroups) {
+#pragma unroll
+            for (int m = 0; m < NM; ++m)
+#pragma unroll
+              for (int r = 0; r < NRB; ++r)
+                acc[m][r][tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[m][r], b[tg][0],
+                                                                       acc[m][r][tg], 0, 0, 0);
+          }
+        }
+      }
+    } else if constexpr (FP8) {
       // Widened operands of one k-step at a time (all U would not fit
       // beside the loads in flight).
 #pragma unroll
@@ -164,7 +253,7 @@ __global__ __launch_bounds__(256) void decode_kernel(
 #pragma unroll
         for (int m = 0; m < NM; ++m)
 #pragma unroll
-          for (int rb = 0; rb < NRB; ++rb) a[m][rb] = slice_frag(m, 16 * rb + li, u);
+          for (int rb = 0; rb < NRB; ++rb) a[m][rb] = slice_frag(m, 16 * rb + li, u, 1.f);
 #pragma unroll
         for (int tg = 0; tg < TG; ++tg) {
           if (tg < ngroups) {
@@ -184,7 +273,7 @@ __global__ __launch_bounds__(256) void decode_kernel(
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
-          for (int u = 0; u < U; ++u) a[m][rb][u] = slice_frag(m, 16 * rb + li, u);
+          for (int u = 0; u < U; ++u) a[m][rb][u] = slice_frag(m, 16 * rb + li, u, 1.f);
 #pragma unroll
       for (int tg = 0; tg < TG; ++tg) {
         if (tg < ngroups) {
@@ -204,8 +293,13 @@ __global__ __launch_bounds__(256) void decode_kernel(
     bf16x8 a[NM][NRB];
 #pragma unroll
     for (int r = 0; r < NRB; ++r) {
-      a[0][r] = global_frag(w1, r * rbs + (int64_t)k * ES);
-      if (GLU) a[NM - 1][r] = global_frag(w2, r * rbs + (int64_t)k * ES);
+      float s1 = 1.f, s2 = 1.f;
+      if constexpr (MX4) {
+        s1 = e8m0_to_f32(sb1[(int64_t)r * 16 * KB + k / 32]);
+        if (GLU) s2 = e8m0_to_f32(sb2[(int64_t)r * 16 * KB + k / 32]);
+      }
+      a[0][r] = global_frag(w1, r * rbs + kbytes(k), s1);
+      if (GLU) a[NM - 1][r] = global_frag(w2, r * rbs + kbytes(k), s2);
     }
 #pragma unroll
     for (int tg = 0; tg < TG; ++tg) {
@@ -255,7 +349,7 @@ __global__ __launch_bounds__(256) void decode_kernel(
 #pragma unroll
     for (int r = 0; r < NRB; ++r) {
       if constexpr (FP8) {
-        const float *S = (m == 0) ? S1 : S2;
+        const float *S = static_cast<const float *>((m == 0) ? S1 : S2);
         sc[m][r] = *reinterpret_cast<const f32x4 *>(S + (int64_t)e * wrows + row0 + 16 * r +
                                                     4 * (lane >> 4));
       } else {
@@ -290,15 +384,15 @@ __global__ __launch_bounds__(256) void decode_kernel(
   }
 }
 
-template <bool GLU, bool FP8>
+template <bool GLU, int WF>
 hipError_t launch_decode(int tg, dim3 grid, hipStream_t st, const uint16_t *x, int64_t ldx,
                          const int32_t *perm, const int32_t *offsets, const int32_t *kept_offsets,
-                         int kslots, const void *W1, const void *W2, const float *S1,
-                         const float *S2, int64_t wrows, int K, int act, float bg, float bu,
+                         int kslots, const void *W1, const void *W2, const void *S1,
+                         const void *S2, int64_t wrows, int K, int act, float bg, float bu,
                          void *out, int64_t ldo) {
 #define MOE_DECODE_CASE(TGV)                                                                  \
   case TGV:                                                                                   \
-    hipLaunchKernelGGL((decode_kernel<GLU, TGV, FP8>), grid, dim3(256), 0, st, x, ldx, perm,  \
+    hipLaunchKernelGGL((decode_kernel<GLU, TGV, WF>), grid, dim3(256), 0, st, x, ldx, perm,   \
                        offsets, kept_offsets, kslots, W1, W2, S1, S2, wrows, K, act, bg, bu,  \
                        out, ldo);                                                             \
     break;
@@ -317,30 +411,37 @@ hipError_t launch_decode(int tg, dim3 grid, hipStream_t st, const uint16_t *x, i
 
 hipError_t launch_decode_gu(const uint16_t *x, int64_t T, int w, const int32_t *perm,
                             const int32_t *offsets, const int32_t *kept_offsets, int kslots,
-                            const void *Wg, const void *Wu, const float *sg, const float *su,
-                            int h, int N, int act, float bg, float bu, uint16_t *hid,
+                            const void *Wg, const void *Wu, const void *sg, const void *su,
+                            int wfmt, int h, int N, int act, float bg, float bu, uint16_t *hid,
                             hipStream_t st) {
   const int64_t maxrows = T < kDecodeMaxRows ? T : kDecodeMaxRows;
   const int tg = (int)((maxrows + 15) / 16);
   const dim3 grid(h / RB, N);
-  if (sg != nullptr)
-    return launch_decode<true, true>(tg, grid, st, x, w, perm, offsets, kept_offsets, kslots, Wg,
-                                     Wu, sg, su, h, w, act, bg, bu, hid, h);
-  return launch_decode<true, false>(tg, grid, st, x, w, perm, offsets, kept_offsets, kslots, Wg,
-                                    Wu, nullptr, nullptr, h, w, act, bg, bu, hid, h);
+  if (wfmt == WF_FP8)
+    return launch_decode<true, WF_FP8>(tg, grid, st, x, w, perm, offsets, kept_offsets, kslots,
+                                       Wg, Wu, sg, su, h, w, act, bg, bu, hid, h);
+  if (wfmt == WF_MX4)
+    return launch_decode<true, WF_MX4>(tg, grid, st, x, w, perm, offsets, kept_offsets, kslots,
+                                       Wg, Wu, sg, su, h, w, act, bg, bu, hid, h);
+  return launch_decode<true, WF_BF16>(tg, grid, st, x, w, perm, offsets, kept_offsets, kslots,
+                                      Wg, Wu, nullptr, nullptr, h, w, act, bg, bu, hid, h);
 }
 
 hipError_t launch_decode_down(const uint16_t *hid, int64_t T, const int32_t *kept_offsets,
-                              const void *Wd, const float *sd, int h, int w, int N,
+                              const void *Wd, const void *sd, int wfmt, int h, int w, int N,
                               float *y_perm, hipStream_t st) {
   const int64_t maxrows = T < kDecodeMaxRows ? T : kDecodeMaxRows;
   const int tg = (int)((maxrows + 15) / 16);
   const dim3 grid(w / RB, N);
-  if (sd != nullptr)
-    return launch_decode<false, true>(tg, grid, st, hid, h, nullptr, nullptr, kept_offsets, 1,
-                                      Wd, nullptr, sd, nullptr, w, h, 0, 1.f, 1.f, y_perm, w);
-  return launch_decode<false, false>(tg, grid, st, hid, h, nullptr, nullptr, kept_offsets, 1, Wd,
-                                     nullptr, nullptr, nullptr, w, h, 0, 1.f, 1.f, y_perm, w);
+  if (wfmt == WF_FP8)
+    return launch_decode<false, WF_FP8>(tg, grid, st, hid, h, nullptr, nullptr, kept_offsets, 1,
+                                        Wd, nullptr, sd, nullptr, w, h, 0, 1.f, 1.f, y_perm, w);
+  if (wfmt == WF_MX4)
+    return launch_decode<false, WF_MX4>(tg, grid, st, hid, h, nullptr, nullptr, kept_offsets, 1,
+                                        Wd, nullptr, sd, nullptr, w, h, 0, 1.f, 1.f, y_perm, w);
+  return launch_decode<false, WF_BF16>(tg, grid, st, hid, h, nullptr, nullptr, kept_offsets, 1,
+                                       Wd, nullptr, nullptr, nullptr, w, h, 0, 1.f, 1.f, y_perm,
+                                       w);
 }
 
 }  // namespace moe

@@ -91,15 +91,17 @@ hipError_t launch_qb_update(const float *logits, int64_t T, int N, int k, const 
 // ---- decode-sized experts (decode.hip) -------------------------------------
 // Max rows per expert the decode kernels take.
 constexpr int kDecodeMaxRows = 64;
-// W* are bf16, or E4M3 codes when the row scales s* are given (fp32, one
-// per weight row: [N, h] for gate/up, [N, w] for down).
+// Routed-expert weight formats of the decode kernels (wfmt): bf16; E4M3
+// codes with fp32 row scales s* ([N, h] gate/up, [N, w] down); MXFP4 (E2M1
+// codes two a byte) with E8M0 block scales s* ([N, rows, K/32]).
+enum WeightFormat { WFMT_BF16 = 0, WFMT_FP8 = 1, WFMT_MXFP4 = 2 };
 hipError_t launch_decode_gu(const uint16_t *x, int64_t T, int w, const int32_t *perm,
                             const int32_t *offsets, const int32_t *kept_offsets, int kslots,
-                            const void *Wg, const void *Wu, const float *sg, const float *su,
-                            int h, int N, int act, float bg, float bu, uint16_t *hid,
+                            const void *Wg, const void *Wu, const void *sg, const void *su,
+                            int wfmt, int h, int N, int act, float bg, float bu, uint16_t *hid,
                             hipStream_t st);
 hipError_t launch_decode_down(const uint16_t *hid, int64_t T, const int32_t *kept_offsets,
-                              const void *Wd, const float *sd, int h, int w, int N,
+                              const void *Wd, const void *sd, int wfmt, int h, int w, int N,
                               float *y_perm, hipStream_t st);
 
 // ---- fp32 SIMT experts (simt.hip) ------------------------------------------

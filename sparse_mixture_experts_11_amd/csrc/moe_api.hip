@@ -45,8 +45,23 @@ bool is_latent(const moe_desc_t &d) { return d.l > 0; }
 int xwidth(const moe_desc_t &d) { return is_latent(d) ? d.l : d.d; }
 bool bf16_path(const moe_desc_t &d) { return d.act_dtype == MOE_BF16; }
 bool decode_path(const moe_desc_t &d) { return bf16_path(d) && d.T <= kDecodeMaxRows; }
+// MXFP4 expert weights run on the decode kernels only (T <= 64 tokens), and
+// their 4-byte block-scale loads need each contraction width (the expert
+// input width and h) below one 2048-wide window set or a multiple of 512.
+bool mxfp4_ok(const moe_desc_t &d) {
+  if (d.w_dtype != MOE_MXFP4) return true;
+  const int w = d.l > 0 ? d.l : d.d;
+  auto width_ok = [](int k) { return k < 2048 || k % 512 == 0; };
+  return decode_path(d) && width_ok(w) && width_ok(d.h);
+}
 bool router_gemm(const moe_desc_t &d) { return d.N > kRouteWaveMaxN; }
 bool fp8_experts(const moe_desc_t &d) { return d.w_dtype == MOE_FP8_E4M3; }
+bool mxfp4_experts(const moe_desc_t &d) { return d.w_dtype == MOE_MXFP4; }
+// Routed-expert weights that come with scales.
+bool scaled_experts(const moe_desc_t &d) { return fp8_experts(d) || mxfp4_experts(d); }
+int weight_format(const moe_desc_t &d) {
+  return fp8_experts(d) ? WFMT_FP8 : (mxfp4_experts(d) ? WFMT_MXFP4 : WFMT_BF16);
+}
 
 Layout layout(const moe_desc_t &d) {
   Layout L;
@@ -107,7 +122,8 @@ moe_status_t validate(const moe_desc_t *dp) {
       d.k > kMaxK || d.capacity < -1)
     return MOE_ERR_ARG;
   if ((d.act_dtype != MOE_F32 && d.act_dtype != MOE_BF16) ||
-      (d.w_dtype != MOE_F32 && d.w_dtype != MOE_BF16 && d.w_dtype != MOE_FP8_E4M3) ||
+      (d.w_dtype != MOE_F32 && d.w_dtype != MOE_BF16 && d.w_dtype != MOE_FP8_E4M3 &&
+       d.w_dtype != MOE_MXFP4) ||
       (d.router_dtype != MOE_F32 && d.router_dtype != MOE_BF16))
     return MOE_ERR_ARG;
   if ((d.gate != MOE_GATE_RENORM && d.gate != MOE_GATE_PROB) ||
@@ -123,8 +139,8 @@ moe_status_t validate(const moe_desc_t *dp) {
   if (d.T * (int64_t)d.k > (int64_t)INT32_MAX) return MOE_ERR_UNSUPPORTED;
 
   // What the kernels implement (no fallback path).
-  // Expert weights in the activation dtype, or fp8 E4M3 under bf16 activations.
-  if (d.act_dtype != d.w_dtype && !(fp8_experts(d) && d.act_dtype == MOE_BF16))
+  // Expert weights in the activation dtype, or fp8 / MXFP4 under bf16 activations.
+  if (d.act_dtype != d.w_dtype && !(scaled_experts(d) && d.act_dtype == MOE_BF16))
     return MOE_ERR_UNSUPPORTED;
   if (d.d % 8 != 0) return MOE_ERR_UNSUPPORTED;
   if (d.act_dtype == MOE_F32) {
@@ -236,10 +252,10 @@ hipError_t do_tile_prefix(const moe_desc_t &d, const Layout &L, const int32_t *k
                             st);
 }
 
-// sg, su, sd: fp8 row scales (null for bf16 / fp32 weights).
+// sg, su, sd: fp8 row scales or MXFP4 block scales (null for bf16 / fp32).
 hipError_t do_ffn_gate_up(const moe_desc_t &d, const Layout &L, const void *x, const int32_t *perm,
                           const int32_t *offsets, const int32_t *kept_offsets, const void *Wg,
-                          const void *Wu, const float *sg, const float *su, void *ws,
+                          const void *Wu, const void *sg, const void *su, void *ws,
                           hipStream_t st) {
   const int w = xwidth(d);
   if (!bf16_path(d))
@@ -248,16 +264,16 @@ hipError_t do_ffn_gate_up(const moe_desc_t &d, const Layout &L, const void *x, c
                           d.N, d.act, d.beta_g, d.beta_u, region<float>(ws, L.hid), st);
   if (decode_path(d))
     return launch_decode_gu(static_cast<const uint16_t *>(x), d.T, w, perm, offsets, kept_offsets,
-                            d.k, Wg, Wu, sg, su, d.h, d.N, d.act, d.beta_g, d.beta_u,
-                            region<uint16_t>(ws, L.hid), st);
+                            d.k, Wg, Wu, sg, su, weight_format(d), d.h, d.N, d.act, d.beta_g,
+                            d.beta_u, region<uint16_t>(ws, L.hid), st);
   GemmArgs a;
   memset(&a, 0, sizeof(a));
   a.A = static_cast<const uint16_t *>(x);
   a.lda = w;
   a.B = Wg;
   a.B2 = Wu;
-  a.bscale = sg;
-  a.bscale2 = su;
+  a.bscale = static_cast<const float *>(sg);
+  a.bscale2 = static_cast<const float *>(su);
   a.strideB = (int64_t)d.h * w;
   a.K = w;
   a.ncols = d.h;
@@ -278,20 +294,20 @@ hipError_t do_ffn_gate_up(const moe_desc_t &d, const Layout &L, const void *x, c
 }
 
 hipError_t do_ffn_down(const moe_desc_t &d, const Layout &L, const int32_t *kept_offsets,
-                       const void *Wd, const float *sd, float *y_perm, void *ws, hipStream_t st) {
+                       const void *Wd, const void *sd, float *y_perm, void *ws, hipStream_t st) {
   const int w = xwidth(d);
   if (!bf16_path(d))
     return launch_simt_down(region<float>(ws, L.hid), kept_offsets,
                             static_cast<const float *>(Wd), d.h, w, d.N, y_perm, st);
   if (decode_path(d))
-    return launch_decode_down(region<uint16_t>(ws, L.hid), d.T, kept_offsets, Wd, sd, d.h, w,
-                              d.N, y_perm, st);
+    return launch_decode_down(region<uint16_t>(ws, L.hid), d.T, kept_offsets, Wd, sd,
+                              weight_format(d), d.h, w, d.N, y_perm, st);
   GemmArgs a;
   memset(&a, 0, sizeof(a));
   a.A = region<uint16_t>(ws, L.hid);
   a.lda = d.h;
   a.B = Wd;
-  a.bscale = sd;
+  a.bscale = static_cast<const float *>(sd);
   a.strideB = (int64_t)w * d.h;
   a.K = d.h;
   a.ncols = w;
@@ -365,10 +381,11 @@ moe_status_t forward_impl(const moe_desc_t *desc, const moe_weights_t *wts, cons
       wts->W_gate == nullptr || wts->W_up == nullptr || wts->W_down == nullptr)
     return MOE_ERR_ARG;
   if (is_latent(d) && (wts->W_ldown == nullptr || wts->W_lup == nullptr)) return MOE_ERR_ARG;
-  // Row scales: all three with fp8 expert weights, none otherwise.
+  // Scales: all three with fp8 / MXFP4 expert weights, none otherwise.
   const bool any_scale = wts->gate_scale || wts->up_scale || wts->down_scale;
   const bool all_scales = wts->gate_scale && wts->up_scale && wts->down_scale;
-  if (fp8_experts(d) ? !all_scales : any_scale) return MOE_ERR_ARG;
+  if (scaled_experts(d) ? !all_scales : any_scale) return MOE_ERR_ARG;
+  if (!mxfp4_ok(d)) return MOE_ERR_UNSUPPORTED;
   if (is_latent(d) && d.n_shared > 0 &&
       (wts->Ws_gate == nullptr || wts->Ws_up == nullptr || wts->Ws_down == nullptr))
     return MOE_ERR_ARG;
@@ -558,8 +575,8 @@ moe_status_t moe_dispatch(const moe_desc_t *desc, const int32_t *topk_idx, int32
 moe_status_t moe_expert_ffn_scaled(const moe_desc_t *desc, const void *x, const int32_t *perm,
                                    const int32_t *offsets, const int32_t *kept_offsets,
                                    const void *W_gate, const void *W_up, const void *W_down,
-                                   const float *gate_scale, const float *up_scale,
-                                   const float *down_scale, float *y_perm, void *ws,
+                                   const void *gate_scale, const void *up_scale,
+                                   const void *down_scale, float *y_perm, void *ws,
                                    size_t ws_bytes, moe_stream_t stream) {
   const moe_status_t v = validate(desc);
   if (v != MOE_OK) return v;
@@ -568,7 +585,8 @@ moe_status_t moe_expert_ffn_scaled(const moe_desc_t *desc, const void *x, const 
     return MOE_ERR_ARG;
   const bool any_scale = gate_scale || up_scale || down_scale;
   const bool all_scales = gate_scale && up_scale && down_scale;
-  if (fp8_experts(*desc) ? !all_scales : any_scale) return MOE_ERR_ARG;
+  if (scaled_experts(*desc) ? !all_scales : any_scale) return MOE_ERR_ARG;
+  if (!mxfp4_ok(*desc)) return MOE_ERR_UNSUPPORTED;
   const Layout L = layout(*desc);
   if (ws == nullptr || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   const hipStream_t st = reinterpret_cast<hipStream_t>(stream);

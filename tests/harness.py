@@ -102,11 +102,33 @@ def upload_stacked_fp8(cfg: C.Layer, which: str, device="cuda"):
     return codes, scale
 
 
+def upload_stacked_mxfp4(cfg: C.Layer, which: str, device="cuda"):
+    """MXFP4 routed-expert tensor on the device: (packed E2M1 codes uint8
+    [N, rows, cols/2], E8M0 scale bytes [N, rows, cols/32])."""
+    xw, h, N = cfg.x_width, cfg.h, cfg.N
+    rows, cols = (h, xw) if which in ("gate", "up") else (xw, h)
+    import synth as S
+    tid, std = {"gate": (S.TID_W_GATE, 1 / math.sqrt(xw)), "up": (S.TID_W_UP, 1 / math.sqrt(xw)),
+                "down": (S.TID_W_DOWN, 1 / math.sqrt(h))}[which]
+    packed = torch.empty((N, rows, cols // 2), dtype=torch.uint8, device=device)
+    scale = torch.empty((N, rows, cols // 32), dtype=torch.uint8, device=device)
+    step = max(1, min(N, (256 << 20) // (rows * cols // 2)))
+    for e0 in range(0, N, step):
+        n = min(step, N - e0)
+        m = S.normal_mxfp4_rows(cfg.seed, tid, n * rows, cols, std, start=e0 * rows * cols)
+        packed[e0:e0 + n].copy_(torch.from_numpy(m.packed.reshape(n, rows, cols // 2)))
+        scale[e0:e0 + n].copy_(torch.from_numpy(m.block_scale.reshape(n, rows, cols // 32)))
+    return packed, scale
+
+
 def upload_layer(cfg: C.Layer, device="cuda") -> Dict[str, torch.Tensor]:
     w = {"W_route": to_device(cfg.w_route(), device)}
     if cfg.w_dtype == "fp8":
         for name in ("gate", "up", "down"):
             w["W_" + name], w[name + "_scale"] = upload_stacked_fp8(cfg, name, device)
+    elif cfg.w_dtype == "mxfp4":
+        for name in ("gate", "up", "down"):
+            w["W_" + name], w[name + "_scale"] = upload_stacked_mxfp4(cfg, name, device)
     else:
         for name in ("gate", "up", "down"):
             w["W_" + name] = upload_stacked(cfg, name, device)

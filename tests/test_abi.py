@@ -183,7 +183,7 @@ def test_fp8_weights_validate():
     f32 = H.desc_for(C.TINY.with_(w_dtype="fp8"))
     assert call_forward_fp8(f32, ws_bytes=1 << 40) == L.MOE_ERR_UNSUPPORTED
     d3 = H.desc_for(C.MIXTRAL_DECODE_FP8)
-    d3.w_dtype = 3
+    d3.w_dtype = 4
     assert call_forward_fp8(d3) == L.MOE_ERR_ARG
     # The expert stage: the unscaled entry point cannot take fp8 weights.
     big = 1 << 40
@@ -196,3 +196,23 @@ def test_fp8_weights_validate():
                FAKE, big, n) == L.MOE_ERR_ARG
     assert ffn(ctypes.byref(plain), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, n, n, FAKE,
                FAKE, big, n) == L.MOE_ERR_ARG
+
+
+def test_mxfp4_weights_validate():
+    lib = L.load()
+    n = None
+    d = H.desc_for(C.MIXTRAL_DECODE_MXFP4)
+    assert d.w_dtype == L.MOE_MXFP4
+    assert call_forward_fp8(d) == L.MOE_ERR_WORKSPACE
+    assert call_forward_fp8(d, scales=(None, None, None)) == L.MOE_ERR_ARG
+    # Decode kernels only (T <= 64), and 2048-or-wider contraction widths a
+    # multiple of 512.
+    big_t = H.desc_for(C.MIXTRAL_DECODE_MXFP4.with_(T=65))
+    assert call_forward_fp8(big_t, ws_bytes=1 << 40) == L.MOE_ERR_UNSUPPORTED
+    odd = H.desc_for(C.MIXTRAL_DECODE_MXFP4.with_(d=2176))
+    assert call_forward_fp8(odd, ws_bytes=1 << 40) == L.MOE_ERR_UNSUPPORTED
+    ok_small = H.desc_for(C.MIXTRAL_DECODE_MXFP4.with_(d=1152, h=1920))
+    assert call_forward_fp8(ok_small) == L.MOE_ERR_WORKSPACE
+    ffn = lib.moe_expert_ffn_scaled
+    assert ffn(ctypes.byref(big_t), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+               FAKE, FAKE, 1 << 40, n) == L.MOE_ERR_UNSUPPORTED
