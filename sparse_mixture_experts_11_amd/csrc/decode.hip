@@ -176,8 +176,10 @@ __global__ __launch_bounds__(256) void decode_kernel(
   int k = 0;
   for (; k + 32 * U <= Kw; k += 32 * U) {
     u32x4 v[NM][kLoads];
-    // Token fragments of the whole window up front (MXFP4: per k-step in its
-    // loop below, 16 k-steps of them would not fit beside the loads).
+    // Token fragments of the whole window up front (MXFP4: in groups of 4
+    // k-steps in its loop below; 16 k-steps of them would not fit beside
+    // the loads, and one k-step at a time leaves their latency exposed:
+    // 0.253 vs 0.235 ms for the Mixtral T=32 forward).
     constexpr int UB = MX4 ? 1 : U;
     bf16x8 b[TG][UB];
 #pragma unroll
@@ -218,29 +220,42 @@ __global__ __launch_bounds__(256) void decode_kernel(
           for (int j = 0; j < 4; ++j)
             sw[m][rb][j] = *reinterpret_cast<const uint32_t *>(
                 (m == 0 ? sb1 : sb2) + (int64_t)rb * 16 * KB + k / 32 + 4 * j);
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
+      // Token fragments in groups of 4 k-steps, the next group loading
+      // while this one computes.
+      bf16x8 bq[2][TG][4];
+      auto load_group = [&](int grp, bf16x8 (&dst)[TG][4]) {
 #pragma unroll
         for (int tg = 0; tg < TG; ++tg)
-          b[tg][0] = (tg < ngroups && xv[tg])
-                         ? *reinterpret_cast<const bf16x8 *>(xr[tg] + k + 32 * u)
-                         : zero;
-        bf16x8 a[NM][NRB];
 #pragma unroll
-        for (int m = 0; m < NM; ++m)
+          for (int uu = 0; uu < 4; ++uu)
+            dst[tg][uu] = (tg < ngroups && xv[tg])
+                              ? *reinterpret_cast<const bf16x8 *>(xr[tg] + k + 32 * (4 * grp + uu))
+                              : zero;
+      };
+      load_group(0, bq[0]);
 #pragma unroll
-          for (int rb = 0; rb < NRB; ++rb)
-            a[m][rb] = slice_frag(m, 16 * rb + li, u,
-                                  e8m0_to_f32((sw[m][rb][u >> 2] >> (8 * (u & 3))) & 0xFF));
+      for (int grp = 0; grp < U / 4; ++grp) {
+        if (grp + 1 < U / 4) load_group(grp + 1, bq[(grp + 1) & 1]);
 #pragma unroll
-        for (int tg = 0; tg < TG; ++tg) {
-          if (tg < ngroups) {
+        for (int uu = 0; uu < 4; ++uu) {
+          const int u = 4 * grp + uu;
+          bf16x8 a[NM][NRB];
 #pragma unroll
-            for (int m = 0; m < NM; ++m)
+          for (int m = 0; m < NM; ++m)
 #pragma unroll
-              for (int r = 0; r < NRB; ++r)
-                acc[m][r][tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[m][r], b[tg][0],
-                                                                       acc[m][r][tg], 0, 0, 0);
+            for (int rb = 0; rb < NRB; ++rb)
+              a[m][rb] = slice_frag(m, 16 * rb + li, u,
+                                    e8m0_to_f32((sw[m][rb][u >> 2] >> (8 * (u & 3))) & 0xFF));
+#pragma unroll
+          for (int tg = 0; tg < TG; ++tg) {
+            if (tg < ngroups) {
+#pragma unroll
+              for (int m = 0; m < NM; ++m)
+#pragma unroll
+                for (int r = 0; r < NRB; ++r)
+                  acc[m][r][tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                      a[m][r], bq[grp & 1][tg][uu], acc[m][r][tg], 0, 0, 0);
+            }
           }
         }
       }
