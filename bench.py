@@ -38,7 +38,7 @@ def parse():
     p.add_argument("--mxfp4-decode-workload", default="mixtral_decode_t32_mxfp4",
                    help="the decode workload with MXFP4 expert weights ('' to skip)")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-sample-tokens", type=int, default=384)
+    p.add_argument("--cpu-sample-tokens", type=int, default=1536)
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 1 GiB device-to-device copy (3 times) so that "
                         "hardware byte counters can be scaled against a known size")
