@@ -216,3 +216,21 @@ def test_mxfp4_weights_validate():
     ffn = lib.moe_expert_ffn_scaled
     assert ffn(ctypes.byref(big_t), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                FAKE, FAKE, 1 << 40, n) == L.MOE_ERR_UNSUPPORTED
+
+
+def test_header_compiles_as_plain_c(tmp_path):
+    # The boundary is a C ABI: include/moe.h must stand on its own in C99.
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "use_header.c"
+    src.write_text('#include "moe.h"\n'
+                   "int main(void) {\n"
+                   "  moe_desc_t d; moe_weights_t w = {0}; moe_outputs_t o = {0};\n"
+                   "  moe_desc_init(&d); (void)w; (void)o;\n"
+                   "  return (int)MOE_MXFP4 - 3;\n"
+                   "}\n")
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror",
+                    "-I", os.path.join(ROOT, "include"), "-c", str(src), "-o",
+                    str(tmp_path / "use_header.o")], check=True)
