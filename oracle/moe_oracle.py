@@ -51,7 +51,10 @@ Readings where the pages are silent (listed again in the design doc):
     stored row is its scale times each code's exact value;
   * MXFP4 expert weights (the MCU page stores 4-bit experts): OCP MX FP4,
     E2M1 elements in runs of 32 along a row sharing one E8M0 scale, two
-    elements a byte with the even element in the low nibble.
+    elements a byte with the even element in the low nibble;
+  * router backward: the selected sets, the expert outputs and f are held
+    fixed (piecewise-constant or separate steps); the loss is
+    <dy, y> + aux_scale * L_aux.
 
 Pins (tests/test_oracle_pins.py): the capacity example [10,3,2,1] -> drops
 6/4/0; the balanced/collapsed aux example (1.0000 / 2.8449); the parameter
@@ -69,6 +72,10 @@ format's landmarks (448, 2^-9, 2^-6, -0, NaN) and a hand-expanded scaled
 matrix.  MXFP4 pins: E8M0 against torch.float8_e8m0fnu; every E2M1 value
 against torch's decode of the E4M3 code with the same sign, exponent and
 mantissa (E2M1 is a subset of E4M3); a hand-expanded two-block matrix.
+Router backward pins: torch autograd of an independently written forward;
+central differences of the oracle's own loss; the softmax gradient sums to
+zero per token; a balanced f makes the aux gradient vanish; renorm with
+k = N equals the prob gate.
 Parity unpinned: the exact SiTU-GLU form, the LatentMoE wiring and the
 Quantile Balancing readings (score, cutoff, q, bins) are readings, pinned
 only through the limits and invariants above.
@@ -210,6 +217,57 @@ def route(u: np.ndarray, w_route: np.ndarray, k: int, gate: str,
         idx = select_topk(sb, k)
         margin = topk_margin(sb, k)
     return {"z": z, "p": p, "idx": idx, "a": gate_weights(p, idx, gate), "margin": margin}
+
+
+# ---------------------------------------------------------------------------
+# Router backward  (page "MoE: how sparse activation saves compute", §3.2
+# eqs. z, p, a, y and §3.4 eq. L_aux, differentiated)
+# ---------------------------------------------------------------------------
+#
+# For a total loss L = <dy, y> + aux_scale * L_aux, with the selected set S_t
+# and the expert outputs F_i(x_t) held fixed (the selection is piecewise
+# constant in z and the experts' own gradients are a separate step), and f
+# held fixed (an arg-max count), the router's share of the gradient is:
+#   da_{t,s} = dy_t . F_{i_s}(x_t) for kept slots, 0 for dropped ones;
+#   renorm gate a_s = p_s / sum_S p: dp_j = (da_j - sum_s da_s a_s) / sum_S p
+#   for j in S_t (0 elsewhere); prob gate a = p: dp_j = da_j;
+#   L_aux = alpha N sum_i f_i P_i with P_i = mean_t p_{t,i} adds
+#   aux_scale * alpha * N * f_i / T to every dp_{t,i};
+#   softmax: dz_t = p_t * (dp_t - p_t . dp_t);
+#   dW_route = dz^T u and du = dz W_route (the router's part of du).
+
+
+def route_backward(u: np.ndarray, w_route: np.ndarray, idx: np.ndarray, row_of: np.ndarray,
+                   y_rows: np.ndarray, dy: np.ndarray, *, gate: str, f: np.ndarray,
+                   alpha: float, aux_scale: float) -> Dict[str, np.ndarray]:
+    """Router backward, steps as above.  u [T, d], w_route [N, d], idx [T, k],
+    row_of [T*k] (-1 for a dropped slot), y_rows [R, d] the experts' outputs
+    of the kept rows, dy [T, d], f [N] the forward's arg-max shares."""
+    T, d = u.shape
+    N = w_route.shape[0]
+    k = idx.shape[1]
+    z = router_logits(u, w_route)
+    p = softmax(z)
+    da = np.zeros((T, k))
+    for t in range(T):
+        for s in range(k):
+            r = int(row_of[t * k + s])
+            if r >= 0:
+                da[t, s] = float(dy[t] @ y_rows[r])
+    psel = np.take_along_axis(p, idx, axis=1)
+    if gate == "renorm":
+        ssum = psel.sum(axis=1, keepdims=True)
+        a = psel / ssum
+        g = (da - (da * a).sum(axis=1, keepdims=True)) / ssum
+    elif gate == "prob":
+        g = da
+    else:
+        raise ValueError(gate)
+    dp = np.zeros((T, N))
+    np.put_along_axis(dp, idx, g, axis=1)
+    dp = dp + aux_scale * alpha * N * np.asarray(f, dtype=np.float64)[None, :] / T
+    dz = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+    return {"p": p, "da": da, "dp": dp, "dz": dz, "dW_route": dz.T @ u, "du": dz @ w_route}
 
 
 # ---------------------------------------------------------------------------

@@ -727,3 +727,103 @@ def test_synth_mxfp4_rows_follow_the_bf16_draws():
     # <= a quarter of the value's binade step; the top binade saturates at 6.
     sc = 2.0 ** (q.block_scale.astype(int) - 127)
     assert np.all(np.abs(w - blk) <= np.maximum(np.abs(blk) / 4, 0.25 * sc[..., None]) + 1e-15)
+
+
+# ---------------------------------------------------------------------------
+# Router backward (page 3, §3.2 eqs. z, p, a, y and §3.4 eq. L_aux,
+# differentiated with the selection, the expert outputs and f held fixed)
+# ---------------------------------------------------------------------------
+
+
+def _rb_case(seed, T=24, d=16, N=6, k=2, gate="renorm", cap=None):
+    rng = np.random.default_rng(seed)
+    u = rng.standard_normal((T, d))
+    w = rng.standard_normal((N, d)) / math.sqrt(d)
+    r = O.route(u, w, k, gate)
+    disp = O.dispatch(r["idx"], N, cap)
+    R = int(disp["kept_offsets"][-1])
+    y_rows = rng.standard_normal((max(R, 1), d))
+    dy = rng.standard_normal((T, d))
+    f = O.balance_stats(r["p"], 0.01)["f"]
+    return u, w, r, disp, y_rows, dy, f
+
+
+def _rb_loss(u, w, idx, row_of, y_rows, dy, gate, f, alpha, aux_scale):
+    # The forward loss with the selection held at idx: <dy, y> + aux_scale L_aux.
+    p = O.softmax(O.router_logits(u, w))
+    a = O.gate_weights(p, idx, gate)
+    y = O.combine_rows(y_rows, row_of, a)
+    N = w.shape[0]
+    return float(np.sum(dy * y)) + aux_scale * alpha * N * float(np.sum(f * p.mean(axis=0)))
+
+
+@pytest.mark.parametrize("gate,cap", [("renorm", None), ("prob", None), ("renorm", 6)])
+def test_route_backward_matches_torch_autograd(gate, cap):
+    u, w, r, disp, y_rows, dy, f = _rb_case(3, gate=gate, cap=cap)
+    k = r["idx"].shape[1]
+    alpha, lam = 0.01, 3.0
+    g = O.route_backward(u, w, r["idx"], disp["row_of"], y_rows, dy, gate=gate, f=f,
+                         alpha=alpha, aux_scale=lam)
+    # An independent torch forward; autograd differentiates it.
+    ut = torch.tensor(u, requires_grad=True)
+    wt = torch.tensor(w, requires_grad=True)
+    pt = torch.softmax(ut @ wt.T, dim=1)
+    it = torch.tensor(r["idx"])
+    ps = torch.gather(pt, 1, it)
+    at = ps / ps.sum(dim=1, keepdim=True) if gate == "renorm" else ps
+    rows = torch.tensor(disp["row_of"].reshape(-1, k))
+    F = torch.tensor(y_rows)[rows.clamp(min=0)] * (rows >= 0).unsqueeze(-1)
+    y = (at.unsqueeze(-1) * F).sum(dim=1)
+    N = w.shape[0]
+    loss = (torch.tensor(dy) * y).sum() + lam * alpha * N * (torch.tensor(f) * pt.mean(0)).sum()
+    loss.backward()
+    assert np.allclose(g["dW_route"], wt.grad.numpy(), rtol=1e-10, atol=1e-12)
+    assert np.allclose(g["du"], ut.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_route_backward_central_differences():
+    u, w, r, disp, y_rows, dy, f = _rb_case(4)
+    alpha, lam = 0.01, 2.0
+    g = O.route_backward(u, w, r["idx"], disp["row_of"], y_rows, dy, gate="renorm", f=f,
+                         alpha=alpha, aux_scale=lam)
+    assert np.all(r["margin"] > 1e-3)   # steps below cannot change the selection
+    eps = 1e-6
+    for (n, c) in [(0, 0), (2, 5), (5, 15), (3, 7)]:
+        wp, wm = w.copy(), w.copy()
+        wp[n, c] += eps
+        wm[n, c] -= eps
+        num = (_rb_loss(u, wp, r["idx"], disp["row_of"], y_rows, dy, "renorm", f, alpha, lam) -
+               _rb_loss(u, wm, r["idx"], disp["row_of"], y_rows, dy, "renorm", f, alpha, lam)) / (2 * eps)
+        assert abs(num - g["dW_route"][n, c]) <= 1e-6 * max(1.0, abs(num))
+
+
+def test_route_backward_invariants():
+    u, w, r, disp, y_rows, dy, f = _rb_case(5)
+    g = O.route_backward(u, w, r["idx"], disp["row_of"], y_rows, dy, gate="renorm", f=f,
+                         alpha=0.01, aux_scale=1.0)
+    # The softmax gradient sums to zero over the experts of each token.
+    assert np.allclose(g["dz"].sum(axis=1), 0.0, atol=1e-12)
+    # With f perfectly balanced, L_aux = alpha N sum_i P_i / N = alpha is
+    # constant, so the aux term contributes no gradient.
+    N = w.shape[0]
+    zero_dy = np.zeros_like(dy)
+    flat = O.route_backward(u, w, r["idx"], disp["row_of"], y_rows, zero_dy, gate="renorm",
+                            f=np.full(N, 1.0 / N), alpha=0.01, aux_scale=5.0)
+    assert np.abs(flat["dz"]).max() < 1e-15
+    # ... while an unbalanced f pushes the hot expert's logits down.
+    hot = np.zeros(N)
+    hot[0] = 1.0
+    push = O.route_backward(u, w, r["idx"], disp["row_of"], y_rows, zero_dy, gate="renorm",
+                            f=hot, alpha=0.01, aux_scale=5.0)
+    assert np.all(push["dz"][:, 0] > 0)   # gradient ascent direction: descent lowers z_0
+
+
+def test_route_backward_renorm_over_all_experts_is_the_prob_gate():
+    # With k = N, sum_S p = 1, so renorm and prob weights coincide; their
+    # gate gradients differ by a per-token constant that the softmax removes.
+    u, w, r, disp, y_rows, dy, f = _rb_case(6, N=4, k=4)
+    a = O.route_backward(u, w, r["idx"], disp["row_of"], y_rows, dy, gate="renorm", f=f,
+                         alpha=0.01, aux_scale=1.0)
+    b = O.route_backward(u, w, r["idx"], disp["row_of"], y_rows, dy, gate="prob", f=f,
+                         alpha=0.01, aux_scale=1.0)
+    assert np.allclose(a["dz"], b["dz"], rtol=1e-12, atol=1e-14)
