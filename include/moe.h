@@ -141,6 +141,9 @@ typedef struct moe_outputs {
   float *stats;
   int32_t *counts, *offsets, *kept_offsets, *perm, *row_of;
   uint8_t *drop;
+  float *y_perm; /* [sum_i min(L_i, C), w] fp32: the experts' outputs of the
+                    kept rows (what moe_expert_ffn writes; the input of
+                    moe_route_backward) */
 } moe_outputs_t;
 
 /* Sets every field of *desc to the "unset" sentinel. */
@@ -199,6 +202,30 @@ moe_status_t moe_route_biased(const moe_desc_t *desc, const void *u, const void 
 moe_status_t moe_qb_update(const moe_desc_t *desc, const void *u, const void *W_route,
                            const float *bias, int32_t q, int32_t method, float *new_bias,
                            void *ws, size_t ws_bytes, moe_stream_t stream);
+
+/* Router backward (page "MoE: how sparse activation saves compute", §3.2
+   eqs. z, p, a, y and §3.4 eq. L_aux, differentiated): the router's share of
+   the gradient of L = <dy, y> + aux_scale * L_aux, with the selected sets,
+   the expert outputs and the arg-max shares f held fixed.
+     u, W_route        the forward's inputs (bf16)
+     topk_idx, row_of  the forward's selection and row map (moe_outputs_t)
+     stats             the forward's statistics; f = stats[0..N)
+     y_perm            the forward's expert outputs [R, d] fp32
+     dy                [T, d] bf16, the gradient of the loss at y
+     aux_scale         weight of L_aux (alpha is desc->aux_alpha)
+     dz                [T, N] fp32 out: gradient at the router logits
+     dW_route          [N, d] fp32 out
+     du                [T, d] fp32 out: the router's part of the gradient at u
+                       (the experts' part is not computed here)
+   Steps: da = dy_t . F per kept slot; the renorm (or prob) gate backward;
+   the aux term aux_scale alpha N f_i / T on every dp; the softmax backward;
+   dW_route = dz^T u; du = dz W_route.  Plain layers with bf16 activations
+   and router only (MOE_ERR_UNSUPPORTED otherwise). */
+moe_status_t moe_route_backward(const moe_desc_t *desc, const void *u, const void *W_route,
+                                const int32_t *topk_idx, const int32_t *row_of,
+                                const float *stats, const float *y_perm, const void *dy,
+                                float aux_scale, float *dz, float *dW_route, float *du, void *ws,
+                                size_t ws_bytes, moe_stream_t stream);
 
 /* Dispatch: group the T*k (token, slot) entries e = t*k + s by expert in
    token order (sections 3.5, 3.6, 3.8).

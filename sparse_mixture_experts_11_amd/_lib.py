@@ -15,7 +15,8 @@ MOE_ACT_SWIGLU, MOE_ACT_SITU_GLU = 0, 1
 # Every symbol include/moe.h declares.
 EXPORTS = ("moe_desc_init", "moe_status_string", "moe_workspace_bytes",
            "moe_capacity_from_factor", "moe_route", "moe_route_biased", "moe_qb_update",
-           "moe_dispatch", "moe_expert_ffn", "moe_expert_ffn_scaled", "moe_combine",
+           "moe_route_backward", "moe_dispatch", "moe_expert_ffn", "moe_expert_ffn_scaled",
+           "moe_combine",
            "moe_forward", "moe_forward_traced", "moe_stage_name")
 
 
@@ -39,7 +40,7 @@ class MoeWeights(ctypes.Structure):
 class MoeOutputs(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("topk_idx", "topk_w", "stats", "counts",
                                                 "offsets", "kept_offsets", "perm", "row_of",
-                                                "drop")]
+                                                "drop", "y_perm")]
 
 
 class LibraryMissing(RuntimeError):
@@ -74,6 +75,8 @@ def load() -> ctypes.CDLL:
     lib.moe_route_biased.restype = I32
     lib.moe_qb_update.argtypes = [D, P, P, P, I32, I32, P, P, SZ, P]
     lib.moe_qb_update.restype = I32
+    lib.moe_route_backward.argtypes = [D, P, P, P, P, P, P, P, ctypes.c_float, P, P, P, P, SZ, P]
+    lib.moe_route_backward.restype = I32
     lib.moe_dispatch.argtypes = [D, P, P, P, P, P, P, P, P, SZ, P]
     lib.moe_dispatch.restype = I32
     lib.moe_expert_ffn.argtypes = [D, P, P, P, P, P, P, P, P, P, SZ, P]

@@ -113,6 +113,15 @@ def moe_qb_update(desc, u, W_route, bias, new_bias, ws, q=0, method=QB_EXACT,
                                   _stream(stream)), "moe_qb_update")
 
 
+def moe_route_backward(desc, u, W_route, topk_idx, row_of, stats, y_perm, dy, dz, dW_route, du,
+                       ws, aux_scale=1.0, stream=None) -> None:
+    _check(L.load().moe_route_backward(ctypes.byref(desc), _ptr(u), _ptr(W_route),
+                                       _ptr(topk_idx), _ptr(row_of), _ptr(stats), _ptr(y_perm),
+                                       _ptr(dy), float(aux_scale), _ptr(dz), _ptr(dW_route),
+                                       _ptr(du), _ptr(ws), ws.numel(), _stream(stream)),
+           "moe_route_backward")
+
+
 def moe_dispatch(desc, topk_idx, counts, offsets, kept_offsets, perm, row_of, drop, ws,
                  stream=None) -> None:
     _check(L.load().moe_dispatch(ctypes.byref(desc), _ptr(topk_idx), _ptr(counts), _ptr(offsets),

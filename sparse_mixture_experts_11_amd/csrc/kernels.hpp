@@ -88,6 +88,18 @@ hipError_t launch_gemm(const GemmArgs &a, int epi, int64_t mtiles_bound, hipStre
 hipError_t launch_qb_update(const float *logits, int64_t T, int N, int k, const float *bias, int q,
                             int method, float *req, float *new_bias, hipStream_t st);
 
+// ---- router backward (route_bwd.hip) ---------------------------------------
+// dz [T, N] from the logits, the forward's selection (idx, row_of), its
+// expert outputs y_perm [R, d] and dy [T, d] (bf16); then dW_route [N, d]
+// (through fp32 partials part [chunks][N][d]) and the router's du [T, d].
+// aux_coef = aux_scale * alpha * N / T; stats[0..N) holds f.
+int64_t route_bwd_chunks(int64_t T, int N, int d);
+hipError_t launch_route_backward(const float *logits, int64_t T, int N, int k, int d, int renorm,
+                                 const int32_t *idx, const int32_t *row_of, const float *y_perm,
+                                 const uint16_t *dy, const float *stats, float aux_coef,
+                                 const uint16_t *u, const uint16_t *w_route, float *part,
+                                 float *dz, float *dw, float *du, hipStream_t st);
+
 // ---- decode-sized experts (decode.hip) -------------------------------------
 // Max rows per expert the decode kernels take.
 constexpr int kDecodeMaxRows = 64;

@@ -29,6 +29,7 @@ struct Layout {
   size_t counts, offsets, kept_offsets, perm, row_of, drop, blk_counts, tile_start;
   size_t x_l, hid, y_perm, rn, hs, ys;
   size_t qb_logits, qb_req;  // Quantile Balancing: logits [T, N], required [N, T]
+  size_t rb_part;             // router backward: fp32 partial sums of dW_route
   size_t total;
 };
 
@@ -102,6 +103,8 @@ Layout layout(const moe_desc_t &d) {
   }
   L.qb_logits = take((size_t)d.T * d.N * 4);
   L.qb_req = take((size_t)d.T * d.N * 4);
+  L.rb_part = is_latent(d) ? 0
+                           : take((size_t)route_bwd_chunks(d.T, d.N, d.d) * d.N * d.d * 4);
   L.total = off;
   return L;
 }
@@ -405,7 +408,7 @@ moe_status_t forward_impl(const moe_desc_t *desc, const moe_weights_t *wts, cons
   int32_t *perm = o.perm ? o.perm : region<int32_t>(ws, L.perm);
   int32_t *row_of = o.row_of ? o.row_of : region<int32_t>(ws, L.row_of);
   uint8_t *drop = o.drop ? o.drop : region<uint8_t>(ws, L.drop);
-  float *y_perm = region<float>(ws, L.y_perm);
+  float *y_perm = o.y_perm ? o.y_perm : region<float>(ws, L.y_perm);
 
   Tracer tr{events, n_events, 0, st};
   MOE_TRY(tr.mark());
@@ -556,6 +559,37 @@ moe_status_t moe_qb_update(const moe_desc_t *desc, const void *u, const void *W_
                      d.N, EP_F32, nullptr, nullptr, 0, st));
   return hip_status(launch_qb_update(logits, d.T, d.N, d.k, bias, (int)qq, method,
                                      region<float>(ws, L.qb_req), new_bias, st));
+}
+
+moe_status_t moe_route_backward(const moe_desc_t *desc, const void *u, const void *W_route,
+                                const int32_t *topk_idx, const int32_t *row_of,
+                                const float *stats, const float *y_perm, const void *dy,
+                                float aux_scale, float *dz, float *dW_route, float *du, void *ws,
+                                size_t ws_bytes, moe_stream_t stream) {
+  const moe_status_t v = validate(desc);
+  if (v != MOE_OK) return v;
+  const moe_desc_t &d = *desc;
+  if (u == nullptr || W_route == nullptr || topk_idx == nullptr || row_of == nullptr ||
+      stats == nullptr || y_perm == nullptr || dy == nullptr || dz == nullptr ||
+      dW_route == nullptr || du == nullptr)
+    return MOE_ERR_ARG;
+  if (!isfinite(aux_scale)) return MOE_ERR_ARG;
+  // Plain layer; the logits come from the bf16 MFMA GEMM.
+  if (is_latent(d) || d.act_dtype != MOE_BF16 || d.router_dtype != MOE_BF16)
+    return MOE_ERR_UNSUPPORTED;
+  const Layout L = layout(d);
+  if (ws == nullptr || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  float *logits = region<float>(ws, L.qb_logits);
+  MOE_TRY(dense_gemm(static_cast<const uint16_t *>(u), d.d, 0,
+                     static_cast<const uint16_t *>(W_route), nullptr, 0, d.d, d.N, 1, d.T, logits,
+                     d.N, EP_F32, nullptr, nullptr, 0, st));
+  const float aux_coef = aux_scale * d.aux_alpha * (float)d.N / (float)d.T;
+  return hip_status(launch_route_backward(
+      logits, d.T, d.N, d.k, d.d, d.gate == MOE_GATE_RENORM ? 1 : 0, topk_idx, row_of, y_perm,
+      static_cast<const uint16_t *>(dy), stats, aux_coef, static_cast<const uint16_t *>(u),
+      static_cast<const uint16_t *>(W_route), region<float>(ws, L.rb_part), dz, dW_route, du,
+      st));
 }
 
 moe_status_t moe_dispatch(const moe_desc_t *desc, const int32_t *topk_idx, int32_t *counts,

@@ -234,3 +234,21 @@ def test_header_compiles_as_plain_c(tmp_path):
     subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror",
                     "-I", os.path.join(ROOT, "include"), "-c", str(src), "-o",
                     str(tmp_path / "use_header.o")], check=True)
+
+
+def test_route_backward_validates():
+    lib = L.load()
+    rb = lib.moe_route_backward
+    n = None
+    big = 1 << 40
+    d = good()
+    args = lambda desc, **kw: [ctypes.byref(desc)] + [kw.get(a, FAKE) for a in (  # noqa: E731
+        "u", "w", "idx", "row_of", "stats", "y_perm", "dy")] + [kw.get("aux", 1.0)] + [
+        kw.get(a, FAKE) for a in ("dz", "dw", "du")] + [FAKE, kw.get("ws", big), n]
+    assert rb(*args(d, ws=10)) == L.MOE_ERR_WORKSPACE
+    for a in ("u", "w", "idx", "row_of", "stats", "y_perm", "dy", "dz", "dw", "du"):
+        assert rb(*args(d, **{a: n})) == L.MOE_ERR_ARG, a
+    assert rb(*args(d, aux=float("nan"))) == L.MOE_ERR_ARG
+    assert rb(*args(H.desc_for(C.LATENT))) == L.MOE_ERR_UNSUPPORTED     # plain layers only
+    assert rb(*args(H.desc_for(C.TINY))) == L.MOE_ERR_UNSUPPORTED       # bf16 only
+    assert rb(*args(H.desc_for(C.MCU_BATCH))) == L.MOE_ERR_UNSUPPORTED  # fp32 router
