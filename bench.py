@@ -142,7 +142,46 @@ def run_workload(cfg, steps, warmup):
          "alg": algorithmic(cfg, kept), "desc": desc}
     if cfg.act_dtype == "bf16" and cfg.router_dtype == "bf16":
         r["quantile_balancing"] = time_qb(moe, desc, u, w["W_route"], ws, cfg, steps)
+        if not cfg.latent:
+            r["route_backward"] = time_route_backward(moe, H, desc, u, w, y, out, ws, cfg, steps)
     return r
+
+
+def time_route_backward(moe, H, desc, u, w, y, out, ws, cfg, steps):
+    """moe_route_backward after a forward that hands out its expert outputs,
+    with a seeded upstream gradient dy; averaged over `steps`.  Algorithmic
+    bytes: u twice (logits GEMM, dW_route), dy, the kept expert-output rows
+    (fp32), du written (fp32), dz and the logits (T x N fp32, three passes)."""
+    import torch
+
+    import synth as S
+
+    kept = int(H.to_host(out["kept_offsets"])[-1])
+    y_perm = torch.empty((max(kept, 1), cfg.d), dtype=torch.float32, device="cuda")
+    out = dict(out, y_perm=y_perm)
+    moe.moe_forward(desc, w, u, y, out, ws)
+    dy = H.to_device(S.normal_stored(cfg.seed + 1, 96, cfg.T * cfg.d, 0.5, "bf16")
+                     .reshape(cfg.T, cfg.d))
+    dz = torch.empty((cfg.T, cfg.N), dtype=torch.float32, device="cuda")
+    dw = torch.empty((cfg.N, cfg.d), dtype=torch.float32, device="cuda")
+    du = torch.empty((cfg.T, cfg.d), dtype=torch.float32, device="cuda")
+    args = (desc, u, w["W_route"], out["topk_idx"], out["row_of"], out["stats"], y_perm, dy, dz,
+            dw, du, ws)
+    for _ in range(2):
+        moe.moe_route_backward(*args, aux_scale=1.0)
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(steps):
+        moe.moe_route_backward(*args, aux_scale=1.0)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    T, d, N = cfg.T, cfg.d, cfg.N
+    alg = 2 * T * d * 2 + T * d * 2 + kept * d * 4 + T * d * 4 + 3 * T * N * 4
+    return {"ms": ms, "algorithmic_bytes": alg, "gb_s": alg / (ms / 1e3) / 1e9,
+            "hbm_frac": alg / (ms / 1e3) / 1e9 / PEAK_HBM_GBS}
 
 
 def time_qb(moe, desc, u, w_route, ws, cfg, steps):
@@ -255,6 +294,8 @@ def main():
     }
     if "quantile_balancing" in r:
         line["quantile_balancing"] = r["quantile_balancing"]
+    if "route_backward" in r:
+        line["route_backward"] = r["route_backward"]
     for key, name in (("decode", args.decode_workload), ("decode_fp8", args.fp8_decode_workload),
                       ("decode_mxfp4", args.mxfp4_decode_workload)):
         if not name:

@@ -12,10 +12,11 @@
 //   rb_dz_kernel:   a wave per token (16 per block): softmax of the logits,
 //                   the k dot products dy_t . y_perm[row] over d, the gate and
 //                   softmax backward through a per-wave LDS row of p and dp.
-//   rb_dw_kernel:   fp32 partial sums of dz^T u over chunks of tokens, a
-//                   thread per column of u and 8 experts per block;
+//   rb_dw_kernel:   fp32 partial sums of dz^T u over chunks of tokens: a
+//                   thread per 8 columns of u (one 16-byte load a token) and
+//                   8 experts, the chunk's dz staged in LDS;
 //   rb_dw_reduce:   the chunks summed in chunk order (deterministic).
-//   rb_du_kernel:   a thread per column of W_route and 16 tokens per block.
+//   rb_du_kernel:   a thread per 8 columns of W_route and 8 tokens.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -24,9 +25,10 @@ namespace moe {
 namespace {
 
 constexpr int kRbTokens = 16;    // waves (tokens) per block in rb_dz_kernel
-constexpr int kRbMaxN = 1024;
 constexpr int kDwExperts = 8;    // experts per rb_dw_kernel block
-constexpr int kDuTokens = 16;    // tokens per rb_du_kernel block
+constexpr int kDwChunk = 64;     // tokens per rb_dw_kernel chunk (at least)
+constexpr int kDwStage = 256;    // tokens of dz staged in LDS at a time
+constexpr int kDuTokens = 8;     // tokens per rb_du_kernel thread
 constexpr int kRbMaxK = 32;      // slots per token (k <= 32)
 
 template <int NPL>
@@ -35,8 +37,8 @@ __global__ __launch_bounds__(64 * kRbTokens) void rb_dz_kernel(
     const int32_t *__restrict__ idx, const int32_t *__restrict__ row_of,
     const float *__restrict__ y_perm, const uint16_t *__restrict__ dy,
     const float *__restrict__ stats, float aux_coef, float *__restrict__ dz) {
-  __shared__ float sp[kRbTokens][kRbMaxN];   // p of the wave's token
-  __shared__ float sdp[kRbTokens][kRbMaxN];  // dp of the wave's token
+  __shared__ float sp[kRbTokens][64 * NPL];   // p of the wave's token
+  __shared__ float sdp[kRbTokens][64 * NPL];  // dp of the wave's token
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   const int64_t t = (int64_t)blockIdx.x * kRbTokens + wv;
@@ -132,29 +134,64 @@ __global__ __launch_bounds__(64 * kRbTokens) void rb_dz_kernel(
   }
 }
 
-// part[ch][n][c] = sum over tokens t of chunk ch of dz[t][n] * u[t][c].
+// Eight bf16 (one 16-byte load) -> fp32.
+__device__ __forceinline__ void bf16x8_to_f32(const uint4 raw, float (&x)[8]) {
+  const uint32_t wds[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    x[2 * q] = __uint_as_float(wds[q] << 16);
+    x[2 * q + 1] = __uint_as_float(wds[q] & 0xFFFF0000u);
+  }
+}
+
+// part[ch][n][c] = sum over tokens t of chunk ch of dz[t][n] * u[t][c]; a
+// thread owns columns 8i .. 8i+7 (d % 8 == 0) and the block's 8 experts.
 __global__ __launch_bounds__(256) void rb_dw_kernel(const float *__restrict__ dz,
                                                     const uint16_t *__restrict__ u, int64_t T,
                                                     int N, int d, int64_t chunk,
                                                     float *__restrict__ part) {
-  const int c = blockIdx.x * 256 + threadIdx.x;
+  __shared__ float sdz[kDwStage * kDwExperts];  // dz of kDwStage tokens
+  const int c = (blockIdx.x * 256 + threadIdx.x) * 8;
   const int n0 = blockIdx.y * kDwExperts;
   const int64_t t0 = blockIdx.z * chunk;
   const int64_t t1 = (t0 + chunk) < T ? (t0 + chunk) : T;
-  float acc[kDwExperts];
+  float acc[kDwExperts][8];
 #pragma unroll
-  for (int j = 0; j < kDwExperts; ++j) acc[j] = 0.f;
-  if (c < d) {
-    for (int64_t t = t0; t < t1; ++t) {
-      const float x = __uint_as_float((uint32_t)u[t * d + c] << 16);
+  for (int j = 0; j < kDwExperts; ++j)
 #pragma unroll
-      for (int j = 0; j < kDwExperts; ++j)
-        if (n0 + j < N) acc[j] += dz[t * N + n0 + j] * x;
+    for (int q = 0; q < 8; ++q) acc[j][q] = 0.f;
+  for (int64_t s0 = t0; s0 < t1; s0 += kDwStage) {
+    const int nt = (int)((t1 - s0) < kDwStage ? (t1 - s0) : kDwStage);
+    __syncthreads();  // the previous stage's reads are done
+    for (int i = threadIdx.x; i < nt * kDwExperts; i += 256) {
+      const int tt = i / kDwExperts, j = i % kDwExperts;
+      sdz[i] = (n0 + j < N) ? dz[(s0 + tt) * N + n0 + j] : 0.f;
     }
+    __syncthreads();
+    if (c < d) {
+      const uint16_t *up = u + s0 * d + c;
+#pragma unroll 4
+      for (int tt = 0; tt < nt; ++tt) {
+        float x[8];
+        bf16x8_to_f32(*reinterpret_cast<const uint4 *>(up + (int64_t)tt * d), x);
 #pragma unroll
-    for (int j = 0; j < kDwExperts; ++j)
-      if (n0 + j < N) part[((int64_t)blockIdx.z * N + n0 + j) * d + c] = acc[j];
+        for (int j = 0; j < kDwExperts; ++j) {
+          const float g = sdz[tt * kDwExperts + j];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) acc[j][q] += g * x[q];
+        }
+      }
+    }
   }
+  if (c >= d) return;
+#pragma unroll
+  for (int j = 0; j < kDwExperts; ++j)
+    if (n0 + j < N) {
+      float *dst = part + ((int64_t)blockIdx.z * N + n0 + j) * d + c;
+      *reinterpret_cast<float4 *>(dst) = make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
+      *reinterpret_cast<float4 *>(dst + 4) =
+          make_float4(acc[j][4], acc[j][5], acc[j][6], acc[j][7]);
+    }
 }
 
 __global__ __launch_bounds__(256) void rb_dw_reduce_kernel(const float *__restrict__ part,
@@ -167,32 +204,44 @@ __global__ __launch_bounds__(256) void rb_dw_reduce_kernel(const float *__restri
   dw[i] = s;
 }
 
-// du[t][c] = sum_n dz[t][n] * W_route[n][c].
+// du[t][c] = sum_n dz[t][n] * W_route[n][c]: a thread owns columns
+// 8i .. 8i+7 of kDuTokens tokens.
 __global__ __launch_bounds__(256) void rb_du_kernel(const float *__restrict__ dz,
                                                     const uint16_t *__restrict__ w, int64_t T,
                                                     int N, int d, float *__restrict__ du) {
-  const int c = blockIdx.x * 256 + threadIdx.x;
+  const int c = (blockIdx.x * 256 + threadIdx.x) * 8;
   const int64_t t0 = (int64_t)blockIdx.y * kDuTokens;
   if (c >= d) return;
-  float acc[kDuTokens];
+  float acc[kDuTokens][8];
 #pragma unroll
-  for (int j = 0; j < kDuTokens; ++j) acc[j] = 0.f;
+  for (int j = 0; j < kDuTokens; ++j)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[j][q] = 0.f;
   for (int n = 0; n < N; ++n) {
-    const float x = __uint_as_float((uint32_t)w[(int64_t)n * d + c] << 16);
+    float x[8];
+    bf16x8_to_f32(*reinterpret_cast<const uint4 *>(w + (int64_t)n * d + c), x);
 #pragma unroll
-    for (int j = 0; j < kDuTokens; ++j)
-      if (t0 + j < T) acc[j] += dz[(t0 + j) * N + n] * x;
+    for (int j = 0; j < kDuTokens; ++j) {
+      const float g = (t0 + j < T) ? dz[(t0 + j) * N + n] : 0.f;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[j][q] += g * x[q];
+    }
   }
 #pragma unroll
   for (int j = 0; j < kDuTokens; ++j)
-    if (t0 + j < T) du[(t0 + j) * d + c] = acc[j];
+    if (t0 + j < T) {
+      float *dst = du + (t0 + j) * d + c;
+      *reinterpret_cast<float4 *>(dst) = make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
+      *reinterpret_cast<float4 *>(dst + 4) =
+          make_float4(acc[j][4], acc[j][5], acc[j][6], acc[j][7]);
+    }
 }
 
 }  // namespace
 
 int64_t route_bwd_chunks(int64_t T, int N, int d) {
-  // Partial-sum chunks of at least 256 tokens, at most 64 MiB of partials.
-  const int64_t by_tokens = (T + 255) / 256;
+  // Partial-sum chunks of at least kDwChunk tokens, at most 64 MiB of partials.
+  const int64_t by_tokens = (T + kDwChunk - 1) / kDwChunk;
   int64_t by_bytes = ((int64_t)64 << 20) / ((int64_t)N * d * 4);
   if (by_bytes < 1) by_bytes = 1;
   return by_tokens < by_bytes ? by_tokens : by_bytes;
@@ -215,14 +264,14 @@ hipError_t launch_route_backward(const float *logits, int64_t T, int N, int k, i
   if (e != hipSuccess) return e;
   const int64_t chunks = route_bwd_chunks(T, N, d);
   const int64_t chunk = (T + chunks - 1) / chunks;
-  hipLaunchKernelGGL(rb_dw_kernel, dim3((unsigned)((d + 255) / 256),
+  hipLaunchKernelGGL(rb_dw_kernel, dim3((unsigned)((d / 8 + 255) / 256),
                                         (unsigned)((N + kDwExperts - 1) / kDwExperts),
                                         (unsigned)chunks),
                      dim3(256), 0, st, dz, u, T, N, d, chunk, part);
   const int64_t nd = (int64_t)N * d;
   hipLaunchKernelGGL(rb_dw_reduce_kernel, dim3((unsigned)((nd + 255) / 256)), dim3(256), 0, st,
                      part, chunks, nd, dw);
-  hipLaunchKernelGGL(rb_du_kernel, dim3((unsigned)((d + 255) / 256),
+  hipLaunchKernelGGL(rb_du_kernel, dim3((unsigned)((d / 8 + 255) / 256),
                                         (unsigned)((T + kDuTokens - 1) / kDuTokens)),
                      dim3(256), 0, st, dz, w_route, T, N, d, du);
   return hipGetLastError();
