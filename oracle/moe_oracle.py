@@ -75,7 +75,8 @@ mantissa (E2M1 is a subset of E4M3); a hand-expanded two-block matrix.
 Router backward pins: torch autograd of an independently written forward;
 central differences of the oracle's own loss; the softmax gradient sums to
 zero per token; a balanced f makes the aux gradient vanish; renorm with
-k = N equals the prob gate.
+k = N equals the prob gate.  Experts backward pins: torch autograd of an
+independently written SwiGLU / SiTU-GLU layer (capacity drops included).
 Parity unpinned: the exact SiTU-GLU form, the LatentMoE wiring and the
 Quantile Balancing readings (score, cutoff, q, bins) are readings, pinned
 only through the limits and invariants above.
@@ -268,6 +269,58 @@ def route_backward(u: np.ndarray, w_route: np.ndarray, idx: np.ndarray, row_of: 
     dp = dp + aux_scale * alpha * N * np.asarray(f, dtype=np.float64)[None, :] / T
     dz = p * (dp - (p * dp).sum(axis=1, keepdims=True))
     return {"p": p, "da": da, "dp": dp, "dz": dz, "dW_route": dz.T @ u, "du": dz @ w_route}
+
+
+def act_backward(act: str, g: np.ndarray, v: np.ndarray, dh: np.ndarray,
+                 beta_g: float = 4.0, beta_u: float = 25.0):
+    """(dg, dv) for h = act(g, v) given dh.  SwiGLU h = silu(g) v with
+    silu'(g) = s(g) (1 + g (1 - s(g))), s the logistic function; SiTU-GLU
+    caps both factors first (g' = beta_g tanh(g / beta_g), likewise v), which
+    adds the factors 1 - tanh^2."""
+    if act == "swiglu":
+        sg = 1.0 / (1.0 + np.exp(-g))
+        return dh * v * sg * (1.0 + g * (1.0 - sg)), dh * g * sg
+    if act == "situ":
+        tg, tv = np.tanh(g / beta_g), np.tanh(v / beta_u)
+        gc, vc = beta_g * tg, beta_u * tv
+        sg = 1.0 / (1.0 + np.exp(-gc))
+        dgc = dh * vc * sg * (1.0 + gc * (1.0 - sg))
+        dvc = dh * gc * sg
+        return dgc * (1.0 - tg * tg), dvc * (1.0 - tv * tv)
+    raise ValueError(act)
+
+
+def experts_backward(x: np.ndarray, disp: Dict[str, np.ndarray], a: np.ndarray,
+                     experts: ExpertFn, dy: np.ndarray, *, act: str, k: int,
+                     beta_g: float = 4.0, beta_u: float = 25.0) -> Dict[str, np.ndarray]:
+    """The experts' share of the gradient of <dy, y>, y_t = sum_kept a_{t,s}
+    F_{i_s}(x_t) (page "MoE: how sparse activation saves compute", §3.1 eq.
+    F and §3.2 eq. y, differentiated): for each kept row of expert i with
+    token t and weight a, dY = a dy_t; with G = W_gate x, U = W_up x,
+    H = act(G, U): dH = W_down^T dY, (dG, dU) = act'(G, U) dH,
+    dx_t += W_gate^T dG + W_up^T dU, dW_down += dY H^T, dW_gate += dG x^T,
+    dW_up += dU x^T.  Experts with no kept row get zero gradients."""
+    T, w = x.shape
+    N = len(disp["counts"])
+    dx = np.zeros((T, w))
+    dWg, dWu, dWd = [], [], []
+    for e in range(N):
+        wg, wu, wd = _expert64(experts, e)
+        lo, kept = int(disp["offsets"][e]), int(disp["kept_counts"][e])
+        ent = disp["perm"][lo:lo + kept]
+        toks, slots = ent // k, ent % k
+        xr = x[toks]
+        g, v = xr @ wg.T, xr @ wu.T
+        hh = make_act(act, beta_g, beta_u)(g, v)
+        dY = a[toks, slots][:, None] * dy[toks]
+        dh = dY @ wd
+        dg, dv = act_backward(act, g, v, dh, beta_g, beta_u)
+        np.add.at(dx, toks, dg @ wg + dv @ wu)
+        dWd.append(dY.T @ hh)
+        dWg.append(dg.T @ xr)
+        dWu.append(dv.T @ xr)
+    return {"dx": dx, "dW_gate": np.stack(dWg), "dW_up": np.stack(dWu),
+            "dW_down": np.stack(dWd)}
 
 
 # ---------------------------------------------------------------------------

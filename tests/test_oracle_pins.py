@@ -827,3 +827,40 @@ def test_route_backward_renorm_over_all_experts_is_the_prob_gate():
     b = O.route_backward(u, w, r["idx"], disp["row_of"], y_rows, dy, gate="prob", f=f,
                          alpha=0.01, aux_scale=1.0)
     assert np.allclose(a["dz"], b["dz"], rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("act,cap", [("swiglu", None), ("situ", None), ("swiglu", 5)])
+def test_experts_backward_matches_torch_autograd(act, cap):
+    rng = np.random.default_rng(8)
+    T, d, h, N, k = 20, 12, 10, 4, 2
+    x = rng.standard_normal((T, d))
+    wr = rng.standard_normal((N, d)) / math.sqrt(d)
+    W = [(rng.standard_normal((h, d)) / math.sqrt(d), rng.standard_normal((h, d)) / math.sqrt(d),
+          rng.standard_normal((d, h)) / math.sqrt(h)) for _ in range(N)]
+    r = O.route(x, wr, k, "renorm")
+    disp = O.dispatch(r["idx"], N, cap)
+    dy = rng.standard_normal((T, d))
+    bg, bu = 1.5, 2.0   # small caps so the tanh factors matter
+    g = O.experts_backward(x, disp, r["a"], lambda e: W[e], dy, act=act, k=k, beta_g=bg, beta_u=bu)
+    # Independent torch forward of the expert part (weights a held fixed).
+    xt = torch.tensor(x, requires_grad=True)
+    Wt = [tuple(torch.tensor(m, requires_grad=True) for m in ws) for ws in W]
+    y = torch.zeros((T, d), dtype=torch.float64)
+    for t in range(T):
+        for s in range(k):
+            if disp["row_of"][t * k + s] < 0:
+                continue
+            wg, wu, wd = Wt[int(r["idx"][t, s])]
+            gg, vv = wg @ xt[t], wu @ xt[t]
+            if act == "situ":
+                gg, vv = bg * torch.tanh(gg / bg), bu * torch.tanh(vv / bu)
+            y[t] = y[t] + float(r["a"][t, s]) * (wd @ (torch.nn.functional.silu(gg) * vv))
+    (torch.tensor(dy) * y).sum().backward()
+    assert np.allclose(g["dx"], xt.grad.numpy(), rtol=1e-10, atol=1e-12)
+    for e in range(N):
+        assert np.allclose(g["dW_gate"][e], Wt[e][0].grad.numpy() if Wt[e][0].grad is not None
+                           else 0.0, rtol=1e-10, atol=1e-12)
+        assert np.allclose(g["dW_up"][e], Wt[e][1].grad.numpy() if Wt[e][1].grad is not None
+                           else 0.0, rtol=1e-10, atol=1e-12)
+        assert np.allclose(g["dW_down"][e], Wt[e][2].grad.numpy() if Wt[e][2].grad is not None
+                           else 0.0, rtol=1e-10, atol=1e-12)
