@@ -227,6 +227,38 @@ moe_status_t moe_route_backward(const moe_desc_t *desc, const void *u, const voi
                                 float aux_scale, float *dz, float *dW_route, float *du, void *ws,
                                 size_t ws_bytes, moe_stream_t stream);
 
+/* Workspace of moe_experts_backward (its own; larger than the forward's:
+   the recomputed gate/up, dY/dG/dU rows, transposed weight copies and the
+   expert-segmented transposes the weight gradients reduce over).  Returns
+   MOE_ERR_UNSUPPORTED where moe_experts_backward does. */
+moe_status_t moe_backward_workspace_bytes(const moe_desc_t *desc, size_t *bytes);
+
+/* The experts' backward (page "MoE: how sparse activation saves compute",
+   §3.1 eq. F and §3.2 eq. y, differentiated): the experts' share of the
+   gradient of L = <dy, y> with the combine weights held fixed (their own
+   gradient is moe_route_backward's).  For each kept row of expert i with
+   token t and weight a: dY = a dy_t; G = W_gate x, U = W_up x (recomputed);
+   dH = W_down^T dY; (dG, dU) = act'(G, U) dH; dx_t += W_gate^T dG +
+   W_up^T dU; dW_down += dY act(G, U)^T; dW_gate += dG x^T; dW_up += dU x^T.
+     w         W_gate, W_up, W_down of the forward (bf16)
+     u         [T, d] bf16 the forward's input (x = u for the plain layer)
+     topk_w, offsets, kept_offsets, perm, row_of   the forward's (moe_outputs_t)
+     dy        [T, d] bf16
+     dx        [T, d] fp32 out: the experts' part of the gradient at u
+     dW_gate, dW_up [N, h, d], dW_down [N, d, h]  fp32 out, all three or
+               none (null: input gradient only); experts with no kept row
+               get zeros
+     ws        moe_backward_workspace_bytes() bytes
+   Intermediates are rounded to bf16 where they feed the MFMA GEMMs (dY, G,
+   U, dG, dU); every sum is fp32.  Plain layers with bf16 activations and
+   weights only (MOE_ERR_UNSUPPORTED otherwise). */
+moe_status_t moe_experts_backward(const moe_desc_t *desc, const moe_weights_t *w, const void *u,
+                                  const float *topk_w, const int32_t *offsets,
+                                  const int32_t *kept_offsets, const int32_t *perm,
+                                  const int32_t *row_of, const void *dy, float *dx,
+                                  float *dW_gate, float *dW_up, float *dW_down, void *ws,
+                                  size_t ws_bytes, moe_stream_t stream);
+
 /* Dispatch: group the T*k (token, slot) entries e = t*k + s by expert in
    token order (sections 3.5, 3.6, 3.8).
      topk_idx     [T, k] int32 in (values in [0, N); a token names an expert once)

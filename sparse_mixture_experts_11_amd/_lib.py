@@ -15,7 +15,8 @@ MOE_ACT_SWIGLU, MOE_ACT_SITU_GLU = 0, 1
 # Every symbol include/moe.h declares.
 EXPORTS = ("moe_desc_init", "moe_status_string", "moe_workspace_bytes",
            "moe_capacity_from_factor", "moe_route", "moe_route_biased", "moe_qb_update",
-           "moe_route_backward", "moe_dispatch", "moe_expert_ffn", "moe_expert_ffn_scaled",
+           "moe_route_backward", "moe_backward_workspace_bytes", "moe_experts_backward",
+           "moe_dispatch", "moe_expert_ffn", "moe_expert_ffn_scaled",
            "moe_combine",
            "moe_forward", "moe_forward_traced", "moe_stage_name")
 
@@ -77,6 +78,10 @@ def load() -> ctypes.CDLL:
     lib.moe_qb_update.restype = I32
     lib.moe_route_backward.argtypes = [D, P, P, P, P, P, P, P, ctypes.c_float, P, P, P, P, SZ, P]
     lib.moe_route_backward.restype = I32
+    lib.moe_backward_workspace_bytes.argtypes = [D, ctypes.POINTER(SZ)]
+    lib.moe_backward_workspace_bytes.restype = I32
+    lib.moe_experts_backward.argtypes = [D, ctypes.c_void_p] + [P] * 12 + [SZ, P]
+    lib.moe_experts_backward.restype = I32
     lib.moe_dispatch.argtypes = [D, P, P, P, P, P, P, P, P, SZ, P]
     lib.moe_dispatch.restype = I32
     lib.moe_expert_ffn.argtypes = [D, P, P, P, P, P, P, P, P, P, SZ, P]

@@ -122,6 +122,29 @@ def moe_route_backward(desc, u, W_route, topk_idx, row_of, stats, y_perm, dy, dz
            "moe_route_backward")
 
 
+def moe_backward_workspace_bytes(desc) -> int:
+    n = ctypes.c_size_t(0)
+    _check(L.load().moe_backward_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)),
+           "moe_backward_workspace_bytes")
+    return n.value
+
+
+def backward_workspace(desc, device="cuda") -> torch.Tensor:
+    return torch.empty(max(moe_backward_workspace_bytes(desc), 1), dtype=torch.uint8,
+                       device=device)
+
+
+def moe_experts_backward(desc, weights: Mapping[str, torch.Tensor], u, topk_w, offsets,
+                         kept_offsets, perm, row_of, dy, dx, ws, dW_gate=None, dW_up=None,
+                         dW_down=None, stream=None) -> None:
+    w = _weights(weights)
+    _check(L.load().moe_experts_backward(ctypes.byref(desc), ctypes.byref(w), _ptr(u),
+                                         _ptr(topk_w), _ptr(offsets), _ptr(kept_offsets),
+                                         _ptr(perm), _ptr(row_of), _ptr(dy), _ptr(dx),
+                                         _ptr(dW_gate), _ptr(dW_up), _ptr(dW_down), _ptr(ws),
+                                         ws.numel(), _stream(stream)), "moe_experts_backward")
+
+
 def moe_dispatch(desc, topk_idx, counts, offsets, kept_offsets, perm, row_of, drop, ws,
                  stream=None) -> None:
     _check(L.load().moe_dispatch(ctypes.byref(desc), _ptr(topk_idx), _ptr(counts), _ptr(offsets),

@@ -1,0 +1,224 @@
+// The experts' backward (page "MoE: how sparse activation saves compute",
+// §3.1 eq. F and §3.2 eq. y, differentiated): for each kept row of expert i
+// with token t and weight a,
+//   dY = a dy_t;  G = W_gate x, U = W_up x (recomputed);
+//   dH = W_down^T dY;  (dG, dU) = act'(G, U) dH;
+//   dx_t += W_gate^T dG + W_up^T dU;
+//   dW_down += dY act(G, U)^T;  dW_gate += dG x^T;  dW_up += dU x^T.
+// The products run on the grouped GEMM: dH and (dG, dU) in one launch whose
+// epilogue applies the activation's backward, dx rows against transposed
+// copies of W_gate | W_up, and the weight gradients as "K segment" GEMMs that
+// reduce over each expert's own rows.  This file holds the data movement
+// around them:
+//   bwd_gather_dy_kernel: dY rows (a dy_t) in the expert-sorted row order;
+//   transpose_bf16_kernel: [B][R][C] -> [B][C][ld] at a column offset, 64x64
+//     tiles through LDS (the weight copies the GEMMs read K-contiguous);
+//   kseg_kernel: each expert's rows padded to a multiple of 128 (at least
+//     128), as a prefix of column offsets;
+//   seg_transpose_kernel: row-major [rows][width] -> [width][Rpad], row r of
+//     expert g to column kseg[g] + r - kept_offsets[g]; optionally gathered
+//     token rows (x) or act(G, U) computed on the way;
+//   fill_zero_kernel, rows_sum_kernel (dx_t = sum of its kept rows).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+namespace {
+
+__global__ __launch_bounds__(256) void bwd_gather_dy_kernel(const uint16_t *__restrict__ dy,
+                                                            int d, int k,
+                                                            const int32_t *__restrict__ row_of,
+                                                            const float *__restrict__ topk_w,
+                                                            uint16_t *__restrict__ dy_perm) {
+  const int64_t ent = blockIdx.x;
+  const int r = row_of[ent];
+  if (r < 0) return;
+  const float a = topk_w[ent];
+  const uint16_t *src = dy + (ent / k) * (int64_t)d;
+  uint16_t *dst = dy_perm + (int64_t)r * d;
+  for (int c = threadIdx.x * 8; c < d; c += 256 * 8) {
+    const uint4 raw = *reinterpret_cast<const uint4 *>(src + c);
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+    uint4 o;
+    uint32_t *ow = reinterpret_cast<uint32_t *>(&o);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      ow[q] = pack_bf16x2_hw(a * __uint_as_float(w[q] << 16),
+                             a * __uint_as_float(w[q] & 0xFFFF0000u));
+    *reinterpret_cast<uint4 *>(dst + c) = o;
+  }
+}
+
+// dst[b][c][col0 + r] = src[b][r][c]: src [B][R][C], dst rows of length ld.
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t *__restrict__ src,
+                                                             int R, int C,
+                                                             uint16_t *__restrict__ dst,
+                                                             int64_t ld, int col0) {
+  __shared__ uint16_t tile[64][66];
+  const int b = blockIdx.z;
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const uint16_t *s = src + (int64_t)b * R * C;
+  uint16_t *o = dst + (int64_t)b * C * ld;
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int rr = i / 64, cc = i % 64;
+    tile[rr][cc] = (r0 + rr < R && c0 + cc < C) ? s[(int64_t)(r0 + rr) * C + c0 + cc] : 0;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int cc = i / 64, rr = i % 64;
+    if (r0 + rr < R && c0 + cc < C) o[(int64_t)(c0 + cc) * ld + col0 + r0 + rr] = tile[rr][cc];
+  }
+}
+
+// kseg[g] = sum over g' < g of 128 * max(1, ceil(m_g' / 128)), m = kept rows.
+__global__ __launch_bounds__(1024) void kseg_kernel(const int32_t *__restrict__ kept_offsets,
+                                                    int G, int32_t *__restrict__ kseg) {
+  __shared__ int tmp[1024];
+  int run = 0;
+  for (int base = 0; base < G; base += 1024) {
+    const int g = base + threadIdx.x;
+    const int m = (g < G) ? kept_offsets[g + 1] - kept_offsets[g] : 0;
+    tmp[threadIdx.x] = (g < G) ? 128 * (m > 0 ? (m + 127) / 128 : 1) : 0;
+    __syncthreads();
+    for (int o = 1; o < 1024; o <<= 1) {
+      const int add = (int)threadIdx.x >= o ? tmp[threadIdx.x - o] : 0;
+      __syncthreads();
+      tmp[threadIdx.x] += add;
+      __syncthreads();
+    }
+    if (g < G) kseg[g + 1] = run + tmp[threadIdx.x];
+    run += tmp[1023];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) kseg[0] = 0;
+}
+
+__global__ __launch_bounds__(256) void fill_zero_kernel(uint4 *__restrict__ p, int64_t n16) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16;
+       i += (int64_t)gridDim.x * 256)
+    p[i] = uint4{0u, 0u, 0u, 0u};
+}
+
+// Rows r of the expert-sorted layout (R rows) to columns of dst [width][ld]:
+// expert g = the group with kept_offsets[g] <= r < kept_offsets[g+1], column
+// kseg[g] + r - kept_offsets[g].  Source row: r (src, row stride lds), or the
+// token row perm[offsets[g] + j] / kslots when perm is given; with src2 the
+// value is act(src, src2) (the hidden of the recomputed gate and up).
+__global__ __launch_bounds__(256) void seg_transpose_kernel(
+    const uint16_t *__restrict__ src, const uint16_t *__restrict__ src2, int64_t lds, int width,
+    const int32_t *__restrict__ kept_offsets, const int32_t *__restrict__ offsets,
+    const int32_t *__restrict__ perm, int kslots, const int32_t *__restrict__ kseg, int G,
+    int act, float bg, float bu, uint16_t *__restrict__ dst, int64_t ld) {
+  __shared__ uint16_t tile[64][66];
+  __shared__ int64_t srow[64];
+  __shared__ int dcol[64];
+  const int R = kept_offsets[G];
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  if (r0 >= R) return;
+  if (threadIdx.x < 64) {
+    const int r = r0 + threadIdx.x;
+    if (r < R) {
+      int lo = 0, hi = G;  // largest g with kept_offsets[g] <= r
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (kept_offsets[mid] <= r) lo = mid; else hi = mid;
+      }
+      const int j = r - kept_offsets[lo];
+      srow[threadIdx.x] = perm ? (int64_t)(perm[offsets[lo] + j] / kslots) : (int64_t)r;
+      dcol[threadIdx.x] = kseg[lo] + j;
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int rr = i / 64, cc = i % 64;
+    uint16_t v = 0;
+    if (r0 + rr < R && c0 + cc < width) {
+      const int64_t at = srow[rr] * lds + c0 + cc;
+      if (src2 != nullptr) {
+        const float h = glu_act(__uint_as_float((uint32_t)src[at] << 16),
+                                __uint_as_float((uint32_t)src2[at] << 16), act, bg, bu);
+        v = (uint16_t)(pack_bf16x2_hw(h, 0.f) & 0xFFFFu);
+      } else {
+        v = src[at];
+      }
+    }
+    tile[rr][cc] = v;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int cc = i / 64, rr = i % 64;
+    if (r0 + rr < R && c0 + cc < width) dst[(int64_t)(c0 + cc) * ld + dcol[rr]] = tile[rr][cc];
+  }
+}
+
+// dx[t][c] = sum over the kept slots of t of rows[row_of[t*k + s]][c], fp32.
+__global__ __launch_bounds__(256) void rows_sum_kernel(const float *__restrict__ rows, int d,
+                                                       int k, const int32_t *__restrict__ row_of,
+                                                       float *__restrict__ dx) {
+  const int64_t t = blockIdx.x;
+  for (int c = threadIdx.x * 4; c < d; c += 256 * 4) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s = 0; s < k; ++s) {
+      const int r = row_of[t * k + s];
+      if (r < 0) continue;
+      const float4 v = *reinterpret_cast<const float4 *>(rows + (int64_t)r * d + c);
+      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+    *reinterpret_cast<float4 *>(dx + t * d + c) = acc;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_bwd_gather_dy(const uint16_t *dy, int64_t T, int d, int k,
+                                const int32_t *row_of, const float *topk_w, uint16_t *dy_perm,
+                                hipStream_t st) {
+  hipLaunchKernelGGL(bwd_gather_dy_kernel, dim3((unsigned)(T * k)), dim3(256), 0, st, dy, d, k,
+                     row_of, topk_w, dy_perm);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_bf16(const uint16_t *src, int B, int R, int C, uint16_t *dst,
+                                 int64_t ld, int col0, hipStream_t st) {
+  hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)((C + 63) / 64),
+                                                 (unsigned)((R + 63) / 64), (unsigned)B),
+                     dim3(256), 0, st, src, R, C, dst, ld, col0);
+  return hipGetLastError();
+}
+
+hipError_t launch_kseg(const int32_t *kept_offsets, int G, int32_t *kseg, hipStream_t st) {
+  hipLaunchKernelGGL(kseg_kernel, dim3(1), dim3(1024), 0, st, kept_offsets, G, kseg);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t st) {
+  const int64_t n16 = (int64_t)(bytes / 16);
+  if (n16 == 0) return hipSuccess;
+  const int64_t blocks = (n16 + 255) / 256 < 4096 ? (n16 + 255) / 256 : 4096;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, st,
+                     static_cast<uint4 *>(p), n16);
+  return hipGetLastError();
+}
+
+hipError_t launch_seg_transpose(const uint16_t *src, const uint16_t *src2, int64_t lds,
+                                int width, int64_t rows_bound, const int32_t *kept_offsets,
+                                const int32_t *offsets, const int32_t *perm, int kslots,
+                                const int32_t *kseg, int G, int act, float bg, float bu,
+                                uint16_t *dst, int64_t ld, hipStream_t st) {
+  if (rows_bound == 0) return hipSuccess;
+  hipLaunchKernelGGL(seg_transpose_kernel, dim3((unsigned)((width + 63) / 64),
+                                                (unsigned)((rows_bound + 63) / 64)),
+                     dim3(256), 0, st, src, src2, lds, width, kept_offsets, offsets, perm,
+                     kslots, kseg, G, act, bg, bu, dst, ld);
+  return hipGetLastError();
+}
+
+hipError_t launch_rows_sum(const float *rows, int64_t T, int d, int k, const int32_t *row_of,
+                           float *dx, hipStream_t st) {
+  hipLaunchKernelGGL(rows_sum_kernel, dim3((unsigned)T), dim3(256), 0, st, rows, d, k, row_of,
+                     dx);
+  return hipGetLastError();
+}
+
+}  // namespace moe

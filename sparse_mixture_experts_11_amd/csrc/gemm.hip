@@ -70,9 +70,10 @@ __device__ __forceinline__ bf16x8 lds_frag8(const char *tile, int r, int kq) {
 }
 
 // BM = 256 (waves 128x64) or 192 (waves 96x64, for experts with few rows).
-template <int EPI, int BM, bool FP8 = false>
+template <int EPI, int BM, bool FP8 = false, bool KSEG = false>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
   static_assert(!FP8 || EPI == EP_GLU || EPI == EP_F32, "fp8 weights: routed experts only");
+  static_assert(!KSEG || (EPI == EP_F32 && !FP8), "k segments: fp32 weight gradients");
   constexpr int ES = FP8 ? 1 : 2;          // bytes per B element
   constexpr int MI = BM / 64;              // 32-row A blocks per wave
   constexpr int kABytes = BM * BK * 2;     // 32 or 24 KiB per A stage
@@ -83,7 +84,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
   // ---- which tile: XCD-aware remap (block i runs on XCD i % 8: each XCD
   // takes one contiguous eighth of the real tiles), then (group, m-super, n,
   // m) order so the tiles running together on one XCD share A and B rows.
-  const int glu = (EPI == EP_GLU);
+  const int glu = (EPI == EP_GLU || EPI == EP_GU);
   const int64_t NT = glu ? (a.ncols + 127) / 128 : (a.ncols + BN - 1) / BN;
   const int64_t real_tiles = (a.mode == GM_DENSE)
                                  ? (int64_t)a.G * ((a.M_dense + BM - 1) / BM) * NT
@@ -162,11 +163,11 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
       const int64_t n = n_tile * BN + r;
       brow = n < a.ncols ? n : a.ncols - 1;
     }
-    boff[i] = (uint32_t)(brow * a.K * ES) + (uint32_t)(pc << 4);
+    boff[i] = (uint32_t)(brow * (KSEG ? a.ldb : a.K) * ES) + (uint32_t)(pc << 4);
   }
   const char *Bg = static_cast<const char *>(a.B) + (int64_t)g * a.strideB * ES;
   const char *Ug = glu ? static_cast<const char *>(a.B2) + (int64_t)g * a.strideB * ES : Bg;
-  const uint32_t bbytes = (uint32_t)((int64_t)a.ncols * a.K * ES);
+  const uint32_t bbytes = (uint32_t)((int64_t)a.ncols * (KSEG ? a.ldb : a.K) * ES);
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.A, 0xFFFFFFFFu);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bg, bbytes);
   const __amdgpu_buffer_rsrc_t ru = make_rsrc(Ug, bbytes);
@@ -174,8 +175,10 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
   // Direct global -> LDS loads: instruction i of wave w fills the 1 KiB of
   // rows 64i + 8w .. +7 and lane l lands at byte 16 l of it.
   typedef __attribute__((address_space(3))) void *lds_ptr_t;
+  // K segments: this group's k range starts at kbase.
+  const int kbase = KSEG ? a.kseg[g] : 0;
   auto aload = [&](int k0, int buf) {
-    const uint32_t so = (uint32_t)k0 * 2;
+    const uint32_t so = (uint32_t)(kbase + k0) * 2;
     char *ta = smem + buf * kABytes;
 #pragma unroll
     for (int i = 0; i < MI; ++i)
@@ -183,7 +186,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
                                                aoff[i], so, 0, 0);
   };
   auto bload = [&](int k0, int buf, int half) {
-    const uint32_t so = (uint32_t)k0 * ES;
+    const uint32_t so = (uint32_t)(kbase + k0) * ES;
     char *tb = smem + 2 * kABytes + buf * kBBytes;
     if constexpr (FP8) {
       // GLU: rows 0-127 gate, 128-255 up.
@@ -265,7 +268,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
   // MFMAs: B(kt+2) during sub-steps 0-1 of step kt (buffer (kt+2) % 3 was
   // released by the barrier ending step kt-1), A(kt+2) during sub-step 3
   // after step kt's barrier.  Before a barrier only B(kt+2) may still fly.
-  const int KT = a.K / BK;
+  const int KT = (KSEG ? a.kseg[g + 1] - a.kseg[g] : a.K) / BK;
   aload(0, 0);
   bload(0, 0, 0);
   bload(0, 0, 1);
@@ -386,7 +389,22 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
     if (r >= mrows) continue;
     const int64_t orow = (a.mode == GM_DENSE) ? (int64_t)g * a.out_group_stride + m0 + r
                                               : seg0 + m0 + r;
-    if constexpr (EPI == EP_GLU) {
+    if constexpr (EPI == EP_GU) {
+      // Gate and up sums, each rounded to bf16.
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t col = n_tile * 128 + wn * 32 + 8 * q + 4 * khalf;
+        if (col >= a.ncols) continue;
+        uint2 pg, pu;
+        pg.x = pack_bf16x2_hw(acc[i][0][4 * q], acc[i][0][4 * q + 1]);
+        pg.y = pack_bf16x2_hw(acc[i][0][4 * q + 2], acc[i][0][4 * q + 3]);
+        pu.x = pack_bf16x2_hw(acc[i][1][4 * q], acc[i][1][4 * q + 1]);
+        pu.y = pack_bf16x2_hw(acc[i][1][4 * q + 2], acc[i][1][4 * q + 3]);
+        *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(a.out) + orow * a.ldo + col) = pg;
+        *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(a.out2) + orow * a.ldo + col) =
+            pu;
+      }
+    } else if constexpr (EPI == EP_GLU) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int64_t col = n_tile * 128 + wn * 32 + 8 * q + 4 * khalf;
@@ -419,6 +437,28 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
           if constexpr (EPI == EP_F32) {
             *reinterpret_cast<float4 *>(reinterpret_cast<float *>(a.out) + orow * a.ldo + col) =
                 make_float4(v[0], v[1], v[2], v[3]);
+          } else if constexpr (EPI == EP_GLU_BWD) {
+            // v = dH at (orow, col..col+3): the activation's backward with
+            // the recomputed G and U of the same entries.
+            const uint2 gr = *reinterpret_cast<const uint2 *>(a.gsrc + orow * a.ldg + col);
+            const uint2 ur = *reinterpret_cast<const uint2 *>(a.usrc + orow * a.ldg + col);
+            const float gv[4] = {__uint_as_float(gr.x << 16), __uint_as_float(gr.x & 0xFFFF0000u),
+                                 __uint_as_float(gr.y << 16), __uint_as_float(gr.y & 0xFFFF0000u)};
+            const float uv[4] = {__uint_as_float(ur.x << 16), __uint_as_float(ur.x & 0xFFFF0000u),
+                                 __uint_as_float(ur.y << 16), __uint_as_float(ur.y & 0xFFFF0000u)};
+            float dg[4], du[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              glu_act_backward(gv[e], uv[e], v[e], a.act, a.beta_g, a.beta_u, dg[e], du[e]);
+            uint2 pg, pu;
+            pg.x = pack_bf16x2_hw(dg[0], dg[1]);
+            pg.y = pack_bf16x2_hw(dg[2], dg[3]);
+            pu.x = pack_bf16x2_hw(du[0], du[1]);
+            pu.y = pack_bf16x2_hw(du[2], du[3]);
+            *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(a.out) + orow * a.ldo + col) =
+                pg;
+            *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(a.out2) + orow * a.ldo + col) =
+                pu;
           } else {
             if constexpr (EPI == EP_ADD_BF16) {
               const float4 p0 = *reinterpret_cast<const float4 *>(a.add0 + orow * a.ldo + col);
@@ -468,6 +508,21 @@ __global__ __launch_bounds__(1024) void tile_prefix_kernel(const int32_t *__rest
 // kernel instance is referenced from a non-template function.
 hipError_t launch_kernel(const GemmArgs &a, int epi, int bm, int64_t grid, hipStream_t st) {
   const dim3 g(grid), b(kThreads);
+  if (a.kseg != nullptr) {
+    if (epi != EP_F32 || bm != 256) return hipErrorInvalidValue;
+    grouped_gemm_kernel<EP_F32, 256, false, true><<<g, b, 0, st>>>(a);
+    return hipGetLastError();
+  }
+  if (epi == EP_GU || epi == EP_GLU_BWD) {
+    if (epi == EP_GU) {
+      if (bm == 192) grouped_gemm_kernel<EP_GU, 192><<<g, b, 0, st>>>(a);
+      else grouped_gemm_kernel<EP_GU, 256><<<g, b, 0, st>>>(a);
+    } else {
+      if (bm == 192) grouped_gemm_kernel<EP_GLU_BWD, 192><<<g, b, 0, st>>>(a);
+      else grouped_gemm_kernel<EP_GLU_BWD, 256><<<g, b, 0, st>>>(a);
+    }
+    return hipGetLastError();
+  }
   if (a.bscale != nullptr) {
     if (epi != EP_GLU && epi != EP_F32) return hipErrorInvalidValue;
     if (epi == EP_GLU) {
@@ -520,7 +575,8 @@ hipError_t launch_tile_prefix(const int32_t *kept_offsets, int G, int bm, int32_
 
 hipError_t launch_gemm(const GemmArgs &a, int epi, int64_t mtiles_bound, hipStream_t st) {
   const int bm = a.bm == 192 ? 192 : 256;
-  const int64_t NT = (epi == EP_GLU) ? (a.ncols + 127) / 128 : (a.ncols + BN - 1) / BN;
+  const int64_t NT = (epi == EP_GLU || epi == EP_GU) ? (a.ncols + 127) / 128
+                                                      : (a.ncols + BN - 1) / BN;
   int64_t tiles;
   if (a.mode == GM_DENSE) tiles = (int64_t)a.G * ((a.M_dense + bm - 1) / bm) * NT;
   else tiles = mtiles_bound * NT;

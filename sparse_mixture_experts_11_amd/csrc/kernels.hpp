@@ -42,7 +42,10 @@ hipError_t launch_small_tail(const float *part_p, const int32_t *part_cnt, int w
 
 // ---- grouped GEMM on bf16 MFMA (gemm.hip) -----------------------------------
 enum GemmMode { GM_GATHER = 0, GM_SEGMENT = 1, GM_DENSE = 2 };
-enum GemmEpi { EP_GLU = 0, EP_F32 = 1, EP_BF16 = 2, EP_ADD_BF16 = 3 };
+// EP_GU (backward): the GLU tile's gate and up sums stored as bf16 (out,
+// out2).  EP_GLU_BWD (backward): the product is dH; with G = gsrc, U = usrc
+// ([rows][ncols] bf16, row stride ldo / 2) it stores dG to out and dU to out2.
+enum GemmEpi { EP_GLU = 0, EP_F32 = 1, EP_BF16 = 2, EP_ADD_BF16 = 3, EP_GU = 4, EP_GLU_BWD = 5 };
 
 struct GemmArgs {
   // A: rows of K bf16 values, row stride lda (elements).
@@ -72,6 +75,14 @@ struct GemmArgs {
   int act;                    // 0 SwiGLU, 1 SiTU-GLU
   float beta_g, beta_u;
   int bm;                     // m-tile height: 192, else 256
+  void *out2;                 // EP_GU: up sums; EP_GLU_BWD: dU
+  const uint16_t *gsrc, *usrc;  // EP_GLU_BWD: G and U
+  int64_t ldg;                // EP_GLU_BWD: row stride of G and U (elements)
+  // K segments (dense tiles, every group's own k range): group g reduces over
+  // k in [kseg[g], kseg[g+1]) (multiples of 128, at least 128), B rows have
+  // stride ldb.  Used with EP_F32 for the experts' weight gradients.
+  const int32_t *kseg;
+  int64_t ldb;
 };
 // m-tile height for groups of about rows_per_group rows (192 or 256).
 int gemm_pick_bm(double rows_per_group);
@@ -99,6 +110,22 @@ hipError_t launch_route_backward(const float *logits, int64_t T, int N, int k, i
                                  const uint16_t *dy, const float *stats, float aux_coef,
                                  const uint16_t *u, const uint16_t *w_route, float *part,
                                  float *dz, float *dw, float *du, hipStream_t st);
+
+// ---- the experts' backward helpers (experts_bwd.hip) -------------------------
+hipError_t launch_bwd_gather_dy(const uint16_t *dy, int64_t T, int d, int k,
+                                const int32_t *row_of, const float *topk_w, uint16_t *dy_perm,
+                                hipStream_t st);
+hipError_t launch_transpose_bf16(const uint16_t *src, int B, int R, int C, uint16_t *dst,
+                                 int64_t ld, int col0, hipStream_t st);
+hipError_t launch_kseg(const int32_t *kept_offsets, int G, int32_t *kseg, hipStream_t st);
+hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t st);
+hipError_t launch_seg_transpose(const uint16_t *src, const uint16_t *src2, int64_t lds,
+                                int width, int64_t rows_bound, const int32_t *kept_offsets,
+                                const int32_t *offsets, const int32_t *perm, int kslots,
+                                const int32_t *kseg, int G, int act, float bg, float bu,
+                                uint16_t *dst, int64_t ld, hipStream_t st);
+hipError_t launch_rows_sum(const float *rows, int64_t T, int d, int k, const int32_t *row_of,
+                           float *dx, hipStream_t st);
 
 // ---- decode-sized experts (decode.hip) -------------------------------------
 // Max rows per expert the decode kernels take.

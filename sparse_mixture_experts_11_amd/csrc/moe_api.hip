@@ -180,6 +180,56 @@ moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ER
     if (e_ != hipSuccess) return MOE_ERR_HIP;  \
   } while (0)
 
+// ---- the experts' backward: its own workspace ---------------------------------
+struct BwdLayout {
+  size_t tile_start, kseg, dy_perm, g, u, dgu, dx_perm, wdt, wgut, dyt, ht, xt, dgt, dut;
+  int64_t R, Rpad;
+  size_t total;
+};
+
+BwdLayout bwd_layout(const moe_desc_t &d) {
+  BwdLayout L;
+  memset(&L, 0, sizeof(L));
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align256(bytes);
+    return o;
+  };
+  const size_t R = (size_t)kept_rows_bound(d), N = d.N, D = d.d, H = d.h;
+  const size_t Rpad = R + 128 * N;  // each expert's rows padded to 128, at least 128
+  L.R = (int64_t)R;
+  L.Rpad = (int64_t)Rpad;
+  L.tile_start = take((N + 1) * 4);
+  L.kseg = take((N + 1) * 4);
+  L.dy_perm = take(R * D * 2);
+  L.g = take(R * H * 2);
+  L.u = take(R * H * 2);
+  L.dgu = take(R * 2 * H * 2);
+  L.dx_perm = take(R * D * 4);
+  L.wdt = take(N * H * D * 2);
+  L.wgut = take(N * D * 2 * H * 2);
+  L.dyt = take(D * Rpad * 2);
+  L.ht = take(H * Rpad * 2);
+  L.xt = take(D * Rpad * 2);
+  L.dgt = take(H * Rpad * 2);
+  L.dut = take(H * Rpad * 2);
+  L.total = off;
+  return L;
+}
+
+// What the experts' backward supports: plain layers, bf16 activations and
+// bf16 expert weights, 32-bit offsets into its transposed operands.
+moe_status_t bwd_supported(const moe_desc_t &d) {
+  if (is_latent(d) || d.act_dtype != MOE_BF16 || d.w_dtype != MOE_BF16)
+    return MOE_ERR_UNSUPPORTED;
+  const uint64_t R = (uint64_t)kept_rows_bound(d), Rpad = R + 128ull * d.N;
+  const uint64_t wmax = (uint64_t)(d.d > d.h ? d.d : d.h);
+  if (wmax * Rpad * 2 >= k4G || R * 2ull * d.h * 2 >= k4G || 2ull * d.h * d.d * 2 >= k4G)
+    return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
 // ---- stages (no validation; callers validated) ------------------------------
 
 hipError_t do_route(const moe_desc_t &d, const Layout &L, const void *u, const void *W_route,
@@ -559,6 +609,178 @@ moe_status_t moe_qb_update(const moe_desc_t *desc, const void *u, const void *W_
                      d.N, EP_F32, nullptr, nullptr, 0, st));
   return hip_status(launch_qb_update(logits, d.T, d.N, d.k, bias, (int)qq, method,
                                      region<float>(ws, L.qb_req), new_bias, st));
+}
+
+moe_status_t moe_backward_workspace_bytes(const moe_desc_t *desc, size_t *bytes) {
+  if (bytes == nullptr) return MOE_ERR_ARG;
+  *bytes = 0;
+  const moe_status_t v = validate(desc);
+  if (v != MOE_OK) return v;
+  const moe_status_t s = bwd_supported(*desc);
+  if (s != MOE_OK) return s;
+  *bytes = bwd_layout(*desc).total;
+  return MOE_OK;
+}
+
+moe_status_t moe_experts_backward(const moe_desc_t *desc, const moe_weights_t *wts, const void *u,
+                                  const float *topk_w, const int32_t *offsets,
+                                  const int32_t *kept_offsets, const int32_t *perm,
+                                  const int32_t *row_of, const void *dy, float *dx,
+                                  float *dW_gate, float *dW_up, float *dW_down, void *ws,
+                                  size_t ws_bytes, moe_stream_t stream) {
+  const moe_status_t v = validate(desc);
+  if (v != MOE_OK) return v;
+  const moe_desc_t &d = *desc;
+  if (wts == nullptr || wts->W_gate == nullptr || wts->W_up == nullptr ||
+      wts->W_down == nullptr || u == nullptr || topk_w == nullptr || offsets == nullptr ||
+      kept_offsets == nullptr || perm == nullptr || row_of == nullptr || dy == nullptr ||
+      dx == nullptr)
+    return MOE_ERR_ARG;
+  const bool any_w = dW_gate || dW_up || dW_down, all_w = dW_gate && dW_up && dW_down;
+  if (any_w && !all_w) return MOE_ERR_ARG;
+  const moe_status_t s = bwd_supported(d);
+  if (s != MOE_OK) return s;
+  const BwdLayout L = bwd_layout(d);
+  if (ws == nullptr || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int bm = routed_bm(d);
+  const int64_t mt = gemm_mtile_bound(L.R, d.N, bm);
+  int32_t *tile_start = region<int32_t>(ws, L.tile_start);
+  uint16_t *dy_perm = region<uint16_t>(ws, L.dy_perm);
+  uint16_t *G = region<uint16_t>(ws, L.g), *U = region<uint16_t>(ws, L.u);
+  uint16_t *dgu = region<uint16_t>(ws, L.dgu);
+  float *dx_perm = region<float>(ws, L.dx_perm);
+  uint16_t *wdt = region<uint16_t>(ws, L.wdt), *wgut = region<uint16_t>(ws, L.wgut);
+  const uint16_t *Wg = static_cast<const uint16_t *>(wts->W_gate);
+  const uint16_t *Wu = static_cast<const uint16_t *>(wts->W_up);
+  const uint16_t *Wd = static_cast<const uint16_t *>(wts->W_down);
+  MOE_TRY(launch_tile_prefix(kept_offsets, d.N, bm, tile_start, st));
+  // dY = a dy_t per kept row.
+  MOE_TRY(launch_bwd_gather_dy(static_cast<const uint16_t *>(dy), d.T, d.d, d.k, row_of, topk_w,
+                               dy_perm, st));
+  // G, U recomputed (bf16).
+  {
+    GemmArgs a;
+    memset(&a, 0, sizeof(a));
+    a.A = static_cast<const uint16_t *>(u);
+    a.lda = d.d;
+    a.B = Wg;
+    a.B2 = Wu;
+    a.strideB = (int64_t)d.h * d.d;
+    a.K = d.d;
+    a.ncols = d.h;
+    a.mode = GM_GATHER;
+    a.G = d.N;
+    a.kslots = d.k;
+    a.perm = perm;
+    a.offsets = offsets;
+    a.kept_offsets = kept_offsets;
+    a.tile_start = tile_start;
+    a.out = G;
+    a.out2 = U;
+    a.ldo = d.h;
+    a.bm = bm;
+    MOE_TRY(launch_gemm(a, EP_GU, mt, st));
+  }
+  // K-contiguous copies: W_down^T [N][h][d]; [W_gate^T | W_up^T] [N][d][2h].
+  MOE_TRY(launch_transpose_bf16(Wd, d.N, d.d, d.h, wdt, d.d, 0, st));
+  MOE_TRY(launch_transpose_bf16(Wg, d.N, d.h, d.d, wgut, 2 * (int64_t)d.h, 0, st));
+  MOE_TRY(launch_transpose_bf16(Wu, d.N, d.h, d.d, wgut, 2 * (int64_t)d.h, d.h, st));
+  // dH = W_down^T dY, and in the epilogue (dG, dU) = act'(G, U) dH.
+  {
+    GemmArgs a;
+    memset(&a, 0, sizeof(a));
+    a.A = dy_perm;
+    a.lda = d.d;
+    a.B = wdt;
+    a.strideB = (int64_t)d.h * d.d;
+    a.K = d.d;
+    a.ncols = d.h;
+    a.mode = GM_SEGMENT;
+    a.G = d.N;
+    a.kept_offsets = kept_offsets;
+    a.tile_start = tile_start;
+    a.out = dgu;
+    a.out2 = dgu + d.h;
+    a.ldo = 2 * (int64_t)d.h;
+    a.gsrc = G;
+    a.usrc = U;
+    a.ldg = d.h;
+    a.act = d.act;
+    a.beta_g = d.beta_g;
+    a.beta_u = d.beta_u;
+    a.bm = bm;
+    MOE_TRY(launch_gemm(a, EP_GLU_BWD, mt, st));
+  }
+  // dx rows = [dG | dU] [W_gate ; W_up], then summed per token.
+  {
+    GemmArgs a;
+    memset(&a, 0, sizeof(a));
+    a.A = dgu;
+    a.lda = 2 * (int64_t)d.h;
+    a.B = wgut;
+    a.strideB = (int64_t)d.d * 2 * d.h;
+    a.K = 2 * d.h;
+    a.ncols = d.d;
+    a.mode = GM_SEGMENT;
+    a.G = d.N;
+    a.kept_offsets = kept_offsets;
+    a.tile_start = tile_start;
+    a.out = dx_perm;
+    a.ldo = d.d;
+    a.bm = bm;
+    MOE_TRY(launch_gemm(a, EP_F32, mt, st));
+  }
+  MOE_TRY(launch_rows_sum(dx_perm, d.T, d.d, d.k, row_of, dx, st));
+  if (!all_w) return MOE_OK;
+  // Weight gradients: per-expert K segments over the expert's own rows.
+  int32_t *kseg = region<int32_t>(ws, L.kseg);
+  uint16_t *dyt = region<uint16_t>(ws, L.dyt), *ht = region<uint16_t>(ws, L.ht);
+  uint16_t *xt = region<uint16_t>(ws, L.xt), *dgt = region<uint16_t>(ws, L.dgt);
+  uint16_t *dut = region<uint16_t>(ws, L.dut);
+  const int64_t Rp = L.Rpad;
+  MOE_TRY(launch_kseg(kept_offsets, d.N, kseg, st));
+  MOE_TRY(launch_fill_zero(dyt, (size_t)d.d * Rp * 2, st));
+  MOE_TRY(launch_fill_zero(ht, (size_t)d.h * Rp * 2, st));
+  MOE_TRY(launch_fill_zero(xt, (size_t)d.d * Rp * 2, st));
+  MOE_TRY(launch_fill_zero(dgt, (size_t)d.h * Rp * 2, st));
+  MOE_TRY(launch_fill_zero(dut, (size_t)d.h * Rp * 2, st));
+  MOE_TRY(launch_seg_transpose(dy_perm, nullptr, d.d, d.d, L.R, kept_offsets, offsets, nullptr,
+                               d.k, kseg, d.N, 0, 1.f, 1.f, dyt, Rp, st));
+  MOE_TRY(launch_seg_transpose(G, U, d.h, d.h, L.R, kept_offsets, offsets, nullptr, d.k, kseg,
+                               d.N, d.act, d.beta_g, d.beta_u, ht, Rp, st));
+  MOE_TRY(launch_seg_transpose(static_cast<const uint16_t *>(u), nullptr, d.d, d.d, L.R,
+                               kept_offsets, offsets, perm, d.k, kseg, d.N, 0, 1.f, 1.f, xt, Rp,
+                               st));
+  MOE_TRY(launch_seg_transpose(dgu, nullptr, 2 * (int64_t)d.h, d.h, L.R, kept_offsets, offsets,
+                               nullptr, d.k, kseg, d.N, 0, 1.f, 1.f, dgt, Rp, st));
+  MOE_TRY(launch_seg_transpose(dgu + d.h, nullptr, 2 * (int64_t)d.h, d.h, L.R, kept_offsets,
+                               offsets, nullptr, d.k, kseg, d.N, 0, 1.f, 1.f, dut, Rp, st));
+  auto kseg_gemm = [&](const uint16_t *A, int M, const uint16_t *B, int ncols, float *out) {
+    GemmArgs a;
+    memset(&a, 0, sizeof(a));
+    a.A = A;
+    a.lda = Rp;
+    a.B = B;
+    a.strideB = 0;
+    a.K = 128;  // the k range comes from kseg
+    a.ncols = ncols;
+    a.mode = GM_DENSE;
+    a.G = d.N;
+    a.M_dense = M;
+    a.a_group_rows = 0;
+    a.out = out;
+    a.ldo = ncols;
+    a.out_group_stride = M;
+    a.kseg = kseg;
+    a.ldb = Rp;
+    a.bm = 256;
+    return launch_gemm(a, EP_F32, 0, st);
+  };
+  MOE_TRY(kseg_gemm(dyt, d.d, ht, d.h, dW_down));
+  MOE_TRY(kseg_gemm(dgt, d.h, xt, d.d, dW_gate));
+  MOE_TRY(kseg_gemm(dut, d.h, xt, d.d, dW_up));
+  return MOE_OK;
 }
 
 moe_status_t moe_route_backward(const moe_desc_t *desc, const void *u, const void *W_route,

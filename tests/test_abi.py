@@ -252,3 +252,28 @@ def test_route_backward_validates():
     assert rb(*args(H.desc_for(C.LATENT))) == L.MOE_ERR_UNSUPPORTED     # plain layers only
     assert rb(*args(H.desc_for(C.TINY))) == L.MOE_ERR_UNSUPPORTED       # bf16 only
     assert rb(*args(H.desc_for(C.MCU_BATCH))) == L.MOE_ERR_UNSUPPORTED  # fp32 router
+
+
+def test_experts_backward_validates():
+    lib = L.load()
+    eb = lib.moe_experts_backward
+    n = None
+    big = 1 << 40
+    d = good()
+    assert moe.moe_backward_workspace_bytes(d) > moe.moe_workspace_bytes(d)
+    w = L.MoeWeights(*([4096] * 4 + [None] * 9))
+
+    def call(desc, wts=w, **kw):
+        ptrs = [kw.get(a, FAKE) for a in ("u", "tw", "off", "koff", "perm", "row", "dy", "dx",
+                                          "dwg", "dwu", "dwd")]
+        return eb(ctypes.byref(desc), ctypes.byref(wts), *ptrs, FAKE, kw.get("ws", big), n)
+    assert call(d, ws=10) == L.MOE_ERR_WORKSPACE
+    for a in ("u", "tw", "off", "koff", "perm", "row", "dy", "dx"):
+        assert call(d, **{a: n}) == L.MOE_ERR_ARG, a
+    assert call(d, dwg=n, dwu=n, dwd=n, ws=10) == L.MOE_ERR_WORKSPACE   # input gradient only
+    assert call(d, dwu=n) == L.MOE_ERR_ARG                              # all three or none
+    assert call(d, L.MoeWeights(*([4096] * 3 + [None] * 10))) == L.MOE_ERR_ARG
+    assert call(H.desc_for(C.LATENT)) == L.MOE_ERR_UNSUPPORTED
+    assert call(H.desc_for(C.MIXTRAL_PREFILL_FP8)) == L.MOE_ERR_UNSUPPORTED
+    with pytest.raises(moe.MoeError):
+        moe.moe_backward_workspace_bytes(H.desc_for(C.LATENT))

@@ -1,0 +1,120 @@
+"""The experts' backward on the GPU (moe_experts_backward) against the fp64
+oracle's experts_backward, on the same inputs: the oracle's routing, weights
+(rounded to fp32, as the library takes them) and dispatch, and a seeded
+upstream gradient dy.  Input gradient dx and the weight gradients dW_gate,
+dW_up, dW_down; SwiGLU and SiTU-GLU, both m-tile heights, capacity drops,
+h below one 256-column tile, and dx at the full Mixtral prefill shape on
+sampled tokens."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import sparse_mixture_experts_11_amd as moe
+import synth as S
+from synth import configs as C
+from tests import harness as H
+from tests import parity as PR
+from tests.test_gpu_parity import CASES, MIX_S, log, oracle_capacity, sample_tokens
+
+pytestmark = pytest.mark.gpu
+
+EB_CASES = {
+    "mixtral_small_t1000": CASES["mixtral_small_t1000"],             # 256-row m-tiles
+    "mixtral_small_t1200_bm192": CASES["mixtral_small_t1200_bm192"],  # 192-row m-tiles
+    "switch_small_t2000": CASES["switch_small_t2000"],               # k=1 prob, drops
+    "mix_situ_t900": MIX_S.with_(name="mix_situ_t900", T=900, act="situ", beta_g=2.0,
+                                 beta_u=3.0),
+    "mcu_t4096": CASES["mcu_t4096"],                                 # h = 128
+}
+
+
+def gpu_inputs(cfg, seed=41):
+    u64 = O.expand(cfg.u())
+    r = O.route(u64, O.expand(cfg.w_route()), cfg.k, cfg.gate)
+    disp = O.dispatch(r["idx"], cfg.N, oracle_capacity(cfg))
+    a32 = S.round_to(r["a"], "f32")
+    dy_st = S.normal_stored(seed, 95, cfg.T * cfg.d, 0.5, "bf16").reshape(cfg.T, cfg.d)
+    return u64, r, disp, a32, dy_st
+
+
+def run_gpu(cfg, disp, a32, dy_st, weights=True):
+    desc = H.desc_for(cfg)
+    w = H.upload_layer(cfg)
+    i32 = lambda x: H.to_device(np.asarray(x).astype(np.int32))  # noqa: E731
+    dx = torch.full((cfg.T, cfg.d), float("nan"), device="cuda")
+    dW = {}
+    if weights:
+        dW = {"dW_gate": torch.full((cfg.N, cfg.h, cfg.d), float("nan"), device="cuda"),
+              "dW_up": torch.full((cfg.N, cfg.h, cfg.d), float("nan"), device="cuda"),
+              "dW_down": torch.full((cfg.N, cfg.d, cfg.h), float("nan"), device="cuda")}
+    moe.moe_experts_backward(desc, w, H.to_device(cfg.u()), H.to_device(a32.reshape(-1)),
+                             i32(disp["offsets"]), i32(disp["kept_offsets"]), i32(disp["perm"]),
+                             i32(disp["row_of"]), H.to_device(dy_st), dx,
+                             moe.backward_workspace(desc), **dW)
+    torch.cuda.synchronize()
+    return H.to_host(dx).astype(np.float64), {k: H.to_host(v).astype(np.float64)
+                                              for k, v in dW.items()}
+
+
+@pytest.mark.parametrize("name", list(EB_CASES))
+def test_experts_backward_parity(name):
+    cfg = EB_CASES[name]
+    log(f"[experts backward] {name} T={cfg.T} d={cfg.d} h={cfg.h} N={cfg.N} k={cfg.k} "
+        f"act={cfg.act}")
+    u64, r, disp, a32, dy_st = gpu_inputs(cfg)
+    ref = O.experts_backward(u64, disp, O.expand(a32), lambda e: cfg.expert(e),
+                             O.expand(dy_st), act=cfg.act, k=cfg.k, beta_g=cfg.beta_g,
+                             beta_u=cfg.beta_u)
+    dx, dW = run_gpu(cfg, disp, a32, dy_st)
+    errs = {"dx": PR.rel_err(dx, ref["dx"])}
+    for key in ("dW_gate", "dW_up", "dW_down"):
+        errs[key] = PR.rel_err(dW[key], ref[key])
+    log("  " + ", ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+    assert max(errs.values()) <= PR.TOL["bf16"]
+    # experts that kept no row get exact zeros
+    empty = np.flatnonzero(np.diff(disp["kept_offsets"]) == 0)
+    for e in empty:
+        assert not np.any(dW["dW_down"][e]) and not np.any(dW["dW_gate"][e])
+
+
+def test_experts_backward_input_gradient_only():
+    cfg = EB_CASES["mixtral_small_t1000"]
+    log("[experts backward] dx only")
+    u64, r, disp, a32, dy_st = gpu_inputs(cfg)
+    ref = O.experts_backward(u64, disp, O.expand(a32), lambda e: cfg.expert(e),
+                             O.expand(dy_st), act=cfg.act, k=cfg.k)
+    dx, _ = run_gpu(cfg, disp, a32, dy_st, weights=False)
+    assert PR.rel_err(dx, ref["dx"]) <= PR.TOL["bf16"]
+
+
+@pytest.mark.timeout(900)
+def test_experts_backward_full_size_mixtral_dx_sampled():
+    cfg = C.MIXTRAL_PREFILL
+    log(f"[experts backward full] {cfg.name}")
+    u64, r, disp, a32, dy_st = gpu_inputs(cfg)
+    tokens = sample_tokens(cfg.T, 12, cfg.seed)
+    # The oracle on the sampled tokens' kept rows only.
+    keep = np.isin(disp["perm"] // cfg.k, tokens)
+    sub = dict(disp)
+    N = cfg.N
+    perm, offs, kept = [], [0], []
+    for e in range(N):
+        lo, n = int(disp["offsets"][e]), int(disp["kept_counts"][e])
+        ent = disp["perm"][lo:lo + n]
+        ent = ent[np.isin(ent // cfg.k, tokens)]
+        perm.append(ent)
+        kept.append(len(ent))
+        offs.append(offs[-1] + len(ent))
+    sub["perm"] = np.concatenate(perm)
+    sub["offsets"] = np.array(offs)
+    sub["kept_counts"] = np.array(kept)
+    sub["counts"] = np.array(kept)
+    ref = O.experts_backward(u64, sub, O.expand(a32), lambda e: cfg.expert(e), O.expand(dy_st),
+                             act=cfg.act, k=cfg.k)
+    dx, _ = run_gpu(cfg, disp, a32, dy_st, weights=False)
+    err = PR.rel_err(dx[tokens], ref["dx"][tokens])
+    log(f"  dx rel err {err:.2e} on {len(tokens)} tokens ({int(keep.sum())} rows)")
+    assert err <= PR.TOL["bf16"]
