@@ -144,7 +144,47 @@ def run_workload(cfg, steps, warmup):
         r["quantile_balancing"] = time_qb(moe, desc, u, w["W_route"], ws, cfg, steps)
         if not cfg.latent:
             r["route_backward"] = time_route_backward(moe, H, desc, u, w, y, out, ws, cfg, steps)
+            if cfg.w_dtype == "bf16":
+                r["experts_backward"] = time_experts_backward(moe, H, desc, u, w, out, cfg,
+                                                              max(3, steps // 4))
     return r
+
+
+def time_experts_backward(moe, H, desc, u, w, out, cfg, steps):
+    """moe_experts_backward (dx and all three weight gradients) after a
+    forward, with a seeded dy; averaged over `steps`.  Algorithmic work:
+    8 GEMM-sized products of R x d x h (gate/up recompute 2, dH 1, dx 2,
+    dW_down 1, dW_gate + dW_up 2), 2 R d h flops each."""
+    import torch
+
+    import synth as S
+
+    kept = int(H.to_host(out["kept_offsets"])[-1])
+    ws = moe.backward_workspace(desc)
+    dy = H.to_device(S.normal_stored(cfg.seed + 1, 95, cfg.T * cfg.d, 0.5, "bf16")
+                     .reshape(cfg.T, cfg.d))
+    dx = torch.empty((cfg.T, cfg.d), dtype=torch.float32, device="cuda")
+    dW = {"dW_gate": torch.empty((cfg.N, cfg.h, cfg.d), dtype=torch.float32, device="cuda"),
+          "dW_up": torch.empty((cfg.N, cfg.h, cfg.d), dtype=torch.float32, device="cuda"),
+          "dW_down": torch.empty((cfg.N, cfg.d, cfg.h), dtype=torch.float32, device="cuda")}
+    args = (desc, w, u, out["topk_w"], out["offsets"], out["kept_offsets"], out["perm"],
+            out["row_of"], dy, dx, ws)
+    moe.moe_experts_backward(*args, **dW)
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(steps):
+        moe.moe_experts_backward(*args, **dW)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    flops = 16.0 * kept * cfg.d * cfg.h
+    del ws, dW
+    return {"ms": ms, "algorithmic_tflop": flops / 1e12,
+            "tflops": flops / (ms / 1e3) / 1e12,
+            "mfma_frac": flops / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
+            "workspace_gb": moe.moe_backward_workspace_bytes(desc) / 1e9}
 
 
 def time_route_backward(moe, H, desc, u, w, y, out, ws, cfg, steps):
@@ -296,6 +336,8 @@ def main():
         line["quantile_balancing"] = r["quantile_balancing"]
     if "route_backward" in r:
         line["route_backward"] = r["route_backward"]
+    if "experts_backward" in r:
+        line["experts_backward"] = r["experts_backward"]
     for key, name in (("decode", args.decode_workload), ("decode_fp8", args.fp8_decode_workload),
                       ("decode_mxfp4", args.mxfp4_decode_workload)):
         if not name:
