@@ -1,5 +1,6 @@
 """MI355X-native sparse mixture-of-experts feed-forward layer: the forward
-pass, the Quantile Balancing bias update and the router backward.
+pass, the Quantile Balancing bias update and the backward pass (router and
+experts).
 
 The compute path is libmoe.so (hand-written HIP for gfx950, C ABI in
 include/moe.h); this package is its thin Python binding.
