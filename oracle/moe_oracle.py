@@ -54,7 +54,10 @@ Readings where the pages are silent (listed again in the design doc):
     elements a byte with the even element in the low nibble;
   * router backward: the selected sets, the expert outputs and f are held
     fixed (piecewise-constant or separate steps); the loss is
-    <dy, y> + aux_scale * L_aux.
+    <dy, y> + aux_scale * L_aux;
+  * LatentMoE backward: the same loss and the same fixed quantities; the
+    router's part takes dr (the gradient at the aggregated r) in place of
+    dy.
 
 Pins (tests/test_oracle_pins.py): the capacity example [10,3,2,1] -> drops
 6/4/0; the balanced/collapsed aux example (1.0000 / 2.8449); the parameter
@@ -77,6 +80,11 @@ central differences of the oracle's own loss; the softmax gradient sums to
 zero per token; a balanced f makes the aux gradient vanish; renorm with
 k = N equals the prob gate.  Experts backward pins: torch autograd of an
 independently written SwiGLU / SiTU-GLU layer (capacity drops included).
+LatentMoE backward pins: torch autograd of an independently written latent
+layer (routing, capacity, SiTU-GLU, RMSNorm, shared experts, aux term);
+unselected experts get exactly zero gradient (the demo's own check); the
+RMSNorm backward against torch's rms_norm under autograd and, with eps = 0,
+orthogonal to r (the norm is scale-free).
 Parity unpinned: the exact SiTU-GLU form, the LatentMoE wiring and the
 Quantile Balancing readings (score, cutoff, q, bins) are readings, pinned
 only through the limits and invariants above.
@@ -657,6 +665,77 @@ def latent_forward(u_st: np.ndarray, w_route_st: np.ndarray, experts: ExpertFn,
         y = y + expert_forward(ux, sg, su, sd, swiglu)
     return {**rt, "disp": disp, "x_l": xl, "r": rsum, "r_norm": rn, "y": y,
             "stats": balance_stats(rt["p"], alpha)}
+
+
+# ---------------------------------------------------------------------------
+# LatentMoE backward  (page "Stable LatentMoE interactive demo": the layer of
+# the width-separation and RMSNorm passages, differentiated; the demo's own
+# check is that only the selected experts receive gradient)
+# ---------------------------------------------------------------------------
+#
+# With n = RMSNorm(r) = r / rho, rho = sqrt(mean(r^2) + eps) per token:
+#   dn_m/dr_j = delta_mj / rho - r_m r_j / (l rho^3), so
+#   dr = (dn - n mean(dn * n)) / rho.
+# The rest is the chain rule through y = W_lup n + sum_j S_j(u),
+# r = sum_kept a E_i(x_l), x_l = W_ldown u; the router's part comes from
+# route_backward with dy replaced by dr and the expert outputs at width l.
+
+
+def rmsnorm_backward(r: np.ndarray, dn: np.ndarray, eps: float) -> np.ndarray:
+    """dr for n = r / sqrt(mean(r^2) + eps) (per row), given dn."""
+    rho = np.sqrt(np.mean(r * r, axis=-1, keepdims=True) + eps)
+    n = r / rho
+    return (dn - n * np.mean(dn * n, axis=-1, keepdims=True)) / rho
+
+
+def latent_backward(u_st: np.ndarray, w_route_st: np.ndarray, experts: ExpertFn,
+                    w_ldown_st: np.ndarray, w_lup_st: np.ndarray, shared: ExpertFn,
+                    n_shared: int, dy: np.ndarray, *, k: int, gate: str = "renorm",
+                    act: str = "situ", capacity: Optional[int] = None, beta_g: float = 4.0,
+                    beta_u: float = 25.0, rms_eps: float = 1e-6, alpha: float = 0.01,
+                    aux_scale: float = 0.0) -> Dict[str, object]:
+    """Gradient of L = <dy, y> + aux_scale L_aux for the LatentMoE layer of
+    latent_forward, with the selected sets, the capacity drops and f held
+    fixed.  Returns du, dz, dW_route, dW_ldown, dW_lup, the routed experts'
+    dW_gate / dW_up / dW_down [N, ...] (zero for an expert with no kept row),
+    the shared experts' dWs_gate / dWs_up / dWs_down, and the intermediates
+    x_l, r, dn, dr."""
+    u = expand(u_st)
+    wr, wld, wlu = expand(w_route_st), expand(w_ldown_st), expand(w_lup_st)
+    N = wr.shape[0]
+    rt = route(u, wr, k, gate)
+    disp = dispatch(rt["idx"], N, capacity)
+    xl = u @ wld.T
+    fn = make_act(act, beta_g, beta_u)
+    rows = expert_rows(xl, disp, experts, fn, k)
+    y_rows = np.zeros((int(disp["kept_offsets"][-1]), wld.shape[0]))
+    for j, v in rows.items():
+        y_rows[j] = v
+    r = combine_rows(y_rows, disp["row_of"], rt["a"])
+    n = rmsnorm(r, rms_eps)
+    dn = dy @ wlu
+    dr = rmsnorm_backward(r, dn, rms_eps)
+    ex = experts_backward(xl, disp, rt["a"], experts, dr, act=act, k=k, beta_g=beta_g,
+                          beta_u=beta_u)
+    rb = route_backward(u, wr, rt["idx"], disp["row_of"], y_rows, dr, gate=gate,
+                        f=balance_stats(rt["p"], alpha)["f"], alpha=alpha, aux_scale=aux_scale)
+    du = rb["du"] + ex["dx"] @ wld
+    dWs_g, dWs_u, dWs_d = [], [], []
+    for j in range(n_shared):
+        sg, su, sd = (expand(w) for w in shared(j))
+        g, v = u @ sg.T, u @ su.T
+        dg, dv = act_backward("swiglu", g, v, dy @ sd)
+        du = du + dg @ sg + dv @ su
+        dWs_d.append(dy.T @ swiglu(g, v))
+        dWs_g.append(dg.T @ u)
+        dWs_u.append(dv.T @ u)
+    out = {"du": du, "dz": rb["dz"], "dW_route": rb["dW_route"], "dW_ldown": ex["dx"].T @ u,
+           "dW_lup": dy.T @ n, "dW_gate": ex["dW_gate"], "dW_up": ex["dW_up"],
+           "dW_down": ex["dW_down"], "x_l": xl, "r": r, "dn": dn, "dr": dr, "dx_l": ex["dx"],
+           "route": rt, "disp": disp, "y_rows": y_rows}
+    if n_shared:
+        out.update(dWs_gate=np.stack(dWs_g), dWs_up=np.stack(dWs_u), dWs_down=np.stack(dWs_d))
+    return out
 
 
 def relative_error(y: np.ndarray, y_ref: np.ndarray) -> float:

@@ -864,3 +864,116 @@ def test_experts_backward_matches_torch_autograd(act, cap):
                            else 0.0, rtol=1e-10, atol=1e-12)
         assert np.allclose(g["dW_down"][e], Wt[e][2].grad.numpy() if Wt[e][2].grad is not None
                            else 0.0, rtol=1e-10, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# LatentMoE backward (page 5: the width-separation, RMSNorm and SiTU-GLU
+# passages, differentiated; the demo checks that only selected experts
+# receive gradient)
+# ---------------------------------------------------------------------------
+
+
+def _latent_case(seed, T=24, d=16, l=12, H=10, N=6, S=2, hs=9):
+    rng = np.random.default_rng(seed)
+    u = rng.standard_normal((T, d))
+    wr = rng.standard_normal((N, d)) / math.sqrt(d)
+    wld = rng.standard_normal((l, d)) / math.sqrt(d)
+    wlu = rng.standard_normal((d, l)) / math.sqrt(l)
+    W = [(rng.standard_normal((H, l)) / math.sqrt(l), rng.standard_normal((H, l)) / math.sqrt(l),
+          rng.standard_normal((l, H)) / math.sqrt(H)) for _ in range(N)]
+    Sw = [(rng.standard_normal((hs, d)) / math.sqrt(d), rng.standard_normal((hs, d)) / math.sqrt(d),
+           rng.standard_normal((d, hs)) / math.sqrt(hs)) for _ in range(S)]
+    dy = rng.standard_normal((T, d))
+    return u, wr, wld, wlu, W, Sw, dy
+
+
+@pytest.mark.parametrize("cap,aux", [(None, 0.0), (7, 0.7)])
+def test_latent_backward_matches_torch_autograd(cap, aux):
+    T, d, l, N, k, S = 24, 16, 12, 6, 2, 2
+    u, wr, wld, wlu, W, Sw, dy = _latent_case(12)
+    bg, bu, eps, alpha = 1.5, 2.0, 1e-3, 0.01
+    g = O.latent_backward(u, wr, lambda e: W[e], wld, wlu, lambda j: Sw[j], S, dy, k=k,
+                          act="situ", capacity=cap, beta_g=bg, beta_u=bu, rms_eps=eps,
+                          alpha=alpha, aux_scale=aux)
+    if cap is not None:
+        assert int(g["disp"]["drop"].sum()) > 0
+    # Independent torch forward: route on u, renormalised top-k, token-order
+    # capacity, experts at width l with SiTU-GLU, RMSNorm, W_lup, shared
+    # SwiGLU experts at width d, and the aux term with f held fixed.
+    leaf = lambda m: torch.tensor(m, requires_grad=True)  # noqa: E731
+    ut, wrt, wldt, wlut = leaf(u), leaf(wr), leaf(wld), leaf(wlu)
+    Wt = [tuple(leaf(m) for m in ws) for ws in W]
+    St = [tuple(leaf(m) for m in ws) for ws in Sw]
+    z = ut @ wrt.T
+    z.retain_grad()
+    p = torch.softmax(z, dim=1)
+    top = torch.topk(p, k, dim=1).indices
+    psel = torch.gather(p, 1, top)
+    a = psel / psel.sum(dim=1, keepdim=True)
+    kept = np.ones((T, k), dtype=bool)
+    if cap is not None:
+        seen = np.zeros(N, dtype=int)
+        for t in range(T):
+            for s in range(k):
+                e = int(top[t, s])
+                kept[t, s] = seen[e] < cap
+                seen[e] += 1
+    xl = ut @ wldt.T
+    rows = []
+    for t in range(T):
+        acc = torch.zeros(l, dtype=torch.float64)
+        for s in range(k):
+            if kept[t, s]:
+                wg, wu, wd = Wt[int(top[t, s])]
+                gg, vv = wg @ xl[t], wu @ xl[t]
+                gg, vv = bg * torch.tanh(gg / bg), bu * torch.tanh(vv / bu)
+                acc = acc + a[t, s] * (wd @ (F.silu(gg) * vv))
+        rows.append(acc)
+    r = torch.stack(rows)
+    y = F.rms_norm(r, (l,), eps=eps) @ wlut.T
+    for sg, su, sd in St:
+        y = y + (F.silu(ut @ sg.T) * (ut @ su.T)) @ sd.T
+    f = torch.tensor(np.bincount(np.argmax(p.detach().numpy(), axis=1), minlength=N) / T)
+    loss = (torch.tensor(dy) * y).sum() + aux * alpha * N * (f * p.mean(dim=0)).sum()
+    loss.backward()
+    close = lambda x, ref: np.allclose(x, 0.0 if ref is None else ref.numpy(),  # noqa: E731
+                                       rtol=1e-9, atol=1e-11)
+    assert close(g["du"], ut.grad)
+    assert close(g["dz"], z.grad)
+    assert close(g["dW_route"], wrt.grad)
+    assert close(g["dW_ldown"], wldt.grad)
+    assert close(g["dW_lup"], wlut.grad)
+    for e in range(N):
+        assert close(g["dW_gate"][e], Wt[e][0].grad)
+        assert close(g["dW_up"][e], Wt[e][1].grad)
+        assert close(g["dW_down"][e], Wt[e][2].grad)
+    for j in range(S):
+        assert close(g["dWs_gate"][j], St[j][0].grad)
+        assert close(g["dWs_up"][j], St[j][1].grad)
+        assert close(g["dWs_down"][j], St[j][2].grad)
+
+
+def test_latent_backward_only_selected_experts_receive_gradient():
+    # 6 tokens, top-1 over 12 experts: at least 6 experts are never selected.
+    u, wr, wld, wlu, W, Sw, dy = _latent_case(13, T=6, N=12)
+    g = O.latent_backward(u, wr, lambda e: W[e], wld, wlu, lambda j: Sw[j], 2, dy, k=1,
+                          act="situ", rms_eps=1e-6)
+    used = set(int(e) for e in g["route"]["idx"].ravel())
+    assert len(used) <= 6
+    for e in range(12):
+        total = sum(float(np.abs(g[n][e]).sum()) for n in ("dW_gate", "dW_up", "dW_down"))
+        assert (total > 0) == (e in used)
+
+
+def test_rmsnorm_backward_against_torch_and_scale_free():
+    rng = np.random.default_rng(14)
+    r = rng.standard_normal((5, 7)) * 3.0
+    dn = rng.standard_normal((5, 7))
+    for eps in (1e-6, 0.3):
+        rt = torch.tensor(r, requires_grad=True)
+        (torch.tensor(dn) * F.rms_norm(rt, (7,), eps=eps)).sum().backward()
+        assert np.allclose(O.rmsnorm_backward(r, dn, eps), rt.grad.numpy(), rtol=1e-12,
+                           atol=1e-14)
+    # eps = 0: RMSNorm(c r) = RMSNorm(r), so the gradient has no component along r.
+    dr = O.rmsnorm_backward(r, dn, 0.0)
+    assert np.max(np.abs((dr * r).sum(axis=1))) < 1e-12
