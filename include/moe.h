@@ -227,10 +227,12 @@ moe_status_t moe_route_backward(const moe_desc_t *desc, const void *u, const voi
                                 float aux_scale, float *dz, float *dW_route, float *du, void *ws,
                                 size_t ws_bytes, moe_stream_t stream);
 
-/* Workspace of moe_experts_backward (its own; larger than the forward's:
-   the recomputed gate/up, dY/dG/dU rows, transposed weight copies and the
-   expert-segmented transposes the weight gradients reduce over).  Returns
-   MOE_ERR_UNSUPPORTED where moe_experts_backward does. */
+/* Workspace of moe_experts_backward (plain layer) or moe_latent_backward
+   (latent layer): its own, larger than the forward's (the recomputed
+   gate/up, dY/dG/dU rows, transposed weight copies and the expert-segmented
+   transposes the weight gradients reduce over; for the latent layer also its
+   per-token rows and the transposed operands of the T-long contractions).
+   Returns MOE_ERR_UNSUPPORTED where those entry points do. */
 moe_status_t moe_backward_workspace_bytes(const moe_desc_t *desc, size_t *bytes);
 
 /* The experts' backward (page "MoE: how sparse activation saves compute",
@@ -251,13 +253,55 @@ moe_status_t moe_backward_workspace_bytes(const moe_desc_t *desc, size_t *bytes)
      ws        moe_backward_workspace_bytes() bytes
    Intermediates are rounded to bf16 where they feed the MFMA GEMMs (dY, G,
    U, dG, dU); every sum is fp32.  Plain layers with bf16 activations and
-   weights only (MOE_ERR_UNSUPPORTED otherwise). */
+   weights only (MOE_ERR_UNSUPPORTED otherwise; moe_latent_backward covers
+   the latent layer). */
 moe_status_t moe_experts_backward(const moe_desc_t *desc, const moe_weights_t *w, const void *u,
                                   const float *topk_w, const int32_t *offsets,
                                   const int32_t *kept_offsets, const int32_t *perm,
                                   const int32_t *row_of, const void *dy, float *dx,
                                   float *dW_gate, float *dW_up, float *dW_down, void *ws,
                                   size_t ws_bytes, moe_stream_t stream);
+
+/* Gradients of the latent layer (device pointers, fp32, row-major; shapes
+   with the weights' at moe_weights_t). */
+typedef struct moe_latent_grads {
+  float *du;                 /* [T, d] */
+  float *dz;                 /* [T, N] gradient at the router logits */
+  float *dW_route;           /* [N, d] */
+  float *dW_ldown;           /* [l, d] */
+  float *dW_lup;             /* [d, l] */
+  float *dW_gate, *dW_up;    /* [N, h, l]; zero for an expert with no kept row */
+  float *dW_down;            /* [N, l, h] */
+  float *dWs_gate, *dWs_up;  /* [n_shared, h_shared, d]; unused if n_shared = 0 */
+  float *dWs_down;           /* [n_shared, d, h_shared] */
+} moe_latent_grads_t;
+
+/* The LatentMoE layer's backward (page "Stable LatentMoE interactive demo":
+   the layer of its width-separation, RMSNorm and SiTU-GLU passages,
+   differentiated): the whole gradient of L = <dy, y> + aux_scale * L_aux
+   with the selected sets, the capacity drops and f held fixed.  With
+   x_l = W_ldown u, r = sum_kept a E_i(x_l), n = r / sqrt(mean(r^2) + eps)
+   and y = W_lup n + sum_j S_j(u):
+     dn = dy W_lup; dW_lup = dy^T n; dr = (dn - n mean(dn * n)) / rms;
+     the routed experts' backward at width l driven by dr (dx_l and their
+     weight gradients, as moe_experts_backward);
+     the router's backward driven by dr and the expert outputs (dz, dW_route
+     and its part of du, as moe_route_backward);
+     du += dx_l W_ldown; dW_ldown = dx_l^T u;
+     each shared expert's backward on u and dy (weight 1 for every token).
+     u        [T, d] bf16, the forward's input
+     fwd      the forward's outputs: topk_idx, topk_w, stats, offsets,
+              kept_offsets, perm, row_of and y_perm [R, l] are required
+     dy       [T, d] bf16
+     g        all of its pointers (the shared ones only when n_shared > 0)
+     ws       moe_backward_workspace_bytes() bytes
+   x_l, dr, n and dx_l are rounded to bf16 where they feed the MFMA GEMMs;
+   every sum is fp32.  bf16 activations, expert weights and router only
+   (MOE_ERR_UNSUPPORTED otherwise, and for a plain layer). */
+moe_status_t moe_latent_backward(const moe_desc_t *desc, const moe_weights_t *w, const void *u,
+                                 const moe_outputs_t *fwd, const void *dy, float aux_scale,
+                                 const moe_latent_grads_t *g, void *ws, size_t ws_bytes,
+                                 moe_stream_t stream);
 
 /* Dispatch: group the T*k (token, slot) entries e = t*k + s by expert in
    token order (sections 3.5, 3.6, 3.8).

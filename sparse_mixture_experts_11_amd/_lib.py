@@ -16,6 +16,7 @@ MOE_ACT_SWIGLU, MOE_ACT_SITU_GLU = 0, 1
 EXPORTS = ("moe_desc_init", "moe_status_string", "moe_workspace_bytes",
            "moe_capacity_from_factor", "moe_route", "moe_route_biased", "moe_qb_update",
            "moe_route_backward", "moe_backward_workspace_bytes", "moe_experts_backward",
+           "moe_latent_backward",
            "moe_dispatch", "moe_expert_ffn", "moe_expert_ffn_scaled",
            "moe_combine",
            "moe_forward", "moe_forward_traced", "moe_stage_name")
@@ -42,6 +43,12 @@ class MoeOutputs(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("topk_idx", "topk_w", "stats", "counts",
                                                 "offsets", "kept_offsets", "perm", "row_of",
                                                 "drop", "y_perm")]
+
+
+class MoeLatentGrads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("du", "dz", "dW_route", "dW_ldown", "dW_lup",
+                                                "dW_gate", "dW_up", "dW_down", "dWs_gate",
+                                                "dWs_up", "dWs_down")]
 
 
 class LibraryMissing(RuntimeError):
@@ -82,6 +89,10 @@ def load() -> ctypes.CDLL:
     lib.moe_backward_workspace_bytes.restype = I32
     lib.moe_experts_backward.argtypes = [D, ctypes.c_void_p] + [P] * 12 + [SZ, P]
     lib.moe_experts_backward.restype = I32
+    lib.moe_latent_backward.argtypes = [D, ctypes.POINTER(MoeWeights), P,
+                                        ctypes.POINTER(MoeOutputs), P, ctypes.c_float,
+                                        ctypes.POINTER(MoeLatentGrads), P, SZ, P]
+    lib.moe_latent_backward.restype = I32
     lib.moe_dispatch.argtypes = [D, P, P, P, P, P, P, P, P, SZ, P]
     lib.moe_dispatch.restype = I32
     lib.moe_expert_ffn.argtypes = [D, P, P, P, P, P, P, P, P, P, SZ, P]

@@ -145,6 +145,22 @@ def moe_experts_backward(desc, weights: Mapping[str, torch.Tensor], u, topk_w, o
                                          ws.numel(), _stream(stream)), "moe_experts_backward")
 
 
+def moe_latent_backward(desc, weights: Mapping[str, torch.Tensor], u,
+                        fwd: Mapping[str, torch.Tensor], dy, grads: Mapping[str, torch.Tensor],
+                        ws, aux_scale: float = 0.0, stream=None) -> None:
+    """grads: du, dz, dW_route, dW_ldown, dW_lup, dW_gate, dW_up, dW_down and,
+    with shared experts, dWs_gate, dWs_up, dWs_down (fp32 tensors)."""
+    w = _weights(weights)
+    g = L.MoeLatentGrads()
+    for name, _ in L.MoeLatentGrads._fields_:
+        t = grads.get(name)
+        setattr(g, name, None if t is None else _ptr(t).value)
+    _check(L.load().moe_latent_backward(ctypes.byref(desc), ctypes.byref(w), _ptr(u),
+                                        _outputs(fwd), _ptr(dy), float(aux_scale),
+                                        ctypes.byref(g), _ptr(ws), ws.numel(), _stream(stream)),
+           "moe_latent_backward")
+
+
 def moe_dispatch(desc, topk_idx, counts, offsets, kept_offsets, perm, row_of, drop, ws,
                  stream=None) -> None:
     _check(L.load().moe_dispatch(ctypes.byref(desc), _ptr(topk_idx), _ptr(counts), _ptr(offsets),

@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 SO = os.path.join(HERE, "libmoe.so")
 SOURCES = ["moe_api.hip", "route.hip", "dispatch.hip", "gemm.hip", "decode.hip", "simt.hip",
-           "combine.hip", "qb.hip", "route_bwd.hip", "experts_bwd.hip"]
+           "combine.hip", "qb.hip", "route_bwd.hip", "experts_bwd.hip", "latent_bwd.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -105,11 +105,12 @@ hipError_t launch_qb_update(const float *logits, int64_t T, int N, int k, const 
 // (through fp32 partials part [chunks][N][d]) and the router's du [T, d].
 // aux_coef = aux_scale * alpha * N / T; stats[0..N) holds f.
 int64_t route_bwd_chunks(int64_t T, int N, int d);
-hipError_t launch_route_backward(const float *logits, int64_t T, int N, int k, int d, int renorm,
-                                 const int32_t *idx, const int32_t *row_of, const float *y_perm,
-                                 const uint16_t *dy, const float *stats, float aux_coef,
-                                 const uint16_t *u, const uint16_t *w_route, float *part,
-                                 float *dz, float *dw, float *du, hipStream_t st);
+// d: width of u and W_route; dyw: width of dy and y_perm (d, or l).
+hipError_t launch_route_backward(const float *logits, int64_t T, int N, int k, int d, int dyw,
+                                 int renorm, const int32_t *idx, const int32_t *row_of,
+                                 const float *y_perm, const uint16_t *dy, const float *stats,
+                                 float aux_coef, const uint16_t *u, const uint16_t *w_route,
+                                 float *part, float *dz, float *dw, float *du, hipStream_t st);
 
 // ---- the experts' backward helpers (experts_bwd.hip) -------------------------
 hipError_t launch_bwd_gather_dy(const uint16_t *dy, int64_t T, int d, int k,
@@ -126,6 +127,20 @@ hipError_t launch_seg_transpose(const uint16_t *src, const uint16_t *src2, int64
                                 uint16_t *dst, int64_t ld, hipStream_t st);
 hipError_t launch_rows_sum(const float *rows, int64_t T, int d, int k, const int32_t *row_of,
                            float *dx, hipStream_t st);
+
+// ---- the LatentMoE backward's per-token steps (latent_bwd.hip) --------------
+// dr = RMSNorm backward at r = sum_kept a y_perm rows, given dn [T, width]
+// fp32; writes dr and n = RMSNorm(r) as bf16 [T, width] (width <= 4096).
+hipError_t launch_rms_backward(const float *y_perm, const int32_t *row_of, const float *topk_w,
+                               int64_t T, int k, int width, float eps, const float *dn,
+                               uint16_t *dr, uint16_t *n_out, hipStream_t st);
+// n % 4 == 0 elements.
+hipError_t launch_cast_bf16(const float *src, int64_t n, uint16_t *dst, hipStream_t st);
+hipError_t launch_add_f32(float *dst, const float *src, int64_t n, hipStream_t st);
+// Every token to each of S experts with weight 1: w [T*S], perm [S*T],
+// row_of [T*S], offsets and kept_offsets [S+1].
+hipError_t launch_shared_route(int64_t T, int S, float *w, int32_t *perm, int32_t *row_of,
+                               int32_t *offsets, int32_t *kept_offsets, hipStream_t st);
 
 // ---- decode-sized experts (decode.hip) -------------------------------------
 // Max rows per expert the decode kernels take.

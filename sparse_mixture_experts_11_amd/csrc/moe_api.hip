@@ -181,52 +181,82 @@ moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ER
   } while (0)
 
 // ---- the experts' backward: its own workspace ---------------------------------
+// One group of experts: N experts of input width w and hidden h, k entries
+// per token, at most R kept rows.  The plain layer's routed experts are one
+// such group; the latent layer has two (routed at width l, shared at d).
+int routed_bm(const moe_desc_t &d);
+
+struct BwdDims {
+  int64_t T, R;
+  int N, k, w, h, act, bm;
+  float bg, bu;
+};
+
+BwdDims routed_dims(const moe_desc_t &d) {
+  return BwdDims{d.T, kept_rows_bound(d), d.N, d.k, xwidth(d), d.h, d.act, routed_bm(d),
+                 d.beta_g, d.beta_u};
+}
+
+// The latent layer's shared experts: every token takes each of them.
+BwdDims shared_dims(const moe_desc_t &d) {
+  return BwdDims{d.T, d.T * d.n_shared, d.n_shared, d.n_shared, d.d, d.h_shared,
+                 MOE_ACT_SWIGLU, gemm_pick_bm((double)d.T), 1.f, 1.f};
+}
+
 struct BwdLayout {
   size_t tile_start, kseg, dy_perm, g, u, dgu, dx_perm, wdt, wgut, dyt, ht, xt, dgt, dut;
-  int64_t R, Rpad;
+  int64_t Rpad;
   size_t total;
 };
 
-BwdLayout bwd_layout(const moe_desc_t &d) {
+BwdLayout bwd_layout(const BwdDims &D, size_t base = 0) {
   BwdLayout L;
   memset(&L, 0, sizeof(L));
-  size_t off = 0;
+  size_t off = base;
   auto take = [&](size_t bytes) {
     const size_t o = off;
     off += align256(bytes);
     return o;
   };
-  const size_t R = (size_t)kept_rows_bound(d), N = d.N, D = d.d, H = d.h;
+  const size_t R = (size_t)D.R, N = D.N, W = D.w, H = D.h;
   const size_t Rpad = R + 128 * N;  // each expert's rows padded to 128, at least 128
-  L.R = (int64_t)R;
   L.Rpad = (int64_t)Rpad;
   L.tile_start = take((N + 1) * 4);
   L.kseg = take((N + 1) * 4);
-  L.dy_perm = take(R * D * 2);
+  L.dy_perm = take(R * W * 2);
   L.g = take(R * H * 2);
   L.u = take(R * H * 2);
   L.dgu = take(R * 2 * H * 2);
-  L.dx_perm = take(R * D * 4);
-  L.wdt = take(N * H * D * 2);
-  L.wgut = take(N * D * 2 * H * 2);
-  L.dyt = take(D * Rpad * 2);
+  L.dx_perm = take(R * W * 4);
+  L.wdt = take(N * H * W * 2);
+  L.wgut = take(N * W * 2 * H * 2);
+  L.dyt = take(W * Rpad * 2);
   L.ht = take(H * Rpad * 2);
-  L.xt = take(D * Rpad * 2);
+  L.xt = take(W * Rpad * 2);
   L.dgt = take(H * Rpad * 2);
   L.dut = take(H * Rpad * 2);
-  L.total = off;
+  L.total = off - base;
   return L;
 }
 
-// What the experts' backward supports: plain layers, bf16 activations and
-// bf16 expert weights, 32-bit offsets into its transposed operands.
+// 32-bit offsets into the group's transposed and row-major operands.
+bool bwd_dims_ok(const BwdDims &D) {
+  const uint64_t R = (uint64_t)D.R, Rpad = R + 128ull * D.N;
+  const uint64_t wmax = (uint64_t)(D.w > D.h ? D.w : D.h);
+  return wmax * Rpad * 2 < k4G && R * 2ull * D.h * 2 < k4G && 2ull * D.h * D.w * 2 < k4G &&
+         R * (uint64_t)D.w * 4 < k4G;
+}
+
+// What the backward supports: bf16 activations, bf16 expert weights (and a
+// bf16 router for the latent layer, whose router backward runs here too),
+// 32-bit offsets into its transposed operands.
 moe_status_t bwd_supported(const moe_desc_t &d) {
-  if (is_latent(d) || d.act_dtype != MOE_BF16 || d.w_dtype != MOE_BF16)
-    return MOE_ERR_UNSUPPORTED;
-  const uint64_t R = (uint64_t)kept_rows_bound(d), Rpad = R + 128ull * d.N;
-  const uint64_t wmax = (uint64_t)(d.d > d.h ? d.d : d.h);
-  if (wmax * Rpad * 2 >= k4G || R * 2ull * d.h * 2 >= k4G || 2ull * d.h * d.d * 2 >= k4G)
-    return MOE_ERR_UNSUPPORTED;
+  if (d.act_dtype != MOE_BF16 || d.w_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (!bwd_dims_ok(routed_dims(d))) return MOE_ERR_UNSUPPORTED;
+  if (is_latent(d)) {
+    if (d.router_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+    if (d.n_shared > 0 && !bwd_dims_ok(shared_dims(d))) return MOE_ERR_UNSUPPORTED;
+  }
   return MOE_OK;
 }
 
@@ -520,6 +550,213 @@ moe_status_t forward_impl(const moe_desc_t *desc, const moe_weights_t *wts, cons
   return MOE_OK;
 }
 
+// The experts' backward for one group of experts (see BwdDims): dx [T, w]
+// fp32 (written, not accumulated) and, when dWg is not null, the three weight
+// gradients.  L's regions are offsets into ws.
+hipError_t experts_bwd_core(const BwdDims &D, const BwdLayout &L, void *ws, const uint16_t *x,
+                            const uint16_t *Wg, const uint16_t *Wu, const uint16_t *Wd,
+                            const float *topk_w, const int32_t *offsets,
+                            const int32_t *kept_offsets, const int32_t *perm,
+                            const int32_t *row_of, const uint16_t *dy, float *dx, float *dWg,
+                            float *dWu, float *dWd, hipStream_t st) {
+  const int bm = D.bm;
+  const int64_t mt = gemm_mtile_bound(D.R, D.N, bm);
+  int32_t *tile_start = region<int32_t>(ws, L.tile_start);
+  uint16_t *dy_perm = region<uint16_t>(ws, L.dy_perm);
+  uint16_t *G = region<uint16_t>(ws, L.g), *U = region<uint16_t>(ws, L.u);
+  uint16_t *dgu = region<uint16_t>(ws, L.dgu);
+  float *dx_perm = region<float>(ws, L.dx_perm);
+  uint16_t *wdt = region<uint16_t>(ws, L.wdt), *wgut = region<uint16_t>(ws, L.wgut);
+  const int64_t W = D.w, H = D.h;
+  hipError_t e;
+#define MOE_BWD_TRY(expr)              \
+  do {                                 \
+    e = (expr);                        \
+    if (e != hipSuccess) return e;     \
+  } while (0)
+  MOE_BWD_TRY(launch_tile_prefix(kept_offsets, D.N, bm, tile_start, st));
+  // dY = a dy_t per kept row.
+  MOE_BWD_TRY(launch_bwd_gather_dy(dy, D.T, D.w, D.k, row_of, topk_w, dy_perm, st));
+  // G, U recomputed (bf16).
+  {
+    GemmArgs a;
+    memset(&a, 0, sizeof(a));
+    a.A = x;
+    a.lda = W;
+    a.B = Wg;
+    a.B2 = Wu;
+    a.strideB = H * W;
+    a.K = D.w;
+    a.ncols = D.h;
+    a.mode = GM_GATHER;
+    a.G = D.N;
+    a.kslots = D.k;
+    a.perm = perm;
+    a.offsets = offsets;
+    a.kept_offsets = kept_offsets;
+    a.tile_start = tile_start;
+    a.out = G;
+    a.out2 = U;
+    a.ldo = H;
+    a.bm = bm;
+    MOE_BWD_TRY(launch_gemm(a, EP_GU, mt, st));
+  }
+  // K-contiguous copies: W_down^T [N][h][w]; [W_gate^T | W_up^T] [N][w][2h].
+  MOE_BWD_TRY(launch_transpose_bf16(Wd, D.N, D.w, D.h, wdt, W, 0, st));
+  MOE_BWD_TRY(launch_transpose_bf16(Wg, D.N, D.h, D.w, wgut, 2 * H, 0, st));
+  MOE_BWD_TRY(launch_transpose_bf16(Wu, D.N, D.h, D.w, wgut, 2 * H, D.h, st));
+  // dH = W_down^T dY, and in the epilogue (dG, dU) = act'(G, U) dH.
+  {
+    GemmArgs a;
+    memset(&a, 0, sizeof(a));
+    a.A = dy_perm;
+    a.lda = W;
+    a.B = wdt;
+    a.strideB = H * W;
+    a.K = D.w;
+    a.ncols = D.h;
+    a.mode = GM_SEGMENT;
+    a.G = D.N;
+    a.kept_offsets = kept_offsets;
+    a.tile_start = tile_start;
+    a.out = dgu;
+    a.out2 = dgu + H;
+    a.ldo = 2 * H;
+    a.gsrc = G;
+    a.usrc = U;
+    a.ldg = H;
+    a.act = D.act;
+    a.beta_g = D.bg;
+    a.beta_u = D.bu;
+    a.bm = bm;
+    MOE_BWD_TRY(launch_gemm(a, EP_GLU_BWD, mt, st));
+  }
+  // dx rows = [dG | dU] [W_gate ; W_up], then summed per token.
+  {
+    GemmArgs a;
+    memset(&a, 0, sizeof(a));
+    a.A = dgu;
+    a.lda = 2 * H;
+    a.B = wgut;
+    a.strideB = W * 2 * H;
+    a.K = 2 * D.h;
+    a.ncols = D.w;
+    a.mode = GM_SEGMENT;
+    a.G = D.N;
+    a.kept_offsets = kept_offsets;
+    a.tile_start = tile_start;
+    a.out = dx_perm;
+    a.ldo = W;
+    a.bm = bm;
+    MOE_BWD_TRY(launch_gemm(a, EP_F32, mt, st));
+  }
+  MOE_BWD_TRY(launch_rows_sum(dx_perm, D.T, D.w, D.k, row_of, dx, st));
+  if (dWg == nullptr) return hipSuccess;
+  // Weight gradients: per-expert K segments over the expert's own rows.
+  int32_t *kseg = region<int32_t>(ws, L.kseg);
+  uint16_t *dyt = region<uint16_t>(ws, L.dyt), *ht = region<uint16_t>(ws, L.ht);
+  uint16_t *xt = region<uint16_t>(ws, L.xt), *dgt = region<uint16_t>(ws, L.dgt);
+  uint16_t *dut = region<uint16_t>(ws, L.dut);
+  const int64_t Rp = L.Rpad;
+  MOE_BWD_TRY(launch_kseg(kept_offsets, D.N, kseg, st));
+  MOE_BWD_TRY(launch_fill_zero(dyt, (size_t)W * Rp * 2, st));
+  MOE_BWD_TRY(launch_fill_zero(ht, (size_t)H * Rp * 2, st));
+  MOE_BWD_TRY(launch_fill_zero(xt, (size_t)W * Rp * 2, st));
+  MOE_BWD_TRY(launch_fill_zero(dgt, (size_t)H * Rp * 2, st));
+  MOE_BWD_TRY(launch_fill_zero(dut, (size_t)H * Rp * 2, st));
+  MOE_BWD_TRY(launch_seg_transpose(dy_perm, nullptr, W, D.w, D.R, kept_offsets, offsets, nullptr,
+                                   D.k, kseg, D.N, 0, 1.f, 1.f, dyt, Rp, st));
+  MOE_BWD_TRY(launch_seg_transpose(G, U, H, D.h, D.R, kept_offsets, offsets, nullptr, D.k, kseg,
+                                   D.N, D.act, D.bg, D.bu, ht, Rp, st));
+  MOE_BWD_TRY(launch_seg_transpose(x, nullptr, W, D.w, D.R, kept_offsets, offsets, perm, D.k,
+                                   kseg, D.N, 0, 1.f, 1.f, xt, Rp, st));
+  MOE_BWD_TRY(launch_seg_transpose(dgu, nullptr, 2 * H, D.h, D.R, kept_offsets, offsets, nullptr,
+                                   D.k, kseg, D.N, 0, 1.f, 1.f, dgt, Rp, st));
+  MOE_BWD_TRY(launch_seg_transpose(dgu + H, nullptr, 2 * H, D.h, D.R, kept_offsets, offsets,
+                                   nullptr, D.k, kseg, D.N, 0, 1.f, 1.f, dut, Rp, st));
+  auto kseg_gemm = [&](const uint16_t *A, int M, const uint16_t *B, int ncols, float *out) {
+    GemmArgs a;
+    memset(&a, 0, sizeof(a));
+    a.A = A;
+    a.lda = Rp;
+    a.B = B;
+    a.strideB = 0;
+    a.K = 128;  // the k range comes from kseg
+    a.ncols = ncols;
+    a.mode = GM_DENSE;
+    a.G = D.N;
+    a.M_dense = M;
+    a.a_group_rows = 0;
+    a.out = out;
+    a.ldo = ncols;
+    a.out_group_stride = M;
+    a.kseg = kseg;
+    a.ldb = Rp;
+    a.bm = 256;
+    return launch_gemm(a, EP_F32, 0, st);
+  };
+  MOE_BWD_TRY(kseg_gemm(dyt, D.w, ht, D.h, dWd));
+  MOE_BWD_TRY(kseg_gemm(dgt, D.h, xt, D.w, dWg));
+  MOE_BWD_TRY(kseg_gemm(dut, D.h, xt, D.w, dWu));
+#undef MOE_BWD_TRY
+  return hipSuccess;
+}
+
+// ---- the latent layer's backward: its workspace ---------------------------------
+// The experts' regions (sized for the larger of the routed and shared
+// groups, used by one then the other) come first, then the latent steps'.
+struct LatBwdLayout {
+  size_t core;                                 // experts' regions, at offset 0
+  size_t xl, dn, dr, nb, wlupt, wldt, dyt, nt;  // latent steps
+  size_t dxl, dxlb, dxlt, ut, tmp, logits, rb_part;
+  size_t sh_w, sh_perm, sh_row, sh_off, sh_koff;
+  int64_t Tp;  // T padded: the K of the T-long contractions
+  size_t total;
+};
+
+LatBwdLayout lat_bwd_layout(const moe_desc_t &d) {
+  LatBwdLayout L;
+  memset(&L, 0, sizeof(L));
+  size_t core = bwd_layout(routed_dims(d)).total;
+  if (d.n_shared > 0) {
+    const size_t cs = bwd_layout(shared_dims(d)).total;
+    if (cs > core) core = cs;
+  }
+  L.core = core;
+  size_t off = align256(core);
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align256(bytes);
+    return o;
+  };
+  const size_t T = (size_t)d.T, l = (size_t)d.l, D = (size_t)d.d, S = (size_t)d.n_shared;
+  const int64_t Tp = ((d.T + 63) / 64) * 64;
+  L.Tp = Tp < 128 ? 128 : Tp;
+  const size_t tp = (size_t)L.Tp;
+  L.xl = take(T * l * 2);
+  L.dn = take(T * l * 4);
+  L.dr = take(T * l * 2);
+  L.nb = take(T * l * 2);
+  L.wlupt = take(l * D * 2);
+  L.wldt = take(D * l * 2);
+  L.dyt = take(D * tp * 2);
+  L.nt = take(l * tp * 2);
+  L.dxl = take(T * l * 4);
+  L.dxlb = take(T * l * 2);
+  L.dxlt = take(l * tp * 2);
+  L.ut = take(D * tp * 2);
+  L.tmp = take(T * D * 4);
+  L.logits = take(T * (size_t)d.N * 4);
+  L.rb_part = take((size_t)route_bwd_chunks(d.T, d.N, d.d) * d.N * d.d * 4);
+  L.sh_w = take(T * S * 4);
+  L.sh_perm = take(T * S * 4);
+  L.sh_row = take(T * S * 4);
+  L.sh_off = take((S + 1) * 4);
+  L.sh_koff = take((S + 1) * 4);
+  L.total = off;
+  return L;
+}
+
 }  // namespace
 
 extern "C" {
@@ -618,7 +855,7 @@ moe_status_t moe_backward_workspace_bytes(const moe_desc_t *desc, size_t *bytes)
   if (v != MOE_OK) return v;
   const moe_status_t s = bwd_supported(*desc);
   if (s != MOE_OK) return s;
-  *bytes = bwd_layout(*desc).total;
+  *bytes = is_latent(*desc) ? lat_bwd_layout(*desc).total : bwd_layout(routed_dims(*desc)).total;
   return MOE_OK;
 }
 
@@ -638,148 +875,125 @@ moe_status_t moe_experts_backward(const moe_desc_t *desc, const moe_weights_t *w
     return MOE_ERR_ARG;
   const bool any_w = dW_gate || dW_up || dW_down, all_w = dW_gate && dW_up && dW_down;
   if (any_w && !all_w) return MOE_ERR_ARG;
+  if (is_latent(d)) return MOE_ERR_UNSUPPORTED;  // moe_latent_backward
   const moe_status_t s = bwd_supported(d);
   if (s != MOE_OK) return s;
-  const BwdLayout L = bwd_layout(d);
+  const BwdDims D = routed_dims(d);
+  const BwdLayout L = bwd_layout(D);
+  if (ws == nullptr || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  return hip_status(experts_bwd_core(
+      D, L, ws, static_cast<const uint16_t *>(u), static_cast<const uint16_t *>(wts->W_gate),
+      static_cast<const uint16_t *>(wts->W_up), static_cast<const uint16_t *>(wts->W_down), topk_w,
+      offsets, kept_offsets, perm, row_of, static_cast<const uint16_t *>(dy), dx, dW_gate, dW_up,
+      dW_down, reinterpret_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_latent_backward(const moe_desc_t *desc, const moe_weights_t *wts, const void *u,
+                                 const moe_outputs_t *fwd, const void *dy, float aux_scale,
+                                 const moe_latent_grads_t *g, void *ws, size_t ws_bytes,
+                                 moe_stream_t stream) {
+  const moe_status_t v = validate(desc);
+  if (v != MOE_OK) return v;
+  const moe_desc_t &d = *desc;
+  if (!is_latent(d)) return MOE_ERR_UNSUPPORTED;  // moe_route_backward + moe_experts_backward
+  if (wts == nullptr || u == nullptr || fwd == nullptr || dy == nullptr || g == nullptr)
+    return MOE_ERR_ARG;
+  if (wts->W_route == nullptr || wts->W_gate == nullptr || wts->W_up == nullptr ||
+      wts->W_down == nullptr || wts->W_ldown == nullptr || wts->W_lup == nullptr)
+    return MOE_ERR_ARG;
+  if (d.n_shared > 0 &&
+      (wts->Ws_gate == nullptr || wts->Ws_up == nullptr || wts->Ws_down == nullptr))
+    return MOE_ERR_ARG;
+  if (fwd->topk_idx == nullptr || fwd->topk_w == nullptr || fwd->stats == nullptr ||
+      fwd->offsets == nullptr || fwd->kept_offsets == nullptr || fwd->perm == nullptr ||
+      fwd->row_of == nullptr || fwd->y_perm == nullptr)
+    return MOE_ERR_ARG;
+  if (g->du == nullptr || g->dz == nullptr || g->dW_route == nullptr || g->dW_ldown == nullptr ||
+      g->dW_lup == nullptr || g->dW_gate == nullptr || g->dW_up == nullptr ||
+      g->dW_down == nullptr)
+    return MOE_ERR_ARG;
+  if (d.n_shared > 0 && (g->dWs_gate == nullptr || g->dWs_up == nullptr || g->dWs_down == nullptr))
+    return MOE_ERR_ARG;
+  if (!isfinite(aux_scale)) return MOE_ERR_ARG;
+  const moe_status_t s = bwd_supported(d);
+  if (s != MOE_OK) return s;
+  const LatBwdLayout L = lat_bwd_layout(d);
   if (ws == nullptr || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const int bm = routed_bm(d);
-  const int64_t mt = gemm_mtile_bound(L.R, d.N, bm);
-  int32_t *tile_start = region<int32_t>(ws, L.tile_start);
-  uint16_t *dy_perm = region<uint16_t>(ws, L.dy_perm);
-  uint16_t *G = region<uint16_t>(ws, L.g), *U = region<uint16_t>(ws, L.u);
-  uint16_t *dgu = region<uint16_t>(ws, L.dgu);
-  float *dx_perm = region<float>(ws, L.dx_perm);
-  uint16_t *wdt = region<uint16_t>(ws, L.wdt), *wgut = region<uint16_t>(ws, L.wgut);
-  const uint16_t *Wg = static_cast<const uint16_t *>(wts->W_gate);
-  const uint16_t *Wu = static_cast<const uint16_t *>(wts->W_up);
-  const uint16_t *Wd = static_cast<const uint16_t *>(wts->W_down);
-  MOE_TRY(launch_tile_prefix(kept_offsets, d.N, bm, tile_start, st));
-  // dY = a dy_t per kept row.
-  MOE_TRY(launch_bwd_gather_dy(static_cast<const uint16_t *>(dy), d.T, d.d, d.k, row_of, topk_w,
-                               dy_perm, st));
-  // G, U recomputed (bf16).
+  const uint16_t *U = static_cast<const uint16_t *>(u);
+  const uint16_t *DY = static_cast<const uint16_t *>(dy);
+  const uint16_t *Wldown = static_cast<const uint16_t *>(wts->W_ldown);
+  const uint16_t *Wlup = static_cast<const uint16_t *>(wts->W_lup);
+  const int64_t T = d.T, Tp = L.Tp;
+  const int l = d.l, D = d.d;
+  uint16_t *xl = region<uint16_t>(ws, L.xl), *dr = region<uint16_t>(ws, L.dr);
+  uint16_t *nb = region<uint16_t>(ws, L.nb), *wlupt = region<uint16_t>(ws, L.wlupt);
+  uint16_t *wldt = region<uint16_t>(ws, L.wldt), *dyt = region<uint16_t>(ws, L.dyt);
+  uint16_t *nt = region<uint16_t>(ws, L.nt), *dxlb = region<uint16_t>(ws, L.dxlb);
+  uint16_t *dxlt = region<uint16_t>(ws, L.dxlt), *ut = region<uint16_t>(ws, L.ut);
+  float *dn = region<float>(ws, L.dn), *dxl = region<float>(ws, L.dxl);
+  float *tmp = region<float>(ws, L.tmp), *logits = region<float>(ws, L.logits);
+  // x_l = W_ldown u, recomputed as the forward rounded it.
+  MOE_TRY(dense_gemm(U, D, 0, Wldown, nullptr, 0, D, l, 1, T, xl, l, EP_BF16, nullptr, nullptr, 0,
+                     st));
+  // dn = dy W_lup (W_lup^T as the K-contiguous operand), then dr and n.
+  MOE_TRY(launch_transpose_bf16(Wlup, 1, D, l, wlupt, D, 0, st));
+  MOE_TRY(dense_gemm(DY, D, 0, wlupt, nullptr, 0, D, l, 1, T, dn, l, EP_F32, nullptr, nullptr, 0,
+                     st));
+  MOE_TRY(launch_rms_backward(fwd->y_perm, fwd->row_of, fwd->topk_w, T, d.k, l, d.rms_eps, dn, dr,
+                              nb, st));
+  // dW_lup = dy^T n: a contraction over the tokens (both operands transposed,
+  // T padded with zeros).
+  MOE_TRY(launch_fill_zero(dyt, (size_t)D * Tp * 2, st));
+  MOE_TRY(launch_fill_zero(nt, (size_t)l * Tp * 2, st));
+  MOE_TRY(launch_transpose_bf16(DY, 1, (int)T, D, dyt, Tp, 0, st));
+  MOE_TRY(launch_transpose_bf16(nb, 1, (int)T, l, nt, Tp, 0, st));
+  MOE_TRY(dense_gemm(dyt, Tp, 0, nt, nullptr, 0, (int)Tp, l, 1, D, g->dW_lup, l, EP_F32, nullptr,
+                     nullptr, 0, st));
+  // The routed experts at width l, driven by dr.
   {
-    GemmArgs a;
-    memset(&a, 0, sizeof(a));
-    a.A = static_cast<const uint16_t *>(u);
-    a.lda = d.d;
-    a.B = Wg;
-    a.B2 = Wu;
-    a.strideB = (int64_t)d.h * d.d;
-    a.K = d.d;
-    a.ncols = d.h;
-    a.mode = GM_GATHER;
-    a.G = d.N;
-    a.kslots = d.k;
-    a.perm = perm;
-    a.offsets = offsets;
-    a.kept_offsets = kept_offsets;
-    a.tile_start = tile_start;
-    a.out = G;
-    a.out2 = U;
-    a.ldo = d.h;
-    a.bm = bm;
-    MOE_TRY(launch_gemm(a, EP_GU, mt, st));
+    const BwdDims Dr = routed_dims(d);
+    const BwdLayout Lr = bwd_layout(Dr);
+    MOE_TRY(experts_bwd_core(Dr, Lr, ws, xl, static_cast<const uint16_t *>(wts->W_gate),
+                             static_cast<const uint16_t *>(wts->W_up),
+                             static_cast<const uint16_t *>(wts->W_down), fwd->topk_w,
+                             fwd->offsets, fwd->kept_offsets, fwd->perm, fwd->row_of, dr, dxl,
+                             g->dW_gate, g->dW_up, g->dW_down, st));
   }
-  // K-contiguous copies: W_down^T [N][h][d]; [W_gate^T | W_up^T] [N][d][2h].
-  MOE_TRY(launch_transpose_bf16(Wd, d.N, d.d, d.h, wdt, d.d, 0, st));
-  MOE_TRY(launch_transpose_bf16(Wg, d.N, d.h, d.d, wgut, 2 * (int64_t)d.h, 0, st));
-  MOE_TRY(launch_transpose_bf16(Wu, d.N, d.h, d.d, wgut, 2 * (int64_t)d.h, d.h, st));
-  // dH = W_down^T dY, and in the epilogue (dG, dU) = act'(G, U) dH.
-  {
-    GemmArgs a;
-    memset(&a, 0, sizeof(a));
-    a.A = dy_perm;
-    a.lda = d.d;
-    a.B = wdt;
-    a.strideB = (int64_t)d.h * d.d;
-    a.K = d.d;
-    a.ncols = d.h;
-    a.mode = GM_SEGMENT;
-    a.G = d.N;
-    a.kept_offsets = kept_offsets;
-    a.tile_start = tile_start;
-    a.out = dgu;
-    a.out2 = dgu + d.h;
-    a.ldo = 2 * (int64_t)d.h;
-    a.gsrc = G;
-    a.usrc = U;
-    a.ldg = d.h;
-    a.act = d.act;
-    a.beta_g = d.beta_g;
-    a.beta_u = d.beta_u;
-    a.bm = bm;
-    MOE_TRY(launch_gemm(a, EP_GLU_BWD, mt, st));
+  // The router, driven by dr and the expert outputs at width l; writes du.
+  MOE_TRY(dense_gemm(U, D, 0, static_cast<const uint16_t *>(wts->W_route), nullptr, 0, D, d.N, 1,
+                     T, logits, d.N, EP_F32, nullptr, nullptr, 0, st));
+  const float aux_coef = aux_scale * d.aux_alpha * (float)d.N / (float)d.T;
+  MOE_TRY(launch_route_backward(logits, T, d.N, d.k, D, l, d.gate == MOE_GATE_RENORM ? 1 : 0,
+                                fwd->topk_idx, fwd->row_of, fwd->y_perm, dr, fwd->stats, aux_coef,
+                                U, static_cast<const uint16_t *>(wts->W_route),
+                                region<float>(ws, L.rb_part), g->dz, g->dW_route, g->du, st));
+  // Through W_ldown: du += dx_l W_ldown; dW_ldown = dx_l^T u.
+  MOE_TRY(launch_cast_bf16(dxl, T * l, dxlb, st));
+  MOE_TRY(launch_transpose_bf16(Wldown, 1, l, D, wldt, l, 0, st));
+  MOE_TRY(dense_gemm(dxlb, l, 0, wldt, nullptr, 0, l, D, 1, T, tmp, D, EP_F32, nullptr, nullptr, 0,
+                     st));
+  MOE_TRY(launch_add_f32(g->du, tmp, T * D, st));
+  MOE_TRY(launch_fill_zero(dxlt, (size_t)l * Tp * 2, st));
+  MOE_TRY(launch_fill_zero(ut, (size_t)D * Tp * 2, st));
+  MOE_TRY(launch_transpose_bf16(dxlb, 1, (int)T, l, dxlt, Tp, 0, st));
+  MOE_TRY(launch_transpose_bf16(U, 1, (int)T, D, ut, Tp, 0, st));
+  MOE_TRY(dense_gemm(dxlt, Tp, 0, ut, nullptr, 0, (int)Tp, D, 1, l, g->dW_ldown, D, EP_F32,
+                     nullptr, nullptr, 0, st));
+  // The shared experts: every token, weight 1, on u and dy.
+  if (d.n_shared > 0) {
+    const BwdDims Ds = shared_dims(d);
+    const BwdLayout Ls = bwd_layout(Ds);
+    float *sw = region<float>(ws, L.sh_w);
+    int32_t *sperm = region<int32_t>(ws, L.sh_perm), *srow = region<int32_t>(ws, L.sh_row);
+    int32_t *soff = region<int32_t>(ws, L.sh_off), *skoff = region<int32_t>(ws, L.sh_koff);
+    MOE_TRY(launch_shared_route(T, d.n_shared, sw, sperm, srow, soff, skoff, st));
+    MOE_TRY(experts_bwd_core(Ds, Ls, ws, U, static_cast<const uint16_t *>(wts->Ws_gate),
+                             static_cast<const uint16_t *>(wts->Ws_up),
+                             static_cast<const uint16_t *>(wts->Ws_down), sw, soff, skoff, sperm,
+                             srow, DY, tmp, g->dWs_gate, g->dWs_up, g->dWs_down, st));
+    MOE_TRY(launch_add_f32(g->du, tmp, T * D, st));
   }
-  // dx rows = [dG | dU] [W_gate ; W_up], then summed per token.
-  {
-    GemmArgs a;
-    memset(&a, 0, sizeof(a));
-    a.A = dgu;
-    a.lda = 2 * (int64_t)d.h;
-    a.B = wgut;
-    a.strideB = (int64_t)d.d * 2 * d.h;
-    a.K = 2 * d.h;
-    a.ncols = d.d;
-    a.mode = GM_SEGMENT;
-    a.G = d.N;
-    a.kept_offsets = kept_offsets;
-    a.tile_start = tile_start;
-    a.out = dx_perm;
-    a.ldo = d.d;
-    a.bm = bm;
-    MOE_TRY(launch_gemm(a, EP_F32, mt, st));
-  }
-  MOE_TRY(launch_rows_sum(dx_perm, d.T, d.d, d.k, row_of, dx, st));
-  if (!all_w) return MOE_OK;
-  // Weight gradients: per-expert K segments over the expert's own rows.
-  int32_t *kseg = region<int32_t>(ws, L.kseg);
-  uint16_t *dyt = region<uint16_t>(ws, L.dyt), *ht = region<uint16_t>(ws, L.ht);
-  uint16_t *xt = region<uint16_t>(ws, L.xt), *dgt = region<uint16_t>(ws, L.dgt);
-  uint16_t *dut = region<uint16_t>(ws, L.dut);
-  const int64_t Rp = L.Rpad;
-  MOE_TRY(launch_kseg(kept_offsets, d.N, kseg, st));
-  MOE_TRY(launch_fill_zero(dyt, (size_t)d.d * Rp * 2, st));
-  MOE_TRY(launch_fill_zero(ht, (size_t)d.h * Rp * 2, st));
-  MOE_TRY(launch_fill_zero(xt, (size_t)d.d * Rp * 2, st));
-  MOE_TRY(launch_fill_zero(dgt, (size_t)d.h * Rp * 2, st));
-  MOE_TRY(launch_fill_zero(dut, (size_t)d.h * Rp * 2, st));
-  MOE_TRY(launch_seg_transpose(dy_perm, nullptr, d.d, d.d, L.R, kept_offsets, offsets, nullptr,
-                               d.k, kseg, d.N, 0, 1.f, 1.f, dyt, Rp, st));
-  MOE_TRY(launch_seg_transpose(G, U, d.h, d.h, L.R, kept_offsets, offsets, nullptr, d.k, kseg,
-                               d.N, d.act, d.beta_g, d.beta_u, ht, Rp, st));
-  MOE_TRY(launch_seg_transpose(static_cast<const uint16_t *>(u), nullptr, d.d, d.d, L.R,
-                               kept_offsets, offsets, perm, d.k, kseg, d.N, 0, 1.f, 1.f, xt, Rp,
-                               st));
-  MOE_TRY(launch_seg_transpose(dgu, nullptr, 2 * (int64_t)d.h, d.h, L.R, kept_offsets, offsets,
-                               nullptr, d.k, kseg, d.N, 0, 1.f, 1.f, dgt, Rp, st));
-  MOE_TRY(launch_seg_transpose(dgu + d.h, nullptr, 2 * (int64_t)d.h, d.h, L.R, kept_offsets,
-                               offsets, nullptr, d.k, kseg, d.N, 0, 1.f, 1.f, dut, Rp, st));
-  auto kseg_gemm = [&](const uint16_t *A, int M, const uint16_t *B, int ncols, float *out) {
-    GemmArgs a;
-    memset(&a, 0, sizeof(a));
-    a.A = A;
-    a.lda = Rp;
-    a.B = B;
-    a.strideB = 0;
-    a.K = 128;  // the k range comes from kseg
-    a.ncols = ncols;
-    a.mode = GM_DENSE;
-    a.G = d.N;
-    a.M_dense = M;
-    a.a_group_rows = 0;
-    a.out = out;
-    a.ldo = ncols;
-    a.out_group_stride = M;
-    a.kseg = kseg;
-    a.ldb = Rp;
-    a.bm = 256;
-    return launch_gemm(a, EP_F32, 0, st);
-  };
-  MOE_TRY(kseg_gemm(dyt, d.d, ht, d.h, dW_down));
-  MOE_TRY(kseg_gemm(dgt, d.h, xt, d.d, dW_gate));
-  MOE_TRY(kseg_gemm(dut, d.h, xt, d.d, dW_up));
   return MOE_OK;
 }
 
@@ -808,7 +1022,7 @@ moe_status_t moe_route_backward(const moe_desc_t *desc, const void *u, const voi
                      d.N, EP_F32, nullptr, nullptr, 0, st));
   const float aux_coef = aux_scale * d.aux_alpha * (float)d.N / (float)d.T;
   return hip_status(launch_route_backward(
-      logits, d.T, d.N, d.k, d.d, d.gate == MOE_GATE_RENORM ? 1 : 0, topk_idx, row_of, y_perm,
+      logits, d.T, d.N, d.k, d.d, d.d, d.gate == MOE_GATE_RENORM ? 1 : 0, topk_idx, row_of, y_perm,
       static_cast<const uint16_t *>(dy), stats, aux_coef, static_cast<const uint16_t *>(u),
       static_cast<const uint16_t *>(W_route), region<float>(ws, L.rb_part), dz, dW_route, du,
       st));

@@ -10,7 +10,9 @@
 //   dW_route = dz^T u,   du = dz W_route   (the router's share of du)
 //
 //   rb_dz_kernel:   a wave per token (16 per block): softmax of the logits,
-//                   the k dot products dy_t . y_perm[row] over d, the gate and
+//                   the k dot products dy_t . y_perm[row] (over d, or over l
+//                   for the latent layer, whose dy is the gradient at the
+//                   aggregated r), the gate and
 //                   softmax backward through a per-wave LDS row of p and dp.
 //   rb_dw_kernel:   fp32 partial sums of dz^T u over chunks of tokens: a
 //                   thread per 8 columns of u (one 16-byte load a token) and
@@ -247,15 +249,15 @@ int64_t route_bwd_chunks(int64_t T, int N, int d) {
   return by_tokens < by_bytes ? by_tokens : by_bytes;
 }
 
-hipError_t launch_route_backward(const float *logits, int64_t T, int N, int k, int d, int renorm,
-                                 const int32_t *idx, const int32_t *row_of, const float *y_perm,
-                                 const uint16_t *dy, const float *stats, float aux_coef,
-                                 const uint16_t *u, const uint16_t *w_route, float *part,
-                                 float *dz, float *dw, float *du, hipStream_t st) {
+hipError_t launch_route_backward(const float *logits, int64_t T, int N, int k, int d, int dyw,
+                                 int renorm, const int32_t *idx, const int32_t *row_of,
+                                 const float *y_perm, const uint16_t *dy, const float *stats,
+                                 float aux_coef, const uint16_t *u, const uint16_t *w_route,
+                                 float *part, float *dz, float *dw, float *du, hipStream_t st) {
   const dim3 g1((unsigned)((T + kRbTokens - 1) / kRbTokens)), b1(64 * kRbTokens);
-#define MOE_RB_CASE(NPLV)                                                                        \
-  hipLaunchKernelGGL(rb_dz_kernel<NPLV>, g1, b1, 0, st, logits, T, N, k, d, renorm, idx, row_of, \
-                     y_perm, dy, stats, aux_coef, dz)
+#define MOE_RB_CASE(NPLV)                                                                  \
+  hipLaunchKernelGGL(rb_dz_kernel<NPLV>, g1, b1, 0, st, logits, T, N, k, dyw, renorm, idx, \
+                     row_of, y_perm, dy, stats, aux_coef, dz)
   if (N <= 64) MOE_RB_CASE(1);
   else if (N <= 256) MOE_RB_CASE(4);
   else MOE_RB_CASE(16);

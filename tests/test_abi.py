@@ -276,4 +276,40 @@ def test_experts_backward_validates():
     assert call(H.desc_for(C.LATENT)) == L.MOE_ERR_UNSUPPORTED
     assert call(H.desc_for(C.MIXTRAL_PREFILL_FP8)) == L.MOE_ERR_UNSUPPORTED
     with pytest.raises(moe.MoeError):
-        moe.moe_backward_workspace_bytes(H.desc_for(C.LATENT))
+        moe.moe_backward_workspace_bytes(H.desc_for(C.LATENT_FP8))
+
+
+def test_latent_backward_validates():
+    lib = L.load()
+    lb = lib.moe_latent_backward
+    n = None
+    big = 1 << 40
+    d = H.desc_for(C.LATENT)
+    # The latent backward's workspace holds the routed experts' regions
+    # (transposed weights among them) and is larger than the forward's.
+    assert moe.moe_backward_workspace_bytes(d) > moe.moe_workspace_bytes(d)
+    wnames = [f for f, _ in L.MoeWeights._fields_]
+    onames = [f for f, _ in L.MoeOutputs._fields_]
+    gnames = [f for f, _ in L.MoeLatentGrads._fields_]
+
+    def call(desc, drop=(), aux=0.0, ws=big, shared=True):
+        w = L.MoeWeights(**{f: (None if f in drop or f in ("selection_bias", "gate_scale",
+                                                           "up_scale", "down_scale")
+                                or (not shared and f.startswith("Ws_")) else 4096)
+                            for f in wnames})
+        o = L.MoeOutputs(**{f: (None if f in drop or f in ("counts", "drop") else 4096)
+                            for f in onames})
+        g = L.MoeLatentGrads(**{f: (None if f in drop or (not shared and f.startswith("dWs_"))
+                                    else 4096) for f in gnames})
+        return lb(ctypes.byref(desc), ctypes.byref(w), FAKE, ctypes.byref(o),
+                  None if "dy" in drop else FAKE, aux, ctypes.byref(g), FAKE, ws, n)
+    assert call(d, ws=10) == L.MOE_ERR_WORKSPACE
+    for f in wnames[:9] + ["topk_idx", "topk_w", "stats", "offsets", "kept_offsets", "perm",
+                           "row_of", "y_perm", "dy"] + gnames:
+        assert call(d, drop=(f,)) == L.MOE_ERR_ARG, f
+    assert call(d, aux=float("inf")) == L.MOE_ERR_ARG
+    d0 = H.desc_for(C.LATENT)
+    d0.n_shared, d0.h_shared = 0, 0
+    assert call(d0, shared=False, ws=10) == L.MOE_ERR_WORKSPACE   # no shared pointers needed
+    assert call(good()) == L.MOE_ERR_UNSUPPORTED                   # plain: the other two
+    assert call(H.desc_for(C.LATENT_FP8)) == L.MOE_ERR_UNSUPPORTED
