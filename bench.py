@@ -147,7 +147,62 @@ def run_workload(cfg, steps, warmup):
             if cfg.w_dtype == "bf16":
                 r["experts_backward"] = time_experts_backward(moe, H, desc, u, w, out, cfg,
                                                               max(3, steps // 4))
+        elif cfg.w_dtype == "bf16":
+            r["latent_backward"] = time_latent_backward(moe, H, desc, u, w, y, out, ws, cfg,
+                                                        max(3, steps // 4))
     return r
+
+
+def time_latent_backward(moe, H, desc, u, w, y, out, ws, cfg, steps):
+    """moe_latent_backward (every gradient) after a forward that hands out its
+    expert outputs, with a seeded dy; averaged over `steps`.  Algorithmic
+    work: the routed experts' 8 products of R x l x H and the shared experts'
+    8 of T x d x h_s (2 m n k flops each), five T x d x l products (x_l
+    recomputed, dn, dW_lup, du through W_ldown, dW_ldown) and three T x N x d
+    (logits, dW_route, the router's du)."""
+    import torch
+
+    import synth as S
+
+    kept = int(H.to_host(out["kept_offsets"])[-1])
+    y_perm = torch.empty((max(kept, 1), cfg.l), dtype=torch.float32, device="cuda")
+    out = dict(out, y_perm=y_perm)
+    moe.moe_forward(desc, w, u, y, out, ws)
+    torch.cuda.synchronize()
+    del ws
+    torch.cuda.empty_cache()
+    dy = H.to_device(S.normal_stored(cfg.seed + 1, 96, cfg.T * cfg.d, 0.5, "bf16")
+                     .reshape(cfg.T, cfg.d))
+    f = lambda *s: torch.empty(s, dtype=torch.float32, device="cuda")  # noqa: E731
+    g = {"du": f(cfg.T, cfg.d), "dz": f(cfg.T, cfg.N), "dW_route": f(cfg.N, cfg.d),
+         "dW_ldown": f(cfg.l, cfg.d), "dW_lup": f(cfg.d, cfg.l),
+         "dW_gate": f(cfg.N, cfg.h, cfg.l), "dW_up": f(cfg.N, cfg.h, cfg.l),
+         "dW_down": f(cfg.N, cfg.l, cfg.h)}
+    if cfg.n_shared:
+        g.update(dWs_gate=f(cfg.n_shared, cfg.h_shared, cfg.d),
+                 dWs_up=f(cfg.n_shared, cfg.h_shared, cfg.d),
+                 dWs_down=f(cfg.n_shared, cfg.d, cfg.h_shared))
+    bws = moe.backward_workspace(desc)
+    args = (desc, w, u, out, dy, g, bws)
+    moe.moe_latent_backward(*args, aux_scale=1.0)
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(steps):
+        moe.moe_latent_backward(*args, aux_scale=1.0)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    T, d, l = cfg.T, cfg.d, cfg.l
+    flops = (16.0 * kept * l * cfg.h + 16.0 * cfg.n_shared * T * d * cfg.h_shared
+             + 10.0 * T * d * l + 6.0 * T * cfg.N * d)
+    res = {"ms": ms, "algorithmic_tflop": flops / 1e12, "tflops": flops / (ms / 1e3) / 1e12,
+           "mfma_frac": flops / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
+           "workspace_gb": moe.moe_backward_workspace_bytes(desc) / 1e9}
+    del bws, g
+    torch.cuda.empty_cache()
+    return res
 
 
 def time_experts_backward(moe, H, desc, u, w, out, cfg, steps):
@@ -338,6 +393,8 @@ def main():
         line["route_backward"] = r["route_backward"]
     if "experts_backward" in r:
         line["experts_backward"] = r["experts_backward"]
+    if "latent_backward" in r:
+        line["latent_backward"] = r["latent_backward"]
     for key, name in (("decode", args.decode_workload), ("decode_fp8", args.fp8_decode_workload),
                       ("decode_mxfp4", args.mxfp4_decode_workload)):
         if not name:

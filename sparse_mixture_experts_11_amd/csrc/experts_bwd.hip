@@ -12,12 +12,15 @@
 // around them:
 //   bwd_gather_dy_kernel: dY rows (a dy_t) in the expert-sorted row order;
 //   transpose_bf16_kernel: [B][R][C] -> [B][C][ld] at a column offset, 64x64
-//     tiles through LDS (the weight copies the GEMMs read K-contiguous);
+//     tiles through LDS with 16-byte loads and stores (the weight copies the
+//     GEMMs read K-contiguous);
 //   kseg_kernel: each expert's rows padded to a multiple of 128 (at least
 //     128), as a prefix of column offsets;
 //   seg_transpose_kernel: row-major [rows][width] -> [width][Rpad], row r of
-//     expert g to column kseg[g] + r - kept_offsets[g]; optionally gathered
-//     token rows (x) or act(G, U) computed on the way;
+//     expert g to column kseg[g] + r - kept_offsets[g] and zeros in the rest
+//     of the expert's padded segment (tiled over the destination columns,
+//     16-byte loads and stores); optionally gathered token rows (x) or
+//     act(G, U) computed on the way;
 //   fill_zero_kernel, rows_sum_kernel (dx_t = sum of its kept rows).
 #include "common.hpp"
 #include "kernels.hpp"
@@ -50,24 +53,53 @@ __global__ __launch_bounds__(256) void bwd_gather_dy_kernel(const uint16_t *__re
   }
 }
 
-// dst[b][c][col0 + r] = src[b][r][c]: src [B][R][C], dst rows of length ld.
+// dst[b][c][col0 + r] = src[b][r][c]: src [B][R][C], dst rows of length ld
+// (C, ld and col0 multiples of 8).  A 64x64 tile per block: 16-byte row
+// loads into LDS (pitch 66 halves: the column reads below hit distinct
+// banks), 16-byte stores of 8 consecutive source rows of one column.
 __global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t *__restrict__ src,
                                                              int R, int C,
                                                              uint16_t *__restrict__ dst,
                                                              int64_t ld, int col0) {
-  __shared__ uint16_t tile[64][66];
+  __shared__ uint32_t tile[64 * 33];
   const int b = blockIdx.z;
   const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
   const uint16_t *s = src + (int64_t)b * R * C;
   uint16_t *o = dst + (int64_t)b * C * ld;
-  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-    const int rr = i / 64, cc = i % 64;
-    tile[rr][cc] = (r0 + rr < R && c0 + cc < C) ? s[(int64_t)(r0 + rr) * C + c0 + cc] : 0;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int i = threadIdx.x + 256 * h;
+    const int r = i >> 3, c8 = (i & 7) << 3;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (r0 + r < R && c0 + c8 < C)
+      v = *reinterpret_cast<const uint4 *>(s + (int64_t)(r0 + r) * C + c0 + c8);
+    uint32_t *t = tile + r * 33 + (c8 >> 1);
+    t[0] = v.x;
+    t[1] = v.y;
+    t[2] = v.z;
+    t[3] = v.w;
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-    const int cc = i / 64, rr = i % 64;
-    if (r0 + rr < R && c0 + cc < C) o[(int64_t)(c0 + cc) * ld + col0 + r0 + rr] = tile[rr][cc];
+  const uint16_t *th = reinterpret_cast<const uint16_t *>(tile);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int i = threadIdx.x + 256 * h;
+    const int cc = i >> 3, r8 = (i & 7) << 3;
+    if (c0 + cc >= C || r0 + r8 >= R) continue;
+    uint16_t e[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) e[j] = th[(r8 + j) * 66 + cc];
+    uint16_t *out = o + (int64_t)(c0 + cc) * ld + col0 + r0 + r8;
+    if (r0 + r8 + 8 <= R) {
+      uint4 w;
+      w.x = (uint32_t)e[0] | ((uint32_t)e[1] << 16);
+      w.y = (uint32_t)e[2] | ((uint32_t)e[3] << 16);
+      w.z = (uint32_t)e[4] | ((uint32_t)e[5] << 16);
+      w.w = (uint32_t)e[6] | ((uint32_t)e[7] << 16);
+      *reinterpret_cast<uint4 *>(out) = w;
+    } else {
+      for (int j = 0; j < R - r0 - r8; ++j) out[j] = e[j];
+    }
   }
 }
 
@@ -110,45 +142,64 @@ __global__ __launch_bounds__(256) void seg_transpose_kernel(
     const int32_t *__restrict__ kept_offsets, const int32_t *__restrict__ offsets,
     const int32_t *__restrict__ perm, int kslots, const int32_t *__restrict__ kseg, int G,
     int act, float bg, float bu, uint16_t *__restrict__ dst, int64_t ld) {
-  __shared__ uint16_t tile[64][66];
-  __shared__ int64_t srow[64];
-  __shared__ int dcol[64];
-  const int R = kept_offsets[G];
-  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
-  if (r0 >= R) return;
-  if (threadIdx.x < 64) {
-    const int r = r0 + threadIdx.x;
-    if (r < R) {
-      int lo = 0, hi = G;  // largest g with kept_offsets[g] <= r
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (kept_offsets[mid] <= r) lo = mid; else hi = mid;
-      }
-      const int j = r - kept_offsets[lo];
-      srow[threadIdx.x] = perm ? (int64_t)(perm[offsets[lo] + j] / kslots) : (int64_t)r;
-      dcol[threadIdx.x] = kseg[lo] + j;
-    }
+  __shared__ uint32_t tile[64 * 33];
+  // This block's 64 destination columns lie in one expert's padded segment
+  // (segments are multiples of 128 wide).
+  const int p0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  if (p0 >= kseg[G]) return;
+  int lo = 0, hi = G;  // largest g with kseg[g] <= p0
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (kseg[mid] <= p0) lo = mid; else hi = mid;
   }
-  __syncthreads();
-  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-    const int rr = i / 64, cc = i % 64;
-    uint16_t v = 0;
-    if (r0 + rr < R && c0 + cc < width) {
-      const int64_t at = srow[rr] * lds + c0 + cc;
+  const int m = kept_offsets[lo + 1] - kept_offsets[lo];
+  const int j0 = p0 - kseg[lo];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int i = threadIdx.x + 256 * h;
+    const int r = i >> 3, c8 = (i & 7) << 3;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (j0 + r < m && c0 + c8 < width) {
+      const int j = j0 + r;
+      const int64_t row = perm ? (int64_t)(perm[offsets[lo] + j] / kslots)
+                               : (int64_t)(kept_offsets[lo] + j);
+      const int64_t at = row * lds + c0 + c8;
+      v = *reinterpret_cast<const uint4 *>(src + at);
       if (src2 != nullptr) {
-        const float h = glu_act(__uint_as_float((uint32_t)src[at] << 16),
-                                __uint_as_float((uint32_t)src2[at] << 16), act, bg, bu);
-        v = (uint16_t)(pack_bf16x2_hw(h, 0.f) & 0xFFFFu);
-      } else {
-        v = src[at];
+        const uint4 w = *reinterpret_cast<const uint4 *>(src2 + at);
+        const uint32_t gv[4] = {v.x, v.y, v.z, v.w}, uv[4] = {w.x, w.y, w.z, w.w};
+        uint32_t o[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          o[q] = pack_bf16x2_hw(
+              glu_act(__uint_as_float(gv[q] << 16), __uint_as_float(uv[q] << 16), act, bg, bu),
+              glu_act(__uint_as_float(gv[q] & 0xFFFF0000u), __uint_as_float(uv[q] & 0xFFFF0000u),
+                      act, bg, bu));
+        v = make_uint4(o[0], o[1], o[2], o[3]);
       }
     }
-    tile[rr][cc] = v;
+    uint32_t *t = tile + r * 33 + (c8 >> 1);
+    t[0] = v.x;
+    t[1] = v.y;
+    t[2] = v.z;
+    t[3] = v.w;
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-    const int cc = i / 64, rr = i % 64;
-    if (r0 + rr < R && c0 + cc < width) dst[(int64_t)(c0 + cc) * ld + dcol[rr]] = tile[rr][cc];
+  const uint16_t *th = reinterpret_cast<const uint16_t *>(tile);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int i = threadIdx.x + 256 * h;
+    const int cc = i >> 3, r8 = (i & 7) << 3;
+    if (c0 + cc >= width) continue;
+    uint16_t e[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) e[j] = th[(r8 + j) * 66 + cc];
+    uint4 w;
+    w.x = (uint32_t)e[0] | ((uint32_t)e[1] << 16);
+    w.y = (uint32_t)e[2] | ((uint32_t)e[3] << 16);
+    w.z = (uint32_t)e[4] | ((uint32_t)e[5] << 16);
+    w.w = (uint32_t)e[6] | ((uint32_t)e[7] << 16);
+    *reinterpret_cast<uint4 *>(dst + (int64_t)(c0 + cc) * ld + p0 + r8) = w;
   }
 }
 
@@ -181,6 +232,7 @@ hipError_t launch_bwd_gather_dy(const uint16_t *dy, int64_t T, int d, int k,
 
 hipError_t launch_transpose_bf16(const uint16_t *src, int B, int R, int C, uint16_t *dst,
                                  int64_t ld, int col0, hipStream_t st) {
+  if (C % 8 != 0 || ld % 8 != 0 || col0 % 8 != 0) return hipErrorInvalidValue;
   hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)((C + 63) / 64),
                                                  (unsigned)((R + 63) / 64), (unsigned)B),
                      dim3(256), 0, st, src, R, C, dst, ld, col0);
@@ -202,13 +254,13 @@ hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t st) {
 }
 
 hipError_t launch_seg_transpose(const uint16_t *src, const uint16_t *src2, int64_t lds,
-                                int width, int64_t rows_bound, const int32_t *kept_offsets,
+                                int width, const int32_t *kept_offsets,
                                 const int32_t *offsets, const int32_t *perm, int kslots,
                                 const int32_t *kseg, int G, int act, float bg, float bu,
                                 uint16_t *dst, int64_t ld, hipStream_t st) {
-  if (rows_bound == 0) return hipSuccess;
+  if (width % 8 != 0 || lds % 8 != 0 || ld % 64 != 0) return hipErrorInvalidValue;
   hipLaunchKernelGGL(seg_transpose_kernel, dim3((unsigned)((width + 63) / 64),
-                                                (unsigned)((rows_bound + 63) / 64)),
+                                                (unsigned)(ld / 64)),
                      dim3(256), 0, st, src, src2, lds, width, kept_offsets, offsets, perm,
                      kslots, kseg, G, act, bg, bu, dst, ld);
   return hipGetLastError();

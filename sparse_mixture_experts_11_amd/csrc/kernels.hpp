@@ -120,8 +120,11 @@ hipError_t launch_transpose_bf16(const uint16_t *src, int B, int R, int C, uint1
                                  int64_t ld, int col0, hipStream_t st);
 hipError_t launch_kseg(const int32_t *kept_offsets, int G, int32_t *kseg, hipStream_t st);
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t st);
+// dst [width][ld]: each expert's padded segment [kseg[g], kseg[g+1]) of the
+// ld columns (ld a multiple of 64, >= kseg[G]) gets the expert's rows and
+// zeros after them.
 hipError_t launch_seg_transpose(const uint16_t *src, const uint16_t *src2, int64_t lds,
-                                int width, int64_t rows_bound, const int32_t *kept_offsets,
+                                int width, const int32_t *kept_offsets,
                                 const int32_t *offsets, const int32_t *perm, int kslots,
                                 const int32_t *kseg, int G, int act, float bg, float bu,
                                 uint16_t *dst, int64_t ld, hipStream_t st);

@@ -219,7 +219,8 @@ BwdLayout bwd_layout(const BwdDims &D, size_t base = 0) {
     return o;
   };
   const size_t R = (size_t)D.R, N = D.N, W = D.w, H = D.h;
-  const size_t Rpad = R + 128 * N;  // each expert's rows padded to 128, at least 128
+  // each expert's rows padded to 128 (at least 128); a multiple of 64
+  const size_t Rpad = (R + 128 * N + 63) / 64 * 64;
   L.Rpad = (int64_t)Rpad;
   L.tile_start = take((N + 1) * 4);
   L.kseg = take((N + 1) * 4);
@@ -241,7 +242,7 @@ BwdLayout bwd_layout(const BwdDims &D, size_t base = 0) {
 
 // 32-bit offsets into the group's transposed and row-major operands.
 bool bwd_dims_ok(const BwdDims &D) {
-  const uint64_t R = (uint64_t)D.R, Rpad = R + 128ull * D.N;
+  const uint64_t R = (uint64_t)D.R, Rpad = (R + 128ull * D.N + 63) / 64 * 64;
   const uint64_t wmax = (uint64_t)(D.w > D.h ? D.w : D.h);
   return wmax * Rpad * 2 < k4G && R * 2ull * D.h * 2 < k4G && 2ull * D.h * D.w * 2 < k4G &&
          R * (uint64_t)D.w * 4 < k4G;
@@ -659,21 +660,16 @@ hipError_t experts_bwd_core(const BwdDims &D, const BwdLayout &L, void *ws, cons
   uint16_t *dut = region<uint16_t>(ws, L.dut);
   const int64_t Rp = L.Rpad;
   MOE_BWD_TRY(launch_kseg(kept_offsets, D.N, kseg, st));
-  MOE_BWD_TRY(launch_fill_zero(dyt, (size_t)W * Rp * 2, st));
-  MOE_BWD_TRY(launch_fill_zero(ht, (size_t)H * Rp * 2, st));
-  MOE_BWD_TRY(launch_fill_zero(xt, (size_t)W * Rp * 2, st));
-  MOE_BWD_TRY(launch_fill_zero(dgt, (size_t)H * Rp * 2, st));
-  MOE_BWD_TRY(launch_fill_zero(dut, (size_t)H * Rp * 2, st));
-  MOE_BWD_TRY(launch_seg_transpose(dy_perm, nullptr, W, D.w, D.R, kept_offsets, offsets, nullptr,
-                                   D.k, kseg, D.N, 0, 1.f, 1.f, dyt, Rp, st));
-  MOE_BWD_TRY(launch_seg_transpose(G, U, H, D.h, D.R, kept_offsets, offsets, nullptr, D.k, kseg,
-                                   D.N, D.act, D.bg, D.bu, ht, Rp, st));
-  MOE_BWD_TRY(launch_seg_transpose(x, nullptr, W, D.w, D.R, kept_offsets, offsets, perm, D.k,
-                                   kseg, D.N, 0, 1.f, 1.f, xt, Rp, st));
-  MOE_BWD_TRY(launch_seg_transpose(dgu, nullptr, 2 * H, D.h, D.R, kept_offsets, offsets, nullptr,
-                                   D.k, kseg, D.N, 0, 1.f, 1.f, dgt, Rp, st));
-  MOE_BWD_TRY(launch_seg_transpose(dgu + H, nullptr, 2 * H, D.h, D.R, kept_offsets, offsets,
-                                   nullptr, D.k, kseg, D.N, 0, 1.f, 1.f, dut, Rp, st));
+  MOE_BWD_TRY(launch_seg_transpose(dy_perm, nullptr, W, D.w, kept_offsets, offsets, nullptr, D.k,
+                                   kseg, D.N, 0, 1.f, 1.f, dyt, Rp, st));
+  MOE_BWD_TRY(launch_seg_transpose(G, U, H, D.h, kept_offsets, offsets, nullptr, D.k, kseg, D.N,
+                                   D.act, D.bg, D.bu, ht, Rp, st));
+  MOE_BWD_TRY(launch_seg_transpose(x, nullptr, W, D.w, kept_offsets, offsets, perm, D.k, kseg,
+                                   D.N, 0, 1.f, 1.f, xt, Rp, st));
+  MOE_BWD_TRY(launch_seg_transpose(dgu, nullptr, 2 * H, D.h, kept_offsets, offsets, nullptr, D.k,
+                                   kseg, D.N, 0, 1.f, 1.f, dgt, Rp, st));
+  MOE_BWD_TRY(launch_seg_transpose(dgu + H, nullptr, 2 * H, D.h, kept_offsets, offsets, nullptr,
+                                   D.k, kseg, D.N, 0, 1.f, 1.f, dut, Rp, st));
   auto kseg_gemm = [&](const uint16_t *A, int M, const uint16_t *B, int ncols, float *out) {
     GemmArgs a;
     memset(&a, 0, sizeof(a));
