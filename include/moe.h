@@ -229,10 +229,12 @@ moe_status_t moe_route_backward(const moe_desc_t *desc, const void *u, const voi
 
 /* Workspace of moe_experts_backward (plain layer) or moe_latent_backward
    (latent layer): its own, larger than the forward's (the recomputed
-   gate/up, dY/dG/dU rows, transposed weight copies and the expert-segmented
-   transposes the weight gradients reduce over; for the latent layer also its
-   per-token rows and the transposed operands of the T-long contractions).
-   Returns MOE_ERR_UNSUPPORTED where those entry points do. */
+   gate/up, dY/dG/dU rows and the expert-segmented transposes the weight
+   gradients reduce over; for the latent layer also its per-token rows and
+   the transposed operands of the T-long contractions; K-contiguous copies of
+   W_down and W_gate | W_up only for experts that average more than 1024
+   kept rows, which are otherwise read as stored).  Returns
+   MOE_ERR_UNSUPPORTED where those entry points do. */
 moe_status_t moe_backward_workspace_bytes(const moe_desc_t *desc, size_t *bytes);
 
 /* The experts' backward (page "MoE: how sparse activation saves compute",

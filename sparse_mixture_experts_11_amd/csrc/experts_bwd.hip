@@ -6,14 +6,15 @@
 //   dx_t += W_gate^T dG + W_up^T dU;
 //   dW_down += dY act(G, U)^T;  dW_gate += dG x^T;  dW_up += dU x^T.
 // The products run on the grouped GEMM: dH and (dG, dU) in one launch whose
-// epilogue applies the activation's backward, dx rows against transposed
-// copies of W_gate | W_up, and the weight gradients as "K segment" GEMMs that
+// epilogue applies the activation's backward, dx rows against W_gate | W_up
+// (both of these read the weights as stored, through the GEMM's
+// transposed-B mode), and the weight gradients as "K segment" GEMMs that
 // reduce over each expert's own rows.  This file holds the data movement
 // around them:
 //   bwd_gather_dy_kernel: dY rows (a dy_t) in the expert-sorted row order;
 //   transpose_bf16_kernel: [B][R][C] -> [B][C][ld] at a column offset, 64x64
-//     tiles through LDS with 16-byte loads and stores (the weight copies the
-//     GEMMs read K-contiguous);
+//     tiles through LDS with 16-byte loads and stores (the latent layer's
+//     token-long operands and projection matrices);
 //   kseg_kernel: each expert's rows padded to a multiple of 128 (at least
 //     128), as a prefix of column offsets;
 //   seg_transpose_kernel: row-major [rows][width] -> [width][Rpad], row r of

@@ -31,6 +31,12 @@
 // The bf16 epilogues store 4 columns at a time: their column counts (h, d, l)
 // are multiples of 128.
 //
+// Transposed B (the experts' backward: dH against W_down, dx against
+// [W_gate ; W_up], read as stored): the B stage holds [64 k][256 n] rows
+// filled by the same direct loads (each k row is one contiguous 512-byte run
+// of the weights), and each B fragment is two ds_read_b64_tr_b16, which hand
+// every lane four consecutive k of one column.
+//
 // FP8 weights (routed experts, EP_GLU and EP_F32): B holds OCP E4M3 codes,
 // one 64-byte row per weight row and k-step in a 16 KiB stage, 16-byte
 // chunk c of row r at chunk c ^ ((r >> 2) & 3); each fragment read takes 8
@@ -70,10 +76,12 @@ __device__ __forceinline__ bf16x8 lds_frag8(const char *tile, int r, int kq) {
 }
 
 // BM = 256 (waves 128x64) or 192 (waves 96x64, for experts with few rows).
-template <int EPI, int BM, bool FP8 = false, bool KSEG = false>
+template <int EPI, int BM, bool FP8 = false, bool KSEG = false, bool BT = false>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
   static_assert(!FP8 || EPI == EP_GLU || EPI == EP_F32, "fp8 weights: routed experts only");
   static_assert(!KSEG || (EPI == EP_F32 && !FP8), "k segments: fp32 weight gradients");
+  static_assert(!BT || (!FP8 && !KSEG && EPI != EP_GLU && EPI != EP_GU),
+                "transposed B: bf16, one B row per output column");
   constexpr int ES = FP8 ? 1 : 2;          // bytes per B element
   constexpr int MI = BM / 64;              // 32-row A blocks per wave
   constexpr int kABytes = BM * BK * 2;     // 32 or 24 KiB per A stage
@@ -151,8 +159,19 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
   }
   // B rows: bf16, instruction i fills rows 64i + tid/8 (8 lanes a row);
   // fp8, instruction i (0, 1) fills rows 128i + tid/4 (4 lanes a row).
+  // Transposed B: the stage is [64 k][256 n] (512-byte rows, 16-byte chunk c
+  // of row k at chunk c ^ 4 (k & 3)); instruction i of wave w fills rows
+  // 2 (8i + w) and 2 (8i + w) + 1, lane l row + l / 32, chunk l % 32.
 #pragma unroll
   for (int i = 0; i < (FP8 ? 2 : 4); ++i) {
+    if constexpr (BT) {
+      const int kr = 2 * (8 * i + wave) + (lane >> 5);
+      const int c = (lane & 31) ^ ((kr & 3) << 2);
+      int64_t n = n_tile * BN + 8 * c;
+      if (n + 8 > a.ncols) n = a.ncols - 8;
+      boff[i] = (uint32_t)((kr * a.ldbt + n) * 2);
+      continue;
+    }
     const int r = FP8 ? (tid >> 2) + 128 * i : lr + 64 * i;
     const int pc = FP8 ? ((tid & 3) ^ ((r >> 2) & 3)) : (lc ^ (r & 7));
     int64_t brow;
@@ -166,8 +185,12 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
     boff[i] = (uint32_t)(brow * (KSEG ? a.ldb : a.K) * ES) + (uint32_t)(pc << 4);
   }
   const char *Bg = static_cast<const char *>(a.B) + (int64_t)g * a.strideB * ES;
-  const char *Ug = glu ? static_cast<const char *>(a.B2) + (int64_t)g * a.strideB * ES : Bg;
-  const uint32_t bbytes = (uint32_t)((int64_t)a.ncols * (KSEG ? a.ldb : a.K) * ES);
+  const char *Ug = (glu || (BT && a.ksplit > 0))
+                       ? static_cast<const char *>(a.B2) + (int64_t)g * a.strideB * ES
+                       : Bg;
+  const uint32_t bbytes =
+      BT ? (uint32_t)((int64_t)(a.ksplit > 0 ? a.ksplit : a.K) * a.ldbt * 2)
+         : (uint32_t)((int64_t)a.ncols * (KSEG ? a.ldb : a.K) * ES);
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.A, 0xFFFFFFFFu);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bg, bbytes);
   const __amdgpu_buffer_rsrc_t ru = make_rsrc(Ug, bbytes);
@@ -188,7 +211,18 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
   auto bload = [&](int k0, int buf, int half) {
     const uint32_t so = (uint32_t)(kbase + k0) * ES;
     char *tb = smem + 2 * kABytes + buf * kBBytes;
-    if constexpr (FP8) {
+    if constexpr (BT) {
+      // A k-step lies wholly in B or in B2 (ksplit is a multiple of BK).
+      const bool second = a.ksplit > 0 && k0 >= a.ksplit;
+      const uint32_t sot = (uint32_t)((int64_t)(second ? k0 - a.ksplit : k0) * a.ldbt * 2);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int i = 2 * half + j;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(second ? ru : rb,
+                                                 (lds_ptr_t)(tb + (8 * i + wave) * 1024), 16,
+                                                 boff[i], sot, 0, 0);
+      }
+    } else if constexpr (FP8) {
       // GLU: rows 0-127 gate, 128-255 up.
       __builtin_amdgcn_raw_ptr_buffer_load_lds((glu && half) ? ru : rb,
                                                (lds_ptr_t)(tb + (128 * half + 16 * wave) * 64),
@@ -212,6 +246,22 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
   for (int j = 0; j < 2; ++j)
     brow_l[j] = glu ? (wn * 32 + j * 128 + (lane & 31)) : (wn * 64 + j * 32 + (lane & 31));
   const int khalf = lane >> 5;
+  // Transposed B: each fragment (8 consecutive k of one column n) is two
+  // transposing LDS reads of 4 k each.  Within a 16-lane group (g16 = lane
+  // / 16, r = lane % 16) lane r addresses row 8 (g16 / 2) + r / 4 (+ 4 for
+  // the second read, + 16 per sub-step) at column n0 + 4 (r % 4), and lane
+  // 4q + e receives element e of the rows addressed by lanes q, q + 4,
+  // q + 8, q + 12: the four k of column n0 + 4q + e.
+  int bt_off[2];
+  if constexpr (BT) {
+    const int g16 = lane >> 4, r = lane & 15;
+    const int kr = 8 * (g16 >> 1) + (r >> 2);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int n = wn * 64 + j * 32 + 16 * (g16 & 1) + 4 * (r & 3);
+      bt_off[j] = kr * 512 + (((n >> 3) ^ ((kr & 3) << 2)) << 4) + (n & 7) * 2;
+    }
+  }
 
   f32x16 acc[4][2];
 #pragma unroll
@@ -228,8 +278,23 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
     const int c = ks * 2 + khalf;
 #pragma unroll
     for (int i = 0; i < MI; ++i) xa[i] = lds_frag(ta, arow_l[i], c);
+    if constexpr (BT) {
+      typedef short v4s __attribute__((ext_vector_type(4)));
+      typedef __attribute__((address_space(3))) v4s *lds_v4s_t;
+      typedef short v8s __attribute__((ext_vector_type(8)));
 #pragma unroll
-    for (int j = 0; j < 2; ++j) xb[j] = FP8 ? lds_frag8(tb, brow_l[j], c) : lds_frag(tb, brow_l[j], c);
+      for (int j = 0; j < 2; ++j) {
+        const char *p0 = tb + bt_off[j] + ks * 16 * 512;
+        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t)(p0));
+        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t)(p0 + 4 * 512));
+        const v8s w = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        xb[j] = __builtin_bit_cast(bf16x8, w);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        xb[j] = FP8 ? lds_frag8(tb, brow_l[j], c) : lds_frag(tb, brow_l[j], c);
+    }
   };
   auto mfma16 = [&](const bf16x8 (&xa)[4], const bf16x8 (&xb)[2]) {
 #pragma unroll
@@ -511,6 +576,18 @@ hipError_t launch_kernel(const GemmArgs &a, int epi, int bm, int64_t grid, hipSt
   if (a.kseg != nullptr) {
     if (epi != EP_F32 || bm != 256) return hipErrorInvalidValue;
     grouped_gemm_kernel<EP_F32, 256, false, true><<<g, b, 0, st>>>(a);
+    return hipGetLastError();
+  }
+  if (a.bt) {
+    if (epi != EP_GLU_BWD && epi != EP_F32) return hipErrorInvalidValue;
+    if (a.ncols % 8 != 0 || a.ldbt % 8 != 0 || a.ksplit % BK != 0) return hipErrorInvalidValue;
+    if (epi == EP_GLU_BWD) {
+      if (bm == 192) grouped_gemm_kernel<EP_GLU_BWD, 192, false, false, true><<<g, b, 0, st>>>(a);
+      else grouped_gemm_kernel<EP_GLU_BWD, 256, false, false, true><<<g, b, 0, st>>>(a);
+    } else {
+      if (bm == 192) grouped_gemm_kernel<EP_F32, 192, false, false, true><<<g, b, 0, st>>>(a);
+      else grouped_gemm_kernel<EP_F32, 256, false, false, true><<<g, b, 0, st>>>(a);
+    }
     return hipGetLastError();
   }
   if (epi == EP_GU || epi == EP_GLU_BWD) {

@@ -83,6 +83,13 @@ struct GemmArgs {
   // stride ldb.  Used with EP_F32 for the experts' weight gradients.
   const int32_t *kseg;
   int64_t ldb;
+  // Transposed B (bt != 0): B_g stored [K][ldbt], element (n, k) at
+  // k * ldbt + n (the weights as the forward keeps them, read without a
+  // transposed copy).  With ksplit > 0, k >= ksplit comes from B2 at row
+  // k - ksplit (the stacked [W_gate ; W_up] of the dx product).
+  int bt;
+  int64_t ldbt;
+  int ksplit;
 };
 // m-tile height for groups of about rows_per_group rows (192 or 256).
 int gemm_pick_bm(double rows_per_group);

@@ -192,6 +192,16 @@ struct BwdDims {
   float bg, bu;
 };
 
+// dH and dx read W_down and W_gate | W_up either as stored (the GEMM's
+// transposed-B mode) or from K-contiguous copies made first.  The copies
+// cost a read and a write of every weight; the transposed-B mode costs
+// about a fifth more GEMM time (measured on gfx950).  Per weight element
+// that is 4 bytes of copy traffic against about 6 flops per kept row, so
+// the copies pay only for experts with many rows: above 1024 rows per
+// expert on average (the Mixtral prefill shape has 4096; the LatentMoE
+// shape 146, where the copies would also take 59 GB of workspace).
+bool bwd_weight_copies(const BwdDims &D) { return D.R > 1024ll * D.N; }
+
 BwdDims routed_dims(const moe_desc_t &d) {
   return BwdDims{d.T, kept_rows_bound(d), d.N, d.k, xwidth(d), d.h, d.act, routed_bm(d),
                  d.beta_g, d.beta_u};
@@ -229,8 +239,10 @@ BwdLayout bwd_layout(const BwdDims &D, size_t base = 0) {
   L.u = take(R * H * 2);
   L.dgu = take(R * 2 * H * 2);
   L.dx_perm = take(R * W * 4);
-  L.wdt = take(N * H * W * 2);
-  L.wgut = take(N * W * 2 * H * 2);
+  if (bwd_weight_copies(D)) {
+    L.wdt = take(N * H * W * 2);
+    L.wgut = take(N * W * 2 * H * 2);
+  }
   L.dyt = take(W * Rpad * 2);
   L.ht = take(H * Rpad * 2);
   L.xt = take(W * Rpad * 2);
@@ -567,7 +579,6 @@ hipError_t experts_bwd_core(const BwdDims &D, const BwdLayout &L, void *ws, cons
   uint16_t *G = region<uint16_t>(ws, L.g), *U = region<uint16_t>(ws, L.u);
   uint16_t *dgu = region<uint16_t>(ws, L.dgu);
   float *dx_perm = region<float>(ws, L.dx_perm);
-  uint16_t *wdt = region<uint16_t>(ws, L.wdt), *wgut = region<uint16_t>(ws, L.wgut);
   const int64_t W = D.w, H = D.h;
   hipError_t e;
 #define MOE_BWD_TRY(expr)              \
@@ -602,17 +613,29 @@ hipError_t experts_bwd_core(const BwdDims &D, const BwdLayout &L, void *ws, cons
     a.bm = bm;
     MOE_BWD_TRY(launch_gemm(a, EP_GU, mt, st));
   }
-  // K-contiguous copies: W_down^T [N][h][w]; [W_gate^T | W_up^T] [N][w][2h].
-  MOE_BWD_TRY(launch_transpose_bf16(Wd, D.N, D.w, D.h, wdt, W, 0, st));
-  MOE_BWD_TRY(launch_transpose_bf16(Wg, D.N, D.h, D.w, wgut, 2 * H, 0, st));
-  MOE_BWD_TRY(launch_transpose_bf16(Wu, D.N, D.h, D.w, wgut, 2 * H, D.h, st));
+  // W_down and W_gate | W_up as the K-contiguous operands of dH and dx:
+  // copies [N][h][w] and [N][w][2h], or the weights as stored.
+  const bool copies = bwd_weight_copies(D);
+  uint16_t *wdt = copies ? region<uint16_t>(ws, L.wdt) : nullptr;
+  uint16_t *wgut = copies ? region<uint16_t>(ws, L.wgut) : nullptr;
+  if (copies) {
+    MOE_BWD_TRY(launch_transpose_bf16(Wd, D.N, D.w, D.h, wdt, W, 0, st));
+    MOE_BWD_TRY(launch_transpose_bf16(Wg, D.N, D.h, D.w, wgut, 2 * H, 0, st));
+    MOE_BWD_TRY(launch_transpose_bf16(Wu, D.N, D.h, D.w, wgut, 2 * H, D.h, st));
+  }
   // dH = W_down^T dY, and in the epilogue (dG, dU) = act'(G, U) dH.
   {
     GemmArgs a;
     memset(&a, 0, sizeof(a));
     a.A = dy_perm;
     a.lda = W;
-    a.B = wdt;
+    if (copies) {
+      a.B = wdt;
+    } else {
+      a.B = Wd;
+      a.bt = 1;
+      a.ldbt = H;
+    }
     a.strideB = H * W;
     a.K = D.w;
     a.ncols = D.h;
@@ -638,8 +661,17 @@ hipError_t experts_bwd_core(const BwdDims &D, const BwdLayout &L, void *ws, cons
     memset(&a, 0, sizeof(a));
     a.A = dgu;
     a.lda = 2 * H;
-    a.B = wgut;
-    a.strideB = W * 2 * H;
+    if (copies) {
+      a.B = wgut;
+      a.strideB = W * 2 * H;
+    } else {
+      a.B = Wg;
+      a.B2 = Wu;
+      a.bt = 1;
+      a.ldbt = W;
+      a.ksplit = D.h;
+      a.strideB = W * H;
+    }
     a.K = 2 * D.h;
     a.ncols = D.w;
     a.mode = GM_SEGMENT;

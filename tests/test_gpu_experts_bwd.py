@@ -3,8 +3,9 @@ oracle's experts_backward, on the same inputs: the oracle's routing, weights
 (rounded to fp32, as the library takes them) and dispatch, and a seeded
 upstream gradient dy.  Input gradient dx and the weight gradients dW_gate,
 dW_up, dW_down; SwiGLU and SiTU-GLU, both m-tile heights, capacity drops,
-h below one 256-column tile, and dx at the full Mixtral prefill shape on
-sampled tokens."""
+h below one 256-column tile, both ways of reading W_down and W_gate | W_up
+(as stored, or through K-contiguous copies for experts with many rows), and
+dx at the full Mixtral prefill shape on sampled tokens."""
 from __future__ import annotations
 
 import numpy as np
@@ -28,6 +29,9 @@ EB_CASES = {
     "mix_situ_t900": MIX_S.with_(name="mix_situ_t900", T=900, act="situ", beta_g=2.0,
                                  beta_u=3.0),
     "mcu_t4096": CASES["mcu_t4096"],                                 # h = 128
+    # more than 1024 rows per expert: W_down and W_gate | W_up through
+    # K-contiguous copies (fewer rows: read as stored)
+    "mix_copies_t4200": MIX_S.with_(name="mix_copies_t4200", T=4200, d=512, h=1024, N=4),
 }
 
 
