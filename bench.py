@@ -38,6 +38,8 @@ def parse():
     p.add_argument("--mxfp4-decode-workload", default="mixtral_decode_t32_mxfp4",
                    help="the decode workload with MXFP4 expert weights ('' to skip)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-backward", action="store_true",
+                   help="skip the backward-pass timings (forward and its stages only)")
     p.add_argument("--cpu-sample-tokens", type=int, default=1536)
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 1 GiB device-to-device copy (3 times) so that "
@@ -93,7 +95,7 @@ def measured_traffic(workload):
     return rec["bytes"]
 
 
-def run_workload(cfg, steps, warmup):
+def run_workload(cfg, steps, warmup, backward=True):
     import numpy as np
     import torch
 
@@ -142,7 +144,9 @@ def run_workload(cfg, steps, warmup):
          "alg": algorithmic(cfg, kept), "desc": desc}
     if cfg.act_dtype == "bf16" and cfg.router_dtype == "bf16":
         r["quantile_balancing"] = time_qb(moe, desc, u, w["W_route"], ws, cfg, steps)
-        if not cfg.latent:
+        if not backward:
+            pass
+        elif not cfg.latent:
             r["route_backward"] = time_route_backward(moe, H, desc, u, w, y, out, ws, cfg, steps)
             if cfg.w_dtype == "bf16":
                 r["experts_backward"] = time_experts_backward(moe, H, desc, u, w, out, cfg,
@@ -344,7 +348,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     cfg = C.ALL[args.workload]
     print(f"[bench] {cfg.name}: uploading weights", file=sys.stderr, flush=True)
-    r = run_workload(cfg, args.steps, args.warmup)
+    r = run_workload(cfg, args.steps, args.warmup, backward=not args.no_backward)
     tok_s = cfg.T / (r["ms_per_step"] / 1e3)
     alg = r["alg"]
     total_flops = alg["gu_flops"] + alg["down_flops"]
@@ -401,7 +405,7 @@ def main():
             continue
         dc = C.ALL[name]
         print(f"[bench] {dc.name}", file=sys.stderr, flush=True)
-        rd = run_workload(dc, args.steps, args.warmup)
+        rd = run_workload(dc, args.steps, args.warmup, backward=False)
         a = rd["alg"]
         wbytes = a["gu_bytes"] + a["down_bytes"]
         line[key] = {
