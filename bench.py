@@ -40,7 +40,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-backward", action="store_true",
                    help="skip the backward-pass timings (forward and its stages only)")
-    p.add_argument("--cpu-sample-tokens", type=int, default=1536)
+    p.add_argument("--cpu-sample-tokens", type=int, default=6144)
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 1 GiB device-to-device copy (3 times) so that "
                         "hardware byte counters can be scaled against a known size")
