@@ -248,10 +248,13 @@ def route(u: np.ndarray, w_route: np.ndarray, k: int, gate: str,
 
 def route_backward(u: np.ndarray, w_route: np.ndarray, idx: np.ndarray, row_of: np.ndarray,
                    y_rows: np.ndarray, dy: np.ndarray, *, gate: str, f: np.ndarray,
-                   alpha: float, aux_scale: float) -> Dict[str, np.ndarray]:
+                   alpha: float, aux_scale: float,
+                   n_tokens: Optional[int] = None) -> Dict[str, np.ndarray]:
     """Router backward, steps as above.  u [T, d], w_route [N, d], idx [T, k],
     row_of [T*k] (-1 for a dropped slot), y_rows [R, d] the experts' outputs
-    of the kept rows, dy [T, d], f [N] the forward's arg-max shares."""
+    of the kept rows, dy [T, d], f [N] the forward's arg-max shares.
+    n_tokens: the layer's token count in the aux term's 1/T when u holds only
+    some of its tokens (default: all of them)."""
     T, d = u.shape
     N = w_route.shape[0]
     k = idx.shape[1]
@@ -274,7 +277,8 @@ def route_backward(u: np.ndarray, w_route: np.ndarray, idx: np.ndarray, row_of: 
         raise ValueError(gate)
     dp = np.zeros((T, N))
     np.put_along_axis(dp, idx, g, axis=1)
-    dp = dp + aux_scale * alpha * N * np.asarray(f, dtype=np.float64)[None, :] / T
+    dp = dp + aux_scale * alpha * N * np.asarray(f, dtype=np.float64)[None, :] / (
+        T if n_tokens is None else n_tokens)
     dz = p * (dp - (p * dp).sum(axis=1, keepdims=True))
     return {"p": p, "da": da, "dp": dp, "dz": dz, "dW_route": dz.T @ u, "du": dz @ w_route}
 
@@ -312,9 +316,17 @@ def experts_backward(x: np.ndarray, disp: Dict[str, np.ndarray], a: np.ndarray,
     N = len(disp["counts"])
     dx = np.zeros((T, w))
     dWg, dWu, dWd = [], [], []
+    shapes = None
     for e in range(N):
-        wg, wu, wd = _expert64(experts, e)
         lo, kept = int(disp["offsets"][e]), int(disp["kept_counts"][e])
+        if kept == 0 and shapes is not None:
+            # no kept row: zero gradients (the weights are not needed)
+            dWd.append(np.zeros(shapes[2]))
+            dWg.append(np.zeros(shapes[0]))
+            dWu.append(np.zeros(shapes[1]))
+            continue
+        wg, wu, wd = _expert64(experts, e)
+        shapes = (wg.shape, wu.shape, wd.shape)
         ent = disp["perm"][lo:lo + kept]
         toks, slots = ent // k, ent % k
         xr = x[toks]
@@ -406,15 +418,19 @@ def capacity_from_factor(T: int, N: int, k: int, c: float) -> int:
     return int(math.ceil((c * k * T) / N))
 
 
-def dispatch(idx: np.ndarray, N: int, capacity: Optional[int]) -> Dict[str, np.ndarray]:
+def dispatch(idx: np.ndarray, N: int, capacity: Optional[int],
+             kept: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
     """Group the (token, slot) dispatches by expert, in token order.
 
     rank(t, s) counts the earlier tokens that chose the same expert; a dispatch
     is kept iff rank < C.  perm lists entries t*k+s sorted by (expert, token);
     row_of gives each kept entry its row in the expert-sorted kept rows.
+    ``kept`` [T, k] may give the kept flags instead (a subset of a larger
+    dispatch's tokens: its kept entries are still the first of each expert in
+    token order); capacity is then ignored.
     """
     T, k = idx.shape
-    C = None if capacity is None or capacity < 0 else int(capacity)
+    C = None if capacity is None or capacity < 0 or kept is not None else int(capacity)
     counts = np.zeros(N, dtype=np.int64)
     rank = np.zeros((T, k), dtype=np.int64)
     for t in range(T):
@@ -422,10 +438,14 @@ def dispatch(idx: np.ndarray, N: int, capacity: Optional[int]) -> Dict[str, np.n
             e = int(idx[t, s])
             rank[t, s] = counts[e]
             counts[e] += 1
-    kept_counts = counts if C is None else np.minimum(counts, C)
+    if kept is not None:
+        kept = np.asarray(kept, dtype=bool).reshape(T, k)
+        kept_counts = np.bincount(idx[kept].astype(np.int64), minlength=N)
+    else:
+        kept_counts = counts if C is None else np.minimum(counts, C)
+        kept = np.ones((T, k), dtype=bool) if C is None else rank < C
     offsets = np.concatenate([[0], np.cumsum(counts)])
     kept_offsets = np.concatenate([[0], np.cumsum(kept_counts)])
-    kept = np.ones((T, k), dtype=bool) if C is None else rank < C
     perm = np.empty(T * k, dtype=np.int64)
     row_of = np.full(T * k, -1, dtype=np.int64)
     for t in range(T):
@@ -736,6 +756,50 @@ def latent_backward(u_st: np.ndarray, w_route_st: np.ndarray, experts: ExpertFn,
     if n_shared:
         out.update(dWs_gate=np.stack(dWs_g), dWs_up=np.stack(dWs_u), dWs_down=np.stack(dWs_d))
     return out
+
+
+def latent_backward_tokens(u_st: np.ndarray, w_route_st: np.ndarray, experts: ExpertFn,
+                           w_ldown_st: np.ndarray, w_lup_st: np.ndarray, shared: ExpertFn,
+                           n_shared: int, dy_rows: np.ndarray, tokens: np.ndarray, *, k: int,
+                           gate: str = "renorm", act: str = "situ",
+                           capacity: Optional[int] = None, beta_g: float = 4.0,
+                           beta_u: float = 25.0, rms_eps: float = 1e-6, alpha: float = 0.01,
+                           aux_scale: float = 0.0) -> Dict[str, object]:
+    """latent_backward's du and dz rows of the given tokens only (dy_rows
+    [len(tokens), d] their upstream gradient).  Each token's du and dz depend
+    only on its own routing, its own rows and, through f and the capacity
+    ranks, on the routing of all tokens, which is computed in full; the
+    experts run on the sampled tokens' rows only (renumbered 0..n-1)."""
+    u = expand(u_st)
+    wr, wld, wlu = expand(w_route_st), expand(w_ldown_st), expand(w_lup_st)
+    T, N = u.shape[0], wr.shape[0]
+    tokens = np.asarray(tokens, dtype=np.int64)
+    rt = route(u, wr, k, gate)
+    full = dispatch(rt["idx"], N, capacity)
+    f = balance_stats(rt["p"], alpha)["f"]
+    idx = rt["idx"][tokens]
+    a = rt["a"][tokens]
+    kept = full["row_of"].reshape(T, k)[tokens] >= 0
+    disp = dispatch(idx, N, None, kept=kept)
+    ut = u[tokens]
+    xl = ut @ wld.T
+    rows = expert_rows(xl, disp, experts, make_act(act, beta_g, beta_u), k)
+    y_rows = np.zeros((int(disp["kept_offsets"][-1]), wld.shape[0]))
+    for j, v in rows.items():
+        y_rows[j] = v
+    r = combine_rows(y_rows, disp["row_of"], a)
+    dr = rmsnorm_backward(r, dy_rows @ wlu, rms_eps)
+    ex = experts_backward(xl, disp, a, experts, dr, act=act, k=k, beta_g=beta_g,
+                          beta_u=beta_u)
+    rb = route_backward(ut, wr, idx, disp["row_of"], y_rows, dr, gate=gate, f=f, alpha=alpha,
+                        aux_scale=aux_scale, n_tokens=T)
+    du = rb["du"] + ex["dx"] @ wld
+    for j in range(n_shared):
+        sg, su, sd = (expand(w) for w in shared(j))
+        g, v = ut @ sg.T, ut @ su.T
+        dg, dv = act_backward("swiglu", g, v, dy_rows @ sd)
+        du = du + dg @ sg + dv @ su
+    return {"du": du, "dz": rb["dz"], "dr": dr, "idx": idx, "margin": rt["margin"][tokens]}
 
 
 def relative_error(y: np.ndarray, y_ref: np.ndarray) -> float:

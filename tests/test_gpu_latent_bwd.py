@@ -124,3 +124,47 @@ def test_latent_backward_after_gpu_forward():
                             aux_scale=0.3)
     torch.cuda.synchronize()
     compare(cfg, g, ref)
+
+
+@pytest.mark.timeout(1500)
+def test_latent_backward_full_size_sampled():
+    """The full LatentMoE workload (T=8192, 896 experts, top-16, 2 shared):
+    GPU forward, then every gradient on the GPU; du and dz compared on
+    sampled tokens against the oracle's per-token form (their 16 experts
+    each), with the aux term on."""
+    from synth import configs as C
+    from tests.test_gpu_parity import sample_tokens
+    cfg = C.LATENT
+    aux = 0.5
+    log(f"[latent backward full] {cfg.name}: uploading {cfg.N} experts")
+    desc = H.desc_for(cfg)
+    w = H.upload_layer(cfg)
+    u = H.to_device(cfg.u())
+    out = H.out_buffers(cfg)
+    out["y_perm"] = torch.empty((cfg.T * cfg.k, cfg.l), dtype=torch.float32, device="cuda")
+    ws = moe.workspace(desc)
+    moe.moe_forward(desc, w, u, H.y_buffer(cfg), out, ws)
+    torch.cuda.synchronize()
+    del ws
+    dy_st = S.normal_stored(45, 96, cfg.T * cfg.d, 0.5, "bf16").reshape(cfg.T, cfg.d)
+    g = grad_buffers(cfg)
+    log("  backward")
+    moe.moe_latent_backward(desc, w, u, out, H.to_device(dy_st), g, moe.backward_workspace(desc),
+                            aux_scale=aux)
+    torch.cuda.synchronize()
+    tokens = sample_tokens(cfg.T, 4, cfg.seed)
+    log(f"  oracle on tokens {tokens.tolist()}")
+    ref = O.latent_backward_tokens(cfg.u(), cfg.w_route(), lambda e: cfg.expert(e), cfg.w_ldown(),
+                                   cfg.w_lup(), lambda j: cfg.shared(j), cfg.n_shared,
+                                   O.expand(dy_st[tokens]), tokens, k=cfg.k, gate=cfg.gate,
+                                   act=cfg.act, beta_g=cfg.beta_g, beta_u=cfg.beta_u,
+                                   rms_eps=cfg.rms_eps, alpha=cfg.aux_alpha, aux_scale=aux)
+    gidx = H.to_host(out["topk_idx"]).reshape(cfg.T, cfg.k)[tokens]
+    same = np.array([set(a.tolist()) == set(b.tolist()) for a, b in zip(gidx, ref["idx"])])
+    assert same.all() or np.all(ref["margin"][~same] < PR.NEAR_TIE)
+    du = H.to_host(g["du"][torch.as_tensor(tokens, device="cuda")]).astype(np.float64)
+    dz = H.to_host(g["dz"][torch.as_tensor(tokens, device="cuda")]).astype(np.float64)
+    e_du = PR.rel_err(du[same], ref["du"][same])
+    e_dz = PR.rel_err(dz[same], ref["dz"][same])
+    log(f"  du rel err {e_du:.2e}, dz rel err {e_dz:.2e} on {int(same.sum())} tokens")
+    assert max(e_du, e_dz) <= PR.TOL["bf16"]

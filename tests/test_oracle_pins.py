@@ -977,3 +977,20 @@ def test_rmsnorm_backward_against_torch_and_scale_free():
     # eps = 0: RMSNorm(c r) = RMSNorm(r), so the gradient has no component along r.
     dr = O.rmsnorm_backward(r, dn, 0.0)
     assert np.max(np.abs((dr * r).sum(axis=1))) < 1e-12
+
+
+@pytest.mark.parametrize("cap,aux", [(None, 0.0), (7, 0.6)])
+def test_latent_backward_tokens_matches_whole_layer(cap, aux):
+    # The sampled-token form (used at full size) gives the whole-layer
+    # backward's du and dz rows for those tokens, capacity drops included.
+    u, wr, wld, wlu, W, Sw, dy = _latent_case(15)
+    kw = dict(k=2, act="situ", capacity=cap, beta_g=1.5, beta_u=2.0, rms_eps=1e-3, aux_scale=aux)
+    g = O.latent_backward(u, wr, lambda e: W[e], wld, wlu, lambda j: Sw[j], 2, dy, **kw)
+    if cap is not None:
+        assert int(g["disp"]["drop"].sum()) > 0
+    tokens = np.array([0, 3, 11, 17, 23])
+    t = O.latent_backward_tokens(u, wr, lambda e: W[e], wld, wlu, lambda j: Sw[j], 2, dy[tokens],
+                                 tokens, **kw)
+    assert np.allclose(t["du"], g["du"][tokens], rtol=1e-12, atol=1e-13)
+    assert np.allclose(t["dz"], g["dz"][tokens], rtol=1e-12, atol=1e-13)
+    assert np.allclose(t["dr"], g["dr"][tokens], rtol=1e-12, atol=1e-13)
