@@ -228,22 +228,44 @@ def time_experts_backward(moe, H, desc, u, w, out, cfg, steps):
           "dW_down": torch.empty((cfg.N, cfg.d, cfg.h), dtype=torch.float32, device="cuda")}
     args = (desc, w, u, out["topk_w"], out["offsets"], out["kept_offsets"], out["perm"],
             out["row_of"], dy, dx, ws)
-    moe.moe_experts_backward(*args, **dW)
-    a = torch.cuda.Event(enable_timing=True)
-    b = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    a.record()
-    for _ in range(steps):
-        moe.moe_experts_backward(*args, **dW)
-    b.record()
-    torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / steps
+
+    def timed(fn):
+        fn()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    ms = timed(lambda: moe.moe_experts_backward(*args, **dW))
     flops = 16.0 * kept * cfg.d * cfg.h
+    res = {"ms": ms, "algorithmic_tflop": flops / 1e12,
+           "tflops": flops / (ms / 1e3) / 1e12,
+           "mfma_frac": flops / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
+           "workspace_gb": moe.moe_backward_workspace_bytes(desc) / 1e9}
+    # With the forward keeping G | U (moe_outputs_t.gate_up): the backward
+    # skips the recompute (6 of the 8 products remain); the forward pays for
+    # writing the 2 R h bf16 values.
+    if cfg.T > 64:
+        gu = torch.empty((max(kept, 1), 2 * cfg.h), dtype=torch.bfloat16, device="cuda")
+        fws = moe.workspace(desc)
+        y = torch.empty((cfg.T, cfg.d), dtype=torch.bfloat16, device="cuda")
+        out_gu = dict(out, gate_up=gu)
+        f_plain = timed(lambda: moe.moe_forward(desc, w, u, y, out, fws))
+        f_save = timed(lambda: moe.moe_forward(desc, w, u, y, out_gu, fws))
+        ms_s = timed(lambda: moe.moe_experts_backward(*args, gate_up=gu, **dW))
+        flops_s = 12.0 * kept * cfg.d * cfg.h
+        res["saved_gate_up"] = {"ms": ms_s, "algorithmic_tflop": flops_s / 1e12,
+                                "tflops": flops_s / (ms_s / 1e3) / 1e12,
+                                "mfma_frac": flops_s / (ms_s / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
+                                "forward_ms_plain": f_plain, "forward_ms_saving": f_save}
+        del gu, fws
     del ws, dW
-    return {"ms": ms, "algorithmic_tflop": flops / 1e12,
-            "tflops": flops / (ms / 1e3) / 1e12,
-            "mfma_frac": flops / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
-            "workspace_gb": moe.moe_backward_workspace_bytes(desc) / 1e9}
+    return res
 
 
 def time_route_backward(moe, H, desc, u, w, y, out, ws, cfg, steps):

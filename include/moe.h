@@ -144,6 +144,12 @@ typedef struct moe_outputs {
   float *y_perm; /* [sum_i min(L_i, C), w] fp32: the experts' outputs of the
                     kept rows (what moe_expert_ffn writes; the input of
                     moe_route_backward) */
+  void *gate_up; /* [sum_i min(L_i, C), 2h] bf16: each kept row's gate sums
+                    G = W_gate x (columns 0..h-1) and up sums U = W_up x
+                    (columns h..2h-1), rounded to bf16, kept so that the
+                    backward need not recompute them.  Only with bf16
+                    activations and expert weights on the tiled path (T > 64);
+                    MOE_ERR_UNSUPPORTED otherwise. */
 } moe_outputs_t;
 
 /* Sets every field of *desc to the "unset" sentinel. */
@@ -247,6 +253,9 @@ moe_status_t moe_backward_workspace_bytes(const moe_desc_t *desc, size_t *bytes)
      w         W_gate, W_up, W_down of the forward (bf16)
      u         [T, d] bf16 the forward's input (x = u for the plain layer)
      topk_w, offsets, kept_offsets, perm, row_of   the forward's (moe_outputs_t)
+     gate_up   the forward's saved G | U rows (moe_outputs_t.gate_up), or
+               null: G and U are then recomputed (the same values: the
+               forward rounds the same fp32 sums)
      dy        [T, d] bf16
      dx        [T, d] fp32 out: the experts' part of the gradient at u
      dW_gate, dW_up [N, h, d], dW_down [N, d, h]  fp32 out, all three or
@@ -260,9 +269,9 @@ moe_status_t moe_backward_workspace_bytes(const moe_desc_t *desc, size_t *bytes)
 moe_status_t moe_experts_backward(const moe_desc_t *desc, const moe_weights_t *w, const void *u,
                                   const float *topk_w, const int32_t *offsets,
                                   const int32_t *kept_offsets, const int32_t *perm,
-                                  const int32_t *row_of, const void *dy, float *dx,
-                                  float *dW_gate, float *dW_up, float *dW_down, void *ws,
-                                  size_t ws_bytes, moe_stream_t stream);
+                                  const int32_t *row_of, const void *gate_up, const void *dy,
+                                  float *dx, float *dW_gate, float *dW_up, float *dW_down,
+                                  void *ws, size_t ws_bytes, moe_stream_t stream);
 
 /* Gradients of the latent layer (device pointers, fp32, row-major; shapes
    with the weights' at moe_weights_t). */
@@ -293,7 +302,9 @@ typedef struct moe_latent_grads {
      each shared expert's backward on u and dy (weight 1 for every token).
      u        [T, d] bf16, the forward's input
      fwd      the forward's outputs: topk_idx, topk_w, stats, offsets,
-              kept_offsets, perm, row_of and y_perm [R, l] are required
+              kept_offsets, perm, row_of and y_perm [R, l] are required;
+              gate_up [R, 2h] is used when set (the routed experts' G | U,
+              otherwise recomputed)
      dy       [T, d] bf16
      g        all of its pointers (the shared ones only when n_shared > 0)
      ws       moe_backward_workspace_bytes() bytes

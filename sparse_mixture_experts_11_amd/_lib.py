@@ -42,7 +42,7 @@ class MoeWeights(ctypes.Structure):
 class MoeOutputs(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("topk_idx", "topk_w", "stats", "counts",
                                                 "offsets", "kept_offsets", "perm", "row_of",
-                                                "drop", "y_perm")]
+                                                "drop", "y_perm", "gate_up")]
 
 
 class MoeLatentGrads(ctypes.Structure):
@@ -87,7 +87,7 @@ def load() -> ctypes.CDLL:
     lib.moe_route_backward.restype = I32
     lib.moe_backward_workspace_bytes.argtypes = [D, ctypes.POINTER(SZ)]
     lib.moe_backward_workspace_bytes.restype = I32
-    lib.moe_experts_backward.argtypes = [D, ctypes.c_void_p] + [P] * 12 + [SZ, P]
+    lib.moe_experts_backward.argtypes = [D, ctypes.c_void_p] + [P] * 13 + [SZ, P]
     lib.moe_experts_backward.restype = I32
     lib.moe_latent_backward.argtypes = [D, ctypes.POINTER(MoeWeights), P,
                                         ctypes.POINTER(MoeOutputs), P, ctypes.c_float,

@@ -136,13 +136,16 @@ def backward_workspace(desc, device="cuda") -> torch.Tensor:
 
 def moe_experts_backward(desc, weights: Mapping[str, torch.Tensor], u, topk_w, offsets,
                          kept_offsets, perm, row_of, dy, dx, ws, dW_gate=None, dW_up=None,
-                         dW_down=None, stream=None) -> None:
+                         dW_down=None, gate_up=None, stream=None) -> None:
+    """gate_up: the forward's saved G | U rows (outputs "gate_up"), or None
+    to recompute them."""
     w = _weights(weights)
     _check(L.load().moe_experts_backward(ctypes.byref(desc), ctypes.byref(w), _ptr(u),
                                          _ptr(topk_w), _ptr(offsets), _ptr(kept_offsets),
-                                         _ptr(perm), _ptr(row_of), _ptr(dy), _ptr(dx),
-                                         _ptr(dW_gate), _ptr(dW_up), _ptr(dW_down), _ptr(ws),
-                                         ws.numel(), _stream(stream)), "moe_experts_backward")
+                                         _ptr(perm), _ptr(row_of), _ptr(gate_up), _ptr(dy),
+                                         _ptr(dx), _ptr(dW_gate), _ptr(dW_up), _ptr(dW_down),
+                                         _ptr(ws), ws.numel(), _stream(stream)),
+           "moe_experts_backward")
 
 
 def moe_latent_backward(desc, weights: Mapping[str, torch.Tensor], u,

@@ -24,7 +24,8 @@
 //
 // Epilogues: EP_GLU pairs 128 gate columns with the matching 128 up columns in
 // one tile and writes act(gate, up) as bf16 (the hidden of a SwiGLU or
-// SiTU-GLU expert); EP_F32 stores the fp32 product through LDS so each store
+// SiTU-GLU expert), EP_GLU_SAVE also the gate and up sums themselves (bf16,
+// kept for the backward); EP_F32 stores the fp32 product through LDS so each store
 // writes a whole output row, and handles any column count (the router logits
 // have N columns); EP_BF16 stores the rounded product; EP_ADD_BF16 adds two
 // fp32 matrices before rounding (the latent layer's shared-expert outputs).
@@ -80,7 +81,8 @@ template <int EPI, int BM, bool FP8 = false, bool KSEG = false, bool BT = false>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
   static_assert(!FP8 || EPI == EP_GLU || EPI == EP_F32, "fp8 weights: routed experts only");
   static_assert(!KSEG || (EPI == EP_F32 && !FP8), "k segments: fp32 weight gradients");
-  static_assert(!BT || (!FP8 && !KSEG && EPI != EP_GLU && EPI != EP_GU),
+  static_assert(!FP8 || EPI != EP_GLU_SAVE, "saved gate/up sums: bf16 weights");
+  static_assert(!BT || (!FP8 && !KSEG && EPI != EP_GLU && EPI != EP_GU && EPI != EP_GLU_SAVE),
                 "transposed B: bf16, one B row per output column");
   constexpr int ES = FP8 ? 1 : 2;          // bytes per B element
   constexpr int MI = BM / 64;              // 32-row A blocks per wave
@@ -92,7 +94,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
   // ---- which tile: XCD-aware remap (block i runs on XCD i % 8: each XCD
   // takes one contiguous eighth of the real tiles), then (group, m-super, n,
   // m) order so the tiles running together on one XCD share A and B rows.
-  const int glu = (EPI == EP_GLU || EPI == EP_GU);
+  const int glu = (EPI == EP_GLU || EPI == EP_GU || EPI == EP_GLU_SAVE);
   const int64_t NT = glu ? (a.ncols + 127) / 128 : (a.ncols + BN - 1) / BN;
   const int64_t real_tiles = (a.mode == GM_DENSE)
                                  ? (int64_t)a.G * ((a.M_dense + BM - 1) / BM) * NT
@@ -469,11 +471,22 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
         *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(a.out2) + orow * a.ldo + col) =
             pu;
       }
-    } else if constexpr (EPI == EP_GLU) {
+    } else if constexpr (EPI == EP_GLU || EPI == EP_GLU_SAVE) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int64_t col = n_tile * 128 + wn * 32 + 8 * q + 4 * khalf;
         if (col >= a.ncols) continue;
+        if constexpr (EPI == EP_GLU_SAVE) {
+          // G and U, each rounded to bf16, as the backward's recompute would.
+          uint2 pg, pu;
+          pg.x = pack_bf16x2_hw(acc[i][0][4 * q], acc[i][0][4 * q + 1]);
+          pg.y = pack_bf16x2_hw(acc[i][0][4 * q + 2], acc[i][0][4 * q + 3]);
+          pu.x = pack_bf16x2_hw(acc[i][1][4 * q], acc[i][1][4 * q + 1]);
+          pu.y = pack_bf16x2_hw(acc[i][1][4 * q + 2], acc[i][1][4 * q + 3]);
+          uint16_t *gu = reinterpret_cast<uint16_t *>(a.out2) + orow * a.ldg + col;
+          *reinterpret_cast<uint2 *>(gu) = pg;
+          *reinterpret_cast<uint2 *>(gu + a.ncols) = pu;
+        }
         float v[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -590,6 +603,12 @@ hipError_t launch_kernel(const GemmArgs &a, int epi, int bm, int64_t grid, hipSt
     }
     return hipGetLastError();
   }
+  if (epi == EP_GLU_SAVE) {
+    if (a.bscale != nullptr) return hipErrorInvalidValue;
+    if (bm == 192) grouped_gemm_kernel<EP_GLU_SAVE, 192><<<g, b, 0, st>>>(a);
+    else grouped_gemm_kernel<EP_GLU_SAVE, 256><<<g, b, 0, st>>>(a);
+    return hipGetLastError();
+  }
   if (epi == EP_GU || epi == EP_GLU_BWD) {
     if (epi == EP_GU) {
       if (bm == 192) grouped_gemm_kernel<EP_GU, 192><<<g, b, 0, st>>>(a);
@@ -652,7 +671,8 @@ hipError_t launch_tile_prefix(const int32_t *kept_offsets, int G, int bm, int32_
 
 hipError_t launch_gemm(const GemmArgs &a, int epi, int64_t mtiles_bound, hipStream_t st) {
   const int bm = a.bm == 192 ? 192 : 256;
-  const int64_t NT = (epi == EP_GLU || epi == EP_GU) ? (a.ncols + 127) / 128
+  const int64_t NT = (epi == EP_GLU || epi == EP_GU || epi == EP_GLU_SAVE)
+                         ? (a.ncols + 127) / 128
                                                       : (a.ncols + BN - 1) / BN;
   int64_t tiles;
   if (a.mode == GM_DENSE) tiles = (int64_t)a.G * ((a.M_dense + bm - 1) / bm) * NT;

@@ -45,7 +45,10 @@ enum GemmMode { GM_GATHER = 0, GM_SEGMENT = 1, GM_DENSE = 2 };
 // EP_GU (backward): the GLU tile's gate and up sums stored as bf16 (out,
 // out2).  EP_GLU_BWD (backward): the product is dH; with G = gsrc, U = usrc
 // ([rows][ncols] bf16, row stride ldo / 2) it stores dG to out and dU to out2.
-enum GemmEpi { EP_GLU = 0, EP_F32 = 1, EP_BF16 = 2, EP_ADD_BF16 = 3, EP_GU = 4, EP_GLU_BWD = 5 };
+enum GemmEpi {
+  EP_GLU = 0, EP_F32 = 1, EP_BF16 = 2, EP_ADD_BF16 = 3, EP_GU = 4, EP_GLU_BWD = 5,
+  EP_GLU_SAVE = 6  // EP_GLU that also stores the gate and up sums (bf16) for the backward
+};
 
 struct GemmArgs {
   // A: rows of K bf16 values, row stride lda (elements).
@@ -75,9 +78,10 @@ struct GemmArgs {
   int act;                    // 0 SwiGLU, 1 SiTU-GLU
   float beta_g, beta_u;
   int bm;                     // m-tile height: 192, else 256
-  void *out2;                 // EP_GU: up sums; EP_GLU_BWD: dU
+  void *out2;                 // EP_GU: up sums; EP_GLU_BWD: dU; EP_GLU_SAVE: [G | U]
+                              // rows of stride ldg (U at column offset ncols)
   const uint16_t *gsrc, *usrc;  // EP_GLU_BWD: G and U
-  int64_t ldg;                // EP_GLU_BWD: row stride of G and U (elements)
+  int64_t ldg;                // EP_GLU_BWD, EP_GLU_SAVE: row stride of G and U (elements)
   // K segments (dense tiles, every group's own k range): group g reduces over
   // k in [kseg[g], kseg[g+1]) (multiples of 128, at least 128), B rows have
   // stride ldb.  Used with EP_F32 for the experts' weight gradients.

@@ -349,10 +349,12 @@ hipError_t do_tile_prefix(const moe_desc_t &d, const Layout &L, const int32_t *k
 }
 
 // sg, su, sd: fp8 row scales or MXFP4 block scales (null for bf16 / fp32).
+// gate_up: null, or [R, 2h] bf16 rows receiving G | U as well (tiled path,
+// bf16 weights; validated by the caller).
 hipError_t do_ffn_gate_up(const moe_desc_t &d, const Layout &L, const void *x, const int32_t *perm,
                           const int32_t *offsets, const int32_t *kept_offsets, const void *Wg,
                           const void *Wu, const void *sg, const void *su, void *ws,
-                          hipStream_t st) {
+                          hipStream_t st, void *gate_up = nullptr) {
   const int w = xwidth(d);
   if (!bf16_path(d))
     return launch_simt_gu(static_cast<const float *>(x), perm, offsets, kept_offsets, d.k,
@@ -386,7 +388,12 @@ hipError_t do_ffn_gate_up(const moe_desc_t &d, const Layout &L, const void *x, c
   a.beta_g = d.beta_g;
   a.beta_u = d.beta_u;
   a.bm = routed_bm(d);
-  return launch_gemm(a, EP_GLU, gemm_mtile_bound(kept_rows_bound(d), d.N, a.bm), st);
+  if (gate_up != nullptr) {
+    a.out2 = gate_up;
+    a.ldg = 2 * (int64_t)d.h;
+  }
+  return launch_gemm(a, gate_up != nullptr ? EP_GLU_SAVE : EP_GLU,
+                     gemm_mtile_bound(kept_rows_bound(d), d.N, a.bm), st);
 }
 
 hipError_t do_ffn_down(const moe_desc_t &d, const Layout &L, const int32_t *kept_offsets,
@@ -492,6 +499,9 @@ moe_status_t forward_impl(const moe_desc_t *desc, const moe_weights_t *wts, cons
   moe_outputs_t o;
   memset(&o, 0, sizeof(o));
   if (out != nullptr) o = *out;
+  // Saved gate/up sums come from the tiled GEMM's epilogue (bf16 weights).
+  if (o.gate_up != nullptr && (ffn_path(d) != FFN_TILED || d.w_dtype != MOE_BF16))
+    return MOE_ERR_UNSUPPORTED;
   int32_t *idx = o.topk_idx ? o.topk_idx : region<int32_t>(ws, L.idx);
   float *tw = o.topk_w ? o.topk_w : region<float>(ws, L.w);
   float *stats = o.stats ? o.stats : region<float>(ws, L.stats);
@@ -524,7 +534,7 @@ moe_status_t forward_impl(const moe_desc_t *desc, const moe_weights_t *wts, cons
     x = xl;
   }
   MOE_TRY(do_ffn_gate_up(d, L, x, perm, offsets, kept_offsets, wts->W_gate, wts->W_up,
-                         wts->gate_scale, wts->up_scale, ws, st));
+                         wts->gate_scale, wts->up_scale, ws, st, o.gate_up));
   MOE_TRY(tr.mark());
   MOE_TRY(do_ffn_down(d, L, kept_offsets, wts->W_down, wts->down_scale, y_perm, ws, st));
   MOE_TRY(tr.mark());
@@ -566,17 +576,21 @@ moe_status_t forward_impl(const moe_desc_t *desc, const moe_weights_t *wts, cons
 // The experts' backward for one group of experts (see BwdDims): dx [T, w]
 // fp32 (written, not accumulated) and, when dWg is not null, the three weight
 // gradients.  L's regions are offsets into ws.
+// gate_up: the forward's saved [G | U] rows ([R, 2h] bf16), or null to
+// recompute them.
 hipError_t experts_bwd_core(const BwdDims &D, const BwdLayout &L, void *ws, const uint16_t *x,
                             const uint16_t *Wg, const uint16_t *Wu, const uint16_t *Wd,
                             const float *topk_w, const int32_t *offsets,
                             const int32_t *kept_offsets, const int32_t *perm,
-                            const int32_t *row_of, const uint16_t *dy, float *dx, float *dWg,
-                            float *dWu, float *dWd, hipStream_t st) {
+                            const int32_t *row_of, const uint16_t *gate_up, const uint16_t *dy,
+                            float *dx, float *dWg, float *dWu, float *dWd, hipStream_t st) {
   const int bm = D.bm;
   const int64_t mt = gemm_mtile_bound(D.R, D.N, bm);
   int32_t *tile_start = region<int32_t>(ws, L.tile_start);
   uint16_t *dy_perm = region<uint16_t>(ws, L.dy_perm);
-  uint16_t *G = region<uint16_t>(ws, L.g), *U = region<uint16_t>(ws, L.u);
+  const uint16_t *G = gate_up ? gate_up : region<uint16_t>(ws, L.g);
+  const uint16_t *U = gate_up ? gate_up + D.h : region<uint16_t>(ws, L.u);
+  const int64_t ldgu = gate_up ? 2 * (int64_t)D.h : (int64_t)D.h;
   uint16_t *dgu = region<uint16_t>(ws, L.dgu);
   float *dx_perm = region<float>(ws, L.dx_perm);
   const int64_t W = D.w, H = D.h;
@@ -589,8 +603,8 @@ hipError_t experts_bwd_core(const BwdDims &D, const BwdLayout &L, void *ws, cons
   MOE_BWD_TRY(launch_tile_prefix(kept_offsets, D.N, bm, tile_start, st));
   // dY = a dy_t per kept row.
   MOE_BWD_TRY(launch_bwd_gather_dy(dy, D.T, D.w, D.k, row_of, topk_w, dy_perm, st));
-  // G, U recomputed (bf16).
-  {
+  // G, U recomputed (bf16) unless the forward kept them.
+  if (gate_up == nullptr) {
     GemmArgs a;
     memset(&a, 0, sizeof(a));
     a.A = x;
@@ -607,8 +621,8 @@ hipError_t experts_bwd_core(const BwdDims &D, const BwdLayout &L, void *ws, cons
     a.offsets = offsets;
     a.kept_offsets = kept_offsets;
     a.tile_start = tile_start;
-    a.out = G;
-    a.out2 = U;
+    a.out = region<uint16_t>(ws, L.g);
+    a.out2 = region<uint16_t>(ws, L.u);
     a.ldo = H;
     a.bm = bm;
     MOE_BWD_TRY(launch_gemm(a, EP_GU, mt, st));
@@ -648,7 +662,7 @@ hipError_t experts_bwd_core(const BwdDims &D, const BwdLayout &L, void *ws, cons
     a.ldo = 2 * H;
     a.gsrc = G;
     a.usrc = U;
-    a.ldg = H;
+    a.ldg = ldgu;
     a.act = D.act;
     a.beta_g = D.bg;
     a.beta_u = D.bu;
@@ -694,8 +708,8 @@ hipError_t experts_bwd_core(const BwdDims &D, const BwdLayout &L, void *ws, cons
   MOE_BWD_TRY(launch_kseg(kept_offsets, D.N, kseg, st));
   MOE_BWD_TRY(launch_seg_transpose(dy_perm, nullptr, W, D.w, kept_offsets, offsets, nullptr, D.k,
                                    kseg, D.N, 0, 1.f, 1.f, dyt, Rp, st));
-  MOE_BWD_TRY(launch_seg_transpose(G, U, H, D.h, kept_offsets, offsets, nullptr, D.k, kseg, D.N,
-                                   D.act, D.bg, D.bu, ht, Rp, st));
+  MOE_BWD_TRY(launch_seg_transpose(G, U, ldgu, D.h, kept_offsets, offsets, nullptr, D.k, kseg,
+                                   D.N, D.act, D.bg, D.bu, ht, Rp, st));
   MOE_BWD_TRY(launch_seg_transpose(x, nullptr, W, D.w, kept_offsets, offsets, perm, D.k, kseg,
                                    D.N, 0, 1.f, 1.f, xt, Rp, st));
   MOE_BWD_TRY(launch_seg_transpose(dgu, nullptr, 2 * H, D.h, kept_offsets, offsets, nullptr, D.k,
@@ -890,9 +904,9 @@ moe_status_t moe_backward_workspace_bytes(const moe_desc_t *desc, size_t *bytes)
 moe_status_t moe_experts_backward(const moe_desc_t *desc, const moe_weights_t *wts, const void *u,
                                   const float *topk_w, const int32_t *offsets,
                                   const int32_t *kept_offsets, const int32_t *perm,
-                                  const int32_t *row_of, const void *dy, float *dx,
-                                  float *dW_gate, float *dW_up, float *dW_down, void *ws,
-                                  size_t ws_bytes, moe_stream_t stream) {
+                                  const int32_t *row_of, const void *gate_up, const void *dy,
+                                  float *dx, float *dW_gate, float *dW_up, float *dW_down,
+                                  void *ws, size_t ws_bytes, moe_stream_t stream) {
   const moe_status_t v = validate(desc);
   if (v != MOE_OK) return v;
   const moe_desc_t &d = *desc;
@@ -912,8 +926,9 @@ moe_status_t moe_experts_backward(const moe_desc_t *desc, const moe_weights_t *w
   return hip_status(experts_bwd_core(
       D, L, ws, static_cast<const uint16_t *>(u), static_cast<const uint16_t *>(wts->W_gate),
       static_cast<const uint16_t *>(wts->W_up), static_cast<const uint16_t *>(wts->W_down), topk_w,
-      offsets, kept_offsets, perm, row_of, static_cast<const uint16_t *>(dy), dx, dW_gate, dW_up,
-      dW_down, reinterpret_cast<hipStream_t>(stream)));
+      offsets, kept_offsets, perm, row_of, static_cast<const uint16_t *>(gate_up),
+      static_cast<const uint16_t *>(dy), dx, dW_gate, dW_up, dW_down,
+      reinterpret_cast<hipStream_t>(stream)));
 }
 
 moe_status_t moe_latent_backward(const moe_desc_t *desc, const moe_weights_t *wts, const void *u,
@@ -985,8 +1000,9 @@ moe_status_t moe_latent_backward(const moe_desc_t *desc, const moe_weights_t *wt
     MOE_TRY(experts_bwd_core(Dr, Lr, ws, xl, static_cast<const uint16_t *>(wts->W_gate),
                              static_cast<const uint16_t *>(wts->W_up),
                              static_cast<const uint16_t *>(wts->W_down), fwd->topk_w,
-                             fwd->offsets, fwd->kept_offsets, fwd->perm, fwd->row_of, dr, dxl,
-                             g->dW_gate, g->dW_up, g->dW_down, st));
+                             fwd->offsets, fwd->kept_offsets, fwd->perm, fwd->row_of,
+                             static_cast<const uint16_t *>(fwd->gate_up), dr, dxl, g->dW_gate,
+                             g->dW_up, g->dW_down, st));
   }
   // The router, driven by dr and the expert outputs at width l; writes du.
   MOE_TRY(dense_gemm(U, D, 0, static_cast<const uint16_t *>(wts->W_route), nullptr, 0, D, d.N, 1,
@@ -1019,7 +1035,7 @@ moe_status_t moe_latent_backward(const moe_desc_t *desc, const moe_weights_t *wt
     MOE_TRY(experts_bwd_core(Ds, Ls, ws, U, static_cast<const uint16_t *>(wts->Ws_gate),
                              static_cast<const uint16_t *>(wts->Ws_up),
                              static_cast<const uint16_t *>(wts->Ws_down), sw, soff, skoff, sperm,
-                             srow, DY, tmp, g->dWs_gate, g->dWs_up, g->dWs_down, st));
+                             srow, nullptr, DY, tmp, g->dWs_gate, g->dWs_up, g->dWs_down, st));
     MOE_TRY(launch_add_f32(g->du, tmp, T * D, st));
   }
   return MOE_OK;

@@ -264,10 +264,11 @@ def test_experts_backward_validates():
     w = L.MoeWeights(*([4096] * 4 + [None] * 9))
 
     def call(desc, wts=w, **kw):
-        ptrs = [kw.get(a, FAKE) for a in ("u", "tw", "off", "koff", "perm", "row", "dy", "dx",
-                                          "dwg", "dwu", "dwd")]
+        ptrs = [kw.get(a, FAKE) for a in ("u", "tw", "off", "koff", "perm", "row")] + [
+            kw.get("gu", None)] + [kw.get(a, FAKE) for a in ("dy", "dx", "dwg", "dwu", "dwd")]
         return eb(ctypes.byref(desc), ctypes.byref(wts), *ptrs, FAKE, kw.get("ws", big), n)
     assert call(d, ws=10) == L.MOE_ERR_WORKSPACE
+    assert call(d, gu=FAKE, ws=10) == L.MOE_ERR_WORKSPACE     # saved gate/up: optional
     for a in ("u", "tw", "off", "koff", "perm", "row", "dy", "dx"):
         assert call(d, **{a: n}) == L.MOE_ERR_ARG, a
     assert call(d, dwg=n, dwu=n, dwd=n, ws=10) == L.MOE_ERR_WORKSPACE   # input gradient only
@@ -313,3 +314,22 @@ def test_latent_backward_validates():
     assert call(d0, shared=False, ws=10) == L.MOE_ERR_WORKSPACE   # no shared pointers needed
     assert call(good()) == L.MOE_ERR_UNSUPPORTED                   # plain: the other two
     assert call(H.desc_for(C.LATENT_FP8)) == L.MOE_ERR_UNSUPPORTED
+
+
+def test_forward_saved_gate_up_validates():
+    # Saved gate/up sums come from the tiled GEMM with bf16 weights only.
+    lib = L.load()
+
+    def call(cfg):
+        d = H.desc_for(cfg)
+        w = L.MoeWeights(*([4096] * 4 + [None] * 9))
+        if cfg.latent:
+            w.W_ldown = w.W_lup = w.Ws_gate = w.Ws_up = w.Ws_down = 4096
+        if cfg.w_dtype in ("fp8", "mxfp4"):
+            w.gate_scale = w.up_scale = w.down_scale = 4096
+        o = L.MoeOutputs(gate_up=4096)
+        return lib.moe_forward(ctypes.byref(d), ctypes.byref(w), FAKE, FAKE, ctypes.byref(o),
+                               FAKE, 1 << 40, None)
+    assert call(C.MIXTRAL_DECODE) == L.MOE_ERR_UNSUPPORTED       # decode kernels
+    assert call(C.MIXTRAL_PREFILL_FP8) == L.MOE_ERR_UNSUPPORTED  # fp8 weights
+    assert call(C.TINY) == L.MOE_ERR_UNSUPPORTED                 # fp32 path

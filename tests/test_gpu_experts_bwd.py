@@ -122,3 +122,52 @@ def test_experts_backward_full_size_mixtral_dx_sampled():
     err = PR.rel_err(dx[tokens], ref["dx"][tokens])
     log(f"  dx rel err {err:.2e} on {len(tokens)} tokens ({int(keep.sum())} rows)")
     assert err <= PR.TOL["bf16"]
+
+
+@pytest.mark.parametrize("name", ["mixtral_small_t1000", "mix_situ_t900"])
+def test_experts_backward_with_saved_gate_up(name):
+    """The forward keeps each kept row's G | U (moe_outputs_t.gate_up); the
+    backward fed with them gives exactly the recomputing backward's results
+    (the same fp32 sums, rounded the same way), and the kept values match the
+    oracle's gate and up products."""
+    cfg = EB_CASES[name]
+    log(f"[experts backward] saved gate/up {name}")
+    desc = H.desc_for(cfg)
+    w = H.upload_layer(cfg)
+    u = H.to_device(cfg.u())
+    out = H.out_buffers(cfg)
+    out["gate_up"] = torch.empty((cfg.T * cfg.k, 2 * cfg.h), dtype=torch.bfloat16, device="cuda")
+    moe.moe_forward(desc, w, u, H.y_buffer(cfg), out, moe.workspace(desc))
+    torch.cuda.synchronize()
+    # Saved values against the oracle's G = W_gate x, U = W_up x per kept row.
+    u64 = O.expand(cfg.u())
+    perm = H.to_host(out["perm"]).astype(np.int64)
+    offs = H.to_host(out["offsets"]).astype(np.int64)
+    koffs = H.to_host(out["kept_offsets"]).astype(np.int64)
+    gu = H.to_host(out["gate_up"])
+    errs = []
+    for e in range(cfg.N):
+        kept = int(koffs[e + 1] - koffs[e])
+        if kept == 0:
+            continue
+        wg, wu, _ = (O.expand(m) for m in cfg.expert(e))
+        rows = np.arange(koffs[e], koffs[e] + kept)
+        x = u64[perm[offs[e]:offs[e] + kept] // cfg.k]
+        ref = np.concatenate([x @ wg.T, x @ wu.T], axis=1)
+        errs.append(PR.rel_err(O.expand(gu[rows]), ref))
+    log(f"  saved G|U rel err {max(errs):.2e}")
+    assert max(errs) <= PR.TOL["bf16"]
+    dy = H.to_device(S.normal_stored(41, 95, cfg.T * cfg.d, 0.5, "bf16").reshape(cfg.T, cfg.d))
+    res = []
+    for saved in (None, out["gate_up"]):
+        dx = torch.empty((cfg.T, cfg.d), device="cuda")
+        dW = {"dW_gate": torch.empty((cfg.N, cfg.h, cfg.d), device="cuda"),
+              "dW_up": torch.empty((cfg.N, cfg.h, cfg.d), device="cuda"),
+              "dW_down": torch.empty((cfg.N, cfg.d, cfg.h), device="cuda")}
+        moe.moe_experts_backward(desc, w, u, out["topk_w"], out["offsets"], out["kept_offsets"],
+                                 out["perm"], out["row_of"], dy, dx, moe.backward_workspace(desc),
+                                 gate_up=saved, **dW)
+        torch.cuda.synchronize()
+        res.append([dx] + [dW[k] for k in ("dW_gate", "dW_up", "dW_down")])
+    for a, b in zip(*res):
+        assert torch.equal(a, b)

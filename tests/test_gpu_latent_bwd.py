@@ -103,11 +103,14 @@ def test_latent_backward_parity(name):
     compare(cfg, g, ref)
 
 
-def test_latent_backward_after_gpu_forward():
+@pytest.mark.parametrize("save_gate_up", [False, True])
+def test_latent_backward_after_gpu_forward(save_gate_up):
     """The GPU forward's own outputs feed the backward (same selection as the
-    oracle's on this seed: every token's margin is far from a tie)."""
+    oracle's on this seed: every token's margin is far from a tie), with the
+    routed experts' G | U recomputed or kept by the forward."""
     cfg = LAT
-    log("[latent backward] chained forward -> backward latent_small_t700")
+    log(f"[latent backward] chained forward -> backward latent_small_t700, saved G|U "
+        f"{save_gate_up}")
     dy_st = S.normal_stored(44, 96, cfg.T * cfg.d, 0.5, "bf16").reshape(cfg.T, cfg.d)
     ref = oracle_backward(cfg, O.expand(dy_st), 0.3)
     desc = H.desc_for(cfg)
@@ -115,6 +118,8 @@ def test_latent_backward_after_gpu_forward():
     out = H.out_buffers(cfg)
     R = int(ref["disp"]["kept_offsets"][-1])
     out["y_perm"] = torch.empty((R, cfg.l), dtype=torch.float32, device="cuda")
+    if save_gate_up:
+        out["gate_up"] = torch.empty((R, 2 * cfg.h), dtype=torch.bfloat16, device="cuda")
     u = H.to_device(cfg.u())
     moe.moe_forward(desc, w, u, H.y_buffer(cfg), out, moe.workspace(desc))
     torch.cuda.synchronize()
