@@ -32,6 +32,8 @@ EB_CASES = {
     # more than 1024 rows per expert: W_down and W_gate | W_up through
     # K-contiguous copies (fewer rows: read as stored)
     "mix_copies_t4200": MIX_S.with_(name="mix_copies_t4200", T=4200, d=512, h=1024, N=4),
+    # decode-sized: a few rows per expert, some experts without rows
+    "mix_t37": CASES["mixtral_small_t37_decode"],
 }
 
 
@@ -171,3 +173,28 @@ def test_experts_backward_with_saved_gate_up(name):
         res.append([dx] + [dW[k] for k in ("dW_gate", "dW_up", "dW_down")])
     for a, b in zip(*res):
         assert torch.equal(a, b)
+
+
+def test_experts_backward_capacity_zero():
+    """Capacity 0: every slot is dropped, so every gradient is exactly zero."""
+    cfg = EB_CASES["mixtral_small_t1000"]
+    log("[experts backward] capacity 0")
+    desc = H.desc_for(cfg, capacity=0)
+    w = H.upload_layer(cfg)
+    u = H.to_device(cfg.u())
+    r = O.route(O.expand(cfg.u()), O.expand(cfg.w_route()), cfg.k, cfg.gate)
+    disp = O.dispatch(r["idx"], cfg.N, 0)
+    assert int(disp["kept_offsets"][-1]) == 0
+    i32 = lambda x: H.to_device(np.asarray(x).astype(np.int32))  # noqa: E731
+    dy = H.to_device(S.normal_stored(41, 95, cfg.T * cfg.d, 0.5, "bf16").reshape(cfg.T, cfg.d))
+    dx = torch.full((cfg.T, cfg.d), float("nan"), device="cuda")
+    dW = {"dW_gate": torch.full((cfg.N, cfg.h, cfg.d), float("nan"), device="cuda"),
+          "dW_up": torch.full((cfg.N, cfg.h, cfg.d), float("nan"), device="cuda"),
+          "dW_down": torch.full((cfg.N, cfg.d, cfg.h), float("nan"), device="cuda")}
+    moe.moe_experts_backward(desc, w, u, H.to_device(S.round_to(r["a"], "f32").reshape(-1)),
+                             i32(disp["offsets"]), i32(disp["kept_offsets"]), i32(disp["perm"]),
+                             i32(disp["row_of"]), dy, dx, moe.backward_workspace(desc), **dW)
+    torch.cuda.synchronize()
+    assert not torch.any(dx != 0)
+    for t in dW.values():
+        assert not torch.any(t != 0)
