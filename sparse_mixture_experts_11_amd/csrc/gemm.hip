@@ -20,7 +20,9 @@
 // MFMAs instead of in one burst after the barrier.
 // Tiles are found on the device from the per-group m-tile prefix and spread
 // over the XCDs in contiguous ranges; surplus workgroups exit, so the host
-// never waits for the routing result.
+// never waits for the routing result.  In an expert's last, partly filled
+// m-tile a wave whose last 32-row block holds no row skips that block's
+// fragment reads and MFMAs (a second copy of the main loop).
 //
 // Epilogues: EP_GLU pairs 128 gate columns with the matching 128 up columns in
 // one tile and writes act(gate, up) as bf16 (the hidden of a SwiGLU or
@@ -44,6 +46,7 @@
 // codes and widens them exactly to bf16, and the per-row scales multiply the
 // fp32 sums in the epilogue.
 #include <cmath>
+#include <type_traits>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -274,12 +277,17 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   bf16x8 fa[4], fb[2], na[4], nb[2];
+  // The main loop, for the first M of the wave's MI 32-row A blocks: a wave
+  // whose last block lies wholly past the tile's rows (an expert's last,
+  // partly filled m-tile) skips that block's fragment reads and MFMAs.
+  auto main_loop = [&](auto mconst) {
+  constexpr int M = decltype(mconst)::value;
   auto read_frags = [&](int kt, int ks, bf16x8 (&xa)[4], bf16x8 (&xb)[2]) {
     const char *ta = smem + (kt & 1) * kABytes;
     const char *tb = smem + 2 * kABytes + (kt % 3) * kBBytes;
     const int c = ks * 2 + khalf;
 #pragma unroll
-    for (int i = 0; i < MI; ++i) xa[i] = lds_frag(ta, arow_l[i], c);
+    for (int i = 0; i < M; ++i) xa[i] = lds_frag(ta, arow_l[i], c);
     if constexpr (BT) {
       typedef short v4s __attribute__((ext_vector_type(4)));
       typedef __attribute__((address_space(3))) v4s *lds_v4s_t;
@@ -300,14 +308,14 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
   };
   auto mfma16 = [&](const bf16x8 (&xa)[4], const bf16x8 (&xb)[2]) {
 #pragma unroll
-    for (int i = 0; i < MI; ++i)
+    for (int i = 0; i < M; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xb[j], xa[i], acc[i][j], 0, 0, 0);
   };
   auto copy_frags = [&]() {
 #pragma unroll
-    for (int i = 0; i < MI; ++i) fa[i] = na[i];
+    for (int i = 0; i < M; ++i) fa[i] = na[i];
 #pragma unroll
     for (int j = 0; j < 2; ++j) fb[j] = nb[j];
   };
@@ -319,7 +327,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
     READ_STMT;                                                          \
     EXTRA_STMT;                                                         \
     mfma16(fa, fb);                                                     \
-    _Pragma("unroll") for (int i_ = 0; i_ < MI; ++i_) {                 \
+    _Pragma("unroll") for (int i_ = 0; i_ < M; ++i_) {                  \
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                \
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                \
       __builtin_amdgcn_sched_group_barrier(EXTRA_MASK, EXTRA_N, 0);     \
@@ -377,6 +385,9 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
     MOE_SUBSTEP(read_frags(kt + 1, 3, na, nb), (void)0, 0x000, 0);
     mfma16(fa, fb);
   }
+  };  // main_loop
+  if (mrows - wm * (BM / 2) > (MI - 1) * 32) main_loop(std::integral_constant<int, MI>{});
+  else main_loop(std::integral_constant<int, MI - 1>{});
 #undef MOE_WAIT_LOADS
 #undef MOE_SUBSTEP
 
