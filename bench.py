@@ -138,10 +138,34 @@ def run_workload(cfg, steps, warmup, backward=True):
                  for j, s in enumerate(stages)}
     per_step = [ev[i][0].elapsed_time(ev[i][-1]) for i in range(steps)]
     kept = np.diff(H.to_host(out["kept_offsets"]))
+    graph_ms = None
+    if cfg.T <= 64:
+        # Launch-bound decode: the same forward captured once in a HIP graph
+        # and replayed (the library allocates nothing and never syncs).
+        cs = torch.cuda.Stream()
+        cs.wait_stream(stream)
+        with torch.cuda.stream(cs):
+            moe.moe_forward(desc, w, u, y, out, ws)
+        stream.wait_stream(cs)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            moe.moe_forward(desc, w, u, y, out, ws)
+        graph.replay()
+        torch.cuda.synchronize()
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        for _ in range(steps):
+            graph.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        graph_ms = g0.elapsed_time(g1) / steps
+        del graph
     r = {"ms_per_step": total_ms / steps, "stages_ms": per_stage,
          "traced_step_ms": {"median": float(np.median(per_step)), "min": float(np.min(per_step)),
                             "mean": float(np.mean(per_step))},
-         "alg": algorithmic(cfg, kept), "desc": desc}
+         "alg": algorithmic(cfg, kept), "desc": desc, "graph_ms_per_step": graph_ms}
     if cfg.act_dtype == "bf16" and cfg.router_dtype == "bf16":
         r["quantile_balancing"] = time_qb(moe, desc, u, w["W_route"], ws, cfg, steps)
         if not backward:
@@ -413,6 +437,8 @@ def main():
         "stages_ms": r["stages_ms"],
         "roofline": roof,
     }
+    if r.get("graph_ms_per_step") is not None:
+        line["graph_ms_per_step"] = r["graph_ms_per_step"]
     if "quantile_balancing" in r:
         line["quantile_balancing"] = r["quantile_balancing"]
     if "route_backward" in r:
@@ -433,7 +459,8 @@ def main():
         line[key] = {
             "workload": dc.name, "expert_weights": dc.w_dtype,
             "tokens_per_s": dc.T / (rd["ms_per_step"] / 1e3),
-            "ms_per_step": rd["ms_per_step"], "stages_ms": rd["stages_ms"],
+            "ms_per_step": rd["ms_per_step"], "graph_ms_per_step": rd["graph_ms_per_step"],
+            "stages_ms": rd["stages_ms"],
             "selected_expert_weight_bytes": wbytes,
             "hbm_frac_whole_forward": wbytes / (rd["ms_per_step"] / 1e3) / 1e9 / PEAK_HBM_GBS,
             "hbm_frac_expert_kernels": wbytes / ((rd["stages_ms"]["expert_gate_up"] +
