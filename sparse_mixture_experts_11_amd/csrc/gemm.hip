@@ -514,6 +514,28 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
         *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(a.out) + orow * a.ldo + col) = pk;
       }
     } else {
+      // The epilogue's own inputs (G and U; the fp32 addends) for this row
+      // block are all loaded before the first store, so their latencies
+      // overlap instead of queueing behind each store.
+      uint2 gpre[2][4], upre[2][4];
+      float4 apre0[2][4], apre1[2][4];
+      if constexpr (EPI == EP_GLU_BWD || EPI == EP_ADD_BF16) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int64_t col = n_tile * BN + wn * 64 + j * 32 + 8 * q + 4 * khalf;
+            if (col >= a.ncols) continue;
+            if constexpr (EPI == EP_GLU_BWD) {
+              gpre[j][q] = *reinterpret_cast<const uint2 *>(a.gsrc + orow * a.ldg + col);
+              upre[j][q] = *reinterpret_cast<const uint2 *>(a.usrc + orow * a.ldg + col);
+            } else {
+              apre0[j][q] = *reinterpret_cast<const float4 *>(a.add0 + orow * a.ldo + col);
+              if (a.add1 != nullptr)
+                apre1[j][q] = *reinterpret_cast<const float4 *>(a.add1 + orow * a.ldo + col);
+            }
+          }
+      }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
 #pragma unroll
@@ -529,8 +551,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
           } else if constexpr (EPI == EP_GLU_BWD) {
             // v = dH at (orow, col..col+3): the activation's backward with
             // the recomputed G and U of the same entries.
-            const uint2 gr = *reinterpret_cast<const uint2 *>(a.gsrc + orow * a.ldg + col);
-            const uint2 ur = *reinterpret_cast<const uint2 *>(a.usrc + orow * a.ldg + col);
+            const uint2 gr = gpre[j][q];
+            const uint2 ur = upre[j][q];
             const float gv[4] = {__uint_as_float(gr.x << 16), __uint_as_float(gr.x & 0xFFFF0000u),
                                  __uint_as_float(gr.y << 16), __uint_as_float(gr.y & 0xFFFF0000u)};
             const float uv[4] = {__uint_as_float(ur.x << 16), __uint_as_float(ur.x & 0xFFFF0000u),
@@ -550,10 +572,10 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
                 pu;
           } else {
             if constexpr (EPI == EP_ADD_BF16) {
-              const float4 p0 = *reinterpret_cast<const float4 *>(a.add0 + orow * a.ldo + col);
+              const float4 p0 = apre0[j][q];
               v[0] += p0.x; v[1] += p0.y; v[2] += p0.z; v[3] += p0.w;
               if (a.add1 != nullptr) {
-                const float4 p1 = *reinterpret_cast<const float4 *>(a.add1 + orow * a.ldo + col);
+                const float4 p1 = apre1[j][q];
                 v[0] += p1.x; v[1] += p1.y; v[2] += p1.z; v[3] += p1.w;
               }
             }
