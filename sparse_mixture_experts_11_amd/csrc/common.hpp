@@ -81,6 +81,21 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
   return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
+// OCP E8M0 scale byte -> its fp32 value 2^(s - 127) (0xFF: NaN).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
+  return __uint_as_float(s == 0 ? 0x00400000u : (s == 0xFF ? 0x7FC00000u : s << 23));
+}
+
+// Eight E2M1 codes (4 bytes, element 2i in the low nibble of byte i) times
+// 2^(s - 127) -> the bf16x8 MFMA operand (exact while in the bf16 range).
+__device__ __forceinline__ bf16x8 e2m1x8_to_bf16x8(uint32_t raw, float scale) {
+  const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(raw, scale, 0);
+  const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(raw, scale, 1);
+  const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(raw, scale, 2);
+  const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(raw, scale, 3);
+  return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
 // Backward of h = act(g, v): (dg, dv) from dh.  SwiGLU: silu'(g) =
 // s(g) (1 + g (1 - s(g))); SiTU-GLU caps both factors with beta tanh(x / beta)
 // first, which multiplies by 1 - tanh^2.

@@ -49,20 +49,6 @@ template <bool GLU, int WF>
 constexpr int unroll_of() { return WF == WF_BF16 ? (GLU ? 4 : 8) : 256 / kstep_bytes<WF>(); }
 
 // An E8M0 scale byte as the f32 2^(s - 127) (0: 2^-127, 0xFF: NaN).
-__device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
-  return __uint_as_float(s == 0 ? 0x00400000u : (s == 0xFF ? 0x7FC00000u : s << 23));
-}
-
-// Eight E2M1 codes (4 bytes, element 2i in the low nibble of byte i) times
-// 2^(s - 127) -> the bf16x8 MFMA operand (exact while in the bf16 range).
-__device__ __forceinline__ bf16x8 e2m1x8_to_bf16x8(uint32_t raw, float scale) {
-  const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(raw, scale, 0);
-  const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(raw, scale, 1);
-  const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(raw, scale, 2);
-  const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(raw, scale, 3);
-  return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-}
-
 // S1, S2: fp32 row scales [N][wrows] (WF_FP8) or E8M0 block scales
 // [N][wrows][K/32] (WF_MX4).
 template <bool GLU, int TG, int WF>

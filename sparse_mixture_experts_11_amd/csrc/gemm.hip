@@ -40,6 +40,12 @@
 // of the weights), and each B fragment is two ds_read_b64_tr_b16, which hand
 // every lane four consecutive k of one column.
 //
+// MXFP4 weights (routed experts, EP_GLU and EP_F32, K <= 4096): 8 KiB B
+// stages of 32-byte rows of packed E2M1 pairs, one direct load per wave per
+// stage; the tile's E8M0 scales (256 rows x K/32 bytes) are loaded into LDS
+// ahead of stage 0, and each fragment's 8 codes are widened with their
+// block's scale by v_cvt_scalef32_pk_bf16_fp4 (exact in bf16).
+//
 // FP8 weights (routed experts, EP_GLU and EP_F32): B holds OCP E4M3 codes,
 // one 64-byte row per weight row and k-step in a 16 KiB stage, 16-byte
 // chunk c of row r at chunk c ^ ((r >> 2) & 3); each fragment read takes 8
@@ -79,15 +85,33 @@ __device__ __forceinline__ bf16x8 lds_frag8(const char *tile, int r, int kq) {
   return e4m3x8_to_bf16x8(raw.x, raw.y);
 }
 
+// MXFP4 B stage: 32-byte rows of packed E2M1 (64 k per row and k-step),
+// 16-byte chunk c of row r at chunk c ^ ((r >> 3) & 1); four codes of the
+// fragment's eight (k-step quarter kq of row r) are one u32.
+__device__ __forceinline__ uint32_t lds_frag4(const char *tile, int r, int kq) {
+  const int c = kq >> 2;
+  return *reinterpret_cast<const uint32_t *>(tile + r * 32 + ((c ^ ((r >> 3) & 1)) << 4) +
+                                             4 * (kq & 3));
+}
+
 // BM = 256 (waves 128x64) or 192 (waves 96x64, for experts with few rows).
-template <int EPI, int BM, bool FP8 = false, bool KSEG = false, bool BT = false>
+// MX4: B holds MXFP4 weights (packed E2M1 + one E8M0 scale byte per 32 k);
+// K <= 4096 so that a tile's scales (256 rows x K/32 bytes) stay in LDS.
+template <int EPI, int BM, bool FP8 = false, bool KSEG = false, bool BT = false,
+          bool MX4 = false>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
   static_assert(!FP8 || EPI == EP_GLU || EPI == EP_F32, "fp8 weights: routed experts only");
+  static_assert(!MX4 || ((EPI == EP_GLU || EPI == EP_F32) && !FP8 && !KSEG && !BT),
+                "MXFP4 weights: routed experts only");
   static_assert(!KSEG || (EPI == EP_F32 && !FP8), "k segments: fp32 weight gradients");
   static_assert(!FP8 || EPI != EP_GLU_SAVE, "saved gate/up sums: bf16 weights");
   static_assert(!BT || (!FP8 && !KSEG && EPI != EP_GLU && EPI != EP_GU && EPI != EP_GLU_SAVE),
                 "transposed B: bf16, one B row per output column");
-  constexpr int ES = FP8 ? 1 : 2;          // bytes per B element
+  constexpr int ES = FP8 ? 1 : 2;          // bytes per B element (MX4: half a byte)
+  // B stage stride: MX4 stages are 8 KiB, and the tile's scale table
+  // follows the three stages.
+  constexpr int kBStage = MX4 ? 8192 : kBBytes;
+  constexpr int kScaleOff = 3 * 8192;
   constexpr int MI = BM / 64;              // 32-row A blocks per wave
   constexpr int kABytes = BM * BK * 2;     // 32 or 24 KiB per A stage
   // A (activations, L2-resident) double-buffered; B (weights, streamed) in a
@@ -167,8 +191,26 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
   // Transposed B: the stage is [64 k][256 n] (512-byte rows, 16-byte chunk c
   // of row k at chunk c ^ 4 (k & 3)); instruction i of wave w fills rows
   // 2 (8i + w) and 2 (8i + w) + 1, lane l row + l / 32, chunk l % 32.
+  // MXFP4: one instruction per wave fills rows 32 w .. 32 w + 31 (two lanes
+  // a row), waves 0-3 the gate rows and 4-7 the up rows of a GLU tile.
 #pragma unroll
   for (int i = 0; i < (FP8 ? 2 : 4); ++i) {
+    if constexpr (MX4) {
+      if (i == 0) {
+        const int r = tid >> 1;
+        const int pc = (tid & 1) ^ ((r >> 3) & 1);
+        int64_t brow;
+        if (glu) {
+          const int64_t n = n_tile * 128 + (r & 127);
+          brow = n < a.ncols ? n : a.ncols - 1;
+        } else {
+          const int64_t n = n_tile * BN + r;
+          brow = n < a.ncols ? n : a.ncols - 1;
+        }
+        boff[0] = (uint32_t)(brow * (a.K / 2)) + (uint32_t)(pc << 4);
+      }
+      continue;
+    }
     if constexpr (BT) {
       const int kr = 2 * (8 * i + wave) + (lane >> 5);
       const int c = (lane & 31) ^ ((kr & 3) << 2);
@@ -189,13 +231,16 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
     }
     boff[i] = (uint32_t)(brow * (KSEG ? a.ldb : a.K) * ES) + (uint32_t)(pc << 4);
   }
-  const char *Bg = static_cast<const char *>(a.B) + (int64_t)g * a.strideB * ES;
+  const char *Bg = static_cast<const char *>(a.B) + (MX4 ? (int64_t)g * a.strideB / 2
+                                                             : (int64_t)g * a.strideB * ES);
   const char *Ug = (glu || (BT && a.ksplit > 0))
-                       ? static_cast<const char *>(a.B2) + (int64_t)g * a.strideB * ES
+                       ? static_cast<const char *>(a.B2) +
+                             (MX4 ? (int64_t)g * a.strideB / 2 : (int64_t)g * a.strideB * ES)
                        : Bg;
   const uint32_t bbytes =
-      BT ? (uint32_t)((int64_t)(a.ksplit > 0 ? a.ksplit : a.K) * a.ldbt * 2)
-         : (uint32_t)((int64_t)a.ncols * (KSEG ? a.ldb : a.K) * ES);
+      BT    ? (uint32_t)((int64_t)(a.ksplit > 0 ? a.ksplit : a.K) * a.ldbt * 2)
+      : MX4 ? (uint32_t)((int64_t)a.ncols * a.K / 2)
+            : (uint32_t)((int64_t)a.ncols * (KSEG ? a.ldb : a.K) * ES);
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.A, 0xFFFFFFFFu);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bg, bbytes);
   const __amdgpu_buffer_rsrc_t ru = make_rsrc(Ug, bbytes);
@@ -215,8 +260,13 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
   };
   auto bload = [&](int k0, int buf, int half) {
     const uint32_t so = (uint32_t)(kbase + k0) * ES;
-    char *tb = smem + 2 * kABytes + buf * kBBytes;
-    if constexpr (BT) {
+    char *tb = smem + 2 * kABytes + buf * kBStage;
+    if constexpr (MX4) {
+      if (half == 0)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds((glu && wave >= 4) ? ru : rb,
+                                                 (lds_ptr_t)(tb + wave * 1024), 16, boff[0],
+                                                 (uint32_t)k0 / 2, 0, 0);
+    } else if constexpr (BT) {
       // A k-step lies wholly in B or in B2 (ksplit is a multiple of BK).
       const bool second = a.ksplit > 0 && k0 >= a.ksplit;
       const uint32_t sot = (uint32_t)((int64_t)(second ? k0 - a.ksplit : k0) * a.ldbt * 2);
@@ -284,11 +334,21 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
   constexpr int M = decltype(mconst)::value;
   auto read_frags = [&](int kt, int ks, bf16x8 (&xa)[4], bf16x8 (&xb)[2]) {
     const char *ta = smem + (kt & 1) * kABytes;
-    const char *tb = smem + 2 * kABytes + (kt % 3) * kBBytes;
+    const char *tb = smem + 2 * kABytes + (kt % 3) * kBStage;
     const int c = ks * 2 + khalf;
 #pragma unroll
     for (int i = 0; i < M; ++i) xa[i] = lds_frag(ta, arow_l[i], c);
-    if constexpr (BT) {
+    if constexpr (MX4) {
+      // 8 codes of quarter c (32-k block kt * 2 + ks / 2) times the block's
+      // scale from the tile's table.
+      const unsigned char *sct =
+          reinterpret_cast<const unsigned char *>(smem + 2 * kABytes + kScaleOff);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const float sc = e8m0_to_f32(sct[brow_l[j] * (a.K / 32) + kt * 2 + (ks >> 1)]);
+        xb[j] = e2m1x8_to_bf16x8(lds_frag4(tb, brow_l[j], c), sc);
+      }
+    } else if constexpr (BT) {
       typedef short v4s __attribute__((ext_vector_type(4)));
       typedef __attribute__((address_space(3))) v4s *lds_v4s_t;
       typedef short v8s __attribute__((ext_vector_type(8)));
@@ -344,14 +404,49 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
   // released by the barrier ending step kt-1), A(kt+2) during sub-step 3
   // after step kt's barrier.  Before a barrier only B(kt+2) may still fly.
   const int KT = (KSEG ? a.kseg[g + 1] - a.kseg[g] : a.K) / BK;
+  if constexpr (MX4) {
+    // The tile's scale table [256 rows][K/32 bytes], by dword loads ahead of
+    // stage 0 (so stage 0's wait covers them); every wave issues the same
+    // number of loads.
+    const int rdw = a.K / 128;  // dwords of scales per row
+    const int total = 256 * rdw;
+    const int64_t sbytes = (int64_t)a.ncols * (a.K / 32);
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(reinterpret_cast<const unsigned char *>(a.bscale) + g * sbytes,
+                  (uint32_t)sbytes);
+    const __amdgpu_buffer_rsrc_t rs2 =
+        glu ? make_rsrc(reinterpret_cast<const unsigned char *>(a.bscale2) + g * sbytes,
+                        (uint32_t)sbytes)
+            : rs;
+    char *st = smem + 2 * kABytes + kScaleOff;
+    for (int q = 0; q * kThreads < total; ++q) {
+      const int f0 = q * kThreads + tid;
+      const int f = f0 < total ? f0 : total - 1;
+      const int r = f / rdw, dw = f - r * rdw;
+      int64_t brow;
+      if (glu) {
+        const int64_t n = n_tile * 128 + (r & 127);
+        brow = n < a.ncols ? n : a.ncols - 1;
+      } else {
+        const int64_t n = n_tile * BN + r;
+        brow = n < a.ncols ? n : a.ncols - 1;
+      }
+      __builtin_amdgcn_raw_ptr_buffer_load_lds((glu && r >= 128) ? rs2 : rs,
+                                               (lds_ptr_t)(st + q * kThreads * 4 + wave * 256), 4,
+                                               (uint32_t)(brow * (a.K / 32) + 4 * dw), 0, 0, 0);
+    }
+  }
   aload(0, 0);
   bload(0, 0, 0);
   bload(0, 0, 1);
   aload(BK, 1);
   bload(BK, 1, 0);
   bload(BK, 1, 1);
-  // stage 0 landed: stage 1's MI A loads and 4 (fp8: 2) B loads may fly
-  if constexpr (MI == 4 && !FP8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  // stage 0 landed: stage 1's MI A loads and 4 (fp8: 2, MXFP4: 1) B loads
+  // may fly
+  if constexpr (MX4 && MI == 4) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+  else if constexpr (MX4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  else if constexpr (MI == 4 && !FP8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
   else if constexpr (MI == 3 && !FP8) asm volatile("s_waitcnt vmcnt(7)" ::: "memory");
   else if constexpr (MI == 4) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
   else asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
@@ -363,7 +458,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
     MOE_SUBSTEP(read_frags(kt, 2, na, nb), bload((kt + 2) * BK, (kt + 2) % 3, 1), 0x020, 1);
     MOE_SUBSTEP(read_frags(kt, 3, na, nb), (void)0, 0x000, 0);
     // stage kt+1 landed; only B(kt+2) may still fly
-    if constexpr (FP8) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+    if constexpr (MX4) asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
+    else if constexpr (FP8) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
     else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
     barrier_keep_loads();
     __builtin_amdgcn_sched_barrier(0);
@@ -649,6 +745,18 @@ hipError_t launch_kernel(const GemmArgs &a, int epi, int bm, int64_t grid, hipSt
     } else {
       if (bm == 192) grouped_gemm_kernel<EP_GLU_BWD, 192><<<g, b, 0, st>>>(a);
       else grouped_gemm_kernel<EP_GLU_BWD, 256><<<g, b, 0, st>>>(a);
+    }
+    return hipGetLastError();
+  }
+  if (a.mx4) {
+    if ((epi != EP_GLU && epi != EP_F32) || a.bscale == nullptr || a.K > 4096 || a.K % 128 != 0)
+      return hipErrorInvalidValue;
+    if (epi == EP_GLU) {
+      if (bm == 192) grouped_gemm_kernel<EP_GLU, 192, false, false, false, true><<<g, b, 0, st>>>(a);
+      else grouped_gemm_kernel<EP_GLU, 256, false, false, false, true><<<g, b, 0, st>>>(a);
+    } else {
+      if (bm == 192) grouped_gemm_kernel<EP_F32, 192, false, false, false, true><<<g, b, 0, st>>>(a);
+      else grouped_gemm_kernel<EP_F32, 256, false, false, false, true><<<g, b, 0, st>>>(a);
     }
     return hipGetLastError();
   }

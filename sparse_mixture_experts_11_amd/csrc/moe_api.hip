@@ -46,14 +46,17 @@ bool is_latent(const moe_desc_t &d) { return d.l > 0; }
 int xwidth(const moe_desc_t &d) { return is_latent(d) ? d.l : d.d; }
 bool bf16_path(const moe_desc_t &d) { return d.act_dtype == MOE_BF16; }
 bool decode_path(const moe_desc_t &d) { return bf16_path(d) && d.T <= kDecodeMaxRows; }
-// MXFP4 expert weights run on the decode kernels only (T <= 64 tokens), and
-// their 4-byte block-scale loads need each contraction width (the expert
-// input width and h) below one 2048-wide window set or a multiple of 512.
+// MXFP4 expert weights: on the decode kernels (T <= 64 tokens) their
+// 4-byte block-scale loads need each contraction width (the expert input
+// width and h) below one 2048-wide window set or a multiple of 512; the
+// tiled GEMM keeps a tile's scales in LDS, which bounds both widths by 4096.
 bool mxfp4_ok(const moe_desc_t &d) {
   if (d.w_dtype != MOE_MXFP4) return true;
   const int w = d.l > 0 ? d.l : d.d;
+  if (!bf16_path(d)) return false;
+  if (!decode_path(d)) return w <= 4096 && d.h <= 4096;
   auto width_ok = [](int k) { return k < 2048 || k % 512 == 0; };
-  return decode_path(d) && width_ok(w) && width_ok(d.h);
+  return width_ok(w) && width_ok(d.h);
 }
 bool router_gemm(const moe_desc_t &d) { return d.N > kRouteWaveMaxN; }
 bool fp8_experts(const moe_desc_t &d) { return d.w_dtype == MOE_FP8_E4M3; }
@@ -372,6 +375,7 @@ hipError_t do_ffn_gate_up(const moe_desc_t &d, const Layout &L, const void *x, c
   a.B2 = Wu;
   a.bscale = static_cast<const float *>(sg);
   a.bscale2 = static_cast<const float *>(su);
+  a.mx4 = mxfp4_experts(d) ? 1 : 0;
   a.strideB = (int64_t)d.h * w;
   a.K = w;
   a.ncols = d.h;
@@ -411,6 +415,7 @@ hipError_t do_ffn_down(const moe_desc_t &d, const Layout &L, const int32_t *kept
   a.lda = d.h;
   a.B = Wd;
   a.bscale = static_cast<const float *>(sd);
+  a.mx4 = mxfp4_experts(d) ? 1 : 0;
   a.strideB = (int64_t)w * d.h;
   a.K = d.h;
   a.ncols = w;

@@ -163,6 +163,8 @@ def test_status_strings():
 
 def call_forward_fp8(desc, scales=(4096, 4096, 4096), ws_bytes=10):
     w = L.MoeWeights(*([4096] * 4 + [None] * 6 + list(scales)))
+    if desc.l > 0:
+        w.W_ldown = w.W_lup = w.Ws_gate = w.Ws_up = w.Ws_down = 4096
     return L.load().moe_forward(ctypes.byref(desc), ctypes.byref(w), FAKE, FAKE, None, FAKE,
                                 ws_bytes, None)
 
@@ -205,10 +207,13 @@ def test_mxfp4_weights_validate():
     assert d.w_dtype == L.MOE_MXFP4
     assert call_forward_fp8(d) == L.MOE_ERR_WORKSPACE
     assert call_forward_fp8(d, scales=(None, None, None)) == L.MOE_ERR_ARG
-    # Decode kernels only (T <= 64), and 2048-or-wider contraction widths a
-    # multiple of 512.
-    big_t = H.desc_for(C.MIXTRAL_DECODE_MXFP4.with_(T=65))
+    # Decode kernels (T <= 64): 2048-or-wider contraction widths a multiple
+    # of 512; tiled GEMM (T > 64): both contraction widths at most 4096.
+    big_t = H.desc_for(C.MIXTRAL_DECODE_MXFP4.with_(T=65))      # h = 14336
     assert call_forward_fp8(big_t, ws_bytes=1 << 40) == L.MOE_ERR_UNSUPPORTED
+    tiled = H.desc_for(C.MIXTRAL_DECODE_MXFP4.with_(T=65, h=4096))
+    assert call_forward_fp8(tiled) == L.MOE_ERR_WORKSPACE
+    assert call_forward_fp8(H.desc_for(C.LATENT_MXFP4)) == L.MOE_ERR_WORKSPACE
     odd = H.desc_for(C.MIXTRAL_DECODE_MXFP4.with_(d=2176))
     assert call_forward_fp8(odd, ws_bytes=1 << 40) == L.MOE_ERR_UNSUPPORTED
     ok_small = H.desc_for(C.MIXTRAL_DECODE_MXFP4.with_(d=1152, h=1920))

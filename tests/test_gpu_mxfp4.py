@@ -1,9 +1,12 @@
 """MXFP4 routed-expert weights (OCP MX FP4: E2M1 codes two a byte, one E8M0
 scale per 32 elements of a row) on the GPU against the fp64 oracle, which
-expands every block as its scale times the codes' exact values.  MXFP4 runs
-on the decode kernels (up to 64 tokens): windows that fall in the tail loop
-only, the main loop on both projections, four token groups, the latent
-layer, edited block scales, and the full-size Mixtral decode workload."""
+expands every block as its scale times the codes' exact values.  Decode
+kernels (up to 64 tokens): windows that fall in the tail loop only, the main
+loop on both projections, four token groups, the latent layer.  Tiled GEMM
+(more tokens): both m-tile heights, capacity drops, contraction widths that
+are not a multiple of 256 (a scale table of an odd number of dwords per
+row), the latent layer.  Edited block scales on both paths, and the
+full-size Mixtral decode and LatentMoE workloads."""
 from __future__ import annotations
 
 import numpy as np
@@ -27,6 +30,12 @@ MX_CASES = {name: cfg.with_(name=name + "_mxfp4", w_dtype="mxfp4") for name, cfg
     ("mix_d2048_t40", MIX_S.with_(T=40, d=2048, h=2048)),           # main loop on both
     ("switch_small_t48_decode", CASES["switch_small_t48_decode"]),  # top-1 with capacity
     ("latent_small_decode_t20", CASES["latent_small_decode_t20"]),  # latent layer
+    # tiled GEMM
+    ("mixtral_small_t1000", CASES["mixtral_small_t1000"]),          # 256-row m-tiles
+    ("mixtral_small_t1200_bm192", CASES["mixtral_small_t1200_bm192"]),  # 192-row m-tiles
+    ("switch_small_t2000", CASES["switch_small_t2000"]),            # capacity drops
+    ("mix_d1152_t300", MIX_S.with_(T=300, d=1152, h=1920)),         # K/128 odd, h % 256 != 0
+    ("latent_small_t700", CASES["latent_small_t700"]),              # latent layer
 )}
 
 
@@ -39,7 +48,8 @@ def test_mxfp4_forward_parity(name):
     check_forward(cfg, ref, y, out)
 
 
-@pytest.mark.parametrize("name", ["mcu_t1", "mix_d2048_t40", "latent_small_decode_t20"])
+@pytest.mark.parametrize("name", ["mcu_t1", "mix_d2048_t40", "latent_small_decode_t20",
+                                  "mix_d1152_t300", "latent_small_t700"])
 def test_mxfp4_stage_expert_ffn(name):
     cfg = MX_CASES[name]
     log(f"[mxfp4 expert_ffn] {cfg.name}")
@@ -67,11 +77,12 @@ def test_mxfp4_stage_expert_ffn(name):
     assert err <= PR.TOL[cfg.act_dtype]
 
 
-def test_mxfp4_block_scales_are_per_block():
+@pytest.mark.parametrize("name", ["mix_d2048_t40", "mix_d1152_t300"])
+def test_mxfp4_block_scales_are_per_block(name):
     # Every E8M0 scale byte moved by a random -2..+2: the output must follow
     # the oracle with the same edited bytes (a scale applied to the wrong run
     # of 32, the wrong row or the wrong matrix fails this).
-    cfg = MX_CASES["mix_d2048_t40"]
+    cfg = MX_CASES[name]
     log(f"[mxfp4 scale edit] {cfg.name}")
     w = H.upload_layer(cfg)
     rng = np.random.default_rng(12)
@@ -100,3 +111,14 @@ def test_mxfp4_full_size_mixtral_decode():
     ref = oracle_forward(cfg)
     y, out = run_forward(cfg)
     check_forward(cfg, ref, y, out)
+
+
+@pytest.mark.timeout(1200)
+def test_mxfp4_full_size_latent():
+    from tests.test_gpu_parity import sample_tokens
+    cfg = C.LATENT_MXFP4
+    log(f"[mxfp4 full] {cfg.name}: uploading {cfg.N} experts")
+    tokens = sample_tokens(cfg.T, 6, cfg.seed)
+    ref = oracle_forward(cfg, tokens=tokens)
+    y, out = run_forward(cfg)
+    check_forward(cfg, ref, y, out, tokens=tokens)
