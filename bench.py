@@ -211,24 +211,35 @@ def time_latent_backward(moe, H, desc, u, w, y, out, ws, cfg, steps):
                  dWs_up=f(cfg.n_shared, cfg.h_shared, cfg.d),
                  dWs_down=f(cfg.n_shared, cfg.d, cfg.h_shared))
     bws = moe.backward_workspace(desc)
-    args = (desc, w, u, out, dy, g, bws)
-    moe.moe_latent_backward(*args, aux_scale=1.0)
-    a = torch.cuda.Event(enable_timing=True)
-    b = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    a.record()
-    for _ in range(steps):
-        moe.moe_latent_backward(*args, aux_scale=1.0)
-    b.record()
-    torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / steps
+
+    def timed(fwd):
+        moe.moe_latent_backward(desc, w, u, fwd, dy, g, bws, aux_scale=1.0)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(steps):
+            moe.moe_latent_backward(desc, w, u, fwd, dy, g, bws, aux_scale=1.0)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    ms = timed(out)
     T, d, l = cfg.T, cfg.d, cfg.l
     flops = (16.0 * kept * l * cfg.h + 16.0 * cfg.n_shared * T * d * cfg.h_shared
              + 10.0 * T * d * l + 6.0 * T * cfg.N * d)
     res = {"ms": ms, "algorithmic_tflop": flops / 1e12, "tflops": flops / (ms / 1e3) / 1e12,
            "mfma_frac": flops / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
            "workspace_gb": moe.moe_backward_workspace_bytes(desc) / 1e9}
-    del bws, g
+    # With the forward keeping the routed experts' G | U.
+    gu = torch.empty((max(kept, 1), 2 * cfg.h), dtype=torch.bfloat16, device="cuda")
+    fws = moe.workspace(desc)
+    out_gu = dict(out, gate_up=gu)
+    moe.moe_forward(desc, w, u, y, out_gu, fws)
+    torch.cuda.synchronize()
+    del fws
+    res["saved_gate_up_ms"] = timed(out_gu)
+    del bws, g, gu
     torch.cuda.empty_cache()
     return res
 
