@@ -40,7 +40,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-backward", action="store_true",
                    help="skip the backward-pass timings (forward and its stages only)")
-    p.add_argument("--cpu-sample-tokens", type=int, default=6144)
+    p.add_argument("--cpu-sample-tokens", type=int, default=1536,
+                   help="pilot sample of the CPU baseline (the timed sample aims at ~15 s)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 1 GiB device-to-device copy (3 times) so that "
                         "hardware byte counters can be scaled against a known size")
@@ -363,22 +364,32 @@ def time_qb(moe, desc, u, w_route, ws, cfg, steps):
     return res
 
 
-def cpu_baseline(cfg, n_tokens):
-    """The fp64 oracle, as it stands, on the first n tokens of the workload."""
+def cpu_baseline(cfg, n_tokens, target_s=15.0):
+    """The fp64 oracle, as it stands, on the first tokens of the workload:
+    a pilot run on n_tokens sizes the timed run to about target_s seconds
+    (at least n_tokens, at most the whole workload)."""
     import numpy as np  # noqa: F401
     from threadpoolctl import threadpool_info
 
     import oracle as O
 
-    sub = cfg.with_(T=n_tokens)
-    cap = None if cfg.capacity_factor is None else O.capacity_from_factor(
-        sub.T, sub.N, sub.k, sub.capacity_factor)
-    u = sub.u()
-    wr = sub.w_route()
-    t0 = time.perf_counter()
-    O.forward(u, wr, lambda e: sub.expert(e), k=sub.k, gate=sub.gate, act=sub.act,
-              capacity=cap, beta_g=sub.beta_g, beta_u=sub.beta_u, alpha=sub.aux_alpha)
-    dt = time.perf_counter() - t0
+    def run(n):
+        sub = cfg.with_(T=n)
+        cap = None if cfg.capacity_factor is None else O.capacity_from_factor(
+            sub.T, sub.N, sub.k, sub.capacity_factor)
+        u = sub.u()
+        wr = sub.w_route()
+        t0 = time.perf_counter()
+        O.forward(u, wr, lambda e: sub.expert(e), k=sub.k, gate=sub.gate, act=sub.act,
+                  capacity=cap, beta_g=sub.beta_g, beta_u=sub.beta_u, alpha=sub.aux_alpha)
+        return time.perf_counter() - t0
+
+    dt = run(n_tokens)
+    for _ in range(3):  # the fixed cost (expanding the weights) makes one pilot undershoot
+        if dt >= 0.6 * target_s or n_tokens >= cfg.T:
+            break
+        n_tokens = int(min(cfg.T, max(n_tokens + 1, n_tokens * target_s / dt)))
+        dt = run(n_tokens)
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     model = ""
     try:
