@@ -70,9 +70,9 @@ typedef enum {
    per byte, element 2i of a row in the low nibble of byte i, and one E8M0
    scale byte (2^(s - 127), 0xFF NaN) per 32 consecutive elements of a row.
    Both only for the routed experts' weights (w_dtype) under bf16
-   activations.  MXFP4 needs each contraction width (the expert input width
-   and h) below 2048 or a multiple of 512 on the decode path (T <= 64), and
-   both at most 4096 on the tiled path (MOE_ERR_UNSUPPORTED otherwise). */
+   activations.  MXFP4 on the decode path (T <= 64) needs each contraction
+   width (the expert input width and h) below 2048 or a multiple of 512
+   (MOE_ERR_UNSUPPORTED otherwise). */
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2, MOE_MXFP4 = 3 } moe_dtype_t;
 
 /* Combine weight of a selected expert (page "MoE: how sparse activation

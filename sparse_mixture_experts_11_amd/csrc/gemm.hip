@@ -40,10 +40,11 @@
 // of the weights), and each B fragment is two ds_read_b64_tr_b16, which hand
 // every lane four consecutive k of one column.
 //
-// MXFP4 weights (routed experts, EP_GLU and EP_F32, K <= 4096): 8 KiB B
-// stages of 32-byte rows of packed E2M1 pairs, one direct load per wave per
-// stage; the tile's E8M0 scales (256 rows x K/32 bytes) are loaded into LDS
-// ahead of stage 0, and each fragment's 8 codes are widened with their
+// MXFP4 weights (routed experts, EP_GLU and EP_F32): 8 KiB B stages of
+// 32-byte rows of packed E2M1 pairs, one direct load per wave per stage; the
+// tile's E8M0 scales go to LDS in 4096-k chunks (256 rows x 128 bytes), the
+// first ahead of stage 0 and each next one a k-step into the chunk before it
+// (two tables in turn), and each fragment's 8 codes are widened with their
 // block's scale by v_cvt_scalef32_pk_bf16_fp4 (exact in bf16).
 //
 // FP8 weights (routed experts, EP_GLU and EP_F32): B holds OCP E4M3 codes,
@@ -95,8 +96,7 @@ __device__ __forceinline__ uint32_t lds_frag4(const char *tile, int r, int kq) {
 }
 
 // BM = 256 (waves 128x64) or 192 (waves 96x64, for experts with few rows).
-// MX4: B holds MXFP4 weights (packed E2M1 + one E8M0 scale byte per 32 k);
-// K <= 4096 so that a tile's scales (256 rows x K/32 bytes) stay in LDS.
+// MX4: B holds MXFP4 weights (packed E2M1 + one E8M0 scale byte per 32 k).
 template <int EPI, int BM, bool FP8 = false, bool KSEG = false, bool BT = false,
           bool MX4 = false>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
@@ -111,7 +111,10 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
   // B stage stride: MX4 stages are 8 KiB, and the tile's scale table
   // follows the three stages.
   constexpr int kBStage = MX4 ? 8192 : kBBytes;
+  // Two 32 KiB scale tables follow: each holds one 4096-k chunk of the
+  // tile's E8M0 scales ([256 rows][128 bytes]); chunk c sits in table c & 1.
   constexpr int kScaleOff = 3 * 8192;
+  constexpr int kTab = 256 * 128;
   constexpr int MI = BM / 64;              // 32-row A blocks per wave
   constexpr int kABytes = BM * BK * 2;     // 32 or 24 KiB per A stage
   // A (activations, L2-resident) double-buffered; B (weights, streamed) in a
@@ -340,12 +343,12 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
     for (int i = 0; i < M; ++i) xa[i] = lds_frag(ta, arow_l[i], c);
     if constexpr (MX4) {
       // 8 codes of quarter c (32-k block kt * 2 + ks / 2) times the block's
-      // scale from the tile's table.
-      const unsigned char *sct =
-          reinterpret_cast<const unsigned char *>(smem + 2 * kABytes + kScaleOff);
+      // scale from the chunk's table.
+      const unsigned char *sct = reinterpret_cast<const unsigned char *>(
+          smem + 2 * kABytes + kScaleOff + ((kt >> 6) & 1) * kTab);
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const float sc = e8m0_to_f32(sct[brow_l[j] * (a.K / 32) + kt * 2 + (ks >> 1)]);
+        const float sc = e8m0_to_f32(sct[brow_l[j] * 128 + (kt & 63) * 2 + (ks >> 1)]);
         xb[j] = e2m1x8_to_bf16x8(lds_frag4(tb, brow_l[j], c), sc);
       }
     } else if constexpr (BT) {
@@ -404,12 +407,12 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
   // released by the barrier ending step kt-1), A(kt+2) during sub-step 3
   // after step kt's barrier.  Before a barrier only B(kt+2) may still fly.
   const int KT = (KSEG ? a.kseg[g + 1] - a.kseg[g] : a.K) / BK;
-  if constexpr (MX4) {
-    // The tile's scale table [256 rows][K/32 bytes], by dword loads ahead of
-    // stage 0 (so stage 0's wait covers them); every wave issues the same
-    // number of loads.
-    const int rdw = a.K / 128;  // dwords of scales per row
-    const int total = 256 * rdw;
+  // MXFP4: scale table of 4096-k chunk c into table buf, 16 dword loads per
+  // wave (every wave and every chunk the same count, for the in-order load
+  // counting); a short last chunk repeats its last dword.
+  auto load_table = [&](int c, int buf) {
+    const int kc = a.K / 32 - 128 * c;  // this chunk's scale bytes per row
+    const int rdw = (kc < 128 ? kc : 128) / 4;
     const int64_t sbytes = (int64_t)a.ncols * (a.K / 32);
     const __amdgpu_buffer_rsrc_t rs =
         make_rsrc(reinterpret_cast<const unsigned char *>(a.bscale) + g * sbytes,
@@ -418,11 +421,12 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
         glu ? make_rsrc(reinterpret_cast<const unsigned char *>(a.bscale2) + g * sbytes,
                         (uint32_t)sbytes)
             : rs;
-    char *st = smem + 2 * kABytes + kScaleOff;
-    for (int q = 0; q * kThreads < total; ++q) {
-      const int f0 = q * kThreads + tid;
-      const int f = f0 < total ? f0 : total - 1;
-      const int r = f / rdw, dw = f - r * rdw;
+    char *st = smem + 2 * kABytes + kScaleOff + buf * kTab;
+#pragma unroll
+    for (int q = 0; q < kTab / (4 * kThreads); ++q) {
+      const int f = q * kThreads + tid;
+      const int r = f >> 5, dw0 = f & 31;
+      const int dw = dw0 < rdw ? dw0 : rdw - 1;
       int64_t brow;
       if (glu) {
         const int64_t n = n_tile * 128 + (r & 127);
@@ -431,11 +435,12 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
         const int64_t n = n_tile * BN + r;
         brow = n < a.ncols ? n : a.ncols - 1;
       }
-      __builtin_amdgcn_raw_ptr_buffer_load_lds((glu && r >= 128) ? rs2 : rs,
-                                               (lds_ptr_t)(st + q * kThreads * 4 + wave * 256), 4,
-                                               (uint32_t)(brow * (a.K / 32) + 4 * dw), 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          (glu && r >= 128) ? rs2 : rs, (lds_ptr_t)(st + q * kThreads * 4 + wave * 256), 4,
+          (uint32_t)(brow * (a.K / 32) + 128 * c + 4 * dw), 0, 0, 0);
     }
-  }
+  };
+  if constexpr (MX4) load_table(0, 0);  // ahead of stage 0: its wait covers it
   aload(0, 0);
   bload(0, 0, 0);
   bload(0, 0, 1);
@@ -455,11 +460,21 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
   for (int kt = 0; kt + 2 < KT; ++kt) {
     __builtin_amdgcn_sched_barrier(0);
     MOE_SUBSTEP(read_frags(kt, 1, na, nb), bload((kt + 2) * BK, (kt + 2) % 3, 0), 0x020, 1);
+    // MXFP4, K > 4096: the next chunk's scales, one k-step into this chunk
+    // (table (c + 1) & 1 last served chunk c - 1, finished two barriers ago).
+    const bool tab = MX4 && (kt & 63) == 1 && (kt >> 6) < ((KT - 1) >> 6);
+    if constexpr (MX4) {
+      if (tab) load_table((kt >> 6) + 1, ((kt >> 6) + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     MOE_SUBSTEP(read_frags(kt, 2, na, nb), bload((kt + 2) * BK, (kt + 2) % 3, 1), 0x020, 1);
     MOE_SUBSTEP(read_frags(kt, 3, na, nb), (void)0, 0x000, 0);
-    // stage kt+1 landed; only B(kt+2) may still fly
-    if constexpr (MX4) asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
-    else if constexpr (FP8) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+    // stage kt+1 landed; only B(kt+2) may still fly (and a chunk's table
+    // loads issued after it)
+    if constexpr (MX4) {
+      if (tab) asm volatile("s_waitcnt vmcnt(17)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
+    } else if constexpr (FP8) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
     else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
     barrier_keep_loads();
     __builtin_amdgcn_sched_barrier(0);
@@ -749,7 +764,7 @@ hipError_t launch_kernel(const GemmArgs &a, int epi, int bm, int64_t grid, hipSt
     return hipGetLastError();
   }
   if (a.mx4) {
-    if ((epi != EP_GLU && epi != EP_F32) || a.bscale == nullptr || a.K > 4096 || a.K % 128 != 0)
+    if ((epi != EP_GLU && epi != EP_F32) || a.bscale == nullptr || a.K % 128 != 0)
       return hipErrorInvalidValue;
     if (epi == EP_GLU) {
       if (bm == 192) grouped_gemm_kernel<EP_GLU, 192, false, false, false, true><<<g, b, 0, st>>>(a);

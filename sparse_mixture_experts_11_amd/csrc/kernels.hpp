@@ -96,7 +96,7 @@ struct GemmArgs {
   int ksplit;
   // MXFP4 weights (mx4 != 0, EP_GLU / EP_F32): B holds packed E2M1 pairs
   // (row n of group g at byte (g * strideB + n * K) / 2) and bscale /
-  // bscale2 point at E8M0 bytes [G][ncols][K/32]; K <= 4096.
+  // bscale2 point at E8M0 bytes [G][ncols][K/32].
   int mx4;
 };
 // m-tile height for groups of about rows_per_group rows (192 or 256).

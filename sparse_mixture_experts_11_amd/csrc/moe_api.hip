@@ -49,12 +49,12 @@ bool decode_path(const moe_desc_t &d) { return bf16_path(d) && d.T <= kDecodeMax
 // MXFP4 expert weights: on the decode kernels (T <= 64 tokens) their
 // 4-byte block-scale loads need each contraction width (the expert input
 // width and h) below one 2048-wide window set or a multiple of 512; the
-// tiled GEMM keeps a tile's scales in LDS, which bounds both widths by 4096.
+// tiled GEMM takes any width (multiples of 128, as validated).
 bool mxfp4_ok(const moe_desc_t &d) {
   if (d.w_dtype != MOE_MXFP4) return true;
   const int w = d.l > 0 ? d.l : d.d;
   if (!bf16_path(d)) return false;
-  if (!decode_path(d)) return w <= 4096 && d.h <= 4096;
+  if (!decode_path(d)) return true;
   auto width_ok = [](int k) { return k < 2048 || k % 512 == 0; };
   return width_ok(w) && width_ok(d.h);
 }

@@ -205,11 +205,13 @@ MIXTRAL_DECODE_FP8 = MIXTRAL_DECODE.with_(name="mixtral_decode_t32_fp8", w_dtype
 MIXTRAL_PREFILL_FP8 = MIXTRAL_PREFILL.with_(name="mixtral_prefill_t16384_fp8", w_dtype="fp8")
 LATENT_FP8 = LATENT.with_(name="latent_t8192_fp8", w_dtype="fp8")
 # MXFP4 routed-expert weights (E2M1 in blocks of 32 with E8M0 scales): the
-# Mixtral decode workload and the LatentMoE layer (tiled GEMM).
+# Mixtral decode and prefill workloads and the LatentMoE layer.
 MIXTRAL_DECODE_MXFP4 = MIXTRAL_DECODE.with_(name="mixtral_decode_t32_mxfp4", w_dtype="mxfp4")
+MIXTRAL_PREFILL_MXFP4 = MIXTRAL_PREFILL.with_(name="mixtral_prefill_t16384_mxfp4",
+                                              w_dtype="mxfp4")
 LATENT_MXFP4 = LATENT.with_(name="latent_t8192_mxfp4", w_dtype="mxfp4")
 
 ALL = {c.name: c for c in (TINY, TINY_PLANTED, MCU_BATCH, MCU_DECODE, MIXTRAL_PREFILL,
                            MIXTRAL_DECODE, SWITCH_SKEWED, LATENT, MIXTRAL_DECODE_FP8,
                            MIXTRAL_PREFILL_FP8, LATENT_FP8, MIXTRAL_DECODE_MXFP4,
-                           LATENT_MXFP4)}
+                           MIXTRAL_PREFILL_MXFP4, LATENT_MXFP4)}

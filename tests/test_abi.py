@@ -208,18 +208,16 @@ def test_mxfp4_weights_validate():
     assert call_forward_fp8(d) == L.MOE_ERR_WORKSPACE
     assert call_forward_fp8(d, scales=(None, None, None)) == L.MOE_ERR_ARG
     # Decode kernels (T <= 64): 2048-or-wider contraction widths a multiple
-    # of 512; tiled GEMM (T > 64): both contraction widths at most 4096.
-    big_t = H.desc_for(C.MIXTRAL_DECODE_MXFP4.with_(T=65))      # h = 14336
-    assert call_forward_fp8(big_t, ws_bytes=1 << 40) == L.MOE_ERR_UNSUPPORTED
-    tiled = H.desc_for(C.MIXTRAL_DECODE_MXFP4.with_(T=65, h=4096))
-    assert call_forward_fp8(tiled) == L.MOE_ERR_WORKSPACE
+    # of 512; the tiled GEMM (T > 64) takes any width.
+    big_t = H.desc_for(C.MIXTRAL_DECODE_MXFP4.with_(T=65))      # h = 14336, tiled
+    assert call_forward_fp8(big_t) == L.MOE_ERR_WORKSPACE
     assert call_forward_fp8(H.desc_for(C.LATENT_MXFP4)) == L.MOE_ERR_WORKSPACE
     odd = H.desc_for(C.MIXTRAL_DECODE_MXFP4.with_(d=2176))
     assert call_forward_fp8(odd, ws_bytes=1 << 40) == L.MOE_ERR_UNSUPPORTED
     ok_small = H.desc_for(C.MIXTRAL_DECODE_MXFP4.with_(d=1152, h=1920))
     assert call_forward_fp8(ok_small) == L.MOE_ERR_WORKSPACE
     ffn = lib.moe_expert_ffn_scaled
-    assert ffn(ctypes.byref(big_t), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+    assert ffn(ctypes.byref(odd), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                FAKE, FAKE, 1 << 40, n) == L.MOE_ERR_UNSUPPORTED
 
 

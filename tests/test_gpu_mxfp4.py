@@ -4,9 +4,10 @@ expands every block as its scale times the codes' exact values.  Decode
 kernels (up to 64 tokens): windows that fall in the tail loop only, the main
 loop on both projections, four token groups, the latent layer.  Tiled GEMM
 (more tokens): both m-tile heights, capacity drops, contraction widths that
-are not a multiple of 256 (a scale table of an odd number of dwords per
-row), the latent layer.  Edited block scales on both paths, and the
-full-size Mixtral decode and LatentMoE workloads."""
+are not a multiple of 256, wider than one 4096-k scale chunk (a full and a
+short second chunk; a second chunk of two k-steps), the latent layer.
+Edited block scales on both paths, and the full-size Mixtral decode and
+prefill and LatentMoE workloads."""
 from __future__ import annotations
 
 import numpy as np
@@ -35,6 +36,8 @@ MX_CASES = {name: cfg.with_(name=name + "_mxfp4", w_dtype="mxfp4") for name, cfg
     ("mixtral_small_t1200_bm192", CASES["mixtral_small_t1200_bm192"]),  # 192-row m-tiles
     ("switch_small_t2000", CASES["switch_small_t2000"]),            # capacity drops
     ("mix_d1152_t300", MIX_S.with_(T=300, d=1152, h=1920)),         # K/128 odd, h % 256 != 0
+    ("mix_h5120_t600", MIX_S.with_(T=600, d=1024, h=5120)),         # down K = 5120: 2 chunks
+    ("mix_d4224_t400", MIX_S.with_(T=400, d=4224, h=1024)),         # gate/up K: 64 + 2 k-steps
     ("latent_small_t700", CASES["latent_small_t700"]),              # latent layer
 )}
 
@@ -49,7 +52,7 @@ def test_mxfp4_forward_parity(name):
 
 
 @pytest.mark.parametrize("name", ["mcu_t1", "mix_d2048_t40", "latent_small_decode_t20",
-                                  "mix_d1152_t300", "latent_small_t700"])
+                                  "mix_d1152_t300", "mix_h5120_t600", "latent_small_t700"])
 def test_mxfp4_stage_expert_ffn(name):
     cfg = MX_CASES[name]
     log(f"[mxfp4 expert_ffn] {cfg.name}")
@@ -77,7 +80,7 @@ def test_mxfp4_stage_expert_ffn(name):
     assert err <= PR.TOL[cfg.act_dtype]
 
 
-@pytest.mark.parametrize("name", ["mix_d2048_t40", "mix_d1152_t300"])
+@pytest.mark.parametrize("name", ["mix_d2048_t40", "mix_d1152_t300", "mix_h5120_t600"])
 def test_mxfp4_block_scales_are_per_block(name):
     # Every E8M0 scale byte moved by a random -2..+2: the output must follow
     # the oracle with the same edited bytes (a scale applied to the wrong run
@@ -119,6 +122,17 @@ def test_mxfp4_full_size_latent():
     cfg = C.LATENT_MXFP4
     log(f"[mxfp4 full] {cfg.name}: uploading {cfg.N} experts")
     tokens = sample_tokens(cfg.T, 6, cfg.seed)
+    ref = oracle_forward(cfg, tokens=tokens)
+    y, out = run_forward(cfg)
+    check_forward(cfg, ref, y, out, tokens=tokens)
+
+
+@pytest.mark.timeout(900)
+def test_mxfp4_full_size_mixtral_prefill():
+    from tests.test_gpu_parity import sample_tokens
+    cfg = C.MIXTRAL_PREFILL_MXFP4
+    log(f"[mxfp4 full] {cfg.name}")
+    tokens = sample_tokens(cfg.T, 24, cfg.seed)
     ref = oracle_forward(cfg, tokens=tokens)
     y, out = run_forward(cfg)
     check_forward(cfg, ref, y, out, tokens=tokens)
