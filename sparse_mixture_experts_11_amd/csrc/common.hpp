@@ -96,27 +96,6 @@ __device__ __forceinline__ bf16x8 e2m1x8_to_bf16x8(uint32_t raw, float scale) {
   return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
-// Backward of h = act(g, v): (dg, dv) from dh.  SwiGLU: silu'(g) =
-// s(g) (1 + g (1 - s(g))); SiTU-GLU caps both factors with beta tanh(x / beta)
-// first, which multiplies by 1 - tanh^2.
-__device__ __forceinline__ void glu_act_backward(float g, float v, float dh, int situ, float bg,
-                                                 float bu, float &dg, float &dv) {
-  float tg = 0.f, tv = 0.f;
-  if (situ) {
-    tg = tanhf(g / bg);
-    tv = tanhf(v / bu);
-    g = bg * tg;
-    v = bu * tv;
-  }
-  const float s = 1.0f / (1.0f + __expf(-g));
-  dg = dh * v * s * (1.0f + g * (1.0f - s));
-  dv = dh * g * s;
-  if (situ) {
-    dg *= 1.0f - tg * tg;
-    dv *= 1.0f - tv * tv;
-  }
-}
-
 // ---- precise activations (fp32 path) -------------------------------------
 __device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
 
@@ -163,6 +142,28 @@ __device__ __forceinline__ float glu_act_fast(float g, float v, int situ, float 
     v = bu * fast_tanh(v * __builtin_amdgcn_rcpf(bu));
   }
   return fast_silu(g) * v;
+}
+
+// Backward of h = act(g, v): (dg, dv) from dh, on the fast activations above
+// (the GEMM epilogue that feeds bf16 dG and dU).  SwiGLU: silu'(g) =
+// s(g) (1 + g (1 - s(g))); SiTU-GLU caps both factors with beta tanh(x / beta)
+// first, which multiplies by 1 - tanh^2.
+__device__ __forceinline__ void glu_act_backward_fast(float g, float v, float dh, int situ,
+                                                      float bg, float bu, float &dg, float &dv) {
+  float tg = 0.f, tv = 0.f;
+  if (situ) {
+    tg = fast_tanh(g * __builtin_amdgcn_rcpf(bg));
+    tv = fast_tanh(v * __builtin_amdgcn_rcpf(bu));
+    g = bg * tg;
+    v = bu * tv;
+  }
+  const float s = __builtin_amdgcn_rcpf(1.0f + fast_exp(-g));
+  dg = dh * v * s * (1.0f + g * (1.0f - s));
+  dv = dh * g * s;
+  if (situ) {
+    dg *= 1.0f - tg * tg;
+    dv *= 1.0f - tv * tv;
+  }
 }
 
 }  // namespace moe

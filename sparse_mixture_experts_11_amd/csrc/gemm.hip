@@ -671,7 +671,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
             float dg[4], du[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              glu_act_backward(gv[e], uv[e], v[e], a.act, a.beta_g, a.beta_u, dg[e], du[e]);
+              glu_act_backward_fast(gv[e], uv[e], v[e], a.act, a.beta_g, a.beta_u, dg[e],
+                                    du[e]);
             uint2 pg, pu;
             pg.x = pack_bf16x2_hw(dg[0], dg[1]);
             pg.y = pack_bf16x2_hw(dg[2], dg[3]);
