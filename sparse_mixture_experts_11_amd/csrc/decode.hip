@@ -48,7 +48,6 @@ constexpr int kstep_bytes() { return WF == WF_BF16 ? 64 : (WF == WF_FP8 ? 32 : 1
 template <bool GLU, int WF>
 constexpr int unroll_of() { return WF == WF_BF16 ? (GLU ? 4 : 8) : 256 / kstep_bytes<WF>(); }
 
-// An E8M0 scale byte as the f32 2^(s - 127) (0: 2^-127, 0xFF: NaN).
 // S1, S2: fp32 row scales [N][wrows] (WF_FP8) or E8M0 block scales
 // [N][wrows][K/32] (WF_MX4).
 template <bool GLU, int TG, int WF>
@@ -159,21 +158,33 @@ __global__ __launch_bounds__(256) void decode_kernel(
       return *reinterpret_cast<const bf16x8 *>(w + byte_off);
     }
   };
+  // The windows are software-pipelined: window i + 1's loads are issued as
+  // soon as window i's registers are parked in the slice, so they are in
+  // flight while window i is multiplied (Mixtral T=32 FP8 forward 0.299 ->
+  // 0.285 ms).  Not where the window in flight would cost a wave per SIMD:
+  // the MXFP4 gate/up (beside its scale and token registers it exceeds 256
+  // VGPRs: 0.134 -> 0.192 ms) and bf16 with three token groups.
+  constexpr bool kPipe = !(MX4 && GLU) && !(WF == WF_BF16 && TG == 3);
+  const int kfull = Kw - Kw % (32 * U);
+  u32x4 v[NM][kLoads];
+  auto load_window = [&](int kw) {
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int64_t off = (int64_t)(8 * (i % 4)) * rowK + 128 * (i / 4) + kbytes(kw);
+      v[0][i] = *reinterpret_cast<const u32x4 *>(g1 + off);
+      if (GLU) v[NM - 1][i] = *reinterpret_cast<const u32x4 *>(g2 + off);
+    }
+  };
+  if (kPipe && kfull > 0) load_window(0);
   int k = 0;
-  for (; k + 32 * U <= Kw; k += 32 * U) {
-    u32x4 v[NM][kLoads];
+  for (; k < kfull; k += 32 * U) {
+    if (!kPipe) load_window(k);
     // Token fragments of the whole window up front (MXFP4: in groups of 4
     // k-steps in its loop below; 16 k-steps of them would not fit beside
     // the loads, and one k-step at a time leaves their latency exposed:
     // 0.253 vs 0.235 ms for the Mixtral T=32 forward).
     constexpr int UB = MX4 ? 1 : U;
     bf16x8 b[TG][UB];
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      const int64_t off = (int64_t)(8 * (i % 4)) * rowK + 128 * (i / 4) + kbytes(k);
-      v[0][i] = *reinterpret_cast<const u32x4 *>(g1 + off);
-      if (GLU) v[NM - 1][i] = *reinterpret_cast<const u32x4 *>(g2 + off);
-    }
     if constexpr (!MX4) {
 #pragma unroll
       for (int tg = 0; tg < TG; ++tg)
@@ -193,6 +204,7 @@ __global__ __launch_bounds__(256) void decode_kernel(
         *reinterpret_cast<u32x4 *>(slice + m * RB * kPitch + r * kPitch + ((c ^ (r & 15)) << 4)) =
             v[m][i];
       }
+    if (kPipe && k + 32 * U < kfull) load_window(k + 32 * U);
     // MFMA operands: lane l takes row 16 rb + l%16, k values 32u + 8(l/16) .. +7.
     if constexpr (MX4) {
       // The window's 16 block scales of each of the lane's rows (4-byte
