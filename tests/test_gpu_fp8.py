@@ -25,6 +25,8 @@ FP8_CASES = {name: CASES[name].with_(name=name + "_fp8", w_dtype="fp8") for name
     "mcu_t4096",                    # GEMM with K = 128 in the down projection
     "mixtral_small_t37_decode",     # decode kernels
     "mixtral_small_t64_decode",     # decode kernels, four token groups
+    "mixtral_k2176_t30_decode",     # decode: pipelined windows and a remainder
+    "mixtral_k2176_t60_decode",
     "mixtral_small_t1000",          # GEMM, 256-row m-tiles
     "mixtral_small_t1200_bm192",    # GEMM, 192-row m-tiles
     "switch_small_t2000",           # top-1 with capacity drops

@@ -33,6 +33,10 @@ CASES = {
     "mixtral_small_t1000": MIX_S,
     "mixtral_small_t37_decode": MIX_S.with_(T=37),
     "mixtral_small_t64_decode": MIX_S.with_(T=64),
+    # decode with K = 2176: each wave's 544-wide k range holds several
+    # pipelined weight windows and a 32-wide remainder (two and four token groups)
+    "mixtral_k2176_t30_decode": MIX_S.with_(T=30, d=2176, h=2176),
+    "mixtral_k2176_t60_decode": MIX_S.with_(T=60, d=2176, h=2176),
     "mixtral_small_t65": MIX_S.with_(T=65),
     "mixtral_small_t3000_tiled": MIX_S.with_(T=3000),
     # about 300 rows per expert: 192-row m-tiles, two or three per expert
