@@ -20,9 +20,10 @@ hipError_t launch_route_wave(const void *u, bool u_bf16, const void *W, bool w_b
 hipError_t launch_topk_logits(const float *logits, int64_t T, int N, int k, int gate,
                               const float *bias, int32_t *idx, float *w, float *part_p,
                               int32_t *part_cnt, hipStream_t st);
-// f, P, N sum fP, alpha N sum fP from the per-wave partials.
-hipError_t launch_stats_finalize(const float *part_p, const int32_t *part_cnt, int waves,
-                                 int64_t T, int N, float alpha, float *stats, hipStream_t st);
+// f, P, N sum fP, alpha N sum fP from the per-wave partials (which it
+// overwrites: each 256-row slice's sums are left in the slice's first row).
+hipError_t launch_stats_finalize(float *part_p, int32_t *part_cnt, int waves, int64_t T, int N,
+                                 float alpha, float *stats, hipStream_t st);
 
 // ---- dispatch (dispatch.hip) ----------------------------------------------
 int dispatch_blocks(int64_t entries);

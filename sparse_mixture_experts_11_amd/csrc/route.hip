@@ -333,43 +333,71 @@ __global__ __launch_bounds__(kRouteBlock) void topk_logits_kernel(
   }
 }
 
-// stats = [f(N), P(N), N sum f P, alpha N sum f P], in two fixed-order passes:
-// one block per expert reduces its per-wave partials, then one block sums
-// f_i P_i over the experts.
-__global__ __launch_bounds__(256) void stats_expert_kernel(const float *__restrict__ part_p,
-                                                           const int32_t *__restrict__ part_cnt,
-                                                           int waves, int64_t T, int N,
-                                                           float *__restrict__ stats) {
+// stats = [f(N), P(N), N sum f P, alpha N sum f P] (page "MoE: how sparse
+// activation saves compute", section 3.5: f_i the share of tokens whose top
+// expert is i, P_i the mean router probability of expert i), in two
+// fixed-order passes over the per-wave partial rows [waves][N]:
+//  1. block (c, s) sums rows [256 s, 256 s + 256) of a band of EW experts
+//     (EW lanes a row, 256 / EW rows at a time: reads coalesced along the
+//     experts) and leaves the sums in the slice's first row;
+//  2. one block adds the slices' first rows per expert, writes f and P and
+//     sums f_i P_i.
+constexpr int kStatsSliceRows = 256;
+
+__global__ __launch_bounds__(256) void stats_slice_kernel(float *__restrict__ part_p,
+                                                          int32_t *__restrict__ part_cnt,
+                                                          int waves, int N, int EW) {
   __shared__ float sp[256];
-  __shared__ int64_t sc[256];
-  const int n = blockIdx.x;
+  __shared__ int sc[256];
+  const int rr = threadIdx.x / EW, e = threadIdx.x % EW;
+  const int rpp = 256 / EW;
+  const int n = blockIdx.x * EW + e;
+  const int w0 = blockIdx.y * kStatsSliceRows;
+  const int w1 = w0 + kStatsSliceRows < waves ? w0 + kStatsSliceRows : waves;
   float p = 0.f;
-  int64_t c = 0;
-  for (int wv = threadIdx.x; wv < waves; wv += 256) {
-    p += part_p[(int64_t)wv * N + n];
-    c += part_cnt[(int64_t)wv * N + n];
+  int c = 0;
+  if (n < N) {
+    for (int wv = w0 + rr; wv < w1; wv += rpp) {
+      p += part_p[(int64_t)wv * N + n];
+      c += part_cnt[(int64_t)wv * N + n];
+    }
   }
   sp[threadIdx.x] = p;
   sc[threadIdx.x] = c;
   __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if ((int)threadIdx.x < s) {
-      sp[threadIdx.x] += sp[threadIdx.x + s];
-      sc[threadIdx.x] += sc[threadIdx.x + s];
+  for (int s = rpp / 2; s > 0; s >>= 1) {
+    if (rr < s) {
+      sp[threadIdx.x] += sp[threadIdx.x + s * EW];
+      sc[threadIdx.x] += sc[threadIdx.x + s * EW];
     }
     __syncthreads();
   }
-  if (threadIdx.x == 0) {
-    stats[n] = (float)((double)sc[0] / (double)T);
-    stats[N + n] = sp[0] / (float)T;
+  // Only this block reads these columns of this slice, and it has finished.
+  if (rr == 0 && n < N) {
+    part_p[(int64_t)w0 * N + n] = sp[e];
+    part_cnt[(int64_t)w0 * N + n] = sc[e];
   }
 }
 
-__global__ __launch_bounds__(1024) void stats_total_kernel(int N, float alpha,
-                                                           float *__restrict__ stats) {
+__global__ __launch_bounds__(1024) void stats_total_kernel(const float *__restrict__ part_p,
+                                                           const int32_t *__restrict__ part_cnt,
+                                                           int slices, int64_t T, int N,
+                                                           float alpha, float *__restrict__ stats) {
   __shared__ float red[1024];
   float local = 0.f;
-  for (int n = threadIdx.x; n < N; n += 1024) local += stats[n] * stats[N + n];
+  for (int n = threadIdx.x; n < N; n += 1024) {
+    float p = 0.f;
+    int64_t c = 0;
+    for (int s = 0; s < slices; ++s) {
+      p += part_p[(int64_t)s * kStatsSliceRows * N + n];
+      c += part_cnt[(int64_t)s * kStatsSliceRows * N + n];
+    }
+    const float f = (float)((double)c / (double)T);
+    const float P = p / (float)T;
+    stats[n] = f;
+    stats[N + n] = P;
+    local += f * P;
+  }
   red[threadIdx.x] = local;
   __syncthreads();
   for (int s = 512; s > 0; s >>= 1) {
@@ -457,11 +485,15 @@ hipError_t launch_topk_logits(const float *logits, int64_t T, int N, int k, int 
   return hipGetLastError();
 }
 
-hipError_t launch_stats_finalize(const float *part_p, const int32_t *part_cnt, int waves,
-                                 int64_t T, int N, float alpha, float *stats, hipStream_t st) {
-  hipLaunchKernelGGL(stats_expert_kernel, dim3(N), dim3(256), 0, st, part_p, part_cnt, waves, T,
-                     N, stats);
-  hipLaunchKernelGGL(stats_total_kernel, dim3(1), dim3(1024), 0, st, N, alpha, stats);
+hipError_t launch_stats_finalize(float *part_p, int32_t *part_cnt, int waves, int64_t T, int N,
+                                 float alpha, float *stats, hipStream_t st) {
+  int ew = 8;  // expert band: a power of two, 8 .. 64
+  while (ew < 64 && ew < N) ew *= 2;
+  const int slices = (waves + kStatsSliceRows - 1) / kStatsSliceRows;
+  hipLaunchKernelGGL(stats_slice_kernel, dim3((N + ew - 1) / ew, slices), dim3(256), 0, st,
+                     part_p, part_cnt, waves, N, ew);
+  hipLaunchKernelGGL(stats_total_kernel, dim3(1), dim3(1024), 0, st, part_p, part_cnt, slices, T,
+                     N, alpha, stats);
   return hipGetLastError();
 }
 
