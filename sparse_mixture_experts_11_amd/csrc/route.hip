@@ -334,7 +334,7 @@ __global__ __launch_bounds__(kRouteBlock) void topk_logits_kernel(
 }
 
 // stats = [f(N), P(N), N sum f P, alpha N sum f P] (page "MoE: how sparse
-// activation saves compute", section 3.5: f_i the share of tokens whose top
+// activation saves compute", section 3.4: f_i the share of tokens whose top
 // expert is i, P_i the mean router probability of expert i), in two
 // fixed-order passes over the per-wave partial rows [waves][N]:
 //  1. block (c, s) sums rows [256 s, 256 s + 256) of a band of EW experts
