@@ -161,24 +161,30 @@ __global__ __launch_bounds__(256) void decode_kernel(
   // The windows are software-pipelined: window i + 1's loads are issued as
   // soon as window i's registers are parked in the slice, so they are in
   // flight while window i is multiplied (Mixtral T=32 FP8 forward 0.299 ->
-  // 0.285 ms).  Not where the window in flight would cost a wave per SIMD:
-  // the MXFP4 gate/up (beside its scale and token registers it exceeds 256
-  // VGPRs: 0.134 -> 0.192 ms) and bf16 with three token groups.
-  constexpr bool kPipe = !(MX4 && GLU) && !(WF == WF_BF16 && TG == 3);
+  // 0.285 ms).  Only as much of the window goes early as keeps two waves
+  // per SIMD: half of it for the MXFP4 gate/up (the whole window beside its
+  // scale and token registers exceeds 256 VGPRs: 0.134 -> 0.192 ms; half:
+  // 0.135 -> 0.131 ms), none for bf16 with three token groups.
+  constexpr bool kPipe = !(WF == WF_BF16 && TG == 3);
+  // Load instructions per matrix issued a window early; the rest are issued
+  // at the top of the window's own iteration.
+  constexpr int kEarly = (MX4 && GLU) ? kLoads / 2 : kLoads;
   const int kfull = Kw - Kw % (32 * U);
   u32x4 v[NM][kLoads];
-  auto load_window = [&](int kw) {
+  auto load_window = [&](int kw, int i0, int i1) {
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
+      if (i < i0 || i >= i1) continue;
       const int64_t off = (int64_t)(8 * (i % 4)) * rowK + 128 * (i / 4) + kbytes(kw);
       v[0][i] = *reinterpret_cast<const u32x4 *>(g1 + off);
       if (GLU) v[NM - 1][i] = *reinterpret_cast<const u32x4 *>(g2 + off);
     }
   };
-  if (kPipe && kfull > 0) load_window(0);
+  if (kPipe && kfull > 0) load_window(0, 0, kEarly);
   int k = 0;
   for (; k < kfull; k += 32 * U) {
-    if (!kPipe) load_window(k);
+    if (!kPipe) load_window(k, 0, kLoads);
+    else if (kEarly < kLoads) load_window(k, kEarly, kLoads);
     // Token fragments of the whole window up front (MXFP4: in groups of 4
     // k-steps in its loop below; 16 k-steps of them would not fit beside
     // the loads, and one k-step at a time leaves their latency exposed:
@@ -204,7 +210,7 @@ __global__ __launch_bounds__(256) void decode_kernel(
         *reinterpret_cast<u32x4 *>(slice + m * RB * kPitch + r * kPitch + ((c ^ (r & 15)) << 4)) =
             v[m][i];
       }
-    if (kPipe && k + 32 * U < kfull) load_window(k + 32 * U);
+    if (kPipe && k + 32 * U < kfull) load_window(k + 32 * U, 0, kEarly);
     // MFMA operands: lane l takes row 16 rb + l%16, k values 32u + 8(l/16) .. +7.
     if constexpr (MX4) {
       // The window's 16 block scales of each of the lane's rows (4-byte
