@@ -61,10 +61,20 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(
   const int n = threadIdx.x;  // N <= 1024: one expert per thread
   int total = 0;
   if (n < N) {
-    for (int b = 0; b < nblk; ++b) {
-      const int c = blk_counts[(int64_t)b * N + n];
-      blk_counts[(int64_t)b * N + n] = total;  // becomes the chunk's base
-      total += c;
+    // 16 chunks' counts are loaded before any of their bases is stored, so
+    // the loads are in flight together (a store to the same array would
+    // otherwise hold back the next load).
+    constexpr int kB = 16;
+    for (int b0 = 0; b0 < nblk; b0 += kB) {
+      int c[kB];
+#pragma unroll
+      for (int j = 0; j < kB; ++j)
+        c[j] = b0 + j < nblk ? blk_counts[(int64_t)(b0 + j) * N + n] : 0;
+#pragma unroll
+      for (int j = 0; j < kB; ++j) {
+        if (b0 + j < nblk) blk_counts[(int64_t)(b0 + j) * N + n] = total;  // the chunk's base
+        total += c[j];
+      }
     }
     counts[n] = total;
   }
