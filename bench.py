@@ -37,6 +37,11 @@ def parse():
                    help="the decode workload with FP8 E4M3 expert weights ('' to skip)")
     p.add_argument("--mxfp4-decode-workload", default="mixtral_decode_t32_mxfp4",
                    help="the decode workload with MXFP4 expert weights ('' to skip)")
+    p.add_argument("--switch-workload", default="switch_top1_skewed_t16384",
+                   help="the skewed top-1 workload with a capacity limit, reported with its "
+                        "balance statistics and drop ledger ('' to skip)")
+    p.add_argument("--latent-workload", default="latent_t8192",
+                   help="the LatentMoE workload ('' to skip)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-backward", action="store_true",
                    help="skip the backward-pass timings (forward and its stages only)")
@@ -96,6 +101,57 @@ def measured_traffic(workload):
     return rec["bytes"]
 
 
+class SclkSampler:
+    """Samples the GPU's shader clock (the active level of the amdgpu
+    driver's pp_dpm_sclk table) from a host thread while queued work runs."""
+
+    def __init__(self, period_s=0.002):
+        import glob
+        self.path = next((p for p in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+                          if os.access(p, os.R_OK)), None)
+        self.period = period_s
+        self.samples = []
+
+    def _read(self):
+        try:
+            with open(self.path) as f:
+                for ln in f:
+                    if ln.rstrip().endswith("*"):
+                        return float(ln.split(":")[1].strip().split("M")[0])
+        except (OSError, ValueError, IndexError):
+            return None
+        return None
+
+    def _loop(self):
+        while not self.stop.is_set():
+            v = self._read()
+            if v is not None:
+                self.samples.append(v)
+            self.stop.wait(self.period)
+
+    def __enter__(self):
+        import threading
+        self.stop = threading.Event()
+        self.thread = None
+        if self.path is not None:
+            self.thread = threading.Thread(target=self._loop, daemon=True)
+            self.thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self.stop.set()
+        if self.thread is not None:
+            self.thread.join()
+
+    def summary(self):
+        if not self.samples:
+            return None
+        import numpy as np
+        s = np.array(self.samples)
+        return {"median": float(np.median(s)), "min": float(s.min()), "max": float(s.max()),
+                "samples": int(s.size), "source": self.path}
+
+
 def run_workload(cfg, steps, warmup, backward=True):
     import numpy as np
     import torch
@@ -125,7 +181,8 @@ def run_workload(cfg, steps, warmup, backward=True):
     for _ in range(steps):
         moe.moe_forward(desc, w, u, y, out, ws)
     t_end.record(stream)
-    torch.cuda.synchronize()
+    with SclkSampler() as sclk:   # while the queued steps run
+        torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
     # Stage breakdown: the same number of forwards again, each with HIP events
     # recorded between its stages on the same stream.  The markers cost a few
@@ -166,7 +223,8 @@ def run_workload(cfg, steps, warmup, backward=True):
     r = {"ms_per_step": total_ms / steps, "stages_ms": per_stage,
          "traced_step_ms": {"median": float(np.median(per_step)), "min": float(np.min(per_step)),
                             "mean": float(np.mean(per_step))},
-         "alg": algorithmic(cfg, kept), "desc": desc, "graph_ms_per_step": graph_ms}
+         "alg": algorithmic(cfg, kept), "desc": desc, "graph_ms_per_step": graph_ms,
+         "sclk_mhz": sclk.summary(), "counts": H.to_host(out["counts"]), "kept": kept, "stats": H.to_host(out["stats"])}
     if cfg.act_dtype == "bf16" and cfg.router_dtype == "bf16":
         r["quantile_balancing"] = time_qb(moe, desc, u, w["W_route"], ws, cfg, steps)
         if not backward:
@@ -364,32 +422,8 @@ def time_qb(moe, desc, u, w_route, ws, cfg, steps):
     return res
 
 
-def cpu_baseline(cfg, n_tokens, target_s=15.0):
-    """The fp64 oracle, as it stands, on the first tokens of the workload:
-    a pilot run on n_tokens sizes the timed run to about target_s seconds
-    (at least n_tokens, at most the whole workload)."""
-    import numpy as np  # noqa: F401
+def _host_info():
     from threadpoolctl import threadpool_info
-
-    import oracle as O
-
-    def run(n):
-        sub = cfg.with_(T=n)
-        cap = None if cfg.capacity_factor is None else O.capacity_from_factor(
-            sub.T, sub.N, sub.k, sub.capacity_factor)
-        u = sub.u()
-        wr = sub.w_route()
-        t0 = time.perf_counter()
-        O.forward(u, wr, lambda e: sub.expert(e), k=sub.k, gate=sub.gate, act=sub.act,
-                  capacity=cap, beta_g=sub.beta_g, beta_u=sub.beta_u, alpha=sub.aux_alpha)
-        return time.perf_counter() - t0
-
-    dt = run(n_tokens)
-    for _ in range(3):  # the fixed cost (expanding the weights) makes one pilot undershoot
-        if dt >= 0.6 * target_s or n_tokens >= cfg.T:
-            break
-        n_tokens = int(min(cfg.T, max(n_tokens + 1, n_tokens * target_s / dt)))
-        dt = run(n_tokens)
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     model = ""
     try:
@@ -397,10 +431,153 @@ def cpu_baseline(cfg, n_tokens, target_s=15.0):
             model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
     except OSError:
         pass
-    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+    return int(threads), model
+
+
+def _oracle_sample(cfg, n, expert_budget_bytes):
+    """Inputs of one oracle forward over the first n tokens of the workload
+    (the layer taken at T = n, so a capacity limit is recomputed for n), with
+    every weight the sample touches generated and expanded to fp64 up front,
+    so that the timed region holds the oracle's arithmetic only.  For the
+    latent layer n shrinks until the touched routed experts fit the budget."""
+    import numpy as np
+
+    import oracle as O
+
+    while True:
+        sub = cfg.with_(T=n)
+        u = sub.u()
+        wr = sub.w_route()
+        idx = O.route(O.expand(u), O.expand(wr), sub.k, sub.gate)["idx"]
+        touched = sorted(set(int(e) for e in np.unique(idx)))
+        per = 3 * sub.h * sub.x_width * 8
+        if not cfg.latent or len(touched) * per <= expert_budget_bytes or n == 1:
+            break
+        n = max(1, n // 2)
+    experts = {e: tuple(O.expand(m) for m in sub.expert(e)) for e in touched}
+
+    def kw(T):
+        cap = None if cfg.capacity_factor is None else O.capacity_from_factor(
+            T, sub.N, sub.k, sub.capacity_factor)
+        return dict(k=sub.k, gate=sub.gate, act=sub.act, capacity=cap, beta_g=sub.beta_g,
+                    beta_u=sub.beta_u, alpha=sub.aux_alpha)
+
+    if cfg.latent:
+        shared = [tuple(O.expand(m) for m in sub.shared(j)) for j in range(sub.n_shared)]
+        wld, wlu = O.expand(sub.w_ldown()), O.expand(sub.w_lup())
+
+        def run(rows=None):
+            uu = u if rows is None else u[rows]
+            return O.latent_forward(uu, wr, experts.__getitem__, wld, wlu, shared.__getitem__,
+                                    sub.n_shared, rms_eps=sub.rms_eps, **kw(uu.shape[0]))
+    else:
+        def run(rows=None):
+            uu = u if rows is None else u[rows]
+            return O.forward(uu, wr, experts.__getitem__, **kw(uu.shape[0]))
+    return n, run
+
+
+def cpu_baseline(cfg, n_tokens, target_s=15.0, expert_budget_bytes=24e9):
+    """The fp64 oracle, as it stands, on the host: a forward over the first n
+    tokens of the workload with its weights already generated and expanded
+    (the generator is not timed).  A pilot on n_tokens sizes the timed
+    sample to about target_s seconds (at most the whole workload).  A second
+    figure runs the oracle on one thread over a deterministic 1/64 subsample
+    of the timed tokens (every 64th) and scales it up to the whole sample:
+    an extrapolation, labelled as one."""
+    from threadpoolctl import threadpool_limits
+
+    def timed(n):
+        n, run = _oracle_sample(cfg, n, expert_budget_bytes)
+        t0 = time.perf_counter()
+        run()
+        return n, run, time.perf_counter() - t0
+
+    n, run, dt = timed(n_tokens)
+    for _ in range(3):
+        if dt >= 0.6 * target_s or n >= cfg.T or cfg.latent:
+            break
+        n, run, dt = timed(int(min(cfg.T, max(n + 1, n * target_s / dt))))
+    threads, model = _host_info()
+    # Single thread on every 64th token of the sample (the layer taken at the
+    # subsample's size: routing, dispatch and experts over those tokens).
+    rows = list(range(0, n, 64))
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        run(rows)
+        dt1 = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "cpu_model": model, "host_cpus": os.cpu_count(),
-            "sample": f"fp64 oracle forward of the first {n_tokens} of {cfg.T} tokens "
-                      f"(same weights; includes expanding the stored bf16 weights), {dt:.1f} s"}
+            "sample": f"fp64 oracle forward of the first {n} of {cfg.T} tokens, {dt:.1f} s; "
+                      "weights generated and expanded to fp64 before timing",
+            "single_thread_extrapolated": {
+                "value": len(rows) / dt1, "unit": "tokens/s", "cores": 1,
+                "sample": f"every 64th of those {n} tokens ({len(rows)} tokens) on one thread, "
+                          f"{dt1:.2f} s; extrapolation: the {n}-token sample would take "
+                          f"{dt1 * n / len(rows):.1f} s"}}
+
+
+def cpu_baseline_balance_stats(cfg):
+    """The oracle's balance statistics of a whole workload (routing only, all
+    T tokens), for comparison with the GPU's."""
+    import oracle as O
+
+    r = O.route(O.expand(cfg.u()), O.expand(cfg.w_route()), cfg.k, cfg.gate)
+    s = O.balance_stats(r["p"], cfg.aux_alpha)
+    return {"f": [float(x) for x in s["f"]], "P": [float(x) for x in s["P"]],
+            "n_sum_fP": float(s["n_sum_fP"]), "aux": float(s["aux"])}
+
+
+def switch_section(cfg, r):
+    """A top-1 layer with a capacity limit: throughput, the gate/up kernel on
+    its kept rows, the balance statistics f_i, P_i, N sum f P and the
+    auxiliary loss alpha N sum f P (page "MoE: how sparse activation saves
+    compute", section 3.4), and the capacity ledger of section 3.8 (tokens
+    over capacity, empty slots)."""
+    from tests import harness as H
+
+    N = cfg.N
+    a = r["alg"]
+    cap = H.capacity_of(cfg)
+    counts = [int(c) for c in r["counts"]]
+    st = r["stats"]
+    t_gu = r["stages_ms"]["expert_gate_up"] / 1e3
+    return {
+        "workload": cfg.name, "T": cfg.T, "k": cfg.k, "gate": cfg.gate,
+        "tokens_per_s": cfg.T / (r["ms_per_step"] / 1e3), "ms_per_step": r["ms_per_step"],
+        "stages_ms": r["stages_ms"], "sclk_mhz": r["sclk_mhz"],
+        "expert_gate_up_kept_rows": {"rows": a["rows"], "tflop": a["gu_flops"] / 1e12,
+                                     "tflops": a["gu_flops"] / t_gu / 1e12,
+                                     "mfma_frac": a["gu_flops"] / t_gu / 1e12 / PEAK_BF16_TFLOPS},
+        "capacity": cap, "loads": counts, "kept": [int(c) for c in r["kept"]],
+        "dropped": int(sum(max(c - cap, 0) for c in counts)),
+        "empty_slots": int(sum(max(cap - c, 0) for c in counts)),
+        "f": [float(x) for x in st[:N]], "P": [float(x) for x in st[N:2 * N]],
+        "n_sum_fP": float(st[2 * N]), "aux_alpha": cfg.aux_alpha, "aux": float(st[2 * N + 1]),
+    }
+
+
+def latent_section(cfg, r):
+    """The LatentMoE layer: throughput, stages, and the routed expert GEMMs
+    against HBM (their weights, 146 rows per expert on average, make them
+    bandwidth-bound)."""
+    a = r["alg"]
+    t_gu = r["stages_ms"]["expert_gate_up"] / 1e3
+    t_dn = r["stages_ms"]["expert_down"] / 1e3
+    sec = {
+        "workload": cfg.name, "T": cfg.T, "d": cfg.d, "l": cfg.l, "H": cfg.h, "E": cfg.N,
+        "k": cfg.k, "n_shared": cfg.n_shared, "expert_weights": cfg.w_dtype,
+        "tokens_per_s": cfg.T / (r["ms_per_step"] / 1e3), "ms_per_step": r["ms_per_step"],
+        "stages_ms": r["stages_ms"], "sclk_mhz": r["sclk_mhz"],
+        "routed_gate_up": {"weight_bytes": a["gu_bytes"], "gb_s": a["gu_bytes"] / t_gu / 1e9,
+                           "hbm_frac": a["gu_bytes"] / t_gu / 1e9 / PEAK_HBM_GBS},
+        "routed_down": {"weight_bytes": a["down_bytes"], "gb_s": a["down_bytes"] / t_dn / 1e9,
+                        "hbm_frac": a["down_bytes"] / t_dn / 1e9 / PEAK_HBM_GBS},
+        "experts_touched": a["touched"], "rows": a["rows"],
+    }
+    if "latent_backward" in r:
+        sec["latent_backward"] = r["latent_backward"]
+    return sec
 
 
 def main():
@@ -457,6 +634,7 @@ def main():
         "expert_stage_tflops": total_flops / (
             (r["stages_ms"]["expert_gate_up"] + r["stages_ms"]["expert_down"]) / 1e3) / 1e12,
         "stages_ms": r["stages_ms"],
+        "sclk_mhz": r["sclk_mhz"],
         "roofline": roof,
     }
     if r.get("graph_ms_per_step") is not None:
@@ -482,7 +660,7 @@ def main():
             "workload": dc.name, "expert_weights": dc.w_dtype,
             "tokens_per_s": dc.T / (rd["ms_per_step"] / 1e3),
             "ms_per_step": rd["ms_per_step"], "graph_ms_per_step": rd["graph_ms_per_step"],
-            "stages_ms": rd["stages_ms"],
+            "stages_ms": rd["stages_ms"], "sclk_mhz": rd["sclk_mhz"],
             "selected_expert_weight_bytes": wbytes,
             "hbm_frac_whole_forward": wbytes / (rd["ms_per_step"] / 1e3) / 1e9 / PEAK_HBM_GBS,
             "hbm_frac_expert_kernels": wbytes / ((rd["stages_ms"]["expert_gate_up"] +
@@ -490,6 +668,16 @@ def main():
             / 1e9 / PEAK_HBM_GBS,
         }
         del rd
+    if args.switch_workload and args.switch_workload != args.workload:
+        sc = C.ALL[args.switch_workload]
+        print(f"[bench] {sc.name}", file=sys.stderr, flush=True)
+        line["switch_top1"] = switch_section(sc, run_workload(sc, args.steps, args.warmup,
+                                                              backward=False))
+    if args.latent_workload and args.latent_workload != args.workload:
+        lc = C.ALL[args.latent_workload]
+        print(f"[bench] {lc.name}: uploading weights", file=sys.stderr, flush=True)
+        line["latent"] = latent_section(lc, run_workload(lc, args.steps, args.warmup,
+                                                         backward=not args.no_backward))
     if args.copy_calibration:
         src = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda")   # 1 GiB
         dst = torch.empty_like(src)
@@ -500,6 +688,13 @@ def main():
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(cfg, min(args.cpu_sample_tokens, cfg.T))
+        if "switch_top1" in line:
+            ref = cpu_baseline_balance_stats(C.ALL[args.switch_workload])
+            gpu = line["switch_top1"]
+            ref["aux_rel_diff_gpu"] = abs(gpu["aux"] - ref["aux"]) / ref["aux"]
+            ref["f_equal_gpu"] = bool(all(abs(a - b) * gpu["T"] < 0.5
+                                          for a, b in zip(gpu["f"], ref["f"])))
+            line["cpu_baseline"]["switch_top1_balance_stats"] = ref
     print(json.dumps(line), flush=True)
 
 

@@ -187,18 +187,46 @@ def test_deterministic_bitwise():
             assert torch.equal(o1[key], o2[key]), key
 
 
-@pytest.mark.parametrize("name", ["mcu_t1", "mixtral_small_t37_decode", "tiny"])
+# One case per expert-kernel family: fp32 SIMT (tiny), decode-sized T (mcu_t1,
+# T = 37), the tiled grouped GEMM with 256- and 192-row m-tiles, and the
+# latent layer (router GEMM, routed experts at width l).
+PERTURB_CASES = ["tiny", "mcu_t1", "mixtral_small_t37_decode", "mixtral_small_t1000",
+                 "mixtral_small_t1200_bm192", "latent_small_t700"]
+
+
+@pytest.mark.parametrize("name", PERTURB_CASES)
 def test_unselected_expert_perturbation(name):
+    """Only selected experts take part ([LAT]'s check that only selected
+    experts receive gradient, in its forward form): an expert kept out of
+    every token's selection by a very negative selection bias can have its
+    weights scaled by 1000 without changing a single output bit.  The biased
+    forward itself is compared with the oracle's."""
     cfg = CASES[name]
-    log(f"[perturb] {name}")
-    ref_idx = O.route(O.expand(cfg.u()), O.expand(cfg.w_route()), cfg.k, cfg.gate)["idx"]
-    unused = sorted(set(range(cfg.N)) - set(ref_idx.reshape(-1).tolist()))
-    if not unused:
-        pytest.skip("every expert is selected by some token")
+    banned = [cfg.N - 1, 0] if cfg.N > 4 else [cfg.N - 1]
+    bias = np.zeros(cfg.N, dtype=np.float32)
+    bias[banned] = -1e9
+    log(f"[perturb] {name}: experts {banned} kept out by the selection bias")
     w = H.upload_layer(cfg)
+    w["selection_bias"] = H.to_device(bias)
     u = H.to_device(cfg.u())
-    y0, _ = run_forward(cfg, w, u)
-    for e in unused:
+    y0, o0 = run_forward(cfg, w, u)
+    gidx = H.to_host(o0["topk_idx"])
+    assert not np.isin(gidx, banned).any()
+    ref = O.forward(cfg.u(), cfg.w_route(), lambda e: cfg.expert(e), k=cfg.k, gate=cfg.gate,
+                    act=cfg.act, capacity=oracle_capacity(cfg), beta_g=cfg.beta_g,
+                    beta_u=cfg.beta_u, alpha=cfg.aux_alpha, bias=bias.astype(np.float64)) \
+        if not cfg.latent else O.latent_forward(
+            cfg.u(), cfg.w_route(), lambda e: cfg.expert(e), cfg.w_ldown(), cfg.w_lup(),
+            lambda j: cfg.shared(j), cfg.n_shared, k=cfg.k, gate=cfg.gate, act=cfg.act,
+            capacity=oracle_capacity(cfg), beta_g=cfg.beta_g, beta_u=cfg.beta_u,
+            rms_eps=cfg.rms_eps, alpha=cfg.aux_alpha, bias=bias.astype(np.float64))
+    gi = gidx.reshape(cfg.T, cfg.k)
+    same = np.all(gi == ref["idx"], axis=1)
+    assert same.sum() >= cfg.T - max(1, cfg.T // 100)
+    err = PR.rel_err(H.expand_device_output(y0)[same], ref["y"][same])
+    log(f"  biased forward vs oracle: rel err {err:.3e} on {int(same.sum())} tokens")
+    assert err <= PR.TOL[cfg.act_dtype]
+    for e in banned:
         for key in ("W_gate", "W_up", "W_down"):
             w[key][e] *= 1000.0
     y1, _ = run_forward(cfg, w, u)
@@ -346,13 +374,38 @@ def sample_tokens(T, n, seed):
     return np.array(sorted(s))
 
 
+def tile_edge_tokens(cfg, experts=None, tiles=(256, 192)):
+    """Tokens whose rows sit at the edges of the expert GEMMs' m-tiles: in
+    each expert's kept range, its first two and last two rows (the last one
+    in the ragged final tile) and the rows either side of every multiple of
+    the m-tile height (both heights the library chooses between).  The
+    dispatch is the oracle's, over every token."""
+    r = O.route(O.expand(cfg.u()), O.expand(cfg.w_route()), cfg.k, cfg.gate)
+    disp = O.dispatch(r["idx"], cfg.N, oracle_capacity(cfg))
+    toks = set()
+    for e in (range(cfg.N) if experts is None else experts):
+        lo, L = int(disp["offsets"][e]), int(disp["kept_counts"][e])
+        if L == 0:
+            continue
+        js = {0, min(1, L - 1), L - 1, max(L - 2, 0)}
+        for bm in tiles:
+            for m in range(bm, L, bm):
+                js |= {m - 1, m}
+        toks |= {int(disp["perm"][lo + j]) // cfg.k for j in js}
+    return toks, disp
+
+
 @pytest.mark.parametrize("cfg", [C.MIXTRAL_PREFILL, C.MIXTRAL_DECODE, C.SWITCH_SKEWED,
                                  C.MCU_BATCH, C.MCU_DECODE, C.TINY],
                          ids=lambda c: c.name)
 @pytest.mark.timeout(600)
 def test_full_size_forward(cfg):
     log(f"[full] {cfg.name}")
-    tokens = None if cfg.T <= 64 else sample_tokens(cfg.T, 24, cfg.seed)
+    tokens = None
+    if cfg.T > 64:
+        edges = tile_edge_tokens(cfg)[0]
+        tokens = np.array(sorted(set(sample_tokens(cfg.T, 24, cfg.seed).tolist()) | edges))
+        log(f"  {len(tokens)} sampled tokens, {len(edges)} of them at m-tile edges")
     ref = oracle_forward(cfg, tokens=tokens)
     y, out = run_forward(cfg)
     routing = check_forward(cfg, ref, y, out, tokens=tokens)
@@ -367,7 +420,14 @@ def test_full_size_forward(cfg):
 def test_full_size_latent():
     cfg = C.LATENT
     log(f"[full] {cfg.name}: uploading {cfg.N} experts")
-    tokens = sample_tokens(cfg.T, 6, cfg.seed)
+    # Six random tokens, plus the m-tile edges of the expert holding the most
+    # rows (two 192-row tiles, the second ragged) and of the one holding the
+    # fewest (a single ragged tile).
+    r = O.route(O.expand(cfg.u()), O.expand(cfg.w_route()), cfg.k, cfg.gate)
+    L = np.bincount(r["idx"].reshape(-1), minlength=cfg.N)
+    edges, _ = tile_edge_tokens(cfg, experts=[int(L.argmax()), int(L.argmin())], tiles=(192,))
+    tokens = np.array(sorted(set(sample_tokens(cfg.T, 6, cfg.seed).tolist()) | edges))
+    log(f"  {len(tokens)} sampled tokens, {len(edges)} at m-tile edges (loads {L.max()}, {L.min()})")
     ref = oracle_forward(cfg, tokens=tokens)
     y, out = run_forward(cfg)
     check_forward(cfg, ref, y, out, tokens=tokens)

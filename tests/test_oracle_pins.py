@@ -994,3 +994,24 @@ def test_latent_backward_tokens_matches_whole_layer(cap, aux):
     assert np.allclose(t["du"], g["du"][tokens], rtol=1e-12, atol=1e-13)
     assert np.allclose(t["dz"], g["dz"][tokens], rtol=1e-12, atol=1e-13)
     assert np.allclose(t["dr"], g["dr"][tokens], rtol=1e-12, atol=1e-13)
+
+
+def test_relative_error_hand_worked():
+    """The parity checker max|y - y_ref| / max|y_ref|, worked by hand:
+    y_ref = [[1.5, -2], [2, 0]] has max |.| = 2; y = [[1, -2], [3, 0.5]]
+    differs by [[-0.5, 0], [1, 0.5]], largest 1, so the error is 1 / 2.  The
+    denominator is the reference's (swapping the arguments gives 1 / 3), the
+    largest element, not an average or a norm (a mean-based form gives 0.5 /
+    1.375), and a transposed operand is caught: y^T - y_ref =
+    [[-0.5, 5], [-4, 0.5]], error 5 / 2."""
+    y_ref = np.array([[1.5, -2.0], [2.0, 0.0]])
+    y = np.array([[1.0, -2.0], [3.0, 0.5]])
+    assert O.relative_error(y, y_ref) == 0.5
+    assert O.relative_error(y_ref, y) == 1.0 / 3.0
+    assert O.relative_error(y.T, y_ref) == 2.5
+    assert O.relative_error(y_ref, y_ref) == 0.0
+    # bf16 outputs compared as fp32 values: the error is taken in fp64.
+    assert O.relative_error(y.astype(np.float32), y_ref) == 0.5
+    # An all-zero reference (a token whose every slot was dropped) reports
+    # the absolute difference.
+    assert O.relative_error(np.array([0.0, 0.25]), np.zeros(2)) == 0.25
