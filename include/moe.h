@@ -36,8 +36,9 @@
  *                            (there is no fallback path)
  *       MOE_ERR_WORKSPACE    ws is null or smaller than moe_workspace_bytes()
  *       MOE_ERR_HIP          a launch failed (hipGetLastError after launch)
- *   - No exceptions cross the ABI; the library holds no mutable global state,
- *     so calls on different streams with different workspaces may overlap.
+ *   - No exceptions cross the ABI; apart from the per-GPU scratch array of
+ *     moe_forward_noalloc the library holds no mutable global state, so
+ *     calls on different streams with different workspaces may overlap.
  *     Results are bitwise deterministic (no floating-point atomics).
  */
 #ifndef MOE_H
@@ -370,6 +371,24 @@ moe_status_t moe_combine(const moe_desc_t *desc, const float *y_perm, const int3
 moe_status_t moe_forward(const moe_desc_t *desc, const moe_weights_t *w, const void *u,
                          void *y, const moe_outputs_t *out, void *ws, size_t ws_bytes,
                          moe_stream_t stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+   capture, tight serving loops, harnesses that forbid hipMalloc): moe_forward
+   with the library's own scratch in place of the caller's workspace.  The
+   scratch is one static device array of MOE_STATIC_SCRATCH_BYTES per GPU,
+   created with the library's code object on that GPU and held until the
+   process ends; the call allocates and frees nothing.  Layers whose
+   moe_workspace_bytes() exceeds MOE_STATIC_SCRATCH_BYTES (64 MiB: every
+   decode-sized layer of T <= 64 tokens at d = 4096, h = 14336; larger layers
+   such as a 16384-token prefill) return MOE_ERR_WORKSPACE without launching.
+   Every call on one GPU uses that GPU's single array: calls that may overlap
+   on one GPU (different streams, or several host threads) race and must be
+   serialised by the caller; calls on different GPUs do not share it.  The
+   GPU is the one that runs `stream` (the current device for the null
+   stream).  Other arguments, outputs and errors as moe_forward. */
+#define MOE_STATIC_SCRATCH_BYTES (64u << 20)
+moe_status_t moe_forward_noalloc(const moe_desc_t *desc, const moe_weights_t *w, const void *u,
+                                 void *y, const moe_outputs_t *out, moe_stream_t stream);
 
 /* moe_forward that also records events[0..n_events) on the stream: events[0]
    before the first kernel and events[i] after stage i, with the stages in

@@ -11,6 +11,7 @@ MOE_OK, MOE_ERR_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range
 MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_MXFP4 = 0, 1, 2, 3
 MOE_GATE_RENORM, MOE_GATE_PROB = 0, 1
 MOE_ACT_SWIGLU, MOE_ACT_SITU_GLU = 0, 1
+MOE_STATIC_SCRATCH_BYTES = 64 << 20   # moe_forward_noalloc's per-GPU scratch
 
 # Every symbol include/moe.h declares.
 EXPORTS = ("moe_desc_init", "moe_status_string", "moe_workspace_bytes",
@@ -19,7 +20,7 @@ EXPORTS = ("moe_desc_init", "moe_status_string", "moe_workspace_bytes",
            "moe_latent_backward",
            "moe_dispatch", "moe_expert_ffn", "moe_expert_ffn_scaled",
            "moe_combine",
-           "moe_forward", "moe_forward_traced", "moe_stage_name")
+           "moe_forward", "moe_forward_noalloc", "moe_forward_traced", "moe_stage_name")
 
 
 class MoeDesc(ctypes.Structure):
@@ -104,6 +105,9 @@ def load() -> ctypes.CDLL:
     lib.moe_forward.argtypes = [D, ctypes.POINTER(MoeWeights), P, P,
                                 ctypes.POINTER(MoeOutputs), P, SZ, P]
     lib.moe_forward.restype = I32
+    lib.moe_forward_noalloc.argtypes = [D, ctypes.POINTER(MoeWeights), P, P,
+                                        ctypes.POINTER(MoeOutputs), P]
+    lib.moe_forward_noalloc.restype = I32
     lib.moe_forward_traced.argtypes = [D, ctypes.POINTER(MoeWeights), P, P,
                                        ctypes.POINTER(MoeOutputs), P, SZ, P,
                                        ctypes.POINTER(ctypes.c_void_p), I32]

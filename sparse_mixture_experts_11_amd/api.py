@@ -219,6 +219,13 @@ def moe_forward(desc, weights: Mapping[str, torch.Tensor], u, y, out=None, ws=No
            "moe_forward")
 
 
+def moe_forward_noalloc(desc, weights: Mapping[str, torch.Tensor], u, y, out=None,
+                        stream=None) -> None:
+    w = _weights(weights)
+    _check(L.load().moe_forward_noalloc(ctypes.byref(desc), ctypes.byref(w), _ptr(u), _ptr(y),
+                                        _outputs(out), _stream(stream)), "moe_forward_noalloc")
+
+
 def moe_forward_traced(desc, weights, u, y, out, ws, events, stream=None) -> None:
     """events: list of torch.cuda.Event(enable_timing=True); recorded between stages."""
     w = _weights(weights)

@@ -4,6 +4,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/moe.h"
 #include "kernels.hpp"
 
@@ -806,6 +808,48 @@ LatBwdLayout lat_bwd_layout(const moe_desc_t &d) {
 
 }  // namespace
 
+// ---- the static scratch of moe_forward_noalloc ------------------------------
+// One array per GPU, created with the code object on each device.  In host
+// code its name only stands in for the symbol: the device address of a
+// device's copy comes from hipGetSymbolAddress with that device current,
+// looked up on the first call on the device and kept per device.  Nothing in
+// the forward reads a workspace byte it has not written earlier in the same
+// call (its histograms are LDS integer atomics, every partial row and
+// dispatch array is written whole), so the array needs no clearing.
+__device__ __align__(256) uint8_t scratch[MOE_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the scratch array on the device that runs `st`.
+moe_status_t static_scratch(hipStream_t st, void **ptr) {
+  int dev = -1;
+  if (st != nullptr) {
+    if (hipStreamGetDevice(st, &dev) != hipSuccess) return MOE_ERR_HIP;
+  } else if (hipGetDevice(&dev) != hipSuccess) {
+    return MOE_ERR_HIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return MOE_ERR_HIP;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return MOE_ERR_HIP;
+    void *p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev && hipSetDevice(cur) != hipSuccess) return MOE_ERR_HIP;
+    if (e != hipSuccess || p == nullptr) return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 void moe_desc_init(moe_desc_t *d) {
@@ -1144,6 +1188,18 @@ moe_status_t moe_forward(const moe_desc_t *desc, const moe_weights_t *w, const v
                          moe_stream_t stream) {
   return forward_impl(desc, w, u, y, out, ws, ws_bytes, reinterpret_cast<hipStream_t>(stream),
                       nullptr, 0);
+}
+
+moe_status_t moe_forward_noalloc(const moe_desc_t *desc, const moe_weights_t *w, const void *u,
+                                 void *y, const moe_outputs_t *out, moe_stream_t stream) {
+  const moe_status_t v = validate(desc);
+  if (v != MOE_OK) return v;
+  if (layout(*desc).total > (size_t)MOE_STATIC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+  void *ws = nullptr;
+  const moe_status_t s = static_scratch(reinterpret_cast<hipStream_t>(stream), &ws);
+  if (s != MOE_OK) return s;
+  return forward_impl(desc, w, u, y, out, ws, (size_t)MOE_STATIC_SCRATCH_BYTES,
+                      reinterpret_cast<hipStream_t>(stream), nullptr, 0);
 }
 
 moe_status_t moe_forward_traced(const moe_desc_t *desc, const moe_weights_t *w, const void *u,
