@@ -65,6 +65,73 @@ __device__ __forceinline__ T wave_max(T v) {
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
+// ---- lane exchanges without the LDS round trip of a shuffle ----------------
+// Value of lane (lane ^ 1) / (lane ^ 2): DPP quad permutations, no LDS.
+__device__ __forceinline__ float lane_xor1(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float lane_xor2(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+}
+__device__ __forceinline__ int lane_xor1(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);
+}
+__device__ __forceinline__ int lane_xor2(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);
+}
+// Value of lane (lane ^ M) for M < 32 (ds_swizzle bit mode within each half
+// of the wave: no LDS memory access).
+template <int M>
+__device__ __forceinline__ float lane_xor_swz(float v) {
+  static_assert(M > 0 && M < 32, "within a 32-lane half");
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x1F | (M << 10)));
+}
+template <int M>
+__device__ __forceinline__ int lane_xor_swz(int v) {
+  static_assert(M > 0 && M < 32, "within a 32-lane half");
+  return __builtin_amdgcn_ds_swizzle(v, 0x1F | (M << 10));
+}
+// Mirror exchanges inside a row of 16 lanes (lane 7-i of each 8, 15-i of
+// each 16): for reductions whose operation is commutative and associative.
+__device__ __forceinline__ float lane_half_mirror(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float lane_mirror(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
+}
+__device__ __forceinline__ int lane_half_mirror(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);
+}
+__device__ __forceinline__ int lane_mirror(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false);
+}
+
+// Arg-max over the wave of (v, i): the largest v, ties to the smaller i.
+// Every lane returns the same pair.  Rows of 16 lanes reduce through DPP
+// exchanges, then row_bcast:15 and row_bcast:31 fold rows 0-1 into row 1
+// and rows 0-3 into row 3, and lane 63 holds the result.
+__device__ __forceinline__ void argmax_step(float &v, int &i, float ov, int oi) {
+  const bool t = (ov > v) | ((ov == v) & (oi < i));
+  v = t ? ov : v;
+  i = t ? oi : i;
+}
+__device__ __forceinline__ int dpp_bcast15(int v) {
+  return __builtin_amdgcn_update_dpp(v, v, 0x142, 0xA, 0xF, false);
+}
+__device__ __forceinline__ int dpp_bcast31(int v) {
+  return __builtin_amdgcn_update_dpp(v, v, 0x143, 0xC, 0xF, false);
+}
+__device__ __forceinline__ void wave_argmax(float &v, int &i) {
+  argmax_step(v, i, lane_xor1(v), lane_xor1(i));
+  argmax_step(v, i, lane_xor2(v), lane_xor2(i));
+  argmax_step(v, i, lane_half_mirror(v), lane_half_mirror(i));
+  argmax_step(v, i, lane_mirror(v), lane_mirror(i));
+  argmax_step(v, i, __int_as_float(dpp_bcast15(__float_as_int(v))), dpp_bcast15(i));
+  argmax_step(v, i, __int_as_float(dpp_bcast31(__float_as_int(v))), dpp_bcast31(i));
+  v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+  i = __builtin_amdgcn_readlane(i, 63);
+}
+
 // Two fp32 values -> packed bf16 pair (hardware round to nearest even).
 __device__ __forceinline__ uint32_t pack_bf16x2_hw(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));

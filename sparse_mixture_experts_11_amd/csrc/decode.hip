@@ -68,8 +68,10 @@ __global__ __launch_bounds__(256) void decode_kernel(
   static_assert(kPitch >= 256, "the chunk swizzle XORs with 4 row bits: 16 chunks a row");
   // After the loop the same LDS holds the partial sums of waves 1 .. 3.
   constexpr int kRedBytes = NM * NRB * TG * 64 * 16;
-  constexpr int kLds = kWaves * kSlice > (kWaves - 1) * kRedBytes ? kWaves * kSlice
-                                                                  : (kWaves - 1) * kRedBytes;
+  // MXFP4: each wave's window scales, [NM][RB rows][16 bytes], after the slices.
+  constexpr int kScale = MX4 ? NM * RB * 16 : 0;
+  constexpr int kMain = kWaves * (kSlice + kScale);
+  constexpr int kLds = kMain > (kWaves - 1) * kRedBytes ? kMain : (kWaves - 1) * kRedBytes;
   __shared__ __attribute__((aligned(16))) char smem[kLds];
   const int e = blockIdx.y;
   const int M = kept_offsets[e + 1] - kept_offsets[e];
@@ -108,6 +110,7 @@ __global__ __launch_bounds__(256) void decode_kernel(
                              kbytes(kb) + 16 * lc
                        : nullptr;
   char *slice = smem + wave * kSlice;
+  char *sslot = smem + kWaves * kSlice + wave * kScale;  // MXFP4 window scales
   const uint16_t *xr[TG];
   bool xv[TG];
 #pragma unroll
@@ -171,7 +174,31 @@ __global__ __launch_bounds__(256) void decode_kernel(
   constexpr int kEarly = (MX4 && GLU) ? kLoads / 2 : kLoads;
   const int kfull = Kw - Kw % (32 * U);
   u32x4 v[NM][kLoads];
+  // MXFP4: the window's 16 scale bytes of each of the 32 rows go straight to
+  // the wave's scale slot (two dword loads per matrix, lane l: row 16 q +
+  // l / 4, dword l % 4), issued ahead of the window's own loads so that
+  // waiting for those covers them.
+  typedef __attribute__((address_space(3))) void *lds_ptr_t;
+  __amdgpu_buffer_rsrc_t rs[NM];
+  if constexpr (MX4) {
+    const uint32_t sbytes = (uint32_t)(wrows * KB);
+    rs[0] = make_rsrc(static_cast<const uint8_t *>(S1) + (int64_t)e * wrows * KB, sbytes);
+    if constexpr (GLU)
+      rs[NM - 1] = make_rsrc(static_cast<const uint8_t *>(S2) + (int64_t)e * wrows * KB, sbytes);
+  }
   auto load_window = [&](int kw, int i0, int i1) {
+    if constexpr (MX4) {
+      if (i0 == 0) {
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+          for (int q = 0; q < 2; ++q)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rs[m], (lds_ptr_t)(sslot + m * RB * 16 + q * 256), 4,
+                (uint32_t)((row0 + 16 * q + (lane >> 2)) * KB + (kb + kw) / 32 + 4 * (lane & 3)),
+                0, 0, 0);
+      }
+    }
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
       if (i < i0 || i >= i1) continue;
@@ -210,20 +237,27 @@ __global__ __launch_bounds__(256) void decode_kernel(
         *reinterpret_cast<u32x4 *>(slice + m * RB * kPitch + r * kPitch + ((c ^ (r & 15)) << 4)) =
             v[m][i];
       }
-    if (kPipe && k + 32 * U < kfull) load_window(k + 32 * U, 0, kEarly);
-    // MFMA operands: lane l takes row 16 rb + l%16, k values 32u + 8(l/16) .. +7.
+    // MXFP4: the window's 16 block scales of each of the lane's rows, from
+    // the scale slot (its loads were issued before the window's, which are
+    // all complete once the window is parked), read before the next
+    // window's loads may overwrite the slot.
+    uint32_t sw[NM][NRB][4];
     if constexpr (MX4) {
-      // The window's 16 block scales of each of the lane's rows (4-byte
-      // aligned: K % 512 == 0 whenever this loop runs).
-      uint32_t sw[NM][NRB][4];
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
       for (int m = 0; m < NM; ++m)
 #pragma unroll
-        for (int rb = 0; rb < NRB; ++rb)
+        for (int rb = 0; rb < NRB; ++rb) {
+          const u32x4 q4 =
+              *reinterpret_cast<const u32x4 *>(sslot + m * RB * 16 + (16 * rb + li) * 16);
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            sw[m][rb][j] = *reinterpret_cast<const uint32_t *>(
-                (m == 0 ? sb1 : sb2) + (int64_t)rb * 16 * KB + k / 32 + 4 * j);
+          for (int j = 0; j < 4; ++j) sw[m][rb][j] = q4[j];
+        }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
+    if (kPipe && k + 32 * U < kfull) load_window(k + 32 * U, 0, kEarly);
+    // MFMA operands: lane l takes row 16 rb + l%16, k values 32u + 8(l/16) .. +7.
+    if constexpr (MX4) {
       // Token fragments in groups of 4 k-steps, the next group loading
       // while this one computes.
       bf16x8 bq[2][TG][4];
@@ -404,11 +438,12 @@ __global__ __launch_bounds__(256) void decode_kernel(
 }
 
 template <bool GLU, int WF>
-hipError_t launch_decode(int tg, dim3 grid, hipStream_t st, const uint16_t *x, int64_t ldx,
-                         const int32_t *perm, const int32_t *offsets, const int32_t *kept_offsets,
-                         int kslots, const void *W1, const void *W2, const void *S1,
-                         const void *S2, int64_t wrows, int K, int act, float bg, float bu,
+hipError_t launch_decode(int tg, int64_t wrows, int N, hipStream_t st, const uint16_t *x,
+                         int64_t ldx, const int32_t *perm, const int32_t *offsets,
+                         const int32_t *kept_offsets, int kslots, const void *W1, const void *W2,
+                         const void *S1, const void *S2, int K, int act, float bg, float bu,
                          void *out, int64_t ldo) {
+  const dim3 grid((unsigned)(wrows / RB), N);
 #define MOE_DECODE_CASE(TGV)                                                                  \
   case TGV:                                                                                   \
     hipLaunchKernelGGL((decode_kernel<GLU, TGV, WF>), grid, dim3(256), 0, st, x, ldx, perm,   \
@@ -435,15 +470,14 @@ hipError_t launch_decode_gu(const uint16_t *x, int64_t T, int w, const int32_t *
                             hipStream_t st) {
   const int64_t maxrows = T < kDecodeMaxRows ? T : kDecodeMaxRows;
   const int tg = (int)((maxrows + 15) / 16);
-  const dim3 grid(h / RB, N);
   if (wfmt == WF_FP8)
-    return launch_decode<true, WF_FP8>(tg, grid, st, x, w, perm, offsets, kept_offsets, kslots,
-                                       Wg, Wu, sg, su, h, w, act, bg, bu, hid, h);
+    return launch_decode<true, WF_FP8>(tg, h, N, st, x, w, perm, offsets, kept_offsets, kslots,
+                                       Wg, Wu, sg, su, w, act, bg, bu, hid, h);
   if (wfmt == WF_MX4)
-    return launch_decode<true, WF_MX4>(tg, grid, st, x, w, perm, offsets, kept_offsets, kslots,
-                                       Wg, Wu, sg, su, h, w, act, bg, bu, hid, h);
-  return launch_decode<true, WF_BF16>(tg, grid, st, x, w, perm, offsets, kept_offsets, kslots,
-                                      Wg, Wu, nullptr, nullptr, h, w, act, bg, bu, hid, h);
+    return launch_decode<true, WF_MX4>(tg, h, N, st, x, w, perm, offsets, kept_offsets, kslots,
+                                       Wg, Wu, sg, su, w, act, bg, bu, hid, h);
+  return launch_decode<true, WF_BF16>(tg, h, N, st, x, w, perm, offsets, kept_offsets, kslots,
+                                      Wg, Wu, nullptr, nullptr, w, act, bg, bu, hid, h);
 }
 
 hipError_t launch_decode_down(const uint16_t *hid, int64_t T, const int32_t *kept_offsets,
@@ -451,16 +485,14 @@ hipError_t launch_decode_down(const uint16_t *hid, int64_t T, const int32_t *kep
                               float *y_perm, hipStream_t st) {
   const int64_t maxrows = T < kDecodeMaxRows ? T : kDecodeMaxRows;
   const int tg = (int)((maxrows + 15) / 16);
-  const dim3 grid(w / RB, N);
   if (wfmt == WF_FP8)
-    return launch_decode<false, WF_FP8>(tg, grid, st, hid, h, nullptr, nullptr, kept_offsets, 1,
-                                        Wd, nullptr, sd, nullptr, w, h, 0, 1.f, 1.f, y_perm, w);
+    return launch_decode<false, WF_FP8>(tg, w, N, st, hid, h, nullptr, nullptr, kept_offsets, 1,
+                                        Wd, nullptr, sd, nullptr, h, 0, 1.f, 1.f, y_perm, w);
   if (wfmt == WF_MX4)
-    return launch_decode<false, WF_MX4>(tg, grid, st, hid, h, nullptr, nullptr, kept_offsets, 1,
-                                        Wd, nullptr, sd, nullptr, w, h, 0, 1.f, 1.f, y_perm, w);
-  return launch_decode<false, WF_BF16>(tg, grid, st, hid, h, nullptr, nullptr, kept_offsets, 1,
-                                       Wd, nullptr, nullptr, nullptr, w, h, 0, 1.f, 1.f, y_perm,
-                                       w);
+    return launch_decode<false, WF_MX4>(tg, w, N, st, hid, h, nullptr, nullptr, kept_offsets, 1,
+                                        Wd, nullptr, sd, nullptr, h, 0, 1.f, 1.f, y_perm, w);
+  return launch_decode<false, WF_BF16>(tg, w, N, st, hid, h, nullptr, nullptr, kept_offsets, 1,
+                                       Wd, nullptr, nullptr, nullptr, h, 0, 1.f, 1.f, y_perm, w);
 }
 
 }  // namespace moe

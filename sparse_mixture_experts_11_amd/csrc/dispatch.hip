@@ -22,9 +22,61 @@ namespace {
 constexpr int kChunk = 1024;  // entries per chunk
 constexpr int kMaxN = 1024;
 
-__global__ __launch_bounds__(256) void dispatch_count_kernel(const int32_t *__restrict__ idx,
-                                                             int64_t E, int N,
-                                                             int32_t *__restrict__ blk_counts) {
+// Blocks past the last chunk (when stats != nullptr): block (band, slice)
+// sums rows [64 slice, 64 slice + 64) of the router's partial rows [rows][N]
+// for a band of EW experts -- 256 / EW rows at a time, EW lanes a row
+// (reads coalesced along the experts), then a fixed tree -- and leaves the
+// sums in the slice's first row.  The scan launch adds the slices in order.
+constexpr int kStatsSlice = 64;
+
+__device__ void stats_slice(float *__restrict__ part_p, int32_t *__restrict__ part_cnt, int rows,
+                            int N, int EW, int band, int slice) {
+  __shared__ float sp[256];
+  __shared__ int sc[256];
+  const int rr = threadIdx.x / EW, e = threadIdx.x % EW;
+  const int rpp = 256 / EW;
+  const int n = band * EW + e;
+  const int r0 = slice * kStatsSlice;
+  const int r1 = r0 + kStatsSlice < rows ? r0 + kStatsSlice : rows;
+  float p = 0.f;
+  int c = 0;
+  if (n < N)
+    for (int wv = r0 + rr; wv < r1; wv += rpp) {
+      p += part_p[(int64_t)wv * N + n];
+      c += part_cnt[(int64_t)wv * N + n];
+    }
+  sp[threadIdx.x] = p;
+  sc[threadIdx.x] = c;
+  __syncthreads();
+  for (int s = rpp / 2; s > 0; s >>= 1) {
+    if (rr < s) {
+      sp[threadIdx.x] += sp[threadIdx.x + s * EW];
+      sc[threadIdx.x] += sc[threadIdx.x + s * EW];
+    }
+    __syncthreads();
+  }
+  // Only this block reads these columns of this slice, and it has finished.
+  if (rr == 0 && n < N) {
+    part_p[(int64_t)r0 * N + n] = sp[e];
+    part_cnt[(int64_t)r0 * N + n] = sc[e];
+  }
+}
+
+int stats_band_width(int N) {
+  int ew = 8;  // a power of two, 8 .. 64
+  while (ew < 64 && ew < N) ew *= 2;
+  return ew;
+}
+
+__global__ __launch_bounds__(256) void dispatch_count_kernel(
+    const int32_t *__restrict__ idx, int64_t E, int N, int32_t *__restrict__ blk_counts, int nblk,
+    float *__restrict__ part_p, int32_t *__restrict__ part_cnt, int rows, int EW) {
+  if ((int)blockIdx.x >= nblk) {
+    const int sb = (int)blockIdx.x - nblk;
+    const int slices = (rows + kStatsSlice - 1) / kStatsSlice;
+    stats_slice(part_p, part_cnt, rows, N, EW, sb / slices, sb % slices);
+    return;
+  }
   __shared__ int32_t hist[kMaxN];
   for (int n = threadIdx.x; n < N; n += blockDim.x) hist[n] = 0;
   __syncthreads();
@@ -56,9 +108,41 @@ __device__ int block_incl_scan(int v, int *tmp) {
 
 __global__ __launch_bounds__(1024) void dispatch_scan_kernel(
     int32_t *__restrict__ blk_counts, int nblk, int N, int capacity, int32_t *__restrict__ counts,
-    int32_t *__restrict__ offsets, int32_t *__restrict__ kept_offsets) {
+    int32_t *__restrict__ offsets, int32_t *__restrict__ kept_offsets,
+    const float *__restrict__ part_p, const int32_t *__restrict__ part_cnt, int rows, int64_t T,
+    float alpha, float *__restrict__ stats) {
   __shared__ int tmp[1024];
+  __shared__ float red[1024];
   const int n = threadIdx.x;  // N <= 1024: one expert per thread
+  if (stats != nullptr) {
+    // f_n = (arg-max count) / T and P_n = (sum of p) / T from the count
+    // launch's slice sums, in slice order; N sum_n f_n P_n by a fixed tree.
+    float fp = 0.f;
+    if (n < N) {
+      float p = 0.f;
+      int64_t c = 0;
+      for (int r = 0; r < rows; r += kStatsSlice) {
+        p += part_p[(int64_t)r * N + n];
+        c += part_cnt[(int64_t)r * N + n];
+      }
+      const float f = (float)((double)c / (double)T);
+      const float P = p / (float)T;
+      stats[n] = f;
+      stats[N + n] = P;
+      fp = f * P;
+    }
+    red[n] = fp;
+    __syncthreads();
+    for (int s = 512; s > 0; s >>= 1) {
+      if (n < s) red[n] += red[n + s];
+      __syncthreads();
+    }
+    if (n == 0) {
+      const float v = (float)N * red[0];
+      stats[2 * N] = v;
+      stats[2 * N + 1] = alpha * v;
+    }
+  }
   int total = 0;
   if (n < N) {
     // 16 chunks' counts are loaded before any of their bases is stored, so
@@ -247,14 +331,20 @@ int dispatch_blocks(int64_t entries) { return (int)((entries + kChunk - 1) / kCh
 hipError_t launch_dispatch(const int32_t *idx, int64_t T, int k, int N, int capacity,
                            int32_t *counts, int32_t *offsets, int32_t *kept_offsets,
                            int32_t *perm, int32_t *row_of, uint8_t *drop,
-                           int32_t *blk_counts, hipStream_t st) {
+                           int32_t *blk_counts, float *part_p, int32_t *part_cnt,
+                           int rows, float alpha, float *stats, hipStream_t st) {
   const int64_t E = T * k;
   const int nblk = dispatch_blocks(E);
   int nbits = 0;
   while ((1 << nbits) < N) ++nbits;
-  hipLaunchKernelGGL(dispatch_count_kernel, dim3(nblk), dim3(256), 0, st, idx, E, N, blk_counts);
+  const int ew = stats_band_width(N);
+  const int sblocks =
+      stats != nullptr ? ((N + ew - 1) / ew) * ((rows + kStatsSlice - 1) / kStatsSlice) : 0;
+  hipLaunchKernelGGL(dispatch_count_kernel, dim3(nblk + sblocks), dim3(256), 0, st, idx, E, N,
+                     blk_counts, nblk, part_p, part_cnt, rows, ew);
   hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(1024), 0, st, blk_counts, nblk, N,
-                     capacity, counts, offsets, kept_offsets);
+                     capacity, counts, offsets, kept_offsets, part_p, part_cnt, rows, T, alpha,
+                     stats);
   hipLaunchKernelGGL(dispatch_rank_kernel, dim3(nblk), dim3(64), 0, st, idx, E, N, nbits,
                      capacity, blk_counts, offsets, kept_offsets, perm, row_of, drop);
   return hipGetLastError();

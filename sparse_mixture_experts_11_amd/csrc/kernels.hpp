@@ -8,8 +8,9 @@
 namespace moe {
 
 // ---- router (route.hip) ----------------------------------------------------
-// Waves the router kernels launch for T tokens (sizes the stats partials).
-int route_waves(int64_t T, int N);
+// Partial rows [rows][N] of the balance statistics that the router writes
+// for this layer (one per wave, per block or per token, by kernel).
+int route_waves(int64_t T, int N, int d, bool u_bf16, bool w_bf16);
 // Wave-per-token-group router for N <= 64: scores, softmax, top-k, weights.
 // bias: optional [N] selection bias (top-k of z + bias; weights from the
 // unbiased softmax).
@@ -27,10 +28,15 @@ hipError_t launch_stats_finalize(float *part_p, int32_t *part_cnt, int waves, in
 
 // ---- dispatch (dispatch.hip) ----------------------------------------------
 int dispatch_blocks(int64_t entries);
+// With stats != nullptr the count launch also sums the router's partial
+// rows [rows][N] in slices of 64 (extra blocks; each slice's sums overwrite
+// its first row) and the scan launch adds the slices and finishes f, P,
+// N sum f P and alpha N sum f P: the statistics cost no launch of their own.
 hipError_t launch_dispatch(const int32_t *idx, int64_t T, int k, int N, int capacity,
                            int32_t *counts, int32_t *offsets, int32_t *kept_offsets,
                            int32_t *perm, int32_t *row_of, uint8_t *drop,
-                           int32_t *blk_counts, hipStream_t st);
+                           int32_t *blk_counts, float *part_p, int32_t *part_cnt,
+                           int rows, float alpha, float *stats, hipStream_t st);
 // At most 1024 entries and 1024 experts: one launch does the balance
 // statistics (when stats != nullptr, from the router's partial rows) and
 // the whole dispatch (when perm != nullptr).

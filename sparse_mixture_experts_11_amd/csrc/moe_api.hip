@@ -69,6 +69,11 @@ int weight_format(const moe_desc_t &d) {
   return fp8_experts(d) ? WFMT_FP8 : (mxfp4_experts(d) ? WFMT_MXFP4 : WFMT_BF16);
 }
 
+// Partial rows of the balance statistics the router writes for this layer.
+int route_rows(const moe_desc_t &d) {
+  return route_waves(d.T, d.N, d.d, d.act_dtype == MOE_BF16, d.router_dtype == MOE_BF16);
+}
+
 Layout layout(const moe_desc_t &d) {
   Layout L;
   memset(&L, 0, sizeof(L));
@@ -81,7 +86,7 @@ Layout layout(const moe_desc_t &d) {
   const int64_t E = d.T * d.k;
   const int64_t R = kept_rows_bound(d);
   const size_t act = bf16_path(d) ? 2 : 4;
-  const int waves = route_waves(d.T, d.N);
+  const int waves = route_rows(d);
   L.idx = take(E * 4);
   L.w = take(E * 4);
   L.stats = take((2 * (size_t)d.N + 2) * 4);
@@ -308,7 +313,7 @@ hipError_t do_route(const moe_desc_t &d, const Layout &L, const void *u, const v
                           d.d, d.N, d.k, d.gate, bias, idx, w, pp, pc, st);
   }
   if (e != hipSuccess || stats == nullptr) return e;
-  return launch_stats_finalize(pp, pc, route_waves(d.T, d.N), d.T, d.N, d.aux_alpha, stats, st);
+  return launch_stats_finalize(pp, pc, route_rows(d), d.T, d.N, d.aux_alpha, stats, st);
 }
 
 // At most 1024 (token, slot) entries: one single-block launch does the
@@ -322,10 +327,12 @@ hipError_t do_dispatch(const moe_desc_t &d, const Layout &L, const int32_t *idx,
                        uint8_t *drop, float *stats, void *ws, hipStream_t st) {
   if (small_tail(d))
     return launch_small_tail(region<float>(ws, L.part_p), region<int32_t>(ws, L.part_cnt),
-                             route_waves(d.T, d.N), d.T, d.aux_alpha, stats, idx, d.k, d.N,
+                             route_rows(d), d.T, d.aux_alpha, stats, idx, d.k, d.N,
                              d.capacity, counts, offsets, kept_offsets, perm, row_of, drop, st);
   return launch_dispatch(idx, d.T, d.k, d.N, d.capacity, counts, offsets, kept_offsets, perm,
-                         row_of, drop, region<int32_t>(ws, L.blk_counts), st);
+                         row_of, drop, region<int32_t>(ws, L.blk_counts),
+                         region<float>(ws, L.part_p), region<int32_t>(ws, L.part_cnt),
+                         route_rows(d), d.aux_alpha, stats, st);
 }
 
 // Expert-projection kernel family for a layer: fp32 on the vector ALUs,
@@ -522,13 +529,12 @@ moe_status_t forward_impl(const moe_desc_t *desc, const moe_weights_t *wts, cons
 
   Tracer tr{events, n_events, 0, st};
   MOE_TRY(tr.mark());
-  // Small inputs finish the statistics inside the dispatch launch.
-  const bool fused_stats = small_tail(d);
-  MOE_TRY(do_route(d, L, u, wts->W_route, wts->selection_bias, idx, tw,
-                   fused_stats ? nullptr : stats, ws, st));
+  // The dispatch launches finish the balance statistics from the router's
+  // partial rows.
+  MOE_TRY(do_route(d, L, u, wts->W_route, wts->selection_bias, idx, tw, nullptr, ws, st));
   MOE_TRY(tr.mark());
-  MOE_TRY(do_dispatch(d, L, idx, counts, offsets, kept_offsets, perm, row_of, drop,
-                      fused_stats ? stats : nullptr, ws, st));
+  MOE_TRY(do_dispatch(d, L, idx, counts, offsets, kept_offsets, perm, row_of, drop, stats, ws,
+                      st));
   MOE_TRY(do_tile_prefix(d, L, kept_offsets, ws, st));
   MOE_TRY(tr.mark());
   const void *x = u;

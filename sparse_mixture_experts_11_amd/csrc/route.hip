@@ -11,9 +11,61 @@ namespace {
 
 constexpr int kRouteBlock = 256;       // 4 waves
 constexpr int kRouteMaxWaves = 8192;   // wave router, per launch (sizes the stats partials)
-constexpr int kLogitsMaxWaves = 8192;  // top-k over materialised logits (N up to 1024): a wave per token up to 8192 tokens
+constexpr int kTopkBlock = 512;       // top-k over materialised logits (N up to 1024): 8 waves
+constexpr int kTopkMaxBlocks = 512;   // 4096 waves: 4 per SIMD, a token or a few each
 constexpr int kRouteSmallT = 256;      // at or below: one block per token (N <= 64)
 constexpr int kSmallBlock = 512;       // 8 waves: d = 4096 in one load round
+
+// Lane exchange with lane ^ M.
+template <int M>
+__device__ __forceinline__ float xchg(float v) {
+  if constexpr (M == 1) return lane_xor1(v);
+  else if constexpr (M == 2) return lane_xor2(v);
+  else if constexpr (M < 32) return lane_xor_swz<M>(v);
+  else return __shfl_xor(v, 32, kWave);
+}
+
+// The low log2(V) bits of x in reverse order.
+template <int V>
+__device__ __forceinline__ int bit_reverse(int x) {
+  int r = 0;
+#pragma unroll
+  for (int b = 1; b < V; b <<= 1) {
+    r <<= 1;
+    r |= (x & b) ? 1 : 0;
+  }
+  return r;
+}
+
+// One step of a transposed reduction: pairs (r[i], r[i + H]) split between
+// this lane and lane ^ M -- the lane with bit M set keeps the upper member
+// and sends the lower one -- and each kept member adds the partner's.
+template <int H, int M>
+__device__ __forceinline__ void transpose_step(float *r, int lane) {
+  const bool hi = (lane & M) != 0;
+#pragma unroll
+  for (int i = 0; i < H; ++i) {
+    const float a = r[i], b = r[i + H];
+    const float send = hi ? a : b;
+    r[i] = (hi ? b : a) + xchg<M>(send);
+  }
+}
+
+// Sum over the 64 lanes of each of V per-lane values (V a power of two up
+// to 64) in log2(V) transposed steps plus 6 - log2(V) plain ones, instead of
+// V separate wave reductions.  Lane l returns the total of value
+// bit_reverse<V>(l mod V); r is overwritten.  The steps run on lane
+// distances 1, 2, ... so the largest ones (V/2 exchanges) are DPP moves.
+template <int V>
+__device__ __forceinline__ float transpose_reduce(float (&r)[V], int lane) {
+  if constexpr (V >= 2) transpose_step<V / 2, 1>(r, lane); else r[0] += xchg<1>(r[0]);
+  if constexpr (V >= 4) transpose_step<V / 4, 2>(r, lane); else r[0] += xchg<2>(r[0]);
+  if constexpr (V >= 8) transpose_step<V / 8, 4>(r, lane); else r[0] += xchg<4>(r[0]);
+  if constexpr (V >= 16) transpose_step<V / 16, 8>(r, lane); else r[0] += xchg<8>(r[0]);
+  if constexpr (V >= 32) transpose_step<V / 32, 16>(r, lane); else r[0] += xchg<16>(r[0]);
+  if constexpr (V >= 64) transpose_step<1, 32>(r, lane); else r[0] += xchg<32>(r[0]);
+  return r[0];
+}
 
 template <bool BF16>
 __device__ __forceinline__ void load8(const void *base, int64_t off, float (&x)[8]) {
@@ -77,6 +129,7 @@ __device__ __forceinline__ void select_and_write(const float (&z)[NMAX], int N, 
   uint64_t taken = 0;
   int my_idx = 0;
   float my_p = 0.f;
+  float psum = 0.f;  // every lane holds every z: the selection is uniform
   for (int sl = 0; sl < k; ++sl) {
     int best = -1;
     float bz = -INFINITY;
@@ -92,13 +145,13 @@ __device__ __forceinline__ void select_and_write(const float (&z)[NMAX], int N, 
     for (int n = 0; n < NMAX; ++n)
       if (n == best) bp = e[n] * inv;
     taken |= 1ull << best;
+    psum += bp;
     if (sl == 0 && bias == nullptr) first = best;
     if (lane == sl) {
       my_idx = best;
       my_p = bp;
     }
   }
-  const float psum = wave_sum(lane < k ? my_p : 0.f);
   if (lane < k) {
     idx[t * k + lane] = my_idx;
     w[t * k + lane] = (gate == 0) ? my_p / psum : my_p;
@@ -187,11 +240,9 @@ __global__ __launch_bounds__(kSmallBlock) void route_small_kernel(
       }
     }
   }
-#pragma unroll
-  for (int n = 0; n < NMAX; ++n) {
-    const float v = (n < N) ? wave_sum(acc[n]) : 0.f;
-    if (lane == 0) red[wave][n] = v;
-  }
+  // Lane l ends with the wave's total of expert bitrev(l mod NMAX).
+  const float tot = transpose_reduce<NMAX>(acc, lane);
+  if (lane < NMAX) red[wave][bit_reverse<NMAX>(lane)] = tot;
   __syncthreads();
   if (wave != 0) return;
   float z[NMAX];
@@ -209,33 +260,85 @@ __global__ __launch_bounds__(kSmallBlock) void route_small_kernel(
   }
 }
 
-// One wave per token over materialised logits, N <= 64 * NPL.
+// Wave reductions over DPP moves inside rows of 16 lanes, then the rows
+// folded into row 3 by row_bcast:15 and row_bcast:31 and read from lane 63
+// (a fixed order: deterministic).
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = fmaxf(v, lane_xor1(v));
+  v = fmaxf(v, lane_xor2(v));
+  v = fmaxf(v, lane_half_mirror(v));
+  v = fmaxf(v, lane_mirror(v));
+  v = fmaxf(v, __int_as_float(dpp_bcast15(__float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp_bcast31(__float_as_int(v))));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += lane_xor1(v);
+  v += lane_xor2(v);
+  v += lane_half_mirror(v);
+  v += lane_mirror(v);
+  // rows 1 and 3 add rows 0 and 2; then rows 2 and 3 add rows 0 + 1
+  const float a = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false));
+  v += ((threadIdx.x & 16) != 0) ? a : 0.f;
+  const float b = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xC, 0xF, false));
+  v += ((threadIdx.x & 32) != 0) ? b : 0.f;
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// Top-k over materialised logits (N <= 64 * NPL, the router GEMM's output):
+// a wave per token at a time, consecutive tokens per wave; lane l holds
+// experts l, l + 64, ...  Each of the k selection rounds is a lane-local
+// best among the untaken experts and one DPP arg-max over the wave (larger
+// score, ties to the lower expert index); the winner's probability is read
+// from its lane.  The statistics partials of a block's four waves are added
+// in LDS (wave order), so each block writes one partial row.
 template <int NPL>
-__global__ __launch_bounds__(kRouteBlock) void topk_logits_kernel(
+__global__ __launch_bounds__(kTopkBlock) void topk_logits_kernel(
     const float *__restrict__ logits, int64_t T, int N, int k, int gate,
     const float *__restrict__ bias, int32_t *__restrict__ idx, float *__restrict__ w,
     float *__restrict__ part_p, int32_t *__restrict__ part_cnt) {
+  constexpr int kW = kTopkBlock / 64;
+  __shared__ float sp[kW][64 * NPL];
+  __shared__ int sc[kW][64 * NPL];
   const int lane = threadIdx.x & 63;
-  const int wave = blockIdx.x * (kRouteBlock / 64) + (threadIdx.x >> 6);
-  const int nwaves = gridDim.x * (kRouteBlock / 64);
+  const int wib = threadIdx.x >> 6;
+  const int wave = blockIdx.x * kW + wib;
+  const int nwaves = gridDim.x * kW;
   float acc_p[NPL];
   int acc_c[NPL];
+  // Loads are unconditional at clamped indices (a load under a per-element
+  // condition becomes its own branch, and the loads then issue one by one);
+  // entries past N are replaced by -inf after the load.
+  int ncl[NPL];
+#pragma unroll
+  for (int j = 0; j < NPL; ++j) {
+    const int n = lane + 64 * j;
+    ncl[j] = n < N ? n : N - 1;
+  }
+  float bj[NPL];
 #pragma unroll
   for (int j = 0; j < NPL; ++j) {
     acc_p[j] = 0.f;
     acc_c[j] = 0;
+    bj[j] = (bias != nullptr) ? bias[ncl[j]] : 0.f;
+  }
+  float zn[NPL];  // the next token's logits, loaded a token ahead
+  {
+    const int64_t r = wave < T ? wave : T - 1;
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) zn[j] = logits[r * N + ncl[j]];
   }
   for (int64_t t = wave; t < T; t += nwaves) {
     float z[NPL];
 #pragma unroll
-    for (int j = 0; j < NPL; ++j) {
-      const int n = lane + 64 * j;
-      z[j] = (n < N) ? logits[t * N + n] : -INFINITY;
-    }
+    for (int j = 0; j < NPL; ++j) z[j] = (lane + 64 * j < N) ? zn[j] : -INFINITY;
+    const int64_t tn = t + nwaves < T ? t + nwaves : T - 1;
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) zn[j] = logits[tn * N + ncl[j]];
     float m = -INFINITY;
 #pragma unroll
     for (int j = 0; j < NPL; ++j) m = fmaxf(m, z[j]);
-    m = wave_max(m);
+    m = wave_max_dpp(m);
     float e[NPL];
     float s = 0.f;
 #pragma unroll
@@ -243,74 +346,55 @@ __global__ __launch_bounds__(kRouteBlock) void topk_logits_kernel(
       e[j] = (lane + 64 * j < N) ? expf(z[j] - m) : 0.f;
       s += e[j];
     }
-    s = wave_sum(s);
+    s = wave_sum_dpp(s);
     const float inv = 1.0f / s;
     float zs[NPL];  // selection scores
 #pragma unroll
-    for (int j = 0; j < NPL; ++j) {
-      const int n = lane + 64 * j;
-      zs[j] = (bias != nullptr && n < N) ? z[j] + bias[n] : z[j];
-    }
-    int first = 0;  // unbiased arg-max (ties: lower index), for f
+    for (int j = 0; j < NPL; ++j) zs[j] = (bias != nullptr) ? z[j] + bj[j] : z[j];
+    int first = -1;  // unbiased arg-max (ties: lower index), for f
     if (bias != nullptr) {
       float bz = -INFINITY;
       int bn = 0x7FFFFFFF;
 #pragma unroll
       for (int j = 0; j < NPL; ++j) {
         const int n = lane + 64 * j;
-        if (n < N && (bn == 0x7FFFFFFF || z[j] > bz)) {
-          bz = z[j];
-          bn = n;
-        }
+        const bool t = (n < N) & ((bn == 0x7FFFFFFF) | (z[j] > bz));
+        bz = t ? z[j] : bz;
+        bn = t ? n : bn;
       }
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        const float oz = __shfl_xor(bz, o, 64);
-        const int on = __shfl_xor(bn, o, 64);
-        if (oz > bz || (oz == bz && on < bn)) {
-          bz = oz;
-          bn = on;
-        }
-      }
+      wave_argmax(bz, bn);
       first = bn;
     }
     uint32_t taken = 0;
     int my_idx = 0;
     float my_p = 0.f;
+    float psum = 0.f;
     for (int sl = 0; sl < k; ++sl) {
-      // Local best among this lane's untaken experts (ties: lower index).
+      // Lane-local best among the untaken experts (ties: lower index).
       float bz = -INFINITY;
       int bn = 0x7FFFFFFF;
       float bp = 0.f;
 #pragma unroll
       for (int j = 0; j < NPL; ++j) {
         const int n = lane + 64 * j;
-        if (n < N && !((taken >> j) & 1u) && (bn == 0x7FFFFFFF || zs[j] > bz)) {
-          bz = zs[j];
-          bn = n;
-          bp = e[j] * inv;
-        }
+        const bool t = (n < N) & !((taken >> j) & 1u) & ((bn == 0x7FFFFFFF) | (zs[j] > bz));
+        bz = t ? zs[j] : bz;
+        bn = t ? n : bn;
+        bp = t ? e[j] : bp;
       }
-      // Wave arg-max: larger z wins, equal z -> lower expert index.
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        const float oz = __shfl_xor(bz, o, 64);
-        const int on = __shfl_xor(bn, o, 64);
-        const float op = __shfl_xor(bp, o, 64);
-        if (oz > bz || (oz == bz && on < bn)) {
-          bz = oz;
-          bn = on;
-          bp = op;
-        }
-      }
-      if ((bn & 63) == lane) taken |= 1u << (bn >> 6);
-      if (sl == 0 && bias == nullptr) first = bn;
+      bp *= inv;
+      wave_argmax(bz, bn);
+      const int win = __builtin_amdgcn_readfirstlane(bn);
+      // The winning lane's own best is the wave's: its probability.
+      const float p = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bp), win & 63));
+      if ((win & 63) == lane) taken |= 1u << (win >> 6);
+      if (sl == 0 && bias == nullptr) first = win;
       if (lane == sl) {
-        my_idx = bn;
-        my_p = bp;
+        my_idx = win;
+        my_p = p;
       }
+      psum += p;
     }
-    const float psum = wave_sum(lane < k ? my_p : 0.f);
     if (lane < k) {
       idx[t * k + lane] = my_idx;
       w[t * k + lane] = (gate == 0) ? my_p / psum : my_p;
@@ -321,15 +405,220 @@ __global__ __launch_bounds__(kRouteBlock) void topk_logits_kernel(
       acc_c[j] += (lane + 64 * j == first) ? 1 : 0;
     }
   }
-  if (part_p != nullptr) {
+  if (part_p == nullptr) return;
 #pragma unroll
-    for (int j = 0; j < NPL; ++j) {
-      const int n = lane + 64 * j;
-      if (n < N) {
-        part_p[(int64_t)wave * N + n] = acc_p[j];
-        part_cnt[(int64_t)wave * N + n] = acc_c[j];
+  for (int j = 0; j < NPL; ++j) {
+    sp[wib][lane + 64 * j] = acc_p[j];
+    sc[wib][lane + 64 * j] = acc_c[j];
+  }
+  __syncthreads();
+  for (int n = threadIdx.x; n < N; n += kTopkBlock) {
+    float p = sp[0][n];
+    int c = sc[0][n];
+#pragma unroll
+    for (int q = 1; q < kW; ++q) {
+      p += sp[q][n];
+      c += sc[q][n];
+    }
+    part_p[(int64_t)blockIdx.x * N + n] = p;
+    part_cnt[(int64_t)blockIdx.x * N + n] = c;
+  }
+}
+
+// Large T, N <= 8, bf16 u with d = 512 CH: the whole router matrix sits in
+// each block's LDS (rows past N zero; at most 64 KiB), read once per block,
+// and each wave routes 4 tokens at a time with all 4 x CH of its 16-byte
+// u loads in flight together (lane l reads columns 512 c + 8 l .. + 7).  The
+// lane's 4 x 8 partial scores meet in one transposed reduction, the two
+// wave halves' sums pass through LDS, and lane (t, n) of the first 32
+// (token t of the 4, expert n) finishes the selection for its own expert
+// from its token's 8 scores.  bf16 router weights take packed bf16 dot
+// products (v_dot2_f32_bf16, products exact in fp32); fp32 weights
+// widen u and use fp32 fmas.  One partial row of the statistics per block.
+constexpr int kTileTok = 4;
+constexpr int kTileMaxBlocks = 512;  // two blocks (8 waves) per CU
+
+template <bool WB, int CH>
+__global__ __launch_bounds__(kRouteBlock, 2) void route_tile_kernel(
+    const bf16_t *__restrict__ u, const void *__restrict__ W, int64_t T, int d, int N, int k,
+    int gate, const float *__restrict__ bias, int32_t *__restrict__ idx, float *__restrict__ w,
+    float *__restrict__ part_p, int32_t *__restrict__ part_cnt) {
+  constexpr int WES = WB ? 2 : 4;  // bytes per router weight
+  static_assert(8 * 512 * CH * WES <= 65536, "router matrix within 64 KiB");
+  __shared__ __attribute__((aligned(16))) char smem[8 * 512 * CH * WES + kRouteBlock * 4];
+  const int wrow = d * WES;        // bytes per router row in LDS (d = 512 CH)
+  float *zx = reinterpret_cast<float *>(smem + 8 * wrow) + (threadIdx.x >> 6) * 64;
+  const int lane = threadIdx.x & 63;
+  const int wave = blockIdx.x * (kRouteBlock / 64) + (threadIdx.x >> 6);
+  const int nwaves = gridDim.x * (kRouteBlock / 64);
+  const int64_t groups = (T + kTileTok - 1) / kTileTok;
+  // The router matrix goes straight to LDS (16-byte direct loads, all in
+  // flight together; rows past N read as zeros beyond the buffer's end),
+  // and the wave's first 4 x CH u loads follow them before any wait.
+  {
+    typedef __attribute__((address_space(3))) void *lds_ptr_t;
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(W, (uint32_t)(N * wrow));
+    constexpr int kFill = 8 * 512 * CH * WES / (kRouteBlock * 16);
+#pragma unroll
+    for (int i = 0; i < kFill; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rw, (lds_ptr_t)(smem + (i * kRouteBlock + (threadIdx.x & ~63)) * 16), 16,
+          (uint32_t)((i * kRouteBlock + threadIdx.x) * 16), 0, 0, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  u32x4 x[kTileTok][CH];
+  auto load_x = [&](int64_t g) {
+    const int64_t t0 = g * kTileTok;
+#pragma unroll
+    for (int t = 0; t < kTileTok; ++t) {
+      const int64_t tt = (t0 + t < T) ? t0 + t : T - 1;
+#pragma unroll
+      for (int c = 0; c < CH; ++c)
+        x[t][c] = *reinterpret_cast<const u32x4 *>(u + tt * d + c * 512 + lane * 8);
+    }
+  };
+  if (wave < groups) {
+    load_x(wave);
+    __builtin_amdgcn_sched_barrier(0);
+    // In-order load counting: once at most the 4 x CH u loads remain, the
+    // router matrix has landed.
+    if constexpr (CH == 8) asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
+    else if constexpr (CH == 4) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    else if constexpr (CH == 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+  barrier_keep_loads();  // every wave's share of the matrix is in LDS; u loads keep flying
+  const int tl = (lane >> 3) & 3, nl = lane & 7;  // lanes 0..31: (token, expert)
+  float bv[8];  // selection bias, 0 without one
+#pragma unroll
+  for (int j = 0; j < 8; ++j) bv[j] = (bias != nullptr && j < N) ? bias[j] : 0.f;
+  float acc_p = 0.f;
+  int acc_c = 0;
+  for (int64_t g = wave; g < groups; g += nwaves) {
+    const int64_t t0 = g * kTileTok;
+    if (g != wave) load_x(g);
+    __builtin_amdgcn_sched_barrier(0);  // all 4 x CH loads issued before any use
+    float acc[kTileTok * 8];
+#pragma unroll
+    for (int i = 0; i < kTileTok * 8; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+#pragma unroll
+      for (int n = 0; n < 8; ++n) {
+        if constexpr (WB) {
+          const u32x4 wv =
+              *reinterpret_cast<const u32x4 *>(smem + n * wrow + (c * 512 + lane * 8) * 2);
+#pragma unroll
+          for (int t = 0; t < kTileTok; ++t) {
+            float a = acc[t * 8 + n];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              // (elements taken as scalars first: a bit cast of a vector
+              // element inside this loop compiled to element 0 every time)
+              const uint32_t xq = x[t][c][q], wq = wv[q];
+              a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, xq),
+                                                  __builtin_bit_cast(bf16x2, wq), a, false);
+            }
+            acc[t * 8 + n] = a;
+          }
+        } else {
+          const char *wp = smem + n * wrow + (c * 512 + lane * 8) * 4;
+          const float4 w0 = *reinterpret_cast<const float4 *>(wp);
+          const float4 w1 = *reinterpret_cast<const float4 *>(wp + 16);
+          const float wf[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+          for (int t = 0; t < kTileTok; ++t) {
+            float a = acc[t * 8 + n];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              a = fmaf(__uint_as_float(x[t][c][q] << 16), wf[2 * q], a);
+              a = fmaf(__uint_as_float(x[t][c][q] & 0xFFFF0000u), wf[2 * q + 1], a);
+            }
+            acc[t * 8 + n] = a;
+          }
+        }
       }
     }
+    // Lane l (and l ^ 32) now holds half of the sum of value bit_reverse<32>(l mod 32) = t * 8 + n.
+    float r[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) r[i] = acc[i];
+    transpose_step<16, 1>(r, lane);
+    transpose_step<8, 2>(r, lane);
+    transpose_step<4, 4>(r, lane);
+    transpose_step<2, 8>(r, lane);
+    transpose_step<1, 16>(r, lane);
+    zx[(lane & 32) + bit_reverse<32>(lane & 31)] = r[0];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    float z[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) z[j] = zx[tl * 8 + j] + zx[32 + tl * 8 + j];
+    __builtin_amdgcn_wave_barrier();  // every lane has read zx before the next group writes it
+    const int64_t tt = t0 + tl;
+    if (lane < 32 && tt < T && nl < N) {
+      float m = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (j < N) m = fmaxf(m, z[j]);
+      float e[8];
+      float s = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        e[j] = (j < N) ? expf(z[j] - m) : 0.f;
+        s += e[j];
+      }
+      const float inv = 1.0f / s;
+      float zs[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) zs[j] = z[j] + bv[j];
+      // Rank of every expert in the selection order (score descending, ties
+      // to the lower index) and the selected probability mass.
+      int rank_mine = 0, first_mine = 0;
+      float psum = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (j >= N) continue;
+        int rj = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (i < N && i != j && (zs[i] > zs[j] || (zs[i] == zs[j] && i < j))) ++rj;
+        if (rj < k) psum += e[j] * inv;
+        if (j == nl) rank_mine = rj;
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (i < N && i != nl && (z[i] > z[nl] || (z[i] == z[nl] && i < nl))) ++first_mine;
+      const float p = e[nl] * inv;
+      if (rank_mine < k) {
+        idx[tt * k + rank_mine] = nl;
+        w[tt * k + rank_mine] = (gate == 0) ? p / psum : p;
+      }
+      acc_p += p;
+      acc_c += (first_mine == 0) ? 1 : 0;
+    }
+  }
+  if (part_p == nullptr) return;
+  // Lanes n, n + 8, n + 16, n + 24 hold expert n's partials; the block's
+  // four waves then meet in LDS (wave order): one partial row per block.
+  acc_p += xchg<8>(acc_p);
+  acc_c += lane_xor_swz<8>(acc_c);
+  acc_p += xchg<16>(acc_p);
+  acc_c += lane_xor_swz<16>(acc_c);
+  __shared__ float bp[kRouteBlock / 64][8];
+  __shared__ int bc[kRouteBlock / 64][8];
+  if (lane < 8) {
+    bp[threadIdx.x >> 6][lane] = acc_p;
+    bc[threadIdx.x >> 6][lane] = acc_c;
+  }
+  __syncthreads();
+  if (threadIdx.x < N) {
+    const int n = threadIdx.x;
+    part_p[(int64_t)blockIdx.x * N + n] = ((bp[0][n] + bp[1][n]) + bp[2][n]) + bp[3][n];
+    part_cnt[(int64_t)blockIdx.x * N + n] = bc[0][n] + bc[1][n] + bc[2][n] + bc[3][n];
   }
 }
 
@@ -414,7 +703,7 @@ __global__ __launch_bounds__(1024) void stats_total_kernel(const float *__restri
 template <bool UB, bool WB, int NMAX, int TPW>
 hipError_t launch_rw(const void *u, const void *W, int64_t T, int d, int N, int k, int gate,
                      const float *bias, int32_t *idx, float *w, float *pp, int32_t *pc, hipStream_t st) {
-  const int waves = route_waves(T, N);
+  const int waves = route_waves(T, N, d, UB, WB);
   hipLaunchKernelGGL((route_wave_kernel<UB, WB, NMAX, TPW>), dim3(waves / 4), dim3(kRouteBlock), 0,
                      st, u, W, T, d, N, k, gate, bias, idx, w, pp, pc);
   return hipGetLastError();
@@ -428,6 +717,48 @@ hipError_t launch_rs(const void *u, const void *W, int64_t T, int d, int N, int 
   return hipGetLastError();
 }
 
+// The tile router: large T, N <= 8, bf16 u, d = 512 CH with CH in {1, 2, 4,
+// 8} and the 8-row router matrix within 64 KiB of LDS.
+bool route_tile_ok(int64_t T, int N, int d, bool u_bf16, bool w_bf16) {
+  const int ch = d / 512;
+  return T > kRouteSmallT && N <= 8 && u_bf16 && d % 512 == 0 &&
+         (ch == 1 || ch == 2 || ch == 4 || ch == 8) && 8 * d * (w_bf16 ? 2 : 4) <= 65536;
+}
+
+int route_tile_blocks(int64_t T) {
+  const int64_t groups = (T + kTileTok - 1) / kTileTok;
+  const int64_t b = (groups + 3) / 4;
+  return (int)(b < kTileMaxBlocks ? b : kTileMaxBlocks);
+}
+
+template <bool WB>
+hipError_t launch_tile(const void *u, const void *W, int64_t T, int d, int N, int k, int gate,
+                       const float *bias, int32_t *idx, float *w, float *pp, int32_t *pc,
+                       hipStream_t st) {
+  const dim3 grid(route_tile_blocks(T)), block(kRouteBlock);
+  const bf16_t *ub = static_cast<const bf16_t *>(u);
+  switch (d / 512) {
+    case 1:
+      hipLaunchKernelGGL((route_tile_kernel<WB, 1>), grid, block, 0, st, ub, W, T, d, N, k, gate,
+                         bias, idx, w, pp, pc);
+      break;
+    case 2:
+      hipLaunchKernelGGL((route_tile_kernel<WB, 2>), grid, block, 0, st, ub, W, T, d, N, k, gate,
+                         bias, idx, w, pp, pc);
+      break;
+    case 4:
+      hipLaunchKernelGGL((route_tile_kernel<WB, 4>), grid, block, 0, st, ub, W, T, d, N, k, gate,
+                         bias, idx, w, pp, pc);
+      break;
+    default:
+      if constexpr (WB)
+        hipLaunchKernelGGL((route_tile_kernel<WB, 8>), grid, block, 0, st, ub, W, T, d, N, k,
+                           gate, bias, idx, w, pp, pc);
+      break;
+  }
+  return hipGetLastError();
+}
+
 template <bool UB, bool WB>
 hipError_t launch_rw_n(const void *u, const void *W, int64_t T, int d, int N, int k, int gate,
                        const float *bias, int32_t *idx, float *w, float *pp, int32_t *pc, hipStream_t st) {
@@ -437,24 +768,29 @@ hipError_t launch_rw_n(const void *u, const void *W, int64_t T, int d, int N, in
     if (N <= 32) return launch_rs<UB, WB, 32>(u, W, T, d, N, k, gate, bias, idx, w, pp, pc, st);
     return launch_rs<UB, WB, 64>(u, W, T, d, N, k, gate, bias, idx, w, pp, pc, st);
   }
+  if (route_tile_ok(T, N, d, UB, WB))
+    return launch_tile<WB>(u, W, T, d, N, k, gate, bias, idx, w, pp, pc, st);
   if (N <= 8) return launch_rw<UB, WB, 8, 4>(u, W, T, d, N, k, gate, bias, idx, w, pp, pc, st);
   if (N <= 16) return launch_rw<UB, WB, 16, 2>(u, W, T, d, N, k, gate, bias, idx, w, pp, pc, st);
   if (N <= 32) return launch_rw<UB, WB, 32, 1>(u, W, T, d, N, k, gate, bias, idx, w, pp, pc, st);
   return launch_rw<UB, WB, 64, 1>(u, W, T, d, N, k, gate, bias, idx, w, pp, pc, st);
 }
 
+// Top-k over logits: blocks of 8 waves, a token per wave at a time.
+int topk_blocks(int64_t T) {
+  const int64_t b = (T + kTopkBlock / 64 - 1) / (kTopkBlock / 64);
+  return (int)(b < kTopkMaxBlocks ? b : kTopkMaxBlocks);
+}
+
 }  // namespace
 
-int route_waves(int64_t T, int N) {
-  if (N <= 64 && T <= kRouteSmallT) return (int)T;  // one partial row per token
+int route_waves(int64_t T, int N, int d, bool u_bf16, bool w_bf16) {
+  if (N > 64) return topk_blocks(T);                  // one partial row per block
+  if (T <= kRouteSmallT) return (int)T;               // one partial row per token
+  if (route_tile_ok(T, N, d, u_bf16, w_bf16)) return route_tile_blocks(T);  // per block
   const int tpw = N <= 8 ? 4 : (N <= 16 ? 2 : 1);
-  int64_t groups = (T + tpw - 1) / tpw;
-  int64_t cap = kRouteMaxWaves;
-  if (N > 64) {
-    groups = T;
-    cap = kLogitsMaxWaves;
-  }
-  int64_t waves = groups < cap ? groups : cap;
+  const int64_t groups = (T + tpw - 1) / tpw;
+  int64_t waves = groups < kRouteMaxWaves ? groups : kRouteMaxWaves;
   waves = (waves + 3) / 4 * 4;  // whole blocks of 4 waves
   return (int)waves;
 }
@@ -471,8 +807,7 @@ hipError_t launch_route_wave(const void *u, bool u_bf16, const void *W, bool w_b
 hipError_t launch_topk_logits(const float *logits, int64_t T, int N, int k, int gate,
                               const float *bias, int32_t *idx, float *w, float *part_p,
                               int32_t *part_cnt, hipStream_t st) {
-  const int waves = route_waves(T, N);
-  const dim3 grid(waves / 4), block(kRouteBlock);
+  const dim3 grid(topk_blocks(T)), block(kTopkBlock);
   if (N <= 256)
     hipLaunchKernelGGL(topk_logits_kernel<4>, grid, block, 0, st, logits, T, N, k, gate, bias, idx, w,
                        part_p, part_cnt);

@@ -270,6 +270,64 @@ def test_stage_route(name):
     assert abs(s[2 * cfg.N + 1] - stats["aux"]) <= 1e-4 * max(stats["aux"], 1e-3)
 
 
+# Router shapes beyond the workloads: fewer than 8 experts, every d = 512 CH
+# of the LDS-resident router (CH = 1, 2, 4, 8), fp32 router weights, a
+# selection bias, a token count that is not a multiple of the 4-token groups.
+ROUTE_SHAPES = [
+    dict(T=1001, d=2048, N=6, k=3, router_dtype="bf16", bias=False),
+    dict(T=1001, d=2048, N=6, k=3, router_dtype="bf16", bias=True),
+    dict(T=523, d=512, N=5, k=1, router_dtype="f32", bias=True),
+    dict(T=2050, d=1024, N=8, k=2, router_dtype="f32", bias=False),
+    dict(T=4099, d=4096, N=7, k=2, router_dtype="bf16", bias=True),
+    dict(T=300, d=1536, N=8, k=2, router_dtype="bf16", bias=False),  # older wave router
+]
+
+
+@pytest.mark.parametrize("shape", ROUTE_SHAPES, ids=lambda s: "T{T}_d{d}_N{N}_k{k}_{router_dtype}"
+                         "{b}".format(b="_bias" if s["bias"] else "", **s))
+def test_stage_route_shapes(shape):
+    sh = dict(shape)
+    with_bias = sh.pop("bias")
+    cfg = C.MIXTRAL_PREFILL.with_(name="route_shape", h=256, seed=11, **sh)
+    log(f"[route shape] {sh} bias={with_bias}")
+    desc = H.desc_for(cfg)
+    bias = None
+    if with_bias:
+        bias = np.linspace(-0.3, 0.3, cfg.N).astype(np.float32)
+    ref = O.route(O.expand(cfg.u()), O.expand(cfg.w_route()), cfg.k, cfg.gate,
+                  None if bias is None else bias.astype(np.float64))
+    E = cfg.T * cfg.k
+    idx = torch.empty(E, dtype=torch.int32, device="cuda")
+    w = torch.empty(E, dtype=torch.float32, device="cuda")
+    st = torch.empty(2 * cfg.N + 2, dtype=torch.float32, device="cuda")
+    ws = moe.workspace(desc)
+    if bias is None:
+        moe.moe_route(desc, H.to_device(cfg.u()), H.to_device(cfg.w_route()), idx, w, st, ws)
+    else:
+        moe.moe_route_biased(desc, H.to_device(cfg.u()), H.to_device(cfg.w_route()),
+                             H.to_device(bias), idx, w, st, ws)
+    torch.cuda.synchronize()
+    routing = PR.compare_routing(cfg, H.to_host(idx), ref)
+    same = routing["same"]
+    gw = H.to_host(w).reshape(cfg.T, cfg.k)
+    assert np.abs(gw[same] - ref["a"][same]).max() <= PR.W_TOL[cfg.act_dtype]
+    stats = O.balance_stats(ref["p"], cfg.aux_alpha)
+    s = H.to_host(st)
+    if routing["flipped"] == 0:
+        assert np.array_equal(np.rint(s[:cfg.N] * cfg.T).astype(np.int64),
+                              np.rint(stats["f"] * cfg.T).astype(np.int64))
+    assert np.allclose(s[cfg.N:2 * cfg.N], stats["P"], rtol=1e-4, atol=1e-6)
+    assert abs(s[2 * cfg.N + 1] - stats["aux"]) <= 1e-4 * max(stats["aux"], 1e-3)
+    # The forward (statistics finished by the dispatch launches) agrees with
+    # the router's own statistics.
+    w_all = H.upload_layer(cfg)
+    if bias is not None:
+        w_all["selection_bias"] = H.to_device(bias)
+    y, out = run_forward(cfg, w_all)
+    assert torch.equal(out["topk_idx"], idx)
+    assert np.allclose(H.to_host(out["stats"]), s, rtol=1e-5, atol=1e-7)
+
+
 @pytest.mark.parametrize("name", STAGE_CASES + ["switch_small_t48_decode"])
 def test_stage_dispatch(name):
     cfg = CASES[name]
