@@ -15,8 +15,8 @@
 //   transpose_bf16_kernel: [B][R][C] -> [B][C][ld] at a column offset, 64x64
 //     tiles through LDS with 16-byte loads and stores (the latent layer's
 //     token-long operands and projection matrices);
-//   kseg_kernel: each expert's rows padded to a multiple of 128 (at least
-//     128), as a prefix of column offsets;
+//   kseg_kernel: each expert's rows padded to a multiple of 64 (at least
+//     128: two k-steps of the GEMM), as a prefix of column offsets;
 //   seg_transpose_kernel: row-major [rows][width] -> [width][Rpad], row r of
 //     expert g to column kseg[g] + r - kept_offsets[g] and zeros in the rest
 //     of the expert's padded segment (tiled over the destination columns,
@@ -104,7 +104,9 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t *__r
   }
 }
 
-// kseg[g] = sum over g' < g of 128 * max(1, ceil(m_g' / 128)), m = kept rows.
+// kseg[g] = sum over g' < g of max(128, 64 ceil(m_g' / 64)), m = kept rows (a
+// LatentMoE expert's ~146 rows pad to 192, not 256: a quarter fewer MFMAs in
+// its weight gradients).
 __global__ __launch_bounds__(1024) void kseg_kernel(const int32_t *__restrict__ kept_offsets,
                                                     int G, int32_t *__restrict__ kseg) {
   __shared__ int tmp[1024];
@@ -112,7 +114,7 @@ __global__ __launch_bounds__(1024) void kseg_kernel(const int32_t *__restrict__ 
   for (int base = 0; base < G; base += 1024) {
     const int g = base + threadIdx.x;
     const int m = (g < G) ? kept_offsets[g + 1] - kept_offsets[g] : 0;
-    tmp[threadIdx.x] = (g < G) ? 128 * (m > 0 ? (m + 127) / 128 : 1) : 0;
+    tmp[threadIdx.x] = (g < G) ? (m > 64 ? 64 * ((m + 63) / 64) : 128) : 0;
     __syncthreads();
     for (int o = 1; o < 1024; o <<= 1) {
       const int add = (int)threadIdx.x >= o ? tmp[threadIdx.x - o] : 0;
@@ -145,7 +147,7 @@ __global__ __launch_bounds__(256) void seg_transpose_kernel(
     int act, float bg, float bu, uint16_t *__restrict__ dst, int64_t ld) {
   __shared__ uint32_t tile[64 * 33];
   // This block's 64 destination columns lie in one expert's padded segment
-  // (segments are multiples of 128 wide).
+  // (segments are multiples of 64 wide).
   const int p0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
   if (p0 >= kseg[G]) return;
   int lo = 0, hi = G;  // largest g with kseg[g] <= p0

@@ -252,7 +252,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
   // rows 64i + 8w .. +7 and lane l lands at byte 16 l of it.
   typedef __attribute__((address_space(3))) void *lds_ptr_t;
   // K segments: this group's k range starts at kbase.
-  const int kbase = KSEG ? a.kseg[g] : 0;
+  const int kbase = KSEG ? (a.kseg != nullptr ? a.kseg[g] : g * a.kchunk) : 0;
   auto aload = [&](int k0, int buf) {
     const uint32_t so = (uint32_t)(kbase + k0) * 2;
     char *ta = smem + buf * kABytes;
@@ -406,7 +406,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
   // MFMAs: B(kt+2) during sub-steps 0-1 of step kt (buffer (kt+2) % 3 was
   // released by the barrier ending step kt-1), A(kt+2) during sub-step 3
   // after step kt's barrier.  Before a barrier only B(kt+2) may still fly.
-  const int KT = (KSEG ? a.kseg[g + 1] - a.kseg[g] : a.K) / BK;
+  const int KT = (KSEG ? (a.kseg != nullptr ? a.kseg[g + 1] - a.kseg[g] : a.kchunk) : a.K) / BK;
   // MXFP4: scale table of 4096-k chunk c into table buf, 16 dword loads per
   // wave (every wave and every chunk the same count, for the in-order load
   // counting); a short last chunk repeats its last dword.
@@ -731,8 +731,9 @@ __global__ __launch_bounds__(1024) void tile_prefix_kernel(const int32_t *__rest
 // kernel instance is referenced from a non-template function.
 hipError_t launch_kernel(const GemmArgs &a, int epi, int bm, int64_t grid, hipStream_t st) {
   const dim3 g(grid), b(kThreads);
-  if (a.kseg != nullptr) {
+  if (a.kseg != nullptr || a.kchunk > 0) {
     if (epi != EP_F32 || bm != 256) return hipErrorInvalidValue;
+    if (a.kseg == nullptr && (a.mode != GM_DENSE || a.kchunk % 128 != 0)) return hipErrorInvalidValue;
     grouped_gemm_kernel<EP_F32, 256, false, true><<<g, b, 0, st>>>(a);
     return hipGetLastError();
   }

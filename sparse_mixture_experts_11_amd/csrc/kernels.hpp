@@ -18,11 +18,11 @@ hipError_t launch_route_wave(const void *u, bool u_bf16, const void *W, bool w_b
                              int d, int N, int k, int gate, const float *bias, int32_t *idx,
                              float *w, float *part_p, int32_t *part_cnt, hipStream_t st);
 // Softmax + top-k from materialised fp32 logits [T, N] (N <= 1024).
-hipError_t launch_topk_logits(const float *logits, int64_t T, int N, int k, int gate,
-                              const float *bias, int32_t *idx, float *w, float *part_p,
+hipError_t launch_topk_logits(const float *logits, const float *logits2, int64_t T, int N, int k,
+                              int gate, const float *bias, int32_t *idx, float *w, float *part_p,
                               int32_t *part_cnt, hipStream_t st);
 // f, P, N sum fP, alpha N sum fP from the per-wave partials (which it
-// overwrites: each 256-row slice's sums are left in the slice's first row).
+// overwrites: each 32-row slice's sums are left in the slice's first row).
 hipError_t launch_stats_finalize(float *part_p, int32_t *part_cnt, int waves, int64_t T, int N,
                                  float alpha, float *stats, hipStream_t st);
 
@@ -90,7 +90,7 @@ struct GemmArgs {
   const uint16_t *gsrc, *usrc;  // EP_GLU_BWD: G and U
   int64_t ldg;                // EP_GLU_BWD, EP_GLU_SAVE: row stride of G and U (elements)
   // K segments (dense tiles, every group's own k range): group g reduces over
-  // k in [kseg[g], kseg[g+1]) (multiples of 128, at least 128), B rows have
+  // k in [kseg[g], kseg[g+1]) (multiples of 64, at least 128), B rows have
   // stride ldb.  Used with EP_F32 for the experts' weight gradients.
   const int32_t *kseg;
   int64_t ldb;
@@ -105,6 +105,11 @@ struct GemmArgs {
   // (row n of group g at byte (g * strideB + n * K) / 2) and bscale /
   // bscale2 point at E8M0 bytes [G][ncols][K/32].
   int mx4;
+  // Dense split-K (kchunk > 0, EP_F32, GM_DENSE, kseg null): group g
+  // reduces k in [g kchunk, (g + 1) kchunk) (a multiple of 128) of the same
+  // A rows and B rows (row stride ldb) into its own output block of
+  // out_group_stride rows; the caller adds the G partial products.
+  int kchunk;
 };
 // m-tile height for groups of about rows_per_group rows (192 or 256).
 int gemm_pick_bm(double rows_per_group);

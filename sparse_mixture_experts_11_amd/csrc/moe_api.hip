@@ -61,6 +61,13 @@ bool mxfp4_ok(const moe_desc_t &d) {
   return width_ok(w) && width_ok(d.h);
 }
 bool router_gemm(const moe_desc_t &d) { return d.N > kRouteWaveMaxN; }
+// The router GEMM in two K-halves (two [T, N] partial products that the
+// top-k adds) when its 256 x 256 tiles would fill under three quarters of
+// the 256 CUs (LatentMoE at T = 8192: 128 tiles).
+bool router_split(const moe_desc_t &d) {
+  const int64_t tiles = ((int64_t)d.T + 255) / 256 * (((int64_t)d.N + 255) / 256);
+  return router_gemm(d) && tiles < 192 && d.d % 256 == 0 && d.d >= 512;
+}
 bool fp8_experts(const moe_desc_t &d) { return d.w_dtype == MOE_FP8_E4M3; }
 bool mxfp4_experts(const moe_desc_t &d) { return d.w_dtype == MOE_MXFP4; }
 // Routed-expert weights that come with scales.
@@ -92,7 +99,7 @@ Layout layout(const moe_desc_t &d) {
   L.stats = take((2 * (size_t)d.N + 2) * 4);
   L.part_p = take((size_t)waves * d.N * 4);
   L.part_cnt = take((size_t)waves * d.N * 4);
-  L.logits = router_gemm(d) ? take((size_t)d.T * d.N * 4) : 0;
+  L.logits = router_gemm(d) ? take((router_split(d) ? 2 : 1) * (size_t)d.T * d.N * 4) : 0;
   L.counts = take((size_t)d.N * 4);
   L.offsets = take(((size_t)d.N + 1) * 4);
   L.kept_offsets = take(((size_t)d.N + 1) * 4);
@@ -239,7 +246,8 @@ BwdLayout bwd_layout(const BwdDims &D, size_t base = 0) {
     return o;
   };
   const size_t R = (size_t)D.R, N = D.N, W = D.w, H = D.h;
-  // each expert's rows padded to 128 (at least 128); a multiple of 64
+  // each expert's rows padded to a multiple of 64, at least 128 (so under
+  // m + 128 per expert); the total a multiple of 64
   const size_t Rpad = (R + 128 * N + 63) / 64 * 64;
   L.Rpad = (int64_t)Rpad;
   L.tile_start = take((N + 1) * 4);
@@ -304,10 +312,18 @@ hipError_t do_route(const moe_desc_t &d, const Layout &L, const void *u, const v
     a.M_dense = d.T;
     a.out = region<float>(ws, L.logits);
     a.ldo = d.N;
+    const bool split = router_split(d);
+    if (split) {
+      a.G = 2;
+      a.kchunk = d.d / 2;
+      a.ldb = d.d;
+      a.out_group_stride = d.T;
+    }
     e = launch_gemm(a, EP_F32, 0, st);
     if (e != hipSuccess) return e;
-    e = launch_topk_logits(region<float>(ws, L.logits), d.T, d.N, d.k, d.gate, bias, idx, w, pp,
-                           pc, st);
+    const float *z = region<float>(ws, L.logits);
+    e = launch_topk_logits(z, split ? z + (size_t)d.T * d.N : nullptr, d.T, d.N, d.k, d.gate, bias,
+                           idx, w, pp, pc, st);
   } else {
     e = launch_route_wave(u, d.act_dtype == MOE_BF16, W_route, d.router_dtype == MOE_BF16, d.T,
                           d.d, d.N, d.k, d.gate, bias, idx, w, pp, pc, st);

@@ -285,19 +285,37 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
-// Top-k over materialised logits (N <= 64 * NPL, the router GEMM's output):
-// a wave per token at a time, consecutive tokens per wave; lane l holds
-// experts l, l + 64, ...  Each of the k selection rounds is a lane-local
-// best among the untaken experts and one DPP arg-max over the wave (larger
-// score, ties to the lower expert index); the winner's probability is read
-// from its lane.  The statistics partials of a block's four waves are added
-// in LDS (wave order), so each block writes one partial row.
-template <int NPL>
+// Wave minimum of an int (readlane 63 after the DPP steps).
+__device__ __forceinline__ int wave_min_dpp(int v) {
+  v = min(v, lane_xor1(v));
+  v = min(v, lane_xor2(v));
+  v = min(v, lane_half_mirror(v));
+  v = min(v, lane_mirror(v));
+  v = min(v, dpp_bcast15(v));
+  v = min(v, dpp_bcast31(v));
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
+// Top-k over materialised logits (N <= 64 * NPL, the router GEMM's output,
+// or the sum of its two K-halves when SPLIT): a wave per token at a time,
+// consecutive tokens per wave; lane l holds experts l, l + 64, ...  Each
+// lane keeps its three best untaken scores (ties: lower expert index
+// first).  A selection round takes the wave maximum of the lanes' heads (one
+// DPP max), finds the lanes holding it with a ballot (several only on an
+// exact tie, then the lowest expert index wins) and pops the winner's head;
+// a lane whose three entries are all taken while rounds remain triggers a
+// rebuild of every lane's list from its untaken scores (rare: one lane must
+// win three of the k rounds).  The probabilities of the chosen experts are
+// recomputed from their logits with the same operations as the softmax
+// (same values).  The statistics partials of a block's waves are added in
+// LDS (wave order), so each block writes one partial row.
+template <int NPL, bool SPLIT>
 __global__ __launch_bounds__(kTopkBlock) void topk_logits_kernel(
-    const float *__restrict__ logits, int64_t T, int N, int k, int gate,
-    const float *__restrict__ bias, int32_t *__restrict__ idx, float *__restrict__ w,
+    const float *__restrict__ logits, const float *__restrict__ logits2, int64_t T, int N, int k,
+    int gate, const float *__restrict__ bias, int32_t *__restrict__ idx, float *__restrict__ w,
     float *__restrict__ part_p, int32_t *__restrict__ part_cnt) {
   constexpr int kW = kTopkBlock / 64;
+  constexpr int kEmpty = 0x7FFFFFFF;
   __shared__ float sp[kW][64 * NPL];
   __shared__ int sc[kW][64 * NPL];
   const int lane = threadIdx.x & 63;
@@ -309,32 +327,37 @@ __global__ __launch_bounds__(kTopkBlock) void topk_logits_kernel(
   // Loads are unconditional at clamped indices (a load under a per-element
   // condition becomes its own branch, and the loads then issue one by one);
   // entries past N are replaced by -inf after the load.
-  int ncl[NPL];
-#pragma unroll
-  for (int j = 0; j < NPL; ++j) {
+  auto ncl = [&](int j) {
     const int n = lane + 64 * j;
-    ncl[j] = n < N ? n : N - 1;
-  }
+    return n < N ? n : N - 1;
+  };
   float bj[NPL];
 #pragma unroll
   for (int j = 0; j < NPL; ++j) {
     acc_p[j] = 0.f;
     acc_c[j] = 0;
-    bj[j] = (bias != nullptr) ? bias[ncl[j]] : 0.f;
+    bj[j] = (bias != nullptr) ? bias[ncl(j)] : 0.f;
   }
-  float zn[NPL];  // the next token's logits, loaded a token ahead
+  auto logit = [&](float a, float b) { return SPLIT ? a + b : a; };
+  float zn[NPL], zn2[NPL];  // the next token's logits, loaded a token ahead
   {
     const int64_t r = wave < T ? wave : T - 1;
 #pragma unroll
-    for (int j = 0; j < NPL; ++j) zn[j] = logits[r * N + ncl[j]];
+    for (int j = 0; j < NPL; ++j) {
+      zn[j] = logits[r * N + ncl(j)];
+      zn2[j] = SPLIT ? logits2[r * N + ncl(j)] : 0.f;
+    }
   }
   for (int64_t t = wave; t < T; t += nwaves) {
     float z[NPL];
 #pragma unroll
-    for (int j = 0; j < NPL; ++j) z[j] = (lane + 64 * j < N) ? zn[j] : -INFINITY;
+    for (int j = 0; j < NPL; ++j) z[j] = (lane + 64 * j < N) ? logit(zn[j], zn2[j]) : -INFINITY;
     const int64_t tn = t + nwaves < T ? t + nwaves : T - 1;
 #pragma unroll
-    for (int j = 0; j < NPL; ++j) zn[j] = logits[tn * N + ncl[j]];
+    for (int j = 0; j < NPL; ++j) {
+      zn[j] = logits[tn * N + ncl(j)];
+      if (SPLIT) zn2[j] = logits2[tn * N + ncl(j)];
+    }
     float m = -INFINITY;
 #pragma unroll
     for (int j = 0; j < NPL; ++j) m = fmaxf(m, z[j]);
@@ -348,61 +371,104 @@ __global__ __launch_bounds__(kTopkBlock) void topk_logits_kernel(
     }
     s = wave_sum_dpp(s);
     const float inv = 1.0f / s;
-    float zs[NPL];  // selection scores
+    // Unbiased arg-max (ties: lower index), for f: the lowest index whose
+    // logit equals the maximum.
+    int first;
+    {
+      int fl = kEmpty;
 #pragma unroll
-    for (int j = 0; j < NPL; ++j) zs[j] = (bias != nullptr) ? z[j] + bj[j] : z[j];
-    int first = -1;  // unbiased arg-max (ties: lower index), for f
-    if (bias != nullptr) {
-      float bz = -INFINITY;
-      int bn = 0x7FFFFFFF;
-#pragma unroll
-      for (int j = 0; j < NPL; ++j) {
-        const int n = lane + 64 * j;
-        const bool t = (n < N) & ((bn == 0x7FFFFFFF) | (z[j] > bz));
-        bz = t ? z[j] : bz;
-        bn = t ? n : bn;
-      }
-      wave_argmax(bz, bn);
-      first = bn;
+      for (int j = NPL - 1; j >= 0; --j) fl = (z[j] == m && lane + 64 * j < N) ? lane + 64 * j : fl;
+      first = wave_min_dpp(fl);
     }
-    uint32_t taken = 0;
-    int my_idx = 0;
-    float my_p = 0.f;
-    float psum = 0.f;
-    for (int sl = 0; sl < k; ++sl) {
-      // Lane-local best among the untaken experts (ties: lower index).
-      float bz = -INFINITY;
-      int bn = 0x7FFFFFFF;
-      float bp = 0.f;
-#pragma unroll
-      for (int j = 0; j < NPL; ++j) {
-        const int n = lane + 64 * j;
-        const bool t = (n < N) & !((taken >> j) & 1u) & ((bn == 0x7FFFFFFF) | (zs[j] > bz));
-        bz = t ? zs[j] : bz;
-        bn = t ? n : bn;
-        bp = t ? e[j] : bp;
-      }
-      bp *= inv;
-      wave_argmax(bz, bn);
-      const int win = __builtin_amdgcn_readfirstlane(bn);
-      // The winning lane's own best is the wave's: its probability.
-      const float p = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bp), win & 63));
-      if ((win & 63) == lane) taken |= 1u << (win >> 6);
-      if (sl == 0 && bias == nullptr) first = win;
-      if (lane == sl) {
-        my_idx = win;
-        my_p = p;
-      }
-      psum += p;
-    }
-    if (lane < k) {
-      idx[t * k + lane] = my_idx;
-      w[t * k + lane] = (gate == 0) ? my_p / psum : my_p;
-    }
+    // This token's share of the statistics partials (z and e are not needed
+    // past here).
 #pragma unroll
     for (int j = 0; j < NPL; ++j) {
       acc_p[j] += e[j] * inv;
       acc_c[j] += (lane + 64 * j == first) ? 1 : 0;
+    }
+    float zs[NPL];  // selection scores
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) zs[j] = (bias != nullptr) ? z[j] + bj[j] : z[j];
+    // The lane's three best untaken scores, c[0] first (valid entries form
+    // a prefix of j, and j runs in index order, so a strict > keeps ties in
+    // index order).
+    uint32_t taken = 0;
+    float c[3];
+    int nn[3];
+    // Insert score v of expert n; slot i takes it if it is empty (when
+    // CHECK_EMPTY) or v beats it; the lower slots shift down.
+    auto insert = [&](float v, int n, bool ok, bool check_empty) {
+      bool t[3];
+#pragma unroll
+      for (int i = 0; i < 3; ++i)
+        t[i] = ok & ((check_empty & (nn[i] == kEmpty)) | (v > c[i]));
+      c[2] = t[1] ? c[1] : (t[2] ? v : c[2]);
+      nn[2] = t[1] ? nn[1] : (t[2] ? n : nn[2]);
+      c[1] = t[0] ? c[0] : (t[1] ? v : c[1]);
+      nn[1] = t[0] ? nn[0] : (t[1] ? n : nn[1]);
+      c[0] = t[0] ? v : c[0];
+      nn[0] = t[0] ? n : nn[0];
+    };
+    auto clear = [&]() {
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        c[i] = -INFINITY;
+        nn[i] = kEmpty;
+      }
+    };
+    clear();
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+      const int n = lane + 64 * j;
+      // From j = 3 on every slot of a lane with a valid entry j is full,
+      // and entries past N (-inf) beat nothing.
+      insert(zs[j], n, n < N, j < 3);
+    }
+    // After a lane's three entries are taken while rounds remain, every
+    // lane rebuilds from its untaken scores.
+    auto rebuild = [&]() {
+      clear();
+#pragma unroll
+      for (int j = 0; j < NPL; ++j) {
+        const int n = lane + 64 * j;
+        insert(zs[j], n, (n < N) & !((taken >> j) & 1u), true);
+      }
+    };
+    int my_idx = 0;
+    for (int sl = 0; sl < k; ++sl) {
+      const float hm = wave_max_dpp(c[0]);
+      const uint64_t at = __builtin_amdgcn_ballot_w64(c[0] == hm);
+      int win;
+      if (__builtin_popcountll(at) == 1) {
+        win = __builtin_amdgcn_readlane(nn[0], __builtin_ctzll(at));
+      } else {
+        // An exact tie between lanes (or only -inf left): the lowest index.
+        win = wave_min_dpp(c[0] == hm ? nn[0] : kEmpty);
+      }
+      if (lane == sl) my_idx = win;
+      if (lane == (win & 63)) {
+        taken |= 1u << (win >> 6);
+        c[0] = c[1];
+        nn[0] = nn[1];
+        c[1] = c[2];
+        nn[1] = nn[2];
+        c[2] = -INFINITY;
+        nn[2] = kEmpty;
+      }
+      if (sl + 1 < k && __builtin_amdgcn_readlane(nn[0], win & 63) == kEmpty) rebuild();
+    }
+    // Chosen experts' probabilities: the softmax's own arithmetic on the
+    // same logits.
+    float my_p = 0.f;
+    if (lane < k) {
+      const float zz = logit(logits[t * N + my_idx], SPLIT ? logits2[t * N + my_idx] : 0.f);
+      my_p = expf(zz - m) * inv;
+    }
+    const float psum = wave_sum_dpp(my_p);
+    if (lane < k) {
+      idx[t * k + lane] = my_idx;
+      w[t * k + lane] = (gate == 0) ? my_p / psum : my_p;
     }
   }
   if (part_p == nullptr) return;
@@ -626,12 +692,13 @@ __global__ __launch_bounds__(kRouteBlock, 2) void route_tile_kernel(
 // activation saves compute", section 3.4: f_i the share of tokens whose top
 // expert is i, P_i the mean router probability of expert i), in two
 // fixed-order passes over the per-wave partial rows [waves][N]:
-//  1. block (c, s) sums rows [256 s, 256 s + 256) of a band of EW experts
+//  1. block (c, s) sums rows [32 s, 32 s + 32) of a band of EW experts
 //     (EW lanes a row, 256 / EW rows at a time: reads coalesced along the
-//     experts) and leaves the sums in the slice's first row;
+//     experts) and leaves the sums in the slice's first row (32-row slices:
+//     enough blocks to spread the reads, few slices for pass 2);
 //  2. one block adds the slices' first rows per expert, writes f and P and
 //     sums f_i P_i.
-constexpr int kStatsSliceRows = 256;
+constexpr int kStatsSliceRows = 32;
 
 __global__ __launch_bounds__(256) void stats_slice_kernel(float *__restrict__ part_p,
                                                           int32_t *__restrict__ part_cnt,
@@ -804,19 +871,25 @@ hipError_t launch_route_wave(const void *u, bool u_bf16, const void *W, bool w_b
   return launch_rw_n<false, false>(u, W, T, d, N, k, gate, bias, idx, w, part_p, part_cnt, st);
 }
 
-hipError_t launch_topk_logits(const float *logits, int64_t T, int N, int k, int gate,
-                              const float *bias, int32_t *idx, float *w, float *part_p,
+hipError_t launch_topk_logits(const float *logits, const float *logits2, int64_t T, int N, int k,
+                              int gate, const float *bias, int32_t *idx, float *w, float *part_p,
                               int32_t *part_cnt, hipStream_t st) {
   const dim3 grid(topk_blocks(T)), block(kTopkBlock);
-  if (N <= 256)
-    hipLaunchKernelGGL(topk_logits_kernel<4>, grid, block, 0, st, logits, T, N, k, gate, bias, idx, w,
-                       part_p, part_cnt);
-  else if (N <= 512)
-    hipLaunchKernelGGL(topk_logits_kernel<8>, grid, block, 0, st, logits, T, N, k, gate, bias, idx, w,
-                       part_p, part_cnt);
-  else
-    hipLaunchKernelGGL(topk_logits_kernel<16>, grid, block, 0, st, logits, T, N, k, gate, bias, idx, w,
-                       part_p, part_cnt);
+#define MOE_TOPK(NPLV)                                                                          \
+  if (logits2 != nullptr)                                                                       \
+    hipLaunchKernelGGL((topk_logits_kernel<NPLV, true>), grid, block, 0, st, logits, logits2, T, \
+                       N, k, gate, bias, idx, w, part_p, part_cnt);                             \
+  else                                                                                          \
+    hipLaunchKernelGGL((topk_logits_kernel<NPLV, false>), grid, block, 0, st, logits, nullptr,  \
+                       T, N, k, gate, bias, idx, w, part_p, part_cnt);
+  if (N <= 256) {
+    MOE_TOPK(4)
+  } else if (N <= 512) {
+    MOE_TOPK(8)
+  } else {
+    MOE_TOPK(16)
+  }
+#undef MOE_TOPK
   return hipGetLastError();
 }
 

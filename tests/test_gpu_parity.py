@@ -280,6 +280,13 @@ ROUTE_SHAPES = [
     dict(T=2050, d=1024, N=8, k=2, router_dtype="f32", bias=False),
     dict(T=4099, d=4096, N=7, k=2, router_dtype="bf16", bias=True),
     dict(T=300, d=1536, N=8, k=2, router_dtype="bf16", bias=False),  # older wave router
+    # N > 64: router GEMM, then the top-k over its logits (in two K-halves
+    # while the GEMM's tiles would fill under three quarters of the CUs)
+    dict(T=700, d=1024, N=97, k=4, router_dtype="bf16", bias=False, h=128),
+    dict(T=1500, d=512, N=300, k=8, router_dtype="bf16", bias=True, h=128),
+    dict(T=513, d=512, N=1024, k=16, router_dtype="bf16", bias=False, h=128),
+    dict(T=2000, d=256, N=896, k=16, router_dtype="bf16", bias=True, h=128),  # one K pass
+    dict(T=300, d=768, N=65, k=2, router_dtype="bf16", bias=False, h=128),
 ]
 
 
@@ -288,7 +295,8 @@ ROUTE_SHAPES = [
 def test_stage_route_shapes(shape):
     sh = dict(shape)
     with_bias = sh.pop("bias")
-    cfg = C.MIXTRAL_PREFILL.with_(name="route_shape", h=256, seed=11, **sh)
+    sh.setdefault("h", 256)
+    cfg = C.MIXTRAL_PREFILL.with_(name="route_shape", seed=11, **sh)
     log(f"[route shape] {sh} bias={with_bias}")
     desc = H.desc_for(cfg)
     bias = None
@@ -326,6 +334,42 @@ def test_stage_route_shapes(shape):
     y, out = run_forward(cfg, w_all)
     assert torch.equal(out["topk_idx"], idx)
     assert np.allclose(H.to_host(out["stats"]), s, rtol=1e-5, atol=1e-7)
+
+
+@pytest.mark.parametrize("d", [512, 256], ids=["two_k_halves", "one_k_pass"])
+def test_stage_route_logits_exact_ties(d):
+    """Duplicated router rows give bit-identical logits (every output column
+    sums the same products in the same order), so the top-k over logits must
+    break those ties by index: of a duplicated pair (a < b), b is chosen only
+    after a, in a later slot."""
+    cfg = C.MIXTRAL_PREFILL.with_(name="route_ties", T=600, d=d, h=128, N=130, k=8, seed=12,
+                                  router_dtype="bf16")
+    log(f"[route ties] d={d}")
+    desc = H.desc_for(cfg)
+    wr = np.array(cfg.w_route())
+    pairs = [(5, 70), (6, 7), (64, 128), (0, 129)]
+    for a, b in pairs:
+        wr[b] = wr[a]
+    E = cfg.T * cfg.k
+    idx = torch.empty(E, dtype=torch.int32, device="cuda")
+    w = torch.empty(E, dtype=torch.float32, device="cuda")
+    st = torch.empty(2 * cfg.N + 2, dtype=torch.float32, device="cuda")
+    ws = moe.workspace(desc)
+    moe.moe_route(desc, H.to_device(cfg.u()), H.to_device(wr), idx, w, st, ws)
+    torch.cuda.synchronize()
+    gi = H.to_host(idx).reshape(cfg.T, cfg.k)
+    ref = O.route(O.expand(cfg.u()), O.expand(wr), cfg.k, cfg.gate)
+    routing = PR.compare_routing(cfg, gi.reshape(-1), ref)
+    both = 0
+    for t in range(cfg.T):
+        row = list(gi[t])
+        assert len(set(row)) == cfg.k
+        for a, b in pairs:
+            if b in row:
+                assert a in row and row.index(a) < row.index(b), (t, row, a, b)
+                both += 1
+    assert both > 0, "no token selected a duplicated pair"
+    assert routing["flipped"] <= routing["near"]
 
 
 @pytest.mark.parametrize("name", STAGE_CASES + ["switch_small_t48_decode"])
