@@ -11,8 +11,8 @@ namespace {
 
 constexpr int kRouteBlock = 256;       // 4 waves
 constexpr int kRouteMaxWaves = 8192;   // wave router, per launch (sizes the stats partials)
-constexpr int kTopkBlock = 512;       // top-k over materialised logits (N up to 1024): 8 waves
-constexpr int kTopkMaxBlocks = 512;   // 4096 waves: 4 per SIMD, a token or a few each
+constexpr int kTopkBlock = 256;       // top-k over materialised logits (N up to 1024): 4 waves
+constexpr int kTopkMaxBlocks = 512;   // 2048 waves: all resident at once, a few tokens each
 constexpr int kRouteSmallT = 256;      // at or below: one block per token (N <= 64)
 constexpr int kSmallBlock = 512;       // 8 waves: d = 4096 in one load round
 
@@ -322,8 +322,11 @@ __global__ __launch_bounds__(kTopkBlock) void topk_logits_kernel(
   const int wib = threadIdx.x >> 6;
   const int wave = blockIdx.x * kW + wib;
   const int nwaves = gridDim.x * kW;
-  float acc_p[NPL];
-  int acc_c[NPL];
+  // The wave's statistics partials accumulate in its own LDS rows (lane l
+  // owns columns l, l + 64, ...): registers held across the token loop cost
+  // waves per SIMD.
+  float *my_sp = sp[wib];
+  int *my_sc = sc[wib];
   // Loads are unconditional at clamped indices (a load under a per-element
   // condition becomes its own branch, and the loads then issue one by one);
   // entries past N are replaced by -inf after the load.
@@ -334,29 +337,24 @@ __global__ __launch_bounds__(kTopkBlock) void topk_logits_kernel(
   float bj[NPL];
 #pragma unroll
   for (int j = 0; j < NPL; ++j) {
-    acc_p[j] = 0.f;
-    acc_c[j] = 0;
+    my_sp[lane + 64 * j] = 0.f;
+    my_sc[lane + 64 * j] = 0;
     bj[j] = (bias != nullptr) ? bias[ncl(j)] : 0.f;
   }
   auto logit = [&](float a, float b) { return SPLIT ? a + b : a; };
-  float zn[NPL], zn2[NPL];  // the next token's logits, loaded a token ahead
-  {
-    const int64_t r = wave < T ? wave : T - 1;
-#pragma unroll
-    for (int j = 0; j < NPL; ++j) {
-      zn[j] = logits[r * N + ncl(j)];
-      zn2[j] = SPLIT ? logits2[r * N + ncl(j)] : 0.f;
-    }
-  }
   for (int64_t t = wave; t < T; t += nwaves) {
+    // The token's logits (no prefetch of the next token: the registers it
+    // would hold cost waves per SIMD, which hide these loads better).
     float z[NPL];
+    {
+      float za[NPL], zb[NPL];
 #pragma unroll
-    for (int j = 0; j < NPL; ++j) z[j] = (lane + 64 * j < N) ? logit(zn[j], zn2[j]) : -INFINITY;
-    const int64_t tn = t + nwaves < T ? t + nwaves : T - 1;
+      for (int j = 0; j < NPL; ++j) {
+        za[j] = logits[t * N + ncl(j)];
+        zb[j] = SPLIT ? logits2[t * N + ncl(j)] : 0.f;
+      }
 #pragma unroll
-    for (int j = 0; j < NPL; ++j) {
-      zn[j] = logits[tn * N + ncl(j)];
-      if (SPLIT) zn2[j] = logits2[tn * N + ncl(j)];
+      for (int j = 0; j < NPL; ++j) z[j] = (lane + 64 * j < N) ? logit(za[j], zb[j]) : -INFINITY;
     }
     float m = -INFINITY;
 #pragma unroll
@@ -366,7 +364,7 @@ __global__ __launch_bounds__(kTopkBlock) void topk_logits_kernel(
     float s = 0.f;
 #pragma unroll
     for (int j = 0; j < NPL; ++j) {
-      e[j] = (lane + 64 * j < N) ? expf(z[j] - m) : 0.f;
+      e[j] = (lane + 64 * j < N) ? __expf(z[j] - m) : 0.f;
       s += e[j];
     }
     s = wave_sum_dpp(s);
@@ -383,10 +381,8 @@ __global__ __launch_bounds__(kTopkBlock) void topk_logits_kernel(
     // This token's share of the statistics partials (z and e are not needed
     // past here).
 #pragma unroll
-    for (int j = 0; j < NPL; ++j) {
-      acc_p[j] += e[j] * inv;
-      acc_c[j] += (lane + 64 * j == first) ? 1 : 0;
-    }
+    for (int j = 0; j < NPL; ++j) my_sp[lane + 64 * j] += e[j] * inv;
+    if (lane == (first & 63)) my_sc[first] += 1;
     float zs[NPL];  // selection scores
 #pragma unroll
     for (int j = 0; j < NPL; ++j) zs[j] = (bias != nullptr) ? z[j] + bj[j] : z[j];
@@ -463,7 +459,7 @@ __global__ __launch_bounds__(kTopkBlock) void topk_logits_kernel(
     float my_p = 0.f;
     if (lane < k) {
       const float zz = logit(logits[t * N + my_idx], SPLIT ? logits2[t * N + my_idx] : 0.f);
-      my_p = expf(zz - m) * inv;
+      my_p = __expf(zz - m) * inv;
     }
     const float psum = wave_sum_dpp(my_p);
     if (lane < k) {
@@ -472,11 +468,6 @@ __global__ __launch_bounds__(kTopkBlock) void topk_logits_kernel(
     }
   }
   if (part_p == nullptr) return;
-#pragma unroll
-  for (int j = 0; j < NPL; ++j) {
-    sp[wib][lane + 64 * j] = acc_p[j];
-    sc[wib][lane + 64 * j] = acc_c[j];
-  }
   __syncthreads();
   for (int n = threadIdx.x; n < N; n += kTopkBlock) {
     float p = sp[0][n];
