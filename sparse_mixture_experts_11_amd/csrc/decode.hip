@@ -75,7 +75,12 @@ __global__ __launch_bounds__(256) void decode_kernel(
   __shared__ __attribute__((aligned(16))) char smem[kLds];
   const int e = blockIdx.y;
   const int M = kept_offsets[e + 1] - kept_offsets[e];
-  if (M == 0) return;
+  // Token groups of 16: this workgroup takes groups g0 .. g0 + TG - 1 of the
+  // expert's (the grid's z splits an expert's groups between workgroups when
+  // a single one would need more token registers than two waves per SIMD
+  // allow; a workgroup with no group of its own exits at once).
+  const int g0 = blockIdx.z * TG;
+  if (M <= g0 * 16) return;
   const int row0 = blockIdx.x * RB;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -115,14 +120,14 @@ __global__ __launch_bounds__(256) void decode_kernel(
   bool xv[TG];
 #pragma unroll
   for (int tg = 0; tg < TG; ++tg) {
-    const int j = tg * 16 + li;
+    const int j = (g0 + tg) * 16 + li;
     xv[tg] = j < M;
     int64_t row;
     if (GLU) row = xv[tg] ? perm[offsets[e] + j] / kslots : 0;
     else row = kept_offsets[e] + (xv[tg] ? j : 0);
     xr[tg] = x + row * ldx + kb + kq;
   }
-  const int ngroups = (M + 15) / 16;
+  const int ngroups = (M + 15) / 16 - g0;  // this workgroup's groups (may exceed TG)
 
   f32x4 acc[NM][NRB][TG];
 #pragma unroll
@@ -411,7 +416,7 @@ __global__ __launch_bounds__(256) void decode_kernel(
     }
 #pragma unroll
   for (int tg = 0; tg < TG; ++tg) {
-    const int j = tg * 16 + li;
+    const int j = (g0 + tg) * 16 + li;
     if (tg >= ngroups || j >= M) continue;
     const int64_t orow = kept_offsets[e] + j;
 #pragma unroll
@@ -443,19 +448,28 @@ hipError_t launch_decode(int tg, int64_t wrows, int N, hipStream_t st, const uin
                          const int32_t *kept_offsets, int kslots, const void *W1, const void *W2,
                          const void *S1, const void *S2, int K, int act, float bg, float bu,
                          void *out, int64_t ldo) {
-  const dim3 grid((unsigned)(wrows / RB), N);
+  // tg token groups of 16 may be needed per expert (T up to 16 tg).  A
+  // workgroup holds at most two of them in registers (three or four cost a
+  // wave per SIMD: Mixtral T=64 gate/up 0.324 -> 0.312 ms bf16, 0.215 ->
+  // 0.140 ms MXFP4), one for the MXFP4 gate/up at T <= 32 (its widened
+  // operands leave room for two waves per SIMD only with one group: 0.123 ->
+  // 0.117 ms), and the grid's z covers the rest: with k of N experts chosen
+  // per token an expert rarely gets more than half the tokens, so the extra
+  // z workgroups exit at once, and an expert that does use them reads its
+  // weights once per z.
+  const int cap = (GLU && WF == WF_MX4 && tg <= 2) ? 1 : 2;
+  const int tgw = tg < cap ? tg : cap;
+  const dim3 grid((unsigned)(wrows / RB), N, (unsigned)((tg + tgw - 1) / tgw));
 #define MOE_DECODE_CASE(TGV)                                                                  \
   case TGV:                                                                                   \
     hipLaunchKernelGGL((decode_kernel<GLU, TGV, WF>), grid, dim3(256), 0, st, x, ldx, perm,   \
                        offsets, kept_offsets, kslots, W1, W2, S1, S2, wrows, K, act, bg, bu,  \
                        out, ldo);                                                             \
     break;
-  switch (tg) {
+  switch (tgw) {
     MOE_DECODE_CASE(1)
-    MOE_DECODE_CASE(2)
-    MOE_DECODE_CASE(3)
     default:
-    MOE_DECODE_CASE(4)
+    MOE_DECODE_CASE(2)
   }
 #undef MOE_DECODE_CASE
   return hipGetLastError();

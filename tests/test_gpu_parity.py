@@ -235,6 +235,46 @@ def test_unselected_expert_perturbation(name):
     assert torch.equal(a, b)
 
 
+HOT_DECODE_CASES = [
+    # (case, expert weights): at decode sizes a workgroup holds at most two
+    # 16-token groups of an expert (one for the MXFP4 gate/up at T <= 32),
+    # and the grid's z takes the rest; here every token goes to one or two
+    # experts, so those extra workgroups do the work.
+    ("mixtral_small_t64_decode", "bf16"),
+    ("mixtral_small_t64_decode", "fp8"),
+    ("mixtral_small_t64_decode", "mxfp4"),
+    ("mixtral_small_t37_decode", "mxfp4"),
+    ("mixtral_k2176_t30_decode", "fp8"),
+    ("mixtral_k2176_t60_decode", "bf16"),
+]
+
+
+@pytest.mark.parametrize("name,wfmt", HOT_DECODE_CASES, ids=lambda v: str(v))
+def test_decode_hot_experts(name, wfmt):
+    cfg = CASES[name]
+    if wfmt != "bf16":
+        cfg = cfg.with_(name=f"{cfg.name}_{wfmt}", w_dtype=wfmt)
+    hot = [2, 5]
+    bias = np.zeros(cfg.N, dtype=np.float32)
+    bias[hot[0]] = 1e4
+    if cfg.k > 1:
+        bias[hot[1]] = 5e3
+    log(f"[hot decode] {cfg.name} T={cfg.T}: every token to experts {hot[:cfg.k]}")
+    w = H.upload_layer(cfg)
+    w["selection_bias"] = H.to_device(bias)
+    y, out = run_forward(cfg, w)
+    counts = H.to_host(out["counts"])
+    assert counts[hot[0]] == cfg.T
+    ref = O.forward(cfg.u(), cfg.w_route(), lambda e: cfg.expert(e), k=cfg.k, gate=cfg.gate,
+                    act=cfg.act, capacity=oracle_capacity(cfg), beta_g=cfg.beta_g,
+                    beta_u=cfg.beta_u, alpha=cfg.aux_alpha, bias=bias.astype(np.float64))
+    gi = H.to_host(out["topk_idx"]).reshape(cfg.T, cfg.k)
+    assert np.array_equal(gi, ref["idx"])
+    err = PR.rel_err(H.expand_device_output(y), ref["y"])
+    log(f"  rel err {err:.3e}")
+    assert err <= PR.TOL[cfg.act_dtype]
+
+
 # ---------------------------------------------------------------------------
 # Stage tests: each entry point fed oracle-made inputs
 # ---------------------------------------------------------------------------
