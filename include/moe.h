@@ -171,7 +171,9 @@ int32_t moe_capacity_from_factor(int64_t T, int32_t N, int32_t k, double c);
    balance statistics (section 3.4).
      u        [T, d] act_dtype (plain and latent layers both route on u)
      W_route  [N, d] router_dtype
-     topk_idx [T, k] int32 out: experts of each token, by descending p
+     topk_idx [T, k] int32 out: experts of each token, by descending p (ties
+              to the lower index); k distinct experts below N for any input:
+              a score that is NaN ranks below every number
      topk_w   [T, k] fp32 out: combine weights a
      stats    [2N + 2] fp32 out, nullable: f_0..f_{N-1} (share of tokens whose
               argmax is i, before capacity), P_0..P_{N-1} (mean p),

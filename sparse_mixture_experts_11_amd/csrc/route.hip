@@ -111,9 +111,12 @@ __device__ __forceinline__ void select_and_write(const float (&z)[NMAX], int N, 
 #pragma unroll
   for (int n = 0; n < NMAX; ++n)
     if (n == lane) mine_p = e[n] * inv;
-  float zs[NMAX];  // selection scores
+  float zs[NMAX];  // selection scores (a NaN ranks as -inf)
 #pragma unroll
-  for (int n = 0; n < NMAX; ++n) zs[n] = (bias != nullptr && n < N) ? z[n] + bias[n] : z[n];
+  for (int n = 0; n < NMAX; ++n) {
+    const float v = (bias != nullptr && n < N) ? z[n] + bias[n] : z[n];
+    zs[n] = (v == v) ? v : -INFINITY;
+  }
   int first = 0;  // unbiased arg-max (ties: lower index), for f
   if (bias != nullptr) {
     float bz = -INFINITY;
@@ -354,7 +357,12 @@ __global__ __launch_bounds__(kTopkBlock) void topk_logits_kernel(
         zb[j] = SPLIT ? logits2[t * N + ncl(j)] : 0.f;
       }
 #pragma unroll
-      for (int j = 0; j < NPL; ++j) z[j] = (lane + 64 * j < N) ? logit(za[j], zb[j]) : -INFINITY;
+      for (int j = 0; j < NPL; ++j) {
+        // A NaN logit takes part as -inf: every selection below then has a
+        // total order, so it always yields k distinct experts below N.
+        const float v = logit(za[j], zb[j]);
+        z[j] = (lane + 64 * j < N && v == v) ? v : -INFINITY;
+      }
     }
     float m = -INFINITY;
 #pragma unroll
@@ -385,7 +393,10 @@ __global__ __launch_bounds__(kTopkBlock) void topk_logits_kernel(
     if (lane == (first & 63)) my_sc[first] += 1;
     float zs[NPL];  // selection scores
 #pragma unroll
-    for (int j = 0; j < NPL; ++j) zs[j] = (bias != nullptr) ? z[j] + bj[j] : z[j];
+    for (int j = 0; j < NPL; ++j) {
+      const float v = (bias != nullptr) ? z[j] + bj[j] : z[j];
+      zs[j] = (v == v) ? v : -INFINITY;
+    }
     // The lane's three best untaken scores, c[0] first (valid entries form
     // a prefix of j, and j runs in index order, so a strict > keeps ties in
     // index order).
@@ -631,7 +642,12 @@ __global__ __launch_bounds__(kRouteBlock, 2) void route_tile_kernel(
       const float inv = 1.0f / s;
       float zs[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) zs[j] = z[j] + bv[j];
+      for (int j = 0; j < 8; ++j) {
+        // NaN scores rank as -inf, so that the ranks below are distinct and
+        // every slot receives an expert.
+        const float v = z[j] + bv[j];
+        zs[j] = (v == v) ? v : -INFINITY;
+      }
       // Rank of every expert in the selection order (score descending, ties
       // to the lower index) and the selected probability mass.
       int rank_mine = 0, first_mine = 0;

@@ -412,6 +412,33 @@ def test_stage_route_logits_exact_ties(d):
     assert routing["flipped"] <= routing["near"]
 
 
+@pytest.mark.parametrize("shape", [
+    dict(T=4099, d=4096, N=7, k=2),     # tile router (N <= 8, large T)
+    dict(T=100, d=1024, N=8, k=2),      # small-T router
+    dict(T=700, d=1024, N=97, k=4),     # logit GEMM + top-k
+], ids=lambda s: "T{T}_N{N}".format(**s))
+def test_stage_route_nan_scores(shape):
+    """A router row of NaNs makes that expert's scores NaN for every token:
+    the selection must still give k distinct experts below N per token (the
+    NaN expert ranks last), so that nothing downstream indexes out of range."""
+    cfg = C.MIXTRAL_PREFILL.with_(name="route_nan", h=128, seed=13, router_dtype="bf16", **shape)
+    log(f"[route nan] {shape}")
+    desc = H.desc_for(cfg)
+    wr = np.array(cfg.w_route())
+    wr[3] = 0x7FC0  # bf16 quiet NaN
+    E = cfg.T * cfg.k
+    idx = torch.empty(E, dtype=torch.int32, device="cuda")
+    w = torch.empty(E, dtype=torch.float32, device="cuda")
+    st = torch.empty(2 * cfg.N + 2, dtype=torch.float32, device="cuda")
+    ws = moe.workspace(desc)
+    moe.moe_route(desc, H.to_device(cfg.u()), H.to_device(wr), idx, w, st, ws)
+    torch.cuda.synchronize()
+    gi = H.to_host(idx).reshape(cfg.T, cfg.k)
+    assert gi.min() >= 0 and gi.max() < cfg.N
+    assert all(len(set(r)) == cfg.k for r in gi)
+    assert not (gi == 3).any()
+
+
 @pytest.mark.parametrize("name", STAGE_CASES + ["switch_small_t48_decode"])
 def test_stage_dispatch(name):
     cfg = CASES[name]
