@@ -120,6 +120,16 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
   // A (activations, L2-resident) double-buffered; B (weights, streamed) in a
   // ring of three so its loads get two k-steps of cover: 160 / 144 KiB.
   __shared__ __attribute__((aligned(16))) char smem[2 * kABytes + 3 * kBBytes];
+  // 256-row tiles (many rows per expert: each weight chunk serves 8 m-tiles
+  // on the XCD, each activation chunk 4 n-tiles) take the rings the other way
+  // round for bf16 K-contiguous B: A in three buffers, so that the gathered
+  // rows get two k-steps of cover, B in two (Mixtral prefill gate/up 6.04 ->
+  // 5.99 ms, Switch 2.06 -> 2.03 ms).  192-row tiles keep B's three: there
+  // (LatentMoE, few rows per expert) the weights stream from HBM and need
+  // the cover (swapped: 8.09 -> 8.56 ms).
+  constexpr bool kASwap = BM == 256 && !FP8 && !MX4 && !BT && !KSEG;
+  constexpr int kBBase = (kASwap ? 3 : 2) * kABytes;  // B stages start here
+  static_assert(!kASwap || 3 * kABytes + 2 * kBBytes <= 2 * kABytes + 3 * kBBytes, "LDS");
 
   // ---- which tile: XCD-aware remap (block i runs on XCD i % 8: each XCD
   // takes one contiguous eighth of the real tiles), then (group, m-super, n,
@@ -253,17 +263,19 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
   typedef __attribute__((address_space(3))) void *lds_ptr_t;
   // K segments: this group's k range starts at kbase.
   const int kbase = KSEG ? (a.kseg != nullptr ? a.kseg[g] : g * a.kchunk) : 0;
-  auto aload = [&](int k0, int buf) {
+  auto aload_rows = [&](int k0, int buf, int i0, int i1) {
     const uint32_t so = (uint32_t)(kbase + k0) * 2;
     char *ta = smem + buf * kABytes;
 #pragma unroll
     for (int i = 0; i < MI; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(ta + (64 * i + 8 * wave) * 128), 16,
-                                               aoff[i], so, 0, 0);
+      if (i >= i0 && i < i1)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(ta + (64 * i + 8 * wave) * 128),
+                                                 16, aoff[i], so, 0, 0);
   };
+  auto aload = [&](int k0, int buf) { aload_rows(k0, buf, 0, MI); };
   auto bload = [&](int k0, int buf, int half) {
     const uint32_t so = (uint32_t)(kbase + k0) * ES;
-    char *tb = smem + 2 * kABytes + buf * kBStage;
+    char *tb = smem + kBBase + buf * kBStage;
     if constexpr (MX4) {
       if (half == 0)
         __builtin_amdgcn_raw_ptr_buffer_load_lds((glu && wave >= 4) ? ru : rb,
@@ -336,8 +348,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
   auto main_loop = [&](auto mconst) {
   constexpr int M = decltype(mconst)::value;
   auto read_frags = [&](int kt, int ks, bf16x8 (&xa)[4], bf16x8 (&xb)[2]) {
-    const char *ta = smem + (kt & 1) * kABytes;
-    const char *tb = smem + 2 * kABytes + (kt % 3) * kBStage;
+    const char *ta = smem + (kASwap ? kt % 3 : kt & 1) * kABytes;
+    const char *tb = smem + kBBase + (kASwap ? kt & 1 : kt % 3) * kBStage;
     const int c = ks * 2 + khalf;
 #pragma unroll
     for (int i = 0; i < M; ++i) xa[i] = lds_frag(ta, arow_l[i], c);
@@ -457,6 +469,25 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
   else asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
   barrier_keep_loads();
   read_frags(0, 0, fa, fb);
+  if constexpr (kASwap) {
+    // A(kt+2) during sub-steps 0-1 of step kt (buffer (kt+2) % 3 was
+    // released by the barrier ending step kt-1), B(kt+2) after step kt's
+    // barrier; before a barrier only A(kt+2) may still fly.
+    for (int kt = 0; kt + 2 < KT; ++kt) {
+      __builtin_amdgcn_sched_barrier(0);
+      MOE_SUBSTEP(read_frags(kt, 1, na, nb), aload_rows((kt + 2) * BK, (kt + 2) % 3, 0, (MI + 1) / 2),
+                  0x020, 1);
+      MOE_SUBSTEP(read_frags(kt, 2, na, nb), aload_rows((kt + 2) * BK, (kt + 2) % 3, (MI + 1) / 2, MI),
+                  0x020, 1);
+      MOE_SUBSTEP(read_frags(kt, 3, na, nb), (void)0, 0x000, 0);
+      if constexpr (MI == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
+      barrier_keep_loads();
+      __builtin_amdgcn_sched_barrier(0);
+      MOE_SUBSTEP(read_frags(kt + 1, 0, na, nb),
+                  (bload((kt + 2) * BK, kt & 1, 0), bload((kt + 2) * BK, kt & 1, 1)), 0x020, 1);
+    }
+  } else
   for (int kt = 0; kt + 2 < KT; ++kt) {
     __builtin_amdgcn_sched_barrier(0);
     MOE_SUBSTEP(read_frags(kt, 1, na, nb), bload((kt + 2) * BK, (kt + 2) % 3, 0), 0x020, 1);
