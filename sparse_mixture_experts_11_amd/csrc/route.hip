@@ -850,7 +850,7 @@ hipError_t launch_rw_n(const void *u, const void *W, int64_t T, int d, int N, in
   return launch_rw<UB, WB, 64, 1>(u, W, T, d, N, k, gate, bias, idx, w, pp, pc, st);
 }
 
-// Top-k over logits: blocks of 8 waves, a token per wave at a time.
+// Top-k over logits: blocks of kTopkBlock / 64 waves, a token per wave at a time.
 int topk_blocks(int64_t T) {
   const int64_t b = (T + kTopkBlock / 64 - 1) / (kTopkBlock / 64);
   return (int)(b < kTopkMaxBlocks ? b : kTopkMaxBlocks);
