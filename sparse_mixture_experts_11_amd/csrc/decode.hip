@@ -20,8 +20,9 @@
 // windows, 256 k; the operands are widened to bf16 exactly after the LDS
 // read, and the row scales multiply the fp32 sums after the split-K
 // reduction.  MXFP4 weights (E2M1 codes two a byte, one E8M0 scale per 32 k)
-// use 256-byte windows of 512 k; each k-step's operand is 4 bytes, widened
-// with its block scale folded in (v_cvt_scalef32_pk_bf16_fp4, exact).
+// use 128-byte windows of 256 k for the gate/up and 256-byte windows of 512 k
+// for the down; each k-step's operand is 4 bytes, widened with its block
+// scale folded in (v_cvt_scalef32_pk_bf16_fp4, exact).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -45,8 +46,14 @@ constexpr int kstep_bytes() { return WF == WF_BF16 ? 64 : (WF == WF_FP8 ? 32 : 1
 // 16): GLU streams 16 KiB, down 8 KiB, which keeps it at two workgroups per
 // CU (a 512-byte fp8 window's operand registers push it past 256 VGPRs;
 // measured 0.13 vs 0.10 ms at the Mixtral decode shape).
+// MXFP4 gate/up: 128-byte row windows (U = 8), an 8 KiB window a wave, so
+// that three blocks fit a CU (LDS and registers) instead of two (Mixtral
+// T=32 gate/up 0.117 -> 0.110 ms).  The MXFP4 down keeps 256-byte windows
+// (U = 16): with 128-byte ones it ran 0.076 -> 0.081 ms.
 template <bool GLU, int WF>
-constexpr int unroll_of() { return WF == WF_BF16 ? (GLU ? 4 : 8) : 256 / kstep_bytes<WF>(); }
+constexpr int unroll_of() {
+  return WF == WF_BF16 ? (GLU ? 4 : 8) : (WF == WF_MX4 && !GLU ? 16 : 8);
+}
 
 // S1, S2: fp32 row scales [N][wrows] (WF_FP8) or E8M0 block scales
 // [N][wrows][K/32] (WF_MX4).
@@ -65,11 +72,11 @@ __global__ __launch_bounds__(256) void decode_kernel(
   constexpr int kPitch = U * KSB;         // bytes of one row's window in a slice
   constexpr int kLoads = kPitch / 32;     // 1 KiB load instructions per matrix
   constexpr int kSlice = NM * RB * kPitch;  // per-wave LDS slice: one iteration's weights
-  static_assert(kPitch >= 256, "the chunk swizzle XORs with 4 row bits: 16 chunks a row");
+  static_assert(kPitch >= 128, "the chunk swizzle needs 8 chunks a row");
   // After the loop the same LDS holds the partial sums of waves 1 .. 3.
   constexpr int kRedBytes = NM * NRB * TG * 64 * 16;
-  // MXFP4: each wave's window scales, [NM][RB rows][16 bytes], after the slices.
-  constexpr int kScale = MX4 ? NM * RB * 16 : 0;
+  // MXFP4: each wave's window scales, [NM][RB rows][U bytes], after the slices.
+  constexpr int kScale = MX4 ? NM * RB * U : 0;
   constexpr int kMain = kWaves * (kSlice + kScale);
   constexpr int kLds = kMain > (kWaves - 1) * kRedBytes ? kMain : (kWaves - 1) * kRedBytes;
   __shared__ __attribute__((aligned(16))) char smem[kLds];
@@ -88,6 +95,10 @@ __global__ __launch_bounds__(256) void decode_kernel(
   const int kq = (lane >> 4) * 8;     // k offset of this lane's 8 values
   const int Kw = K / kWaves;
   const int kb = wave * Kw;
+  // Row r's 16-byte chunk c sits at chunk c ^ swz(r) of its slice row: the
+  // low 4 row bits with 16 or more chunks a row, row bits 1-3 with 8 (two
+  // 128-byte rows share the 256 bytes of banks).
+  auto swz = [](int r) { return kPitch >= 256 ? (r & 15) : ((r >> 1) & 7); };
 
   // Byte offset of element k of a weight row (k a multiple of 8).
   auto kbytes = [](int64_t k) -> int64_t { return k * KSB / 32; };
@@ -144,16 +155,16 @@ __global__ __launch_bounds__(256) void decode_kernel(
     const char *row = slice + m * RB * kPitch + r * kPitch;
     if constexpr (MX4) {
       const uint32_t raw =
-          *reinterpret_cast<const uint32_t *>(row + ((u ^ li) << 4) + 4 * (lane >> 4));
+          *reinterpret_cast<const uint32_t *>(row + ((u ^ swz(r)) << 4) + 4 * (lane >> 4));
       return e2m1x8_to_bf16x8(raw, sc);
     } else if constexpr (FP8) {
       const int q = lane >> 4;
       const int c = 2 * u + (q >> 1);
-      const uint2 raw = *reinterpret_cast<const uint2 *>(row + ((c ^ li) << 4) + 8 * (q & 1));
+      const uint2 raw = *reinterpret_cast<const uint2 *>(row + ((c ^ swz(r)) << 4) + 8 * (q & 1));
       return e4m3x8_to_bf16x8(raw.x, raw.y);
     } else {
       const int c = 4 * u + (lane >> 4);
-      return *reinterpret_cast<const bf16x8 *>(row + ((c ^ li) << 4));
+      return *reinterpret_cast<const bf16x8 *>(row + ((c ^ swz(r)) << 4));
     }
   };
   auto global_frag = [&](const char *w, int64_t byte_off, float sc) -> bf16x8 {
@@ -172,17 +183,20 @@ __global__ __launch_bounds__(256) void decode_kernel(
   // 0.285 ms).  Only as much of the window goes early as keeps two waves
   // per SIMD: half of it for the MXFP4 gate/up (the whole window beside its
   // scale and token registers exceeds 256 VGPRs: 0.134 -> 0.192 ms; half:
-  // 0.135 -> 0.131 ms), none for bf16 with three token groups.
-  constexpr bool kPipe = !(WF == WF_BF16 && TG == 3);
+  // 0.135 -> 0.131 ms; with 128-byte windows the whole window goes early).
+  // A window's token fragments are loaded at the top of its own iteration,
+  // before the next window's weight loads.
+  constexpr bool kPipe = true;
   // Load instructions per matrix issued a window early; the rest are issued
   // at the top of the window's own iteration.
-  constexpr int kEarly = (MX4 && GLU) ? kLoads / 2 : kLoads;
+  constexpr int kEarly = kLoads;
   const int kfull = Kw - Kw % (32 * U);
   u32x4 v[NM][kLoads];
-  // MXFP4: the window's 16 scale bytes of each of the 32 rows go straight to
-  // the wave's scale slot (two dword loads per matrix, lane l: row 16 q +
-  // l / 4, dword l % 4), issued ahead of the window's own loads so that
-  // waiting for those covers them.
+  // MXFP4: the window's U scale bytes of each of the 32 rows go straight to
+  // the wave's scale slot (U = 8: one dword load per matrix, lane l: row
+  // l / 2, dword l % 2; U = 16: two, lane l: row 16 q + l / 4, dword l % 4),
+  // issued ahead of the window's own loads so that waiting for those covers
+  // them.
   typedef __attribute__((address_space(3))) void *lds_ptr_t;
   __amdgpu_buffer_rsrc_t rs[NM];
   if constexpr (MX4) {
@@ -193,15 +207,23 @@ __global__ __launch_bounds__(256) void decode_kernel(
   }
   auto load_window = [&](int kw, int i0, int i1) {
     if constexpr (MX4) {
+      static_assert(U == 8 || U == 16, "scale slot layouts for 8 or 16 bytes a row");
       if (i0 == 0) {
 #pragma unroll
-        for (int m = 0; m < NM; ++m)
-#pragma unroll
-          for (int q = 0; q < 2; ++q)
+        for (int m = 0; m < NM; ++m) {
+          if constexpr (U == 8) {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rs[m], (lds_ptr_t)(sslot + m * RB * 16 + q * 256), 4,
-                (uint32_t)((row0 + 16 * q + (lane >> 2)) * KB + (kb + kw) / 32 + 4 * (lane & 3)),
-                0, 0, 0);
+                rs[m], (lds_ptr_t)(sslot + m * RB * U), 4,
+                (uint32_t)((row0 + (lane >> 1)) * KB + (kb + kw) / 32 + 4 * (lane & 1)), 0, 0, 0);
+          } else {
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+              __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                  rs[m], (lds_ptr_t)(sslot + m * RB * U + q * 256), 4,
+                  (uint32_t)((row0 + 16 * q + (lane >> 2)) * KB + (kb + kw) / 32 + 4 * (lane & 3)),
+                  0, 0, 0);
+          }
+        }
       }
     }
 #pragma unroll
@@ -217,13 +239,13 @@ __global__ __launch_bounds__(256) void decode_kernel(
   for (; k < kfull; k += 32 * U) {
     if (!kPipe) load_window(k, 0, kLoads);
     else if (kEarly < kLoads) load_window(k, kEarly, kLoads);
-    // Token fragments of the whole window up front (MXFP4: in groups of 4
-    // k-steps in its loop below; 16 k-steps of them would not fit beside
-    // the loads, and one k-step at a time leaves their latency exposed:
-    // 0.253 vs 0.235 ms for the Mixtral T=32 forward).
-    constexpr int UB = MX4 ? 1 : U;
+    // Token fragments of the whole window up front (the MXFP4 down's 16
+    // k-steps of them would not fit beside the loads: it takes them in
+    // groups of 4 k-steps in its loop below).
+    constexpr bool kGrouped = MX4 && U == 16;
+    constexpr int UB = kGrouped ? 1 : U;
     bf16x8 b[TG][UB];
-    if constexpr (!MX4) {
+    if constexpr (!kGrouped) {
 #pragma unroll
       for (int tg = 0; tg < TG; ++tg)
 #pragma unroll
@@ -232,37 +254,44 @@ __global__ __launch_bounds__(256) void decode_kernel(
                          ? *reinterpret_cast<const bf16x8 *>(xr[tg] + k + 32 * u)
                          : zero;
     }
-    // Into the wave's own slice: row r's 16-byte chunk c sits at chunk c ^ (r & 15).
+    // Into the wave's own slice, swizzled.
 #pragma unroll
     for (int m = 0; m < NM; ++m)
 #pragma unroll
       for (int i = 0; i < kLoads; ++i) {
         const int r = 8 * (i % 4) + lr;
         const int c = 8 * (i / 4) + lc;
-        *reinterpret_cast<u32x4 *>(slice + m * RB * kPitch + r * kPitch + ((c ^ (r & 15)) << 4)) =
+        *reinterpret_cast<u32x4 *>(slice + m * RB * kPitch + r * kPitch + ((c ^ swz(r)) << 4)) =
             v[m][i];
       }
-    // MXFP4: the window's 16 block scales of each of the lane's rows, from
+    // MXFP4: the window's U block scales of each of the lane's rows, from
     // the scale slot (its loads were issued before the window's, which are
     // all complete once the window is parked), read before the next
-    // window's loads may overwrite the slot.
-    uint32_t sw[NM][NRB][4];
+    // window's loads may overwrite the slot.  The wait also covers the token
+    // loads just issued, which the MFMAs below need first anyway.
+    uint32_t sw[NM][NRB][U / 4];
     if constexpr (MX4) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
       for (int m = 0; m < NM; ++m)
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb) {
-          const u32x4 q4 =
-              *reinterpret_cast<const u32x4 *>(sslot + m * RB * 16 + (16 * rb + li) * 16);
+          const char *src = sslot + m * RB * U + (16 * rb + li) * U;
+          if constexpr (U == 8) {
+            const uint2 q2 = *reinterpret_cast<const uint2 *>(src);
+            sw[m][rb][0] = q2.x;
+            sw[m][rb][1] = q2.y;
+          } else {
+            const u32x4 q4 = *reinterpret_cast<const u32x4 *>(src);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) sw[m][rb][j] = q4[j];
+            for (int j = 0; j < U / 4; ++j) sw[m][rb][j] = q4[j];
+          }
         }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
     if (kPipe && k + 32 * U < kfull) load_window(k + 32 * U, 0, kEarly);
     // MFMA operands: lane l takes row 16 rb + l%16, k values 32u + 8(l/16) .. +7.
-    if constexpr (MX4) {
+    if constexpr (kGrouped) {
       // Token fragments in groups of 4 k-steps, the next group loading
       // while this one computes.
       bf16x8 bq[2][TG][4];
@@ -299,6 +328,29 @@ __global__ __launch_bounds__(256) void decode_kernel(
                   acc[m][r][tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                       a[m][r], bq[grp & 1][tg][uu], acc[m][r][tg], 0, 0, 0);
             }
+          }
+        }
+      }
+    } else if constexpr (MX4) {
+      // Widened operands of one k-step at a time, each with its block scale.
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        bf16x8 a[NM][NRB];
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+          for (int rb = 0; rb < NRB; ++rb)
+            a[m][rb] = slice_frag(m, 16 * rb + li, u,
+                                  e8m0_to_f32((sw[m][rb][u >> 2] >> (8 * (u & 3))) & 0xFF));
+#pragma unroll
+        for (int tg = 0; tg < TG; ++tg) {
+          if (tg < ngroups) {
+#pragma unroll
+            for (int m = 0; m < NM; ++m)
+#pragma unroll
+              for (int r = 0; r < NRB; ++r)
+                acc[m][r][tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[m][r], b[tg][u],
+                                                                       acc[m][r][tg], 0, 0, 0);
           }
         }
       }
