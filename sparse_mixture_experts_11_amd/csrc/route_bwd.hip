@@ -9,7 +9,7 @@
 //   softmax:  dz_t = p_t * (dp_t - p_t . dp_t)
 //   dW_route = dz^T u,   du = dz W_route   (the router's share of du)
 //
-//   rb_dz_kernel:   a wave per token (16 per block): softmax of the logits,
+//   rb_dz_kernel:   a wave per token (8 per block): softmax of the logits,
 //                   the k dot products dy_t . y_perm[row] (over d, or over l
 //                   for the latent layer, whose dy is the gradient at the
 //                   aggregated r), the gate and
@@ -17,7 +17,8 @@
 //   rb_dw_kernel:   fp32 partial sums of dz^T u over chunks of tokens: a
 //                   thread per 8 columns of u (one 16-byte load a token) and
 //                   8 experts, the chunk's dz staged in LDS;
-//   rb_dw_reduce:   the chunks summed in chunk order (deterministic).
+//   rb_dw_reduce:   the chunks summed in a fixed order (deterministic): 16
+//                   interleaved runs of chunks, then the runs in order.
 //   rb_du_kernel:   a thread per 8 columns of W_route and 8 tokens.
 #include "common.hpp"
 #include "kernels.hpp"
@@ -26,7 +27,7 @@ namespace moe {
 
 namespace {
 
-constexpr int kRbTokens = 16;    // waves (tokens) per block in rb_dz_kernel
+constexpr int kRbTokens = 8;     // waves (tokens) per block in rb_dz_kernel
 constexpr int kDwExperts = 8;    // experts per rb_dw_kernel block
 constexpr int kDwChunk = 64;     // tokens per rb_dw_kernel chunk (at least)
 constexpr int kDwStage = 256;    // tokens of dz staged in LDS at a time
@@ -196,14 +197,40 @@ __global__ __launch_bounds__(256) void rb_dw_kernel(const float *__restrict__ dz
     }
 }
 
-__global__ __launch_bounds__(256) void rb_dw_reduce_kernel(const float *__restrict__ part,
-                                                           int64_t chunks, int64_t nd,
-                                                           float *__restrict__ dw) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= nd) return;
-  float s = 0.f;
-  for (int64_t ch = 0; ch < chunks; ++ch) s += part[ch * nd + i];
-  dw[i] = s;
+// dw[i] = sum over the chunks of part[ch][i] in a fixed order: a block owns
+// 256 consecutive outputs (a float4 a lane); wave g sums chunks g, g + 16,
+// g + 32, ... in order (1 KiB loads, all of a wave's in flight together) and
+// the 16 wave sums are added in wave order.
+constexpr int kRedWaves = 16;
+__global__ __launch_bounds__(64 * kRedWaves) void rb_dw_reduce_kernel(
+    const float *__restrict__ part, int64_t chunks, int64_t nd, float *__restrict__ dw) {
+  __shared__ float4 sp[kRedWaves][64];
+  const int lane = threadIdx.x & 63, g = threadIdx.x >> 6;
+  const int64_t i = ((int64_t)blockIdx.x * 64 + lane) * 4;  // nd % 4 == 0
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (i < nd) {
+#pragma unroll 8
+    for (int64_t ch = g; ch < chunks; ch += kRedWaves) {
+      const float4 p = *reinterpret_cast<const float4 *>(part + ch * nd + i);
+      s.x += p.x;
+      s.y += p.y;
+      s.z += p.z;
+      s.w += p.w;
+    }
+  }
+  sp[g][lane] = s;
+  __syncthreads();
+  if (g != 0 || i >= nd) return;
+  float4 t = sp[0][lane];
+#pragma unroll
+  for (int q = 1; q < kRedWaves; ++q) {
+    const float4 p = sp[q][lane];
+    t.x += p.x;
+    t.y += p.y;
+    t.z += p.z;
+    t.w += p.w;
+  }
+  *reinterpret_cast<float4 *>(dw + i) = t;
 }
 
 // du[t][c] = sum_n dz[t][n] * W_route[n][c]: a thread owns columns
@@ -271,8 +298,8 @@ hipError_t launch_route_backward(const float *logits, int64_t T, int N, int k, i
                                         (unsigned)chunks),
                      dim3(256), 0, st, dz, u, T, N, d, chunk, part);
   const int64_t nd = (int64_t)N * d;
-  hipLaunchKernelGGL(rb_dw_reduce_kernel, dim3((unsigned)((nd + 255) / 256)), dim3(256), 0, st,
-                     part, chunks, nd, dw);
+  hipLaunchKernelGGL(rb_dw_reduce_kernel, dim3((unsigned)((nd + 255) / 256)), dim3(64 * kRedWaves),
+                     0, st, part, chunks, nd, dw);
   hipLaunchKernelGGL(rb_du_kernel, dim3((unsigned)((d / 8 + 255) / 256),
                                         (unsigned)((T + kDuTokens - 1) / kDuTokens)),
                      dim3(256), 0, st, dz, w_route, T, N, d, du);
