@@ -180,12 +180,11 @@ __global__ __launch_bounds__(256) void decode_kernel(
   // The windows are software-pipelined: window i + 1's loads are issued as
   // soon as window i's registers are parked in the slice, so they are in
   // flight while window i is multiplied (Mixtral T=32 FP8 forward 0.299 ->
-  // 0.285 ms).  Only as much of the window goes early as keeps two waves
-  // per SIMD: half of it for the MXFP4 gate/up (the whole window beside its
-  // scale and token registers exceeds 256 VGPRs: 0.134 -> 0.192 ms; half:
-  // 0.135 -> 0.131 ms; with 128-byte windows the whole window goes early).
-  // A window's token fragments are loaded at the top of its own iteration,
-  // before the next window's weight loads.
+  // 0.285 ms).  The whole window goes early in every format (the MXFP4
+  // gate/up's earlier 256-byte windows could send only half of theirs: the
+  // whole one beside the scale and token registers took it past 256 VGPRs,
+  // 0.134 -> 0.192 ms).  A window's token fragments are loaded at the top of
+  // its own iteration, before the next window's weight loads.
   constexpr bool kPipe = true;
   // Load instructions per matrix issued a window early; the rest are issued
   // at the top of the window's own iteration.

@@ -68,10 +68,13 @@ constexpr int kThreads = 512;  // 8 waves: two per SIMD
 constexpr int kBBytes = BN * BK * 2;   // 32 KiB per B stage
 constexpr int kMSuper = 8;                       // m-tiles per scheduling group
 
-// Byte offset of 16-byte chunk c of row r inside one [256][64] bf16 tile
-// (chunk XOR-swizzled with the row's low three bits).
+// Byte offset of 16-byte chunk c of row r inside one [256][64] bf16 tile.
+// The chunk is XOR-swizzled with row bits 1-3: two 128-byte rows share the
+// 64 banks, so the 16 rows of a fragment read's lane phase land on 16
+// distinct 16-byte bank groups (bits 0-2 left rows r and r + 8 on the same
+// banks, a 2-way conflict on every fragment read).
 __device__ __forceinline__ uint32_t swz(int r, int c) {
-  return (uint32_t)(r * 128 + ((c ^ (r & 7)) << 4));
+  return (uint32_t)(r * 128 + ((c ^ ((r >> 1) & 7)) << 4));
 }
 
 __device__ __forceinline__ bf16x8 lds_frag(const char *tile, int r, int c) {
@@ -196,7 +199,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
     if (a.mode == GM_GATHER) arow = a.perm[a.offsets[g] + rr] / a.kslots;
     else if (a.mode == GM_SEGMENT) arow = seg0 + rr;
     else arow = (int64_t)g * a.a_group_rows + rr;
-    const int pc = lc ^ (r & 7);  // the chunk this lane's LDS slot holds
+    const int pc = lc ^ ((r >> 1) & 7);  // the chunk this lane's LDS slot holds
     aoff[i] = (uint32_t)(arow * a.lda * 2) + (uint32_t)(pc << 4);
   }
   // B rows: bf16, instruction i fills rows 64i + tid/8 (8 lanes a row);
@@ -233,7 +236,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
       continue;
     }
     const int r = FP8 ? (tid >> 2) + 128 * i : lr + 64 * i;
-    const int pc = FP8 ? ((tid & 3) ^ ((r >> 2) & 3)) : (lc ^ (r & 7));
+    const int pc = FP8 ? ((tid & 3) ^ ((r >> 2) & 3)) : (lc ^ ((r >> 1) & 7));
     int64_t brow;
     if (glu) {
       const int64_t n = n_tile * 128 + (r & 127);
