@@ -40,6 +40,19 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t v
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
 }
 
+// Wait until at most N vector-memory loads of this wave are outstanding
+// (gfx9 s_waitcnt field layout: vmcnt bits 3:0 and 15:14, expcnt 6:4 and
+// lgkmcnt 11:8 left at their maxima, i.e. not waited for).  Issued as the
+// builtin, the compiler's own wait insertion sees it and adds no stricter
+// wait for the loads it covers; the empty asm keeps memory accesses from
+// being moved across it.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  asm volatile("" ::: "memory");
+}
+
 // Workgroup barrier that leaves vector-memory loads in flight: LDS traffic
 // is drained (lgkmcnt 0) but, unlike __syncthreads(), no vmcnt(0) is forced,
 // so callers wait for exactly the loads they need with s_waitcnt vmcnt(N).

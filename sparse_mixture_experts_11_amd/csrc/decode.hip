@@ -23,6 +23,8 @@
 // use 128-byte windows of 256 k for the gate/up and 256-byte windows of 512 k
 // for the down; each k-step's operand is 4 bytes, widened with its block
 // scale folded in (v_cvt_scalef32_pk_bf16_fp4, exact).
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -42,17 +44,16 @@ template <int WF>
 constexpr int kstep_bytes() { return WF == WF_BF16 ? 64 : (WF == WF_FP8 ? 32 : 16); }
 // k-steps of 32 per iteration.  bf16: 16 KiB of weights per wave per
 // iteration (GLU: 2 matrices x 32 rows x 256 B, U = 4; down: 32 rows x
-// 512 B, U = 8).  fp8 and MXFP4: 256-byte row windows for both (U = 8 and
-// 16): GLU streams 16 KiB, down 8 KiB, which keeps it at two workgroups per
-// CU (a 512-byte fp8 window's operand registers push it past 256 VGPRs;
-// measured 0.13 vs 0.10 ms at the Mixtral decode shape).
-// MXFP4 gate/up: 128-byte row windows (U = 8), an 8 KiB window a wave, so
-// that three blocks fit a CU (LDS and registers) instead of two (Mixtral
-// T=32 gate/up 0.117 -> 0.110 ms).  The MXFP4 down keeps 256-byte windows
-// (U = 16): with 128-byte ones it ran 0.076 -> 0.081 ms.
-template <bool GLU, int WF>
+// 512 B, U = 8).  fp8: 256-byte row windows (U = 8): GLU streams 16 KiB,
+// down 8 KiB (a 512-byte fp8 window's operand registers push it past 256
+// VGPRs; measured 0.13 vs 0.10 ms at the Mixtral decode shape).  MXFP4
+// gate/up: 128-byte row windows (U = 8), an 8 KiB window a wave (Mixtral
+// T=32 gate/up 0.117 -> 0.110 ms against 256-byte ones).  The MXFP4 down
+// takes 256-byte windows (U = 16) with one token group a workgroup (the
+// window's 16 token fragments beside it) and 128-byte ones with two.
+template <bool GLU, int WF, int TG>
 constexpr int unroll_of() {
-  return WF == WF_BF16 ? (GLU ? 4 : 8) : (WF == WF_MX4 && !GLU ? 16 : 8);
+  return WF == WF_BF16 ? (GLU ? 4 : 8) : (WF == WF_MX4 && !GLU && TG == 1 ? 16 : 8);
 }
 
 // S1, S2: fp32 row scales [N][wrows] (WF_FP8) or E8M0 block scales
@@ -68,7 +69,7 @@ __global__ __launch_bounds__(256) void decode_kernel(
   constexpr bool MX4 = WF == WF_MX4;
   constexpr int NM = GLU ? 2 : 1;
   constexpr int KSB = kstep_bytes<WF>();  // bytes per row per 32-k step
-  constexpr int U = unroll_of<GLU, WF>();
+  constexpr int U = unroll_of<GLU, WF, TG>();
   constexpr int kPitch = U * KSB;         // bytes of one row's window in a slice
   constexpr int kLoads = kPitch / 32;     // 1 KiB load instructions per matrix
   constexpr int kSlice = NM * RB * kPitch;  // per-wave LDS slice: one iteration's weights
@@ -120,15 +121,30 @@ __global__ __launch_bounds__(256) void decode_kernel(
   // Whole-line loads: instruction i takes rows 8*(i%4) + lane/8 and the
   // 128-byte piece i/4 of the iteration's window; lane%8 picks 16 bytes.
   const int lr = lane >> 3, lc = lane & 7;
-  const char *g1 = static_cast<const char *>(W1) + ((int64_t)e * wrows + row0 + lr) * rowK +
-                   kbytes(kb) + 16 * lc;
-  const char *g2 = GLU ? static_cast<const char *>(W2) + ((int64_t)e * wrows + row0 + lr) * rowK +
-                             kbytes(kb) + 16 * lc
-                       : nullptr;
+  // The window loads go through buffer resources over the workgroup's 32
+  // weight rows: one lane offset per matrix, the rest uniform.
+  const uint32_t blk_bytes = (uint32_t)(RB * rowK);
+  const __amdgpu_buffer_rsrc_t rw1 = make_rsrc(
+      static_cast<const char *>(W1) + ((int64_t)e * wrows + row0) * rowK, blk_bytes);
+  const __amdgpu_buffer_rsrc_t rw2 =
+      GLU ? make_rsrc(static_cast<const char *>(W2) + ((int64_t)e * wrows + row0) * rowK,
+                      blk_bytes)
+          : rw1;
+  const uint32_t wlo = (uint32_t)(lr * rowK + kbytes(kb) + 16 * lc);
   char *slice = smem + wave * kSlice;
   char *sslot = smem + kWaves * kSlice + wave * kScale;  // MXFP4 window scales
   const uint16_t *xr[TG];
   bool xv[TG];
+  // Token fragments of the windows are read through a buffer resource over
+  // x: a lane with no token (past the expert's rows, or a group the expert
+  // does not have) reads past the resource's end and gets zeros, so every
+  // window issues the same loads with no branch around them, and the
+  // compiler's waits for a window's weights count exactly the token loads
+  // issued after them (with a branch per load it waited for those too, so
+  // the next window's weights were requested only once the current window's
+  // tokens had arrived).
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, kDecodeXBytes);
+  uint32_t xo[TG];
 #pragma unroll
   for (int tg = 0; tg < TG; ++tg) {
     const int j = (g0 + tg) * 16 + li;
@@ -137,6 +153,7 @@ __global__ __launch_bounds__(256) void decode_kernel(
     if (GLU) row = xv[tg] ? perm[offsets[e] + j] / kslots : 0;
     else row = kept_offsets[e] + (xv[tg] ? j : 0);
     xr[tg] = x + row * ldx + kb + kq;
+    xo[tg] = xv[tg] ? (uint32_t)((row * ldx + kb + kq) * 2) : kDecodeXBytes;
   }
   const int ngroups = (M + 15) / 16 - g0;  // this workgroup's groups (may exceed TG)
 
@@ -177,19 +194,20 @@ __global__ __launch_bounds__(256) void decode_kernel(
       return *reinterpret_cast<const bf16x8 *>(w + byte_off);
     }
   };
-  // The windows are software-pipelined: window i + 1's loads are issued as
-  // soon as window i's registers are parked in the slice, so they are in
-  // flight while window i is multiplied (Mixtral T=32 FP8 forward 0.299 ->
-  // 0.285 ms).  The whole window goes early in every format (the MXFP4
-  // gate/up's earlier 256-byte windows could send only half of theirs: the
-  // whole one beside the scale and token registers took it past 256 VGPRs,
-  // 0.134 -> 0.192 ms).  A window's token fragments are loaded at the top of
-  // its own iteration, before the next window's weight loads.
-  constexpr bool kPipe = true;
-  // Load instructions per matrix issued a window early; the rest are issued
-  // at the top of the window's own iteration.
-  constexpr int kEarly = kLoads;
-  const int kfull = Kw - Kw % (32 * U);
+  // The windows are software-pipelined.  An iteration requests its
+  // window's token fragments (L2 hits), parks the window's weights (requested
+  // one iteration earlier) in the slice, requests the next window's weights
+  // and only then waits for its tokens, so a window of weights is in flight
+  // while this one is multiplied and the token latency overlaps that request
+  // instead of delaying it.  Every load of an iteration is unconditional, so
+  // the waits count them exactly.
+  // MXFP4 windows load their scales as dwords, which needs every wave's K
+  // start 4-byte aligned in the scale rows (K / 128 a multiple of 4): K a
+  // multiple of 512; other widths take the per-k-step loop below for the
+  // whole K.
+  const int nwin = (MX4 && K % 512 != 0) ? 0 : Kw / (32 * U);
+  const int kfull = nwin * 32 * U;
+  constexpr int kTokLoads = TG * U;  // token loads issued after a window's weights
   u32x4 v[NM][kLoads];
   // MXFP4: the window's U scale bytes of each of the 32 rows go straight to
   // the wave's scale slot (U = 8: one dword load per matrix, lane l: row
@@ -204,55 +222,48 @@ __global__ __launch_bounds__(256) void decode_kernel(
     if constexpr (GLU)
       rs[NM - 1] = make_rsrc(static_cast<const uint8_t *>(S2) + (int64_t)e * wrows * KB, sbytes);
   }
-  auto load_window = [&](int kw, int i0, int i1) {
+  auto load_window = [&](int kw) {
     if constexpr (MX4) {
       static_assert(U == 8 || U == 16, "scale slot layouts for 8 or 16 bytes a row");
-      if (i0 == 0) {
 #pragma unroll
-        for (int m = 0; m < NM; ++m) {
-          if constexpr (U == 8) {
+      for (int m = 0; m < NM; ++m) {
+        if constexpr (U == 8) {
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rs[m], (lds_ptr_t)(sslot + m * RB * U), 4,
+              (uint32_t)((row0 + (lane >> 1)) * KB + (kb + kw) / 32 + 4 * (lane & 1)), 0, 0, 0);
+        } else {
+#pragma unroll
+          for (int q = 0; q < 2; ++q)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rs[m], (lds_ptr_t)(sslot + m * RB * U), 4,
-                (uint32_t)((row0 + (lane >> 1)) * KB + (kb + kw) / 32 + 4 * (lane & 1)), 0, 0, 0);
-          } else {
-#pragma unroll
-            for (int q = 0; q < 2; ++q)
-              __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                  rs[m], (lds_ptr_t)(sslot + m * RB * U + q * 256), 4,
-                  (uint32_t)((row0 + 16 * q + (lane >> 2)) * KB + (kb + kw) / 32 + 4 * (lane & 3)),
-                  0, 0, 0);
-          }
+                rs[m], (lds_ptr_t)(sslot + m * RB * U + q * 256), 4,
+                (uint32_t)((row0 + 16 * q + (lane >> 2)) * KB + (kb + kw) / 32 + 4 * (lane & 3)),
+                0, 0, 0);
         }
       }
     }
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
-      if (i < i0 || i >= i1) continue;
-      const int64_t off = (int64_t)(8 * (i % 4)) * rowK + 128 * (i / 4) + kbytes(kw);
-      v[0][i] = *reinterpret_cast<const u32x4 *>(g1 + off);
-      if (GLU) v[NM - 1][i] = *reinterpret_cast<const u32x4 *>(g2 + off);
+      const uint32_t so = (uint32_t)(8 * (i % 4) * rowK + kbytes(kw));
+      v[0][i] = buf_load16(rw1, wlo + 128 * (i / 4), so);
+      if (GLU) v[NM - 1][i] = buf_load16(rw2, wlo + 128 * (i / 4), so);
     }
   };
-  if (kPipe && kfull > 0) load_window(0, 0, kEarly);
-  int k = 0;
-  for (; k < kfull; k += 32 * U) {
-    if (!kPipe) load_window(k, 0, kLoads);
-    else if (kEarly < kLoads) load_window(k, kEarly, kLoads);
-    // Token fragments of the whole window up front (the MXFP4 down's 16
-    // k-steps of them would not fit beside the loads: it takes them in
-    // groups of 4 k-steps in its loop below).
-    constexpr bool kGrouped = MX4 && U == 16;
-    constexpr int UB = kGrouped ? 1 : U;
-    bf16x8 b[TG][UB];
-    if constexpr (!kGrouped) {
+  // One window; LAST (the final window, peeled off the loop) requests no
+  // next one, so every path through the loop body issues the same loads and
+  // the compiler's waits for the token fragments stop short of the next
+  // window's requests.
+  auto window_step = [&](const int k, auto last_c) {
+    constexpr bool LAST = decltype(last_c)::value;
+    // The window's token fragments (zeros for lanes with no token).
+    bf16x8 b[TG][U];
 #pragma unroll
-      for (int tg = 0; tg < TG; ++tg)
+    for (int tg = 0; tg < TG; ++tg)
 #pragma unroll
-        for (int u = 0; u < U; ++u)
-          b[tg][u] = (tg < ngroups && xv[tg])
-                         ? *reinterpret_cast<const bf16x8 *>(xr[tg] + k + 32 * u)
-                         : zero;
-    }
+      for (int u = 0; u < U; ++u)
+        b[tg][u] = __builtin_bit_cast(bf16x8, buf_load16(rx, xo[tg] + 2 * (k + 32 * u), 0));
+    // (the scheduler would otherwise sink some token loads below the next
+    // window's requests, and waiting for them would wait for that window)
+    __builtin_amdgcn_sched_barrier(0);
     // Into the wave's own slice, swizzled.
 #pragma unroll
     for (int m = 0; m < NM; ++m)
@@ -264,13 +275,12 @@ __global__ __launch_bounds__(256) void decode_kernel(
             v[m][i];
       }
     // MXFP4: the window's U block scales of each of the lane's rows, from
-    // the scale slot (its loads were issued before the window's, which are
-    // all complete once the window is parked), read before the next
-    // window's loads may overwrite the slot.  The wait also covers the token
-    // loads just issued, which the MFMAs below need first anyway.
+    // the scale slot (its loads were issued before this window's token
+    // loads, so they are complete once at most those remain), read before
+    // the next window's loads may overwrite the slot.
     uint32_t sw[NM][NRB][U / 4];
     if constexpr (MX4) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      wait_vmcnt<kTokLoads>();
 #pragma unroll
       for (int m = 0; m < NM; ++m)
 #pragma unroll
@@ -288,49 +298,15 @@ __global__ __launch_bounds__(256) void decode_kernel(
         }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
-    if (kPipe && k + 32 * U < kfull) load_window(k + 32 * U, 0, kEarly);
+    // The next window's weights; the MFMAs below then wait for this
+    // window's tokens only.
+    if constexpr (!LAST) load_window(k + 32 * U);
+    __builtin_amdgcn_sched_barrier(0);
     // MFMA operands: lane l takes row 16 rb + l%16, k values 32u + 8(l/16) .. +7.
-    if constexpr (kGrouped) {
-      // Token fragments in groups of 4 k-steps, the next group loading
-      // while this one computes.
-      bf16x8 bq[2][TG][4];
-      auto load_group = [&](int grp, bf16x8 (&dst)[TG][4]) {
-#pragma unroll
-        for (int tg = 0; tg < TG; ++tg)
-#pragma unroll
-          for (int uu = 0; uu < 4; ++uu)
-            dst[tg][uu] = (tg < ngroups && xv[tg])
-                              ? *reinterpret_cast<const bf16x8 *>(xr[tg] + k + 32 * (4 * grp + uu))
-                              : zero;
-      };
-      load_group(0, bq[0]);
-#pragma unroll
-      for (int grp = 0; grp < U / 4; ++grp) {
-        if (grp + 1 < U / 4) load_group(grp + 1, bq[(grp + 1) & 1]);
-#pragma unroll
-        for (int uu = 0; uu < 4; ++uu) {
-          const int u = 4 * grp + uu;
-          bf16x8 a[NM][NRB];
-#pragma unroll
-          for (int m = 0; m < NM; ++m)
-#pragma unroll
-            for (int rb = 0; rb < NRB; ++rb)
-              a[m][rb] = slice_frag(m, 16 * rb + li, u,
-                                    e8m0_to_f32((sw[m][rb][u >> 2] >> (8 * (u & 3))) & 0xFF));
-#pragma unroll
-          for (int tg = 0; tg < TG; ++tg) {
-            if (tg < ngroups) {
-#pragma unroll
-              for (int m = 0; m < NM; ++m)
-#pragma unroll
-                for (int r = 0; r < NRB; ++r)
-                  acc[m][r][tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                      a[m][r], bq[grp & 1][tg][uu], acc[m][r][tg], 0, 0, 0);
-            }
-          }
-        }
-      }
-    } else if constexpr (MX4) {
+    // A group the expert does not have multiplies its zero token fragments:
+    // a branch around it would let the compiler sink that group's token
+    // loads into the branch, below the next window's requests.
+    if constexpr (MX4) {
       // Widened operands of one k-step at a time, each with its block scale.
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -342,16 +318,13 @@ __global__ __launch_bounds__(256) void decode_kernel(
             a[m][rb] = slice_frag(m, 16 * rb + li, u,
                                   e8m0_to_f32((sw[m][rb][u >> 2] >> (8 * (u & 3))) & 0xFF));
 #pragma unroll
-        for (int tg = 0; tg < TG; ++tg) {
-          if (tg < ngroups) {
+        for (int tg = 0; tg < TG; ++tg)
 #pragma unroll
-            for (int m = 0; m < NM; ++m)
+          for (int m = 0; m < NM; ++m)
 #pragma unroll
-              for (int r = 0; r < NRB; ++r)
-                acc[m][r][tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[m][r], b[tg][u],
-                                                                       acc[m][r][tg], 0, 0, 0);
-          }
-        }
+            for (int r = 0; r < NRB; ++r)
+              acc[m][r][tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[m][r], b[tg][u],
+                                                                     acc[m][r][tg], 0, 0, 0);
       }
     } else if constexpr (FP8) {
       // Widened operands of one k-step at a time (all U would not fit
@@ -364,16 +337,13 @@ __global__ __launch_bounds__(256) void decode_kernel(
 #pragma unroll
           for (int rb = 0; rb < NRB; ++rb) a[m][rb] = slice_frag(m, 16 * rb + li, u, 1.f);
 #pragma unroll
-        for (int tg = 0; tg < TG; ++tg) {
-          if (tg < ngroups) {
+        for (int tg = 0; tg < TG; ++tg)
 #pragma unroll
-            for (int m = 0; m < NM; ++m)
+          for (int m = 0; m < NM; ++m)
 #pragma unroll
-              for (int r = 0; r < NRB; ++r)
-                acc[m][r][tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[m][r], b[tg][u],
-                                                                       acc[m][r][tg], 0, 0, 0);
-          }
-        }
+            for (int r = 0; r < NRB; ++r)
+              acc[m][r][tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[m][r], b[tg][u],
+                                                                     acc[m][r][tg], 0, 0, 0);
       }
     } else {
       bf16x8 a[NM][NRB][U];
@@ -384,20 +354,23 @@ __global__ __launch_bounds__(256) void decode_kernel(
 #pragma unroll
           for (int u = 0; u < U; ++u) a[m][rb][u] = slice_frag(m, 16 * rb + li, u, 1.f);
 #pragma unroll
-      for (int tg = 0; tg < TG; ++tg) {
-        if (tg < ngroups) {
+      for (int tg = 0; tg < TG; ++tg)
 #pragma unroll
-          for (int u = 0; u < U; ++u)
+        for (int u = 0; u < U; ++u)
 #pragma unroll
-            for (int m = 0; m < NM; ++m)
+          for (int m = 0; m < NM; ++m)
 #pragma unroll
-              for (int r = 0; r < NRB; ++r)
-                acc[m][r][tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[m][r][u], b[tg][u],
-                                                                       acc[m][r][tg], 0, 0, 0);
-        }
-      }
+            for (int r = 0; r < NRB; ++r)
+              acc[m][r][tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[m][r][u], b[tg][u],
+                                                                     acc[m][r][tg], 0, 0, 0);
     }
+  };
+  if (nwin > 0) {
+    load_window(0);
+    for (int wi = 0; wi + 1 < nwin; ++wi) window_step(wi * 32 * U, std::false_type{});
+    window_step((nwin - 1) * 32 * U, std::true_type{});
   }
+  int k = kfull;
   for (; k < Kw; k += 32) {
     bf16x8 a[NM][NRB];
 #pragma unroll
@@ -500,15 +473,15 @@ hipError_t launch_decode(int tg, int64_t wrows, int N, hipStream_t st, const uin
                          const void *S1, const void *S2, int K, int act, float bg, float bu,
                          void *out, int64_t ldo) {
   // tg token groups of 16 may be needed per expert (T up to 16 tg).  A
-  // workgroup holds at most two of them in registers (three or four cost a
-  // wave per SIMD: Mixtral T=64 gate/up 0.324 -> 0.312 ms bf16, 0.215 ->
-  // 0.140 ms MXFP4), one for the MXFP4 gate/up at T <= 32 (its widened
-  // operands leave room for two waves per SIMD only with one group: 0.123 ->
-  // 0.117 ms), and the grid's z covers the rest: with k of N experts chosen
-  // per token an expert rarely gets more than half the tokens, so the extra
-  // z workgroups exit at once, and an expert that does use them reads its
-  // weights once per z.
-  const int cap = (GLU && WF == WF_MX4 && tg <= 2) ? 1 : 2;
+  // workgroup holds one of them up to T = 32 and two beyond (three or four
+  // cost a wave per SIMD: Mixtral T=64 gate/up 0.324 -> 0.312 ms bf16,
+  // 0.215 -> 0.140 ms MXFP4), and the grid's z covers the rest: with k of N
+  // experts chosen per token an expert rarely gets more than half the
+  // tokens, so the extra z workgroups exit at once, and an expert that does
+  // use them reads its weights once per z.  One group a workgroup frees the
+  // second group's token registers (Mixtral T=32, against two: MXFP4
+  // forward 0.201 -> 0.190 ms, FP8 0.268 -> 0.265 ms, bf16 unchanged).
+  const int cap = tg <= 2 ? 1 : 2;
   const int tgw = tg < cap ? tg : cap;
   const dim3 grid((unsigned)(wrows / RB), N, (unsigned)((tg + tgw - 1) / tgw));
 #define MOE_DECODE_CASE(TGV)                                                                  \

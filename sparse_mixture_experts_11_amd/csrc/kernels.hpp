@@ -175,6 +175,10 @@ hipError_t launch_shared_route(int64_t T, int S, float *w, int32_t *perm, int32_
 // ---- decode-sized experts (decode.hip) -------------------------------------
 // Max rows per expert the decode kernels take.
 constexpr int kDecodeMaxRows = 64;
+// The decode kernels read their activations (token rows) through a buffer
+// resource of this many bytes from the matrix's start; the launchers refuse
+// a matrix that does not fit it.
+constexpr uint32_t kDecodeXBytes = 1u << 31;
 // Routed-expert weight formats of the decode kernels (wfmt): bf16; E4M3
 // codes with fp32 row scales s* ([N, h] gate/up, [N, w] down); MXFP4 (E2M1
 // codes two a byte) with E8M0 block scales s* ([N, rows, K/32]).

@@ -29,6 +29,9 @@ MX_CASES = {name: cfg.with_(name=name + "_mxfp4", w_dtype="mxfp4") for name, cfg
     ("mixtral_small_t37_decode", CASES["mixtral_small_t37_decode"]),  # down K = 2048: one window
     ("mixtral_small_t64_decode", CASES["mixtral_small_t64_decode"]),  # four token groups
     ("mix_d2048_t40", MIX_S.with_(T=40, d=2048, h=2048)),           # main loop on both
+    # gate/up K = 1152 (not a multiple of 512): the per-k-step loop for all
+    # of K; down K = 2560: one 512-k window a wave and a 128-k remainder
+    ("mix_d1152_t24_decode", MIX_S.with_(T=24, d=1152, h=2560)),
     ("switch_small_t48_decode", CASES["switch_small_t48_decode"]),  # top-1 with capacity
     ("latent_small_decode_t20", CASES["latent_small_decode_t20"]),  # latent layer
     # tiled GEMM
