@@ -31,7 +31,9 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
 }
 
-// Raw buffer resource over [base, base + bytes); reads past the end return 0.
+// Raw buffer resource over [base, base + bytes); a read whose lane offset
+// (plus the immediate) reaches past the end returns 0 (offsets that must be
+// range-checked go in the lane offset, not the scalar one).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
 }

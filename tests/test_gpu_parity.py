@@ -319,6 +319,12 @@ ROUTE_SHAPES = [
     dict(T=523, d=512, N=5, k=1, router_dtype="f32", bias=True),
     dict(T=2050, d=1024, N=8, k=2, router_dtype="f32", bias=False),
     dict(T=4099, d=4096, N=7, k=2, router_dtype="bf16", bias=True),
+    # d = 4096 (the tile router's CH = 8): a token count just past the
+    # one-block-per-token router, a partial last 4-token group with every
+    # expert selected, three experts with top-1 and a selection bias
+    dict(T=300, d=4096, N=8, k=2, router_dtype="bf16", bias=False),
+    dict(T=2061, d=4096, N=8, k=8, router_dtype="bf16", bias=False),
+    dict(T=2500, d=4096, N=3, k=1, router_dtype="bf16", bias=True),
     dict(T=300, d=1536, N=8, k=2, router_dtype="bf16", bias=False),  # older wave router
     # N > 64: router GEMM, then the top-k over its logits (in two K-halves
     # while the GEMM's tiles would fill under three quarters of the CUs)
