@@ -612,7 +612,8 @@ def main():
         kernel = "simt_gu_kernel (fp32 expert gate/up)"
     elif cfg.T <= 64:
         wf = {"bf16": 0, "fp8": 1, "mxfp4": 2}[cfg.w_dtype]
-        kernel = f"decode_kernel<true, 2, {wf}> (expert gate/up)"
+        tg = 1 if cfg.T <= 32 else 2   # token groups a workgroup holds
+        kernel = f"decode_kernel<true, {tg}, {wf}> (expert gate/up)"
     else:
         kernel = (f"grouped_gemm_kernel<EP_GLU, {tile_rows(cfg)}"
                   f"{', true' if cfg.w_dtype == 'fp8' else ''}> (expert gate/up)")

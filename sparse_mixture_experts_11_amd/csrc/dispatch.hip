@@ -92,10 +92,21 @@ __global__ __launch_bounds__(256) void dispatch_count_kernel(
 }
 
 // Inclusive block scan of one value per thread (blockDim.x == 1024).
-__device__ int block_incl_scan(int v, int *tmp) {
+// First level of a halving tree over n values: the largest power of two
+// below n (0 for n = 1), so that its levels pair exactly the nonzero ones.
+__device__ __forceinline__ int tree_top(int n) {
+  int s = 1;
+  while (s < n) s <<= 1;
+  return s >> 1;
+}
+
+// Inclusive scan of v over threads 0 .. n - 1 (the values of threads n and
+// above are not used and need not be zero): log2(n) steps instead of
+// log2(blockDim), each with its two barriers.
+__device__ int block_incl_scan(int v, int *tmp, int n) {
   tmp[threadIdx.x] = v;
   __syncthreads();
-  for (int o = 1; o < (int)blockDim.x; o <<= 1) {
+  for (int o = 1; o < n; o <<= 1) {
     const int add = (int)threadIdx.x >= o ? tmp[threadIdx.x - o] : 0;
     __syncthreads();
     tmp[threadIdx.x] += add;
@@ -133,7 +144,8 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(
     }
     red[n] = fp;
     __syncthreads();
-    for (int s = 512; s > 0; s >>= 1) {
+    // Levels at or past N would add the zeros of threads N and above.
+    for (int s = tree_top(N); s > 0; s >>= 1) {
       if (n < s) red[n] += red[n + s];
       __syncthreads();
     }
@@ -163,8 +175,8 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(
     counts[n] = total;
   }
   const int kept = (n < N) ? ((capacity >= 0 && total > capacity) ? capacity : total) : 0;
-  const int inc_all = block_incl_scan(n < N ? total : 0, tmp);
-  const int inc_kept = block_incl_scan(kept, tmp);
+  const int inc_all = block_incl_scan(n < N ? total : 0, tmp, N);
+  const int inc_kept = block_incl_scan(kept, tmp, N);
   if (n < N) {
     offsets[n + 1] = inc_all;
     kept_offsets[n + 1] = inc_kept;
@@ -241,18 +253,34 @@ __global__ __launch_bounds__(1024) void small_tail_kernel(
   const int lane = tid & 63;
   const int wave = tid >> 6;
 
+  // The dispatch's expert id, requested before the statistics so that its
+  // latency overlaps theirs.
+  int e = (perm != nullptr && tid < E) ? idx[tid] : -1;
   if (stats != nullptr) {
     // f_n = (argmax count) / T, P_n = (sum of p) / T, partial rows summed in
-    // row order; N * sum_n f_n P_n by a fixed tree.
+    // row order; N * sum_n f_n P_n by a fixed tree.  The rows come through
+    // LDS 1024 values at a time, every thread loading one (one round trip
+    // per 1024 values instead of one per 8 rows).
     float fp = 0.f;
-    if (tid < N) {
-      float p = 0.f;
-      int64_t c = 0;
-#pragma unroll 8
-      for (int wv = 0; wv < waves; ++wv) {  // independent loads, issued in batches
-        p += part_p[(int64_t)wv * N + tid];
-        c += part_cnt[(int64_t)wv * N + tid];
+    float p = 0.f;
+    int64_t c = 0;
+    const int64_t nval = (int64_t)waves * N;
+    for (int64_t v0 = 0; v0 < nval; v0 += 1024) {
+      const int64_t v = v0 + tid;
+      red[tid] = v < nval ? part_p[v] : 0.f;
+      tmp[tid] = v < nval ? part_cnt[v] : 0;
+      __syncthreads();
+      if (tid < N) {
+        // this chunk's rows of column tid, in row order
+        const int64_t r0 = (v0 + N - 1 - tid) / N;  // first row r with r N + tid >= v0
+        for (int64_t r = r0; r * N + tid < v0 + 1024 && r < waves; ++r) {
+          p += red[r * N + tid - v0];
+          c += tmp[r * N + tid - v0];
+        }
       }
+      __syncthreads();
+    }
+    if (tid < N) {
       const float f = (float)((double)c / (double)T);
       const float P = p / (float)T;
       stats[tid] = f;
@@ -261,7 +289,8 @@ __global__ __launch_bounds__(1024) void small_tail_kernel(
     }
     red[tid] = fp;
     __syncthreads();
-    for (int s = 512; s > 0; s >>= 1) {
+    // Levels at or past N would add the zeros of threads N and above.
+    for (int s = tree_top(N); s > 0; s >>= 1) {
       if (tid < s) red[tid] += red[tid + s];
       __syncthreads();
     }
@@ -275,7 +304,6 @@ __global__ __launch_bounds__(1024) void small_tail_kernel(
 
   for (int i = tid; i < kTailWaves * N; i += 1024) hist[i / N][i % N] = 0;
   __syncthreads();
-  int e = (tid < E) ? idx[tid] : -1;
   const bool ok = e >= 0 && e < N;
   if (!ok) e = -1;
   uint64_t same = __ballot(ok);
@@ -294,8 +322,8 @@ __global__ __launch_bounds__(1024) void small_tail_kernel(
   if (tid < N)
     for (int w = 0; w < kTailWaves; ++w) total += hist[w][tid];
   const int kept = (tid < N) ? ((capacity >= 0 && total > capacity) ? capacity : total) : 0;
-  const int inc_all = block_incl_scan(tid < N ? total : 0, tmp);
-  const int inc_kept = block_incl_scan(kept, tmp);
+  const int inc_all = block_incl_scan(tid < N ? total : 0, tmp, N);
+  const int inc_kept = block_incl_scan(kept, tmp, N);
   if (tid < N) {
     base_all[tid] = inc_all - total;
     base_kept[tid] = inc_kept - kept;
