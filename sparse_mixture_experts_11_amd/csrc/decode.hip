@@ -20,9 +20,10 @@
 // windows, 256 k; the operands are widened to bf16 exactly after the LDS
 // read, and the row scales multiply the fp32 sums after the split-K
 // reduction.  MXFP4 weights (E2M1 codes two a byte, one E8M0 scale per 32 k)
-// use 128-byte windows of 256 k for the gate/up and 256-byte windows of 512 k
-// for the down; each k-step's operand is 4 bytes, widened with its block
-// scale folded in (v_cvt_scalef32_pk_bf16_fp4, exact).
+// use 128-byte windows of 256 k for the gate/up and, for the down, 256-byte
+// windows of 512 k with one token group a workgroup (128-byte ones with
+// two); each k-step's operand is 4 bytes, widened with its block scale
+// folded in (v_cvt_scalef32_pk_bf16_fp4, exact).
 #include <type_traits>
 
 #include "common.hpp"
