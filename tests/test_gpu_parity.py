@@ -236,10 +236,12 @@ def test_unselected_expert_perturbation(name):
 
 
 HOT_DECODE_CASES = [
-    # (case, expert weights): at decode sizes a workgroup holds at most two
-    # 16-token groups of an expert (one for the MXFP4 gate/up at T <= 32),
-    # and the grid's z takes the rest; here every token goes to one or two
-    # experts, so those extra workgroups do the work.
+    # (case, expert weights): at decode sizes a workgroup holds one 16-token
+    # group of an expert up to T = 32 and two beyond, and the grid's z takes
+    # the rest; here every token goes to one or two experts, so those extra
+    # workgroups do the work.
+    ("mixtral_small_t32_decode", "bf16"),
+    ("mixtral_small_t32_decode", "mxfp4"),
     ("mixtral_small_t64_decode", "bf16"),
     ("mixtral_small_t64_decode", "fp8"),
     ("mixtral_small_t64_decode", "mxfp4"),
@@ -249,9 +251,14 @@ HOT_DECODE_CASES = [
 ]
 
 
+# Hot-expert cases beyond CASES: T = 32, two workgroups of one group each
+# on the hot experts (the MXFP4 down on 512-k windows).
+HOT_ONLY = {"mixtral_small_t32_decode": MIX_S.with_(T=32)}
+
+
 @pytest.mark.parametrize("name,wfmt", HOT_DECODE_CASES, ids=lambda v: str(v))
 def test_decode_hot_experts(name, wfmt):
-    cfg = CASES[name]
+    cfg = CASES[name] if name in CASES else HOT_ONLY[name]
     if wfmt != "bf16":
         cfg = cfg.with_(name=f"{cfg.name}_{wfmt}", w_dtype=wfmt)
     hot = [2, 5]
