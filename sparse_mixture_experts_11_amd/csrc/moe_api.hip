@@ -47,7 +47,15 @@ int64_t kept_rows_bound(const moe_desc_t &d) {
 bool is_latent(const moe_desc_t &d) { return d.l > 0; }
 int xwidth(const moe_desc_t &d) { return is_latent(d) ? d.l : d.d; }
 bool bf16_path(const moe_desc_t &d) { return d.act_dtype == MOE_BF16; }
-bool decode_path(const moe_desc_t &d) { return bf16_path(d) && d.T <= kDecodeMaxRows; }
+// Decode kernels: at most kDecodeMaxRows tokens, and token matrices (x
+// [T, w] into the gate/up, the hidden rows [R, h] into the down) within the
+// kDecodeXBytes their buffer resources address; larger layers take the
+// tiled GEMM.
+bool decode_path(const moe_desc_t &d) {
+  const int64_t w = d.l > 0 ? d.l : d.d;
+  return bf16_path(d) && d.T <= kDecodeMaxRows && d.T * w * 2 < (int64_t)kDecodeXBytes &&
+         kept_rows_bound(d) * (int64_t)d.h * 2 < (int64_t)kDecodeXBytes;
+}
 // MXFP4 expert weights: on the decode kernels (T <= 64 tokens) their
 // 4-byte block-scale loads need each contraction width (the expert input
 // width and h) below one 2048-wide window set or a multiple of 512; the
